@@ -1,0 +1,162 @@
+"""ctypes binding of the C++ oracle (``dgc_oracle.cpp``).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  All arrays are host
+NumPy arrays; every function checks dtypes and contiguity before the call.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dgc_oracle.cpp")
+_LIB = os.path.join(_HERE, "libdgc_oracle.so")
+
+# Plain IEEE binary32 arithmetic: no contraction into FMA, no fast-math.
+CXXFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-std=c++17", "-shared", "-fPIC"]
+
+_lib = None
+
+
+def lib_path():
+    return _LIB
+
+
+def build(verbose=False):
+    """Compile the oracle with g++ (always recompiles)."""
+    cmd = ["g++"] + CXXFLAGS + [_SRC, "-o", _LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def load():
+    """Load the oracle library, building it first if it is missing or stale."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if (not os.path.exists(_LIB)
+            or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_clip_scale.argtypes = [P, i64, ctypes.c_double, P, P]
+    lib.orc_clip_scale.restype = ctypes.c_int
+    lib.orc_momentum.argtypes = [P, i64, ctypes.c_float, ctypes.c_float, P, P]
+    lib.orc_momentum.restype = None
+    lib.orc_select_mask.argtypes = [P, P, i64, i64, P, P]
+    lib.orc_select_mask.restype = i64
+    lib.orc_encode.argtypes = [P, P, i64, P, P, i64]
+    lib.orc_encode.restype = i64
+    lib.orc_decode_accumulate.argtypes = [P, P, i64, P, i64]
+    lib.orc_decode_accumulate.restype = ctypes.c_int
+    lib.orc_k_for_density.argtypes = [i64, i64, i64]
+    lib.orc_k_for_density.restype = i64
+    lib.orc_step.argtypes = [ctypes.c_int32, P, P, P, P, P, ctypes.c_float,
+                             ctypes.c_double, P, P, P, P]
+    lib.orc_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a, dtype):
+    assert isinstance(a, np.ndarray), type(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    assert a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads():
+    return int(load().orc_num_threads())
+
+
+def clip_scale(g, clip):
+    """Return (norm: float, scale: np.float32) for gradient g (float32)."""
+    lib = load()
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    lib.orc_clip_scale(_ptr(g, np.float32), g.size, float(clip),
+                       _ptr(norm, np.float64), _ptr(scale, np.float32))
+    return float(norm[0]), np.float32(scale[0])
+
+
+def momentum(g, scale, m, u, v):
+    """In place: u <- m*u + g*scale ; v <- v + u (binary32)."""
+    assert g.size == u.size == v.size
+    load().orc_momentum(_ptr(g, np.float32), g.size, float(np.float32(scale)),
+                        float(np.float32(m)), _ptr(u, np.float32),
+                        _ptr(v, np.float32))
+
+
+def select_mask(u, v, k):
+    """Top-k of |v| for one tensor + masking, in place.  Returns (idx, val)."""
+    assert u.size == v.size
+    k = int(k)
+    idx = np.zeros(max(k, 1), np.uint32)
+    val = np.zeros(max(k, 1), np.float32)
+    got = load().orc_select_mask(_ptr(u, np.float32), _ptr(v, np.float32),
+                                 v.size, k, _ptr(idx, np.uint32),
+                                 _ptr(val, np.float32))
+    if got < 0:
+        raise ValueError("k out of range")
+    return idx[:got].copy(), val[:got].copy()
+
+
+def encode(idx, val, cap=None):
+    """Zero-run encoding of one tensor's (idx, val).  Returns (runs, vals)."""
+    k = idx.size
+    assert val.size == k
+    if cap is None:
+        cap = k + (int(idx[-1]) + 1) // 65536 + 1 if k else 1
+    runs = np.zeros(max(cap, 1), np.uint16)
+    vals = np.zeros(max(cap, 1), np.float32)
+    e = load().orc_encode(_ptr(idx, np.uint32), _ptr(val, np.float32), k,
+                          _ptr(runs, np.uint16), _ptr(vals, np.float32), cap)
+    if e == -1:
+        raise ValueError("encode capacity exceeded")
+    if e == -2:
+        raise ValueError("indices not strictly ascending")
+    return runs[:e].copy(), vals[:e].copy()
+
+
+def decode_accumulate(runs, vals, dense):
+    """dense += decoded stream (in place).  Returns 0, or -1 on a bad stream."""
+    assert runs.size == vals.size
+    return int(load().orc_decode_accumulate(
+        _ptr(runs, np.uint16), _ptr(vals, np.float32), runs.size,
+        _ptr(dense, np.float32), dense.size))
+
+
+def k_for_density(n, num, den):
+    return int(load().orc_k_for_density(int(n), int(num), int(den)))
+
+
+def step(sizes, k, g, u, v, m, clip):
+    """One learner step over tensors laid end to end (in place on u, v).
+
+    Returns (idx, val, norm, scale); idx/val hold every tensor's k entries
+    back to back in tensor order, with local (per-tensor) indices.
+    """
+    sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+    k = np.ascontiguousarray(k, dtype=np.int64)
+    K = int(k.sum())
+    idx = np.zeros(max(K, 1), np.uint32)
+    val = np.zeros(max(K, 1), np.float32)
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    rc = load().orc_step(len(sizes), _ptr(sizes, np.int64), _ptr(k, np.int64),
+                         _ptr(g, np.float32), _ptr(u, np.float32),
+                         _ptr(v, np.float32), float(np.float32(m)),
+                         float(clip), _ptr(idx, np.uint32),
+                         _ptr(val, np.float32), _ptr(norm, np.float64),
+                         _ptr(scale, np.float32))
+    if rc != 0:
+        raise ValueError("bad k")
+    return idx[:K].copy(), val[:K].copy(), float(norm[0]), np.float32(scale[0])

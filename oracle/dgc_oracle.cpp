@@ -1,0 +1,252 @@
+/*
+ * dgc_oracle.cpp -- plain CPU oracle for the per-learner DGC compressor.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the two meet only through
+ * arrays handed to both by the seeded input generators.
+ *
+ * Source of the method: the review page "[Paper Review] Deep Gradient
+ * Compression: Reducing the Communication Bandwidth for Distributed Training"
+ * (nubint.ai), section "Proposed method" (sparsification with local
+ * accumulation, 32-bit nonzero / 16-bit zero-run encoding, momentum
+ * correction, local gradient clipping, momentum factor masking, warm-up),
+ * and its Abstract (99.9% of the exchange is redundant; synchronous SGD
+ * gradient exchange).  The page prints no formulas; the readings used here
+ * are:
+ *   clip:     S = sum g_i^2 in binary64; norm = sqrt(S); if clip > 0 and
+ *             norm > clip then s = (float)(clip / norm) else s = 1;
+ *             g'_i = fl32(g_i * s)
+ *   momentum: u_i = fl32(fl32(m * u_i) + g'_i);  v_i = fl32(v_i + u_i)
+ *   select:   key_i = bits(v_i) & 0x7FFFFFFF; the k entries that come first
+ *             under (key descending, index ascending)
+ *   mask:     u_i = v_i = +0.0f for every selected i, the rest untouched
+ *   encode:   per selected j ascending, gap G = j - prev - 1; floor(G/65536)
+ *             filler entries (65535, +0.0f) then (G mod 65536, v_j)
+ *   decode:   pos = -1; per entry pos += run + 1; dense[pos] += value
+ *
+ * Arithmetic: binary32 with round-to-nearest-even, no FMA contraction
+ * (built with -ffp-contract=off, no fast-math), denormals kept.
+ *
+ * Sum order of S: the definition fixes none.  Here S is summed in fixed
+ * 65536-element blocks (each block left to right in binary64, then the
+ * block sums left to right), so the result does not depend on the thread
+ * count.  Every other loop is element-wise or per tensor and so has no
+ * order to fix.
+ */
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+const int64_t kNormBlock = 65536;
+
+inline uint32_t f32_bits(float x) {
+    uint32_t b;
+    std::memcpy(&b, &x, 4);
+    return b;
+}
+
+inline uint32_t magnitude_key(float x) { return f32_bits(x) & 0x7FFFFFFFu; }
+
+}  // namespace
+
+extern "C" {
+
+/* Number of OpenMP threads the oracle will use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Local gradient clipping (DGC review, "Proposed method": clipping bounds the
+ * gradient within each node).  One norm over the learner's whole gradient.
+ * Returns 0; writes the binary64 norm and the binary32 scale.
+ */
+int orc_clip_scale(const float* g, int64_t n, double clip, double* norm_out,
+                   float* scale_out) {
+    int64_t nblocks = (n + kNormBlock - 1) / kNormBlock;
+    std::vector<double> part((size_t)std::max<int64_t>(nblocks, 1), 0.0);
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int64_t lo = b * kNormBlock, hi = std::min(n, lo + kNormBlock);
+        double acc = 0.0;
+        for (int64_t i = lo; i < hi; ++i) {
+            double x = (double)g[i];
+            acc += x * x;
+        }
+        part[(size_t)b] = acc;
+    }
+    double S = 0.0;
+    for (int64_t b = 0; b < nblocks; ++b) S += part[(size_t)b];
+    double norm = std::sqrt(S);
+    float s = 1.0f;
+    if (clip > 0.0 && norm > clip) s = (float)(clip / norm);
+    *norm_out = norm;
+    *scale_out = s;
+    return 0;
+}
+
+/*
+ * Momentum correction with local accumulation (DGC review, "Proposed
+ * method": momentum correction; small gradients accumulate locally).
+ * u <- m*u + g*s ; v <- v + u, each product and sum rounded to binary32.
+ */
+void orc_momentum(const float* g, int64_t n, float scale, float m, float* u,
+                  float* v) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float gs = g[i] * scale;
+        float mu = m * u[i];
+        float un = mu + gs;
+        u[i] = un;
+        v[i] = v[i] + un;
+    }
+}
+
+/*
+ * Exact top-k of |v| for one tensor, then momentum factor masking (DGC
+ * review, "Proposed method": only large gradients are sent; momentum factor
+ * masking; the AdaComp page's "Citations in the corpus" note that "large"
+ * means large in absolute value).
+ *
+ * T = the k-th largest key (std::nth_element); every key > T is taken, and
+ * of the keys == T the first r = k - #{key > T} in index order.  Writes the
+ * k local indices ascending and the signed values of v before masking, then
+ * sets u and v to +0.0f at those indices.  Returns the number written (k),
+ * or -1 if k is outside [0, n].
+ */
+int64_t orc_select_mask(float* u, float* v, int64_t n, int64_t k,
+                        uint32_t* idx, float* val) {
+    if (k < 0 || k > n) return -1;
+    if (k == 0) return 0;
+    std::vector<uint32_t> keys((size_t)n);
+    for (int64_t i = 0; i < n; ++i) keys[(size_t)i] = magnitude_key(v[i]);
+    std::vector<uint32_t> work(keys);
+    std::nth_element(work.begin(), work.begin() + (k - 1), work.end(),
+                     [](uint32_t a, uint32_t b) { return a > b; });
+    uint32_t T = work[(size_t)(k - 1)];
+    int64_t above = 0;
+    for (int64_t i = 0; i < n; ++i) above += keys[(size_t)i] > T;
+    int64_t ties_left = k - above;
+    int64_t out = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t key = keys[(size_t)i];
+        bool take = key > T;
+        if (!take && key == T && ties_left > 0) {
+            take = true;
+            --ties_left;
+        }
+        if (take) {
+            idx[out] = (uint32_t)i;
+            val[out] = v[i];
+            ++out;
+        }
+    }
+    for (int64_t j = 0; j < out; ++j) {
+        u[idx[j]] = 0.0f;
+        v[idx[j]] = 0.0f;
+    }
+    return out;
+}
+
+/*
+ * Zero-run encoding of one tensor's sparse gradient (DGC review, "Proposed
+ * method": 32-bit nonzeros and 16-bit run lengths of zeros).  A gap longer
+ * than a 16-bit run can say is split by filler entries (65535, +0.0f), each
+ * of which stands for 65535 zeros plus one slot holding zero.
+ * Returns the entry count E, or -1 if cap entries are not enough, or -2 if
+ * the indices are not strictly ascending.
+ */
+int64_t orc_encode(const uint32_t* idx, const float* val, int64_t k,
+                   uint16_t* runs, float* vals, int64_t cap) {
+    int64_t prev = -1, e = 0;
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t cur = (int64_t)idx[j];
+        if (cur <= prev) return -2;
+        int64_t gap = cur - prev - 1;
+        while (gap > 65535) {
+            if (e >= cap) return -1;
+            runs[e] = 65535;
+            vals[e] = 0.0f;
+            ++e;
+            gap -= 65536;
+        }
+        if (e >= cap) return -1;
+        runs[e] = (uint16_t)gap;
+        vals[e] = val[j];
+        ++e;
+        prev = cur;
+    }
+    return e;
+}
+
+/*
+ * Decode one tensor's stream and add it into dense (the aggregation of the
+ * learners' sparse gradients in synchronous SGD, DGC review Abstract).
+ * Returns 0, or -1 if the stream walks past the end of the tensor (dense is
+ * then left with the entries before the bad one added).
+ */
+int orc_decode_accumulate(const uint16_t* runs, const float* vals, int64_t E,
+                          float* dense, int64_t n) {
+    int64_t pos = -1;
+    for (int64_t e = 0; e < E; ++e) {
+        pos += (int64_t)runs[e] + 1;
+        if (pos >= n) return -1;
+        dense[pos] = dense[pos] + vals[e];
+    }
+    return 0;
+}
+
+/*
+ * Warm-up sparsity schedule (DGC review, "Proposed method": sparsity rises
+ * gradually).  k = ceil(n * num / den) in integer arithmetic, density num/den.
+ */
+int64_t orc_k_for_density(int64_t n, int64_t num, int64_t den) {
+    if (n <= 0 || num <= 0 || den <= 0) return 0;
+    return (n * num + den - 1) / den;
+}
+
+/*
+ * One learner step over T tensors laid end to end: clip over the whole
+ * gradient, momentum correction, then per tensor select + mask.  idx/val
+ * receive each tensor's k entries back to back (tensor order).  Returns 0,
+ * or -1 on a bad k.
+ */
+int orc_step(int32_t T, const int64_t* sizes, const int64_t* k, const float* g,
+             float* u, float* v, float m, double clip, uint32_t* idx,
+             float* val, double* norm_out, float* scale_out) {
+    int64_t n = 0;
+    for (int32_t t = 0; t < T; ++t) n += sizes[t];
+    orc_clip_scale(g, n, clip, norm_out, scale_out);
+    orc_momentum(g, n, *scale_out, m, u, v);
+    std::vector<int64_t> off((size_t)T + 1, 0), koff((size_t)T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        if (k[t] < 0 || k[t] > sizes[t]) return -1;
+        off[(size_t)t + 1] = off[(size_t)t] + sizes[t];
+        koff[(size_t)t + 1] = koff[(size_t)t] + k[t];
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t got = orc_select_mask(u + off[(size_t)t], v + off[(size_t)t],
+                                      sizes[t], k[t], idx + koff[(size_t)t],
+                                      val + koff[(size_t)t]);
+        if (got != k[t]) bad = 1;
+    }
+    return bad ? -1 : 0;
+}
+
+}  /* extern "C" */
