@@ -1,0 +1,254 @@
+"""Benchmark of the per-learner DGC compressor on one MI355X.
+
+One step = the whole hot path over one batch of synthetic gradients: for each
+of the W learners, dgc_compress (clip, momentum correction, exact top-k,
+compaction, masking) and dgc_encode; then the dense sum is zeroed and all W
+streams are decoded into it (dgc_decode_accumulate).  Inputs are resident in
+HBM before the timed region; each step uses the next of the workload's
+gradient steps, cycling.
+
+Prints one JSON line: value = gradient elements compressed per second
+(all learners) in G elem/s; roofline = the element-wise pass (the dominant
+kernel) timed with HIP events on its stream; cpu_baseline = the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat1b]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_flat1b_traffic.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "sparsified_gradient_compression_amd", "csrc", f)
+    for f in ("dgc_device.hpp", "kernels_compress.hpp")
+]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(n_elems):
+    """HBM bytes per launch of the element-wise pass from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if rec.get("n_elems") != n_elems:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flat1b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-chunks", type=int, default=32)
+    ap.add_argument("--fused-only", action="store_true",
+                    help="time only dgc_compress calls (for profiling runs)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, host_samples, n_chunks):
+    """The oracle as it stands on the first n_chunks tensors of learner 0,
+    one call sequence per gradient step (compress + encode + decode)."""
+    import oracle
+    sizes = np.array(wl.sizes[:n_chunks], np.int64)
+    k = np.array([oracle.k_for_density(int(s), wl.densities[0].numerator,
+                                       wl.densities[0].denominator) for s in sizes])
+    n = int(sizes.sum())
+    u = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dense = np.zeros(n, np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    koff = np.concatenate([[0], np.cumsum(k)])
+    t0 = time.perf_counter()
+    for g in host_samples:
+        idx, val, _, _ = oracle.step(sizes, k, g, u, v, wl.momentum, wl.clip)
+        dense[:] = 0
+        for t in range(len(sizes)):
+            r, vv = oracle.encode(idx[koff[t]:koff[t + 1]], val[koff[t]:koff[t + 1]])
+            oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+    dt = time.perf_counter() - t0
+    elems = n * len(host_samples)
+    return {
+        "value": round(elems / dt / 1e9, 4),
+        "unit": "G elem/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"learner 0, {len(host_samples)} steps, first {n_chunks} of "
+                   f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
+                   "momentum, exact top-k, mask, encode, decode; "
+                   f"{dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparsified_gradient_compression_amd import dgc
+    from sparsified_gradient_compression_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dgc.lib()
+    torch.cuda.set_device(0)
+    wl = W.get(args.workload)
+    T = len(wl.sizes)
+    ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
+    kmax = [max(k[t] for k in ks) for t in range(T)]
+    n = wl.n
+
+    # ---- inputs: every (learner, step) gradient resident in HBM
+    grads = {}
+    host_samples = []
+    g_host = np.empty(n, np.float32)
+    n_sample = sum(wl.sizes[:args.cpu_sample_chunks])
+    for t in range(wl.steps):
+        for w in range(wl.learners):
+            t0 = time.perf_counter()
+            W.gradient(wl, w, t, out=g_host)
+            grads[(w, t)] = torch.from_numpy(g_host).cuda()
+            if w == 0 and not args.no_cpu_baseline:
+                host_samples.append(g_host[:n_sample].copy())
+            log(f"gradient learner {w} step {t}: {time.perf_counter() - t0:.1f} s")
+    torch.cuda.synchronize()
+
+    learners = [dgc.Learner(list(wl.sizes), kmax, wl.momentum) for _ in range(wl.learners)]
+    for L in learners:
+        L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
+    dense = torch.zeros(n, dtype=torch.float32, device="cuda")
+
+    def one_step(s):
+        t = s % wl.steps
+        k = ks[t]
+        for w, L in enumerate(learners):
+            L.compress(grads[(w, t)], k, wl.clip)
+            if not args.fused_only:
+                L.encode(k)
+        if not args.fused_only:
+            dense.zero_()
+            dgc.decode_accumulate(learners[0],
+                                  [(L.runs, L.vals, L.entries) for L in learners], dense)
+
+    for s in range(args.warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+    for L in learners:
+        for tm in range(4):
+            L.kernel_time(tm)
+        assert L.status() == dgc.DGC_OK
+    log("timed region")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, args.warmup + args.steps):
+        one_step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for L in learners:
+        assert L.status() == dgc.DGC_OK
+    times = {}
+    for name, tm in (("fused", dgc.DGC_TIMER_FUSED), ("compress", dgc.DGC_TIMER_COMPRESS),
+                     ("encode", dgc.DGC_TIMER_ENCODE), ("decode", dgc.DGC_TIMER_DECODE)):
+        tot, cnt = 0.0, 0
+        for L in learners:
+            a, b = L.kernel_time(tm)
+            tot += a
+            cnt += b
+        times[name] = (tot, cnt)
+    path = [L.path_counts() for L in learners]
+
+    elems = n * wl.learners * args.steps
+    value = elems / elapsed / 1e9
+    fused_ms = times["fused"][0] / max(times["fused"][1], 1)
+    compress_ms = times["compress"][0] / max(times["compress"][1], 1)
+    fused_bytes = 20 * n  # read g, u, v; write u, v
+    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
+    k_total = sum(ks[0])
+    clip = 1 if wl.clip > 0 else 0
+    pipeline_bytes = n * (20 + 4 * clip) + 16 * k_total
+    traffic = measured_traffic(n)
+
+    out = {
+        "metric": "gradient elements compressed/sec (G elem/s) and % of MI355X peak HBM GB/s",
+        "value": round(value, 3),
+        "unit": "G elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "elements_per_learner": n,
+            "tensors": T,
+            "learners": wl.learners,
+            "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
+            "density": str(wl.densities[0]),
+            "clip": wl.clip,
+            "momentum": wl.momentum,
+            "gradient_steps": wl.steps,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_fused (clip-scale + momentum correction + accumulation + candidate output)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": fused_bytes,
+            "avg_launch_ms": round(fused_ms, 4),
+        },
+        "detail": {
+            "compress_ms_per_learner_step": round(compress_ms, 4),
+            "encode_ms_per_call": round(times["encode"][0] / max(times["encode"][1], 1), 4),
+            "decode_ms_per_call": round(times["decode"][0] / max(times["decode"][1], 1), 4),
+            "compress_pipeline_alg_GBps": round(pipeline_bytes / (compress_ms * 1e-3) / 1e9, 1),
+            "compress_pipeline_frac_of_peak": round(
+                pipeline_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "compress_G_elem_per_s": round(n / (compress_ms * 1e-3) / 1e9, 2),
+            "select_path_window_dense": path[0],
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * dgc.h -- C ABI of libdgc, the per-learner sparsifying gradient compressor
+ * of Deep Gradient Compression (DGC) on AMD Instinct MI355X (gfx950).
+ *
+ * The method is described on the review page "[Paper Review] Deep Gradient
+ * Compression: Reducing the Communication Bandwidth for Distributed
+ * Training" (nubint.ai), section "Proposed method": send only the large
+ * gradients and accumulate the small ones locally; encode the sent ones as
+ * 32-bit nonzeros with 16-bit zero run lengths; momentum correction; local
+ * gradient clipping; momentum factor masking; warm-up to a rising sparsity.
+ * Its Abstract places this in synchronous data-parallel SGD, where the
+ * learners' sparse gradients are summed.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensors of one learner's gradient lie end to end in one flat
+ *   binary32 array ("layout"): tensor t has n_t elements at offset
+ *   o_t = n_0 + ... + n_{t-1}.  Indices in outputs are local to their tensor
+ *   (uint32), so every n_t must be below 2^32.
+ * - Pointers named "device" are HIP device memory owned by the caller;
+ *   "host" pointers are ordinary host memory read during the call only.
+ *   The library never allocates device memory; it mallocs only the small
+ *   host-side dgc_state, freed by dgc_destroy_state.
+ * - Calls enqueue work on the given stream and return without waiting for
+ *   it (except dgc_get_status, dgc_get_path_counts and dgc_init_state, which
+ *   synchronise).  Results are valid once the stream reaches that point.
+ * - A dgc_state belongs to one learner (its u, v and workspace).  Calls on
+ *   one state must not run concurrently on two streams.
+ * - Return codes: DGC_OK (0) or a negative DGC_E* code.  Argument errors are
+ *   detected on the host before anything is enqueued.  Errors found by the
+ *   kernels (a corrupt stream) are latched in the workspace and reported by
+ *   dgc_get_status.
+ * - Arithmetic is IEEE binary32 with round-to-nearest-even, no FMA
+ *   contraction and denormals kept, so results are reproducible bit for
+ *   bit; the only binary64 value is the clipping norm.
+ */
+#ifndef DGC_H_
+#define DGC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DGC_OK 0
+#define DGC_EINVAL (-1)    /* bad argument: null pointer, size, k, alignment */
+#define DGC_ECAPACITY (-2) /* workspace or output buffer too small */
+#define DGC_EHIP (-3)      /* a HIP runtime call or kernel launch failed */
+#define DGC_ECORRUPT (-4)  /* a decoded stream ran past its tensor's end */
+
+/* Options for dgc_set_option. */
+#define DGC_OPT_SELECT_PATH 1   /* value 0: automatic (default); 1: always the
+                                   dense exact path (no sample window) */
+#define DGC_OPT_KERNEL_TIMING 2 /* value 1: bracket the work of each call with
+                                   HIP events on the call's stream (read with
+                                   dgc_get_kernel_time); 0: off (default) */
+
+/* Timers for dgc_get_kernel_time. */
+#define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress */
+#define DGC_TIMER_COMPRESS 1  /* all of dgc_compress */
+#define DGC_TIMER_ENCODE 2    /* all of dgc_encode */
+#define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate */
+
+typedef struct dgc_state dgc_state;
+
+/*
+ * Workspace size for a layout.
+ *   n_tensors  number of tensors T >= 1
+ *   sizes      host int64[T], element counts n_t, 0 <= n_t < 2^32
+ *   k_max      host int64[T], the largest k_t that dgc_compress will be
+ *              given for tensor t (0 <= k_max[t] <= n_t); it sizes the
+ *              candidate buffers and the encoded stream capacity
+ *   bytes      out: bytes of device workspace dgc_init_state needs
+ * Returns DGC_OK or DGC_EINVAL.
+ */
+int dgc_workspace_bytes(int32_t n_tensors, const int64_t* sizes,
+                        const int64_t* k_max, size_t* bytes);
+
+/*
+ * Create the state of one learner.
+ *   st         out: new state (free with dgc_destroy_state)
+ *   momentum   momentum constant m of the momentum correction (e.g. 0.9f)
+ *   u, v       device float[n]: momentum buffer u and accumulated gradient
+ *              v, n = sum of sizes, 16-byte aligned; zeroed here on stream
+ *   workspace  device memory of at least dgc_workspace_bytes bytes,
+ *              256-byte aligned, owned by the caller for the state's life
+ *   stream     stream for the zeroing and the copy of layout tables; the
+ *              call waits for it before returning
+ * The state keeps the pointers; the caller keeps the memory alive.
+ * Returns DGC_OK, DGC_EINVAL, DGC_ECAPACITY (workspace too small) or
+ * DGC_EHIP.
+ */
+int dgc_init_state(dgc_state** st, int32_t n_tensors, const int64_t* sizes,
+                   const int64_t* k_max, float momentum, float* u, float* v,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * One compression step of the learner (DGC review, "Proposed method":
+ * local gradient clipping, momentum correction, sparsification with local
+ * accumulation, momentum factor masking):
+ *   1. if clip > 0: S = sum g_i^2 over the whole gradient (binary64),
+ *      norm = sqrt(S), s = (float)(clip / norm) if norm > clip else 1;
+ *      if clip <= 0: s = 1 and no norm is computed
+ *   2. u_i = fl(fl(m * u_i) + fl(g_i * s));  v_i = fl(v_i + u_i)
+ *   3. per tensor: the k_t entries first under (|v_i| descending, index
+ *      ascending), with |v_i| compared as the bit pattern of v_i with the
+ *      sign cleared (so +0 == -0; NaN payloads rank above infinity)
+ *   4. those entries are written out and u_i = v_i = +0.0f at them; every
+ *      other u_i, v_i keeps its value (the residual)
+ * Arguments:
+ *   g          device const float[n], 16-byte aligned: this step's gradient
+ *   k          host int64[T], 0 <= k[t] <= k_max[t]  (warm-up: any k per step)
+ *   clip       clipping threshold; <= 0 turns clipping off
+ *   out_idx    device uint32[sum k], 4-byte aligned: tensor t's k_t local
+ *              indices, ascending, at offset K_t = k_0 + ... + k_{t-1}
+ *   out_val    device float[sum k]: the matching values of v (signed, taken
+ *              before masking), same offsets
+ *   out_norm   device double[1]: the norm, or -1.0 when clipping is off
+ *   out_scale  device float[1]: the scale s applied to g
+ * Exact for every k and input; the path taken (sample window or dense
+ * histogram) changes only the speed.  Returns DGC_OK, DGC_EINVAL or
+ * DGC_EHIP.
+ */
+int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
+                 uint32_t* out_idx, float* out_val, double* out_norm,
+                 float* out_scale, hipStream_t stream);
+
+/*
+ * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is
+ * the first entry slot of tensor t; tensor t may use up to
+ * cap_offsets[t+1] - cap_offsets[t] = k_max[t] + floor(n_t / 65536) entries,
+ * enough for any selection of at most k_max[t] indices.
+ */
+int dgc_stream_capacity(const dgc_state* st, int64_t* cap_offsets);
+
+/*
+ * Zero-run encoding (DGC review, "Proposed method": 32-bit nonzeros and
+ * 16-bit run lengths of zeros).  Per tensor, per selected index j in
+ * ascending order with gap G = j - prev - 1 (prev = -1 at the start):
+ * floor(G / 65536) filler entries (run 65535, value +0.0f), then the entry
+ * (G mod 65536, value).  Zeros after the last selected index are not
+ * encoded.  Each entry counts as 6 bytes (16-bit run + 32-bit value).
+ *   k          host int64[T], as given to dgc_compress
+ *   idx, val   device: dgc_compress's outputs for those k
+ *   runs       device uint16[cap_offsets[T]]: runs, tensor t's at
+ *              cap_offsets[t] (structure of arrays, little endian)
+ *   vals       device float[cap_offsets[T]]: values, same slots
+ *   entries    device int64[T]: out, entry count E_t per tensor
+ * idx must be strictly ascending within each tensor (as dgc_compress
+ * writes it).  Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_encode(const dgc_state* st, const int64_t* k, const uint32_t* idx,
+               const float* val, uint16_t* runs, float* vals, int64_t* entries,
+               hipStream_t stream);
+
+/*
+ * Decode several learners' streams and add them into one dense sum (the
+ * gradient exchange of synchronous SGD, DGC review Abstract):
+ * for w = 0 .. n_learners-1 in order, per tensor, pos = -1 and for each
+ * entry pos += run + 1; dense[o_t + pos] = fl(dense[o_t + pos] + value).
+ * Fillers are added too (+0.0f).  The sum is not averaged.
+ *   runs, vals, entries  host arrays of n_learners device pointers, each
+ *                        stream laid out as dgc_encode writes it for this
+ *                        state's layout
+ *   dense      device float[n]: accumulated in place (zero it first for a
+ *              fresh sum)
+ * A stream whose positions pass its tensor's end, or whose E_t is negative
+ * or above capacity, adds nothing past that point and latches
+ * DGC_ECORRUPT for dgc_get_status.  No float atomics are used: the result
+ * is the same bits every run.  Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_decode_accumulate(const dgc_state* st, int32_t n_learners,
+                          const uint16_t* const* runs,
+                          const float* const* vals,
+                          const int64_t* const* entries, float* dense,
+                          hipStream_t stream);
+
+/*
+ * Wait for the state's last stream and return the latched device-side
+ * error (DGC_OK or DGC_ECORRUPT), clearing it.  Returns DGC_EHIP if the
+ * wait fails.
+ */
+int dgc_get_status(dgc_state* st);
+
+/*
+ * How the last dgc_compress selected: per tensor it used either the sample
+ * window (candidates gathered during the element-wise pass) or the dense
+ * exact path.  Waits for the stream.  Either count may be NULL.
+ */
+int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense);
+
+/* Set an option (DGC_OPT_*).  Returns DGC_OK or DGC_EINVAL. */
+int dgc_set_option(dgc_state* st, int32_t option, int64_t value);
+
+/*
+ * With DGC_OPT_KERNEL_TIMING on: total milliseconds and number of the
+ * intervals of `timer` (DGC_TIMER_*) recorded since the last read, measured
+ * between HIP events on the stream each call ran on.  Waits for those
+ * events; resets the timer.  Either output may be NULL.
+ */
+int dgc_get_kernel_time(dgc_state* st, int32_t timer, double* total_ms,
+                        int64_t* count);
+
+/* Free the host-side state.  Device memory stays the caller's. */
+void dgc_destroy_state(dgc_state* st);
+
+/* Static text for a return code. */
+const char* dgc_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGC_H_ */

@@ -1,0 +1,650 @@
+// dgc_api.hip -- host side of libdgc: argument checks, workspace layout and
+// the launch sequence of each entry point.  See include/dgc.h for the
+// contract of every function.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dgc.h"
+#include "dgc_device.hpp"
+#include "kernels_codec.hpp"
+#include "kernels_compress.hpp"
+
+using namespace dgc;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Host-side layout of one state and the carving of its workspace.
+struct Plan {
+    int32_t T = 0;
+    std::vector<int64_t> sizes, kmax;
+    // tables uploaded at init (int64): o, pbase, tbase, abase, sbase,
+    // slines, ebase, etbase -- each T+1 long (slines padded)
+    std::vector<int64_t> o, pbase, tbase, abase, sbase, slines, ebase, etbase;
+    std::vector<uint32_t> pmap, smap, emap;
+    int64_t n = 0, P = 0, TT = 0, A = 0, S = 0, E = 0, ET = 0, NB = 0;
+    int64_t tiles = 0;  // entries of each per-tile array
+    // workspace byte offsets
+    size_t off_tab = 0, off_pmap = 0, off_smap = 0, off_emap = 0, off_k = 0,
+           off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
+           off_runb = 0, off_runc = 0, off_ord = 0, off_atiles = 0,
+           off_aoff = 0, off_amap = 0, off_arena = 0, off_olist = 0,
+           off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
+           total = 0;
+};
+
+// Candidate arena capacity of one tensor: every element for small tensors,
+// else room for 8 k_max + 16384 candidates (the sample window aims at about
+// 2-4 k; more candidates than this send the tensor to the dense path).
+int64_t arena_cap(int64_t n, int64_t kmax) {
+    if (n <= kSmallN) return n;
+    return std::min<int64_t>(n, 8 * kmax + 16384);
+}
+
+int64_t sample_lines(int64_t n) {
+    if (n <= kSmallN) return 0;
+    int64_t lines = cdiv(n, kLine);
+    return std::min<int64_t>(lines, std::max<int64_t>(kMinSampleLines, lines / 256));
+}
+
+int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
+    if (T <= 0 || !sizes || !kmax) return DGC_EINVAL;
+    p.T = T;
+    p.sizes.assign(sizes, sizes + T);
+    p.kmax.assign(kmax, kmax + T);
+    p.o.assign(T + 1, 0);
+    p.pbase.assign(T + 1, 0);
+    p.tbase.assign(T + 1, 0);
+    p.abase.assign(T + 1, 0);
+    p.sbase.assign(T + 1, 0);
+    p.slines.assign(T + 1, 0);
+    p.ebase.assign(T + 1, 0);
+    p.etbase.assign(T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t n = sizes[t], km = kmax[t];
+        if (n < 0 || n >= (int64_t(1) << 32) || km < 0 || km > n) return DGC_EINVAL;
+        p.o[t + 1] = p.o[t] + n;
+        p.pbase[t + 1] = p.pbase[t] + cdiv(n, kPiece);
+        p.tbase[t + 1] = p.tbase[t] + cdiv(n, kTile);
+        p.abase[t + 1] = p.abase[t] + arena_cap(n, km);
+        p.slines[t] = sample_lines(n);
+        p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
+        p.ebase[t + 1] = p.ebase[t] + km + n / 65536;
+        p.etbase[t + 1] = p.etbase[t] + cdiv(km + n / 65536, kTile);
+    }
+    p.n = p.o[T];
+    p.P = p.pbase[T];
+    p.TT = p.tbase[T];
+    p.A = p.abase[T];
+    p.S = p.sbase[T];
+    p.E = p.ebase[T];
+    p.ET = p.etbase[T];
+    p.NB = cdiv(p.n, kNormChunk);
+    if (p.P >= (int64_t(1) << 32) || p.TT >= (int64_t(1) << 32)) return DGC_EINVAL;
+    // tiles over k never exceed tiles over n, so TT also bounds encode tiles
+    p.tiles = std::max<int64_t>(std::max<int64_t>(p.TT, p.ET), 1);
+    p.pmap.resize(size_t(p.P));
+    p.smap.resize(size_t(p.S));
+    p.emap.resize(size_t(p.ET));
+    for (int32_t t = 0; t < T; ++t) {
+        for (int64_t i = p.pbase[t]; i < p.pbase[t + 1]; ++i) p.pmap[size_t(i)] = uint32_t(t);
+        for (int64_t i = p.sbase[t]; i < p.sbase[t + 1]; ++i) p.smap[size_t(i)] = uint32_t(t);
+        for (int64_t i = p.etbase[t]; i < p.etbase[t + 1]; ++i) p.emap[size_t(i)] = uint32_t(t);
+    }
+    // carve
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + std::max<size_t>(bytes, 1));
+        return at;
+    };
+    const size_t T1 = size_t(T) + 1;
+    p.off_tab = take(8 * T1 * sizeof(int64_t));
+    p.off_pmap = take(size_t(p.P) * 4);
+    p.off_smap = take(size_t(p.S) * 4);
+    p.off_emap = take(size_t(p.ET) * 4);
+    p.off_k = take((3 * T1) * sizeof(int64_t));
+    p.off_kmap = take(size_t(p.TT) * 4);
+    p.off_ts = take(size_t(T) * sizeof(TensorState));
+    p.off_sc = take(sizeof(Scalars));
+    p.off_hist = take(size_t(T) * kHistBins * 4);
+    p.off_shist = take(size_t(T) * kHistBins * 4);
+    p.off_runb = take(size_t(p.P) * 4);
+    p.off_runc = take(size_t(p.P) * 4);
+    p.off_ord = take(size_t(p.P) * 4);
+    p.off_atiles = take(size_t(T) * 4);
+    p.off_aoff = take(T1 * 4);
+    p.off_amap = take(size_t(p.TT) * 4);
+    p.off_arena = take(size_t(p.A) * 8);
+    p.off_olist = take(size_t(p.A) * 8);
+    p.off_ta = take(size_t(p.tiles) * 4);
+    p.off_tb = take(size_t(p.tiles) * 4);
+    p.off_tc = take(size_t(p.tiles) * 4);
+    p.off_t64 = take(size_t(p.tiles) * 8);
+    p.off_part = take(size_t(std::max<int64_t>(p.NB, 1)) * 8);
+    p.total = off;
+    return DGC_OK;
+}
+
+}  // namespace
+
+// A ring of HIP event pairs bracketing one kind of work on the caller's
+// stream.  A slot is read back (host wait) before it is reused.
+struct Timer {
+    static constexpr int kRing = 64;
+    hipEvent_t start[kRing] = {};
+    hipEvent_t stop[kRing] = {};
+    bool busy[kRing] = {};
+    bool created = false;
+    int next = 0;
+    int open = -1;
+    double acc_ms = 0.0;
+    int64_t count = 0;
+};
+
+struct dgc_state {
+    Plan plan;
+    bool timing = false;
+    Timer timers[4];
+    float m = 0.9f;
+    float* u = nullptr;
+    float* v = nullptr;
+    char* ws = nullptr;
+    int num_cus = 256;
+    int select_path = 0;
+    int fused_blocks = 0;  // 0: automatic
+    hipStream_t last_stream = nullptr;
+    std::vector<int64_t> k_last;  // k of the last upload
+    std::vector<int64_t> k_tables;  // k, koff, ktbase (host copy)
+    std::vector<uint32_t> kmap_host;
+    bool k_valid = false;
+    int64_t KT = 0;  // tiles over k of the last upload
+    // device views
+    DevLayout L{};
+    DevK K{};
+    TensorState* ts = nullptr;
+    Scalars* sc = nullptr;
+    uint32_t *hist = nullptr, *shist = nullptr, *run_base = nullptr,
+             *run_cnt = nullptr, *ord_off = nullptr, *atiles = nullptr,
+             *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
+             *tc = nullptr;
+    uint2 *arena = nullptr, *olist = nullptr;
+    uint64_t* t64 = nullptr;
+    double* partial = nullptr;
+};
+
+namespace {
+
+int timer_collect(Timer& tm, int slot) {
+    if (!tm.busy[slot]) return DGC_OK;
+    if (hipEventSynchronize(tm.stop[slot]) != hipSuccess) return DGC_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, tm.start[slot], tm.stop[slot]) != hipSuccess)
+        return DGC_EHIP;
+    tm.acc_ms += ms;
+    tm.count += 1;
+    tm.busy[slot] = false;
+    return DGC_OK;
+}
+
+int timer_begin(dgc_state* st, int which, hipStream_t s) {
+    if (!st->timing) return DGC_OK;
+    Timer& tm = st->timers[which];
+    if (!tm.created) {
+        for (int i = 0; i < Timer::kRing; ++i)
+            if (hipEventCreate(&tm.start[i]) != hipSuccess ||
+                hipEventCreate(&tm.stop[i]) != hipSuccess)
+                return DGC_EHIP;
+        tm.created = true;
+    }
+    int slot = tm.next;
+    if (timer_collect(tm, slot) != DGC_OK) return DGC_EHIP;
+    if (hipEventRecord(tm.start[slot], s) != hipSuccess) return DGC_EHIP;
+    tm.open = slot;
+    return DGC_OK;
+}
+
+int timer_end(dgc_state* st, int which, hipStream_t s) {
+    if (!st->timing) return DGC_OK;
+    Timer& tm = st->timers[which];
+    if (tm.open < 0) return DGC_OK;
+    if (hipEventRecord(tm.stop[tm.open], s) != hipSuccess) return DGC_EHIP;
+    tm.busy[tm.open] = true;
+    tm.next = (tm.open + 1) % Timer::kRing;
+    tm.open = -1;
+    return DGC_OK;
+}
+
+void timers_destroy(dgc_state* st) {
+    for (Timer& tm : st->timers) {
+        if (!tm.created) continue;
+        for (int i = 0; i < Timer::kRing; ++i) {
+            (void)hipEventDestroy(tm.start[i]);
+            (void)hipEventDestroy(tm.stop[i]);
+        }
+        tm.created = false;
+    }
+}
+
+#define DGC_TRY(expr)                      \
+    do {                                   \
+        int rc_ = (expr);                  \
+        if (rc_ != DGC_OK) return rc_;     \
+    } while (0)
+
+#define DGC_LAUNCH_CHECK()                                   \
+    do {                                                     \
+        if (hipGetLastError() != hipSuccess) return DGC_EHIP; \
+    } while (0)
+
+bool aligned(const void* p, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+int grid_for(int64_t work, int64_t cap) {
+    return int(std::max<int64_t>(1, std::min<int64_t>(work, cap)));
+}
+
+// Upload k, its output offsets and its tile map when they change.
+int upload_k(dgc_state* st, const int64_t* k, hipStream_t s) {
+    const Plan& p = st->plan;
+    const int32_t T = p.T;
+    if (st->k_valid && std::memcmp(st->k_last.data(), k, size_t(T) * 8) == 0)
+        return DGC_OK;
+    st->k_last.assign(k, k + T);
+    std::vector<int64_t>& tb = st->k_tables;
+    tb.assign(3 * (size_t(T) + 1), 0);
+    int64_t* kk = tb.data();
+    int64_t* koff = kk + (T + 1);
+    int64_t* ktb = koff + (T + 1);
+    for (int32_t t = 0; t < T; ++t) {
+        kk[t] = k[t];
+        koff[t + 1] = koff[t] + k[t];
+        ktb[t + 1] = ktb[t] + cdiv(k[t], kTile);
+    }
+    st->KT = ktb[T];
+    st->kmap_host.resize(size_t(std::max<int64_t>(st->KT, 1)));
+    for (int32_t t = 0; t < T; ++t)
+        for (int64_t i = ktb[t]; i < ktb[t + 1]; ++i) st->kmap_host[size_t(i)] = uint32_t(t);
+    // Pageable-source copies are staged by the runtime before returning,
+    // so the host vectors may change on the next call.
+    if (hipMemcpyAsync(st->ws + p.off_k, tb.data(), tb.size() * 8,
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+        return DGC_EHIP;
+    if (st->KT > 0 &&
+        hipMemcpyAsync(st->ws + p.off_kmap, st->kmap_host.data(),
+                       size_t(st->KT) * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+        return DGC_EHIP;
+    st->k_valid = true;
+    return DGC_OK;
+}
+
+int check_k(const dgc_state* st, const int64_t* k) {
+    if (!k) return DGC_EINVAL;
+    for (int32_t t = 0; t < st->plan.T; ++t)
+        if (k[t] < 0 || k[t] > st->plan.kmax[size_t(t)]) return DGC_EINVAL;
+    return DGC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dgc_workspace_bytes(int32_t n_tensors, const int64_t* sizes,
+                        const int64_t* k_max, size_t* bytes) {
+    if (!bytes) return DGC_EINVAL;
+    Plan p;
+    int rc = make_plan(n_tensors, sizes, k_max, p);
+    if (rc != DGC_OK) return rc;
+    *bytes = p.total;
+    return DGC_OK;
+}
+
+int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
+                   const int64_t* k_max, float momentum, float* u, float* v,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    if (!out) return DGC_EINVAL;
+    *out = nullptr;
+    dgc_state* st = new (std::nothrow) dgc_state;
+    if (!st) return DGC_EINVAL;
+    int rc = make_plan(n_tensors, sizes, k_max, st->plan);
+    const Plan& p = st->plan;
+    if (rc == DGC_OK && (!workspace || !aligned(workspace, kAlign))) rc = DGC_EINVAL;
+    if (rc == DGC_OK && p.n > 0 && (!u || !v || !aligned(u, 16) || !aligned(v, 16)))
+        rc = DGC_EINVAL;
+    if (rc == DGC_OK && workspace_bytes < p.total) rc = DGC_ECAPACITY;
+    if (!std::isfinite(momentum)) rc = DGC_EINVAL;
+    if (rc != DGC_OK) {
+        delete st;
+        return rc;
+    }
+    st->m = momentum;
+    st->u = u;
+    st->v = v;
+    st->ws = static_cast<char*>(workspace);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&st->num_cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess) {
+        delete st;
+        return DGC_EHIP;
+    }
+    char* ws = st->ws;
+    const int32_t T = p.T;
+    const size_t T1 = size_t(T) + 1;
+    // layout tables
+    std::vector<int64_t> tab(8 * T1, 0);
+    const std::vector<int64_t>* src[8] = {&p.o, &p.pbase, &p.tbase, &p.abase,
+                                          &p.sbase, &p.slines, &p.ebase, &p.etbase};
+    for (int i = 0; i < 8; ++i)
+        std::copy(src[i]->begin(), src[i]->end(), tab.begin() + i * T1);
+    int64_t* dtab = reinterpret_cast<int64_t*>(ws + p.off_tab);
+    st->L.T = T;
+    st->L.o = dtab;
+    st->L.pbase = dtab + T1;
+    st->L.tbase = dtab + 2 * T1;
+    st->L.abase = dtab + 3 * T1;
+    st->L.sbase = dtab + 4 * T1;
+    st->L.slines = dtab + 5 * T1;
+    st->L.ebase = dtab + 6 * T1;
+    st->L.etbase = dtab + 7 * T1;
+    st->L.pmap = reinterpret_cast<uint32_t*>(ws + p.off_pmap);
+    st->L.smap = reinterpret_cast<uint32_t*>(ws + p.off_smap);
+    st->L.emap = reinterpret_cast<uint32_t*>(ws + p.off_emap);
+    int64_t* dk = reinterpret_cast<int64_t*>(ws + p.off_k);
+    st->K.k = dk;
+    st->K.koff = dk + T1;
+    st->K.ktbase = dk + 2 * T1;
+    st->K.kmap = reinterpret_cast<uint32_t*>(ws + p.off_kmap);
+    st->ts = reinterpret_cast<TensorState*>(ws + p.off_ts);
+    st->sc = reinterpret_cast<Scalars*>(ws + p.off_sc);
+    st->hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
+    st->shist = reinterpret_cast<uint32_t*>(ws + p.off_shist);
+    st->run_base = reinterpret_cast<uint32_t*>(ws + p.off_runb);
+    st->run_cnt = reinterpret_cast<uint32_t*>(ws + p.off_runc);
+    st->ord_off = reinterpret_cast<uint32_t*>(ws + p.off_ord);
+    st->atiles = reinterpret_cast<uint32_t*>(ws + p.off_atiles);
+    st->aoff = reinterpret_cast<uint32_t*>(ws + p.off_aoff);
+    st->amap = reinterpret_cast<uint32_t*>(ws + p.off_amap);
+    st->arena = reinterpret_cast<uint2*>(ws + p.off_arena);
+    st->olist = reinterpret_cast<uint2*>(ws + p.off_olist);
+    st->ta = reinterpret_cast<uint32_t*>(ws + p.off_ta);
+    st->tb = reinterpret_cast<uint32_t*>(ws + p.off_tb);
+    st->tc = reinterpret_cast<uint32_t*>(ws + p.off_tc);
+    st->t64 = reinterpret_cast<uint64_t*>(ws + p.off_t64);
+    st->partial = reinterpret_cast<double*>(ws + p.off_part);
+
+    bool ok = true;
+    ok = ok && hipMemcpyAsync(dtab, tab.data(), tab.size() * 8,
+                              hipMemcpyHostToDevice, stream) == hipSuccess;
+    if (p.P) ok = ok && hipMemcpyAsync(ws + p.off_pmap, p.pmap.data(), size_t(p.P) * 4,
+                                       hipMemcpyHostToDevice, stream) == hipSuccess;
+    if (p.S) ok = ok && hipMemcpyAsync(ws + p.off_smap, p.smap.data(), size_t(p.S) * 4,
+                                       hipMemcpyHostToDevice, stream) == hipSuccess;
+    if (p.ET) ok = ok && hipMemcpyAsync(ws + p.off_emap, p.emap.data(), size_t(p.ET) * 4,
+                                        hipMemcpyHostToDevice, stream) == hipSuccess;
+    // zero the scratch after the tables (histograms must start at zero) and
+    // the state vectors u and v
+    if (ok) {
+        size_t zero_from = p.off_ts;
+        int64_t words = int64_t((p.total - zero_from) / 4);
+        k_fill_u32<<<grid_for(cdiv(words, kBlock), 4096), kBlock, 0, stream>>>(
+            reinterpret_cast<uint32_t*>(ws + zero_from), words, 0u);
+        if (p.n) {
+            k_fill_u32<<<grid_for(cdiv(p.n, kBlock), 8192), kBlock, 0, stream>>>(
+                reinterpret_cast<uint32_t*>(u), p.n, 0u);
+            k_fill_u32<<<grid_for(cdiv(p.n, kBlock), 8192), kBlock, 0, stream>>>(
+                reinterpret_cast<uint32_t*>(v), p.n, 0u);
+        }
+        ok = hipGetLastError() == hipSuccess;
+    }
+    ok = ok && hipStreamSynchronize(stream) == hipSuccess;
+    if (!ok) {
+        delete st;
+        return DGC_EHIP;
+    }
+    st->last_stream = stream;
+    *out = st;
+    return DGC_OK;
+}
+
+int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
+                 uint32_t* out_idx, float* out_val, double* out_norm,
+                 float* out_scale, hipStream_t stream) {
+    if (!st) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (p.n > 0 && (!g || !aligned(g, 16))) return DGC_EINVAL;
+    if (K > 0 && (!out_idx || !out_val || !aligned(out_idx, 4) || !aligned(out_val, 4)))
+        return DGC_EINVAL;
+    if (std::isnan(clip)) return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const int T = p.T;
+    const bool clip_on = clip > 0.0;
+    const int pg = st->num_cus * 8;  // persistent grids
+
+    DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    k_prep<<<grid_for(cdiv(T, kBlock), 64), kBlock, 0, stream>>>(st->ts, T, st->sc,
+                                                                   clip_on ? 1 : 0);
+    if (clip_on) {
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
+    } else {
+        k_copy_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
+    }
+    DGC_LAUNCH_CHECK();
+    const int force_dense = st->select_path == 1;
+    if (p.S > 0 && !force_dense) {
+        k_sample<<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
+                                                  st->m, st->shist);
+    }
+    k_window<<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts, force_dense);
+    DGC_LAUNCH_CHECK();
+    if (p.P > 0) {
+        int fb = st->fused_blocks > 0 ? st->fused_blocks : st->num_cus * 8;
+        DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+        k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
+            g, st->u, st->v, st->L, st->ts, st->sc, st->m, st->arena, st->run_base,
+            st->run_cnt, p.P);
+        DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+    }
+    k_piece_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->run_cnt,
+                                           st->ord_off, st->atiles);
+    k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
+    k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
+    DGC_LAUNCH_CHECK();
+    if (K > 0) {
+        const int hg = grid_for(p.TT, pg);
+        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
+                                             st->run_base, st->ord_off, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
+                                             st->run_base, st->ord_off, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
+                                             st->run_base, st->ord_off, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        DGC_LAUNCH_CHECK();
+        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist,
+                                                st->amap, st->aoff, st->ta);
+        k_emit_scan<<<T, kBlock, 0, stream>>>(T, st->aoff, st->ta, st->tb, st->tc);
+        k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
+                                                st->olist, st->amap, st->aoff, st->tb,
+                                                st->tc, out_idx, out_val, st->sc);
+        DGC_LAUNCH_CHECK();
+    }
+    DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
+int dgc_stream_capacity(const dgc_state* st, int64_t* cap_offsets) {
+    if (!st || !cap_offsets) return DGC_EINVAL;
+    std::copy(st->plan.ebase.begin(), st->plan.ebase.end(), cap_offsets);
+    return DGC_OK;
+}
+
+int dgc_encode(const dgc_state* cst, const int64_t* k, const uint32_t* idx,
+               const float* val, uint16_t* runs, float* vals, int64_t* entries,
+               hipStream_t stream) {
+    dgc_state* st = const_cast<dgc_state*>(cst);
+    if (!st) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (!entries || !aligned(entries, 8)) return DGC_EINVAL;
+    if (K > 0 && (!idx || !val || !runs || !vals || !aligned(idx, 4) ||
+                  !aligned(val, 4) || !aligned(runs, 2) || !aligned(vals, 4)))
+        return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const int T = p.T;
+    const int pg = st->num_cus * 8;
+    DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
+    if (st->KT > 0)
+        k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, idx, st->ta,
+                                                                 st->sc, st->KT);
+    k_enc_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ta, st->tb, entries);
+    if (st->KT > 0)
+        k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, idx, val,
+                                                                 st->tb, runs, vals, st->KT);
+    DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_ENCODE, stream));
+    return DGC_OK;
+}
+
+int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
+                          const uint16_t* const* runs, const float* const* vals,
+                          const int64_t* const* entries, float* dense,
+                          hipStream_t stream) {
+    dgc_state* st = const_cast<dgc_state*>(cst);
+    if (!st || n_learners < 0) return DGC_EINVAL;
+    if (n_learners == 0) return DGC_OK;
+    const Plan& p = st->plan;
+    if (!runs || !vals || !entries) return DGC_EINVAL;
+    if (p.n > 0 && (!dense || !aligned(dense, 4))) return DGC_EINVAL;
+    for (int32_t w = 0; w < n_learners; ++w) {
+        if (!entries[w] || !aligned(entries[w], 8)) return DGC_EINVAL;
+        if (p.E > 0 && (!runs[w] || !vals[w] || !aligned(runs[w], 2) ||
+                        !aligned(vals[w], 4)))
+            return DGC_EINVAL;
+    }
+    st->last_stream = stream;
+    if (p.ET == 0) return DGC_OK;
+    const int T = p.T;
+    const int pg = grid_for(p.ET, st->num_cus * 8);
+    DGC_TRY(timer_begin(st, DGC_TIMER_DECODE, stream));
+    for (int32_t w = 0; w < n_learners; ++w) {
+        k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, runs[w], entries[w], st->ta,
+                                               st->sc, p.ET);
+        k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, st->ta, st->t64);
+        k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, runs[w], vals[w], entries[w],
+                                               st->t64, dense, st->sc, p.ET);
+        DGC_LAUNCH_CHECK();
+    }
+    DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
+    return DGC_OK;
+}
+
+int dgc_get_status(dgc_state* st) {
+    if (!st) return DGC_EINVAL;
+    if (hipStreamSynchronize(st->last_stream) != hipSuccess) return DGC_EHIP;
+    uint32_t status = 0;
+    if (hipMemcpy(&status, &st->sc->status, 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return DGC_EHIP;
+    if (status) {
+        uint32_t zero = 0;
+        if (hipMemcpy(&st->sc->status, &zero, 4, hipMemcpyHostToDevice) != hipSuccess)
+            return DGC_EHIP;
+    }
+    if (status == kErrCorrupt) return DGC_ECORRUPT;
+    if (status) return DGC_EHIP;
+    return DGC_OK;
+}
+
+int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense) {
+    if (!st) return DGC_EINVAL;
+    if (hipStreamSynchronize(st->last_stream) != hipSuccess) return DGC_EHIP;
+    std::vector<TensorState> h(size_t(st->plan.T));
+    if (hipMemcpy(h.data(), st->ts, h.size() * sizeof(TensorState),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return DGC_EHIP;
+    int64_t nw = 0, nd = 0;
+    for (const TensorState& s : h) {
+        nw += s.mode == kModeList;
+        nd += s.mode == kModeDense;
+    }
+    if (n_window) *n_window = nw;
+    if (n_dense) *n_dense = nd;
+    return DGC_OK;
+}
+
+int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
+    if (!st) return DGC_EINVAL;
+    if (option == DGC_OPT_SELECT_PATH) {
+        if (value != 0 && value != 1) return DGC_EINVAL;
+        st->select_path = int(value);
+        return DGC_OK;
+    }
+    if (option == DGC_OPT_KERNEL_TIMING) {
+        if (value != 0 && value != 1) return DGC_EINVAL;
+        st->timing = value == 1;
+        return DGC_OK;
+    }
+    return DGC_EINVAL;
+}
+
+int dgc_get_kernel_time(dgc_state* st, int32_t timer, double* total_ms,
+                        int64_t* count) {
+    if (!st || timer < 0 || timer > 3) return DGC_EINVAL;
+    Timer& tm = st->timers[timer];
+    for (int i = 0; i < Timer::kRing; ++i)
+        if (timer_collect(tm, i) != DGC_OK) return DGC_EHIP;
+    if (total_ms) *total_ms = tm.acc_ms;
+    if (count) *count = tm.count;
+    tm.acc_ms = 0.0;
+    tm.count = 0;
+    return DGC_OK;
+}
+
+void dgc_destroy_state(dgc_state* st) {
+    if (!st) return;
+    timers_destroy(st);
+    delete st;
+}
+
+const char* dgc_error_string(int code) {
+    switch (code) {
+        case DGC_OK: return "ok";
+        case DGC_EINVAL: return "invalid argument";
+        case DGC_ECAPACITY: return "workspace or buffer too small";
+        case DGC_EHIP: return "HIP runtime error";
+        case DGC_ECORRUPT: return "corrupt stream";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+// dgc_device.hpp -- constants, device-visible layout structs and wave/block
+// helpers shared by the libdgc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgc {
+
+// ---------------------------------------------------------------- sizes
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;                 // threads per workgroup (4 waves)
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Element-wise pass: one wave owns one "piece" of up to 1024 consecutive
+// elements of one tensor (64 lanes x 4 float4).  Candidates of a piece are
+// written as one index-ordered run.
+constexpr int kPieceShift = 10;
+constexpr int64_t kPiece = int64_t(1) << kPieceShift;
+
+// Generic tiles for histogram / emit / encode / decode passes: 4096 items
+// per workgroup visit (16 per thread).
+constexpr int kTileShift = 12;
+constexpr int64_t kTile = int64_t(1) << kTileShift;
+constexpr int kPerThread = int(kTile / kBlock);  // 16
+
+// Radix select on the 31-bit magnitude key: digits of 11, 10, 10 bits.
+constexpr int kBins0 = 2048;
+constexpr int kHistBins = 2048;  // histogram row per tensor (largest digit)
+
+// Sample window: 32-element lines; tensors above kSmallN elements sample
+// max(kMinSampleLines, lines/256) lines; smaller tensors take every element
+// as a candidate.
+constexpr int64_t kLine = 32;
+constexpr int64_t kSmallN = 65536;
+constexpr int64_t kMinSampleLines = 512;
+constexpr int64_t kLinesPerSampleBlock = 64;
+
+// Binary64 norm: one workgroup per 2^20 elements, fixed order.
+constexpr int64_t kNormChunk = int64_t(1) << 20;
+
+// Per-tensor selection modes (decided after the element-wise pass).
+constexpr uint32_t kModeSkip = 0;   // k = 0
+constexpr uint32_t kModeList = 1;   // select among the gathered candidates
+constexpr uint32_t kModeDense = 2;  // exact select over the whole tensor
+
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;  // above every 31-bit key
+
+// Device-side error latch values (negated DGC_* codes).
+constexpr uint32_t kErrCorrupt = 4;
+constexpr uint32_t kErrInternal = 3;
+
+// ---------------------------------------------------------------- structs
+
+// Per-tensor selection state, one per tensor in the workspace.
+struct TensorState {
+    uint32_t lo_key;  // candidate threshold from the sample window
+    uint32_t cursor;  // candidates reserved in the arena (may pass capacity)
+    uint32_t mode;    // kMode*
+    uint32_t len;     // items of the select source (list length or n_t)
+    uint32_t prefix;  // radix-select prefix; the threshold key T at the end
+    uint32_t krem;    // k still to place within the prefix; r at the end
+    uint32_t pad0, pad1;
+};
+
+// Per-call scalars.
+struct Scalars {
+    double norm;
+    float scale;
+    uint32_t status;  // latched kErr* (0 = fine)
+    uint32_t pad[12];
+};
+
+// Layout tables (device pointers into the workspace), passed by value.
+struct DevLayout {
+    int32_t T;
+    const int64_t* o;       // [T+1] element offsets
+    const int64_t* pbase;   // [T+1] first piece of each tensor
+    const int64_t* tbase;   // [T+1] first select/emit tile (ceil(n_t/kTile))
+    const int64_t* abase;   // [T+1] candidate arena offsets (capacity)
+    const int64_t* sbase;   // [T+1] first sample block
+    const int64_t* slines;  // [T] sampled lines (0 = no sampling)
+    const int64_t* ebase;   // [T+1] encoded stream capacity offsets
+    const int64_t* etbase;  // [T+1] tiles over encoded capacity
+    const uint32_t* pmap;   // [pieces] tensor of each piece
+    const uint32_t* smap;   // [sample blocks] tensor of each sample block
+    const uint32_t* emap;   // [capacity tiles] tensor of each tile
+};
+
+// Per-call k tables.
+struct DevK {
+    const int64_t* k;       // [T]
+    const int64_t* koff;    // [T+1] output offsets
+    const int64_t* ktbase;  // [T+1] tiles over k (ceil(k_t/kTile))
+    const uint32_t* kmap;   // [k tiles] tensor of each tile
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t mag_key(float x) {
+    return __float_as_uint(x) & 0x7FFFFFFFu;
+}
+
+// u <- fl(fl(m*u) + fl(g*s)); v <- fl(v + u).  Each operation rounds once
+// (explicit _rn intrinsics: never contracted into an FMA).
+__device__ __forceinline__ void momentum_update(float g, float s, float m,
+                                                float& u, float& v) {
+    float gs = __fmul_rn(g, s);
+    float mu = __fmul_rn(m, u);
+    u = __fadd_rn(mu, gs);
+    v = __fadd_rn(v, u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    return (uint64_t(1) << lane_id()) - 1;
+}
+
+__device__ __forceinline__ int wave_uniform(int x) {
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Largest t in [0, T) with base[t] <= x (base is non-decreasing, base[T] is
+// the total, x < base[T]).  Empty segments are skipped.
+__device__ __forceinline__ int find_seg(const int64_t* __restrict__ base,
+                                        int T, int64_t x) {
+    int lo = 0, hi = T;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (base[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// Inclusive scan within a wave (Hillis-Steele with shuffles).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Exclusive scan across the 256-thread block.  `lds` holds kWavesPerBlock
+// values.  Every thread must call it.  Returns the exclusive prefix; `total`
+// receives the block sum.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T x, T* lds, T& total) {
+    const int lane = lane_id();
+    const int wid = threadIdx.x >> 6;
+    T inc = wave_inclusive_scan(x);
+    if (lane == kWave - 1) lds[wid] = inc;
+    __syncthreads();
+    T wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        T s = lds[w];
+        if (w < wid) wpre += s;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return wpre + inc - x;
+}
+
+// Sum across the block in a fixed order (deterministic for floating point).
+__device__ __forceinline__ double block_sum_fixed(double x, double* lds) {
+    const int lane = lane_id();
+    const int wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
+    if (lane == 0) lds[wid] = x;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) t += lds[w];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ void latch_error(Scalars* sc, uint32_t code) {
+    atomicMax(&sc->status, code);
+}
+
+// 32-bit integer mix (the finaliser of MurmurHash3) for sample offsets.
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+}  // namespace dgc

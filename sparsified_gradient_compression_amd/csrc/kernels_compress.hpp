@@ -1,0 +1,694 @@
+// kernels_compress.hpp -- the compression step on gfx950.
+//
+// Method: DGC review page (nubint.ai), "Proposed method": local gradient
+// clipping, momentum correction with local accumulation, sending only the
+// largest |v| entries, momentum factor masking.  Selection is exact top-k
+// per tensor with ties to the lower index.
+//
+// Pass structure for one step (all on the caller's stream, no host sync):
+//   norm_partial/norm_final  binary64 sum of g^2 (only with clipping)
+//   sample/window            per tensor, keys of the would-be v on sampled
+//                            32-element lines -> a candidate threshold lo
+//   fused                    u, v update (20 B/elem); keys >= lo are
+//                            written, index-ordered per 1024-element piece,
+//                            into the tensor's candidate arena
+//   piece_scan               per tensor: choose the source (candidates when
+//                            they are complete and at least k, else the
+//                            whole tensor) and the order of the pieces
+//   hist<D>/resolve<D>       three radix digits (11,10,10 bits) -> the k-th
+//                            largest key T and the tie quota r
+//   emit_count/scan/write    index-ordered output of {key > T} plus the
+//                            first r ties, and u = v = +0 there
+#pragma once
+
+#include "dgc_device.hpp"
+
+namespace dgc {
+
+// ---------------------------------------------------------------- prep
+
+// Zero `n` 32-bit words (a fill kernel: safe inside captured graphs).
+__global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* __restrict__ p,
+                                                     int64_t n, uint32_t val) {
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * kBlock)
+        p[i] = val;
+}
+
+// Per-call reset of tensor states and scalars.
+__global__ __launch_bounds__(kBlock) void k_prep(TensorState* __restrict__ ts,
+                                                 int T, Scalars* __restrict__ sc,
+                                                 int clip_on) {
+    for (int t = blockIdx.x * kBlock + threadIdx.x; t < T;
+         t += gridDim.x * kBlock) {
+        TensorState s = {};
+        s.lo_key = kNoKey;
+        ts[t] = s;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && !clip_on) {
+        sc->norm = -1.0;
+        sc->scale = 1.0f;
+    }
+}
+
+// ---------------------------------------------------------------- norm
+
+// Block b sums g^2 over [b*kNormChunk, min(n, (b+1)*kNormChunk)) in
+// binary64: thread-strided float4 loads, one accumulator per float4 lane
+// slot, then a fixed-order block reduction.  The squares of binary32 values
+// are exact in binary64, so only the additions round.
+__global__ __launch_bounds__(kBlock) void k_norm_partial(
+    const float* __restrict__ g, int64_t n, double* __restrict__ partial) {
+    __shared__ double lds[kWavesPerBlock];
+    const int64_t lo = int64_t(blockIdx.x) * kNormChunk;
+    const int64_t hi = min(n, lo + kNormChunk);
+    const int64_t vlo = lo >> 2, vhi = hi >> 2;  // whole float4 units
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int64_t i = vlo + threadIdx.x;
+    for (; i + 3 * kBlock < vhi; i += 4 * kBlock) {
+        float4 x0 = g4[i], x1 = g4[i + kBlock], x2 = g4[i + 2 * kBlock],
+               x3 = g4[i + 3 * kBlock];
+        a0 += double(x0.x) * double(x0.x); a1 += double(x0.y) * double(x0.y);
+        a2 += double(x0.z) * double(x0.z); a3 += double(x0.w) * double(x0.w);
+        a0 += double(x1.x) * double(x1.x); a1 += double(x1.y) * double(x1.y);
+        a2 += double(x1.z) * double(x1.z); a3 += double(x1.w) * double(x1.w);
+        a0 += double(x2.x) * double(x2.x); a1 += double(x2.y) * double(x2.y);
+        a2 += double(x2.z) * double(x2.z); a3 += double(x2.w) * double(x2.w);
+        a0 += double(x3.x) * double(x3.x); a1 += double(x3.y) * double(x3.y);
+        a2 += double(x3.z) * double(x3.z); a3 += double(x3.w) * double(x3.w);
+    }
+    for (; i < vhi; i += kBlock) {
+        float4 x = g4[i];
+        a0 += double(x.x) * double(x.x); a1 += double(x.y) * double(x.y);
+        a2 += double(x.z) * double(x.z); a3 += double(x.w) * double(x.w);
+    }
+    // tail elements beyond the last whole float4 (only the last block)
+    for (int64_t e = (vhi << 2) + threadIdx.x; e < hi; e += kBlock)
+        a0 += double(g[e]) * double(g[e]);
+    double s = block_sum_fixed((a0 + a1) + (a2 + a3), lds);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+// One block: S = fixed-order sum of the partials; norm = sqrt(S);
+// s = (float)(clip / norm) if norm > clip else 1 (all in binary64, one
+// rounding to binary32 at the end).
+__global__ __launch_bounds__(kBlock) void k_norm_final(
+    const double* __restrict__ partial, int64_t nb, double clip,
+    Scalars* __restrict__ sc, double* __restrict__ out_norm,
+    float* __restrict__ out_scale) {
+    __shared__ double lds[kWavesPerBlock];
+    double a = 0.0;
+    for (int64_t i = threadIdx.x; i < nb; i += kBlock) a += partial[i];
+    double S = block_sum_fixed(a, lds);
+    if (threadIdx.x == 0) {
+        double norm = sqrt(S);
+        float s = 1.0f;
+        if (clip > 0.0 && norm > clip) s = float(clip / norm);
+        sc->norm = norm;
+        sc->scale = s;
+        if (out_norm) *out_norm = norm;
+        if (out_scale) *out_scale = s;
+    }
+}
+
+// Copy the per-call scalars to the caller's outputs (clipping off).
+__global__ void k_copy_scalars(const Scalars* __restrict__ sc,
+                               double* __restrict__ out_norm,
+                               float* __restrict__ out_scale) {
+    if (threadIdx.x == 0) {
+        if (out_norm) *out_norm = sc->norm;
+        if (out_scale) *out_scale = sc->scale;
+    }
+}
+
+// ---------------------------------------------------------------- sample
+
+// Keys of the would-be v on sampled lines.  Block b belongs to one tensor
+// (sbase); it visits kLinesPerSampleBlock of the tensor's sampled lines, one
+// 32-lane group per line.  Sampled line j lies at a hashed offset inside
+// the j-th of slines equal strides, so sampling does not alias with the
+// tensor's row structure.
+__global__ __launch_bounds__(kBlock) void k_sample(
+    const float* __restrict__ g, const float* __restrict__ u,
+    const float* __restrict__ v, DevLayout L, const Scalars* __restrict__ sc,
+    float m, uint32_t* __restrict__ shist) {
+    __shared__ uint32_t h[kBins0];
+    for (int b = threadIdx.x; b < kBins0; b += kBlock) h[b] = 0;
+    __syncthreads();
+    const int64_t sb = blockIdx.x;
+    const int t = int(L.smap[sb]);
+    const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+    const int64_t lines = (nt + kLine - 1) / kLine;
+    const int64_t ls = L.slines[t];
+    const int64_t stride = lines / ls;
+    const int64_t j0 = (sb - L.sbase[t]) * kLinesPerSampleBlock;
+    const int64_t j1 = min(ls, j0 + kLinesPerSampleBlock);
+    const float s = sc->scale;
+    const int grp = threadIdx.x >> 5, gl = threadIdx.x & 31;
+    for (int64_t j = j0 + grp; j < j1; j += kBlock / 32) {
+        uint32_t r = mix32(uint32_t(j) * 0x9E3779B9u ^ uint32_t(t) * 0x7F4A7C15u);
+        int64_t line = j * stride + int64_t(r % uint64_t(stride));
+        int64_t e = line * kLine + gl;
+        if (e < nt) {
+            float uu = u[o + e], vv = v[o + e];
+            momentum_update(g[o + e], s, m, uu, vv);
+            atomicAdd(&h[mag_key(vv) >> 20], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* row = shist + int64_t(t) * kHistBins;
+    for (int b = threadIdx.x; b < kBins0; b += kBlock)
+        if (h[b]) atomicAdd(&row[b], h[b]);
+}
+
+// One block per tensor: choose the candidate threshold lo.  With S sampled
+// keys and mu = S*k/n expected above the true k-th key, lo is the lower
+// edge of the top-digit bin that holds the j-th largest sampled key,
+// j = ceil(mu + 6 sqrt(mu) + 8).  Small tensors take every element
+// (lo = 0); k = 0 takes none.
+__global__ __launch_bounds__(kBlock) void k_window(
+    DevLayout L, DevK K, uint32_t* __restrict__ shist,
+    TensorState* __restrict__ ts, int force_dense) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    const int64_t k = K.k[t];
+    uint32_t* row = shist + int64_t(t) * kHistBins;
+    constexpr int per = kBins0 / kBlock;  // 8 bins per thread, from the top
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        int b = kBins0 - 1 - (threadIdx.x * per + q);
+        c[q] = row[b];
+        mine += c[q];
+    }
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(mine, lds, total);
+    // leave the row zeroed for the next step
+#pragma unroll
+    for (int q = 0; q < per; ++q) row[kBins0 - 1 - (threadIdx.x * per + q)] = 0;
+    // Exactly one thread writes lo_key (k_prep left it at kNoKey, which
+    // sends the tensor to the dense path should no bin qualify).
+    if (k <= 0 || force_dense) {
+        if (threadIdx.x == 0) ts[t].lo_key = kNoKey;
+        return;
+    }
+    if (L.slines[t] == 0) {
+        if (threadIdx.x == 0) ts[t].lo_key = 0;
+        return;
+    }
+    const double mu = double(total) * double(k) / double(nt);
+    const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
+    if (jd > double(total)) {
+        if (threadIdx.x == 0) ts[t].lo_key = 0;
+        return;
+    }
+    const uint32_t j = uint32_t(jd);
+    uint32_t run = above;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < j && j <= run + c[q]) {
+            int b = kBins0 - 1 - (threadIdx.x * per + q);
+            ts[t].lo_key = uint32_t(b) << 20;
+        }
+        run += c[q];
+    }
+}
+
+// ---------------------------------------------------------------- fused
+
+// Element-wise momentum correction + accumulation, and candidate output.
+// A wave owns one piece (<= 1024 elements, one tensor).  It loads g, u, v
+// as float4 (64 lanes x 4 units), updates u and v in registers and stores
+// them, then writes the piece's candidates (key >= lo) as one run in index
+// order: ballot + popcount give each candidate its rank, one atomicAdd on
+// the tensor's cursor reserves the run.
+template <bool kAligned>
+__device__ __forceinline__ void fused_piece(
+    const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
+    int64_t e0, int64_t e1, int64_t o, float s, float m, uint32_t lo,
+    uint32_t* cursor, uint64_t cap, uint2* __restrict__ arena,
+    uint32_t* __restrict__ run_base, uint32_t* __restrict__ run_cnt,
+    int64_t p) {
+    const int lane = lane_id();
+    float vn[4][4];
+    bool f[4][4];
+    if (kAligned) {
+        // e0 is a multiple of 4: 256 float4 units cover the piece.
+        const int64_t ubase = e0 >> 2;
+        float4 gv[4], uv[4], vv[4];
+        bool full[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t el = (ubase + i * kWave + lane) << 2;
+            full[i] = el + 4 <= e1;
+            if (full[i]) {
+                gv[i] = *reinterpret_cast<const float4*>(g + el);
+                uv[i] = *reinterpret_cast<const float4*>(u + el);
+                vv[i] = *reinterpret_cast<const float4*>(v + el);
+            } else {
+                float tg[4] = {0, 0, 0, 0}, tu[4] = {0, 0, 0, 0},
+                      tv[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (el + c < e1) { tg[c] = g[el + c]; tu[c] = u[el + c]; tv[c] = v[el + c]; }
+                gv[i] = make_float4(tg[0], tg[1], tg[2], tg[3]);
+                uv[i] = make_float4(tu[0], tu[1], tu[2], tu[3]);
+                vv[i] = make_float4(tv[0], tv[1], tv[2], tv[3]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t el = (ubase + i * kWave + lane) << 2;
+            float gg[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+            float uu[4] = {uv[i].x, uv[i].y, uv[i].z, uv[i].w};
+            float vv4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                momentum_update(gg[c], s, m, uu[c], vv4[c]);
+                vn[i][c] = vv4[c];
+                f[i][c] = (el + c < e1) && mag_key(vv4[c]) >= lo;
+            }
+            if (full[i]) {
+                *reinterpret_cast<float4*>(u + el) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+                *reinterpret_cast<float4*>(v + el) = make_float4(vv4[0], vv4[1], vv4[2], vv4[3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (el + c < e1) { u[el + c] = uu[c]; v[el + c] = vv4[c]; }
+            }
+        }
+    } else {
+        // Unaligned piece start: 16 scalar rounds of 64 consecutive elements.
+        // Element (i, c) of a lane is e0 + (i*4 + c)*64 + lane; ranks below
+        // follow (i, c, lane) order, which is index order here.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                int64_t el = e0 + int64_t(i * 4 + c) * kWave + lane;
+                bool ok = el < e1;
+                float gg = ok ? g[el] : 0.f, uu = ok ? u[el] : 0.f,
+                      vv = ok ? v[el] : 0.f;
+                momentum_update(gg, s, m, uu, vv);
+                if (ok) { u[el] = uu; v[el] = vv; }
+                vn[i][c] = vv;
+                f[i][c] = ok && mag_key(vv) >= lo;
+            }
+        }
+    }
+    // Ranks in index order.
+    uint32_t rank[4][4];
+    uint32_t total = 0;
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint64_t b[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = __ballot(f[i][c]);
+        if (kAligned) {
+            // order within round i: (lane, c)
+            uint32_t before = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) before += __popcll(b[c] & lt);
+            uint32_t own = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                rank[i][c] = total + before + own;
+                own += f[i][c];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) total += __popcll(b[c]);
+        } else {
+            // order within round i: (c, lane)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                rank[i][c] = total + __popcll(b[c] & lt);
+                total += __popcll(b[c]);
+            }
+        }
+    }
+    uint32_t base = 0;
+    if (total) {
+        if (lane == 0) base = atomicAdd(cursor, total);
+        base = __shfl(base, 0, kWave);
+    }
+    if (lane == 0) { run_base[p] = base; run_cnt[p] = total; }
+    if (total) {
+        const int64_t unit0 = e0 >> 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (f[i][c]) {
+                    uint64_t slot = uint64_t(base) + rank[i][c];
+                    int64_t el = kAligned ? (((unit0 + i * kWave + lane) << 2) + c)
+                                          : (e0 + int64_t(i * 4 + c) * kWave + lane);
+                    if (slot < cap)
+                        arena[slot] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
+                }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_fused(
+    const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
+    DevLayout L, TensorState* __restrict__ ts, const Scalars* __restrict__ sc,
+    float m, uint2* __restrict__ arena, uint32_t* __restrict__ run_base,
+    uint32_t* __restrict__ run_cnt, int64_t n_pieces) {
+    const float s = sc->scale;
+    const int64_t w0 = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+    const int64_t nw = (int64_t(gridDim.x) * kBlock) >> 6;
+    for (int64_t p = w0; p < n_pieces; p += nw) {
+        const int t = wave_uniform(int(L.pmap[p]));
+        const int64_t o = L.o[t];
+        const int64_t e0 = o + ((p - L.pbase[t]) << kPieceShift);
+        const int64_t e1 = min(e0 + kPiece, L.o[t + 1]);
+        const uint32_t lo = ts[t].lo_key;
+        const int64_t ab = L.abase[t];
+        const uint64_t cap = uint64_t(L.abase[t + 1] - ab);
+        if ((e0 & 3) == 0)
+            fused_piece<true>(g, u, v, e0, e1, o, s, m, lo, &ts[t].cursor, cap,
+                              arena + ab, run_base, run_cnt, p);
+        else
+            fused_piece<false>(g, u, v, e0, e1, o, s, m, lo, &ts[t].cursor, cap,
+                               arena + ab, run_base, run_cnt, p);
+    }
+}
+
+// ---------------------------------------------------------------- source
+
+// One block per tensor: decide the selection source and, for the candidate
+// list, the exclusive scan of the pieces' run lengths (their index order).
+// Also counts the source's 4096-item tiles for the active-tile map.
+__global__ __launch_bounds__(kBlock) void k_piece_scan(
+    DevLayout L, DevK K, TensorState* __restrict__ ts,
+    const uint32_t* __restrict__ run_cnt, uint32_t* __restrict__ ord_off,
+    uint32_t* __restrict__ atiles) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    const int64_t k = K.k[t];
+    const uint32_t cur = ts[t].cursor;
+    const uint64_t cap = uint64_t(L.abase[t + 1] - L.abase[t]);
+    uint32_t mode;
+    if (k <= 0) mode = kModeSkip;
+    else if (uint64_t(cur) > cap || int64_t(cur) < k) mode = kModeDense;
+    else mode = kModeList;
+    const int64_t len = mode == kModeList ? int64_t(cur) : nt;
+    if (threadIdx.x == 0) {
+        ts[t].mode = mode;
+        ts[t].len = uint32_t(len);
+        ts[t].prefix = 0;
+        ts[t].krem = uint32_t(k > 0 ? k : 0);
+        atiles[t] = mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift);
+    }
+    if (mode != kModeList) return;
+    const int64_t p0 = L.pbase[t], p1 = L.pbase[t + 1];
+    uint32_t carry = 0;
+    for (int64_t base = p0; base < p1; base += kBlock) {
+        int64_t p = base + threadIdx.x;
+        uint32_t c = p < p1 ? run_cnt[p] : 0;
+        uint32_t tot;
+        uint32_t ex = block_exclusive_scan(c, lds, tot);
+        if (p < p1) ord_off[p] = carry + ex;
+        carry += tot;
+    }
+}
+
+// One block: exclusive scan of the active tile counts -> aoff[T+1].
+__global__ __launch_bounds__(kBlock) void k_active_scan(
+    int T, const uint32_t* __restrict__ atiles, uint32_t* __restrict__ aoff) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    uint32_t carry = 0;
+    for (int base = 0; base < T; base += kBlock) {
+        int t = base + threadIdx.x;
+        uint32_t c = t < T ? atiles[t] : 0;
+        uint32_t tot;
+        uint32_t ex = block_exclusive_scan(c, lds, tot);
+        if (t < T) aoff[t] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) aoff[T] = carry;
+}
+
+// One block per tensor: amap[a] = t for the tensor's active tiles.
+__global__ __launch_bounds__(kBlock) void k_active_map(
+    const uint32_t* __restrict__ atiles, const uint32_t* __restrict__ aoff,
+    uint32_t* __restrict__ amap) {
+    const int t = blockIdx.x;
+    const uint32_t a0 = aoff[t], n = atiles[t];
+    for (uint32_t j = threadIdx.x; j < n; j += kBlock) amap[a0 + j] = uint32_t(t);
+}
+
+// ---------------------------------------------------------------- select
+
+template <int D>
+struct Digit;
+template <> struct Digit<0> { static constexpr int shift = 20, bits = 11; };
+template <> struct Digit<1> { static constexpr int shift = 10, bits = 10; };
+template <> struct Digit<2> { static constexpr int shift = 0, bits = 10; };
+
+__device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
+    __syncthreads();
+    for (int b = threadIdx.x; b < kHistBins; b += kBlock) {
+        uint32_t c = h[b];
+        if (c) { atomicAdd(&row[b], c); h[b] = 0; }
+    }
+    __syncthreads();
+}
+
+// Active tiles: a in [0, aoff[T]) is tile (a - aoff[t]) of tensor
+// t = amap[a]; the tile covers source items [4096 j, 4096 j + 4096) of the
+// tensor's source (candidate list or whole tensor), clipped to len.
+
+// Histogram of digit D over the keys that match the prefix found so far.
+// Workgroups stride over the active tiles.  In the first pass the
+// candidate list is also put into index order: arena -> olist.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_hist(
+    DevLayout L, const TensorState* __restrict__ ts,
+    const float* __restrict__ v, const uint2* __restrict__ arena,
+    uint2* __restrict__ olist, const uint32_t* __restrict__ run_base,
+    const uint32_t* __restrict__ ord_off, const uint32_t* __restrict__ amap,
+    const uint32_t* __restrict__ aoff, uint32_t* __restrict__ hist) {
+    constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
+    constexpr uint32_t dmask = (1u << bits) - 1;
+    __shared__ uint32_t h[kHistBins];
+    for (int b = threadIdx.x; b < kHistBins; b += kBlock) h[b] = 0;
+    __syncthreads();
+    const uint32_t A = aoff[L.T];
+    int cur_t = -1;
+    for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
+        const int t = int(amap[a]);
+        const uint32_t mode = ts[t].mode;
+        const int64_t len = ts[t].len;
+        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
+        if (t != cur_t) {
+            if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
+            cur_t = t;
+        }
+        const uint32_t prefix = ts[t].prefix;
+        const int64_t i1 = min(len, i0 + kTile);
+        if (mode == kModeDense) {
+            const float* vt_ = v + L.o[t];
+            for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
+                uint32_t key = mag_key(vt_[i]);
+                if (D == 0 || (key >> (shift + bits)) == prefix)
+                    atomicAdd(&h[(key >> shift) & dmask], 1u);
+            }
+        } else {
+            const int64_t ab = L.abase[t];
+            const uint2* src = (D == 0 ? arena : olist) + ab;
+            for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
+                uint2 e = src[i];
+                uint32_t key = e.y & 0x7FFFFFFFu;
+                if (D == 0 || (key >> (shift + bits)) == prefix)
+                    atomicAdd(&h[(key >> shift) & dmask], 1u);
+                if (D == 0) {
+                    int64_t p = L.pbase[t] + (e.x >> kPieceShift);
+                    uint32_t pos = ord_off[p] + (uint32_t(i) - run_base[p]);
+                    olist[ab + pos] = e;
+                }
+            }
+        }
+    }
+    if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
+}
+
+// One block per tensor: find the bin of digit D holding the krem-th largest
+// matching key; extend the prefix and reduce krem.  Clears the histogram.
+// After D = 2, prefix is the k-th largest key T and krem is the number of
+// keys equal to T to take (r).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_resolve(
+    TensorState* __restrict__ ts, uint32_t* __restrict__ hist,
+    Scalars* __restrict__ sc) {
+    constexpr int bins = 1 << Digit<D>::bits;
+    constexpr int per = bins / kBlock;
+    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ int found;
+    const int t = blockIdx.x;
+    if (ts[t].mode == kModeSkip) return;
+    uint32_t* row = hist + int64_t(t) * kHistBins;
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        c[q] = row[bins - 1 - (threadIdx.x * per + q)];
+        mine += c[q];
+    }
+    if (threadIdx.x == 0) found = 0;
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(mine, lds, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
+    const uint32_t krem = ts[t].krem;
+    const uint32_t prefix = ts[t].prefix;
+    __syncthreads();  // every thread has read prefix/krem before the update
+    uint32_t run = above;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            uint32_t b = uint32_t(bins - 1 - (threadIdx.x * per + q));
+            ts[t].prefix = (prefix << Digit<D>::bits) | b;
+            ts[t].krem = krem - run;
+            found = 1;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && !found) latch_error(sc, kErrInternal);
+}
+
+// ---------------------------------------------------------------- emit
+
+// Item i of tensor t's source: local index and value bits.
+__device__ __forceinline__ uint2 source_item(uint32_t mode, const float* vt_,
+                                             const uint2* ol, int64_t i) {
+    if (mode == kModeDense) return make_uint2(uint32_t(i), __float_as_uint(vt_[i]));
+    return ol[i];
+}
+
+// (key > T) counts in the high 16 bits, (key == T) in the low 16 bits of
+// thread tid's items [i0 + 16 tid, i0 + 16 tid + 16).
+__device__ __forceinline__ uint32_t count_items(uint32_t mode, const float* vt_,
+                                                const uint2* ol, int64_t s0,
+                                                int64_t len, uint32_t T) {
+    uint32_t cnt = 0;
+    for (int q = 0; q < kPerThread; ++q) {
+        int64_t i = s0 + q;
+        if (i < len) {
+            uint32_t key = source_item(mode, vt_, ol, i).y & 0x7FFFFFFFu;
+            cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
+        }
+    }
+    return cnt;
+}
+
+// Per active tile: packed (#key > T, #key == T).
+__global__ __launch_bounds__(kBlock) void k_emit_count(
+    DevLayout L, const TensorState* __restrict__ ts,
+    const float* __restrict__ v, const uint2* __restrict__ olist,
+    const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
+    uint32_t* __restrict__ tile_cnt) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const uint32_t A = aoff[L.T];
+    for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
+        const int t = int(amap[a]);
+        const uint32_t mode = ts[t].mode;
+        const int64_t len = ts[t].len;
+        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
+        const uint32_t T = ts[t].prefix;
+        const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
+        uint32_t cnt = count_items(mode, v + L.o[t], olist + L.abase[t], s0, len, T);
+        uint32_t tot;
+        block_exclusive_scan(cnt, lds, tot);
+        if (threadIdx.x == 0) tile_cnt[a] = tot;
+    }
+}
+
+// One block per tensor: exclusive scan of its tiles' (>T, ==T) counts.
+__global__ __launch_bounds__(kBlock) void k_emit_scan(
+    int T_, const uint32_t* __restrict__ aoff,
+    const uint32_t* __restrict__ tile_cnt, uint32_t* __restrict__ off_gt,
+    uint32_t* __restrict__ off_eq) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
+    uint32_t cg = 0, ce = 0;
+    for (uint32_t base = a0; base < a1; base += kBlock) {
+        uint32_t a = base + threadIdx.x;
+        uint32_t x = a < a1 ? tile_cnt[a] : 0;
+        uint32_t tg, te;
+        uint32_t eg = block_exclusive_scan(x >> 16, lds, tg);
+        uint32_t ee = block_exclusive_scan(x & 0xFFFFu, lds, te);
+        if (a < a1) { off_gt[a] = cg + eg; off_eq[a] = ce + ee; }
+        cg += tg;
+        ce += te;
+    }
+}
+
+// Per active tile: write the selected items in index order and mask u, v
+// there.  An item with key > T, or key == T while fewer than r ties precede
+// it, is sent; its output slot is (#sent before it) =
+// gt_before + min(eq_before, r).
+__global__ __launch_bounds__(kBlock) void k_emit_write(
+    DevLayout L, DevK K, const TensorState* __restrict__ ts,
+    float* __restrict__ u, float* __restrict__ v,
+    const uint2* __restrict__ olist, const uint32_t* __restrict__ amap,
+    const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ off_gt,
+    const uint32_t* __restrict__ off_eq, uint32_t* __restrict__ out_idx,
+    float* __restrict__ out_val, Scalars* __restrict__ sc) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const uint32_t A = aoff[L.T];
+    for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
+        const int t = int(amap[a]);
+        const uint32_t mode = ts[t].mode;
+        const int64_t len = ts[t].len;
+        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
+        const uint32_t T = ts[t].prefix, r = ts[t].krem;
+        const int64_t o = L.o[t];
+        float* vt_ = v + o;
+        const uint2* ol = olist + L.abase[t];
+        const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
+        uint32_t cnt = count_items(mode, vt_, ol, s0, len, T);
+        uint32_t tot;
+        uint32_t ex = block_exclusive_scan(cnt, lds, tot);
+        uint32_t gt = off_gt[a] + (ex >> 16);
+        uint32_t eq = off_eq[a] + (ex & 0xFFFFu);
+        uint32_t* oi = out_idx + K.koff[t];
+        float* ov = out_val + K.koff[t];
+        const int64_t kt = K.k[t];
+        const int64_t nt = L.o[t + 1] - o;
+        bool bad = false;
+        for (int q = 0; q < kPerThread; ++q) {
+            int64_t i = s0 + q;
+            if (i >= len) break;
+            uint2 it = source_item(mode, vt_, ol, i);
+            uint32_t key = it.y & 0x7FFFFFFFu;
+            bool send = false;
+            uint32_t slot = 0;
+            if (key > T) {
+                send = true;
+                slot = gt + min(eq, r);
+                ++gt;
+            } else if (key == T) {
+                if (eq < r) { send = true; slot = gt + eq; }
+                ++eq;
+            }
+            if (send) {
+                // never write outside the outputs, whatever the counts say
+                if (int64_t(slot) >= kt || int64_t(it.x) >= nt) { bad = true; continue; }
+                oi[slot] = it.x;
+                ov[slot] = __uint_as_float(it.y);
+                u[o + it.x] = 0.0f;
+                vt_[it.x] = 0.0f;
+            }
+        }
+        if (bad) latch_error(sc, kErrInternal);
+    }
+}
+
+}  // namespace dgc

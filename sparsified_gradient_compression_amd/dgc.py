@@ -1,0 +1,291 @@
+"""ctypes binding of libdgc (include/dgc.h): the same entry points, with
+torch tensors marshalled to device pointers.  No computation happens here;
+every step of the compressor runs in the HIP kernels of libdgc.so, and the
+binding refuses to run without that library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+DGC_OK = 0
+DGC_EINVAL = -1
+DGC_ECAPACITY = -2
+DGC_EHIP = -3
+DGC_ECORRUPT = -4
+DGC_OPT_SELECT_PATH = 1
+DGC_OPT_KERNEL_TIMING = 2
+DGC_TIMER_FUSED = 0
+DGC_TIMER_COMPRESS = 1
+DGC_TIMER_ENCODE = 2
+DGC_TIMER_DECODE = 3
+
+_lib = None
+
+
+class DGCError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {dgc_error_string(code)} ({code})")
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdgc.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m sparsified_gradient_compression_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    L.dgc_workspace_bytes.argtypes = [i32, P, P, ctypes.POINTER(ctypes.c_size_t)]
+    L.dgc_workspace_bytes.restype = ctypes.c_int
+    L.dgc_init_state.argtypes = [ctypes.POINTER(P), i32, P, P, ctypes.c_float,
+                                 P, P, P, ctypes.c_size_t, P]
+    L.dgc_init_state.restype = ctypes.c_int
+    L.dgc_compress.argtypes = [P, P, P, ctypes.c_double, P, P, P, P, P]
+    L.dgc_compress.restype = ctypes.c_int
+    L.dgc_stream_capacity.argtypes = [P, P]
+    L.dgc_stream_capacity.restype = ctypes.c_int
+    L.dgc_encode.argtypes = [P, P, P, P, P, P, P, P]
+    L.dgc_encode.restype = ctypes.c_int
+    L.dgc_decode_accumulate.argtypes = [P, i32, P, P, P, P, P]
+    L.dgc_decode_accumulate.restype = ctypes.c_int
+    L.dgc_get_status.argtypes = [P]
+    L.dgc_get_status.restype = ctypes.c_int
+    L.dgc_get_path_counts.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.dgc_get_path_counts.restype = ctypes.c_int
+    L.dgc_set_option.argtypes = [P, i32, i64]
+    L.dgc_set_option.restype = ctypes.c_int
+    L.dgc_get_kernel_time.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(i64)]
+    L.dgc_get_kernel_time.restype = ctypes.c_int
+    L.dgc_destroy_state.argtypes = [P]
+    L.dgc_destroy_state.restype = None
+    L.dgc_error_string.argtypes = [ctypes.c_int]
+    L.dgc_error_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _hp(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dp(t) -> Optional[int]:
+    """Device pointer of a torch tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != DGC_OK:
+        raise DGCError(rc, what)
+
+
+# ---------------------------------------------------------------- entry points
+
+def dgc_error_string(code: int) -> str:
+    return lib().dgc_error_string(int(code)).decode()
+
+
+def dgc_workspace_bytes(sizes: Sequence[int], k_max: Sequence[int]) -> int:
+    s, km = _i64(sizes), _i64(k_max)
+    out = ctypes.c_size_t(0)
+    _check(lib().dgc_workspace_bytes(len(s), _hp(s), _hp(km), ctypes.byref(out)),
+           "dgc_workspace_bytes")
+    return int(out.value)
+
+
+def dgc_init_state(sizes, k_max, momentum: float, u, v, workspace,
+                   stream=None) -> ctypes.c_void_p:
+    s, km = _i64(sizes), _i64(k_max)
+    st = ctypes.c_void_p()
+    _check(lib().dgc_init_state(ctypes.byref(st), len(s), _hp(s), _hp(km),
+                                float(momentum), _dp(u), _dp(v), _dp(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream(stream)),
+           "dgc_init_state")
+    return st
+
+
+def dgc_compress(st, g, k, clip: float, out_idx, out_val, out_norm=None,
+                 out_scale=None, stream=None):
+    kk = _i64(k)
+    _check(lib().dgc_compress(st, _dp(g), _hp(kk), float(clip), _dp(out_idx),
+                              _dp(out_val), _dp(out_norm), _dp(out_scale),
+                              _stream(stream)),
+           "dgc_compress")
+
+
+def dgc_stream_capacity(st, n_tensors: int) -> np.ndarray:
+    out = np.zeros(n_tensors + 1, np.int64)
+    _check(lib().dgc_stream_capacity(st, _hp(out)), "dgc_stream_capacity")
+    return out
+
+
+def dgc_encode(st, k, idx, val, runs, vals, entries, stream=None):
+    kk = _i64(k)
+    _check(lib().dgc_encode(st, _hp(kk), _dp(idx), _dp(val), _dp(runs), _dp(vals),
+                            _dp(entries), _stream(stream)),
+           "dgc_encode")
+
+
+def dgc_decode_accumulate(st, runs: Sequence, vals: Sequence, entries: Sequence,
+                          dense, stream=None):
+    W = len(runs)
+    assert len(vals) == W and len(entries) == W
+    Arr = ctypes.c_void_p * max(W, 1)
+    r = Arr(*[_dp(x) for x in runs])
+    vv = Arr(*[_dp(x) for x in vals])
+    e = Arr(*[_dp(x) for x in entries])
+    _check(lib().dgc_decode_accumulate(st, W, ctypes.cast(r, ctypes.c_void_p),
+                                       ctypes.cast(vv, ctypes.c_void_p),
+                                       ctypes.cast(e, ctypes.c_void_p), _dp(dense),
+                                       _stream(stream)),
+           "dgc_decode_accumulate")
+
+
+def dgc_get_status(st) -> int:
+    return int(lib().dgc_get_status(st))
+
+
+def dgc_get_path_counts(st) -> Tuple[int, int]:
+    nw, nd = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().dgc_get_path_counts(st, ctypes.byref(nw), ctypes.byref(nd)),
+           "dgc_get_path_counts")
+    return int(nw.value), int(nd.value)
+
+
+def dgc_set_option(st, option: int, value: int):
+    _check(lib().dgc_set_option(st, int(option), int(value)), "dgc_set_option")
+
+
+def dgc_get_kernel_time(st, timer: int) -> Tuple[float, int]:
+    ms, cnt = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().dgc_get_kernel_time(st, int(timer), ctypes.byref(ms),
+                                     ctypes.byref(cnt)),
+           "dgc_get_kernel_time")
+    return float(ms.value), int(cnt.value)
+
+
+def dgc_destroy_state(st):
+    lib().dgc_destroy_state(st)
+
+
+# ---------------------------------------------------------------- host logic
+
+def k_for_density(n: int, density: Fraction) -> int:
+    """Warm-up schedule (DGC review, "Proposed method": sparsity rises step
+    by step): k = ceil(n * density) with density an exact fraction, in
+    integer arithmetic."""
+    d = Fraction(density)
+    return int(-((-int(n) * d.numerator) // d.denominator)) if n > 0 else 0
+
+
+class Learner:
+    """One learner's device state for a tensor layout: u, v, workspace and
+    output buffers, as torch tensors on the current device."""
+
+    def __init__(self, sizes: Sequence[int], k_max: Sequence[int],
+                 momentum: float = 0.9, device="cuda", stream=None):
+        import torch
+        self.sizes = [int(s) for s in sizes]
+        self.k_max = [int(x) for x in k_max]
+        self.T = len(self.sizes)
+        self.n = int(sum(self.sizes))
+        dev = torch.device(device)
+        self.u = torch.empty(max(self.n, 1), dtype=torch.float32, device=dev)
+        self.v = torch.empty(max(self.n, 1), dtype=torch.float32, device=dev)
+        ws = dgc_workspace_bytes(self.sizes, self.k_max)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.state = dgc_init_state(self.sizes, self.k_max, momentum, self.u,
+                                    self.v, self.workspace, stream)
+        K = max(int(sum(self.k_max)), 1)
+        self.idx = torch.empty(K, dtype=torch.int32, device=dev)
+        self.val = torch.empty(K, dtype=torch.float32, device=dev)
+        self.norm = torch.empty(1, dtype=torch.float64, device=dev)
+        self.scale = torch.empty(1, dtype=torch.float32, device=dev)
+        self.cap = dgc_stream_capacity(self.state, self.T)
+        C = max(int(self.cap[-1]), 1)
+        self.runs = torch.empty(C, dtype=torch.int16, device=dev)
+        self.vals = torch.empty(C, dtype=torch.float32, device=dev)
+        self.entries = torch.empty(self.T, dtype=torch.int64, device=dev)
+
+    def compress(self, g, k: Sequence[int], clip: float, stream=None):
+        """One step; returns (idx, val) views holding sum(k) entries."""
+        K = int(sum(int(x) for x in k))
+        dgc_compress(self.state, g, k, clip, self.idx, self.val, self.norm,
+                     self.scale, stream)
+        return self.idx[:K], self.val[:K]
+
+    def encode(self, k: Sequence[int], stream=None):
+        dgc_encode(self.state, k, self.idx, self.val, self.runs, self.vals,
+                   self.entries, stream)
+        return self.runs, self.vals, self.entries
+
+    def set_option(self, option: int, value: int):
+        dgc_set_option(self.state, option, value)
+
+    def status(self) -> int:
+        return dgc_get_status(self.state)
+
+    def path_counts(self) -> Tuple[int, int]:
+        return dgc_get_path_counts(self.state)
+
+    def kernel_time(self, timer: int) -> Tuple[float, int]:
+        return dgc_get_kernel_time(self.state, timer)
+
+    def close(self):
+        if self.state is not None:
+            dgc_destroy_state(self.state)
+            self.state = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode_accumulate(layout_learner: Learner, streams: List[Tuple], dense,
+                      stream=None):
+    """dense += the decoded streams [(runs, vals, entries), ...] in order."""
+    dgc_decode_accumulate(layout_learner.state, [s[0] for s in streams],
+                          [s[1] for s in streams], [s[2] for s in streams],
+                          dense, stream)

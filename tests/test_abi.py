@@ -1,0 +1,115 @@
+"""The C-ABI library: it loads, exports every entry point that include/dgc.h
+declares, and its host-side argument checks return the documented codes
+without touching a GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+from sparsified_gradient_compression_amd import dgc
+
+HEADER = os.path.join(ROOT, "include", "dgc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dgc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 12, names
+    L = dgc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dgc.lib_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (dgc_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_error_strings():
+    assert dgc.dgc_error_string(0) == "ok"
+    assert dgc.dgc_error_string(-1) == "invalid argument"
+    assert dgc.dgc_error_string(-4) == "corrupt stream"
+    assert dgc.dgc_error_string(123) == "unknown error"
+
+
+def test_workspace_bytes_validation():
+    L = dgc.lib()
+    out = ctypes.c_size_t(0)
+
+    def call(sizes, kmax):
+        s = np.asarray(sizes, np.int64)
+        k = np.asarray(kmax, np.int64)
+        return L.dgc_workspace_bytes(len(s), s.ctypes.data, k.ctypes.data,
+                                     ctypes.byref(out))
+
+    assert call([10, 20], [1, 1]) == 0 and out.value > 0
+    assert call([10], [11]) == dgc.DGC_EINVAL       # k_max > n
+    assert call([10], [-1]) == dgc.DGC_EINVAL
+    assert call([1 << 32], [1]) == dgc.DGC_EINVAL   # local indices are 32-bit
+    assert call([-5], [0]) == dgc.DGC_EINVAL
+    assert L.dgc_workspace_bytes(0, None, None, ctypes.byref(out)) == dgc.DGC_EINVAL
+    assert call([0, 7], [0, 7]) == 0                # empty tensors are allowed
+
+
+def test_workspace_grows_with_k_max():
+    small = dgc.dgc_workspace_bytes([1 << 24] * 4, [16778] * 4)
+    big = dgc.dgc_workspace_bytes([1 << 24] * 4, [1 << 22] * 4)
+    assert big > small
+
+
+def test_init_and_calls_reject_bad_arguments_before_any_launch():
+    L = dgc.lib()
+    st = ctypes.c_void_p()
+    s = np.array([100], np.int64)
+    k = np.array([1], np.int64)
+    # no workspace
+    assert L.dgc_init_state(ctypes.byref(st), 1, s.ctypes.data, k.ctypes.data,
+                            0.9, 256, 256, None, 0, None) == dgc.DGC_EINVAL
+    # misaligned workspace
+    assert L.dgc_init_state(ctypes.byref(st), 1, s.ctypes.data, k.ctypes.data,
+                            0.9, 256, 256, 4096 + 8, 1 << 20, None) == dgc.DGC_EINVAL
+    # workspace too small
+    assert L.dgc_init_state(ctypes.byref(st), 1, s.ctypes.data, k.ctypes.data,
+                            0.9, 256, 256, 4096, 16, None) == dgc.DGC_ECAPACITY
+    # misaligned u
+    assert L.dgc_init_state(ctypes.byref(st), 1, s.ctypes.data, k.ctypes.data,
+                            0.9, 260, 256, 4096, 1 << 30, None) == dgc.DGC_EINVAL
+    assert st.value is None
+    assert L.dgc_compress(None, None, None, 0.0, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_encode(None, None, None, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_decode_accumulate(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_get_status(None) == dgc.DGC_EINVAL
+    assert L.dgc_set_option(None, 1, 0) == dgc.DGC_EINVAL
+    L.dgc_destroy_state(None)
+
+
+def test_k_schedule_host_logic():
+    assert dgc.k_for_density(350_000_000, Fraction(1, 1000)) == 350_000
+    assert dgc.k_for_density(1 << 20, Fraction(1, 1000)) == 1049
+    assert dgc.k_for_density(1 << 24, Fraction(1, 1000)) == 16778
+    assert dgc.k_for_density(64, Fraction(1, 1000)) == 1
+    assert dgc.k_for_density(0, Fraction(1, 1000)) == 0
+    for n in range(1, 3000, 7):
+        for d in (Fraction(1, 4), Fraction(1, 250), Fraction(3, 7)):
+            want = -(-n * d.numerator // d.denominator)
+            assert dgc.k_for_density(n, d) == want
+
+
+def test_build_flags_keep_ieee_binary32():
+    from sparsified_gradient_compression_amd import build
+    flags = " ".join(build.HIPCC_FLAGS)
+    assert "-ffp-contract=off" in flags
+    assert "-fno-gpu-flush-denormals-to-zero" in flags
+    assert "-packed-fp32-ops" in flags
+    assert "gfx950" in flags

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit for
+bit on selected indices, values, encoded streams, u/v state and dense sums;
+the clipping norm to relative 1e-6.
+
+Sizes here span several pieces and tiles with ragged tails; the full-size
+workloads are in test_gpu_fullsize.py.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import (Pair, compare_streams, f32_bits, first_diff,
+                         gpu_streams, oracle_streams, say)
+from sparsified_gradient_compression_amd import dgc
+from sparsified_gradient_compression_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dgc.lib()  # raises if the HIP library is missing
+    return torch
+
+
+def ks_for(wl, step):
+    return [dgc.k_for_density(s, wl.densities[step]) for s in wl.sizes]
+
+
+def run_workload(wl, steps=None, learners=None, path=0, encode=True, tag=""):
+    steps = wl.steps if steps is None else steps
+    learners = wl.learners if learners is None else learners
+    kmax = [max(dgc.k_for_density(s, d) for d in wl.densities) for s in wl.sizes]
+    pairs = [Pair(list(wl.sizes), kmax, wl.momentum) for _ in range(learners)]
+    for p in pairs:
+        p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    for t in range(steps):
+        k = ks_for(wl, t)
+        outs = []
+        for w, p in enumerate(pairs):
+            say(f"{tag} step {t} learner {w} n={wl.n} T={len(wl.sizes)}")
+            g = W.gradient(wl, w, t)
+            got, (o_idx, o_val) = p.step(g, k, wl.clip, tag=f"{tag} s{t} w{w}")
+            if encode:
+                want = oracle_streams(wl.sizes, k, o_idx, o_val)
+                gs = gpu_streams(p, k)
+                compare_streams(gs, want, tag=f"{tag} s{t} w{w}")
+                outs.append(want)
+        if encode:
+            check_decode(pairs, outs, wl.sizes, tag=f"{tag} s{t}")
+    return pairs
+
+
+def check_decode(pairs, streams_per_learner, sizes, tag=""):
+    """Decode every learner's GPU-encoded stream (learner order) into one
+    dense sum and compare with the oracle decoding the oracle's streams."""
+    import torch
+    n = int(sum(sizes))
+    dense = torch.zeros(max(n, 1), dtype=torch.float32, device="cuda")
+    dgc.decode_accumulate(pairs[0].learner,
+                          [(p.learner.runs, p.learner.vals, p.learner.entries)
+                           for p in pairs], dense)
+    got = dense[:n].cpu().numpy()
+    assert pairs[0].learner.status() == dgc.DGC_OK
+    want = np.zeros(n, np.float32)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    for streams in streams_per_learner:
+        for t, (wr, wv) in enumerate(streams):
+            assert oracle.decode_accumulate(wr, wv, want[off[t]:off[t + 1]]) == 0
+    assert np.array_equal(f32_bits(got), f32_bits(want)), (tag, first_diff(got, want))
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_flat1m(path):
+    """2**20 Laplace entries, k = 1049, one step, no clipping."""
+    run_workload(W.get("flat1m"), path=path, tag=f"flat1m/p{path}")
+
+
+def test_resnet50_scaled_three_steps():
+    wl = W.scaled(W.get("resnet50"), 8)
+    run_workload(wl, steps=3, tag="rn50/8")
+
+
+def test_deepspeech_scaled_four_learners():
+    wl = W.scaled(W.get("deepspeech"), 40)
+    run_workload(wl, tag="ds/40")
+
+
+def test_warmup_schedule_scaled():
+    wl = W.scaled(W.get("warmup350m"), 100)
+    run_workload(wl, tag="warm/100")
+
+
+def test_flat1b_shape_scaled():
+    wl = W.scaled(W.get("flat1b"), 256)
+    run_workload(wl, steps=2, learners=2, tag="1b/256")
+
+
+# ---------------------------------------------------------------- edge cases
+
+RAGGED = [1, 0, 3, 64, 1000, 1023, 1025, 4097, 65536, 65537, 300001, 7]
+
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ragged_layout(path, seed):
+    """Odd sizes (misaligned tensor starts, partial float4 units, partial
+    pieces and tiles), an empty tensor, k from 0 to n."""
+    rng = np.random.default_rng([31, seed])
+    sizes = list(RAGGED)
+    n = sum(sizes)
+    ks_steps = []
+    for step in range(3):
+        k = []
+        for s in sizes:
+            choice = rng.integers(0, 5)
+            k.append([0, 1, s, max(1, s // 1000) if s else 0,
+                      int(rng.integers(0, s + 1))][choice] if s else 0)
+        ks_steps.append(k)
+    kmax = [max(ks[t] for ks in ks_steps) for t in range(len(sizes))]
+    p = Pair(sizes, kmax)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    for step, k in enumerate(ks_steps):
+        g = (rng.laplace(0, 1e-2, n) * (rng.random(n) < 0.9)).astype(np.float32)
+        clip = [0.0, 0.5, 1e6][step]
+        got, (o_idx, o_val) = p.step(g, k, clip, tag=f"ragged s{step}")
+        compare_streams(gpu_streams(p, k), oracle_streams(sizes, k, o_idx, o_val),
+                        tag=f"ragged s{step}")
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_ties_and_zeros(path):
+    """Few distinct magnitudes (ties at the threshold everywhere), signed
+    zeros, an all-zero tensor, and k = n."""
+    rng = np.random.default_rng(32)
+    sizes = [200000, 70000, 5000, 131072]
+    n = sum(sizes)
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 0.5, -0.5, 0.25], np.float32)
+    p = Pair(sizes, sizes)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    for step, k in enumerate([[200, 70, 5000, 131], [199999, 0, 1, 131072],
+                              [1, 69999, 2500, 65536]]):
+        g = pool[rng.integers(0, pool.size, n)]
+        g[200000:270000] = 0.0 if step != 1 else -0.0
+        got, (o_idx, o_val) = p.step(g, k, 0.0, tag=f"ties s{step}")
+        compare_streams(gpu_streams(p, k), oracle_streams(sizes, k, o_idx, o_val),
+                        tag=f"ties s{step}")
+
+
+def test_both_paths_agree_and_window_is_used():
+    wl = W.scaled(W.get("flat1b"), 64)
+    k = ks_for(wl, 0)
+    g = W.gradient(wl, 0, 0)
+    res = []
+    for path in (0, 1):
+        p = Pair(list(wl.sizes), k)
+        p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+        got, _ = p.step(g, k, wl.clip, tag=f"paths p{path}")
+        nw, nd = p.learner.path_counts()
+        if path == 0:
+            assert nd == 0 and nw == len(wl.sizes), (nw, nd)
+        else:
+            assert nw == 0 and nd == len(wl.sizes), (nw, nd)
+        res.append(got)
+    assert np.array_equal(res[0].idx, res[1].idx)
+
+
+def test_determinism_repeat_bitwise():
+    wl = W.scaled(W.get("resnet50"), 16)
+    outs = []
+    for rep in range(2):
+        p = Pair(list(wl.sizes), ks_for(wl, 0))
+        for t in range(2):
+            got, _ = p.step(W.gradient(wl, 0, t), ks_for(wl, t), wl.clip,
+                            check_state=False, tag=f"det r{rep}")
+        outs.append((got.idx, f32_bits(got.val), p.learner.v.cpu().numpy().copy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(f32_bits(outs[0][2]), f32_bits(outs[1][2]))
+
+
+def test_checkpoint_resume_bitwise():
+    """The whole learner state is (u, v): 4 steps straight equal 2 steps,
+    a save/restore of u and v into a fresh state, then 2 more steps."""
+    import torch
+    wl = W.scaled(W.get("resnet50"), 32)
+    wl = W.Workload(wl.name, wl.cfg_id, wl.sizes, (Fraction(1, 1000),) * 4, 1,
+                    wl.clip, wl.momentum, wl.dist)
+    k = ks_for(wl, 0)
+    a = Pair(list(wl.sizes), k)
+    for t in range(4):
+        ga, _ = a.step(W.gradient(wl, 0, t), k, wl.clip, tag=f"ckpt a{t}")
+    b = Pair(list(wl.sizes), k)
+    for t in range(2):
+        b.step(W.gradient(wl, 0, t), k, wl.clip, tag=f"ckpt b{t}")
+    saved_u = b.learner.u.clone()
+    saved_v = b.learner.v.clone()
+    c = Pair(list(wl.sizes), k)
+    c.learner.u.copy_(saved_u)
+    c.learner.v.copy_(saved_v)
+    c.u, c.v = b.u.copy(), b.v.copy()
+    for t in range(2, 4):
+        gc, _ = c.step(W.gradient(wl, 0, t), k, wl.clip, tag=f"ckpt c{t}")
+    assert np.array_equal(ga.idx, gc.idx)
+    assert torch.equal(a.learner.v, c.learner.v)
+
+
+# ---------------------------------------------------------------- codec
+
+def test_encode_golden_gaps_on_gpu():
+    """The hand-derived streams of tests/golden/encode_cases.json, encoded
+    by the GPU from the golden indices."""
+    import torch
+    from conftest import load_golden
+    gold = load_golden("encode_cases.json")
+    for case in gold["cases"]:
+        n = case["n"]
+        idx = np.array(case["idx"], np.uint32)
+        val = np.array([int(h, 16) for h in case["val"]], np.uint32).view(np.float32)
+        k = [idx.size]
+        p = Pair([n], [max(idx.size, 1)])
+        ti = torch.from_numpy(idx.view(np.int32)).cuda()
+        tv = torch.from_numpy(val).cuda()
+        L = p.learner
+        L.idx[:idx.size].copy_(ti)
+        L.val[:idx.size].copy_(tv)
+        got = gpu_streams(p, k)[0]
+        want = oracle.encode(idx, val, cap=idx.size + n // 65536 + 1)
+        assert np.array_equal(got[0], want[0]), case["name"]
+        assert np.array_equal(f32_bits(got[1]), f32_bits(want[1])), case["name"]
+        runs_w = case.get("runs")
+        if runs_w is None:
+            runs_w = sum(([x] * c for x, c in case["runs_repeat"]), [])
+        assert got[0].tolist() == runs_w, case["name"]
+        assert L.status() == dgc.DGC_OK
+
+
+def test_decode_flags_corrupt_streams():
+    import torch
+    sizes = [10, 100000]
+    p = Pair(sizes, [3, 5])
+    L = p.learner
+    cap = L.cap
+    runs = torch.zeros(int(cap[-1]), dtype=torch.int16, device="cuda")
+    vals = torch.ones(int(cap[-1]), dtype=torch.float32, device="cuda")
+    # tensor 0: positions 3, 8, 14 -> the third passes the end (n = 10)
+    runs[0:3] = torch.tensor([3, 4, 5], dtype=torch.int16)
+    ent = torch.tensor([3, 0], dtype=torch.int64, device="cuda")
+    dense = torch.zeros(sum(sizes), dtype=torch.float32, device="cuda")
+    dgc.decode_accumulate(L, [(runs, vals, ent)], dense)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert L.status() == dgc.DGC_OK  # cleared by the read
+    d = dense.cpu().numpy()
+    assert d[3] == 1 and d[8] == 1 and d.sum() == 2
+    # an entry count above capacity adds nothing and is flagged
+    ent2 = torch.tensor([int(cap[1] - cap[0]) + 1, 0], dtype=torch.int64, device="cuda")
+    dense.zero_()
+    dgc.decode_accumulate(L, [(runs, vals, ent2)], dense)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert float(dense.abs().sum()) == 0.0
+
+
+def test_k_above_k_max_is_rejected():
+    import torch
+    p = Pair([1000], [5])
+    g = torch.zeros(1000, device="cuda")
+    with pytest.raises(dgc.DGCError):
+        p.learner.compress(g, [6], 0.0)
+    with pytest.raises(dgc.DGCError):
+        p.learner.compress(g[1:], [1], 0.0)  # misaligned gradient
