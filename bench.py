@@ -69,15 +69,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flat1b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-chunks", type=int, default=32)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="cycle the oracle over the sample until this long")
+    ap.add_argument("--grad-steps", type=int, default=0,
+                    help="generate only this many gradient steps and cycle "
+                         "over them (0: all of the workload's; for profiling)")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
     return ap.parse_args()
 
 
-def cpu_baseline(wl, host_samples, n_chunks):
-    """The oracle as it stands on the first n_chunks tensors of learner 0,
-    one call sequence per gradient step (compress + encode + decode)."""
+def cpu_baseline(wl, host_samples, n_chunks, seconds):
+    """The oracle as it stands on the first n_chunks tensors of learner 0:
+    compress + encode + decode per gradient step, cycling over the steps
+    (state carried along) until `seconds` have passed, at most 4 cycles."""
     import oracle
     sizes = np.array(wl.sizes[:n_chunks], np.int64)
     k = np.array([oracle.k_for_density(int(s), wl.densities[0].numerator,
@@ -89,20 +95,25 @@ def cpu_baseline(wl, host_samples, n_chunks):
     offs = np.concatenate([[0], np.cumsum(sizes)])
     koff = np.concatenate([[0], np.cumsum(k)])
     t0 = time.perf_counter()
-    for g in host_samples:
-        idx, val, _, _ = oracle.step(sizes, k, g, u, v, wl.momentum, wl.clip)
-        dense[:] = 0
-        for t in range(len(sizes)):
-            r, vv = oracle.encode(idx[koff[t]:koff[t + 1]], val[koff[t]:koff[t + 1]])
-            oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+    steps = 0
+    for cycle in range(4):
+        for g in host_samples:
+            idx, val, _, _ = oracle.step(sizes, k, g, u, v, wl.momentum, wl.clip)
+            dense[:] = 0
+            for t in range(len(sizes)):
+                r, vv = oracle.encode(idx[koff[t]:koff[t + 1]], val[koff[t]:koff[t + 1]])
+                oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
-    elems = n * len(host_samples)
+    elems = n * steps
     return {
         "value": round(elems / dt / 1e9, 4),
         "unit": "G elem/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"learner 0, {len(host_samples)} steps, first {n_chunks} of "
+        "sample": (f"learner 0, {steps} steps, first {n_chunks} of "
                    f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
                    "momentum, exact top-k, mask, encode, decode; "
                    f"{dt:.1f} s"),
@@ -133,7 +144,8 @@ def main():
     host_samples = []
     g_host = np.empty(n, np.float32)
     n_sample = sum(wl.sizes[:args.cpu_sample_chunks])
-    for t in range(wl.steps):
+    gsteps = args.grad_steps if args.grad_steps > 0 else wl.steps
+    for t in range(gsteps):
         for w in range(wl.learners):
             t0 = time.perf_counter()
             W.gradient(wl, w, t, out=g_host)
@@ -149,7 +161,7 @@ def main():
     dense = torch.zeros(n, dtype=torch.float32, device="cuda")
 
     def one_step(s):
-        t = s % wl.steps
+        t = s % gsteps
         k = ks[t]
         for w, L in enumerate(learners):
             L.compress(grads[(w, t)], k, wl.clip)
@@ -186,6 +198,10 @@ def main():
             cnt += b
         times[name] = (tot, cnt)
     path = [L.path_counts() for L in learners]
+    info = np.concatenate([L.select_info() for L in learners])
+    kk = np.array(ks[(args.warmup + args.steps - 1) % gsteps] * len(learners))
+    listed = info[:, 0] == 1
+    cand_ratio = info[listed, 2] / np.maximum(kk[listed], 1)
 
     elems = n * wl.learners * args.steps
     value = elems / elapsed / 1e9
@@ -241,12 +257,18 @@ def main():
             "compress_pipeline_frac_of_peak": round(
                 pipeline_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "compress_G_elem_per_s": round(n / (compress_ms * 1e-3) / 1e9, 2),
-            "select_path_window_dense": path[0],
+            "select_path_window_dense": [int(sum(p[0] for p in path)),
+                                         int(sum(p[1] for p in path))],
+            "overflow_tensors": int(info[:, 3].sum()),
+            "window_candidates_over_k": ([round(float(cand_ratio.min()), 3),
+                                          round(float(cand_ratio.max()), 3)]
+                                         if cand_ratio.size else None),
         },
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks)
+        out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks,
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -194,6 +194,18 @@ int dgc_get_status(dgc_state* st);
  */
 int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense);
 
+/*
+ * Per-tensor record of the last dgc_compress (waits for the stream):
+ * info (host int64[6 * n_tensors]) receives for each tensor
+ *   [0] path: 0 = k was 0, 1 = sample window, 2 = dense exact path
+ *   [1] candidate threshold key of the sample window (0xFFFFFFFF = none)
+ *   [2] candidates the element-wise pass found
+ *   [3] 1 if a piece found more candidates than its slots hold
+ *   [4] the k-th largest magnitude key T (bits of |v| with sign cleared)
+ *   [5] how many entries equal to T were sent (r)
+ */
+int dgc_get_select_info(dgc_state* st, int64_t* info);
+
 /* Set an option (DGC_OPT_*).  Returns DGC_OK or DGC_EINVAL. */
 int dgc_set_option(dgc_state* st, int32_t option, int64_t value);
 

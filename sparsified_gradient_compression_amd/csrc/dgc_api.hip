@@ -29,27 +29,36 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
     int32_t T = 0;
     std::vector<int64_t> sizes, kmax;
-    // tables uploaded at init (int64): o, pbase, tbase, abase, sbase,
-    // slines, ebase, etbase -- each T+1 long (slines padded)
-    std::vector<int64_t> o, pbase, tbase, abase, sbase, slines, ebase, etbase;
+    // tables uploaded at init (int64): o, pbase, tbase, obase, sbase,
+    // slines, ebase, etbase, slbase, pcap -- each T+1 long (padded)
+    std::vector<int64_t> o, pbase, tbase, obase, sbase, slines, ebase, etbase,
+        slbase, pcap;
     std::vector<uint32_t> pmap, smap, emap;
-    int64_t n = 0, P = 0, TT = 0, A = 0, S = 0, E = 0, ET = 0, NB = 0;
+    int64_t n = 0, P = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t tiles = 0;  // entries of each per-tile array
     // workspace byte offsets
     size_t off_tab = 0, off_pmap = 0, off_smap = 0, off_emap = 0, off_k = 0,
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
-           off_runb = 0, off_runc = 0, off_ord = 0, off_atiles = 0,
-           off_aoff = 0, off_amap = 0, off_arena = 0, off_olist = 0,
+           off_runc = 0, off_ord = 0, off_atiles = 0, off_aoff = 0,
+           off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            total = 0;
 };
 
-// Candidate arena capacity of one tensor: every element for small tensors,
-// else room for 8 k_max + 16384 candidates (the sample window aims at about
-// 2-4 k; more candidates than this send the tensor to the dense path).
-int64_t arena_cap(int64_t n, int64_t kmax) {
+// Candidate slots per 1024-element piece: all of them for small tensors
+// (which take every element as a candidate), else about six times the
+// pieces' share of k_max plus 24 -- the sample window aims at 2-4 k
+// candidates, so a piece overflows (sending its tensor to the dense path)
+// only with a negligible probability for unstructured data.
+int64_t piece_cap(int64_t n, int64_t kmax) {
+    if (n <= kSmallN) return kPiece;
+    return std::min<int64_t>(kPiece, cdiv(6 * kPiece * kmax, n) + 24);
+}
+
+// Capacity of a tensor's ordered candidate list.
+int64_t list_cap(int64_t n, int64_t kmax, int64_t slots) {
     if (n <= kSmallN) return n;
-    return std::min<int64_t>(n, 8 * kmax + 16384);
+    return std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384);
 }
 
 int64_t sample_lines(int64_t n) {
@@ -66,7 +75,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.o.assign(T + 1, 0);
     p.pbase.assign(T + 1, 0);
     p.tbase.assign(T + 1, 0);
-    p.abase.assign(T + 1, 0);
+    p.obase.assign(T + 1, 0);
+    p.slbase.assign(T + 1, 0);
+    p.pcap.assign(T + 1, 0);
     p.sbase.assign(T + 1, 0);
     p.slines.assign(T + 1, 0);
     p.ebase.assign(T + 1, 0);
@@ -75,9 +86,12 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         int64_t n = sizes[t], km = kmax[t];
         if (n < 0 || n >= (int64_t(1) << 32) || km < 0 || km > n) return DGC_EINVAL;
         p.o[t + 1] = p.o[t] + n;
-        p.pbase[t + 1] = p.pbase[t] + cdiv(n, kPiece);
+        const int64_t np_ = cdiv(n, kPiece);
+        p.pbase[t + 1] = p.pbase[t] + np_;
         p.tbase[t + 1] = p.tbase[t] + cdiv(n, kTile);
-        p.abase[t + 1] = p.abase[t] + arena_cap(n, km);
+        p.pcap[t] = piece_cap(n, km);
+        p.slbase[t + 1] = p.slbase[t] + np_ * p.pcap[t];
+        p.obase[t + 1] = p.obase[t] + list_cap(n, km, np_ * p.pcap[t]);
         p.slines[t] = sample_lines(n);
         p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
         p.ebase[t + 1] = p.ebase[t] + km + n / 65536;
@@ -86,7 +100,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.n = p.o[T];
     p.P = p.pbase[T];
     p.TT = p.tbase[T];
-    p.A = p.abase[T];
+    p.A = p.obase[T];
+    p.SL = p.slbase[T];
     p.S = p.sbase[T];
     p.E = p.ebase[T];
     p.ET = p.etbase[T];
@@ -110,7 +125,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         return at;
     };
     const size_t T1 = size_t(T) + 1;
-    p.off_tab = take(8 * T1 * sizeof(int64_t));
+    p.off_tab = take(10 * T1 * sizeof(int64_t));
     p.off_pmap = take(size_t(p.P) * 4);
     p.off_smap = take(size_t(p.S) * 4);
     p.off_emap = take(size_t(p.ET) * 4);
@@ -120,13 +135,12 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_sc = take(sizeof(Scalars));
     p.off_hist = take(size_t(T) * kHistBins * 4);
     p.off_shist = take(size_t(T) * kHistBins * 4);
-    p.off_runb = take(size_t(p.P) * 4);
     p.off_runc = take(size_t(p.P) * 4);
     p.off_ord = take(size_t(p.P) * 4);
     p.off_atiles = take(size_t(T) * 4);
     p.off_aoff = take(T1 * 4);
     p.off_amap = take(size_t(p.TT) * 4);
-    p.off_arena = take(size_t(p.A) * 8);
+    p.off_slots = take(size_t(p.SL) * 8);
     p.off_olist = take(size_t(p.A) * 8);
     p.off_ta = take(size_t(p.tiles) * 4);
     p.off_tb = take(size_t(p.tiles) * 4);
@@ -175,11 +189,11 @@ struct dgc_state {
     DevK K{};
     TensorState* ts = nullptr;
     Scalars* sc = nullptr;
-    uint32_t *hist = nullptr, *shist = nullptr, *run_base = nullptr,
+    uint32_t *hist = nullptr, *shist = nullptr,
              *run_cnt = nullptr, *ord_off = nullptr, *atiles = nullptr,
              *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
              *tc = nullptr;
-    uint2 *arena = nullptr, *olist = nullptr;
+    uint2 *slots = nullptr, *olist = nullptr;
     uint64_t* t64 = nullptr;
     double* partial = nullptr;
 };
@@ -345,21 +359,24 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     const int32_t T = p.T;
     const size_t T1 = size_t(T) + 1;
     // layout tables
-    std::vector<int64_t> tab(8 * T1, 0);
-    const std::vector<int64_t>* src[8] = {&p.o, &p.pbase, &p.tbase, &p.abase,
-                                          &p.sbase, &p.slines, &p.ebase, &p.etbase};
-    for (int i = 0; i < 8; ++i)
+    std::vector<int64_t> tab(10 * T1, 0);
+    const std::vector<int64_t>* src[10] = {&p.o,      &p.pbase, &p.tbase,  &p.obase,
+                                           &p.sbase,  &p.slines, &p.ebase, &p.etbase,
+                                           &p.slbase, &p.pcap};
+    for (int i = 0; i < 10; ++i)
         std::copy(src[i]->begin(), src[i]->end(), tab.begin() + i * T1);
     int64_t* dtab = reinterpret_cast<int64_t*>(ws + p.off_tab);
     st->L.T = T;
     st->L.o = dtab;
     st->L.pbase = dtab + T1;
     st->L.tbase = dtab + 2 * T1;
-    st->L.abase = dtab + 3 * T1;
+    st->L.obase = dtab + 3 * T1;
     st->L.sbase = dtab + 4 * T1;
     st->L.slines = dtab + 5 * T1;
     st->L.ebase = dtab + 6 * T1;
     st->L.etbase = dtab + 7 * T1;
+    st->L.slbase = dtab + 8 * T1;
+    st->L.pcap = dtab + 9 * T1;
     st->L.pmap = reinterpret_cast<uint32_t*>(ws + p.off_pmap);
     st->L.smap = reinterpret_cast<uint32_t*>(ws + p.off_smap);
     st->L.emap = reinterpret_cast<uint32_t*>(ws + p.off_emap);
@@ -372,13 +389,12 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->sc = reinterpret_cast<Scalars*>(ws + p.off_sc);
     st->hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
     st->shist = reinterpret_cast<uint32_t*>(ws + p.off_shist);
-    st->run_base = reinterpret_cast<uint32_t*>(ws + p.off_runb);
     st->run_cnt = reinterpret_cast<uint32_t*>(ws + p.off_runc);
     st->ord_off = reinterpret_cast<uint32_t*>(ws + p.off_ord);
     st->atiles = reinterpret_cast<uint32_t*>(ws + p.off_atiles);
     st->aoff = reinterpret_cast<uint32_t*>(ws + p.off_aoff);
     st->amap = reinterpret_cast<uint32_t*>(ws + p.off_amap);
-    st->arena = reinterpret_cast<uint2*>(ws + p.off_arena);
+    st->slots = reinterpret_cast<uint2*>(ws + p.off_slots);
     st->olist = reinterpret_cast<uint2*>(ws + p.off_olist);
     st->ta = reinterpret_cast<uint32_t*>(ws + p.off_ta);
     st->tb = reinterpret_cast<uint32_t*>(ws + p.off_tb);
@@ -459,30 +475,30 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     k_window<<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts, force_dense);
     DGC_LAUNCH_CHECK();
     if (p.P > 0) {
-        int fb = st->fused_blocks > 0 ? st->fused_blocks : st->num_cus * 8;
+        // one piece per wave unless a grid cap is set (then waves loop)
+        int64_t fb = st->fused_blocks > 0 ? st->fused_blocks : cdiv(p.P, kWavesPerBlock);
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
-            g, st->u, st->v, st->L, st->ts, st->sc, st->m, st->arena, st->run_base,
-            st->run_cnt, p.P);
+            g, st->u, st->v, st->L, st->ts, st->sc, st->m, st->slots, st->run_cnt, p.P);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     k_piece_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->run_cnt,
                                            st->ord_off, st->atiles);
+    if (p.P > 0)
+        k_gather<<<int(cdiv(p.P, kBlock)), kBlock, 0, stream>>>(
+            st->L, st->ts, st->slots, st->run_cnt, st->ord_off, st->olist, p.P);
     k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
     k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
     DGC_LAUNCH_CHECK();
     if (K > 0) {
         const int hg = grid_for(p.TT, pg);
-        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
-                                             st->run_base, st->ord_off, st->amap,
+        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
                                              st->aoff, st->hist);
         k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
-                                             st->run_base, st->ord_off, st->amap,
+        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
                                              st->aoff, st->hist);
         k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->arena, st->olist,
-                                             st->run_base, st->ord_off, st->amap,
+        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
                                              st->aoff, st->hist);
         k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
         DGC_LAUNCH_CHECK();
@@ -599,6 +615,25 @@ int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense) {
     }
     if (n_window) *n_window = nw;
     if (n_dense) *n_dense = nd;
+    return DGC_OK;
+}
+
+int dgc_get_select_info(dgc_state* st, int64_t* info) {
+    if (!st || !info) return DGC_EINVAL;
+    if (hipStreamSynchronize(st->last_stream) != hipSuccess) return DGC_EHIP;
+    std::vector<TensorState> h(size_t(st->plan.T));
+    if (hipMemcpy(h.data(), st->ts, h.size() * sizeof(TensorState),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return DGC_EHIP;
+    for (size_t t = 0; t < h.size(); ++t) {
+        int64_t* r = info + 6 * t;
+        r[0] = h[t].mode;
+        r[1] = h[t].lo_key;
+        r[2] = h[t].total;
+        r[3] = h[t].overflow;
+        r[4] = h[t].prefix;
+        r[5] = h[t].krem;
+    }
     return DGC_OK;
 }
 

@@ -37,8 +37,8 @@ constexpr int64_t kSmallN = 65536;
 constexpr int64_t kMinSampleLines = 512;
 constexpr int64_t kLinesPerSampleBlock = 64;
 
-// Binary64 norm: one workgroup per 2^20 elements, fixed order.
-constexpr int64_t kNormChunk = int64_t(1) << 20;
+// Binary64 norm: one workgroup per 2^18 elements, fixed order.
+constexpr int64_t kNormChunk = int64_t(1) << 18;
 
 // Per-tensor selection modes (decided after the element-wise pass).
 constexpr uint32_t kModeSkip = 0;   // k = 0
@@ -55,13 +55,14 @@ constexpr uint32_t kErrInternal = 3;
 
 // Per-tensor selection state, one per tensor in the workspace.
 struct TensorState {
-    uint32_t lo_key;  // candidate threshold from the sample window
-    uint32_t cursor;  // candidates reserved in the arena (may pass capacity)
-    uint32_t mode;    // kMode*
-    uint32_t len;     // items of the select source (list length or n_t)
-    uint32_t prefix;  // radix-select prefix; the threshold key T at the end
-    uint32_t krem;    // k still to place within the prefix; r at the end
-    uint32_t pad0, pad1;
+    uint32_t lo_key;    // candidate threshold from the sample window
+    uint32_t total;     // candidates found by the element-wise pass
+    uint32_t mode;      // kMode*
+    uint32_t len;       // items of the select source (list length or n_t)
+    uint32_t prefix;    // radix-select prefix; the threshold key T at the end
+    uint32_t krem;      // k still to place within the prefix; r at the end
+    uint32_t overflow;  // some piece found more candidates than its slots
+    uint32_t pad;
 };
 
 // Per-call scalars.
@@ -78,7 +79,9 @@ struct DevLayout {
     const int64_t* o;       // [T+1] element offsets
     const int64_t* pbase;   // [T+1] first piece of each tensor
     const int64_t* tbase;   // [T+1] first select/emit tile (ceil(n_t/kTile))
-    const int64_t* abase;   // [T+1] candidate arena offsets (capacity)
+    const int64_t* obase;   // [T+1] ordered candidate list offsets (capacity)
+    const int64_t* slbase;  // [T+1] candidate slot offsets (pieces x pcap)
+    const int64_t* pcap;    // [T] candidate slots per piece
     const int64_t* sbase;   // [T+1] first sample block
     const int64_t* slines;  // [T] sampled lines (0 = no sampling)
     const int64_t* ebase;   // [T+1] encoded stream capacity offsets

@@ -10,11 +10,12 @@
 //   sample/window            per tensor, keys of the would-be v on sampled
 //                            32-element lines -> a candidate threshold lo
 //   fused                    u, v update (20 B/elem); keys >= lo are
-//                            written, index-ordered per 1024-element piece,
-//                            into the tensor's candidate arena
-//   piece_scan               per tensor: choose the source (candidates when
-//                            they are complete and at least k, else the
-//                            whole tensor) and the order of the pieces
+//                            written, index-ordered, into the fixed slots of
+//                            their 1024-element piece (no atomics)
+//   piece_scan/gather        per tensor: choose the source (candidates when
+//                            none overflowed and there are at least k, else
+//                            the whole tensor); concatenate the pieces' runs
+//                            into one index-ordered candidate list
 //   hist<D>/resolve<D>       three radix digits (11,10,10 bits) -> the k-th
 //                            largest key T and the tie quota r
 //   emit_count/scan/write    index-ordered output of {key > T} plus the
@@ -223,14 +224,13 @@ __global__ __launch_bounds__(kBlock) void k_window(
 // A wave owns one piece (<= 1024 elements, one tensor).  It loads g, u, v
 // as float4 (64 lanes x 4 units), updates u and v in registers and stores
 // them, then writes the piece's candidates (key >= lo) as one run in index
-// order: ballot + popcount give each candidate its rank, one atomicAdd on
-// the tensor's cursor reserves the run.
+// order into the piece's own pcap slots: ballot + popcount give each
+// candidate its rank; no atomics, so the layout is the same every run.
 template <bool kAligned>
 __device__ __forceinline__ void fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     int64_t e0, int64_t e1, int64_t o, float s, float m, uint32_t lo,
-    uint32_t* cursor, uint64_t cap, uint2* __restrict__ arena,
-    uint32_t* __restrict__ run_base, uint32_t* __restrict__ run_cnt,
+    uint32_t pcap, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
     int64_t p) {
     const int lane = lane_id();
     float vn[4][4];
@@ -330,24 +330,19 @@ __device__ __forceinline__ void fused_piece(
             }
         }
     }
-    uint32_t base = 0;
-    if (total) {
-        if (lane == 0) base = atomicAdd(cursor, total);
-        base = __shfl(base, 0, kWave);
-    }
-    if (lane == 0) { run_base[p] = base; run_cnt[p] = total; }
+    // The piece's run goes to its own pcap slots; a count above pcap marks
+    // the overflow (the tensor then takes the dense path).
+    if (lane == 0) run_cnt[p] = total;
     if (total) {
         const int64_t unit0 = e0 >> 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (f[i][c]) {
-                    uint64_t slot = uint64_t(base) + rank[i][c];
+                if (f[i][c] && rank[i][c] < pcap) {
                     int64_t el = kAligned ? (((unit0 + i * kWave + lane) << 2) + c)
                                           : (e0 + int64_t(i * 4 + c) * kWave + lane);
-                    if (slot < cap)
-                        arena[slot] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
+                    slots[rank[i][c]] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
                 }
     }
 }
@@ -355,33 +350,34 @@ __device__ __forceinline__ void fused_piece(
 __global__ __launch_bounds__(kBlock) void k_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     DevLayout L, TensorState* __restrict__ ts, const Scalars* __restrict__ sc,
-    float m, uint2* __restrict__ arena, uint32_t* __restrict__ run_base,
-    uint32_t* __restrict__ run_cnt, int64_t n_pieces) {
+    float m, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
+    int64_t n_pieces) {
     const float s = sc->scale;
     const int64_t w0 = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
     const int64_t nw = (int64_t(gridDim.x) * kBlock) >> 6;
     for (int64_t p = w0; p < n_pieces; p += nw) {
         const int t = wave_uniform(int(L.pmap[p]));
         const int64_t o = L.o[t];
-        const int64_t e0 = o + ((p - L.pbase[t]) << kPieceShift);
+        const int64_t j = p - L.pbase[t];
+        const int64_t e0 = o + (j << kPieceShift);
         const int64_t e1 = min(e0 + kPiece, L.o[t + 1]);
         const uint32_t lo = ts[t].lo_key;
-        const int64_t ab = L.abase[t];
-        const uint64_t cap = uint64_t(L.abase[t + 1] - ab);
+        const uint32_t pcap = uint32_t(L.pcap[t]);
+        uint2* sl = slots + L.slbase[t] + j * pcap;
         if ((e0 & 3) == 0)
-            fused_piece<true>(g, u, v, e0, e1, o, s, m, lo, &ts[t].cursor, cap,
-                              arena + ab, run_base, run_cnt, p);
+            fused_piece<true>(g, u, v, e0, e1, o, s, m, lo, pcap, sl, run_cnt, p);
         else
-            fused_piece<false>(g, u, v, e0, e1, o, s, m, lo, &ts[t].cursor, cap,
-                               arena + ab, run_base, run_cnt, p);
+            fused_piece<false>(g, u, v, e0, e1, o, s, m, lo, pcap, sl, run_cnt, p);
     }
 }
 
 // ---------------------------------------------------------------- source
 
-// One block per tensor: decide the selection source and, for the candidate
-// list, the exclusive scan of the pieces' run lengths (their index order).
-// Also counts the source's 4096-item tiles for the active-tile map.
+// One block per tensor: scan the pieces' candidate counts (their order in
+// the list), then choose the selection source: the candidate list when no
+// piece overflowed its slots and there are at least k candidates, else the
+// whole tensor.  Also counts the source's 4096-item tiles for the
+// active-tile map.
 __global__ __launch_bounds__(kBlock) void k_piece_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
     const uint32_t* __restrict__ run_cnt, uint32_t* __restrict__ ord_off,
@@ -390,31 +386,55 @@ __global__ __launch_bounds__(kBlock) void k_piece_scan(
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t k = K.k[t];
-    const uint32_t cur = ts[t].cursor;
-    const uint64_t cap = uint64_t(L.abase[t + 1] - L.abase[t]);
+    const uint32_t pcap = uint32_t(L.pcap[t]);
+    uint32_t carry = 0;
+    int over = 0;
+    if (k > 0) {
+        const int64_t p0 = L.pbase[t], p1 = L.pbase[t + 1];
+        for (int64_t base = p0; base < p1; base += kBlock) {
+            int64_t p = base + threadIdx.x;
+            uint32_t c = p < p1 ? run_cnt[p] : 0;
+            over |= c > pcap;
+            uint32_t tot;
+            uint32_t ex = block_exclusive_scan(c, lds, tot);
+            if (p < p1) ord_off[p] = carry + ex;
+            carry += tot;
+        }
+    }
+    over = __syncthreads_or(over);
+    const uint64_t cap = uint64_t(L.obase[t + 1] - L.obase[t]);
     uint32_t mode;
     if (k <= 0) mode = kModeSkip;
-    else if (uint64_t(cur) > cap || int64_t(cur) < k) mode = kModeDense;
+    else if (over || uint64_t(carry) > cap || int64_t(carry) < k) mode = kModeDense;
     else mode = kModeList;
-    const int64_t len = mode == kModeList ? int64_t(cur) : nt;
+    const int64_t len = mode == kModeList ? int64_t(carry) : nt;
     if (threadIdx.x == 0) {
+        ts[t].total = carry;
+        ts[t].overflow = uint32_t(over);
         ts[t].mode = mode;
         ts[t].len = uint32_t(len);
         ts[t].prefix = 0;
         ts[t].krem = uint32_t(k > 0 ? k : 0);
         atiles[t] = mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift);
     }
-    if (mode != kModeList) return;
-    const int64_t p0 = L.pbase[t], p1 = L.pbase[t + 1];
-    uint32_t carry = 0;
-    for (int64_t base = p0; base < p1; base += kBlock) {
-        int64_t p = base + threadIdx.x;
-        uint32_t c = p < p1 ? run_cnt[p] : 0;
-        uint32_t tot;
-        uint32_t ex = block_exclusive_scan(c, lds, tot);
-        if (p < p1) ord_off[p] = carry + ex;
-        carry += tot;
-    }
+}
+
+// One thread per piece: copy the piece's candidates from its slots to its
+// place in the tensor's index-ordered list.
+__global__ __launch_bounds__(kBlock) void k_gather(
+    DevLayout L, const TensorState* __restrict__ ts,
+    const uint2* __restrict__ slots, const uint32_t* __restrict__ run_cnt,
+    const uint32_t* __restrict__ ord_off, uint2* __restrict__ olist,
+    int64_t n_pieces) {
+    const int64_t p = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (p >= n_pieces) return;
+    const int t = int(L.pmap[p]);
+    if (ts[t].mode != kModeList) return;
+    const uint32_t cnt = run_cnt[p];
+    const int64_t pcap = L.pcap[t];
+    const uint2* src = slots + L.slbase[t] + (p - L.pbase[t]) * pcap;
+    uint2* dst = olist + L.obase[t] + ord_off[p];
+    for (uint32_t j = 0; j < cnt; ++j) dst[j] = src[j];
 }
 
 // One block: exclusive scan of the active tile counts -> aoff[T+1].
@@ -464,15 +484,13 @@ __device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
 // tensor's source (candidate list or whole tensor), clipped to len.
 
 // Histogram of digit D over the keys that match the prefix found so far.
-// Workgroups stride over the active tiles.  In the first pass the
-// candidate list is also put into index order: arena -> olist.
+// Workgroups stride over the active tiles.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_hist(
     DevLayout L, const TensorState* __restrict__ ts,
-    const float* __restrict__ v, const uint2* __restrict__ arena,
-    uint2* __restrict__ olist, const uint32_t* __restrict__ run_base,
-    const uint32_t* __restrict__ ord_off, const uint32_t* __restrict__ amap,
-    const uint32_t* __restrict__ aoff, uint32_t* __restrict__ hist) {
+    const float* __restrict__ v, const uint2* __restrict__ olist,
+    const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
+    uint32_t* __restrict__ hist) {
     constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
     constexpr uint32_t dmask = (1u << bits) - 1;
     __shared__ uint32_t h[kHistBins];
@@ -499,18 +517,11 @@ __global__ __launch_bounds__(kBlock) void k_hist(
                     atomicAdd(&h[(key >> shift) & dmask], 1u);
             }
         } else {
-            const int64_t ab = L.abase[t];
-            const uint2* src = (D == 0 ? arena : olist) + ab;
+            const uint2* src = olist + L.obase[t];
             for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-                uint2 e = src[i];
-                uint32_t key = e.y & 0x7FFFFFFFu;
+                uint32_t key = src[i].y & 0x7FFFFFFFu;
                 if (D == 0 || (key >> (shift + bits)) == prefix)
                     atomicAdd(&h[(key >> shift) & dmask], 1u);
-                if (D == 0) {
-                    int64_t p = L.pbase[t] + (e.x >> kPieceShift);
-                    uint32_t pos = ord_off[p] + (uint32_t(i) - run_base[p]);
-                    olist[ab + pos] = e;
-                }
             }
         }
     }
@@ -602,7 +613,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
         const int64_t i0 = int64_t(a - aoff[t]) * kTile;
         const uint32_t T = ts[t].prefix;
         const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
-        uint32_t cnt = count_items(mode, v + L.o[t], olist + L.abase[t], s0, len, T);
+        uint32_t cnt = count_items(mode, v + L.o[t], olist + L.obase[t], s0, len, T);
         uint32_t tot;
         block_exclusive_scan(cnt, lds, tot);
         if (threadIdx.x == 0) tile_cnt[a] = tot;
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
         const uint32_t T = ts[t].prefix, r = ts[t].krem;
         const int64_t o = L.o[t];
         float* vt_ = v + o;
-        const uint2* ol = olist + L.abase[t];
+        const uint2* ol = olist + L.obase[t];
         const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
         uint32_t cnt = count_items(mode, vt_, ol, s0, len, T);
         uint32_t tot;

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.dgc_get_status.restype = ctypes.c_int
     L.dgc_get_path_counts.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.dgc_get_path_counts.restype = ctypes.c_int
+    L.dgc_get_select_info.argtypes = [P, P]
+    L.dgc_get_select_info.restype = ctypes.c_int
     L.dgc_set_option.argtypes = [P, i32, i64]
     L.dgc_set_option.restype = ctypes.c_int
     L.dgc_get_kernel_time.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double),
@@ -192,6 +194,13 @@ def dgc_get_path_counts(st) -> Tuple[int, int]:
     return int(nw.value), int(nd.value)
 
 
+def dgc_get_select_info(st, n_tensors: int) -> np.ndarray:
+    """[n_tensors, 6] int64: path, window key, candidates, overflow, T, r."""
+    out = np.zeros((n_tensors, 6), np.int64)
+    _check(lib().dgc_get_select_info(st, _hp(out)), "dgc_get_select_info")
+    return out
+
+
 def dgc_set_option(st, option: int, value: int):
     _check(lib().dgc_set_option(st, int(option), int(value)), "dgc_set_option")
 
@@ -267,6 +276,9 @@ class Learner:
 
     def path_counts(self) -> Tuple[int, int]:
         return dgc_get_path_counts(self.state)
+
+    def select_info(self) -> np.ndarray:
+        return dgc_get_select_info(self.state, self.T)
 
     def kernel_time(self, timer: int) -> Tuple[float, int]:
         return dgc_get_kernel_time(self.state, timer)
