@@ -468,11 +468,16 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     }
     DGC_LAUNCH_CHECK();
     const int force_dense = st->select_path == 1;
+    if (p.S > 0 && !force_dense)
+        k_sample<0><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
+                                                     st->ts, st->m, st->shist);
+    k_window<0><<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts, force_dense);
     if (p.S > 0 && !force_dense) {
-        k_sample<<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
-                                                  st->m, st->shist);
+        k_sample<1><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
+                                                     st->ts, st->m, st->shist);
+        k_window<1><<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts,
+                                              force_dense);
     }
-    k_window<<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts, force_dense);
     DGC_LAUNCH_CHECK();
     if (p.P > 0) {
         // one piece per wave unless a grid cap is set (then waves loop)

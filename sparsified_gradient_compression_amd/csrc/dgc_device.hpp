@@ -62,7 +62,10 @@ struct TensorState {
     uint32_t prefix;    // radix-select prefix; the threshold key T at the end
     uint32_t krem;      // k still to place within the prefix; r at the end
     uint32_t overflow;  // some piece found more candidates than its slots
-    uint32_t pad;
+    uint32_t wbin;      // sample window: chosen top-11-bit bin (or kNoKey)
+    uint32_t wabove;    // sample window: samples above wbin
+    uint32_t wj;        // sample window: rank j of the targeted sample
+    uint32_t pad[4];
 };
 
 // Per-call scalars.

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kBlock) void k_prep(TensorState* __restrict__ ts,
          t += gridDim.x * kBlock) {
         TensorState s = {};
         s.lo_key = kNoKey;
+        s.wbin = kNoKey;
         ts[t] = s;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0 && !clip_on) {
@@ -126,19 +127,24 @@ __global__ void k_copy_scalars(const Scalars* __restrict__ sc,
 // ---------------------------------------------------------------- sample
 
 // Keys of the would-be v on sampled lines.  Block b belongs to one tensor
-// (sbase); it visits kLinesPerSampleBlock of the tensor's sampled lines, one
+// (smap); it visits kLinesPerSampleBlock of the tensor's sampled lines, one
 // 32-lane group per line.  Sampled line j lies at a hashed offset inside
 // the j-th of slines equal strides, so sampling does not alias with the
-// tensor's row structure.
+// tensor's row structure.  Level 0 histograms the top 11 key bits; level 1
+// revisits the same lines and histograms the next 10 bits of the keys whose
+// top 11 bits equal the bin chosen by level 0.
+template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_sample(
     const float* __restrict__ g, const float* __restrict__ u,
     const float* __restrict__ v, DevLayout L, const Scalars* __restrict__ sc,
-    float m, uint32_t* __restrict__ shist) {
+    const TensorState* __restrict__ ts, float m, uint32_t* __restrict__ shist) {
     __shared__ uint32_t h[kBins0];
     for (int b = threadIdx.x; b < kBins0; b += kBlock) h[b] = 0;
     __syncthreads();
     const int64_t sb = blockIdx.x;
     const int t = int(L.smap[sb]);
+    const uint32_t wbin = LEVEL == 1 ? ts[t].wbin : 0u;
+    if (LEVEL == 1 && wbin == kNoKey) return;  // uniform: window already set
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t lines = (nt + kLine - 1) / kLine;
     const int64_t ls = L.slines[t];
@@ -154,7 +160,9 @@ __global__ __launch_bounds__(kBlock) void k_sample(
         if (e < nt) {
             float uu = u[o + e], vv = v[o + e];
             momentum_update(g[o + e], s, m, uu, vv);
-            atomicAdd(&h[mag_key(vv) >> 20], 1u);
+            uint32_t key = mag_key(vv);
+            if (LEVEL == 0) atomicAdd(&h[key >> 20], 1u);
+            else if ((key >> 20) == wbin) atomicAdd(&h[(key >> 10) & 1023u], 1u);
         }
     }
     __syncthreads();
@@ -163,58 +171,77 @@ __global__ __launch_bounds__(kBlock) void k_sample(
         if (h[b]) atomicAdd(&row[b], h[b]);
 }
 
-// One block per tensor: choose the candidate threshold lo.  With S sampled
-// keys and mu = S*k/n expected above the true k-th key, lo is the lower
-// edge of the top-digit bin that holds the j-th largest sampled key,
-// j = ceil(mu + 6 sqrt(mu) + 8).  Small tensors take every element
-// (lo = 0); k = 0 takes none.
+// One block per tensor: place the candidate threshold lo just below the
+// j-th largest sampled key, j = ceil(mu + 6 sqrt(mu) + 8) where mu = S*k/n
+// is how many of the S samples the true top k should hold.  Level 0 finds
+// the top-11-bit bin holding the j-th key (wbin) and how many samples lie
+// above it (wabove); level 1 finds the 10-bit sub-bin inside it, and lo is
+// that sub-bin's lower edge.  Small tensors take every element (lo = 0);
+// k = 0 takes none.  Clears the histogram row for the next use.
+template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_window(
     DevLayout L, DevK K, uint32_t* __restrict__ shist,
     TensorState* __restrict__ ts, int force_dense) {
+    constexpr int bins = LEVEL == 0 ? kBins0 : 1024;
+    constexpr int per = bins / kBlock;
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t k = K.k[t];
     uint32_t* row = shist + int64_t(t) * kHistBins;
-    constexpr int per = kBins0 / kBlock;  // 8 bins per thread, from the top
+    if (LEVEL == 1 && ts[t].wbin == kNoKey) return;  // decided at level 0
     uint32_t c[per];
     uint32_t mine = 0;
 #pragma unroll
     for (int q = 0; q < per; ++q) {
-        int b = kBins0 - 1 - (threadIdx.x * per + q);
-        c[q] = row[b];
+        c[q] = row[bins - 1 - (threadIdx.x * per + q)];
         mine += c[q];
     }
     uint32_t total;
     uint32_t above = block_exclusive_scan(mine, lds, total);
-    // leave the row zeroed for the next step
 #pragma unroll
-    for (int q = 0; q < per; ++q) row[kBins0 - 1 - (threadIdx.x * per + q)] = 0;
-    // Exactly one thread writes lo_key (k_prep left it at kNoKey, which
-    // sends the tensor to the dense path should no bin qualify).
-    if (k <= 0 || force_dense) {
-        if (threadIdx.x == 0) ts[t].lo_key = kNoKey;
-        return;
-    }
-    if (L.slines[t] == 0) {
-        if (threadIdx.x == 0) ts[t].lo_key = 0;
-        return;
-    }
-    const double mu = double(total) * double(k) / double(nt);
-    const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
-    if (jd > double(total)) {
-        if (threadIdx.x == 0) ts[t].lo_key = 0;
-        return;
-    }
-    const uint32_t j = uint32_t(jd);
-    uint32_t run = above;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        if (run < j && j <= run + c[q]) {
-            int b = kBins0 - 1 - (threadIdx.x * per + q);
-            ts[t].lo_key = uint32_t(b) << 20;
+    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
+    if (LEVEL == 0) {
+        // Exactly one thread writes the decision (k_prep left lo_key at
+        // kNoKey, which sends the tensor to the dense path should no bin
+        // qualify).
+        if (k <= 0 || force_dense || L.slines[t] == 0) {
+            if (threadIdx.x == 0) {
+                ts[t].lo_key = (k <= 0 || force_dense) ? kNoKey : 0u;
+                ts[t].wbin = kNoKey;
+            }
+            return;
         }
-        run += c[q];
+        const double mu = double(total) * double(k) / double(nt);
+        const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
+        if (jd > double(total)) {
+            if (threadIdx.x == 0) { ts[t].lo_key = 0; ts[t].wbin = kNoKey; }
+            return;
+        }
+        const uint32_t j = uint32_t(jd);
+        uint32_t run = above;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            if (run < j && j <= run + c[q]) {
+                ts[t].wbin = uint32_t(kBins0 - 1 - (threadIdx.x * per + q));
+                ts[t].wabove = run;
+                ts[t].wj = j;
+            }
+            run += c[q];
+        }
+    } else {
+        __syncthreads();  // every thread has read wbin before it may change
+        const uint32_t jr = ts[t].wj - ts[t].wabove;  // rank inside wbin
+        const uint32_t wbin = ts[t].wbin;
+        uint32_t run = above;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            if (run < jr && jr <= run + c[q]) {
+                uint32_t b2 = uint32_t(bins - 1 - (threadIdx.x * per + q));
+                ts[t].lo_key = (wbin << 20) | (b2 << 10);
+            }
+            run += c[q];
+        }
     }
 }
 
