@@ -33,11 +33,12 @@ struct Plan {
     // slines, ebase, etbase, slbase, pcap -- each T+1 long (padded)
     std::vector<int64_t> o, pbase, tbase, obase, sbase, slines, ebase, etbase,
         slbase, pcap;
-    std::vector<uint32_t> pmap, smap, emap;
+    std::vector<PieceDesc> pdesc;
+    std::vector<uint32_t> smap, emap;
     int64_t n = 0, P = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t tiles = 0;  // entries of each per-tile array
     // workspace byte offsets
-    size_t off_tab = 0, off_pmap = 0, off_smap = 0, off_emap = 0, off_k = 0,
+    size_t off_tab = 0, off_pdesc = 0, off_smap = 0, off_emap = 0, off_k = 0,
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
            off_runc = 0, off_ord = 0, off_atiles = 0, off_aoff = 0,
            off_amap = 0, off_slots = 0, off_olist = 0,
@@ -109,11 +110,16 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     if (p.P >= (int64_t(1) << 32) || p.TT >= (int64_t(1) << 32)) return DGC_EINVAL;
     // tiles over k never exceed tiles over n, so TT also bounds encode tiles
     p.tiles = std::max<int64_t>(std::max<int64_t>(p.TT, p.ET), 1);
-    p.pmap.resize(size_t(p.P));
+    p.pdesc.resize(size_t(p.P));
     p.smap.resize(size_t(p.S));
     p.emap.resize(size_t(p.ET));
     for (int32_t t = 0; t < T; ++t) {
-        for (int64_t i = p.pbase[t]; i < p.pbase[t + 1]; ++i) p.pmap[size_t(i)] = uint32_t(t);
+        for (int64_t i = p.pbase[t]; i < p.pbase[t + 1]; ++i) {
+            PieceDesc& d = p.pdesc[size_t(i)];
+            d.start = p.o[t] + (i - p.pbase[t]) * kPiece;
+            d.tensor = uint32_t(t);
+            d.len = uint32_t(std::min<int64_t>(kPiece, p.o[t + 1] - d.start));
+        }
         for (int64_t i = p.sbase[t]; i < p.sbase[t + 1]; ++i) p.smap[size_t(i)] = uint32_t(t);
         for (int64_t i = p.etbase[t]; i < p.etbase[t + 1]; ++i) p.emap[size_t(i)] = uint32_t(t);
     }
@@ -126,7 +132,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     };
     const size_t T1 = size_t(T) + 1;
     p.off_tab = take(10 * T1 * sizeof(int64_t));
-    p.off_pmap = take(size_t(p.P) * 4);
+    p.off_pdesc = take(size_t(p.P) * sizeof(PieceDesc));
     p.off_smap = take(size_t(p.S) * 4);
     p.off_emap = take(size_t(p.ET) * 4);
     p.off_k = take((3 * T1) * sizeof(int64_t));
@@ -377,7 +383,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->L.etbase = dtab + 7 * T1;
     st->L.slbase = dtab + 8 * T1;
     st->L.pcap = dtab + 9 * T1;
-    st->L.pmap = reinterpret_cast<uint32_t*>(ws + p.off_pmap);
+    st->L.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_pdesc);
     st->L.smap = reinterpret_cast<uint32_t*>(ws + p.off_smap);
     st->L.emap = reinterpret_cast<uint32_t*>(ws + p.off_emap);
     int64_t* dk = reinterpret_cast<int64_t*>(ws + p.off_k);
@@ -405,7 +411,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     bool ok = true;
     ok = ok && hipMemcpyAsync(dtab, tab.data(), tab.size() * 8,
                               hipMemcpyHostToDevice, stream) == hipSuccess;
-    if (p.P) ok = ok && hipMemcpyAsync(ws + p.off_pmap, p.pmap.data(), size_t(p.P) * 4,
+    if (p.P) ok = ok && hipMemcpyAsync(ws + p.off_pdesc, p.pdesc.data(),
+                                       size_t(p.P) * sizeof(PieceDesc),
                                        hipMemcpyHostToDevice, stream) == hipSuccess;
     if (p.S) ok = ok && hipMemcpyAsync(ws + p.off_smap, p.smap.data(), size_t(p.S) * 4,
                                        hipMemcpyHostToDevice, stream) == hipSuccess;

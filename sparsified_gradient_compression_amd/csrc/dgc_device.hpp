@@ -76,6 +76,14 @@ struct Scalars {
     uint32_t pad[12];
 };
 
+// One 1024-element piece of the element-wise pass: global start, tensor,
+// length (16 bytes, one load).
+struct PieceDesc {
+    int64_t start;
+    uint32_t tensor;
+    uint32_t len;
+};
+
 // Layout tables (device pointers into the workspace), passed by value.
 struct DevLayout {
     int32_t T;
@@ -89,7 +97,7 @@ struct DevLayout {
     const int64_t* slines;  // [T] sampled lines (0 = no sampling)
     const int64_t* ebase;   // [T+1] encoded stream capacity offsets
     const int64_t* etbase;  // [T+1] tiles over encoded capacity
-    const uint32_t* pmap;   // [pieces] tensor of each piece
+    const PieceDesc* pdesc; // [pieces] start, tensor and length of each piece
     const uint32_t* smap;   // [sample blocks] tensor of each sample block
     const uint32_t* emap;   // [capacity tiles] tensor of each tile
 };

@@ -26,6 +26,19 @@
 
 namespace dgc {
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Streaming float4 access that bypasses cache residency (each element of
+// g, u, v is touched once per step).
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+    f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void st_stream(float* p, float a, float b, float c, float d) {
+    f4v x = {a, b, c, d};
+    __builtin_nontemporal_store(x, reinterpret_cast<f4v*>(p));
+}
+
 // ---------------------------------------------------------------- prep
 
 // Zero `n` 32-bit words (a fill kernel: safe inside captured graphs).
@@ -69,8 +82,9 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     int64_t i = vlo + threadIdx.x;
     for (; i + 3 * kBlock < vhi; i += 4 * kBlock) {
-        float4 x0 = g4[i], x1 = g4[i + kBlock], x2 = g4[i + 2 * kBlock],
-               x3 = g4[i + 3 * kBlock];
+        float4 x0 = ld_stream(g + 4 * i), x1 = ld_stream(g + 4 * (i + kBlock)),
+               x2 = ld_stream(g + 4 * (i + 2 * kBlock)),
+               x3 = ld_stream(g + 4 * (i + 3 * kBlock));
         a0 += double(x0.x) * double(x0.x); a1 += double(x0.y) * double(x0.y);
         a2 += double(x0.z) * double(x0.z); a3 += double(x0.w) * double(x0.w);
         a0 += double(x1.x) * double(x1.x); a1 += double(x1.y) * double(x1.y);
@@ -253,15 +267,19 @@ __global__ __launch_bounds__(kBlock) void k_window(
 // them, then writes the piece's candidates (key >= lo) as one run in index
 // order into the piece's own pcap slots: ballot + popcount give each
 // candidate its rank; no atomics, so the layout is the same every run.
+// The loads depend only on the piece descriptor; the tensor's metadata is
+// read while they are in flight.
 template <bool kAligned>
 __device__ __forceinline__ void fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    int64_t e0, int64_t e1, int64_t o, float s, float m, uint32_t lo,
-    uint32_t pcap, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
-    int64_t p) {
+    int64_t e0, int64_t e1, int t, const DevLayout& L,
+    const TensorState* __restrict__ ts, float s, float m,
+    uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt, int64_t p) {
     const int lane = lane_id();
     float vn[4][4];
     bool f[4][4];
+    uint32_t lo;
+    int64_t o;
     if (kAligned) {
         // e0 is a multiple of 4: 256 float4 units cover the piece.
         const int64_t ubase = e0 >> 2;
@@ -272,9 +290,9 @@ __device__ __forceinline__ void fused_piece(
             int64_t el = (ubase + i * kWave + lane) << 2;
             full[i] = el + 4 <= e1;
             if (full[i]) {
-                gv[i] = *reinterpret_cast<const float4*>(g + el);
-                uv[i] = *reinterpret_cast<const float4*>(u + el);
-                vv[i] = *reinterpret_cast<const float4*>(v + el);
+                gv[i] = ld_stream(g + el);
+                uv[i] = ld_stream(u + el);
+                vv[i] = ld_stream(v + el);
             } else {
                 float tg[4] = {0, 0, 0, 0}, tu[4] = {0, 0, 0, 0},
                       tv[4] = {0, 0, 0, 0};
@@ -286,6 +304,8 @@ __device__ __forceinline__ void fused_piece(
                 vv[i] = make_float4(tv[0], tv[1], tv[2], tv[3]);
             }
         }
+        lo = ts[t].lo_key;
+        o = L.o[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int64_t el = (ubase + i * kWave + lane) << 2;
@@ -299,8 +319,8 @@ __device__ __forceinline__ void fused_piece(
                 f[i][c] = (el + c < e1) && mag_key(vv4[c]) >= lo;
             }
             if (full[i]) {
-                *reinterpret_cast<float4*>(u + el) = make_float4(uu[0], uu[1], uu[2], uu[3]);
-                *reinterpret_cast<float4*>(v + el) = make_float4(vv4[0], vv4[1], vv4[2], vv4[3]);
+                st_stream(u + el, uu[0], uu[1], uu[2], uu[3]);
+                st_stream(v + el, vv4[0], vv4[1], vv4[2], vv4[3]);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -311,6 +331,8 @@ __device__ __forceinline__ void fused_piece(
         // Unaligned piece start: 16 scalar rounds of 64 consecutive elements.
         // Element (i, c) of a lane is e0 + (i*4 + c)*64 + lane; ranks below
         // follow (i, c, lane) order, which is index order here.
+        lo = ts[t].lo_key;
+        o = L.o[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -361,6 +383,8 @@ __device__ __forceinline__ void fused_piece(
     // the overflow (the tensor then takes the dense path).
     if (lane == 0) run_cnt[p] = total;
     if (total) {
+        const uint32_t pcap = uint32_t(L.pcap[t]);
+        uint2* sl = slots + L.slbase[t] + (p - L.pbase[t]) * int64_t(pcap);
         const int64_t unit0 = e0 >> 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -369,32 +393,28 @@ __device__ __forceinline__ void fused_piece(
                 if (f[i][c] && rank[i][c] < pcap) {
                     int64_t el = kAligned ? (((unit0 + i * kWave + lane) << 2) + c)
                                           : (e0 + int64_t(i * 4 + c) * kWave + lane);
-                    slots[rank[i][c]] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
+                    sl[rank[i][c]] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
                 }
     }
 }
 
 __global__ __launch_bounds__(kBlock) void k_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    DevLayout L, TensorState* __restrict__ ts, const Scalars* __restrict__ sc,
-    float m, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
-    int64_t n_pieces) {
+    DevLayout L, const TensorState* __restrict__ ts,
+    const Scalars* __restrict__ sc, float m, uint2* __restrict__ slots,
+    uint32_t* __restrict__ run_cnt, int64_t n_pieces) {
     const float s = sc->scale;
     const int64_t w0 = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
     const int64_t nw = (int64_t(gridDim.x) * kBlock) >> 6;
     for (int64_t p = w0; p < n_pieces; p += nw) {
-        const int t = wave_uniform(int(L.pmap[p]));
-        const int64_t o = L.o[t];
-        const int64_t j = p - L.pbase[t];
-        const int64_t e0 = o + (j << kPieceShift);
-        const int64_t e1 = min(e0 + kPiece, L.o[t + 1]);
-        const uint32_t lo = ts[t].lo_key;
-        const uint32_t pcap = uint32_t(L.pcap[t]);
-        uint2* sl = slots + L.slbase[t] + j * pcap;
+        const PieceDesc d = L.pdesc[p];
+        const int t = wave_uniform(int(d.tensor));
+        const int64_t e0 = d.start;
+        const int64_t e1 = e0 + d.len;
         if ((e0 & 3) == 0)
-            fused_piece<true>(g, u, v, e0, e1, o, s, m, lo, pcap, sl, run_cnt, p);
+            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
         else
-            fused_piece<false>(g, u, v, e0, e1, o, s, m, lo, pcap, sl, run_cnt, p);
+            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
     }
 }
 
@@ -455,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     int64_t n_pieces) {
     const int64_t p = int64_t(blockIdx.x) * kBlock + threadIdx.x;
     if (p >= n_pieces) return;
-    const int t = int(L.pmap[p]);
+    const int t = int(L.pdesc[p].tensor);
     if (ts[t].mode != kModeList) return;
     const uint32_t cnt = run_cnt[p];
     const int64_t pcap = L.pcap[t];
