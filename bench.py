@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--grad-steps", type=int, default=0,
                     help="generate only this many gradient steps and cycle "
                          "over them (0: all of the workload's; for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, run one plain device copy "
+                         "of 1 GiB (for scaling hardware byte counters)")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
     return ap.parse_args()
@@ -188,6 +191,14 @@ def main():
     elapsed = time.perf_counter() - t0
     for L in learners:
         assert L.status() == dgc.DGC_OK
+    if args.calibrate_copy:
+        # a plain copy of known size: reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     times = {}
     for name, tm in (("fused", dgc.DGC_TIMER_FUSED), ("compress", dgc.DGC_TIMER_COMPRESS),
                      ("encode", dgc.DGC_TIMER_ENCODE), ("decode", dgc.DGC_TIMER_DECODE)):
