@@ -5,8 +5,9 @@
  * The method is described on the review page "[Paper Review] Deep Gradient
  * Compression: Reducing the Communication Bandwidth for Distributed
  * Training" (nubint.ai), section "Proposed method": send only the large
- * gradients and accumulate the small ones locally; encode the sent ones as
- * 32-bit nonzeros with 16-bit zero run lengths; momentum correction; local
+ * entries and keep the rest in a local accumulator; send each value in 32
+ * bits after the 16-bit length of the zero run before it; momentum
+ * correction; local
  * gradient clipping; momentum factor masking; warm-up to a rising sparsity.
  * Its Abstract places this in synchronous data-parallel SGD, where the
  * learners' sparse gradients are summed.
@@ -139,8 +140,8 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
 int dgc_stream_capacity(const dgc_state* st, int64_t* cap_offsets);
 
 /*
- * Zero-run encoding (DGC review, "Proposed method": 32-bit nonzeros and
- * 16-bit run lengths of zeros).  Per tensor, per selected index j in
+ * Zero-run encoding (DGC review, "Proposed method": 32-bit values, each
+ * after a 16-bit zero-run length).  Per tensor, per selected index j in
  * ascending order with gap G = j - prev - 1 (prev = -1 at the start):
  * floor(G / 65536) filler entries (run 65535, value +0.0f), then the entry
  * (G mod 65536, value).  Zeros after the last selected index are not

@@ -9,7 +9,7 @@
  * Source of the method: the review page "[Paper Review] Deep Gradient
  * Compression: Reducing the Communication Bandwidth for Distributed Training"
  * (nubint.ai), section "Proposed method" (sparsification with local
- * accumulation, 32-bit nonzero / 16-bit zero-run encoding, momentum
+ * accumulation, 32-bit value / 16-bit zero-run encoding, momentum
  * correction, local gradient clipping, momentum factor masking, warm-up),
  * and its Abstract (99.9% of the exchange is redundant; synchronous SGD
  * gradient exchange).  The page prints no formulas; the readings used here
@@ -72,7 +72,8 @@ int orc_num_threads(void) {
 
 /*
  * Local gradient clipping (DGC review, "Proposed method": clipping bounds the
- * gradient within each node).  One norm over the learner's whole gradient.
+ * gradient locally, on each learner).  One norm over the learner's whole
+ * gradient.
  * Returns 0; writes the binary64 norm and the binary32 scale.
  */
 int orc_clip_scale(const float* g, int64_t n, double clip, double* norm_out,
@@ -118,9 +119,9 @@ void orc_momentum(const float* g, int64_t n, float scale, float m, float* u,
 
 /*
  * Exact top-k of |v| for one tensor, then momentum factor masking (DGC
- * review, "Proposed method": only large gradients are sent; momentum factor
- * masking; the AdaComp page's "Citations in the corpus" note that "large"
- * means large in absolute value).
+ * review, "Proposed method": only the entries of largest magnitude leave the
+ * learner; momentum factor masking; the AdaComp page's "Citations in the
+ * corpus" rank entries by absolute value).
  *
  * T = the k-th largest key (std::nth_element); every key > T is taken, and
  * of the keys == T the first r = k - #{key > T} in index order.  Writes the
@@ -164,9 +165,10 @@ int64_t orc_select_mask(float* u, float* v, int64_t n, int64_t k,
 
 /*
  * Zero-run encoding of one tensor's sparse gradient (DGC review, "Proposed
- * method": 32-bit nonzeros and 16-bit run lengths of zeros).  A gap longer
- * than a 16-bit run can say is split by filler entries (65535, +0.0f), each
- * of which stands for 65535 zeros plus one slot holding zero.
+ * method": each sent value takes 32 bits and is preceded by the 16-bit
+ * length of the zero run before it).  A gap longer than a 16-bit run can say
+ * is split by filler entries (65535, +0.0f), each of which stands for 65535
+ * zeros plus one slot holding zero.
  * Returns the entry count E, or -1 if cap entries are not enough, or -2 if
  * the indices are not strictly ascending.
  */

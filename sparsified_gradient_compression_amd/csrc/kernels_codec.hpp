@@ -1,8 +1,8 @@
 // kernels_codec.hpp -- zero-run encoding and decode + sum on gfx950.
 //
 // Format: DGC review page (nubint.ai), "Proposed method": sparse gradients
-// are sent as 32-bit nonzero values and 16-bit run lengths of zeros.  Per
-// tensor, for the sent indices j in ascending order with gap
+// leave as 32-bit values, each preceded by the 16-bit length of the zero run
+// before it.  Per tensor, for the sent indices j in ascending order with gap
 // G = j - prev - 1: floor(G/65536) fillers (65535, +0.0f), then
 // (G mod 65536, value).  Runs and values are separate arrays (u16 and f32)
 // at each tensor's capacity offset.
