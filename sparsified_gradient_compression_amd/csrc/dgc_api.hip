@@ -32,33 +32,33 @@ struct Plan {
     // tables uploaded at init (int64): o, pbase, tbase, obase, sbase,
     // slines, ebase, etbase, slbase, pcap -- each T+1 long (padded)
     std::vector<int64_t> o, pbase, tbase, obase, sbase, slines, ebase, etbase,
-        slbase, pcap;
+        slbase, pcap, gbase;
     std::vector<PieceDesc> pdesc;
-    std::vector<uint32_t> smap, emap;
-    int64_t n = 0, P = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
+    std::vector<uint32_t> smap, emap, gmap;
+    int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t tiles = 0;  // entries of each per-tile array
     // workspace byte offsets
     size_t off_tab = 0, off_pdesc = 0, off_smap = 0, off_emap = 0, off_k = 0,
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
-           off_runc = 0, off_ord = 0, off_atiles = 0, off_aoff = 0,
+           off_runc = 0, off_gmap = 0, off_gsum = 0, off_goff = 0, off_atiles = 0, off_aoff = 0,
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            total = 0;
 };
 
-// Candidate slots per 1024-element piece: all of them for small tensors
-// (which take every element as a candidate), else about six times the
-// pieces' share of k_max plus 24 -- the sample window aims at 2-4 k
-// candidates, so a piece overflows (sending its tensor to the dense path)
-// only with a negligible probability for unstructured data.
+// Candidate slots per 1024-element piece: none for small tensors (they take
+// the dense path), else about six times the pieces' share of k_max plus
+// 24 -- the sample window aims at 1.5-2.5 k candidates, so a piece overflows
+// (sending its tensor to the dense path) only with a negligible probability
+// for unstructured data.
 int64_t piece_cap(int64_t n, int64_t kmax) {
-    if (n <= kSmallN) return kPiece;
+    if (n <= kSmallN) return 0;
     return std::min<int64_t>(kPiece, cdiv(6 * kPiece * kmax, n) + 24);
 }
 
 // Capacity of a tensor's ordered candidate list.
 int64_t list_cap(int64_t n, int64_t kmax, int64_t slots) {
-    if (n <= kSmallN) return n;
+    if (n <= kSmallN) return 0;
     return std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384);
 }
 
@@ -79,6 +79,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.obase.assign(T + 1, 0);
     p.slbase.assign(T + 1, 0);
     p.pcap.assign(T + 1, 0);
+    p.gbase.assign(T + 1, 0);
     p.sbase.assign(T + 1, 0);
     p.slines.assign(T + 1, 0);
     p.ebase.assign(T + 1, 0);
@@ -89,6 +90,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.o[t + 1] = p.o[t] + n;
         const int64_t np_ = cdiv(n, kPiece);
         p.pbase[t + 1] = p.pbase[t] + np_;
+        p.gbase[t + 1] = p.gbase[t] + cdiv(np_, kGroup);
         p.tbase[t + 1] = p.tbase[t] + cdiv(n, kTile);
         p.pcap[t] = piece_cap(n, km);
         p.slbase[t + 1] = p.slbase[t] + np_ * p.pcap[t];
@@ -100,6 +102,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     }
     p.n = p.o[T];
     p.P = p.pbase[T];
+    p.G = p.gbase[T];
     p.TT = p.tbase[T];
     p.A = p.obase[T];
     p.SL = p.slbase[T];
@@ -113,6 +116,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.pdesc.resize(size_t(p.P));
     p.smap.resize(size_t(p.S));
     p.emap.resize(size_t(p.ET));
+    p.gmap.resize(size_t(p.G));
     for (int32_t t = 0; t < T; ++t) {
         for (int64_t i = p.pbase[t]; i < p.pbase[t + 1]; ++i) {
             PieceDesc& d = p.pdesc[size_t(i)];
@@ -122,6 +126,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         }
         for (int64_t i = p.sbase[t]; i < p.sbase[t + 1]; ++i) p.smap[size_t(i)] = uint32_t(t);
         for (int64_t i = p.etbase[t]; i < p.etbase[t + 1]; ++i) p.emap[size_t(i)] = uint32_t(t);
+        for (int64_t i = p.gbase[t]; i < p.gbase[t + 1]; ++i) p.gmap[size_t(i)] = uint32_t(t);
     }
     // carve
     size_t off = 0;
@@ -131,7 +136,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         return at;
     };
     const size_t T1 = size_t(T) + 1;
-    p.off_tab = take(10 * T1 * sizeof(int64_t));
+    p.off_tab = take(11 * T1 * sizeof(int64_t));
     p.off_pdesc = take(size_t(p.P) * sizeof(PieceDesc));
     p.off_smap = take(size_t(p.S) * 4);
     p.off_emap = take(size_t(p.ET) * 4);
@@ -142,7 +147,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_hist = take(size_t(T) * kHistBins * 4);
     p.off_shist = take(size_t(T) * kHistBins * 4);
     p.off_runc = take(size_t(p.P) * 4);
-    p.off_ord = take(size_t(p.P) * 4);
+    p.off_gmap = take(size_t(p.G) * 4);
+    p.off_gsum = take(size_t(p.G) * 4);
+    p.off_goff = take(size_t(p.G) * 4);
     p.off_atiles = take(size_t(T) * 4);
     p.off_aoff = take(T1 * 4);
     p.off_amap = take(size_t(p.TT) * 4);
@@ -196,7 +203,7 @@ struct dgc_state {
     TensorState* ts = nullptr;
     Scalars* sc = nullptr;
     uint32_t *hist = nullptr, *shist = nullptr,
-             *run_cnt = nullptr, *ord_off = nullptr, *atiles = nullptr,
+             *run_cnt = nullptr, *gsum = nullptr, *goff = nullptr, *atiles = nullptr,
              *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
              *tc = nullptr;
     uint2 *slots = nullptr, *olist = nullptr;
@@ -365,11 +372,11 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     const int32_t T = p.T;
     const size_t T1 = size_t(T) + 1;
     // layout tables
-    std::vector<int64_t> tab(10 * T1, 0);
-    const std::vector<int64_t>* src[10] = {&p.o,      &p.pbase, &p.tbase,  &p.obase,
+    std::vector<int64_t> tab(11 * T1, 0);
+    const std::vector<int64_t>* src[11] = {&p.o,      &p.pbase,  &p.tbase, &p.obase,
                                            &p.sbase,  &p.slines, &p.ebase, &p.etbase,
-                                           &p.slbase, &p.pcap};
-    for (int i = 0; i < 10; ++i)
+                                           &p.slbase, &p.pcap,   &p.gbase};
+    for (int i = 0; i < 11; ++i)
         std::copy(src[i]->begin(), src[i]->end(), tab.begin() + i * T1);
     int64_t* dtab = reinterpret_cast<int64_t*>(ws + p.off_tab);
     st->L.T = T;
@@ -383,6 +390,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->L.etbase = dtab + 7 * T1;
     st->L.slbase = dtab + 8 * T1;
     st->L.pcap = dtab + 9 * T1;
+    st->L.gbase = dtab + 10 * T1;
+    st->L.gmap = reinterpret_cast<uint32_t*>(ws + p.off_gmap);
     st->L.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_pdesc);
     st->L.smap = reinterpret_cast<uint32_t*>(ws + p.off_smap);
     st->L.emap = reinterpret_cast<uint32_t*>(ws + p.off_emap);
@@ -396,7 +405,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
     st->shist = reinterpret_cast<uint32_t*>(ws + p.off_shist);
     st->run_cnt = reinterpret_cast<uint32_t*>(ws + p.off_runc);
-    st->ord_off = reinterpret_cast<uint32_t*>(ws + p.off_ord);
+    st->gsum = reinterpret_cast<uint32_t*>(ws + p.off_gsum);
+    st->goff = reinterpret_cast<uint32_t*>(ws + p.off_goff);
     st->atiles = reinterpret_cast<uint32_t*>(ws + p.off_atiles);
     st->aoff = reinterpret_cast<uint32_t*>(ws + p.off_aoff);
     st->amap = reinterpret_cast<uint32_t*>(ws + p.off_amap);
@@ -418,6 +428,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
                                        hipMemcpyHostToDevice, stream) == hipSuccess;
     if (p.ET) ok = ok && hipMemcpyAsync(ws + p.off_emap, p.emap.data(), size_t(p.ET) * 4,
                                         hipMemcpyHostToDevice, stream) == hipSuccess;
+    if (p.G) ok = ok && hipMemcpyAsync(ws + p.off_gmap, p.gmap.data(), size_t(p.G) * 4,
+                                       hipMemcpyHostToDevice, stream) == hipSuccess;
     // zero the scratch after the tables (histograms must start at zero) and
     // the state vectors u and v
     if (ok) {
@@ -494,11 +506,13 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
             g, st->u, st->v, st->L, st->ts, st->sc, st->m, st->slots, st->run_cnt, p.P);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
-    k_piece_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->run_cnt,
-                                           st->ord_off, st->atiles);
-    if (p.P > 0)
-        k_gather<<<int(cdiv(p.P, kBlock)), kBlock, 0, stream>>>(
-            st->L, st->ts, st->slots, st->run_cnt, st->ord_off, st->olist, p.P);
+    if (p.G > 0)
+        k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
+    k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
+                                           st->atiles);
+    if (p.G > 0)
+        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots, st->run_cnt,
+                                                  st->goff, st->olist);
     k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
     k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
     DGC_LAUNCH_CHECK();
@@ -516,7 +530,7 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         DGC_LAUNCH_CHECK();
         k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist,
                                                 st->amap, st->aoff, st->ta);
-        k_emit_scan<<<T, kBlock, 0, stream>>>(T, st->aoff, st->ta, st->tb, st->tc);
+        k_emit_scan<<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
         k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
                                                 st->olist, st->amap, st->aoff, st->tb,
                                                 st->tc, out_idx, out_val, st->sc);

@@ -18,6 +18,8 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 // written as one index-ordered run.
 constexpr int kPieceShift = 10;
 constexpr int64_t kPiece = int64_t(1) << kPieceShift;
+// Pieces are scanned in groups of 256 (one workgroup per group).
+constexpr int64_t kGroup = 256;
 
 // Generic tiles for histogram / emit / encode / decode passes: 4096 items
 // per workgroup visit (16 per thread).
@@ -30,8 +32,8 @@ constexpr int kBins0 = 2048;
 constexpr int kHistBins = 2048;  // histogram row per tensor (largest digit)
 
 // Sample window: 32-element lines; tensors above kSmallN elements sample
-// max(kMinSampleLines, lines/256) lines; smaller tensors take every element
-// as a candidate.
+// max(kMinSampleLines, lines/256) lines; smaller tensors skip the window and
+// take the dense exact path (a few passes over at most 256 KiB).
 constexpr int64_t kLine = 32;
 constexpr int64_t kSmallN = 65536;
 constexpr int64_t kMinSampleLines = 512;
@@ -98,6 +100,8 @@ struct DevLayout {
     const int64_t* ebase;   // [T+1] encoded stream capacity offsets
     const int64_t* etbase;  // [T+1] tiles over encoded capacity
     const PieceDesc* pdesc; // [pieces] start, tensor and length of each piece
+    const int64_t* gbase;   // [T+1] first piece group of each tensor
+    const uint32_t* gmap;   // [groups] tensor of each piece group
     const uint32_t* smap;   // [sample blocks] tensor of each sample block
     const uint32_t* emap;   // [capacity tiles] tensor of each tile
 };
@@ -180,6 +184,35 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* lds, T& total) {
     __syncthreads();
     total = tot;
     return wpre + inc - x;
+}
+
+// Exclusive prefix, in thread order, of two 0/1 flags across the block, from
+// wave ballots; also their block totals.  `lds2` holds 2 * kWavesPerBlock
+// values.  Every thread must call it.
+__device__ __forceinline__ void block_flag_prefix2(bool a, bool b, uint32_t* lds2,
+                                                   uint32_t& pa, uint32_t& pb,
+                                                   uint32_t& ta, uint32_t& tb) {
+    const int wid = threadIdx.x >> 6;
+    const uint64_t lt = lanemask_lt();
+    const uint64_t ba = __ballot(a), bb = __ballot(b);
+    if (lane_id() == 0) {
+        lds2[wid] = uint32_t(__popcll(ba));
+        lds2[kWavesPerBlock + wid] = uint32_t(__popcll(bb));
+    }
+    __syncthreads();
+    uint32_t wa = 0, wb = 0;
+    ta = 0;
+    tb = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        uint32_t x = lds2[w], y = lds2[kWavesPerBlock + w];
+        if (w < wid) { wa += x; wb += y; }
+        ta += x;
+        tb += y;
+    }
+    __syncthreads();
+    pa = wa + uint32_t(__popcll(ba & lt));
+    pb = wb + uint32_t(__popcll(bb & lt));
 }
 
 // Sum across the block in a fixed order (deterministic for floating point).

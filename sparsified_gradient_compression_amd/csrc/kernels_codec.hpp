@@ -20,8 +20,23 @@ namespace dgc {
 
 // ---------------------------------------------------------------- encode
 
-// Per k-tile: number of fillers its items need.  Flags indices that are not
-// strictly ascending or not inside the tensor.
+// Tiles of 4096 entries are visited in 16 rounds of 256 consecutive
+// entries (entry i0 + 256 q + tid), so loads and stores are coalesced.
+
+// Fillers needed by entry i of a tensor's sorted index list (0 for an entry
+// whose index is not above the previous one or not inside the tensor, which
+// is flagged).
+__device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
+                                               int64_t nt, bool& bad,
+                                               int64_t& gap) {
+    const int64_t cur = id[i];
+    const int64_t prev = i ? int64_t(id[i - 1]) : -1;
+    if (cur <= prev || cur >= nt) { bad = true; gap = -1; return 0; }
+    gap = cur - prev - 1;
+    return uint32_t(gap >> 16);
+}
+
+// Per k-tile: number of fillers its entries need.
 __global__ __launch_bounds__(kBlock) void k_enc_count(
     DevLayout L, DevK K, const uint32_t* __restrict__ idx,
     uint32_t* __restrict__ tile_f, Scalars* __restrict__ sc, int64_t n_ktiles) {
@@ -31,16 +46,15 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
         const int64_t kt = K.k[t];
         const int64_t nt = L.o[t + 1] - L.o[t];
         const uint32_t* id = idx + K.koff[t];
-        const int64_t s0 = (vt - K.ktbase[t]) * kTile + int64_t(threadIdx.x) * kPerThread;
+        const int64_t i0 = (vt - K.ktbase[t]) * kTile;
         uint32_t f = 0;
         bool bad = false;
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i >= kt) break;
-            int64_t cur = id[i];
-            int64_t prev = i ? int64_t(id[i - 1]) : -1;
-            if (cur <= prev || cur >= nt) { bad = true; continue; }
-            f += uint32_t((cur - prev - 1) >> 16);
+            int64_t i = i0 + q * kBlock + threadIdx.x;
+            if (i < kt) {
+                int64_t gap;
+                f += fillers_of(id, i, nt, bad, gap);
+            }
         }
         if (bad) latch_error(sc, kErrCorrupt);
         uint32_t tot;
@@ -68,6 +82,8 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
     if (threadIdx.x == 0) entries[t] = K.k[t] + int64_t(carry);
 }
 
+// Entry i lands at slot i + (fillers of entries <= i); its own fillers fill
+// the slots just before it.
 __global__ __launch_bounds__(kBlock) void k_enc_write(
     DevLayout L, DevK K, const uint32_t* __restrict__ idx,
     const float* __restrict__ val, const uint32_t* __restrict__ tile_foff,
@@ -80,34 +96,27 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         const uint32_t* id = idx + K.koff[t];
         const float* vl = val + K.koff[t];
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
-        const int64_t s0 = (vt - K.ktbase[t]) * kTile + int64_t(threadIdx.x) * kPerThread;
-        uint32_t f = 0;
+        const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+        uint32_t carry = tile_foff[vt];
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i >= kt) break;
-            int64_t cur = id[i];
-            int64_t prev = i ? int64_t(id[i - 1]) : -1;
-            if (cur <= prev || cur >= nt) continue;
-            f += uint32_t((cur - prev - 1) >> 16);
-        }
-        uint32_t tot;
-        uint32_t fb = tile_foff[vt] + block_exclusive_scan(f, lds, tot);
-        for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i >= kt) break;
-            int64_t cur = id[i];
-            int64_t prev = i ? int64_t(id[i - 1]) : -1;
-            if (cur <= prev || cur >= nt) continue;
-            int64_t gap = cur - prev - 1;
-            uint32_t nf = uint32_t(gap >> 16);
-            int64_t pos = i + int64_t(fb);
-            for (uint32_t z = 0; z < nf; ++z, ++pos)
-                if (pos < cap) { runs[eb + pos] = 65535; vals[eb + pos] = 0.0f; }
-            if (pos < cap) {
-                runs[eb + pos] = uint16_t(gap & 0xFFFF);
-                vals[eb + pos] = vl[i];
+            if (i0 + q * kBlock >= kt) break;  // uniform
+            const int64_t i = i0 + q * kBlock + threadIdx.x;
+            bool bad = false;
+            int64_t gap = -1;
+            const uint32_t nf = i < kt ? fillers_of(id, i, nt, bad, gap) : 0u;
+            uint32_t pre = 0, tot = 0;
+            if (__syncthreads_or(nf != 0))  // fillers are rare: skip the scan
+                pre = block_exclusive_scan(nf, lds, tot);
+            if (i < kt && gap >= 0) {
+                int64_t pos = i + int64_t(carry) + pre;
+                for (uint32_t z = 0; z < nf; ++z, ++pos)
+                    if (pos < cap) { runs[eb + pos] = 65535; vals[eb + pos] = 0.0f; }
+                if (pos < cap) {
+                    runs[eb + pos] = uint16_t(gap & 0xFFFF);
+                    vals[eb + pos] = vl[i];
+                }
             }
-            fb += nf;
+            carry += tot;
         }
     }
 }
@@ -136,10 +145,10 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
             if (e < 0 || e > cap) latch_error(sc, kErrCorrupt);
         }
         const int64_t E = stream_len(entries, t, cap);
-        const int64_t s0 = j * kTile + int64_t(threadIdx.x) * kPerThread;
+        const int64_t i0 = j * kTile;
         uint32_t s = 0;
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
+            int64_t i = i0 + q * kBlock + threadIdx.x;
             if (i < E) s += uint32_t(runs[eb + i]) + 1u;
         }
         uint32_t tot;
@@ -166,10 +175,10 @@ __global__ __launch_bounds__(kBlock) void k_dec_scan(
     }
 }
 
-// dense[o_t + pos] += value for every entry of one learner's stream.
-// Entries whose position reaches the tensor's end add nothing and flag the
-// stream as corrupt (positions only grow, so every later entry is past the
-// end too).
+// dense[o_t + pos] += value for every entry of one learner's stream, where
+// pos = (sum of run + 1 over the entries up to this one) - 1.  Entries whose
+// position reaches the tensor's end add nothing and flag the stream as
+// corrupt (positions only grow, so every later entry is past the end too).
 __global__ __launch_bounds__(kBlock) void k_dec_write(
     DevLayout L, const uint16_t* __restrict__ runs,
     const float* __restrict__ vals, const int64_t* __restrict__ entries,
@@ -181,23 +190,21 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
         const int64_t o = L.o[t], nt = L.o[t + 1] - o;
         const int64_t E = stream_len(entries, t, cap);
-        const int64_t j = vt - L.etbase[t];
-        const int64_t s0 = j * kTile + int64_t(threadIdx.x) * kPerThread;
-        uint32_t s = 0;
-        for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i < E) s += uint32_t(runs[eb + i]) + 1u;
-        }
-        uint32_t tot;
-        uint32_t ex = block_exclusive_scan(s, lds, tot);
-        int64_t pos = int64_t(tile_p[vt]) + ex - 1;
+        const int64_t i0 = (vt - L.etbase[t]) * kTile;
+        uint64_t carry = tile_p[vt];
         bool bad = false;
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i >= E) break;
-            pos += int64_t(runs[eb + i]) + 1;
-            if (pos >= nt) { bad = true; break; }
-            dense[o + pos] = __fadd_rn(dense[o + pos], vals[eb + i]);
+            if (i0 + q * kBlock >= E) break;  // uniform
+            const int64_t i = i0 + q * kBlock + threadIdx.x;
+            const uint32_t w = i < E ? uint32_t(runs[eb + i]) + 1u : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan(w, lds, tot);
+            if (i < E) {
+                const int64_t pos = int64_t(carry) + ex + w - 1;
+                if (pos >= nt) bad = true;
+                else dense[o + pos] = __fadd_rn(dense[o + pos], vals[eb + i]);
+            }
+            carry += tot;
         }
         if (bad) latch_error(sc, kErrCorrupt);
     }

@@ -12,7 +12,7 @@
 //   fused                    u, v update (20 B/elem); keys >= lo are
 //                            written, index-ordered, into the fixed slots of
 //                            their 1024-element piece (no atomics)
-//   piece_scan/gather        per tensor: choose the source (candidates when
+//   group_sum/scan, gather   per tensor: choose the source (candidates when
 //                            none overflowed and there are at least k, else
 //                            the whole tensor); concatenate the pieces' runs
 //                            into one index-ordered candidate list
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(kBlock) void k_sample(
 // is how many of the S samples the true top k should hold.  Level 0 finds
 // the top-11-bit bin holding the j-th key (wbin) and how many samples lie
 // above it (wabove); level 1 finds the 10-bit sub-bin inside it, and lo is
-// that sub-bin's lower edge.  Small tensors take every element (lo = 0);
-// k = 0 takes none.  Clears the histogram row for the next use.
+// that sub-bin's lower edge.  Small tensors (no sampled lines) and k = 0
+// get no candidates.  Clears the histogram row for the next use.
 template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_window(
     DevLayout L, DevK K, uint32_t* __restrict__ shist,
@@ -220,8 +220,9 @@ __global__ __launch_bounds__(kBlock) void k_window(
         // kNoKey, which sends the tensor to the dense path should no bin
         // qualify).
         if (k <= 0 || force_dense || L.slines[t] == 0) {
+            // no candidates: k = 0 skips, small tensors take the dense path
             if (threadIdx.x == 0) {
-                ts[t].lo_key = (k <= 0 || force_dense) ? kNoKey : 0u;
+                ts[t].lo_key = kNoKey;
                 ts[t].wbin = kNoKey;
             }
             return;
@@ -420,31 +421,50 @@ __global__ __launch_bounds__(kBlock) void k_fused(
 
 // ---------------------------------------------------------------- source
 
-// One block per tensor: scan the pieces' candidate counts (their order in
-// the list), then choose the selection source: the candidate list when no
-// piece overflowed its slots and there are at least k candidates, else the
-// whole tensor.  Also counts the source's 4096-item tiles for the
-// active-tile map.
-__global__ __launch_bounds__(kBlock) void k_piece_scan(
+// Piece groups: group g of tensor t holds pieces pbase[t] + 256 (g - gbase[t])
+// onward (at most 256, never past the tensor).
+
+// One block per group: the group's candidate count, with bit 31 set when a
+// piece overflowed its slots.
+__global__ __launch_bounds__(kBlock) void k_group_sum(
+    DevLayout L, const uint32_t* __restrict__ run_cnt, uint32_t* __restrict__ gsum) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int64_t g = blockIdx.x;
+    const int t = int(L.gmap[g]);
+    const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
+    const int64_t p1 = min(p0 + kGroup, L.pbase[t + 1]);
+    const int64_t p = p0 + threadIdx.x;
+    const uint32_t c = p < p1 ? run_cnt[p] : 0u;
+    const int over = __syncthreads_or(c > uint32_t(L.pcap[t]));
+    uint32_t tot;
+    block_exclusive_scan(c, lds, tot);
+    if (threadIdx.x == 0) gsum[g] = tot | (over ? 0x80000000u : 0u);
+}
+
+// One block per tensor: scan its groups' counts (their offsets in the
+// ordered list), then choose the selection source: the candidate list when
+// no piece overflowed and there are at least k candidates, else the whole
+// tensor.  Also counts the source's 4096-item tiles for the active-tile map.
+__global__ __launch_bounds__(kBlock) void k_group_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
-    const uint32_t* __restrict__ run_cnt, uint32_t* __restrict__ ord_off,
+    const uint32_t* __restrict__ gsum, uint32_t* __restrict__ goff,
     uint32_t* __restrict__ atiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t k = K.k[t];
-    const uint32_t pcap = uint32_t(L.pcap[t]);
     uint32_t carry = 0;
     int over = 0;
     if (k > 0) {
-        const int64_t p0 = L.pbase[t], p1 = L.pbase[t + 1];
-        for (int64_t base = p0; base < p1; base += kBlock) {
-            int64_t p = base + threadIdx.x;
-            uint32_t c = p < p1 ? run_cnt[p] : 0;
-            over |= c > pcap;
+        const int64_t g0 = L.gbase[t], g1 = L.gbase[t + 1];
+        for (int64_t base = g0; base < g1; base += kBlock) {
+            int64_t g = base + threadIdx.x;
+            uint32_t x = g < g1 ? gsum[g] : 0u;
+            over |= (x >> 31) != 0;
+            uint32_t c = x & 0x7FFFFFFFu;
             uint32_t tot;
             uint32_t ex = block_exclusive_scan(c, lds, tot);
-            if (p < p1) ord_off[p] = carry + ex;
+            if (g < g1) goff[g] = carry + ex;
             carry += tot;
         }
     }
@@ -466,22 +486,39 @@ __global__ __launch_bounds__(kBlock) void k_piece_scan(
     }
 }
 
-// One thread per piece: copy the piece's candidates from its slots to its
-// place in the tensor's index-ordered list.
+// One block per group: concatenate the group's piece runs into the tensor's
+// index-ordered candidate list.  Threads walk the group's output positions
+// (coalesced writes) and find each one's piece by binary search over the
+// in-group prefix of the run lengths.
 __global__ __launch_bounds__(kBlock) void k_gather(
     DevLayout L, const TensorState* __restrict__ ts,
     const uint2* __restrict__ slots, const uint32_t* __restrict__ run_cnt,
-    const uint32_t* __restrict__ ord_off, uint2* __restrict__ olist,
-    int64_t n_pieces) {
-    const int64_t p = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (p >= n_pieces) return;
-    const int t = int(L.pdesc[p].tensor);
-    if (ts[t].mode != kModeList) return;
-    const uint32_t cnt = run_cnt[p];
+    const uint32_t* __restrict__ goff, uint2* __restrict__ olist) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t pre[kGroup + 1];
+    const int64_t g = blockIdx.x;
+    const int t = int(L.gmap[g]);
+    if (ts[t].mode != kModeList) return;  // uniform
+    const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
+    const int np = int(min(kGroup, L.pbase[t + 1] - p0));
+    const int64_t p = p0 + threadIdx.x;
+    const uint32_t c = threadIdx.x < np ? run_cnt[p] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan(c, lds, tot);
+    pre[threadIdx.x] = ex;
+    if (threadIdx.x == 0) pre[kGroup] = tot;
+    __syncthreads();
     const int64_t pcap = L.pcap[t];
-    const uint2* src = slots + L.slbase[t] + (p - L.pbase[t]) * pcap;
-    uint2* dst = olist + L.obase[t] + ord_off[p];
-    for (uint32_t j = 0; j < cnt; ++j) dst[j] = src[j];
+    const uint2* src0 = slots + L.slbase[t] + (p0 - L.pbase[t]) * pcap;
+    uint2* dst = olist + L.obase[t] + goff[g];
+    for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
+        int lo = 0, hi = np;  // largest j < np with pre[j] <= q
+        while (hi - lo > 1) {
+            int mid = (lo + hi) >> 1;
+            if (pre[mid] <= q) lo = mid; else hi = mid;
+        }
+        dst[q] = src0[int64_t(lo) * pcap + (q - pre[lo])];
+    }
 }
 
 // One block: exclusive scan of the active tile counts -> aoff[T+1].
@@ -629,23 +666,10 @@ __device__ __forceinline__ uint2 source_item(uint32_t mode, const float* vt_,
     return ol[i];
 }
 
-// (key > T) counts in the high 16 bits, (key == T) in the low 16 bits of
-// thread tid's items [i0 + 16 tid, i0 + 16 tid + 16).
-__device__ __forceinline__ uint32_t count_items(uint32_t mode, const float* vt_,
-                                                const uint2* ol, int64_t s0,
-                                                int64_t len, uint32_t T) {
-    uint32_t cnt = 0;
-    for (int q = 0; q < kPerThread; ++q) {
-        int64_t i = s0 + q;
-        if (i < len) {
-            uint32_t key = source_item(mode, vt_, ol, i).y & 0x7FFFFFFFu;
-            cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
-        }
-    }
-    return cnt;
-}
+// Tiles are visited in 16 rounds of 256 consecutive items (item
+// i0 + 256 q + tid), so every load and store of a round is coalesced.
 
-// Per active tile: packed (#key > T, #key == T).
+// Per active tile: packed (#key > T) << 16 | #key == T.
 __global__ __launch_bounds__(kBlock) void k_emit_count(
     DevLayout L, const TensorState* __restrict__ ts,
     const float* __restrict__ v, const uint2* __restrict__ olist,
@@ -659,8 +683,17 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
         const int64_t len = ts[t].len;
         const int64_t i0 = int64_t(a - aoff[t]) * kTile;
         const uint32_t T = ts[t].prefix;
-        const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
-        uint32_t cnt = count_items(mode, v + L.o[t], olist + L.obase[t], s0, len, T);
+        const float* vt_ = v + L.o[t];
+        const uint2* ol = olist + L.obase[t];
+        uint32_t cnt = 0;
+#pragma unroll 4
+        for (int q = 0; q < kPerThread; ++q) {
+            int64_t i = i0 + q * kBlock + threadIdx.x;
+            if (i < len) {
+                uint32_t key = source_item(mode, vt_, ol, i).y & 0x7FFFFFFFu;
+                cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
+            }
+        }
         uint32_t tot;
         block_exclusive_scan(cnt, lds, tot);
         if (threadIdx.x == 0) tile_cnt[a] = tot;
@@ -669,9 +702,8 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
 
 // One block per tensor: exclusive scan of its tiles' (>T, ==T) counts.
 __global__ __launch_bounds__(kBlock) void k_emit_scan(
-    int T_, const uint32_t* __restrict__ aoff,
-    const uint32_t* __restrict__ tile_cnt, uint32_t* __restrict__ off_gt,
-    uint32_t* __restrict__ off_eq) {
+    const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ tile_cnt,
+    uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
@@ -699,7 +731,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ off_gt,
     const uint32_t* __restrict__ off_eq, uint32_t* __restrict__ out_idx,
     float* __restrict__ out_val, Scalars* __restrict__ sc) {
-    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t lds2[2 * kWavesPerBlock];
     const uint32_t A = aoff[L.T];
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
         const int t = int(amap[a]);
@@ -710,40 +742,39 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
         const int64_t o = L.o[t];
         float* vt_ = v + o;
         const uint2* ol = olist + L.obase[t];
-        const int64_t s0 = i0 + int64_t(threadIdx.x) * kPerThread;
-        uint32_t cnt = count_items(mode, vt_, ol, s0, len, T);
-        uint32_t tot;
-        uint32_t ex = block_exclusive_scan(cnt, lds, tot);
-        uint32_t gt = off_gt[a] + (ex >> 16);
-        uint32_t eq = off_eq[a] + (ex & 0xFFFFu);
         uint32_t* oi = out_idx + K.koff[t];
         float* ov = out_val + K.koff[t];
         const int64_t kt = K.k[t];
         const int64_t nt = L.o[t + 1] - o;
+        uint32_t cg = off_gt[a], ce = off_eq[a];
         bool bad = false;
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = s0 + q;
-            if (i >= len) break;
-            uint2 it = source_item(mode, vt_, ol, i);
-            uint32_t key = it.y & 0x7FFFFFFFu;
+            if (i0 + q * kBlock >= len) break;  // uniform
+            const int64_t i = i0 + q * kBlock + threadIdx.x;
+            const bool ok = i < len;
+            uint2 it = ok ? source_item(mode, vt_, ol, i) : make_uint2(0, 0);
+            const uint32_t key = it.y & 0x7FFFFFFFu;
+            const bool gt = ok && key > T, eq = ok && key == T;
+            uint32_t pg, pe, tg, te;
+            block_flag_prefix2(gt, eq, lds2, pg, pe, tg, te);
+            const uint32_t gb = cg + pg, eb = ce + pe;
             bool send = false;
             uint32_t slot = 0;
-            if (key > T) {
-                send = true;
-                slot = gt + min(eq, r);
-                ++gt;
-            } else if (key == T) {
-                if (eq < r) { send = true; slot = gt + eq; }
-                ++eq;
-            }
+            if (gt) { send = true; slot = gb + min(eb, r); }
+            else if (eq && eb < r) { send = true; slot = gb + eb; }
             if (send) {
                 // never write outside the outputs, whatever the counts say
-                if (int64_t(slot) >= kt || int64_t(it.x) >= nt) { bad = true; continue; }
-                oi[slot] = it.x;
-                ov[slot] = __uint_as_float(it.y);
-                u[o + it.x] = 0.0f;
-                vt_[it.x] = 0.0f;
+                if (int64_t(slot) >= kt || int64_t(it.x) >= nt) {
+                    bad = true;
+                } else {
+                    oi[slot] = it.x;
+                    ov[slot] = __uint_as_float(it.y);
+                    u[o + it.x] = 0.0f;
+                    vt_[it.x] = 0.0f;
+                }
             }
+            cg += tg;
+            ce += te;
         }
         if (bad) latch_error(sc, kErrInternal);
     }
