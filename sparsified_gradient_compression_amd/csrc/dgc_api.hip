@@ -41,6 +41,7 @@ struct Plan {
     size_t off_tab = 0, off_pdesc = 0, off_smap = 0, off_emap = 0, off_k = 0,
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
            off_runc = 0, off_gmap = 0, off_gsum = 0, off_goff = 0, off_atiles = 0, off_aoff = 0,
+           off_scratch = 0,
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            total = 0;
@@ -140,14 +141,18 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_pdesc = take(size_t(p.P) * sizeof(PieceDesc));
     p.off_smap = take(size_t(p.S) * 4);
     p.off_emap = take(size_t(p.ET) * 4);
+    p.off_gmap = take(size_t(p.G) * 4);
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
+    // Everything above is written from the host (layout tables at init, k
+    // tables per call); everything from here on is device scratch, zeroed
+    // at init.
+    p.off_scratch = off;
     p.off_ts = take(size_t(T) * sizeof(TensorState));
     p.off_sc = take(sizeof(Scalars));
     p.off_hist = take(size_t(T) * kHistBins * 4);
     p.off_shist = take(size_t(T) * kHistBins * 4);
     p.off_runc = take(size_t(p.P) * 4);
-    p.off_gmap = take(size_t(p.G) * 4);
     p.off_gsum = take(size_t(p.G) * 4);
     p.off_goff = take(size_t(p.G) * 4);
     p.off_atiles = take(size_t(T) * 4);
@@ -418,6 +423,14 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->t64 = reinterpret_cast<uint64_t*>(ws + p.off_t64);
     st->partial = reinterpret_cast<double*>(ws + p.off_part);
 
+    // the uploaded tables must not lie in the scratch zeroed below
+    if (p.off_pdesc >= p.off_scratch || p.off_smap >= p.off_scratch ||
+        p.off_emap >= p.off_scratch || p.off_gmap >= p.off_scratch ||
+        p.off_k >= p.off_scratch || p.off_kmap >= p.off_scratch ||
+        p.off_tab >= p.off_scratch) {
+        delete st;
+        return DGC_EINVAL;
+    }
     bool ok = true;
     ok = ok && hipMemcpyAsync(dtab, tab.data(), tab.size() * 8,
                               hipMemcpyHostToDevice, stream) == hipSuccess;
@@ -433,7 +446,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     // zero the scratch after the tables (histograms must start at zero) and
     // the state vectors u and v
     if (ok) {
-        size_t zero_from = p.off_ts;
+        size_t zero_from = p.off_scratch;
         int64_t words = int64_t((p.total - zero_from) / 4);
         k_fill_u32<<<grid_for(cdiv(words, kBlock), 4096), kBlock, 0, stream>>>(
             reinterpret_cast<uint32_t*>(ws + zero_from), words, 0u);

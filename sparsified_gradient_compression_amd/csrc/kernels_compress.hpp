@@ -433,8 +433,8 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
     const int t = int(L.gmap[g]);
     const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
     const int64_t p1 = min(p0 + kGroup, L.pbase[t + 1]);
-    const int64_t p = p0 + threadIdx.x;
-    const uint32_t c = p < p1 ? run_cnt[p] : 0u;
+    const int64_t p = p0 + int64_t(threadIdx.x);
+    const uint32_t c = (p >= p0 && p < p1) ? run_cnt[p] : 0u;
     const int over = __syncthreads_or(c > uint32_t(L.pcap[t]));
     uint32_t tot;
     block_exclusive_scan(c, lds, tot);
@@ -500,9 +500,10 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     const int t = int(L.gmap[g]);
     if (ts[t].mode != kModeList) return;  // uniform
     const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
-    const int np = int(min(kGroup, L.pbase[t + 1] - p0));
-    const int64_t p = p0 + threadIdx.x;
-    const uint32_t c = threadIdx.x < np ? run_cnt[p] : 0u;
+    const int64_t np = min(kGroup, L.pbase[t + 1] - p0);  // signed: >= 1 here
+    if (np <= 0) return;  // uniform; cannot happen with a valid group map
+    const int tid = int(threadIdx.x);
+    const uint32_t c = tid < np ? run_cnt[p0 + tid] : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan(c, lds, tot);
     pre[threadIdx.x] = ex;
@@ -510,9 +511,12 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     __syncthreads();
     const int64_t pcap = L.pcap[t];
     const uint2* src0 = slots + L.slbase[t] + (p0 - L.pbase[t]) * pcap;
+    // the list path guarantees this; it is checked so that no write can
+    // leave the tensor's list whatever the counts say
+    if (int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
     uint2* dst = olist + L.obase[t] + goff[g];
     for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
-        int lo = 0, hi = np;  // largest j < np with pre[j] <= q
+        int lo = 0, hi = int(np);  // largest j < np with pre[j] <= q
         while (hi - lo > 1) {
             int mid = (lo + hi) >> 1;
             if (pre[mid] <= q) lo = mid; else hi = mid;

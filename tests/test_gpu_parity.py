@@ -47,6 +47,7 @@ def run_workload(wl, steps=None, learners=None, path=0, encode=True, tag=""):
             say(f"{tag} step {t} learner {w} n={wl.n} T={len(wl.sizes)}")
             g = W.gradient(wl, w, t)
             got, (o_idx, o_val) = p.step(g, k, wl.clip, tag=f"{tag} s{t} w{w}")
+            check_paths(p, wl.sizes, k, path, tag=f"{tag} s{t} w{w}")
             if encode:
                 want = oracle_streams(wl.sizes, k, o_idx, o_val)
                 gs = gpu_streams(p, k)
@@ -55,6 +56,19 @@ def run_workload(wl, steps=None, learners=None, path=0, encode=True, tag=""):
         if encode:
             check_decode(pairs, outs, wl.sizes, tag=f"{tag} s{t}")
     return pairs
+
+
+SMALL_N = 65536  # tensors up to this size take the dense path
+
+
+def check_paths(pair, sizes, k, path, tag=""):
+    """On unstructured gradients the automatic path takes the sample
+    window for every tensor above SMALL_N elements (with k > 0) and the
+    dense path for the smaller ones; the forced path is dense throughout."""
+    info = pair.learner.select_info()
+    for t, (n, kt) in enumerate(zip(sizes, k)):
+        want = 0 if kt == 0 else (1 if (path == 0 and n > SMALL_N) else 2)
+        assert info[t, 0] == want, (tag, t, n, kt, info[t].tolist())
 
 
 def check_decode(pairs, streams_per_learner, sizes, tag=""):
