@@ -41,7 +41,7 @@ struct Plan {
     size_t off_tab = 0, off_pdesc = 0, off_smap = 0, off_emap = 0, off_k = 0,
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
            off_runc = 0, off_gmap = 0, off_gsum = 0, off_goff = 0, off_atiles = 0, off_aoff = 0,
-           off_scratch = 0, off_cnt = 0,
+           off_scratch = 0,
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            total = 0;
@@ -165,7 +165,6 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_tc = take(size_t(p.tiles) * 4);
     p.off_t64 = take(size_t(p.tiles) * 8);
     p.off_part = take(size_t(std::max<int64_t>(p.NB, 1)) * 8);
-    p.off_cnt = take((2 + 6 * size_t(T)) * 4);
     p.total = off;
     return DGC_OK;
 }
@@ -215,7 +214,6 @@ struct dgc_state {
     uint2 *slots = nullptr, *olist = nullptr;
     uint64_t* t64 = nullptr;
     double* partial = nullptr;
-    Counters cnt{};
 };
 
 namespace {
@@ -424,14 +422,6 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->tc = reinterpret_cast<uint32_t*>(ws + p.off_tc);
     st->t64 = reinterpret_cast<uint64_t*>(ws + p.off_t64);
     st->partial = reinterpret_cast<double*>(ws + p.off_part);
-    {
-        uint32_t* c = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
-        st->cnt.norm = c;
-        st->cnt.scan = c + 1;
-        st->cnt.sample = c + 2;
-        st->cnt.hist = c + 2 + 2 * size_t(T);
-        st->cnt.emit = c + 2 + 5 * size_t(T);
-    }
 
     // the uploaded tables must not lie in the scratch zeroed below
     if (p.off_pdesc >= p.off_scratch || p.off_smap >= p.off_scratch ||
@@ -499,20 +489,24 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     const int pg = st->num_cus * 8;  // persistent grids
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
-    const int force_dense = st->select_path == 1;
     if (clip_on) {
-        k_norm<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial, st->cnt.norm,
-                                                            clip, st->sc, out_norm, out_scale);
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
     } else if (p.P == 0) {
         k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
     }
+    DGC_LAUNCH_CHECK();
+    const int force_dense = st->select_path == 1;
+    if (p.S > 0 && !force_dense)
+        k_sample<0><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
+                                                     clip_on, st->ts, st->m, st->shist);
+    k_window<0><<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts, force_dense);
     if (p.S > 0 && !force_dense) {
-        k_sample<0><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->K, st->sc,
-                                                     clip_on, st->ts, st->m, st->shist,
-                                                     st->cnt.sample);
-        k_sample<1><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->K, st->sc,
-                                                     clip_on, st->ts, st->m, st->shist,
-                                                     st->cnt.sample);
+        k_sample<1><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
+                                                     clip_on, st->ts, st->m, st->shist);
+        k_window<1><<<T, kBlock, 0, stream>>>(st->L, st->K, st->shist, st->ts,
+                                              force_dense);
     }
     DGC_LAUNCH_CHECK();
     if (p.P > 0) {
@@ -520,35 +514,35 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         int64_t fb = st->fused_blocks > 0 ? st->fused_blocks : cdiv(p.P, kWavesPerBlock);
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
-            g, st->u, st->v, st->L, st->K, st->ts, st->sc, clip_on, force_dense, st->m,
-            st->slots, st->run_cnt, p.P, out_norm, out_scale);
+            g, st->u, st->v, st->L, st->ts, st->sc, clip_on, st->m, st->slots,
+            st->run_cnt, p.P, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (p.G > 0)
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
-                                           st->atiles, st->aoff, st->amap, st->cnt.scan,
-                                           force_dense);
+                                           st->atiles);
     if (p.G > 0)
         k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots, st->run_cnt,
                                                   st->goff, st->olist);
+    k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
+    k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
     DGC_LAUNCH_CHECK();
     if (K > 0) {
         const int hg = grid_for(p.TT, pg);
-        const size_t T_ = size_t(T);
         k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
-                                             st->aoff, st->atiles, st->hist,
-                                             st->cnt.hist, st->sc);
+                                             st->aoff, st->hist);
+        k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
         k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
-                                             st->aoff, st->atiles, st->hist,
-                                             st->cnt.hist + T_, st->sc);
+                                             st->aoff, st->hist);
+        k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
         k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
-                                             st->aoff, st->atiles, st->hist,
-                                             st->cnt.hist + 2 * T_, st->sc);
+                                             st->aoff, st->hist);
+        k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
         DGC_LAUNCH_CHECK();
-        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
-                                                st->aoff, st->atiles, st->ta, st->tb,
-                                                st->tc, st->cnt.emit);
+        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist,
+                                                st->amap, st->aoff, st->ta);
+        k_emit_scan<<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
         k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
                                                 st->olist, st->amap, st->aoff, st->tb,
                                                 st->tc, out_idx, out_val, st->sc);

@@ -5,33 +5,24 @@
 // largest |v| entries, momentum factor masking.  Selection is exact top-k
 // per tensor with ties to the lower index.
 //
-// Launches for one step (all on the caller's stream, no host sync):
-//   norm           binary64 sum of g^2 (only with clipping); the last block
-//                  to finish forms the norm and the scale
-//   sample<0>,<1>  per tensor, keys of the would-be v on sampled 32-element
-//                  lines; the last block of each tensor places the
-//                  candidate threshold (11-bit bin, then 10-bit sub-bin)
-//   fused          u, v update (20 B/elem); keys >= threshold are written,
-//                  index-ordered, into the fixed slots of their
-//                  1024-element piece (no atomics)
-//   group_sum      candidate count per group of 256 pieces
-//   group_scan     per tensor: the source (candidates when none overflowed
-//                  and there are at least k, else the whole tensor); the
-//                  last block maps the active 4096-item tiles
-//   gather         the pieces' runs -> one index-ordered candidate list
-//   hist<0..2>     radix digits (11, 10, 10 bits); the last block of each
-//                  tensor resolves the digit -> at the end the k-th largest
-//                  key T and the tie quota r
-//   emit_count     (>T, ==T) per tile; the last block of each tensor scans
-//   emit_write     index-ordered output of {key > T} plus the first r ties,
-//                  and u = v = +0 there
-//
-// "Last block" finalisation: every block adds to a per-tensor (or global)
-// counter after its writes and a device-scope fence; the block that brings
-// the counter to its expected value does the finalising work after another
-// fence, reading the other blocks' results with device-scope loads, and
-// resets the counter.  Nothing waits on another block, and the result does
-// not depend on which block comes last.
+// Pass structure for one step (all on the caller's stream, no host sync):
+//   norm_partial/norm_final  binary64 sum of g^2 (only with clipping)
+//                            (kernel boundaries order the passes: a
+//                            device-scope fence per workgroup costs more on
+//                            this chip than the extra launches)
+//   sample/window            per tensor, keys of the would-be v on sampled
+//                            32-element lines -> a candidate threshold lo
+//   fused                    u, v update (20 B/elem); keys >= lo are
+//                            written, index-ordered, into the fixed slots of
+//                            their 1024-element piece (no atomics)
+//   group_sum/scan, gather   per tensor: choose the source (candidates when
+//                            none overflowed and there are at least k, else
+//                            the whole tensor); concatenate the pieces' runs
+//                            into one index-ordered candidate list
+//   hist<D>/resolve<D>       three radix digits (11,10,10 bits) -> the k-th
+//                            largest key T and the tie quota r
+//   emit_count/scan/write    index-ordered output of {key > T} plus the
+//                            first r ties, and u = v = +0 there
 #pragma once
 
 #include "dgc_device.hpp"
@@ -51,50 +42,9 @@ __device__ __forceinline__ void st_stream(float* p, float a, float b, float c, f
     __builtin_nontemporal_store(x, reinterpret_cast<f4v*>(p));
 }
 
-// Device-scope (all XCDs) loads and stores of values other blocks of the
-// same launch exchange.
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ void st_dev(T* p, T x) {
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// ---------------------------------------------------------------- prep
 
-// Arrival of this block at `counter` with weight `inc`; true in the one
-// block whose arrival completes `expected` (that block then sees every
-// arriving block's earlier writes, and the counter is reset to 0).  Every
-// thread of the block must call it.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t inc,
-                                            uint32_t expected) {
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t prev = atomicAdd(counter, inc);
-        int last = prev + inc == expected;
-        if (last) st_dev(counter, 0u);
-        s_last = last;
-    }
-    __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __threadfence();
-    return last;
-}
-
-// Counters in the workspace (all start at zero).
-struct Counters {
-    uint32_t* norm;     // [1]
-    uint32_t* scan;     // [1] group_scan -> active map
-    uint32_t* sample;   // [2][T]
-    uint32_t* hist;     // [3][T]
-    uint32_t* emit;     // [T]
-};
-
-// ---------------------------------------------------------------- fill
-
-// Fill `n` 32-bit words (a fill kernel: safe inside captured graphs).
+// Zero `n` 32-bit words (a fill kernel: safe inside captured graphs).
 __global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* __restrict__ p,
                                                      int64_t n, uint32_t val) {
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n;
@@ -102,7 +52,8 @@ __global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* __restrict__ p,
         p[i] = val;
 }
 
-// Scalar outputs when nothing else writes them (an empty layout).
+// Scalar outputs when nothing else writes them (an empty layout with
+// clipping off).
 __global__ void k_set_scalars(Scalars* __restrict__ sc, double* __restrict__ out_norm,
                               float* __restrict__ out_scale) {
     if (threadIdx.x == 0) {
@@ -118,14 +69,9 @@ __global__ void k_set_scalars(Scalars* __restrict__ sc, double* __restrict__ out
 // Block b sums g^2 over [b*kNormChunk, min(n, (b+1)*kNormChunk)) in
 // binary64: thread-strided float4 loads, one accumulator per float4 lane
 // slot, then a fixed-order block reduction.  The squares of binary32 values
-// are exact in binary64, so only the additions round.  The last block sums
-// the partials in a fixed order: S, norm = sqrt(S), and
-// s = (float)(clip / norm) if norm > clip else 1 (binary64, one rounding to
-// binary32 at the end).
-__global__ __launch_bounds__(kBlock) void k_norm(
-    const float* __restrict__ g, int64_t n, double* __restrict__ partial,
-    uint32_t* __restrict__ counter, double clip, Scalars* __restrict__ sc,
-    double* __restrict__ out_norm, float* __restrict__ out_scale) {
+// are exact in binary64, so only the additions round.
+__global__ __launch_bounds__(kBlock) void k_norm_partial(
+    const float* __restrict__ g, int64_t n, double* __restrict__ partial) {
     __shared__ double lds[kWavesPerBlock];
     const int64_t lo = int64_t(blockIdx.x) * kNormChunk;
     const int64_t hi = min(n, lo + kNormChunk);
@@ -154,92 +100,33 @@ __global__ __launch_bounds__(kBlock) void k_norm(
     // tail elements beyond the last whole float4 (only the last block)
     for (int64_t e = (vhi << 2) + threadIdx.x; e < hi; e += kBlock)
         a0 += double(g[e]) * double(g[e]);
-    const double s = block_sum_fixed((a0 + a1) + (a2 + a3), lds);
-    if (threadIdx.x == 0) st_dev(&partial[blockIdx.x], s);
-    if (!arrive_last(counter, 1u, gridDim.x)) return;
+    double s = block_sum_fixed((a0 + a1) + (a2 + a3), lds);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+// One block: S = fixed-order sum of the partials; norm = sqrt(S);
+// s = (float)(clip / norm) if norm > clip else 1 (all in binary64, one
+// rounding to binary32 at the end).
+__global__ __launch_bounds__(kBlock) void k_norm_final(
+    const double* __restrict__ partial, int64_t nb, double clip,
+    Scalars* __restrict__ sc, double* __restrict__ out_norm,
+    float* __restrict__ out_scale) {
+    __shared__ double lds[kWavesPerBlock];
     double a = 0.0;
-    for (int64_t j = threadIdx.x; j < int64_t(gridDim.x); j += kBlock) a += ld_dev(&partial[j]);
-    const double S = block_sum_fixed(a, lds);
+    for (int64_t i = threadIdx.x; i < nb; i += kBlock) a += partial[i];
+    double S = block_sum_fixed(a, lds);
     if (threadIdx.x == 0) {
-        const double norm = sqrt(S);
-        float sc32 = 1.0f;
-        if (clip > 0.0 && norm > clip) sc32 = float(clip / norm);
+        double norm = sqrt(S);
+        float s = 1.0f;
+        if (clip > 0.0 && norm > clip) s = float(clip / norm);
         sc->norm = norm;
-        sc->scale = sc32;
+        sc->scale = s;
         if (out_norm) *out_norm = norm;
-        if (out_scale) *out_scale = sc32;
+        if (out_scale) *out_scale = s;
     }
 }
 
 // ---------------------------------------------------------------- sample
-
-// Place tensor t's candidate threshold lo just below the j-th largest
-// sampled key, j = ceil(mu + 6 sqrt(mu) + 8) where mu = S*k/n is how many of
-// the S samples the true top k should hold.  Level 0 finds the top-11-bit
-// bin holding the j-th key (wbin) and how many samples lie above it
-// (wabove); level 1 finds the 10-bit sub-bin inside it, and lo is that
-// sub-bin's lower edge.  Runs in the last sample block of the tensor; clears
-// the histogram row for the next use.
-template <int LEVEL>
-__device__ __forceinline__ void window_finalize(int t, const DevK& K,
-                                                const DevLayout& L,
-                                                uint32_t* __restrict__ row,
-                                                TensorState* __restrict__ ts) {
-    constexpr int bins = LEVEL == 0 ? kBins0 : 1024;
-    constexpr int per = bins / kBlock;
-    __shared__ uint32_t lds[kWavesPerBlock];
-    const int64_t nt = L.o[t + 1] - L.o[t];
-    const int64_t k = K.k[t];
-    uint32_t c[per];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        c[q] = ld_dev(&row[bins - 1 - (threadIdx.x * per + q)]);
-        mine += c[q];
-    }
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan(mine, lds, total);
-#pragma unroll
-    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
-    if (LEVEL == 0) {
-        // defaults first, then at most one thread overwrites them
-        if (threadIdx.x == 0) {
-            ts[t].lo_key = kNoKey;
-            ts[t].wbin = kNoKey;
-        }
-        __syncthreads();
-        if (k <= 0) return;
-        const double mu = double(total) * double(k) / double(nt);
-        const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
-        if (jd > double(total)) {  // (nearly) everything: take all elements
-            if (threadIdx.x == 0) ts[t].lo_key = 0;
-            return;
-        }
-        const uint32_t j = uint32_t(jd);
-        uint32_t run = above;
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            if (run < j && j <= run + c[q]) {
-                ts[t].wbin = uint32_t(kBins0 - 1 - (threadIdx.x * per + q));
-                ts[t].wabove = run;
-                ts[t].wj = j;
-            }
-            run += c[q];
-        }
-    } else {
-        const uint32_t jr = ts[t].wj - ts[t].wabove;  // rank inside wbin
-        const uint32_t wbin = ts[t].wbin;
-        uint32_t run = above;
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            if (run < jr && jr <= run + c[q]) {
-                uint32_t b2 = uint32_t(bins - 1 - (threadIdx.x * per + q));
-                ts[t].lo_key = (wbin << 20) | (b2 << 10);
-            }
-            run += c[q];
-        }
-    }
-}
 
 // Keys of the would-be v on sampled lines.  Block b belongs to one tensor
 // (smap); it visits kLinesPerSampleBlock of the tensor's sampled lines, one
@@ -247,21 +134,20 @@ __device__ __forceinline__ void window_finalize(int t, const DevK& K,
 // the j-th of slines equal strides, so sampling does not alias with the
 // tensor's row structure.  Level 0 histograms the top 11 key bits; level 1
 // revisits the same lines and histograms the next 10 bits of the keys whose
-// top 11 bits equal the bin chosen by level 0.  The tensor's last block
-// places the window.
+// top 11 bits equal the bin chosen by level 0.
 template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_sample(
     const float* __restrict__ g, const float* __restrict__ u,
-    const float* __restrict__ v, DevLayout L, DevK K,
-    const Scalars* __restrict__ sc, int clip_on, TensorState* __restrict__ ts,
-    float m, uint32_t* __restrict__ shist, uint32_t* __restrict__ counters) {
+    const float* __restrict__ v, DevLayout L, const Scalars* __restrict__ sc,
+    int clip_on, const TensorState* __restrict__ ts, float m,
+    uint32_t* __restrict__ shist) {
     __shared__ uint32_t h[kBins0];
+    for (int b = threadIdx.x; b < kBins0; b += kBlock) h[b] = 0;
+    __syncthreads();
     const int64_t sb = blockIdx.x;
     const int t = int(L.smap[sb]);
     const uint32_t wbin = LEVEL == 1 ? ts[t].wbin : 0u;
-    if (LEVEL == 1 && wbin == kNoKey) return;  // uniform; no block of t arrives
-    for (int b = threadIdx.x; b < kBins0; b += kBlock) h[b] = 0;
-    __syncthreads();
+    if (LEVEL == 1 && wbin == kNoKey) return;  // uniform: window already set
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t lines = (nt + kLine - 1) / kLine;
     const int64_t ls = L.slines[t];
@@ -286,20 +172,83 @@ __global__ __launch_bounds__(kBlock) void k_sample(
     uint32_t* row = shist + int64_t(t) * kHistBins;
     for (int b = threadIdx.x; b < kBins0; b += kBlock)
         if (h[b]) atomicAdd(&row[b], h[b]);
-    const uint32_t nblocks = uint32_t(L.sbase[t + 1] - L.sbase[t]);
-    if (!arrive_last(&counters[int64_t(LEVEL) * L.T + t], 1u, nblocks)) return;
-    window_finalize<LEVEL>(t, K, L, row, ts);
+}
+
+// One block per tensor: place the candidate threshold lo just below the
+// j-th largest sampled key, j = ceil(mu + 6 sqrt(mu) + 8) where mu = S*k/n
+// is how many of the S samples the true top k should hold.  Level 0 finds
+// the top-11-bit bin holding the j-th key (wbin) and how many samples lie
+// above it (wabove); level 1 finds the 10-bit sub-bin inside it, and lo is
+// that sub-bin's lower edge.  Small tensors (no sampled lines) and k = 0
+// get no candidates.  Clears the histogram row for the next use.
+template <int LEVEL>
+__global__ __launch_bounds__(kBlock) void k_window(
+    DevLayout L, DevK K, uint32_t* __restrict__ shist,
+    TensorState* __restrict__ ts, int force_dense) {
+    constexpr int bins = LEVEL == 0 ? kBins0 : 1024;
+    constexpr int per = bins / kBlock;
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    const int64_t k = K.k[t];
+    uint32_t* row = shist + int64_t(t) * kHistBins;
+    if (LEVEL == 1 && ts[t].wbin == kNoKey) return;  // decided at level 0
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        c[q] = row[bins - 1 - (threadIdx.x * per + q)];
+        mine += c[q];
+    }
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(mine, lds, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
+    if (LEVEL == 0) {
+        // Defaults first (no candidates, no second level), then at most one
+        // thread overwrites them.  No candidates sends a tensor with k > 0
+        // to the dense path: small tensors, the forced dense path, or a
+        // window that found no bin.
+        if (threadIdx.x == 0) {
+            ts[t].lo_key = kNoKey;
+            ts[t].wbin = kNoKey;
+        }
+        __syncthreads();
+        if (k <= 0 || force_dense || L.slines[t] == 0) return;
+        const double mu = double(total) * double(k) / double(nt);
+        const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
+        if (jd > double(total)) {  // (nearly) everything: take all elements
+            if (threadIdx.x == 0) ts[t].lo_key = 0;
+            return;
+        }
+        const uint32_t j = uint32_t(jd);
+        uint32_t run = above;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            if (run < j && j <= run + c[q]) {
+                ts[t].wbin = uint32_t(kBins0 - 1 - (threadIdx.x * per + q));
+                ts[t].wabove = run;
+                ts[t].wj = j;
+            }
+            run += c[q];
+        }
+    } else {
+        __syncthreads();  // every thread has read wbin before it may change
+        const uint32_t jr = ts[t].wj - ts[t].wabove;  // rank inside wbin
+        const uint32_t wbin = ts[t].wbin;
+        uint32_t run = above;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            if (run < jr && jr <= run + c[q]) {
+                uint32_t b2 = uint32_t(bins - 1 - (threadIdx.x * per + q));
+                ts[t].lo_key = (wbin << 20) | (b2 << 10);
+            }
+            run += c[q];
+        }
+    }
 }
 
 // ---------------------------------------------------------------- fused
-
-// Candidate threshold of tensor t for this call.
-__device__ __forceinline__ uint32_t window_key(const DevLayout& L, const DevK& K,
-                                               const TensorState* ts, int t,
-                                               int force_dense) {
-    const bool windowed = !force_dense && L.slines[t] > 0 && K.k[t] > 0;
-    return windowed ? ts[t].lo_key : kNoKey;
-}
 
 // Element-wise momentum correction + accumulation, and candidate output.
 // A wave owns one piece (<= 1024 elements, one tensor).  It loads g, u, v
@@ -312,8 +261,8 @@ __device__ __forceinline__ uint32_t window_key(const DevLayout& L, const DevK& K
 template <bool kAligned>
 __device__ __forceinline__ void fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    int64_t e0, int64_t e1, int t, const DevLayout& L, const DevK& K,
-    const TensorState* __restrict__ ts, int force_dense, float s, float m,
+    int64_t e0, int64_t e1, int t, const DevLayout& L,
+    const TensorState* __restrict__ ts, float s, float m,
     uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt, int64_t p) {
     const int lane = lane_id();
     float vn[4][4];
@@ -344,7 +293,7 @@ __device__ __forceinline__ void fused_piece(
                 vv[i] = make_float4(tv[0], tv[1], tv[2], tv[3]);
             }
         }
-        lo = window_key(L, K, ts, t, force_dense);
+        lo = ts[t].lo_key;
         o = L.o[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -371,7 +320,7 @@ __device__ __forceinline__ void fused_piece(
         // Unaligned piece start: 16 scalar rounds of 64 consecutive elements.
         // Element (i, c) of a lane is e0 + (i*4 + c)*64 + lane; ranks below
         // follow (i, c, lane) order, which is index order here.
-        lo = window_key(L, K, ts, t, force_dense);
+        lo = ts[t].lo_key;
         o = L.o[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -438,15 +387,13 @@ __device__ __forceinline__ void fused_piece(
     }
 }
 
-// Tensors without a sample window (small ones, k = 0, or the dense path
-// forced) get no candidates.  With clipping off the scale is 1 and block 0
-// also writes the call's scalar outputs (norm -1, scale 1).
+// With clipping off the scale is 1 and block 0 also writes the call's
+// scalar outputs (norm -1, scale 1).
 __global__ __launch_bounds__(kBlock) void k_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    DevLayout L, DevK K, const TensorState* __restrict__ ts,
-    Scalars* __restrict__ sc, int clip_on, int force_dense, float m,
-    uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt, int64_t n_pieces,
-    double* __restrict__ out_norm, float* __restrict__ out_scale) {
+    DevLayout L, const TensorState* __restrict__ ts, Scalars* __restrict__ sc,
+    int clip_on, float m, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
+    int64_t n_pieces, double* __restrict__ out_norm, float* __restrict__ out_scale) {
     const float s = clip_on ? sc->scale : 1.0f;
     if (!clip_on && blockIdx.x == 0 && threadIdx.x == 0) {
         sc->norm = -1.0;
@@ -462,11 +409,9 @@ __global__ __launch_bounds__(kBlock) void k_fused(
         const int64_t e0 = d.start;
         const int64_t e1 = e0 + d.len;
         if ((e0 & 3) == 0)
-            fused_piece<true>(g, u, v, e0, e1, t, L, K, ts, force_dense, s, m, slots,
-                              run_cnt, p);
+            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
         else
-            fused_piece<false>(g, u, v, e0, e1, t, L, K, ts, force_dense, s, m, slots,
-                               run_cnt, p);
+            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
     }
 }
 
@@ -495,14 +440,11 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
 // One block per tensor: scan its groups' counts (their offsets in the
 // ordered list), then choose the selection source: the candidate list when
 // no piece overflowed and there are at least k candidates, else the whole
-// tensor, and count the source's 4096-item tiles.  The last block to finish
-// lays out the active tiles of all tensors: aoff (exclusive scan of the
-// counts) and amap (tensor of each active tile).
+// tensor.  Also counts the source's 4096-item tiles for the active-tile map.
 __global__ __launch_bounds__(kBlock) void k_group_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
     const uint32_t* __restrict__ gsum, uint32_t* __restrict__ goff,
-    uint32_t* __restrict__ atiles, uint32_t* __restrict__ aoff,
-    uint32_t* __restrict__ amap, uint32_t* __restrict__ counter, int force_dense) {
+    uint32_t* __restrict__ atiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
@@ -530,32 +472,13 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
     else mode = kModeList;
     const int64_t len = mode == kModeList ? int64_t(carry) : nt;
     if (threadIdx.x == 0) {
-        if (window_key(L, K, ts, t, force_dense) == kNoKey) ts[t].lo_key = kNoKey;
         ts[t].total = carry;
         ts[t].overflow = uint32_t(over);
         ts[t].mode = mode;
         ts[t].len = uint32_t(len);
         ts[t].prefix = 0;
         ts[t].krem = uint32_t(k > 0 ? k : 0);
-        st_dev(&atiles[t], mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift));
-    }
-    if (!arrive_last(counter, 1u, uint32_t(L.T))) return;
-    // active tile layout of all tensors
-    uint32_t run = 0;
-    for (int base = 0; base < L.T; base += kBlock) {
-        int tt = base + threadIdx.x;
-        uint32_t c = tt < L.T ? ld_dev(&atiles[tt]) : 0u;
-        uint32_t tot;
-        uint32_t ex = block_exclusive_scan(c, lds, tot);
-        if (tt < L.T) st_dev(&aoff[tt], run + ex);
-        run += tot;
-    }
-    if (threadIdx.x == 0) st_dev(&aoff[L.T], run);
-    __threadfence();
-    __syncthreads();
-    for (int tt = 0; tt < L.T; ++tt) {
-        const uint32_t a0 = ld_dev(&aoff[tt]), na = ld_dev(&atiles[tt]);
-        for (uint32_t jj = threadIdx.x; jj < na; jj += kBlock) amap[a0 + jj] = uint32_t(tt);
+        atiles[t] = mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift);
     }
 }
 
@@ -598,6 +521,31 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     }
 }
 
+// One block: exclusive scan of the active tile counts -> aoff[T+1].
+__global__ __launch_bounds__(kBlock) void k_active_scan(
+    int T, const uint32_t* __restrict__ atiles, uint32_t* __restrict__ aoff) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    uint32_t carry = 0;
+    for (int base = 0; base < T; base += kBlock) {
+        int t = base + threadIdx.x;
+        uint32_t c = t < T ? atiles[t] : 0;
+        uint32_t tot;
+        uint32_t ex = block_exclusive_scan(c, lds, tot);
+        if (t < T) aoff[t] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) aoff[T] = carry;
+}
+
+// One block per tensor: amap[a] = t for the tensor's active tiles.
+__global__ __launch_bounds__(kBlock) void k_active_map(
+    const uint32_t* __restrict__ atiles, const uint32_t* __restrict__ aoff,
+    uint32_t* __restrict__ amap) {
+    const int t = blockIdx.x;
+    const uint32_t a0 = aoff[t], n = atiles[t];
+    for (uint32_t j = threadIdx.x; j < n; j += kBlock) amap[a0 + j] = uint32_t(t);
+}
+
 // ---------------------------------------------------------------- select
 
 template <int D>
@@ -606,46 +554,12 @@ template <> struct Digit<0> { static constexpr int shift = 20, bits = 11; };
 template <> struct Digit<1> { static constexpr int shift = 10, bits = 10; };
 template <> struct Digit<2> { static constexpr int shift = 0, bits = 10; };
 
-// Find the bin of digit D holding the krem-th largest matching key of
-// tensor t; extend the prefix and reduce krem; clear the histogram row.
-// After D = 2, prefix is the k-th largest key T and krem is the number of
-// keys equal to T to take (r).  Runs in the tensor's last histogram block.
-template <int D>
-__device__ __forceinline__ void resolve_digit(int t, uint32_t* __restrict__ row,
-                                              TensorState* __restrict__ ts,
-                                              Scalars* __restrict__ sc) {
-    constexpr int bins = 1 << Digit<D>::bits;
-    constexpr int per = bins / kBlock;
-    __shared__ uint32_t lds[kWavesPerBlock];
-    __shared__ int found;
-    uint32_t c[per];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        c[q] = ld_dev(&row[bins - 1 - (threadIdx.x * per + q)]);
-        mine += c[q];
-    }
-    if (threadIdx.x == 0) found = 0;
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan(mine, lds, total);
-#pragma unroll
-    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
-    const uint32_t krem = ts[t].krem;
-    const uint32_t prefix = ts[t].prefix;
-    __syncthreads();  // every thread has read prefix/krem before the update
-    uint32_t run = above;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        if (run < krem && krem <= run + c[q]) {
-            uint32_t b = uint32_t(bins - 1 - (threadIdx.x * per + q));
-            ts[t].prefix = (prefix << Digit<D>::bits) | b;
-            ts[t].krem = krem - run;
-            found = 1;
-        }
-        run += c[q];
-    }
+__device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
     __syncthreads();
-    if (threadIdx.x == 0 && !found) latch_error(sc, kErrInternal);
+    for (int b = threadIdx.x; b < kHistBins; b += kBlock) {
+        uint32_t c = h[b];
+        if (c) { atomicAdd(&row[b], c); h[b] = 0; }
+    }
     __syncthreads();
 }
 
@@ -654,17 +568,13 @@ __device__ __forceinline__ void resolve_digit(int t, uint32_t* __restrict__ row,
 // tensor's source (candidate list or whole tensor), clipped to len.
 
 // Histogram of digit D over the keys that match the prefix found so far.
-// Workgroups stride over the active tiles, keeping one tensor's histogram
-// in LDS across consecutive tiles; each flush adds it to the tensor's row
-// and reports the tiles it covers; the block that completes a tensor
-// resolves the digit.
+// Workgroups stride over the active tiles.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_hist(
-    DevLayout L, TensorState* __restrict__ ts, const float* __restrict__ v,
-    const uint2* __restrict__ olist, const uint32_t* __restrict__ amap,
-    const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ atiles,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
-    Scalars* __restrict__ sc) {
+    DevLayout L, const TensorState* __restrict__ ts,
+    const float* __restrict__ v, const uint2* __restrict__ olist,
+    const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
+    uint32_t* __restrict__ hist) {
     constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
     constexpr uint32_t dmask = (1u << bits) - 1;
     __shared__ uint32_t h[kHistBins];
@@ -672,27 +582,15 @@ __global__ __launch_bounds__(kBlock) void k_hist(
     __syncthreads();
     const uint32_t A = aoff[L.T];
     int cur_t = -1;
-    uint32_t cur_n = 0;
-    auto flush = [&](int tt, uint32_t ntiles) {
-        uint32_t* row = hist + int64_t(tt) * kHistBins;
-        __syncthreads();
-        for (int b = threadIdx.x; b < kHistBins; b += kBlock) {
-            uint32_t c = h[b];
-            if (c) { atomicAdd(&row[b], c); h[b] = 0; }
-        }
-        if (arrive_last(&counters[tt], ntiles, atiles[tt])) resolve_digit<D>(tt, row, ts, sc);
-    };
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
         const int t = int(amap[a]);
-        if (t != cur_t) {
-            if (cur_t >= 0) flush(cur_t, cur_n);
-            cur_t = t;
-            cur_n = 0;
-        }
-        ++cur_n;
         const uint32_t mode = ts[t].mode;
         const int64_t len = ts[t].len;
         const int64_t i0 = int64_t(a - aoff[t]) * kTile;
+        if (t != cur_t) {
+            if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
+            cur_t = t;
+        }
         const uint32_t prefix = ts[t].prefix;
         const int64_t i1 = min(len, i0 + kTile);
         if (mode == kModeDense) {
@@ -711,7 +609,52 @@ __global__ __launch_bounds__(kBlock) void k_hist(
             }
         }
     }
-    if (cur_t >= 0) flush(cur_t, cur_n);
+    if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
+}
+
+// One block per tensor: find the bin of digit D holding the krem-th largest
+// matching key; extend the prefix and reduce krem.  Clears the histogram.
+// After D = 2, prefix is the k-th largest key T and krem is the number of
+// keys equal to T to take (r).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_resolve(
+    TensorState* __restrict__ ts, uint32_t* __restrict__ hist,
+    Scalars* __restrict__ sc) {
+    constexpr int bins = 1 << Digit<D>::bits;
+    constexpr int per = bins / kBlock;
+    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ int found;
+    const int t = blockIdx.x;
+    if (ts[t].mode == kModeSkip) return;
+    uint32_t* row = hist + int64_t(t) * kHistBins;
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        c[q] = row[bins - 1 - (threadIdx.x * per + q)];
+        mine += c[q];
+    }
+    if (threadIdx.x == 0) found = 0;
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(mine, lds, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
+    const uint32_t krem = ts[t].krem;
+    const uint32_t prefix = ts[t].prefix;
+    __syncthreads();  // every thread has read prefix/krem before the update
+    uint32_t run = above;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            uint32_t b = uint32_t(bins - 1 - (threadIdx.x * per + q));
+            ts[t].prefix = (prefix << Digit<D>::bits) | b;
+            ts[t].krem = krem - run;
+            found = 1;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && !found) latch_error(sc, kErrInternal);
 }
 
 // ---------------------------------------------------------------- emit
@@ -726,15 +669,12 @@ __device__ __forceinline__ uint2 source_item(uint32_t mode, const float* vt_,
 // Tiles are visited in 16 rounds of 256 consecutive items (item
 // i0 + 256 q + tid), so every load and store of a round is coalesced.
 
-// Per active tile: packed (#key > T) << 16 | #key == T.  The block that
-// completes a tensor scans its tiles' counts into per-tile offsets.
+// Per active tile: packed (#key > T) << 16 | #key == T.
 __global__ __launch_bounds__(kBlock) void k_emit_count(
     DevLayout L, const TensorState* __restrict__ ts,
     const float* __restrict__ v, const uint2* __restrict__ olist,
     const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
-    const uint32_t* __restrict__ atiles, uint32_t* __restrict__ tile_cnt,
-    uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq,
-    uint32_t* __restrict__ counters) {
+    uint32_t* __restrict__ tile_cnt) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const uint32_t A = aoff[L.T];
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
@@ -756,21 +696,27 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
         }
         uint32_t tot;
         block_exclusive_scan(cnt, lds, tot);
-        if (threadIdx.x == 0) st_dev(&tile_cnt[a], tot);
-        if (!arrive_last(&counters[t], 1u, atiles[t])) continue;
-        // the tensor's tiles are all counted: exclusive scans of both counts
-        const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
-        uint32_t cg = 0, ce = 0;
-        for (uint32_t base = a0; base < a1; base += kBlock) {
-            uint32_t aa = base + threadIdx.x;
-            uint32_t x = aa < a1 ? ld_dev(&tile_cnt[aa]) : 0u;
-            uint32_t tg, te;
-            uint32_t eg = block_exclusive_scan(x >> 16, lds, tg);
-            uint32_t ee = block_exclusive_scan(x & 0xFFFFu, lds, te);
-            if (aa < a1) { off_gt[aa] = cg + eg; off_eq[aa] = ce + ee; }
-            cg += tg;
-            ce += te;
-        }
+        if (threadIdx.x == 0) tile_cnt[a] = tot;
+    }
+}
+
+// One block per tensor: exclusive scan of its tiles' (>T, ==T) counts.
+__global__ __launch_bounds__(kBlock) void k_emit_scan(
+    const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ tile_cnt,
+    uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
+    uint32_t cg = 0, ce = 0;
+    for (uint32_t base = a0; base < a1; base += kBlock) {
+        uint32_t a = base + threadIdx.x;
+        uint32_t x = a < a1 ? tile_cnt[a] : 0;
+        uint32_t tg, te;
+        uint32_t eg = block_exclusive_scan(x >> 16, lds, tg);
+        uint32_t ee = block_exclusive_scan(x & 0xFFFFu, lds, te);
+        if (a < a1) { off_gt[a] = cg + eg; off_eq[a] = ce + ee; }
+        cg += tg;
+        ce += te;
     }
 }
 
