@@ -31,7 +31,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_flat1b_traffic.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "sparsified_gradient_compression_amd", "csrc", f)
-    for f in ("dgc_device.hpp", "kernels_compress.hpp")
+    for f in ("dgc_device.hpp", "kernel_fused.hpp")
 ]
 
 

@@ -19,8 +19,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdgc.so")
 SOURCES = [os.path.join(CSRC, "dgc_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in
-                     ("dgc_device.hpp", "kernels_compress.hpp",
-                      "kernels_codec.hpp")] + [os.path.join(ROOT, "include", "dgc.h")]
+                     ("dgc_device.hpp", "kernel_fused.hpp",
+                      "kernels_compress.hpp", "kernels_codec.hpp")] + [os.path.join(ROOT, "include", "dgc.h")]
 
 ARCH = os.environ.get("DGC_OFFLOAD_ARCH", "gfx950")
 

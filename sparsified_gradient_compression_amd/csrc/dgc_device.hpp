@@ -13,11 +13,16 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;                 // threads per workgroup (4 waves)
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// Element-wise pass: one wave owns one "piece" of up to 1024 consecutive
-// elements of one tensor (64 lanes x 4 float4).  Candidates of a piece are
-// written as one index-ordered run.
-constexpr int kPieceShift = 10;
+// Element-wise pass: one wave owns one "piece" of kPiece consecutive
+// elements of one tensor (64 lanes x kRounds float4).  Candidates of a
+// piece are written as one index-ordered run.
+#ifndef DGC_PIECE_SHIFT
+#define DGC_PIECE_SHIFT 10
+#endif
+constexpr int kPieceShift = DGC_PIECE_SHIFT;
 constexpr int64_t kPiece = int64_t(1) << kPieceShift;
+constexpr int kRounds = int(kPiece / (4 * 64));
+static_assert(kRounds >= 1 && kRounds <= 8, "piece of 256..2048 elements");
 // Pieces are scanned in groups of 256 (one workgroup per group).
 constexpr int64_t kGroup = 256;
 

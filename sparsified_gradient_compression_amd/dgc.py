@@ -37,7 +37,9 @@ class DGCError(RuntimeError):
 
 
 def lib_path() -> str:
-    return _build.LIB
+    """The library to load: DGC_LIBRARY if set (an alternative build of the
+    same sources), else the in-tree build."""
+    return os.environ.get("DGC_LIBRARY") or _build.LIB
 
 
 def lib() -> ctypes.CDLL:
@@ -45,7 +47,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = _build.LIB
+    path = lib_path()
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with "
