@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one plain device copy "
                          "of 1 GiB (for scaling hardware byte counters)")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="run the learners back to back on one stream")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
     return ap.parse_args()
@@ -162,18 +164,55 @@ def main():
     for L in learners:
         L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
     dense = torch.zeros(n, dtype=torch.float32, device="cuda")
+    main = torch.cuda.current_stream()
+    pipeline = not args.no_pipeline
+    if pipeline:
+        # One stream per learner.  Learner w+1 starts once learner w's
+        # element-wise pass is done (event recorded by the library), so its
+        # clip norm and element-wise pass overlap learner w's short selection
+        # and encode kernels, and no two element-wise passes overlap.
+        streams = [torch.cuda.Stream() for _ in learners]
+        fused_ev = [torch.cuda.Event() for _ in learners]
+        for L, ev in zip(learners, fused_ev):
+            L.set_fused_event(ev)
+        zero_stream = torch.cuda.Stream()
 
     def one_step(s):
         t = s % gsteps
         k = ks[t]
-        for w, L in enumerate(learners):
-            L.compress(grads[(w, t)], k, wl.clip)
+        if not pipeline:
+            for w, L in enumerate(learners):
+                L.compress(grads[(w, t)], k, wl.clip)
+                if not args.fused_only:
+                    L.encode(k)
             if not args.fused_only:
-                L.encode(k)
+                dense.zero_()
+                dgc.decode_accumulate(learners[0],
+                                      [(L.runs, L.vals, L.entries) for L in learners],
+                                      dense)
+            return
+        for w, L in enumerate(learners):
+            st = streams[w]
+            if w == 0:
+                st.wait_stream(main)  # the previous step's decode is done
+            else:
+                st.wait_event(fused_ev[w - 1])
+            with torch.cuda.stream(st):
+                L.compress(grads[(w, t)], k, wl.clip, stream=st)
+                if not args.fused_only:
+                    L.encode(k, stream=st)
         if not args.fused_only:
-            dense.zero_()
+            zero_stream.wait_event(fused_ev[-1])
+            with torch.cuda.stream(zero_stream):
+                dense.zero_()
+            for st in streams + [zero_stream]:
+                main.wait_stream(st)
             dgc.decode_accumulate(learners[0],
-                                  [(L.runs, L.vals, L.entries) for L in learners], dense)
+                                  [(L.runs, L.vals, L.entries) for L in learners], dense,
+                                  stream=main)
+        else:
+            for st in streams:
+                main.wait_stream(st)
 
     for s in range(args.warmup):
         one_step(s)
@@ -268,6 +307,7 @@ def main():
             "compress_pipeline_frac_of_peak": round(
                 pipeline_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "compress_G_elem_per_s": round(n / (compress_ms * 1e-3) / 1e9, 2),
+            "learner_pipelining": pipeline,
             "select_path_window_dense": [int(sum(p[0] for p in path)),
                                          int(sum(p[1] for p in path))],
             "overflow_tensors": int(info[:, 3].sum()),

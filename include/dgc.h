@@ -207,6 +207,17 @@ int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense);
  */
 int dgc_get_select_info(dgc_state* st, int64_t* info);
 
+/*
+ * Pipelining hook: record `ev` on the call's stream right after each
+ * dgc_compress of this state has enqueued its element-wise pass (the one
+ * that streams g, u and v).  A caller running several learners can make the
+ * next learner's stream wait on it, so that learner's bandwidth-heavy
+ * passes start while this one finishes its short selection kernels, and no
+ * two element-wise passes overlap.  NULL turns it off.  The event stays
+ * the caller's.  Returns DGC_OK or DGC_EINVAL.
+ */
+int dgc_set_fused_event(dgc_state* st, hipEvent_t ev);
+
 /* Set an option (DGC_OPT_*).  Returns DGC_OK or DGC_EINVAL. */
 int dgc_set_option(dgc_state* st, int32_t option, int64_t value);
 

@@ -196,6 +196,7 @@ struct dgc_state {
     int num_cus = 256;
     int select_path = 0;
     int fused_blocks = 0;  // 0: automatic
+    hipEvent_t fused_event = nullptr;  // recorded after the element-wise pass
     hipStream_t last_stream = nullptr;
     std::vector<int64_t> k_last;  // k of the last upload
     std::vector<int64_t> k_tables;  // k, koff, ktbase (host copy)
@@ -518,6 +519,8 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
             st->run_cnt, p.P, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
+    if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+        return DGC_EHIP;
     if (p.G > 0)
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
@@ -672,6 +675,12 @@ int dgc_get_select_info(dgc_state* st, int64_t* info) {
         r[4] = h[t].prefix;
         r[5] = h[t].krem;
     }
+    return DGC_OK;
+}
+
+int dgc_set_fused_event(dgc_state* st, hipEvent_t ev) {
+    if (!st) return DGC_EINVAL;
+    st->fused_event = ev;
     return DGC_OK;
 }
 

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.dgc_get_path_counts.restype = ctypes.c_int
     L.dgc_get_select_info.argtypes = [P, P]
     L.dgc_get_select_info.restype = ctypes.c_int
+    L.dgc_set_fused_event.argtypes = [P, P]
+    L.dgc_set_fused_event.restype = ctypes.c_int
     L.dgc_set_option.argtypes = [P, i32, i64]
     L.dgc_set_option.restype = ctypes.c_int
     L.dgc_get_kernel_time.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double),
@@ -203,6 +205,20 @@ def dgc_get_select_info(st, n_tensors: int) -> np.ndarray:
     return out
 
 
+def dgc_set_fused_event(st, event):
+    """event: a torch.cuda.Event (created here if needed), an int handle,
+    or None to turn the hook off."""
+    handle = None
+    if event is not None:
+        if isinstance(event, int):
+            handle = event
+        else:
+            if not event.cuda_event:
+                event.record()  # torch creates the HIP event lazily
+            handle = event.cuda_event
+    _check(lib().dgc_set_fused_event(st, handle), "dgc_set_fused_event")
+
+
 def dgc_set_option(st, option: int, value: int):
     _check(lib().dgc_set_option(st, int(option), int(value)), "dgc_set_option")
 
@@ -272,6 +288,9 @@ class Learner:
 
     def set_option(self, option: int, value: int):
         dgc_set_option(self.state, option, value)
+
+    def set_fused_event(self, event):
+        dgc_set_fused_event(self.state, event)
 
     def status(self) -> int:
         return dgc_get_status(self.state)

@@ -290,3 +290,60 @@ def test_k_above_k_max_is_rejected():
         p.learner.compress(g, [6], 0.0)
     with pytest.raises(dgc.DGCError):
         p.learner.compress(g[1:], [1], 0.0)  # misaligned gradient
+
+
+def test_pipelined_learners_on_streams():
+    """Four learners on four streams, each starting once the previous one's
+    element-wise pass is done (the library records the caller's event after
+    it); encode on the learner's stream, decode on the main stream.  Every
+    learner's outputs and state, and the dense sum, equal the oracle's."""
+    import torch
+    wl = W.scaled(W.get("flat1b"), 64)
+    k = ks_for(wl, 0)
+    sizes = np.array(wl.sizes, np.int64)
+    pairs = [Pair(list(wl.sizes), k, wl.momentum) for _ in range(wl.learners)]
+    streams = [torch.cuda.Stream() for _ in pairs]
+    events = [torch.cuda.Event() for _ in pairs]
+    for p, ev in zip(pairs, events):
+        p.learner.set_fused_event(ev)
+    main = torch.cuda.current_stream()
+    n = wl.n
+    dense = torch.zeros(n, dtype=torch.float32, device="cuda")
+    for t in range(2):
+        grads = [W.gradient(wl, w, t) for w in range(wl.learners)]
+        dev = [torch.from_numpy(g).cuda() for g in grads]
+        torch.cuda.synchronize()
+        for w, p in enumerate(pairs):
+            st = streams[w]
+            if w == 0:
+                st.wait_stream(main)
+            else:
+                st.wait_event(events[w - 1])
+            with torch.cuda.stream(st):
+                p.learner.compress(dev[w], k, wl.clip, stream=st)
+                p.learner.encode(k, stream=st)
+        for st in streams:
+            main.wait_stream(st)
+        dense.zero_()
+        dgc.decode_accumulate(pairs[0].learner,
+                              [(p.learner.runs, p.learner.vals, p.learner.entries)
+                               for p in pairs], dense)
+        torch.cuda.synchronize()
+        want_dense = np.zeros(n, np.float32)
+        offs = np.concatenate([[0], np.cumsum(sizes)])
+        koff = np.concatenate([[0], np.cumsum(k)])
+        for w, p in enumerate(pairs):
+            o_idx, o_val, o_norm, o_s = oracle.step(sizes, np.array(k), grads[w], p.u, p.v,
+                                                    wl.momentum, wl.clip)
+            L = p.learner
+            assert L.status() == dgc.DGC_OK
+            assert np.array_equal(L.idx[:o_idx.size].cpu().numpy().view(np.uint32), o_idx)
+            assert np.array_equal(f32_bits(L.val[:o_val.size].cpu().numpy()), f32_bits(o_val))
+            assert np.array_equal(f32_bits(L.u[:n].cpu().numpy()), f32_bits(p.u))
+            assert np.array_equal(f32_bits(L.v[:n].cpu().numpy()), f32_bits(p.v))
+            for tt in range(len(k)):
+                r, vv = oracle.encode(o_idx[koff[tt]:koff[tt + 1]], o_val[koff[tt]:koff[tt + 1]])
+                assert oracle.decode_accumulate(r, vv, want_dense[offs[tt]:offs[tt + 1]]) == 0
+        assert np.array_equal(f32_bits(dense.cpu().numpy()), f32_bits(want_dense))
+    for p in pairs:
+        p.learner.set_fused_event(None)
