@@ -78,8 +78,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one plain device copy "
                          "of 1 GiB (for scaling hardware byte counters)")
-    ap.add_argument("--no-pipeline", action="store_true",
-                    help="run the learners back to back on one stream")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="run each learner on its own stream, starting once the "
+                         "previous learner's element-wise pass is done")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
     return ap.parse_args()
@@ -165,7 +166,7 @@ def main():
         L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
     dense = torch.zeros(n, dtype=torch.float32, device="cuda")
     main = torch.cuda.current_stream()
-    pipeline = not args.no_pipeline
+    pipeline = args.pipeline
     if pipeline:
         # One stream per learner.  Learner w+1 starts once learner w's
         # element-wise pass is done (event recorded by the library), so its

@@ -26,9 +26,13 @@ static_assert(kRounds >= 1 && kRounds <= 8, "piece of 256..2048 elements");
 // Pieces are scanned in groups of 256 (one workgroup per group).
 constexpr int64_t kGroup = 256;
 
-// Generic tiles for histogram / emit / encode / decode passes: 4096 items
-// per workgroup visit (16 per thread).
-constexpr int kTileShift = 12;
+// Generic tiles for histogram / emit / encode / decode passes: 1024 items
+// per workgroup visit (4 per thread).  Candidate lists are short (a few
+// tens of thousands per tensor), so small tiles keep many workgroups busy.
+#ifndef DGC_TILE_SHIFT
+#define DGC_TILE_SHIFT 10
+#endif
+constexpr int kTileShift = DGC_TILE_SHIFT;
 constexpr int64_t kTile = int64_t(1) << kTileShift;
 constexpr int kPerThread = int(kTile / kBlock);  // 16
 

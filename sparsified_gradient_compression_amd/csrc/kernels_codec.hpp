@@ -7,7 +7,7 @@
 // (G mod 65536, value).  Runs and values are separate arrays (u16 and f32)
 // at each tensor's capacity offset.
 //
-// Both directions are two-level scans over 4096-item tiles: count per tile,
+// Both directions are two-level scans over kTile-item tiles: count per tile,
 // scan per tensor, then write.  The decoder adds each learner's stream with
 // a plain read-modify-write: positions inside one stream are strictly
 // increasing, so no two items of one launch touch the same element, and
@@ -20,7 +20,7 @@ namespace dgc {
 
 // ---------------------------------------------------------------- encode
 
-// Tiles of 4096 entries are visited in 16 rounds of 256 consecutive
+// Tiles of kTile entries are visited in kPerThread rounds of 256 consecutive
 // entries (entry i0 + 256 q + tid), so loads and stores are coalesced.
 
 // Fillers needed by entry i of a tensor's sorted index list (0 for an entry

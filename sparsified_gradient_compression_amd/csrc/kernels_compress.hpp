@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
 // One block per tensor: scan its groups' counts (their offsets in the
 // ordered list), then choose the selection source: the candidate list when
 // no piece overflowed and there are at least k candidates, else the whole
-// tensor.  Also counts the source's 4096-item tiles for the active-tile map.
+// tensor.  Also counts the source's kTile-item tiles for the active-tile map.
 __global__ __launch_bounds__(kBlock) void k_group_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
     const uint32_t* __restrict__ gsum, uint32_t* __restrict__ goff,
@@ -385,7 +385,7 @@ __device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
 }
 
 // Active tiles: a in [0, aoff[T]) is tile (a - aoff[t]) of tensor
-// t = amap[a]; the tile covers source items [4096 j, 4096 j + 4096) of the
+// t = amap[a]; the tile covers source items [kTile j, kTile (j + 1)) of the
 // tensor's source (candidate list or whole tensor), clipped to len.
 
 // Histogram of digit D over the keys that match the prefix found so far.
@@ -487,7 +487,7 @@ __device__ __forceinline__ uint2 source_item(uint32_t mode, const float* vt_,
     return ol[i];
 }
 
-// Tiles are visited in 16 rounds of 256 consecutive items (item
+// Tiles are visited in kPerThread rounds of 256 consecutive items (item
 // i0 + 256 q + tid), so every load and store of a round is coalesced.
 
 // Per active tile: packed (#key > T) << 16 | #key == T.
