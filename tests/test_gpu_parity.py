@@ -146,8 +146,9 @@ def test_ragged_layout(path, seed):
         g = (rng.laplace(0, 1e-2, n) * (rng.random(n) < 0.9)).astype(np.float32)
         clip = [0.0, 0.5, 1e6][step]
         got, (o_idx, o_val) = p.step(g, k, clip, tag=f"ragged s{step}")
-        compare_streams(gpu_streams(p, k), oracle_streams(sizes, k, o_idx, o_val),
-                        tag=f"ragged s{step}")
+        want = oracle_streams(sizes, k, o_idx, o_val)
+        compare_streams(gpu_streams(p, k), want, tag=f"ragged s{step}")
+        check_decode([p], [want], sizes, tag=f"ragged s{step}")
 
 
 @pytest.mark.parametrize("path", [0, 1])
@@ -347,3 +348,90 @@ def test_pipelined_learners_on_streams():
         assert np.array_equal(f32_bits(dense.cpu().numpy()), f32_bits(want_dense))
     for p in pairs:
         p.learner.set_fused_event(None)
+
+
+def _keys(v):
+    return np.asarray(v, np.float32).view(np.uint32) & np.uint32(0x7FFFFFFF)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_both_paths(seed):
+    """Seeded random layouts: 1-40 tensors of 1 to 400k elements (odd sizes,
+    so tensor starts are misaligned), random k per step, clipping on or
+    off, Laplace gradients with zero runs; both selection paths must give
+    the oracle's bits.  The per-tensor threshold key T and tie quota r the
+    library reports must equal the oracle's: T = the k-th largest key of the
+    accumulated v, r = k - #{key > T}."""
+    rng = np.random.default_rng([41, seed])
+    T = int(rng.integers(1, 41))
+    sizes = [int(x) for x in rng.choice([1, 2, 7, 300, 1023, 4099, 65535, 65537,
+                                         131075, 399999], T)]
+    n = sum(sizes)
+    steps = 2
+    ks = [[int(rng.integers(0, s + 1)) if rng.random() < 0.3 else -(-s // 1000)
+           for s in sizes] for _ in range(steps)]
+    kmax = [max(ks[t][i] for t in range(steps)) for i in range(T)]
+    for path in (0, 1):
+        p = Pair(sizes, kmax)
+        p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+        for step in range(steps):
+            g = rng.laplace(0, 1e-2, n).astype(np.float32)
+            g[rng.random(n) < 0.05] = 0.0
+            clip = float(rng.choice([0.0, 0.5, 100.0]))
+            u0, v0 = p.u.copy(), p.v.copy()
+            got, (o_idx, o_val) = p.step(g, ks[step], clip, tag=f"fuzz{seed} p{path} s{step}")
+            # the accumulated v before masking, from the oracle's own steps
+            _, s32 = oracle.clip_scale(g, clip)
+            oracle.momentum(g, s32, 0.9, u0, v0)
+            info = p.learner.select_info()
+            off = np.concatenate([[0], np.cumsum(sizes)])
+            for t in range(T):
+                k_t = ks[step][t]
+                if k_t == 0:
+                    assert info[t, 0] == 0
+                    continue
+                keys = _keys(v0[off[t]:off[t + 1]])
+                Tk = np.sort(keys)[::-1][k_t - 1]
+                r = k_t - int((keys > Tk).sum())
+                assert info[t, 4] == Tk and info[t, 5] == r, (seed, path, step, t,
+                                                              info[t].tolist(), int(Tk), r)
+            want = oracle_streams(sizes, ks[step], o_idx, o_val)
+            compare_streams(gpu_streams(p, ks[step]), want, tag=f"fuzz{seed}")
+
+
+def test_encode_flags_unsorted_indices():
+    """dgc_encode expects each tensor's indices strictly ascending and inside
+    the tensor; anything else latches DGC_ECORRUPT and writes nothing out of
+    place."""
+    import torch
+    p = Pair([1000, 70000], [4, 4])
+    L = p.learner
+    bad = np.array([5, 3, 9, 12, 1, 2, 70000, 7], np.uint32)  # descending / out of range
+    L.idx[:8].copy_(torch.from_numpy(bad.view(np.int32)))
+    L.val[:8].copy_(torch.ones(8))
+    L.runs.zero_()
+    L.encode([4, 4])
+    torch.cuda.synchronize()
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert L.status() == dgc.DGC_OK
+    assert int(L.runs.abs().max()) <= 65535
+
+
+def test_kernel_timers():
+    import torch
+    wl = W.scaled(W.get("flat1b"), 64)
+    k = ks_for(wl, 0)
+    p = Pair(list(wl.sizes), k)
+    L = p.learner
+    L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
+    g = torch.from_numpy(W.gradient(wl, 0, 0)).cuda()
+    for _ in range(3):
+        L.compress(g, k, wl.clip)
+        L.encode(k)
+    ms_f, n_f = L.kernel_time(dgc.DGC_TIMER_FUSED)
+    ms_c, n_c = L.kernel_time(dgc.DGC_TIMER_COMPRESS)
+    ms_e, n_e = L.kernel_time(dgc.DGC_TIMER_ENCODE)
+    assert (n_f, n_c, n_e) == (3, 3, 3)
+    assert 0 < ms_f < ms_c and ms_e > 0
+    assert L.kernel_time(dgc.DGC_TIMER_FUSED) == (0.0, 0)  # read resets
+    L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 0)
