@@ -195,6 +195,36 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* lds, T& total) {
     return wpre + inc - x;
 }
 
+// Exclusive scan of in[0, count) into out[0, count), starting at `carry`,
+// by one block: each thread takes kScanPer consecutive values per round
+// (one block-wide scan per 256 * kScanPer values).  Returns carry + total.
+// Every thread must call it.
+constexpr int kScanPer = 8;
+template <typename TO>
+__device__ __forceinline__ TO block_scan_range(const uint32_t* __restrict__ in,
+                                               TO* __restrict__ out, int64_t count,
+                                               TO carry, TO* lds) {
+    for (int64_t base = 0; base < count; base += int64_t(kBlock) * kScanPer) {
+        const int64_t i0 = base + int64_t(threadIdx.x) * kScanPer;
+        uint32_t x[kScanPer];
+        TO local = 0;
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) {
+            x[q] = i0 + q < count ? in[i0 + q] : 0u;
+            local += TO(x[q]);
+        }
+        TO tot;
+        TO run = carry + block_exclusive_scan(local, lds, tot);
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) {
+            if (i0 + q < count) out[i0 + q] = run;
+            run += TO(x[q]);
+        }
+        carry += tot;
+    }
+    return carry;
+}
+
 // Exclusive prefix, in thread order, of two 0/1 flags across the block, from
 // wave ballots; also their block totals.  `lds2` holds 2 * kWavesPerBlock
 // values.  Every thread must call it.

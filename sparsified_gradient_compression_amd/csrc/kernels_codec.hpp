@@ -70,15 +70,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t kb = K.ktbase[t], ntile = K.ktbase[t + 1] - kb;
-    uint32_t carry = 0;
-    for (int64_t base = 0; base < ntile; base += kBlock) {
-        int64_t j = base + threadIdx.x;
-        uint32_t x = j < ntile ? tile_f[kb + j] : 0;
-        uint32_t tot;
-        uint32_t ex = block_exclusive_scan(x, lds, tot);
-        if (j < ntile) tile_foff[kb + j] = carry + ex;
-        carry += tot;
-    }
+    const uint32_t carry = block_scan_range<uint32_t>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
     if (threadIdx.x == 0) entries[t] = K.k[t] + int64_t(carry);
 }
 
@@ -164,15 +156,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_scan(
     __shared__ uint64_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t tb = L.etbase[t], ntile = L.etbase[t + 1] - tb;
-    uint64_t carry = 0;
-    for (int64_t base = 0; base < ntile; base += kBlock) {
-        int64_t j = base + threadIdx.x;
-        uint64_t x = j < ntile ? tile_s[tb + j] : 0;
-        uint64_t tot;
-        uint64_t ex = block_exclusive_scan(x, lds, tot);
-        if (j < ntile) tile_p[tb + j] = carry + ex;
-        carry += tot;
-    }
+    block_scan_range<uint64_t>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds);
 }
 
 // dense[o_t + pos] += value for every entry of one learner's stream, where
