@@ -435,3 +435,41 @@ def test_kernel_timers():
     assert 0 < ms_f < ms_c and ms_e > 0
     assert L.kernel_time(dgc.DGC_TIMER_FUSED) == (0.0, 0)  # read resets
     L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 0)
+
+
+def test_empty_layout():
+    """Every tensor empty: compress, encode and decode do nothing and report
+    norm -1 / scale 1 with clipping off (norm 0 / scale 1 with it on)."""
+    import torch
+    p = Pair([0, 0], [0, 0])
+    L = p.learner
+    g = torch.zeros(4, device="cuda")
+    L.compress(g, [0, 0], 0.0)
+    torch.cuda.synchronize()
+    assert float(L.norm.cpu()[0]) == -1.0 and float(L.scale.cpu()[0]) == 1.0
+    L.compress(g, [0, 0], 0.5)
+    torch.cuda.synchronize()
+    assert float(L.norm.cpu()[0]) == 0.0 and float(L.scale.cpu()[0]) == 1.0
+    runs, vals, ent = L.encode([0, 0])
+    torch.cuda.synchronize()
+    assert ent.cpu().tolist() == [0, 0]
+    dense = torch.zeros(4, device="cuda")
+    dgc.decode_accumulate(L, [(runs, vals, ent)], dense)
+    assert L.status() == dgc.DGC_OK
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_denormals_and_extremes(path):
+    """Denormal and near-overflow magnitudes: keys are bit patterns, so the
+    order is exact and denormals are kept (no flush to zero)."""
+    rng = np.random.default_rng(51)
+    sizes = [100000, 3000, 262144]
+    n = sum(sizes)
+    p = Pair(sizes, [100, 3000, 262])
+    p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    for step in range(2):
+        g = rng.laplace(0, 1e-38, n).astype(np.float32)  # mostly denormal
+        g[rng.random(n) < 0.001] = np.float32(1e38) * np.float32(rng.choice([-1, 1]))
+        g[rng.random(n) < 0.01] = np.float32(1.4e-45)
+        k = [100, 3000 if step == 0 else 7, 262]
+        p.step(g, k, 0.0, tag=f"denorm p{path} s{step}")
