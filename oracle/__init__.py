@@ -26,4 +26,6 @@ from .c_oracle import (  # noqa: F401
     k_for_density,
     step,
     num_threads,
+    binlocal_select_mask,
+    binlocal_step,
 )

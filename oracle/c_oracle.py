@@ -62,6 +62,12 @@ def load():
     lib.orc_step.argtypes = [ctypes.c_int32, P, P, P, P, P, ctypes.c_float,
                              ctypes.c_double, P, P, P, P]
     lib.orc_step.restype = ctypes.c_int
+    lib.orc_binlocal_select_mask.argtypes = [P, P, i64, i64, i64, P, P, P]
+    lib.orc_binlocal_select_mask.restype = i64
+    lib.orc_binlocal_step.argtypes = [ctypes.c_int32, P, P, P, P, P, P,
+                                      ctypes.c_float, ctypes.c_double, P, P,
+                                      P, P, P, P]
+    lib.orc_binlocal_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -160,3 +166,50 @@ def step(sizes, k, g, u, v, m, clip):
     if rc != 0:
         raise ValueError("bad k")
     return idx[:K].copy(), val[:K].copy(), float(norm[0]), np.float32(scale[0])
+
+
+def binlocal_select_mask(u, v, L, cap=None):
+    """Bin-local selection of one tensor + masking, in place.
+
+    Returns (idx, val, total): the delivered entries (at most cap, index
+    order) and the number of salient entries.
+    """
+    assert u.size == v.size
+    cap = v.size if cap is None else int(cap)
+    idx = np.zeros(max(cap, 1), np.uint32)
+    val = np.zeros(max(cap, 1), np.float32)
+    total = np.zeros(1, np.int64)
+    got = load().orc_binlocal_select_mask(
+        _ptr(u, np.float32), _ptr(v, np.float32), v.size, int(L), cap,
+        _ptr(idx, np.uint32), _ptr(val, np.float32), _ptr(total, np.int64))
+    if got < 0:
+        raise ValueError("bad bin length or capacity")
+    return idx[:got].copy(), val[:got].copy(), int(total[0])
+
+
+def binlocal_step(sizes, L, cap, g, u, v, m, clip):
+    """One learner step with the bin-local selector (in place on u, v).
+
+    Returns (idx, val, count, total, norm, scale).  idx/val have sum(cap)
+    slots; tensor t's delivered entries sit at offset sum(cap[:t]) and only
+    the first count[t] of its cap[t] slots are written.
+    """
+    sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+    L = np.ascontiguousarray(L, dtype=np.int64)
+    cap = np.ascontiguousarray(cap, dtype=np.int64)
+    C = int(cap.sum())
+    idx = np.zeros(max(C, 1), np.uint32)
+    val = np.zeros(max(C, 1), np.float32)
+    count = np.zeros(len(sizes), np.int64)
+    total = np.zeros(len(sizes), np.int64)
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    rc = load().orc_binlocal_step(
+        len(sizes), _ptr(sizes, np.int64), _ptr(L, np.int64),
+        _ptr(cap, np.int64), _ptr(g, np.float32), _ptr(u, np.float32),
+        _ptr(v, np.float32), float(np.float32(m)), float(clip),
+        _ptr(idx, np.uint32), _ptr(val, np.float32), _ptr(count, np.int64),
+        _ptr(total, np.int64), _ptr(norm, np.float64), _ptr(scale, np.float32))
+    if rc != 0:
+        raise ValueError("bad bin length or capacity")
+    return idx[:C], val[:C], count, total, float(norm[0]), np.float32(scale[0])

@@ -5,7 +5,8 @@
 //
 // Self-checks (abort on failure): exactly k entries selected, ascending
 // indices, sent + residual == accumulated v, u and v zero where sent,
-// decode(encode(x)) reproduces the sent values.
+// decode(encode(x)) reproduces the sent values; for the bin-local selector,
+// min(salient, cap) entries delivered, ascending, non-zero, masked.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -26,6 +27,12 @@ int64_t orc_k_for_density(int64_t n, int64_t num, int64_t den);
 int orc_step(int32_t T, const int64_t* sizes, const int64_t* k, const float* g, float* u,
              float* v, float m, double clip, uint32_t* idx, float* val, double* norm,
              float* scale);
+int64_t orc_binlocal_select_mask(float* u, float* v, int64_t n, int64_t L, int64_t cap,
+                                 uint32_t* idx, float* val, int64_t* total);
+int orc_binlocal_step(int32_t T, const int64_t* sizes, const int64_t* L, const int64_t* cap,
+                      const float* g, float* u, float* v, float m, double clip,
+                      uint32_t* idx, float* val, int64_t* count, int64_t* total,
+                      double* norm, float* scale);
 }
 
 #define CHECK(c)                                                        \
@@ -107,6 +114,59 @@ int main() {
             off += sizes[t];
             koff += k[t];
         }
+    }
+    // bin-local selector: bins of random length, capacities from none to all
+    for (int round = 0; round < 30; ++round) {
+        int T = 1 + int(rng() % 4);
+        std::vector<int64_t> sizes(T), L(T), cap(T), count(T), total(T);
+        int64_t n = 0, C = 0;
+        for (int t = 0; t < T; ++t) {
+            sizes[t] = sizes_pool[rng() % 10];
+            L[t] = 1 + int64_t(rng() % 1100);
+            cap[t] = (rng() % 3 == 0) ? sizes[t] : int64_t(rng() % (sizes[t] / 8 + 2));
+            n += sizes[t];
+            C += cap[t];
+        }
+        std::vector<float> g(n), u(n), v(n);
+        std::normal_distribution<float> nd(0.f, 1e-2f);
+        for (int64_t i = 0; i < n; ++i) {
+            g[i] = (rng() % 10 == 0) ? 0.f : nd(rng);
+            u[i] = nd(rng) * 0.1f;
+            v[i] = (rng() % 7 == 0) ? 0.f : nd(rng) * 0.1f;
+        }
+        std::vector<float> u_pre(u), v_pre(v);
+        double norm;
+        float s;
+        orc_clip_scale(g.data(), n, 0.5, &norm, &s);
+        orc_momentum(g.data(), n, s, 0.9f, u_pre.data(), v_pre.data());
+        std::vector<uint32_t> idx(C + 1);
+        std::vector<float> val(C + 1);
+        CHECK(orc_binlocal_step(T, sizes.data(), L.data(), cap.data(), g.data(), u.data(),
+                                v.data(), 0.9f, 0.5, idx.data(), val.data(), count.data(),
+                                total.data(), &norm, &s) == 0);
+        int64_t off = 0, coff = 0;
+        for (int t = 0; t < T; ++t) {
+            CHECK(count[t] == std::min(total[t], cap[t]));
+            for (int64_t j = 0; j < count[t]; ++j) {
+                uint32_t i = idx[coff + j];
+                CHECK(int64_t(i) < sizes[t]);
+                if (j) CHECK(idx[coff + j - 1] < i);
+                CHECK(bits(val[coff + j]) == bits(v_pre[off + i]));
+                CHECK(bits(val[coff + j]) & 0x7FFFFFFFu);
+                CHECK(bits(u[off + i]) == 0 && bits(v[off + i]) == 0);
+            }
+            off += sizes[t];
+            coff += cap[t];
+        }
+    }
+    {
+        float z[3] = {0.f, 0.f, 0.f};
+        uint32_t i3[3];
+        float v3[3];
+        int64_t tot;
+        CHECK(orc_binlocal_select_mask(z, z, 3, 0, 3, i3, v3, &tot) == -1);
+        CHECK(orc_binlocal_select_mask(z, z, 3, 1, -1, i3, v3, &tot) == -1);
+        CHECK(orc_binlocal_select_mask(z, z, 3, 2, 3, i3, v3, &tot) == 0 && tot == 0);
     }
     // a corrupt stream is refused without touching memory past the end
     std::vector<uint16_t> runs = {3, 4, 60000};

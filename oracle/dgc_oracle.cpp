@@ -164,6 +164,62 @@ int64_t orc_select_mask(float* u, float* v, int64_t n, int64_t k,
 }
 
 /*
+ * Bin-local selection of one tensor, then momentum factor masking.
+ *
+ * Source: the AdaComp page ("AdaComp : Adaptive Residual Gradient Compression
+ * for Data-Parallel Distributed Training"), Abstract (residues are selected
+ * locally and the compression rate follows local activity) and "Citations in
+ * the corpus" (the Hitchhiker's Guide entry: each layer's residual vector is
+ * cut into bins of one fixed size, and the largest absolute value in a bin is
+ * that bin's threshold for salient entries).
+ *
+ * The pages do not say what is compared with a bin's threshold.  Comparing
+ * the residual itself would send exactly each bin's maximum, one entry per
+ * bin, a fixed rate; the abstract's rate follows local activity.  Reading
+ * taken: the residual is v after this step's accumulation; entry i of bin b
+ * is salient when v_i is non-zero and v_i looked ahead by this step's update
+ * once more, fl32(v_i + u_i), reaches the bin's largest |v|:
+ *   bins      b = [b*L, min((b+1)*L, n)), restarting at each tensor
+ *   threshold theta_b = max over the bin of key(v_j)
+ *   salient   key(v_i) > 0  and  key(fl32(v_i + u_i)) >= theta_b
+ * with key(x) = bits(x) & 0x7FFFFFFF (|x| ordered as an unsigned integer).
+ * Salient entries are delivered in index order, at most cap of them; the
+ * delivered ones are masked (u = v = +0.0f) and the rest stay in the
+ * residual untouched.
+ *
+ * Writes the delivered local indices (ascending) and the signed values of v
+ * before masking, and the number of salient entries (delivered or not) into
+ * *total.  Returns the number delivered, or -1 if L < 1 or cap < 0.
+ */
+int64_t orc_binlocal_select_mask(float* u, float* v, int64_t n, int64_t L,
+                                 int64_t cap, uint32_t* idx, float* val,
+                                 int64_t* total) {
+    if (L < 1 || cap < 0) return -1;
+    int64_t sal = 0, out = 0;
+    for (int64_t lo = 0; lo < n; lo += L) {
+        int64_t hi = std::min(n, lo + L);
+        uint32_t theta = 0;
+        for (int64_t i = lo; i < hi; ++i) theta = std::max(theta, magnitude_key(v[i]));
+        for (int64_t i = lo; i < hi; ++i) {
+            float ahead = v[i] + u[i];
+            if (magnitude_key(v[i]) == 0 || magnitude_key(ahead) < theta) continue;
+            ++sal;
+            if (out < cap) {
+                idx[out] = (uint32_t)i;
+                val[out] = v[i];
+                ++out;
+            }
+        }
+    }
+    for (int64_t j = 0; j < out; ++j) {
+        u[idx[j]] = 0.0f;
+        v[idx[j]] = 0.0f;
+    }
+    *total = sal;
+    return out;
+}
+
+/*
  * Zero-run encoding of one tensor's sparse gradient (DGC review, "Proposed
  * method": each sent value takes 32 bits and is preceded by the 16-bit
  * length of the zero run before it).  A gap longer than a 16-bit run can say
@@ -249,6 +305,37 @@ int orc_step(int32_t T, const int64_t* sizes, const int64_t* k, const float* g,
         if (got != k[t]) bad = 1;
     }
     return bad ? -1 : 0;
+}
+
+/*
+ * One learner step with the bin-local selector: clip and momentum as in
+ * orc_step, then per tensor orc_binlocal_select_mask with bin length L[t]
+ * and capacity cap[t].  Tensor t's delivered entries go to idx/val at offset
+ * cap[0] + ... + cap[t-1]; count[t] = number delivered, total[t] = number
+ * salient.  Returns 0, or -1 on a bad L or cap.
+ */
+int orc_binlocal_step(int32_t T, const int64_t* sizes, const int64_t* L,
+                      const int64_t* cap, const float* g, float* u, float* v,
+                      float m, double clip, uint32_t* idx, float* val,
+                      int64_t* count, int64_t* total, double* norm_out,
+                      float* scale_out) {
+    int64_t n = 0;
+    for (int32_t t = 0; t < T; ++t) n += sizes[t];
+    orc_clip_scale(g, n, clip, norm_out, scale_out);
+    orc_momentum(g, n, *scale_out, m, u, v);
+    std::vector<int64_t> off((size_t)T + 1, 0), coff((size_t)T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        if (L[t] < 1 || cap[t] < 0) return -1;
+        off[(size_t)t + 1] = off[(size_t)t] + sizes[t];
+        coff[(size_t)t + 1] = coff[(size_t)t] + cap[t];
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        count[t] = orc_binlocal_select_mask(
+            u + off[(size_t)t], v + off[(size_t)t], sizes[t], L[t], cap[t],
+            idx + coff[(size_t)t], val + coff[(size_t)t], total + t);
+    }
+    return 0;
 }
 
 }  /* extern "C" */
