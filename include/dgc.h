@@ -53,17 +53,24 @@ extern "C" {
 #define DGC_EHIP (-3)      /* a HIP runtime call or kernel launch failed */
 #define DGC_ECORRUPT (-4)  /* a decoded stream ran past its tensor's end */
 
+/* Largest bin length of dgc_compress_binlocal. */
+#define DGC_MAX_BIN 1024
+
 /* Options for dgc_set_option. */
 #define DGC_OPT_SELECT_PATH 1   /* value 0: automatic (default); 1: always the
-                                   dense exact path (no sample window) */
+                                   dense exact path (no sample window); for
+                                   dgc_compress_binlocal, every piece's
+                                   entries re-derived in the placement pass
+                                   (no slots) -- the same results, slower */
 #define DGC_OPT_KERNEL_TIMING 2 /* value 1: bracket the work of each call with
                                    HIP events on the call's stream (read with
                                    dgc_get_kernel_time); 0: off (default) */
 
 /* Timers for dgc_get_kernel_time. */
-#define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress */
-#define DGC_TIMER_COMPRESS 1  /* all of dgc_compress */
-#define DGC_TIMER_ENCODE 2    /* all of dgc_encode */
+#define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress or
+                                 dgc_compress_binlocal */
+#define DGC_TIMER_COMPRESS 1  /* all of dgc_compress / dgc_compress_binlocal */
+#define DGC_TIMER_ENCODE 2    /* all of dgc_encode / dgc_encode_counts */
 #define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate */
 
 typedef struct dgc_state dgc_state;
@@ -132,6 +139,45 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
                  float* out_scale, hipStream_t stream);
 
 /*
+ * One compression step with the bin-local selector of AdaComp (the page
+ * "AdaComp : Adaptive Residual Gradient Compression for Data-Parallel
+ * Distributed Training": Abstract -- residues are selected locally and the
+ * rate follows local activity; "Citations in the corpus" -- each layer's
+ * residual vector is cut into fixed-size bins and a bin's largest absolute
+ * value is its threshold).  Steps 1, 2 and 4 are dgc_compress's; step 3
+ * becomes:
+ *   3'. tensor t is cut into bins of bin_len[t] entries from its start (the
+ *       last bin may be shorter); theta_b = max |v_j| over bin b; entry i
+ *       is salient iff v_i != 0 and |fl(v_i + u_i)| >= theta_b, i.e. v
+ *       looked ahead by this step's update u once more reaches the bin's
+ *       largest |v| (magnitudes compared as sign-cleared bit patterns)
+ * The first cap[t] salient entries of tensor t in index order are written
+ * out and masked (u_i = v_i = +0.0f); salient entries beyond cap[t] stay in
+ * the residual untouched.
+ * Arguments:
+ *   g          device const float[n], 16-byte aligned
+ *   bin_len    host int64[T], 1 <= bin_len[t] <= DGC_MAX_BIN
+ *   cap        host int64[T], 0 <= cap[t] <= k_max[t]: most entries to
+ *              deliver for tensor t; cap[t] = n_t never truncates
+ *   clip       as for dgc_compress
+ *   out_idx    device uint32[sum cap]: tensor t's delivered local indices,
+ *              ascending, at offset C_t = cap[0] + ... + cap[t-1]; slots
+ *              past out_count[t] are left as they were
+ *   out_val    device float[sum cap]: the matching values of v before
+ *              masking, same offsets
+ *   out_count  device int64[T], 8-byte aligned: out, entries delivered
+ *              (min(salient, cap[t]))
+ *   out_total  device int64[T] or NULL: out, salient entries per tensor
+ *   out_norm, out_scale  as for dgc_compress
+ * Exact and deterministic; the path (slots or re-derivation) changes only
+ * the speed.  Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
+                          const int64_t* cap, double clip, uint32_t* out_idx,
+                          float* out_val, int64_t* out_count, int64_t* out_total,
+                          double* out_norm, float* out_scale, hipStream_t stream);
+
+/*
  * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is
  * the first entry slot of tensor t; tensor t may use up to
  * cap_offsets[t+1] - cap_offsets[t] = k_max[t] + floor(n_t / 65536) entries,
@@ -160,6 +206,22 @@ int dgc_encode(const dgc_state* st, const int64_t* k, const uint32_t* idx,
                hipStream_t stream);
 
 /*
+ * dgc_encode for a selection whose sizes are on the device (the output of
+ * dgc_compress_binlocal): tensor t's entries are at offset
+ * cap[0] + ... + cap[t-1] of idx / val, and count[t] of them are encoded.
+ *   cap        host int64[T], as given to dgc_compress_binlocal
+ *   count      device const int64[T], 8-byte aligned: entries per tensor;
+ *              a count outside [0, cap[t]] encodes nothing for that tensor
+ *              and latches DGC_ECORRUPT for dgc_get_status
+ *   idx, val, runs, vals, entries  as for dgc_encode
+ * Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_encode_counts(const dgc_state* st, const int64_t* cap,
+                      const int64_t* count, const uint32_t* idx,
+                      const float* val, uint16_t* runs, float* vals,
+                      int64_t* entries, hipStream_t stream);
+
+/*
  * Decode several learners' streams and add them into one dense sum (the
  * gradient exchange of synchronous SGD, DGC review Abstract):
  * for w = 0 .. n_learners-1 in order, per tensor, pos = -1 and for each
@@ -183,7 +245,8 @@ int dgc_decode_accumulate(const dgc_state* st, int32_t n_learners,
 
 /*
  * Wait for the state's last stream and return the latched device-side
- * error (DGC_OK or DGC_ECORRUPT), clearing it.  Returns DGC_EHIP if the
+ * error (DGC_OK or DGC_ECORRUPT: a corrupt stream in decoding, unsorted
+ * input to an encoder, or a bad device count), clearing it.  Returns DGC_EHIP if the
  * wait fails.
  */
 int dgc_get_status(dgc_state* st);

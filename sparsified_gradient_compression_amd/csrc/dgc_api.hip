@@ -12,6 +12,7 @@
 
 #include "dgc.h"
 #include "dgc_device.hpp"
+#include "kernels_binlocal.hpp"
 #include "kernels_codec.hpp"
 #include "kernels_compress.hpp"
 
@@ -36,6 +37,8 @@ struct Plan {
     std::vector<PieceDesc> pdesc;
     std::vector<uint32_t> smap, emap, gmap;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
+    // bin-local selector: most pieces and prefix groups any bin length gives
+    int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
     // workspace byte offsets
     size_t off_tab = 0, off_pdesc = 0, off_smap = 0, off_emap = 0, off_k = 0,
@@ -44,7 +47,8 @@ struct Plan {
            off_scratch = 0,
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
-           total = 0;
+           off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
+           off_blgoff = 0, total = 0;
 };
 
 // Candidate slots per 1024-element piece: none for small tensors (they take
@@ -62,6 +66,10 @@ int64_t list_cap(int64_t n, int64_t kmax, int64_t slots) {
     if (n <= kSmallN) return 0;
     return std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384);
 }
+
+// Bin-local pieces are L * floor(1024 / L) elements, never fewer than 513
+// (1 <= L <= 1024), so a tensor has at most ceil(n / 513) of them.
+constexpr int64_t kBlMinPiece = kMaxBin / 2 + 1;
 
 int64_t sample_lines(int64_t n) {
     if (n <= kSmallN) return 0;
@@ -100,6 +108,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
         p.ebase[t + 1] = p.ebase[t] + km + n / 65536;
         p.etbase[t + 1] = p.etbase[t] + cdiv(km + n / 65536, kTile);
+        p.BP += cdiv(n, kBlMinPiece);
+        p.BG += cdiv(cdiv(n, kBlMinPiece), kBlGroup);
     }
     p.n = p.o[T];
     p.P = p.pbase[T];
@@ -144,6 +154,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_gmap = take(size_t(p.G) * 4);
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
+    p.off_bltab = take(5 * T1 * sizeof(int64_t));
     // Everything above is written from the host (layout tables at init, k
     // tables per call); everything from here on is device scratch, zeroed
     // at init.
@@ -165,6 +176,11 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_tc = take(size_t(p.tiles) * 4);
     p.off_t64 = take(size_t(p.tiles) * 8);
     p.off_part = take(size_t(std::max<int64_t>(p.NB, 1)) * 8);
+    p.off_blpdesc = take(size_t(p.BP) * sizeof(PieceDesc));
+    p.off_blcnt = take(size_t(p.BP) * 4);
+    p.off_blpre = take(size_t(p.BP) * 4);
+    p.off_blgsum = take(size_t(p.BG) * 4);
+    p.off_blgoff = take(size_t(p.BG) * 4);
     p.total = off;
     return DGC_OK;
 }
@@ -203,6 +219,11 @@ struct dgc_state {
     std::vector<uint32_t> kmap_host;
     bool k_valid = false;
     int64_t KT = 0;  // tiles over k of the last upload
+    std::vector<int64_t> bins_last;  // bin lengths of the last upload
+    std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap (host copy)
+    bool bins_valid = false;
+    int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
+    DevBins B{};
     // device views
     DevLayout L{};
     DevK K{};
@@ -330,6 +351,91 @@ int check_k(const dgc_state* st, const int64_t* k) {
     return DGC_OK;
 }
 
+int check_bins(const dgc_state* st, const int64_t* bin_len) {
+    if (!bin_len) return DGC_EINVAL;
+    for (int32_t t = 0; t < st->plan.T; ++t)
+        if (bin_len[t] < 1 || bin_len[t] > kMaxBin) return DGC_EINVAL;
+    return DGC_OK;
+}
+
+// Upload the bin-local tables for these bin lengths when they change, and
+// rebuild the piece descriptors on the device.
+int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
+    const Plan& p = st->plan;
+    const int32_t T = p.T;
+    DGC_TRY(check_bins(st, bin_len));
+    if (st->bins_valid && std::memcmp(st->bins_last.data(), bin_len, size_t(T) * 8) == 0)
+        return DGC_OK;
+    const size_t T1 = size_t(T) + 1;
+    std::vector<int64_t>& tb = st->bl_tables;
+    tb.assign(5 * T1, 0);
+    int64_t* plen = tb.data();
+    int64_t* magic = plen + T1;
+    int64_t* pbase = magic + T1;
+    int64_t* gbase = pbase + T1;
+    int64_t* pcap = gbase + T1;
+    for (int32_t t = 0; t < T; ++t) {
+        const int64_t Lb = bin_len[t], n = p.sizes[size_t(t)];
+        plen[t] = Lb * (kMaxBin / Lb);
+        magic[t] = Lb == 1 ? 0 : ((int64_t(1) << 32) + Lb - 1) / Lb;
+        // the multiply-high bin index must equal e / L on every offset
+        for (int64_t e = 0; e < plen[t]; ++e)
+            if (Lb > 1 && int64_t((uint64_t(e) * uint64_t(magic[t])) >> 32) != e / Lb)
+                return DGC_EINVAL;
+        const int64_t np_ = cdiv(n, plen[t]);
+        pbase[t + 1] = pbase[t] + np_;
+        gbase[t + 1] = gbase[t] + cdiv(np_, kBlGroup);
+        // the tensor's candidate slots, shared out among its pieces
+        const int64_t region = p.slbase[size_t(t) + 1] - p.slbase[size_t(t)];
+        pcap[t] = np_ ? std::min<int64_t>(plen[t], region / np_) : 0;
+    }
+    if (pbase[T] > p.BP || gbase[T] > p.BG) return DGC_EINVAL;
+    if (hipMemcpyAsync(st->ws + p.off_bltab, tb.data(), tb.size() * 8,
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+        return DGC_EHIP;
+    st->BP = pbase[T];
+    st->BG = gbase[T];
+    if (st->BP > 0) {
+        k_bl_pdesc<<<grid_for(cdiv(st->BP, kBlock), cdiv(st->BP, kBlock)), kBlock, 0, s>>>(
+            st->L, st->B, st->BP);
+        if (hipGetLastError() != hipSuccess) return DGC_EHIP;
+    }
+    st->bins_last.assign(bin_len, bin_len + T);
+    st->bins_valid = true;
+    return DGC_OK;
+}
+
+int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
+                const uint32_t* idx, const float* val, uint16_t* runs, float* vals,
+                int64_t* entries, hipStream_t stream) {
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (!entries || !aligned(entries, 8)) return DGC_EINVAL;
+    if (K > 0 && (!idx || !val || !runs || !vals || !aligned(idx, 4) ||
+                  !aligned(val, 4) || !aligned(runs, 2) || !aligned(vals, 4)))
+        return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const int T = p.T;
+    const int pg = st->num_cus * 8;
+    DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
+    if (st->KT > 0)
+        k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
+                                                                 st->ta, st->sc, st->KT);
+    k_enc_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb, entries,
+                                         st->sc);
+    if (st->KT > 0)
+        k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(
+            st->L, st->K, kdev, idx, val, st->tb, runs, vals, st->KT);
+    DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_ENCODE, stream));
+    return DGC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,12 +529,23 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->tc = reinterpret_cast<uint32_t*>(ws + p.off_tc);
     st->t64 = reinterpret_cast<uint64_t*>(ws + p.off_t64);
     st->partial = reinterpret_cast<double*>(ws + p.off_part);
+    int64_t* bt = reinterpret_cast<int64_t*>(ws + p.off_bltab);
+    st->B.plen = bt;
+    st->B.magic = bt + T1;
+    st->B.pbase = bt + 2 * T1;
+    st->B.gbase = bt + 3 * T1;
+    st->B.pcap = bt + 4 * T1;
+    st->B.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_blpdesc);
+    st->B.cnt = reinterpret_cast<uint32_t*>(ws + p.off_blcnt);
+    st->B.pre = reinterpret_cast<uint32_t*>(ws + p.off_blpre);
+    st->B.gsum = reinterpret_cast<uint32_t*>(ws + p.off_blgsum);
+    st->B.goff = reinterpret_cast<uint32_t*>(ws + p.off_blgoff);
 
     // the uploaded tables must not lie in the scratch zeroed below
     if (p.off_pdesc >= p.off_scratch || p.off_smap >= p.off_scratch ||
         p.off_emap >= p.off_scratch || p.off_gmap >= p.off_scratch ||
         p.off_k >= p.off_scratch || p.off_kmap >= p.off_scratch ||
-        p.off_tab >= p.off_scratch) {
+        p.off_tab >= p.off_scratch || p.off_bltab >= p.off_scratch) {
         delete st;
         return DGC_EINVAL;
     }
@@ -555,6 +672,65 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     return DGC_OK;
 }
 
+int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
+                          const int64_t* cap, double clip, uint32_t* out_idx,
+                          float* out_val, int64_t* out_count, int64_t* out_total,
+                          double* out_norm, float* out_scale, hipStream_t stream) {
+    if (!st) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, cap);
+    if (rc != DGC_OK) return rc;
+    DGC_TRY(check_bins(st, bin_len));
+    int64_t C = 0;
+    for (int32_t t = 0; t < p.T; ++t) C += cap[t];
+    if (p.n > 0 && (!g || !aligned(g, 16))) return DGC_EINVAL;
+    if (C > 0 && (!out_idx || !out_val || !aligned(out_idx, 4) || !aligned(out_val, 4)))
+        return DGC_EINVAL;
+    if (!out_count || !aligned(out_count, 8)) return DGC_EINVAL;
+    if (out_total && !aligned(out_total, 8)) return DGC_EINVAL;
+    if (std::isnan(clip)) return DGC_EINVAL;
+    rc = upload_k(st, cap, stream);
+    if (rc != DGC_OK) return rc;
+    rc = upload_bins(st, bin_len, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const int T = p.T;
+    const bool clip_on = clip > 0.0;
+    const uint32_t pcap_limit = st->select_path == 1 ? 0u : 0xFFFFFFFFu;
+
+    DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    if (clip_on) {
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
+    } else if (st->BP == 0) {
+        k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
+    }
+    DGC_LAUNCH_CHECK();
+    const int64_t wb = cdiv(st->BP, kWavesPerBlock);  // one piece per wave
+    if (st->BP > 0) {
+        DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+        k_bl_fused<<<grid_for(wb, wb), kBlock, 0, stream>>>(
+            g, st->u, st->v, st->L, st->K, st->B, st->sc, clip_on, st->m, pcap_limit,
+            st->slots, st->BP, out_norm, out_scale);
+        DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+    }
+    if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+        return DGC_EHIP;
+    if (st->BG > 0) {
+        const int64_t gb = cdiv(st->BG, kWavesPerBlock);
+        k_bl_group<<<grid_for(gb, gb), kBlock, 0, stream>>>(st->L, st->B, st->BG);
+    }
+    k_bl_tscan<<<T, kBlock, 0, stream>>>(st->K, st->B, out_count, out_total);
+    if (st->BP > 0 && C > 0)
+        k_bl_gather<<<grid_for(wb, wb), kBlock, 0, stream>>>(
+            st->u, st->v, st->L, st->K, st->B, pcap_limit, st->slots, st->BP, out_idx,
+            out_val);
+    DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
 int dgc_stream_capacity(const dgc_state* st, int64_t* cap_offsets) {
     if (!st || !cap_offsets) return DGC_EINVAL;
     std::copy(st->plan.ebase.begin(), st->plan.ebase.end(), cap_offsets);
@@ -566,31 +742,15 @@ int dgc_encode(const dgc_state* cst, const int64_t* k, const uint32_t* idx,
                hipStream_t stream) {
     dgc_state* st = const_cast<dgc_state*>(cst);
     if (!st) return DGC_EINVAL;
-    const Plan& p = st->plan;
-    int rc = check_k(st, k);
-    if (rc != DGC_OK) return rc;
-    int64_t K = 0;
-    for (int32_t t = 0; t < p.T; ++t) K += k[t];
-    if (!entries || !aligned(entries, 8)) return DGC_EINVAL;
-    if (K > 0 && (!idx || !val || !runs || !vals || !aligned(idx, 4) ||
-                  !aligned(val, 4) || !aligned(runs, 2) || !aligned(vals, 4)))
-        return DGC_EINVAL;
-    rc = upload_k(st, k, stream);
-    if (rc != DGC_OK) return rc;
-    st->last_stream = stream;
-    const int T = p.T;
-    const int pg = st->num_cus * 8;
-    DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
-    if (st->KT > 0)
-        k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, idx, st->ta,
-                                                                 st->sc, st->KT);
-    k_enc_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ta, st->tb, entries);
-    if (st->KT > 0)
-        k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, idx, val,
-                                                                 st->tb, runs, vals, st->KT);
-    DGC_LAUNCH_CHECK();
-    DGC_TRY(timer_end(st, DGC_TIMER_ENCODE, stream));
-    return DGC_OK;
+    return encode_impl(st, k, nullptr, idx, val, runs, vals, entries, stream);
+}
+
+int dgc_encode_counts(const dgc_state* cst, const int64_t* cap, const int64_t* count,
+                      const uint32_t* idx, const float* val, uint16_t* runs,
+                      float* vals, int64_t* entries, hipStream_t stream) {
+    dgc_state* st = const_cast<dgc_state*>(cst);
+    if (!st || !count || !aligned(count, 8)) return DGC_EINVAL;
+    return encode_impl(st, cap, count, idx, val, runs, vals, entries, stream);
 }
 
 int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,

@@ -1,0 +1,443 @@
+// kernels_binlocal.hpp -- the bin-local selector on gfx950.
+//
+// Source: the AdaComp page ("AdaComp : Adaptive Residual Gradient Compression
+// for Data-Parallel Distributed Training"), Abstract (residues are selected
+// locally; the rate follows local activity) and "Citations in the corpus"
+// (each layer's residual vector is cut into fixed-size bins; a bin's largest
+// absolute value is its threshold).  What meets the threshold is not stated;
+// the rule here: in bin b of L entries (restarting at each tensor),
+//   theta_b = max key(v_j),  entry i is salient iff key(v_i) != 0 and
+//   key(fl32(v_i + u_i)) >= theta_b,
+// with v and u after this step's momentum correction and accumulation, and
+// key(x) = bits(x) & 0x7FFFFFFF.  Clip, momentum and masking are DGC's.  At
+// most cap_t salient entries are delivered per tensor, first in index order;
+// only delivered entries are masked.
+//
+// Pieces here are a whole number of bins (L * floor(1024 / L) elements), so
+// every threshold is known inside the wave that owns the piece:
+//   k_bl_fused   momentum update, per-bin maxima in the wave's LDS, salient
+//                flags, ranks by ballot; the piece's entries go to its own
+//                slots; u and v are masked in registers when the piece's
+//                entries are sure to fit below cap_t.
+//   k_bl_group   per 1024-piece group: exclusive prefix of piece counts.
+//   k_bl_tscan   per tensor: group offsets, delivered and salient counts.
+//   k_bl_gather  per piece: slots -> (idx, val) at the final position, masks
+//                what k_bl_fused could not; a piece that overflowed its
+//                slots is re-derived from u and v (same arithmetic, same
+//                flags).
+#pragma once
+
+#include "dgc_device.hpp"
+#include "kernel_fused.hpp"
+
+namespace dgc {
+
+constexpr int64_t kBlGroup = 1024;  // pieces per prefix group
+constexpr int64_t kMaxBin = kPiece;  // largest bin length
+
+// Bin-local tables (device pointers into the workspace), passed by value.
+struct DevBins {
+    const int64_t* plen;   // [T] piece length, a whole number of bins
+    const int64_t* magic;  // [T] ceil(2^32 / L) (0 when L = 1)
+    const int64_t* pbase;  // [T+1] first piece of each tensor
+    const int64_t* gbase;  // [T+1] first prefix group of each tensor
+    const int64_t* pcap;   // [T] slots per piece
+    PieceDesc* pdesc;      // [pieces]
+    uint32_t* cnt;         // [pieces] salient entries of each piece
+    uint32_t* pre;         // [pieces] exclusive prefix inside its group
+    uint32_t* gsum;        // [groups] salient entries of each group
+    uint32_t* goff;        // [groups] exclusive prefix inside its tensor
+};
+
+// Bin of the element e elements after a piece start (e < 1024): e / L by a
+// multiply-high, exact for e < 2^22 / L.
+__device__ __forceinline__ uint32_t bl_bin(uint32_t e, uint32_t magic) {
+    return magic ? __umulhi(e, magic) : e;
+}
+
+// LDS written by some lanes of a wave and read by others, with no other
+// wave involved: a wave's LDS operations complete in order, so a compiler
+// fence at wavefront scope suffices.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Offset from the piece start of a lane's element (i, c): float4 units
+// (64 lanes x 4) when the start is 16-byte aligned, else 64 consecutive
+// elements per (i, c).  Both orders rank in index order below.
+template <bool kAligned>
+__device__ __forceinline__ uint32_t bl_off(int i, int c, int lane) {
+    return kAligned ? uint32_t(((i * kWave + lane) << 2) + c)
+                    : uint32_t((i * 4 + c) * kWave + lane);
+}
+
+// Salient flags of one piece of len elements.  vn / un hold v and u after
+// the update (anything for elements past len).  th is this wave's 1024-entry
+// LDS row.
+template <bool kAligned>
+__device__ __forceinline__ void bl_flags(const float (&vn)[kRounds][4],
+                                         const float (&un)[kRounds][4],
+                                         uint32_t len, uint32_t magic,
+                                         uint32_t* th, bool (&f)[kRounds][4]) {
+    const int lane = lane_id();
+    uint4* th4 = reinterpret_cast<uint4*>(th);
+    wave_lds_sync();  // after any reads of the row for a previous piece
+#pragma unroll
+    for (int q = 0; q < int(kPiece / (4 * kWave)); ++q)
+        th4[q * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+    // per-bin maxima: runs of one bin inside a lane's four elements are
+    // folded first; a round that lies in one bin is folded across the wave
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        if (kAligned) {
+            const uint32_t r0 = uint32_t(i * kWave * 4);
+            const bool one_bin = bl_bin(r0, magic) == bl_bin(r0 + kWave * 4 - 1, magic);
+            uint32_t rb = bl_bin(bl_off<true>(i, 0, lane), magic);
+            uint32_t rk = bl_off<true>(i, 0, lane) < len ? mag_key(vn[i][0]) : 0u;
+#pragma unroll
+            for (int c = 1; c < 4; ++c) {
+                const uint32_t e = bl_off<true>(i, c, lane);
+                const uint32_t b = bl_bin(e, magic);
+                const uint32_t k = e < len ? mag_key(vn[i][c]) : 0u;
+                if (b != rb) {
+                    if (rk) atomicMax(&th[rb], rk);
+                    rb = b;
+                    rk = k;
+                } else {
+                    rk = max(rk, k);
+                }
+            }
+            if (one_bin) {
+#pragma unroll
+                for (int d = kWave / 2; d >= 1; d >>= 1)
+                    rk = max(rk, uint32_t(__shfl_xor(int(rk), d, kWave)));
+                if (lane == 0 && rk) atomicMax(&th[rb], rk);
+            } else if (rk) {
+                atomicMax(&th[rb], rk);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t e = bl_off<false>(i, c, lane);
+                const uint32_t k = e < len ? mag_key(vn[i][c]) : 0u;
+                if (k) atomicMax(&th[bl_bin(e, magic)], k);
+            }
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t e = bl_off<kAligned>(i, c, lane);
+            const uint32_t key = mag_key(vn[i][c]);
+            const uint32_t ahead = mag_key(__fadd_rn(vn[i][c], un[i][c]));
+            f[i][c] = e < len && key != 0u && ahead >= th[bl_bin(e, magic)];
+        }
+}
+
+// Ranks of the flagged elements in index order, and their number.
+template <bool kAligned>
+__device__ __forceinline__ uint32_t bl_ranks(const bool (&f)[kRounds][4],
+                                             uint32_t (&rank)[kRounds][4]) {
+    const uint64_t lt = lanemask_lt();
+    uint32_t total = 0;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        uint64_t b[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = __ballot(f[i][c]);
+        if (kAligned) {
+            uint32_t before = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) before += __popcll(b[c] & lt);
+            uint32_t own = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                rank[i][c] = total + before + own;
+                own += f[i][c];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) total += __popcll(b[c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                rank[i][c] = total + __popcll(b[c] & lt);
+                total += __popcll(b[c]);
+            }
+        }
+    }
+    return total;
+}
+
+// Whether k_bl_fused masks the piece itself: its entries fit its slots, and
+// even if every element before the piece were salient they would land
+// below the tensor's capacity.
+__device__ __forceinline__ bool bl_masks_early(uint32_t count, uint32_t pcap,
+                                               int64_t start_local, int64_t cap) {
+    return count <= pcap && start_local + int64_t(count) <= cap;
+}
+
+template <bool kAligned>
+__device__ __forceinline__ void bl_fused_piece(
+    const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
+    int64_t e0, uint32_t len, int t, const DevLayout& L, const DevK& K,
+    const DevBins& B, float s, float m, uint32_t pcap_limit, uint2* __restrict__ slots,
+    int64_t p, uint32_t* th) {
+    const int lane = lane_id();
+    const int64_t e1 = e0 + len;
+    float un[kRounds][4], vn[kRounds][4];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        float gg[4] = {0, 0, 0, 0}, uu[4] = {0, 0, 0, 0}, vv[4] = {0, 0, 0, 0};
+        if (kAligned) {
+            const int64_t el = e0 + bl_off<true>(i, 0, lane);
+            if (el + 4 <= e1) {
+                const float4 a = ld_stream(g + el), b = ld_stream(u + el),
+                             c = ld_stream(v + el);
+                gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w;
+                uu[0] = b.x; uu[1] = b.y; uu[2] = b.z; uu[3] = b.w;
+                vv[0] = c.x; vv[1] = c.y; vv[2] = c.z; vv[3] = c.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (el + c < e1) { gg[c] = g[el + c]; uu[c] = u[el + c]; vv[c] = v[el + c]; }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t el = e0 + bl_off<false>(i, c, lane);
+                if (el < e1) { gg[c] = g[el]; uu[c] = u[el]; vv[c] = v[el]; }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            momentum_update(gg[c], s, m, uu[c], vv[c]);
+            un[i][c] = uu[c];
+            vn[i][c] = vv[c];
+        }
+    }
+    const uint32_t magic = uint32_t(B.magic[t]);
+    const int64_t o = L.o[t];
+    const int64_t cap = K.k[t];
+    const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
+    bool f[kRounds][4];
+    uint32_t rank[kRounds][4];
+    bl_flags<kAligned>(vn, un, len, magic, th, f);
+    const uint32_t total = bl_ranks<kAligned>(f, rank);
+    const bool early = bl_masks_early(total, pcap, e0 - o, cap);
+    if (lane == 0) B.cnt[p] = total;
+    if (total && total <= pcap) {
+        uint2* sl = slots + L.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (f[i][c])
+                    sl[rank[i][c]] = make_uint2(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
+                                                __float_as_uint(vn[i][c]));
+    }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        float uu[4], vv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool z = early && f[i][c];
+            uu[c] = z ? 0.0f : un[i][c];
+            vv[c] = z ? 0.0f : vn[i][c];
+        }
+        if (kAligned) {
+            const int64_t el = e0 + bl_off<true>(i, 0, lane);
+            if (el + 4 <= e1) {
+                st_stream(u + el, uu[0], uu[1], uu[2], uu[3]);
+                st_stream(v + el, vv[0], vv[1], vv[2], vv[3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (el + c < e1) { u[el + c] = uu[c]; v[el + c] = vv[c]; }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t el = e0 + bl_off<false>(i, c, lane);
+                if (el < e1) { u[el] = uu[c]; v[el] = vv[c]; }
+            }
+        }
+    }
+}
+
+// Element-wise pass, one wave per piece.  With clipping off block 0 also
+// writes the call's scalar outputs (norm -1, scale 1).  pcap_limit = 0
+// sends every piece through the re-derivation in k_bl_gather (a test hook).
+__global__ __launch_bounds__(kBlock) void k_bl_fused(
+    const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
+    DevLayout L, DevK K, DevBins B, Scalars* __restrict__ sc, int clip_on, float m,
+    uint32_t pcap_limit, uint2* __restrict__ slots, int64_t n_pieces,
+    double* __restrict__ out_norm, float* __restrict__ out_scale) {
+    __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
+    const float s = clip_on ? sc->scale : 1.0f;
+    if (!clip_on && blockIdx.x == 0 && threadIdx.x == 0) {
+        sc->norm = -1.0;
+        sc->scale = 1.0f;
+        if (out_norm) *out_norm = -1.0;
+        if (out_scale) *out_scale = 1.0f;
+    }
+    const int64_t p = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+    if (p >= n_pieces) return;  // no block-wide barrier follows
+    const PieceDesc d = B.pdesc[p];
+    const int t = wave_uniform(int(d.tensor));
+    uint32_t* row = th[threadIdx.x >> 6];
+    if ((d.start & 3) == 0)
+        bl_fused_piece<true>(g, u, v, d.start, d.len, t, L, K, B, s, m, pcap_limit,
+                             slots, p, row);
+    else
+        bl_fused_piece<false>(g, u, v, d.start, d.len, t, L, K, B, s, m, pcap_limit,
+                              slots, p, row);
+}
+
+// Piece descriptors for the current bin lengths, one thread per piece.
+__global__ __launch_bounds__(kBlock) void k_bl_pdesc(DevLayout L, DevBins B,
+                                                     int64_t n_pieces) {
+    const int64_t p = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (p >= n_pieces) return;
+    const int t = find_seg(B.pbase, L.T, p);
+    const int64_t pl = B.plen[t];
+    const int64_t off = (p - B.pbase[t]) * pl;
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    PieceDesc d;
+    d.start = L.o[t] + off;
+    d.tensor = uint32_t(t);
+    d.len = uint32_t(min(pl, nt - off));
+    B.pdesc[p] = d;
+}
+
+// One wave per group of kBlGroup pieces of one tensor: exclusive prefix of
+// the piece counts inside the group, and the group's total.
+__global__ __launch_bounds__(kBlock) void k_bl_group(DevLayout L, DevBins B,
+                                                     int64_t n_groups) {
+    const int64_t gi = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+    if (gi >= n_groups) return;
+    const int lane = lane_id();
+    const int t = find_seg(B.gbase, L.T, gi);
+    const int64_t p0 = B.pbase[t] + (gi - B.gbase[t]) * kBlGroup;
+    const int64_t p1 = min(B.pbase[t + 1], p0 + kBlGroup);
+    constexpr int kPer = int(kBlGroup / kWave);
+    uint32_t c[kPer];
+    uint32_t local = 0;
+    const int64_t q0 = p0 + int64_t(lane) * kPer;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        c[j] = q0 + j < p1 ? B.cnt[q0 + j] : 0u;
+        local += c[j];
+    }
+    const uint32_t inc = wave_inclusive_scan(local);
+    uint32_t run = inc - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (q0 + j < p1) B.pre[q0 + j] = run;
+        run += c[j];
+    }
+    if (lane == kWave - 1) B.gsum[gi] = inc;
+}
+
+// One block per tensor: group offsets, then count = min(total, cap) and
+// total (salient entries, delivered or not).
+__global__ __launch_bounds__(kBlock) void k_bl_tscan(DevK K, DevBins B,
+                                                     int64_t* __restrict__ out_count,
+                                                     int64_t* __restrict__ out_total) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int t = blockIdx.x;
+    const int64_t gb = B.gbase[t], ng = B.gbase[t + 1] - gb;
+    const uint32_t total = block_scan_range<uint32_t>(B.gsum + gb, B.goff + gb, ng, 0u, lds);
+    if (threadIdx.x == 0) {
+        out_count[t] = min(int64_t(total), K.k[t]);
+        if (out_total) out_total[t] = int64_t(total);
+    }
+}
+
+// Re-derive one overflowed piece from u and v (as k_bl_fused left them:
+// unmasked) and deliver its entries from position pos0 on.
+template <bool kAligned>
+__device__ __forceinline__ void bl_redo_piece(
+    float* __restrict__ u, float* __restrict__ v, int64_t e0, uint32_t len,
+    uint32_t magic, int64_t o, int64_t pos0, int64_t nd, int64_t obase,
+    uint32_t* __restrict__ out_idx, float* __restrict__ out_val, uint32_t* th) {
+    const int lane = lane_id();
+    const int64_t e1 = e0 + len;
+    float un[kRounds][4], vn[kRounds][4];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t el = e0 + bl_off<kAligned>(i, c, lane);
+            un[i][c] = el < e1 ? u[el] : 0.0f;
+            vn[i][c] = el < e1 ? v[el] : 0.0f;
+        }
+    bool f[kRounds][4];
+    uint32_t rank[kRounds][4];
+    bl_flags<kAligned>(vn, un, len, magic, th, f);
+    (void)bl_ranks<kAligned>(f, rank);
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (f[i][c] && int64_t(rank[i][c]) < nd) {
+                const uint32_t e = bl_off<kAligned>(i, c, lane);
+                const int64_t at = obase + pos0 + rank[i][c];
+                out_idx[at] = uint32_t(e0 - o) + e;
+                out_val[at] = vn[i][c];
+                u[e0 + e] = 0.0f;
+                v[e0 + e] = 0.0f;
+            }
+}
+
+// Final placement, one wave per piece (grid-stride).  Output of tensor t
+// starts at koff[t]; its piece p starts at goff[group] + pre[p].
+__global__ __launch_bounds__(kBlock) void k_bl_gather(
+    float* __restrict__ u, float* __restrict__ v, DevLayout L, DevK K, DevBins B,
+    uint32_t pcap_limit, const uint2* __restrict__ slots, int64_t n_pieces,
+    uint32_t* __restrict__ out_idx, float* __restrict__ out_val) {
+    __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
+    const int lane = lane_id();
+    uint32_t* row = th[threadIdx.x >> 6];
+    const int64_t w0 = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+    const int64_t nw = (int64_t(gridDim.x) * kBlock) >> 6;
+    for (int64_t p = w0; p < n_pieces; p += nw) {
+        const uint32_t count = B.cnt[p];
+        if (count == 0) continue;
+        const PieceDesc d = B.pdesc[p];
+        const int t = wave_uniform(int(d.tensor));
+        const int64_t o = L.o[t];
+        const int64_t cap = K.k[t];
+        const int64_t jp = p - B.pbase[t];
+        const int64_t pos0 = int64_t(B.goff[B.gbase[t] + jp / kBlGroup]) + B.pre[p];
+        if (pos0 >= cap) continue;
+        const int64_t nd = min(int64_t(count), cap - pos0);
+        const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
+        const int64_t obase = K.koff[t];
+        if (count <= pcap) {
+            const bool early = bl_masks_early(count, pcap, d.start - o, cap);
+            const uint2* sl = slots + L.slbase[t] + jp * int64_t(pcap);
+            for (int64_t r = lane; r < nd; r += kWave) {
+                const uint2 x = sl[r];
+                out_idx[obase + pos0 + r] = x.x;
+                out_val[obase + pos0 + r] = __uint_as_float(x.y);
+                if (!early) {
+                    u[o + x.x] = 0.0f;
+                    v[o + x.x] = 0.0f;
+                }
+            }
+        } else if ((d.start & 3) == 0) {
+            bl_redo_piece<true>(u, v, d.start, d.len, uint32_t(B.magic[t]), o, pos0, nd,
+                                obase, out_idx, out_val, row);
+        } else {
+            bl_redo_piece<false>(u, v, d.start, d.len, uint32_t(B.magic[t]), o, pos0, nd,
+                                 obase, out_idx, out_val, row);
+        }
+    }
+}
+
+}  // namespace dgc

@@ -36,14 +36,25 @@ __device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
     return uint32_t(gap >> 16);
 }
 
+// Entries of tensor t to encode: k_t, or, when the counts live on the
+// device (a data-dependent selector), that count if it lies in [0, k_t] and
+// else none (k_enc_scan flags it).
+__device__ __forceinline__ int64_t enc_len(const DevK& K, const int64_t* kdev, int t) {
+    const int64_t k = K.k[t];
+    if (!kdev) return k;
+    const int64_t c = kdev[t];
+    return (c < 0 || c > k) ? 0 : c;
+}
+
 // Per k-tile: number of fillers its entries need.
 __global__ __launch_bounds__(kBlock) void k_enc_count(
-    DevLayout L, DevK K, const uint32_t* __restrict__ idx,
-    uint32_t* __restrict__ tile_f, Scalars* __restrict__ sc, int64_t n_ktiles) {
+    DevLayout L, DevK K, const int64_t* __restrict__ kdev,
+    const uint32_t* __restrict__ idx, uint32_t* __restrict__ tile_f,
+    Scalars* __restrict__ sc, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     for (int64_t vt = blockIdx.x; vt < n_ktiles; vt += gridDim.x) {
         const int t = int(K.kmap[vt]);
-        const int64_t kt = K.k[t];
+        const int64_t kt = enc_len(K, kdev, t);
         const int64_t nt = L.o[t + 1] - L.o[t];
         const uint32_t* id = idx + K.koff[t];
         const int64_t i0 = (vt - K.ktbase[t]) * kTile;
@@ -65,25 +76,30 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
 
 // One block per tensor: scan the filler counts; E_t = k_t + fillers.
 __global__ __launch_bounds__(kBlock) void k_enc_scan(
-    DevLayout L, DevK K, const uint32_t* __restrict__ tile_f,
-    uint32_t* __restrict__ tile_foff, int64_t* __restrict__ entries) {
+    DevLayout L, DevK K, const int64_t* __restrict__ kdev,
+    const uint32_t* __restrict__ tile_f, uint32_t* __restrict__ tile_foff,
+    int64_t* __restrict__ entries, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t kb = K.ktbase[t], ntile = K.ktbase[t + 1] - kb;
     const uint32_t carry = block_scan_range<uint32_t>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
-    if (threadIdx.x == 0) entries[t] = K.k[t] + int64_t(carry);
+    if (threadIdx.x == 0) {
+        if (kdev && (kdev[t] < 0 || kdev[t] > K.k[t])) latch_error(sc, kErrCorrupt);
+        entries[t] = enc_len(K, kdev, t) + int64_t(carry);
+    }
 }
 
 // Entry i lands at slot i + (fillers of entries <= i); its own fillers fill
 // the slots just before it.
 __global__ __launch_bounds__(kBlock) void k_enc_write(
-    DevLayout L, DevK K, const uint32_t* __restrict__ idx,
-    const float* __restrict__ val, const uint32_t* __restrict__ tile_foff,
-    uint16_t* __restrict__ runs, float* __restrict__ vals, int64_t n_ktiles) {
+    DevLayout L, DevK K, const int64_t* __restrict__ kdev,
+    const uint32_t* __restrict__ idx, const float* __restrict__ val,
+    const uint32_t* __restrict__ tile_foff, uint16_t* __restrict__ runs,
+    float* __restrict__ vals, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     for (int64_t vt = blockIdx.x; vt < n_ktiles; vt += gridDim.x) {
         const int t = int(K.kmap[vt]);
-        const int64_t kt = K.k[t];
+        const int64_t kt = enc_len(K, kdev, t);
         const int64_t nt = L.o[t + 1] - L.o[t];
         const uint32_t* id = idx + K.koff[t];
         const float* vl = val + K.koff[t];

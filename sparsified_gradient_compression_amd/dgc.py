@@ -26,6 +26,7 @@ DGC_TIMER_FUSED = 0
 DGC_TIMER_COMPRESS = 1
 DGC_TIMER_ENCODE = 2
 DGC_TIMER_DECODE = 3
+DGC_MAX_BIN = 1024
 
 _lib = None
 
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
     L.dgc_init_state.restype = ctypes.c_int
     L.dgc_compress.argtypes = [P, P, P, ctypes.c_double, P, P, P, P, P]
     L.dgc_compress.restype = ctypes.c_int
+    L.dgc_compress_binlocal.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
+                                        P, P, P]
+    L.dgc_compress_binlocal.restype = ctypes.c_int
+    L.dgc_encode_counts.argtypes = [P, P, P, P, P, P, P, P, P]
+    L.dgc_encode_counts.restype = ctypes.c_int
     L.dgc_stream_capacity.argtypes = [P, P]
     L.dgc_stream_capacity.restype = ctypes.c_int
     L.dgc_encode.argtypes = [P, P, P, P, P, P, P, P]
@@ -159,6 +165,17 @@ def dgc_compress(st, g, k, clip: float, out_idx, out_val, out_norm=None,
            "dgc_compress")
 
 
+def dgc_compress_binlocal(st, g, bin_len, cap, clip: float, out_idx, out_val,
+                          out_count, out_total=None, out_norm=None,
+                          out_scale=None, stream=None):
+    bl, cc = _i64(bin_len), _i64(cap)
+    _check(lib().dgc_compress_binlocal(st, _dp(g), _hp(bl), _hp(cc), float(clip),
+                                       _dp(out_idx), _dp(out_val), _dp(out_count),
+                                       _dp(out_total), _dp(out_norm),
+                                       _dp(out_scale), _stream(stream)),
+           "dgc_compress_binlocal")
+
+
 def dgc_stream_capacity(st, n_tensors: int) -> np.ndarray:
     out = np.zeros(n_tensors + 1, np.int64)
     _check(lib().dgc_stream_capacity(st, _hp(out)), "dgc_stream_capacity")
@@ -170,6 +187,14 @@ def dgc_encode(st, k, idx, val, runs, vals, entries, stream=None):
     _check(lib().dgc_encode(st, _hp(kk), _dp(idx), _dp(val), _dp(runs), _dp(vals),
                             _dp(entries), _stream(stream)),
            "dgc_encode")
+
+
+def dgc_encode_counts(st, cap, count, idx, val, runs, vals, entries, stream=None):
+    cc = _i64(cap)
+    _check(lib().dgc_encode_counts(st, _hp(cc), _dp(count), _dp(idx), _dp(val),
+                                   _dp(runs), _dp(vals), _dp(entries),
+                                   _stream(stream)),
+           "dgc_encode_counts")
 
 
 def dgc_decode_accumulate(st, runs: Sequence, vals: Sequence, entries: Sequence,
@@ -273,6 +298,8 @@ class Learner:
         self.runs = torch.empty(C, dtype=torch.int16, device=dev)
         self.vals = torch.empty(C, dtype=torch.float32, device=dev)
         self.entries = torch.empty(self.T, dtype=torch.int64, device=dev)
+        self.count = torch.empty(self.T, dtype=torch.int64, device=dev)
+        self.total = torch.empty(self.T, dtype=torch.int64, device=dev)
 
     def compress(self, g, k: Sequence[int], clip: float, stream=None):
         """One step; returns (idx, val) views holding sum(k) entries."""
@@ -280,6 +307,23 @@ class Learner:
         dgc_compress(self.state, g, k, clip, self.idx, self.val, self.norm,
                      self.scale, stream)
         return self.idx[:K], self.val[:K]
+
+    def compress_binlocal(self, g, bin_len: Sequence[int], cap: Sequence[int],
+                          clip: float, stream=None):
+        """One step with the bin-local selector.  Returns (idx, val, count,
+        total): idx/val hold sum(cap) slots, tensor t's count[t] delivered
+        entries first in its cap[t] slots; total[t] = salient entries."""
+        C = int(sum(int(x) for x in cap))
+        dgc_compress_binlocal(self.state, g, bin_len, cap, clip, self.idx,
+                              self.val, self.count, self.total, self.norm,
+                              self.scale, stream)
+        return self.idx[:C], self.val[:C], self.count, self.total
+
+    def encode_counts(self, cap: Sequence[int], stream=None):
+        """Encode what compress_binlocal delivered (counts on the device)."""
+        dgc_encode_counts(self.state, cap, self.count, self.idx, self.val,
+                          self.runs, self.vals, self.entries, stream)
+        return self.runs, self.vals, self.entries
 
     def encode(self, k: Sequence[int], stream=None):
         dgc_encode(self.state, k, self.idx, self.val, self.runs, self.vals,

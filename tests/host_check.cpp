@@ -52,6 +52,10 @@ int main() {
     CHECK(dgc_workspace_bytes(0, one, one, &bytes) == DGC_EINVAL);
     CHECK(dgc_workspace_bytes(1, nullptr, one, &bytes) == DGC_EINVAL);
     CHECK(dgc_workspace_bytes(1, one, one, nullptr) == DGC_EINVAL);
+    CHECK(dgc_compress_binlocal(nullptr, nullptr, one, one, 0.0, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr) == DGC_EINVAL);
+    CHECK(dgc_encode_counts(nullptr, one, nullptr, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, nullptr) == DGC_EINVAL);
     for (int code = -6; code <= 1; ++code) CHECK(dgc_error_string(code) != nullptr);
     dgc_destroy_state(nullptr);
     std::printf("host check: ok\n");

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     L = dgc.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -88,6 +88,10 @@ def test_init_and_calls_reject_bad_arguments_before_any_launch():
     assert st.value is None
     assert L.dgc_compress(None, None, None, 0.0, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_encode(None, None, None, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_compress_binlocal(None, None, None, None, 0.0, None, None, None, None,
+                                   None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_encode_counts(None, None, None, None, None, None, None, None,
+                               None) == dgc.DGC_EINVAL
     assert L.dgc_decode_accumulate(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_get_status(None) == dgc.DGC_EINVAL
     assert L.dgc_set_option(None, 1, 0) == dgc.DGC_EINVAL
@@ -114,3 +118,21 @@ def test_build_flags_keep_ieee_binary32():
     assert "-fno-gpu-flush-denormals-to-zero" in flags
     assert "-packed-fp32-ops" in flags
     assert "gfx950" in flags
+
+
+def test_bin_index_by_multiply_high_is_exact():
+    """The bin-local kernels find the bin of offset e (< 1024) inside a piece
+    as (e * ceil(2^32 / L)) >> 32 (e itself for L = 1); that equals e // L
+    for every bin length the library accepts."""
+    e = np.arange(1024, dtype=np.uint64)
+    for L in range(2, dgc.DGC_MAX_BIN + 1):
+        magic = np.uint64(((1 << 32) + L - 1) // L)
+        assert np.array_equal((e * magic) >> np.uint64(32), e // np.uint64(L)), L
+
+
+def test_bin_local_pieces_hold_whole_bins():
+    """Pieces of L * floor(1024 / L) elements: whole bins, never fewer than
+    513 elements, so ceil(n / 513) pieces per tensor always suffice."""
+    for L in range(1, dgc.DGC_MAX_BIN + 1):
+        plen = L * (1024 // L)
+        assert plen % L == 0 and 513 <= plen <= 1024

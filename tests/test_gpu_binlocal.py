@@ -1,0 +1,300 @@
+"""GPU parity of the bin-local selector (AdaComp page, Abstract and "Citations
+in the corpus"): dgc_compress_binlocal + dgc_encode_counts + decode through
+the C ABI against the CPU oracle, bit for bit on delivered and salient
+counts, indices, values, u/v state, encoded streams and dense sums; the
+clipping norm to relative 1e-6.
+
+Layouts span many pieces with ragged tails and unaligned tensor starts; bin
+lengths from 1 to 1024; capacities from none to all; both placement paths
+(slots, and re-derivation of every piece).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import f32_bits, first_diff, say
+from sparsified_gradient_compression_amd import dgc
+from sparsified_gradient_compression_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dgc.lib()  # raises if the HIP library is missing
+    return torch
+
+
+class BinPair:
+    """One learner on both sides for the bin-local selector."""
+
+    def __init__(self, sizes, k_max, momentum=0.9, path=0):
+        self.sizes = [int(s) for s in sizes]
+        self.learner = dgc.Learner(self.sizes, k_max, momentum)
+        self.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+        n = sum(self.sizes)
+        self.u = np.zeros(n, np.float32)
+        self.v = np.zeros(n, np.float32)
+        self.m = momentum
+
+    def step(self, g, L, cap, clip, tag=""):
+        import torch
+        lr = self.learner
+        gd = torch.from_numpy(g).cuda()
+        idx, val, count, total = lr.compress_binlocal(gd, L, cap, clip)
+        torch.cuda.synchronize()
+        g_idx = idx.cpu().numpy().view(np.uint32)
+        g_val = val.cpu().numpy()
+        g_cnt = count.cpu().numpy()
+        g_tot = total.cpu().numpy()
+        o_idx, o_val, o_cnt, o_tot, o_norm, o_s = oracle.binlocal_step(
+            self.sizes, L, cap, g, self.u, self.v, self.m, clip)
+        assert lr.status() == dgc.DGC_OK, (tag, "status")
+        assert np.array_equal(g_tot, o_tot), (tag, "total", first_diff(g_tot, o_tot))
+        assert np.array_equal(g_cnt, o_cnt), (tag, "count", first_diff(g_cnt, o_cnt))
+        norm = float(lr.norm.cpu()[0])
+        if clip > 0:
+            assert abs(norm - o_norm) <= 1e-6 * o_norm, (tag, norm, o_norm)
+        else:
+            assert norm == -1.0
+        assert np.float32(lr.scale.cpu()[0]) == o_s, (tag, "scale")
+        off = 0
+        for t, c in enumerate(cap):
+            a, b = off, off + int(o_cnt[t])
+            assert np.array_equal(g_idx[a:b], o_idx[a:b]), (
+                tag, t, "idx", first_diff(g_idx[a:b], o_idx[a:b]))
+            assert np.array_equal(f32_bits(g_val[a:b]), f32_bits(o_val[a:b])), (
+                tag, t, "val")
+            off += int(c)
+        gu = lr.u[: len(self.u)].cpu().numpy()
+        gv = lr.v[: len(self.v)].cpu().numpy()
+        assert np.array_equal(f32_bits(gu), f32_bits(self.u)), (
+            tag, "u", first_diff(f32_bits(gu), f32_bits(self.u)))
+        assert np.array_equal(f32_bits(gv), f32_bits(self.v)), (
+            tag, "v", first_diff(f32_bits(gv), f32_bits(self.v)))
+        return o_idx, o_val, o_cnt, o_tot
+
+    def check_encode(self, cap, o_idx, o_val, o_cnt, tag=""):
+        """GPU streams from the device counts against the oracle's encoder;
+        returns the oracle's streams per tensor."""
+        import torch
+        runs, vals, entries = self.learner.encode_counts(cap)
+        torch.cuda.synchronize()
+        assert self.learner.status() == dgc.DGC_OK, (tag, "encode status")
+        scap = self.learner.cap
+        r = runs.cpu().numpy().view(np.uint16)
+        v = vals.cpu().numpy()
+        e = entries.cpu().numpy()
+        want = []
+        off = 0
+        for t, nt in enumerate(self.sizes):
+            i = o_idx[off:off + o_cnt[t]]
+            x = o_val[off:off + o_cnt[t]]
+            wr, wv = oracle.encode(i, x, cap=max(int(cap[t]) + nt // 65536, 1))
+            gr = r[scap[t]:scap[t] + e[t]]
+            gvv = v[scap[t]:scap[t] + e[t]]
+            assert np.array_equal(gr, wr), (tag, t, "runs", first_diff(gr, wr))
+            assert np.array_equal(f32_bits(gvv), f32_bits(wv)), (tag, t, "vals")
+            want.append((wr, wv))
+            off += int(cap[t])
+        return want
+
+
+def check_decode(pairs, streams, sizes, tag=""):
+    import torch
+    n = int(sum(sizes))
+    dense = torch.zeros(max(n, 1), dtype=torch.float32, device="cuda")
+    dgc.decode_accumulate(pairs[0].learner,
+                          [(p.learner.runs, p.learner.vals, p.learner.entries)
+                           for p in pairs], dense)
+    got = dense[:n].cpu().numpy()
+    assert pairs[0].learner.status() == dgc.DGC_OK
+    want = np.zeros(n, np.float32)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    for per_learner in streams:
+        for t, (wr, wv) in enumerate(per_learner):
+            assert oracle.decode_accumulate(wr, wv, want[off[t]:off[t + 1]]) == 0
+    assert np.array_equal(f32_bits(got), f32_bits(want)), (tag, first_diff(got, want))
+
+
+def run(sizes, Ls, caps, grads, clip, learners=1, path=0, k_max=None, tag=""):
+    """Steps of `learners` learners; grads(w, step) -> float32[n]."""
+    k_max = list(sizes) if k_max is None else k_max
+    pairs = [BinPair(sizes, k_max, path=path) for _ in range(learners)]
+    for step, cap in enumerate(caps):
+        streams = []
+        for w, p in enumerate(pairs):
+            say(f"{tag} step {step} learner {w} T={len(sizes)} n={sum(sizes)}")
+            o_idx, o_val, o_cnt, _ = p.step(grads(w, step), Ls, cap, clip,
+                                            tag=f"{tag} s{step} w{w}")
+            streams.append(p.check_encode(cap, o_idx, o_val, o_cnt,
+                                          tag=f"{tag} s{step} w{w}"))
+        check_decode(pairs, streams, sizes, tag=f"{tag} s{step}")
+    return pairs
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("L", [1, 3, 50, 64, 500, 1000, 1024])
+def test_flat1m_bin_lengths(L, path):
+    """One 2**20 tensor, Laplace gradients, two steps, no truncation."""
+    wl = W.get("flat1m")
+    n = wl.n
+    run([n], [L], [[n], [n]], lambda w, s: W.gradient(wl, w, s), 0.0, path=path,
+        tag=f"flat1m L{L} p{path}")
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_resnet50_layout_scaled(path):
+    """ResNet-50's 161 tensors (scaled 1/8: odd sizes, unaligned starts),
+    conv bins of 50 and 500 elsewhere, clipping on, three steps."""
+    wl = W.scaled(W.get("resnet50"), 8)
+    Ls = [50 if s > 10000 else 500 for s in wl.sizes]
+    caps = [list(wl.sizes)] * 3
+    run(list(wl.sizes), Ls, caps, lambda w, s: W.gradient(wl, w, s), wl.clip, path=path,
+        tag=f"rn50/8 p{path}")
+
+
+def test_flat1b_shape_scaled_four_learners():
+    """The 64-chunk layout (scaled 1/256), four learners, two steps."""
+    wl = W.scaled(W.get("flat1b"), 256)
+    sizes = list(wl.sizes)
+    run(sizes, [512] * len(sizes), [sizes] * 2, lambda w, s: W.gradient(wl, w, s),
+        wl.clip, learners=4, tag="1b/256")
+
+
+# ---------------------------------------------------------------- capacity
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_truncation_keeps_the_rest_in_the_residual(path):
+    """Capacities well below the salient count: the first cap entries in
+    index order leave, the rest stay unmasked; three steps so the residual
+    grows; k_max = n keeps the slots large (masking happens in the
+    placement pass for pieces past the capacity)."""
+    rng = np.random.default_rng(61)
+    sizes = [300001, 70000, 4099]
+    n = sum(sizes)
+    caps = [[3000, 700, 41], [100, 0, 4099], [300001, 7, 1]]
+    grads = [rng.laplace(0, 1e-2, n).astype(np.float32) for _ in range(3)]
+    run(sizes, [128, 1000, 7], caps, lambda w, s: grads[s], 0.5, path=path,
+        tag=f"trunc p{path}")
+
+
+def test_small_slots_overflow_into_rederivation():
+    """k_max = n/1000 leaves about 30 slots per piece while ~5% of entries
+    are salient, so most pieces overflow and are re-derived; same bits."""
+    rng = np.random.default_rng(62)
+    sizes = [1 << 20, 200003]
+    n = sum(sizes)
+    k_max = [s // 1000 + 1 for s in sizes]
+    caps = [k_max, k_max]
+    grads = [rng.laplace(0, 1e-3, n).astype(np.float32) for _ in range(2)]
+    run(sizes, [256, 1024], caps, lambda w, s: grads[s], 0.0, k_max=k_max, tag="ovf")
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts(seed):
+    """Seeded random layouts (1-30 tensors of 0 to 300k elements, odd sizes),
+    random bin lengths in [1, 1024], random capacities, clipping on or off,
+    zero runs in the gradients; both placement paths."""
+    rng = np.random.default_rng([63, seed])
+    T = int(rng.integers(1, 31))
+    sizes = [int(x) for x in rng.choice([0, 1, 2, 7, 300, 1023, 1024, 4099, 65537,
+                                         131075, 299999], T)]
+    n = sum(sizes)
+    Ls = [int(x) for x in rng.integers(1, 1025, T)]
+    caps = [[s if rng.random() < 0.5 else int(rng.integers(0, s // 20 + 2)) for s in sizes]
+            for _ in range(2)]
+    caps = [[min(c, s) for c, s in zip(cc, sizes)] for cc in caps]
+    k_max = [max(caps[0][i], caps[1][i]) for i in range(T)]
+    grads = []
+    for _ in range(2):
+        g = rng.laplace(0, 1e-2, n).astype(np.float32)
+        g[rng.random(n) < 0.05] = 0.0
+        grads.append(g)
+    clip = float(rng.choice([0.0, 0.5]))
+    for path in (0, 1):
+        run(sizes, Ls, caps, lambda w, s: grads[s], clip, path=path, k_max=k_max,
+            tag=f"fuzz{seed} p{path}")
+
+
+def test_ties_zeros_and_denormals():
+    """Few distinct magnitudes (many ties at each bin's maximum), exact
+    zeros and denormals; the >= and v != 0 parts of the rule decide."""
+    rng = np.random.default_rng(64)
+    sizes = [65536 + 5, 4096, 999]
+    n = sum(sizes)
+    def grads(w, s):
+        g = rng.choice(np.array([0.0, 1e-40, 0.125, 0.25, 0.5]), n)
+        return (g * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    run(sizes, [64, 2, 333], [sizes] * 3, grads, 0.0, tag="ties")
+
+
+def test_determinism_repeat_bitwise():
+    import torch
+    wl = W.scaled(W.get("flat1b"), 512)
+    sizes = list(wl.sizes)
+    outs = []
+    for _ in range(2):
+        L = dgc.Learner(sizes, sizes)
+        for s in range(2):
+            g = torch.from_numpy(W.gradient(wl, 0, s)).cuda()
+            idx, val, count, total = L.compress_binlocal(g, [300] * len(sizes), sizes,
+                                                         wl.clip)
+        torch.cuda.synchronize()
+        c = count.cpu().numpy()
+        off = np.concatenate([[0], np.cumsum(sizes)])
+        # slots past each tensor's count are not written: compare the rest
+        keep = np.concatenate([np.arange(off[t], off[t] + c[t]) for t in range(len(sizes))])
+        outs.append((idx.cpu().numpy()[keep], f32_bits(val.cpu().numpy())[keep], c.copy(),
+                     total.cpu().numpy().copy(), f32_bits(L.u.cpu().numpy()).copy(),
+                     f32_bits(L.v.cpu().numpy()).copy()))
+        L.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_bad_arguments_and_corrupt_counts():
+    import torch
+    L = dgc.Learner([1000, 5000], [1000, 100])
+    g = torch.zeros(6000, device="cuda")
+    for bl, cap in (([0, 5], [1, 1]), ([5, 1025], [1, 1]), ([5, 5], [1001, 1]),
+                    ([5, 5], [1, 101]), ([5, 5], [-1, 1])):
+        with pytest.raises(dgc.DGCError) as e:
+            L.compress_binlocal(g, bl, cap, 0.0)
+        assert e.value.code == dgc.DGC_EINVAL
+    # a device count above the capacity encodes nothing and latches corrupt
+    L.compress_binlocal(g, [5, 5], [10, 10], 0.0)
+    L.count.copy_(torch.tensor([11, -1], dtype=torch.int64))
+    L.encode_counts([10, 10])
+    torch.cuda.synchronize()
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert L.entries.cpu().tolist() == [0, 0]
+    assert L.status() == dgc.DGC_OK
+
+
+def test_switching_selectors_on_one_state():
+    """Top-k and bin-local steps alternate on one learner; each matches its
+    oracle from the same state."""
+    import torch
+    from gpu_harness import Pair
+    rng = np.random.default_rng(65)
+    sizes = [131075, 70001]
+    n = sum(sizes)
+    p = Pair(sizes, sizes)
+    bp = BinPair.__new__(BinPair)
+    bp.sizes, bp.learner, bp.m = sizes, p.learner, 0.9
+    for step in range(4):
+        g = rng.laplace(0, 1e-2, n).astype(np.float32)
+        if step % 2 == 0:
+            p.step(g, [131, 71], 0.5, tag=f"topk s{step}")
+        else:
+            bp.u, bp.v = p.u, p.v
+            bp.step(g, [100, 7], sizes, 0.5, tag=f"bin s{step}")
