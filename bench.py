@@ -12,7 +12,12 @@ Prints one JSON line: value = gradient elements compressed per second
 kernel) timed with HIP events on its stream; cpu_baseline = the CPU oracle
 timed on a bounded sample of the same workload.
 
+With --selector binlocal the step uses AdaComp's bin-local selector instead
+of exact top-k (dgc_compress_binlocal + dgc_encode_counts, bins of
+--bin-len entries, at most n_t / --cap-den entries delivered per tensor).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat1b]
+                    [--selector topk|binlocal] [--bin-len 512] [--cap-den 8]
 """
 
 import argparse
@@ -28,34 +33,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_flat1b_traffic.json")
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "sparsified_gradient_compression_amd", "csrc", f)
-    for f in ("dgc_device.hpp", "kernel_fused.hpp")
-]
+CSRC = os.path.join(ROOT, "sparsified_gradient_compression_amd", "csrc")
+# committed counter summaries of the element-wise pass, per selector
+TRAFFIC = {
+    "topk": (os.path.join(ROOT, "profiles", "fused_flat1b_traffic.json"),
+             ("dgc_device.hpp", "kernel_fused.hpp")),
+    "binlocal": (os.path.join(ROOT, "profiles", "bl_fused_flat1b_traffic.json"),
+                 ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(selector="topk"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in TRAFFIC[selector][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(n_elems):
+def measured_traffic(n_elems, selector="topk"):
     """HBM bytes per launch of the element-wise pass from the committed
     rocprofv3 counter summary, if it was taken on the current kernel."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC[selector][0]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    if rec.get("kernel_source_sha") != kernel_source_sha(selector):
         return None
     if rec.get("n_elems") != n_elems:
         return None
@@ -83,7 +91,53 @@ def parse():
                          "previous learner's element-wise pass is done")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
+    ap.add_argument("--selector", choices=("topk", "binlocal"), default="topk",
+                    help="exact per-tensor top-k (DGC) or AdaComp's bin-local rule")
+    ap.add_argument("--bin-len", type=int, default=512,
+                    help="bin length for --selector binlocal (1..1024)")
+    ap.add_argument("--cap-den", type=int, default=8,
+                    help="--selector binlocal delivers at most n_t // cap_den "
+                         "entries per tensor")
     return ap.parse_args()
+
+
+def cpu_baseline_binlocal(wl, host_samples, n_chunks, seconds, bin_len, cap_den):
+    """As cpu_baseline, with the oracle's bin-local selector."""
+    import oracle
+    sizes = np.array(wl.sizes[:n_chunks], np.int64)
+    Ls = np.full(len(sizes), bin_len, np.int64)
+    caps = sizes // cap_den
+    n = int(sizes.sum())
+    u = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dense = np.zeros(n, np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    coff = np.concatenate([[0], np.cumsum(caps)])
+    t0 = time.perf_counter()
+    steps = 0
+    for cycle in range(4):
+        for g in host_samples:
+            idx, val, cnt, _, _, _ = oracle.binlocal_step(sizes, Ls, caps, g, u, v,
+                                                          wl.momentum, wl.clip)
+            dense[:] = 0
+            for t in range(len(sizes)):
+                a = coff[t]
+                r, vv = oracle.encode(idx[a:a + cnt[t]], val[a:a + cnt[t]])
+                oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * steps / dt / 1e9, 4),
+        "unit": "G elem/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"learner 0, {steps} steps, first {n_chunks} of "
+                   f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
+                   f"momentum, bin-local select (bins of {bin_len}), mask, encode, "
+                   f"decode; {dt:.1f} s"),
+    }
 
 
 def cpu_baseline(wl, host_samples, n_chunks, seconds):
@@ -141,7 +195,13 @@ def main():
     torch.cuda.set_device(0)
     wl = W.get(args.workload)
     T = len(wl.sizes)
-    ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
+    binlocal = args.selector == "binlocal"
+    if binlocal:
+        bins = [args.bin_len] * T
+        caps = [s // args.cap_den for s in wl.sizes]
+        ks = [caps]  # the delivery capacity takes k's place in the layout
+    else:
+        ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
     kmax = [max(k[t] for k in ks) for t in range(T)]
     n = wl.n
 
@@ -166,7 +226,7 @@ def main():
         L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
     dense = torch.zeros(n, dtype=torch.float32, device="cuda")
     main = torch.cuda.current_stream()
-    pipeline = args.pipeline
+    pipeline = args.pipeline and not binlocal
     if pipeline:
         # One stream per learner.  Learner w+1 starts once learner w's
         # element-wise pass is done (event recorded by the library), so its
@@ -180,7 +240,18 @@ def main():
 
     def one_step(s):
         t = s % gsteps
-        k = ks[t]
+        k = ks[t % len(ks)]
+        if binlocal:
+            for w, L in enumerate(learners):
+                L.compress_binlocal(grads[(w, t)], bins, caps, wl.clip)
+                if not args.fused_only:
+                    L.encode_counts(caps)
+            if not args.fused_only:
+                dense.zero_()
+                dgc.decode_accumulate(learners[0],
+                                      [(L.runs, L.vals, L.entries) for L in learners],
+                                      dense)
+            return
         if not pipeline:
             for w, L in enumerate(learners):
                 L.compress(grads[(w, t)], k, wl.clip)
@@ -248,22 +319,30 @@ def main():
             tot += a
             cnt += b
         times[name] = (tot, cnt)
-    path = [L.path_counts() for L in learners]
-    info = np.concatenate([L.select_info() for L in learners])
-    kk = np.array(ks[(args.warmup + args.steps - 1) % gsteps] * len(learners))
-    listed = info[:, 0] == 1
-    cand_ratio = info[listed, 2] / np.maximum(kk[listed], 1)
-
     elems = n * wl.learners * args.steps
     value = elems / elapsed / 1e9
     fused_ms = times["fused"][0] / max(times["fused"][1], 1)
     compress_ms = times["compress"][0] / max(times["compress"][1], 1)
-    fused_bytes = 20 * n  # read g, u, v; write u, v
-    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
-    k_total = sum(ks[0])
     clip = 1 if wl.clip > 0 else 0
-    pipeline_bytes = n * (20 + 4 * clip) + 16 * k_total
-    traffic = measured_traffic(n)
+    if binlocal:
+        # the last step's salient and delivered counts, all learners
+        salient = int(sum(int(L.total.sum()) for L in learners)) // len(learners)
+        delivered = int(sum(int(L.count.sum()) for L in learners)) // len(learners)
+        truncated = int(sum(int((L.total > L.count).sum()) for L in learners))
+        # read g, u, v; write u, v; 8 B per salient entry into its slot
+        fused_bytes = 20 * n + 8 * salient
+        # + norm re-read; + slot read, output write and u/v masking per entry
+        pipeline_bytes = n * (20 + 4 * clip) + 8 * salient + 16 * delivered
+        kernel_name = ("k_bl_fused (clip-scale + momentum correction + accumulation + "
+                       "per-bin maxima + salient entries to slots)")
+    else:
+        fused_bytes = 20 * n  # read g, u, v; write u, v
+        k_total = sum(ks[0])
+        pipeline_bytes = n * (20 + 4 * clip) + 16 * k_total
+        kernel_name = ("k_fused (clip-scale + momentum correction + accumulation + "
+                       "candidate output)")
+    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
+    traffic = measured_traffic(n, args.selector)
 
     out = {
         "metric": "gradient elements compressed/sec (G elem/s) and % of MI355X peak HBM GB/s",
@@ -280,18 +359,17 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name,
+            "selector": args.selector,
             "elements_per_learner": n,
             "tensors": T,
             "learners": wl.learners,
-            "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
-            "density": str(wl.densities[0]),
             "clip": wl.clip,
             "momentum": wl.momentum,
             "gradient_steps": wl.steps,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_fused (clip-scale + momentum correction + accumulation + candidate output)",
+            "kernel": kernel_name,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -308,19 +386,42 @@ def main():
             "compress_pipeline_frac_of_peak": round(
                 pipeline_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "compress_G_elem_per_s": round(n / (compress_ms * 1e-3) / 1e9, 2),
+        },
+    }
+    det = out["detail"]
+    if binlocal:
+        out["config"].update({"bin_len": args.bin_len,
+                              "cap_per_tensor": f"n_t // {args.cap_den}"})
+        det.update({"salient_per_learner": salient,
+                    "salient_fraction": round(salient / n, 5),
+                    "delivered_per_learner": delivered,
+                    "truncated_tensors": truncated})
+    else:
+        path = [L.path_counts() for L in learners]
+        info = np.concatenate([L.select_info() for L in learners])
+        kk = np.array(ks[(args.warmup + args.steps - 1) % gsteps] * len(learners))
+        listed = info[:, 0] == 1
+        cand_ratio = info[listed, 2] / np.maximum(kk[listed], 1)
+        out["config"].update({
+            "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
+            "density": str(wl.densities[0])})
+        det.update({
             "learner_pipelining": pipeline,
             "select_path_window_dense": [int(sum(p[0] for p in path)),
                                          int(sum(p[1] for p in path))],
             "overflow_tensors": int(info[:, 3].sum()),
             "window_candidates_over_k": ([round(float(cand_ratio.min()), 3),
                                           round(float(cand_ratio.max()), 3)]
-                                         if cand_ratio.size else None),
-        },
-    }
+                                         if cand_ratio.size else None)})
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks,
-                                           args.cpu_seconds)
+        if binlocal:
+            out["cpu_baseline"] = cpu_baseline_binlocal(
+                wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds,
+                args.bin_len, args.cap_den)
+        else:
+            out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks,
+                                               args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

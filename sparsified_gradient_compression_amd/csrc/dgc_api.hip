@@ -154,7 +154,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_gmap = take(size_t(p.G) * 4);
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
-    p.off_bltab = take(5 * T1 * sizeof(int64_t));
+    p.off_bltab = take(6 * T1 * sizeof(int64_t));
     // Everything above is written from the host (layout tables at init, k
     // tables per call); everything from here on is device scratch, zeroed
     // at init.
@@ -220,7 +220,7 @@ struct dgc_state {
     bool k_valid = false;
     int64_t KT = 0;  // tiles over k of the last upload
     std::vector<int64_t> bins_last;  // bin lengths of the last upload
-    std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap (host copy)
+    std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap, slbase (host copy)
     bool bins_valid = false;
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
     DevBins B{};
@@ -368,12 +368,13 @@ int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
         return DGC_OK;
     const size_t T1 = size_t(T) + 1;
     std::vector<int64_t>& tb = st->bl_tables;
-    tb.assign(5 * T1, 0);
+    tb.assign(6 * T1, 0);
     int64_t* plen = tb.data();
     int64_t* magic = plen + T1;
     int64_t* pbase = magic + T1;
     int64_t* gbase = pbase + T1;
     int64_t* pcap = gbase + T1;
+    int64_t* slb = pcap + T1;
     for (int32_t t = 0; t < T; ++t) {
         const int64_t Lb = bin_len[t], n = p.sizes[size_t(t)];
         plen[t] = Lb * (kMaxBin / Lb);
@@ -385,8 +386,11 @@ int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
         const int64_t np_ = cdiv(n, plen[t]);
         pbase[t + 1] = pbase[t] + np_;
         gbase[t + 1] = gbase[t] + cdiv(np_, kBlGroup);
-        // the tensor's candidate slots, shared out among its pieces
-        const int64_t region = p.slbase[size_t(t) + 1] - p.slbase[size_t(t)];
+        // the tensor's 8-byte candidate slots, taken as 16-byte slots
+        // {index, v, u, 0} and shared out among its pieces
+        slb[t] = (p.slbase[size_t(t)] + 1) / 2;
+        const int64_t region =
+            std::max<int64_t>(0, p.slbase[size_t(t) + 1] / 2 - slb[t]);
         pcap[t] = np_ ? std::min<int64_t>(plen[t], region / np_) : 0;
     }
     if (pbase[T] > p.BP || gbase[T] > p.BG) return DGC_EINVAL;
@@ -535,6 +539,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->B.pbase = bt + 2 * T1;
     st->B.gbase = bt + 3 * T1;
     st->B.pcap = bt + 4 * T1;
+    st->B.slbase = bt + 5 * T1;
     st->B.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_blpdesc);
     st->B.cnt = reinterpret_cast<uint32_t*>(ws + p.off_blcnt);
     st->B.pre = reinterpret_cast<uint32_t*>(ws + p.off_blpre);
@@ -712,7 +717,7 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_bl_fused<<<grid_for(wb, wb), kBlock, 0, stream>>>(
             g, st->u, st->v, st->L, st->K, st->B, st->sc, clip_on, st->m, pcap_limit,
-            st->slots, st->BP, out_norm, out_scale);
+            reinterpret_cast<uint4*>(st->slots), st->BP, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
@@ -722,10 +727,14 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
         k_bl_group<<<grid_for(gb, gb), kBlock, 0, stream>>>(st->L, st->B, st->BG);
     }
     k_bl_tscan<<<T, kBlock, 0, stream>>>(st->K, st->B, out_count, out_total);
-    if (st->BP > 0 && C > 0)
-        k_bl_gather<<<grid_for(wb, wb), kBlock, 0, stream>>>(
-            st->u, st->v, st->L, st->K, st->B, pcap_limit, st->slots, st->BP, out_idx,
-            out_val);
+    // also with every cap 0: entries masked in the element-wise pass that
+    // are not delivered get their u and v back here
+    if (st->BP > 0) {
+        const int64_t gb = cdiv(st->BP, int64_t(kBlock));  // kWave pieces per wave
+        k_bl_gather<<<grid_for(gb, gb), kBlock, 0, stream>>>(
+            st->u, st->v, st->L, st->K, st->B, pcap_limit,
+            reinterpret_cast<const uint4*>(st->slots), st->BP, out_idx, out_val);
+    }
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
     return DGC_OK;

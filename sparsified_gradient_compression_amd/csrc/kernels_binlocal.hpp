@@ -16,15 +16,16 @@
 // Pieces here are a whole number of bins (L * floor(1024 / L) elements), so
 // every threshold is known inside the wave that owns the piece:
 //   k_bl_fused   momentum update, per-bin maxima in the wave's LDS, salient
-//                flags, ranks by ballot; the piece's entries go to its own
-//                slots; u and v are masked in registers when the piece's
-//                entries are sure to fit below cap_t.
+//                flags, ranks by ballot; the piece's entries {index, v, u}
+//                go to its own slots and u, v are masked in registers.  A
+//                piece with more entries than slots keeps u, v unmasked.
 //   k_bl_group   per 1024-piece group: exclusive prefix of piece counts.
 //   k_bl_tscan   per tensor: group offsets, delivered and salient counts.
-//   k_bl_gather  per piece: slots -> (idx, val) at the final position, masks
-//                what k_bl_fused could not; a piece that overflowed its
-//                slots is re-derived from u and v (same arithmetic, same
-//                flags).
+//   k_bl_gather  64 pieces per wave: slots -> (idx, val) at their final
+//                positions; entries past the tensor's capacity get their u
+//                and v back from the slot (as if never masked); a piece that
+//                overflowed its slots is re-derived from u and v (same
+//                arithmetic, same flags) and its delivered entries masked.
 #pragma once
 
 #include "dgc_device.hpp"
@@ -42,6 +43,7 @@ struct DevBins {
     const int64_t* pbase;  // [T+1] first piece of each tensor
     const int64_t* gbase;  // [T+1] first prefix group of each tensor
     const int64_t* pcap;   // [T] slots per piece
+    const int64_t* slbase; // [T] first slot of each tensor (16-byte slots)
     PieceDesc* pdesc;      // [pieces]
     uint32_t* cnt;         // [pieces] salient entries of each piece
     uint32_t* pre;         // [pieces] exclusive prefix inside its group
@@ -173,19 +175,11 @@ __device__ __forceinline__ uint32_t bl_ranks(const bool (&f)[kRounds][4],
     return total;
 }
 
-// Whether k_bl_fused masks the piece itself: its entries fit its slots, and
-// even if every element before the piece were salient they would land
-// below the tensor's capacity.
-__device__ __forceinline__ bool bl_masks_early(uint32_t count, uint32_t pcap,
-                                               int64_t start_local, int64_t cap) {
-    return count <= pcap && start_local + int64_t(count) <= cap;
-}
-
 template <bool kAligned>
 __device__ __forceinline__ void bl_fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     int64_t e0, uint32_t len, int t, const DevLayout& L, const DevK& K,
-    const DevBins& B, float s, float m, uint32_t pcap_limit, uint2* __restrict__ slots,
+    const DevBins& B, float s, float m, uint32_t pcap_limit, uint4* __restrict__ slots,
     int64_t p, uint32_t* th) {
     const int lane = lane_id();
     const int64_t e1 = e0 + len;
@@ -222,23 +216,24 @@ __device__ __forceinline__ void bl_fused_piece(
     }
     const uint32_t magic = uint32_t(B.magic[t]);
     const int64_t o = L.o[t];
-    const int64_t cap = K.k[t];
     const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
     bool f[kRounds][4];
     uint32_t rank[kRounds][4];
     bl_flags<kAligned>(vn, un, len, magic, th, f);
     const uint32_t total = bl_ranks<kAligned>(f, rank);
-    const bool early = bl_masks_early(total, pcap, e0 - o, cap);
+    // the slots keep u and v as they were, so masking here can be undone
+    const bool early = total <= pcap;
     if (lane == 0) B.cnt[p] = total;
-    if (total && total <= pcap) {
-        uint2* sl = slots + L.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
+    if (total && early) {
+        uint4* sl = slots + B.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
 #pragma unroll
         for (int i = 0; i < kRounds; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (f[i][c])
-                    sl[rank[i][c]] = make_uint2(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
-                                                __float_as_uint(vn[i][c]));
+                    sl[rank[i][c]] = make_uint4(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
+                                                __float_as_uint(vn[i][c]),
+                                                __float_as_uint(un[i][c]), 0u);
     }
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
@@ -275,7 +270,7 @@ __device__ __forceinline__ void bl_fused_piece(
 __global__ __launch_bounds__(kBlock) void k_bl_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     DevLayout L, DevK K, DevBins B, Scalars* __restrict__ sc, int clip_on, float m,
-    uint32_t pcap_limit, uint2* __restrict__ slots, int64_t n_pieces,
+    uint32_t pcap_limit, uint4* __restrict__ slots, int64_t n_pieces,
     double* __restrict__ out_norm, float* __restrict__ out_scale) {
     __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
     const float s = clip_on ? sc->scale : 1.0f;
@@ -394,49 +389,102 @@ __device__ __forceinline__ void bl_redo_piece(
             }
 }
 
-// Final placement, one wave per piece (grid-stride).  Output of tensor t
-// starts at koff[t]; its piece p starts at goff[group] + pre[p].
+// Final placement, kWave pieces per wave.  Lane j first reads the fields of
+// piece q0 + j; then the wave copies the entries of all slot pieces as one
+// flat list (kUnroll entries per lane per round, so their loads overlap),
+// finding each entry's piece by a binary search over the lanes' prefix
+// sums; then it re-derives the overflowed pieces one after another.
+// Tensor t's output starts at koff[t]; piece p's entries at
+// goff[group of p] + pre[p] within it.
+constexpr int kGatherUnroll = 4;
+
 __global__ __launch_bounds__(kBlock) void k_bl_gather(
     float* __restrict__ u, float* __restrict__ v, DevLayout L, DevK K, DevBins B,
-    uint32_t pcap_limit, const uint2* __restrict__ slots, int64_t n_pieces,
+    uint32_t pcap_limit, const uint4* __restrict__ slots, int64_t n_pieces,
     uint32_t* __restrict__ out_idx, float* __restrict__ out_val) {
     __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
     const int lane = lane_id();
-    uint32_t* row = th[threadIdx.x >> 6];
-    const int64_t w0 = (int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6;
-    const int64_t nw = (int64_t(gridDim.x) * kBlock) >> 6;
-    for (int64_t p = w0; p < n_pieces; p += nw) {
-        const uint32_t count = B.cnt[p];
-        if (count == 0) continue;
-        const PieceDesc d = B.pdesc[p];
-        const int t = wave_uniform(int(d.tensor));
-        const int64_t o = L.o[t];
-        const int64_t cap = K.k[t];
+    const int64_t q0 = ((int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6) * kWave;
+    if (q0 >= n_pieces) return;  // no block-wide barrier follows
+    const int64_t p = q0 + lane;
+    const uint32_t count = p < n_pieces ? B.cnt[p] : 0u;
+    // per-piece fields (lane = piece)
+    int64_t sbase = 0, obase = 0, o = 0;
+    uint32_t nd = 0, work = 0;
+    bool redo = false;
+    if (count) {
+        const int t = int(B.pdesc[p].tensor);
         const int64_t jp = p - B.pbase[t];
         const int64_t pos0 = int64_t(B.goff[B.gbase[t] + jp / kBlGroup]) + B.pre[p];
-        if (pos0 >= cap) continue;
-        const int64_t nd = min(int64_t(count), cap - pos0);
+        const int64_t cap = K.k[t];
         const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
-        const int64_t obase = K.koff[t];
+        nd = uint32_t(max(int64_t(0), min(int64_t(count), cap - pos0)));
+        obase = K.koff[t] + pos0;
+        o = L.o[t];
         if (count <= pcap) {
-            const bool early = bl_masks_early(count, pcap, d.start - o, cap);
-            const uint2* sl = slots + L.slbase[t] + jp * int64_t(pcap);
-            for (int64_t r = lane; r < nd; r += kWave) {
-                const uint2 x = sl[r];
-                out_idx[obase + pos0 + r] = x.x;
-                out_val[obase + pos0 + r] = __uint_as_float(x.y);
-                if (!early) {
-                    u[o + x.x] = 0.0f;
-                    v[o + x.x] = 0.0f;
-                }
-            }
-        } else if ((d.start & 3) == 0) {
-            bl_redo_piece<true>(u, v, d.start, d.len, uint32_t(B.magic[t]), o, pos0, nd,
-                                obase, out_idx, out_val, row);
+            sbase = B.slbase[t] + jp * int64_t(pcap);
+            work = count;
         } else {
-            bl_redo_piece<false>(u, v, d.start, d.len, uint32_t(B.magic[t]), o, pos0, nd,
-                                 obase, out_idx, out_val, row);
+            redo = nd > 0;
         }
+    }
+    // slot pieces: deliver the first nd entries, give the rest their u, v back
+    const uint32_t inc = wave_inclusive_scan(work);
+    const uint32_t excl = inc - work;
+    const uint32_t all = uint32_t(__shfl(int(inc), kWave - 1, kWave));
+    for (uint32_t base = 0; base < all; base += kWave * kGatherUnroll) {
+        uint4 x[kGatherUnroll];
+        uint32_t r[kGatherUnroll];
+        int src[kGatherUnroll];
+#pragma unroll
+        for (int q = 0; q < kGatherUnroll; ++q) {
+            const uint32_t e = base + q * kWave + lane;
+            // largest lane j with excl[j] <= e (a lane with work > 0)
+            int j = 0;
+#pragma unroll
+            for (int step = kWave / 2; step >= 1; step >>= 1) {
+                const uint32_t pv = uint32_t(__shfl(int(excl), j + step, kWave));
+                if (pv <= e) j += step;
+            }
+            src[q] = j;
+            r[q] = e - uint32_t(__shfl(int(excl), j, kWave));
+            const int64_t sb = __shfl(sbase, j, kWave);
+            if (e < all) x[q] = slots[sb + r[q]];
+        }
+#pragma unroll
+        for (int q = 0; q < kGatherUnroll; ++q) {
+            const uint32_t e = base + q * kWave + lane;
+            const int j = src[q];
+            const uint32_t ndj = uint32_t(__shfl(int(nd), j, kWave));
+            const int64_t ob = __shfl(obase, j, kWave);
+            const int64_t oj = __shfl(o, j, kWave);
+            if (e >= all) continue;
+            if (r[q] < ndj) {
+                out_idx[ob + r[q]] = x[q].x;
+                out_val[ob + r[q]] = __uint_as_float(x[q].y);
+            } else {
+                v[oj + x[q].x] = __uint_as_float(x[q].y);
+                u[oj + x[q].x] = __uint_as_float(x[q].z);
+            }
+        }
+    }
+    // overflowed pieces
+    uint64_t todo = __ballot(redo);
+    uint32_t* row = th[threadIdx.x >> 6];
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const PieceDesc d = B.pdesc[q0 + j];
+        const int t = wave_uniform(int(d.tensor));
+        const int64_t ob = __shfl(obase, j, kWave);
+        const int64_t ndj = int64_t(uint32_t(__shfl(int(nd), j, kWave)));
+        const int64_t oj = L.o[t];
+        if ((d.start & 3) == 0)
+            bl_redo_piece<true>(u, v, d.start, d.len, uint32_t(B.magic[t]), oj, 0, ndj, ob,
+                                out_idx, out_val, row);
+        else
+            bl_redo_piece<false>(u, v, d.start, d.len, uint32_t(B.magic[t]), oj, 0, ndj, ob,
+                                 out_idx, out_val, row);
     }
 }
 

@@ -173,14 +173,16 @@ def test_flat1b_shape_scaled_four_learners():
 @pytest.mark.parametrize("path", [0, 1])
 def test_truncation_keeps_the_rest_in_the_residual(path):
     """Capacities well below the salient count: the first cap entries in
-    index order leave, the rest stay unmasked; three steps so the residual
-    grows; k_max = n keeps the slots large (masking happens in the
-    placement pass for pieces past the capacity)."""
+    index order leave, the rest stay unmasked; four steps so the residual
+    grows; k_max = n keeps the slots large, so entries past the capacity
+    are masked in the element-wise pass and restored from their slots."""
     rng = np.random.default_rng(61)
     sizes = [300001, 70000, 4099]
     n = sum(sizes)
-    caps = [[3000, 700, 41], [100, 0, 4099], [300001, 7, 1]]
-    grads = [rng.laplace(0, 1e-2, n).astype(np.float32) for _ in range(3)]
+    # the all-zero step delivers nothing: every entry masked in the
+    # element-wise pass must get its u and v back
+    caps = [[3000, 700, 41], [0, 0, 0], [100, 0, 4099], [300001, 7, 1]]
+    grads = [rng.laplace(0, 1e-2, n).astype(np.float32) for _ in range(4)]
     run(sizes, [128, 1000, 7], caps, lambda w, s: grads[s], 0.5, path=path,
         tag=f"trunc p{path}")
 
