@@ -28,4 +28,7 @@ from .c_oracle import (  # noqa: F401
     num_threads,
     binlocal_select_mask,
     binlocal_step,
+    fmix32,
+    sampled_select_mask,
+    sampled_step,
 )

@@ -68,6 +68,15 @@ def load():
                                       ctypes.c_float, ctypes.c_double, P, P,
                                       P, P, P, P]
     lib.orc_binlocal_step.restype = ctypes.c_int
+    lib.orc_fmix32.argtypes = [ctypes.c_uint32]
+    lib.orc_fmix32.restype = ctypes.c_uint32
+    lib.orc_sampled_select_mask.argtypes = [P, P, i64, i64, i64, ctypes.c_int32,
+                                            P, P, P, P]
+    lib.orc_sampled_select_mask.restype = i64
+    lib.orc_sampled_step.argtypes = [ctypes.c_int32, P, P, P, P, P, P,
+                                     ctypes.c_float, ctypes.c_double, P, P, P,
+                                     P, P, P, P]
+    lib.orc_sampled_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -213,3 +222,53 @@ def binlocal_step(sizes, L, cap, g, u, v, m, clip):
     if rc != 0:
         raise ValueError("bad bin length or capacity")
     return idx[:C], val[:C], count, total, float(norm[0]), np.float32(scale[0])
+
+
+def fmix32(h):
+    """MurmurHash3's 32-bit finalizer, as the oracle computes it."""
+    return int(load().orc_fmix32(int(h) & 0xFFFFFFFF))
+
+
+def sampled_select_mask(u, v, k, t=0, cap=None):
+    """Sampled-threshold selection of one tensor (index t of its layout) +
+    masking, in place.  Returns (idx, val, total, theta)."""
+    assert u.size == v.size
+    cap = v.size if cap is None else int(cap)
+    idx = np.zeros(max(cap, 1), np.uint32)
+    val = np.zeros(max(cap, 1), np.float32)
+    total = np.zeros(1, np.int64)
+    theta = np.zeros(1, np.uint32)
+    got = load().orc_sampled_select_mask(
+        _ptr(u, np.float32), _ptr(v, np.float32), v.size, int(k), cap, int(t),
+        _ptr(idx, np.uint32), _ptr(val, np.float32), _ptr(total, np.int64),
+        _ptr(theta, np.uint32))
+    if got < 0:
+        raise ValueError("bad k or capacity")
+    return idx[:got].copy(), val[:got].copy(), int(total[0]), int(theta[0])
+
+
+def sampled_step(sizes, k, cap, g, u, v, m, clip):
+    """One learner step with the sampled-threshold selector (in place on u,
+    v).  Returns (idx, val, count, total, theta, norm, scale); idx/val have
+    sum(cap) slots, tensor t's delivered entries at offset sum(cap[:t])."""
+    sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+    k = np.ascontiguousarray(k, dtype=np.int64)
+    cap = np.ascontiguousarray(cap, dtype=np.int64)
+    C = int(cap.sum())
+    idx = np.zeros(max(C, 1), np.uint32)
+    val = np.zeros(max(C, 1), np.float32)
+    T = len(sizes)
+    count = np.zeros(T, np.int64)
+    total = np.zeros(T, np.int64)
+    theta = np.zeros(T, np.uint32)
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    rc = load().orc_sampled_step(
+        T, _ptr(sizes, np.int64), _ptr(k, np.int64), _ptr(cap, np.int64),
+        _ptr(g, np.float32), _ptr(u, np.float32), _ptr(v, np.float32),
+        float(np.float32(m)), float(clip), _ptr(idx, np.uint32),
+        _ptr(val, np.float32), _ptr(count, np.int64), _ptr(total, np.int64),
+        _ptr(theta, np.uint32), _ptr(norm, np.float64), _ptr(scale, np.float32))
+    if rc != 0:
+        raise ValueError("bad k or capacity")
+    return idx[:C], val[:C], count, total, theta, float(norm[0]), np.float32(scale[0])

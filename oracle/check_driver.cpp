@@ -33,6 +33,13 @@ int orc_binlocal_step(int32_t T, const int64_t* sizes, const int64_t* L, const i
                       const float* g, float* u, float* v, float m, double clip,
                       uint32_t* idx, float* val, int64_t* count, int64_t* total,
                       double* norm, float* scale);
+int64_t orc_sampled_select_mask(float* u, float* v, int64_t n, int64_t k, int64_t cap,
+                                int32_t t, uint32_t* idx, float* val, int64_t* total,
+                                uint32_t* theta);
+int orc_sampled_step(int32_t T, const int64_t* sizes, const int64_t* k, const int64_t* cap,
+                     const float* g, float* u, float* v, float m, double clip,
+                     uint32_t* idx, float* val, int64_t* count, int64_t* total,
+                     uint32_t* theta, double* norm, float* scale);
 }
 
 #define CHECK(c)                                                        \
@@ -167,6 +174,43 @@ int main() {
         CHECK(orc_binlocal_select_mask(z, z, 3, 0, 3, i3, v3, &tot) == -1);
         CHECK(orc_binlocal_select_mask(z, z, 3, 1, -1, i3, v3, &tot) == -1);
         CHECK(orc_binlocal_select_mask(z, z, 3, 2, 3, i3, v3, &tot) == 0 && tot == 0);
+    }
+    // sampled-threshold selector: whole-tensor and line samples, any k and cap
+    for (int round = 0; round < 30; ++round) {
+        int T = 1 + int(rng() % 4);
+        std::vector<int64_t> sizes(T), k(T), cap(T), count(T), total(T);
+        std::vector<uint32_t> theta(T);
+        int64_t n = 0, C = 0;
+        for (int t = 0; t < T; ++t) {
+            sizes[t] = sizes_pool[rng() % 10];
+            k[t] = sizes[t] ? int64_t(rng() % (sizes[t] + 1)) : 0;
+            cap[t] = (rng() % 2) ? sizes[t] : int64_t(rng() % (sizes[t] / 4 + 2));
+            n += sizes[t];
+            C += cap[t];
+        }
+        std::vector<float> g(n), u(n), v(n);
+        std::normal_distribution<float> nd(0.f, 1e-2f);
+        for (int64_t i = 0; i < n; ++i) {
+            g[i] = (rng() % 10 == 0) ? 0.f : nd(rng);
+            u[i] = nd(rng) * 0.1f;
+            v[i] = nd(rng) * 0.1f;
+        }
+        std::vector<uint32_t> idx(C + 1);
+        std::vector<float> val(C + 1);
+        double norm;
+        float s;
+        CHECK(orc_sampled_step(T, sizes.data(), k.data(), cap.data(), g.data(), u.data(),
+                               v.data(), 0.9f, 0.5, idx.data(), val.data(), count.data(),
+                               total.data(), theta.data(), &norm, &s) == 0);
+        int64_t coff = 0;
+        for (int t = 0; t < T; ++t) {
+            CHECK(count[t] == std::min(total[t], cap[t]));
+            CHECK(k[t] > 0 || (total[t] == 0 && theta[t] == 0xFFFFFFFFu));
+            for (int64_t j = 1; j < count[t]; ++j) CHECK(idx[coff + j - 1] < idx[coff + j]);
+            for (int64_t j = 0; j < count[t]; ++j)
+                CHECK((bits(val[coff + j]) & 0x7FFFFFFFu) >= theta[t]);
+            coff += cap[t];
+        }
     }
     // a corrupt stream is refused without touching memory past the end
     std::vector<uint16_t> runs = {3, 4, 60000};

@@ -220,6 +220,90 @@ int64_t orc_binlocal_select_mask(float* u, float* v, int64_t n, int64_t L,
 }
 
 /*
+ * MurmurHash3's 32-bit finalizer (fmix32), from its published definition
+ * (Austin Appleby, public domain): the counter-based generator that places
+ * the sampled lines below.
+ */
+static uint32_t fmix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+extern "C" uint32_t orc_fmix32(uint32_t h) { return fmix32(h); }
+
+/*
+ * Sampled-threshold selection of one tensor (tensor index t in its layout),
+ * then momentum factor masking.
+ *
+ * Source: the DGC review, "Research questions" (RQ4: hierarchical
+ * thresholding as a runtime strategy for scalable selection) and "Proposed
+ * method" (only large entries are sent).  The page gives no algorithm; the
+ * reading taken is the plainest sampled threshold:
+ *   sample   the tensor's 32-element lines: all of them if n <= 65536, else
+ *            ls = min(lines, max(512, lines / 256)) lines, line j (0 <= j <
+ *            ls) being j*stride + fmix32(j*0x9E3779B9 ^ t*0x7F4A7C15) mod
+ *            stride, stride = lines / ls (32-bit wrapping products); the
+ *            sample is the keys of every element of those lines inside the
+ *            tensor, S of them
+ *   threshold  theta = the J-th largest sampled key, J = ceil(S*k/n): the
+ *            sample's estimate of the k-th largest key
+ *   sent     key(v_i) >= theta and v_i != 0, in index order, at most cap of
+ *            them delivered and masked (u = v = +0.0f); the rest untouched
+ * with key(x) = bits(x) & 0x7FFFFFFF.  k = 0 sends nothing.
+ *
+ * Writes the delivered indices / values (v before masking), the number of
+ * entries at or above the threshold into *total and the threshold into
+ * *theta (0xFFFFFFFF for k = 0).  Returns the number delivered, or -1 for a
+ * k outside [0, n] or a negative cap.
+ */
+int64_t orc_sampled_select_mask(float* u, float* v, int64_t n, int64_t k,
+                                int64_t cap, int32_t t, uint32_t* idx,
+                                float* val, int64_t* total, uint32_t* theta) {
+    if (k < 0 || k > n || cap < 0) return -1;
+    *total = 0;
+    *theta = 0xFFFFFFFFu;
+    if (k == 0) return 0;
+    const int64_t lines = (n + 31) / 32;
+    const int64_t ls = n <= 65536 ? lines
+                                  : std::min<int64_t>(lines, std::max<int64_t>(512, lines / 256));
+    const int64_t stride = lines / ls;
+    std::vector<uint32_t> sample;
+    for (int64_t j = 0; j < ls; ++j) {
+        const uint32_t r = fmix32((uint32_t)j * 0x9E3779B9u ^ (uint32_t)t * 0x7F4A7C15u);
+        const int64_t line = j * stride + (int64_t)(r % (uint64_t)stride);
+        for (int64_t e = line * 32; e < std::min(n, line * 32 + 32); ++e)
+            sample.push_back(magnitude_key(v[e]));
+    }
+    const int64_t S = (int64_t)sample.size();
+    const int64_t J = (S * k + n - 1) / n;
+    std::nth_element(sample.begin(), sample.begin() + (J - 1), sample.end(),
+                     [](uint32_t a, uint32_t b) { return a > b; });
+    const uint32_t th = sample[(size_t)(J - 1)];
+    *theta = th;
+    int64_t sent = 0, out = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t key = magnitude_key(v[i]);
+        if (key == 0 || key < th) continue;
+        ++sent;
+        if (out < cap) {
+            idx[out] = (uint32_t)i;
+            val[out] = v[i];
+            ++out;
+        }
+    }
+    for (int64_t j = 0; j < out; ++j) {
+        u[idx[j]] = 0.0f;
+        v[idx[j]] = 0.0f;
+    }
+    *total = sent;
+    return out;
+}
+
+/*
  * Zero-run encoding of one tensor's sparse gradient (DGC review, "Proposed
  * method": each sent value takes 32 bits and is preceded by the 16-bit
  * length of the zero run before it).  A gap longer than a 16-bit run can say
@@ -334,6 +418,37 @@ int orc_binlocal_step(int32_t T, const int64_t* sizes, const int64_t* L,
         count[t] = orc_binlocal_select_mask(
             u + off[(size_t)t], v + off[(size_t)t], sizes[t], L[t], cap[t],
             idx + coff[(size_t)t], val + coff[(size_t)t], total + t);
+    }
+    return 0;
+}
+
+/*
+ * One learner step with the sampled-threshold selector: clip and momentum as
+ * in orc_step, then per tensor orc_sampled_select_mask with target k[t] and
+ * capacity cap[t] (outputs at offset cap[0] + ... + cap[t-1]); count[t]
+ * delivered, total[t] at or above the threshold, theta[t] the threshold.
+ * Returns 0, or -1 on a bad k or cap.
+ */
+int orc_sampled_step(int32_t T, const int64_t* sizes, const int64_t* k,
+                     const int64_t* cap, const float* g, float* u, float* v,
+                     float m, double clip, uint32_t* idx, float* val,
+                     int64_t* count, int64_t* total, uint32_t* theta,
+                     double* norm_out, float* scale_out) {
+    int64_t n = 0;
+    for (int32_t t = 0; t < T; ++t) n += sizes[t];
+    std::vector<int64_t> off((size_t)T + 1, 0), coff((size_t)T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        if (k[t] < 0 || k[t] > sizes[t] || cap[t] < 0) return -1;
+        off[(size_t)t + 1] = off[(size_t)t] + sizes[t];
+        coff[(size_t)t + 1] = coff[(size_t)t] + cap[t];
+    }
+    orc_clip_scale(g, n, clip, norm_out, scale_out);
+    orc_momentum(g, n, *scale_out, m, u, v);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        count[t] = orc_sampled_select_mask(
+            u + off[(size_t)t], v + off[(size_t)t], sizes[t], k[t], cap[t], t,
+            idx + coff[(size_t)t], val + coff[(size_t)t], total + t, theta + t);
     }
     return 0;
 }
