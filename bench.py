@@ -15,9 +15,12 @@ timed on a bounded sample of the same workload.
 With --selector binlocal the step uses AdaComp's bin-local selector instead
 of exact top-k (dgc_compress_binlocal + dgc_encode_counts, bins of
 --bin-len entries, at most n_t / --cap-den entries delivered per tensor).
+With --selector sampled it uses the sampled (approximate) threshold for the
+same k as top-k (dgc_compress_sampled + dgc_encode_counts, at most 4 k per
+tensor delivered) and reports how far the sent counts are from k.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat1b]
-                    [--selector topk|binlocal] [--bin-len 512] [--cap-den 8]
+                    [--selector topk|binlocal|sampled] [--bin-len 512] [--cap-den 8]
 """
 
 import argparse
@@ -40,6 +43,8 @@ TRAFFIC = {
              ("dgc_device.hpp", "kernel_fused.hpp")),
     "binlocal": (os.path.join(ROOT, "profiles", "bl_fused_flat1b_traffic.json"),
                  ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
+    "sampled": (os.path.join(ROOT, "profiles", "sm_fused_flat1b_traffic.json"),
+                ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
 }
 
 
@@ -91,8 +96,9 @@ def parse():
                          "previous learner's element-wise pass is done")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
-    ap.add_argument("--selector", choices=("topk", "binlocal"), default="topk",
-                    help="exact per-tensor top-k (DGC) or AdaComp's bin-local rule")
+    ap.add_argument("--selector", choices=("topk", "binlocal", "sampled"), default="topk",
+                    help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, or "
+                         "the sampled threshold")
     ap.add_argument("--bin-len", type=int, default=512,
                     help="bin length for --selector binlocal (1..1024)")
     ap.add_argument("--cap-den", type=int, default=8,
@@ -137,6 +143,46 @@ def cpu_baseline_binlocal(wl, host_samples, n_chunks, seconds, bin_len, cap_den)
                    f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
                    f"momentum, bin-local select (bins of {bin_len}), mask, encode, "
                    f"decode; {dt:.1f} s"),
+    }
+
+
+def cpu_baseline_sampled(wl, host_samples, n_chunks, seconds):
+    """As cpu_baseline, with the oracle's sampled-threshold selector."""
+    import oracle
+    sizes = np.array(wl.sizes[:n_chunks], np.int64)
+    d = wl.densities[0]
+    k = np.array([oracle.k_for_density(int(s), d.numerator, d.denominator) for s in sizes])
+    caps = 4 * k
+    n = int(sizes.sum())
+    u = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dense = np.zeros(n, np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    coff = np.concatenate([[0], np.cumsum(caps)])
+    t0 = time.perf_counter()
+    steps = 0
+    for cycle in range(4):
+        for g in host_samples:
+            idx, val, cnt, _, _, _, _ = oracle.sampled_step(sizes, k, caps, g, u, v,
+                                                            wl.momentum, wl.clip)
+            dense[:] = 0
+            for t in range(len(sizes)):
+                a = coff[t]
+                r, vv = oracle.encode(idx[a:a + cnt[t]], val[a:a + cnt[t]])
+                oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * steps / dt / 1e9, 4),
+        "unit": "G elem/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"learner 0, {steps} steps, first {n_chunks} of "
+                   f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
+                   "momentum, sampled threshold, mask, encode, decode; "
+                   f"{dt:.1f} s"),
     }
 
 
@@ -196,13 +242,19 @@ def main():
     wl = W.get(args.workload)
     T = len(wl.sizes)
     binlocal = args.selector == "binlocal"
+    sampled = args.selector == "sampled"
     if binlocal:
         bins = [args.bin_len] * T
         caps = [s // args.cap_den for s in wl.sizes]
         ks = [caps]  # the delivery capacity takes k's place in the layout
+        kmax = caps
     else:
         ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
-    kmax = [max(k[t] for k in ks) for t in range(T)]
+        kmax = [max(k[t] for k in ks) for t in range(T)]
+        if sampled:
+            # deliver at most 4 k per tensor, following each step's k
+            caps_by_step = [[min(s, 4 * kk) for s, kk in zip(wl.sizes, k)] for k in ks]
+            kmax = [max(c[t] for c in caps_by_step) for t in range(T)]
     n = wl.n
 
     # ---- inputs: every (learner, step) gradient resident in HBM
@@ -226,7 +278,7 @@ def main():
         L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
     dense = torch.zeros(n, dtype=torch.float32, device="cuda")
     main = torch.cuda.current_stream()
-    pipeline = args.pipeline and not binlocal
+    pipeline = args.pipeline and not (binlocal or sampled)
     if pipeline:
         # One stream per learner.  Learner w+1 starts once learner w's
         # element-wise pass is done (event recorded by the library), so its
@@ -241,11 +293,15 @@ def main():
     def one_step(s):
         t = s % gsteps
         k = ks[t % len(ks)]
-        if binlocal:
+        if binlocal or sampled:
+            step_caps = caps if binlocal else caps_by_step[t % len(ks)]
             for w, L in enumerate(learners):
-                L.compress_binlocal(grads[(w, t)], bins, caps, wl.clip)
+                if binlocal:
+                    L.compress_binlocal(grads[(w, t)], bins, step_caps, wl.clip)
+                else:
+                    L.compress_sampled(grads[(w, t)], k, step_caps, wl.clip)
                 if not args.fused_only:
-                    L.encode_counts(caps)
+                    L.encode_counts(step_caps)
             if not args.fused_only:
                 dense.zero_()
                 dgc.decode_accumulate(learners[0],
@@ -324,7 +380,7 @@ def main():
     fused_ms = times["fused"][0] / max(times["fused"][1], 1)
     compress_ms = times["compress"][0] / max(times["compress"][1], 1)
     clip = 1 if wl.clip > 0 else 0
-    if binlocal:
+    if binlocal or sampled:
         # the last step's salient and delivered counts, all learners
         salient = int(sum(int(L.total.sum()) for L in learners)) // len(learners)
         delivered = int(sum(int(L.count.sum()) for L in learners)) // len(learners)
@@ -334,7 +390,8 @@ def main():
         # + norm re-read; + slot read, output write and u/v masking per entry
         pipeline_bytes = n * (20 + 4 * clip) + 8 * salient + 16 * delivered
         kernel_name = ("k_bl_fused (clip-scale + momentum correction + accumulation + "
-                       "per-bin maxima + salient entries to slots)")
+                       + ("per-bin maxima + salient entries to slots)" if binlocal else
+                          "entries at or above the sampled threshold to slots)"))
     else:
         fused_bytes = 20 * n  # read g, u, v; write u, v
         k_total = sum(ks[0])
@@ -389,9 +446,20 @@ def main():
         },
     }
     det = out["detail"]
-    if binlocal:
-        out["config"].update({"bin_len": args.bin_len,
-                              "cap_per_tensor": f"n_t // {args.cap_den}"})
+    if binlocal or sampled:
+        if binlocal:
+            out["config"].update({"bin_len": args.bin_len,
+                                  "cap_per_tensor": f"n_t // {args.cap_den}"})
+        else:
+            klast = np.array(ks[(args.warmup + args.steps - 1) % gsteps % len(ks)])
+            ratio = np.concatenate([L.total.cpu().numpy() / np.maximum(klast, 1)
+                                    for L in learners])
+            out["config"].update({"k_per_tensor": int(klast[0]) if len(set(klast)) == 1
+                                  else "per tensor", "density": str(wl.densities[0]),
+                                  "cap_per_tensor": "4 k"})
+            det["sent_over_k_min_mean_max"] = [round(float(ratio.min()), 4),
+                                               round(float(ratio.mean()), 4),
+                                               round(float(ratio.max()), 4)]
         det.update({"salient_per_learner": salient,
                     "salient_fraction": round(salient / n, 5),
                     "delivered_per_learner": delivered,
@@ -419,6 +487,9 @@ def main():
             out["cpu_baseline"] = cpu_baseline_binlocal(
                 wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds,
                 args.bin_len, args.cap_den)
+        elif sampled:
+            out["cpu_baseline"] = cpu_baseline_sampled(
+                wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks,
                                                args.cpu_seconds)

@@ -59,17 +59,18 @@ extern "C" {
 /* Options for dgc_set_option. */
 #define DGC_OPT_SELECT_PATH 1   /* value 0: automatic (default); 1: always the
                                    dense exact path (no sample window); for
-                                   dgc_compress_binlocal, every piece's
-                                   entries re-derived in the placement pass
-                                   (no slots) -- the same results, slower */
+                                   dgc_compress_binlocal and
+                                   dgc_compress_sampled, every piece's entries
+                                   re-derived in the placement pass (no
+                                   slots) -- the same results, slower */
 #define DGC_OPT_KERNEL_TIMING 2 /* value 1: bracket the work of each call with
                                    HIP events on the call's stream (read with
                                    dgc_get_kernel_time); 0: off (default) */
 
 /* Timers for dgc_get_kernel_time. */
-#define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress or
-                                 dgc_compress_binlocal */
-#define DGC_TIMER_COMPRESS 1  /* all of dgc_compress / dgc_compress_binlocal */
+#define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress,
+                                 dgc_compress_binlocal or dgc_compress_sampled */
+#define DGC_TIMER_COMPRESS 1  /* all of one of those calls */
 #define DGC_TIMER_ENCODE 2    /* all of dgc_encode / dgc_encode_counts */
 #define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate */
 
@@ -178,6 +179,37 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
                           double* out_norm, float* out_scale, hipStream_t stream);
 
 /*
+ * One compression step with an approximate, sampled threshold in place of
+ * exact top-k (DGC review, "Research questions": hierarchical thresholding
+ * as a runtime strategy for scalable selection).  Steps 1, 2 and 4 are
+ * dgc_compress's; step 3 becomes:
+ *   3''. per tensor t, a sample of whole 32-element lines of v: every line
+ *        when n_t <= 65536, else ls = min(lines, max(512, lines / 256))
+ *        lines, line j (0 <= j < ls) at j*stride + fmix32(j*0x9E3779B9 ^
+ *        t*0x7F4A7C15) mod stride with stride = lines / ls (32-bit wrapping
+ *        products; fmix32 is MurmurHash3's finalizer); S sampled entries;
+ *        theta_t = the J-th largest sampled |v|, J = ceil(S * k[t] / n_t);
+ *        every entry with v_i != 0 and |v_i| >= theta_t is sent
+ * so about k[t] entries leave, not exactly k[t].  The first cap[t] of them
+ * in index order are written out and masked; the rest stay in the residual.
+ * k[t] = 0 sends nothing.  One pass over g, u, v: no exact-select re-read.
+ * Arguments:
+ *   k          host int64[T], 0 <= k[t] <= n_t: the target count
+ *   cap        host int64[T], 0 <= cap[t] <= k_max[t]: most entries to
+ *              deliver; outputs at offset C_t = cap[0] + ... + cap[t-1]
+ *   g, clip, out_idx, out_val, out_count, out_total, out_norm, out_scale
+ *              as for dgc_compress_binlocal (out_total: entries at or above
+ *              the threshold, delivered or not)
+ * dgc_get_select_info then reports path 3, theta in [1] and [4], S in [2]
+ * and J in [5].  Deterministic; encode with dgc_encode_counts.  Returns
+ * DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
+                         const int64_t* cap, double clip, uint32_t* out_idx,
+                         float* out_val, int64_t* out_count, int64_t* out_total,
+                         double* out_norm, float* out_scale, hipStream_t stream);
+
+/*
  * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is
  * the first entry slot of tensor t; tensor t may use up to
  * cap_offsets[t+1] - cap_offsets[t] = k_max[t] + floor(n_t / 65536) entries,
@@ -259,9 +291,13 @@ int dgc_get_status(dgc_state* st);
 int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense);
 
 /*
- * Per-tensor record of the last dgc_compress (waits for the stream):
+ * Per-tensor record of the last dgc_compress or dgc_compress_sampled (waits
+ * for the stream):
  * info (host int64[6 * n_tensors]) receives for each tensor
- *   [0] path: 0 = k was 0, 1 = sample window, 2 = dense exact path
+ *   [0] path: 0 = k was 0, 1 = sample window, 2 = dense exact path,
+ *       3 = the sampled threshold of dgc_compress_sampled (then [1] and [4]
+ *       hold the threshold, [2] the sample size and [5] the rank J; the
+ *       other fields below describe dgc_compress)
  *   [1] candidate threshold key of the sample window (0xFFFFFFFF = none)
  *   [2] candidates the element-wise pass found
  *   [3] 1 if a piece found more candidates than its slots hold

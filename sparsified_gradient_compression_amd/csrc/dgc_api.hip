@@ -15,6 +15,7 @@
 #include "kernels_binlocal.hpp"
 #include "kernels_codec.hpp"
 #include "kernels_compress.hpp"
+#include "kernels_sampled.hpp"
 
 using namespace dgc;
 
@@ -36,6 +37,11 @@ struct Plan {
         slbase, pcap, gbase;
     std::vector<PieceDesc> pdesc;
     std::vector<uint32_t> smap, emap, gmap;
+    // sampled threshold: lines sampled per tensor (every line of a small
+    // tensor), their sample blocks, and the tensor of each block
+    std::vector<int64_t> aslines, asbase;
+    std::vector<uint32_t> asmap;
+    int64_t AS = 0;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
@@ -48,7 +54,7 @@ struct Plan {
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
-           off_blgoff = 0, total = 0;
+           off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, total = 0;
 };
 
 // Candidate slots per 1024-element piece: none for small tensors (they take
@@ -93,6 +99,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.slines.assign(T + 1, 0);
     p.ebase.assign(T + 1, 0);
     p.etbase.assign(T + 1, 0);
+    p.aslines.assign(T + 1, 0);
+    p.asbase.assign(T + 1, 0);
     for (int32_t t = 0; t < T; ++t) {
         int64_t n = sizes[t], km = kmax[t];
         if (n < 0 || n >= (int64_t(1) << 32) || km < 0 || km > n) return DGC_EINVAL;
@@ -108,6 +116,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
         p.ebase[t + 1] = p.ebase[t] + km + n / 65536;
         p.etbase[t + 1] = p.etbase[t] + cdiv(km + n / 65536, kTile);
+        p.aslines[t] = n <= kSmallN ? cdiv(n, kLine) : p.slines[t];
+        p.asbase[t + 1] = p.asbase[t] + cdiv(p.aslines[t], kLinesPerSampleBlock);
         p.BP += cdiv(n, kBlMinPiece);
         p.BG += cdiv(cdiv(n, kBlMinPiece), kBlGroup);
     }
@@ -121,6 +131,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.E = p.ebase[T];
     p.ET = p.etbase[T];
     p.NB = cdiv(p.n, kNormChunk);
+    p.AS = p.asbase[T];
     if (p.P >= (int64_t(1) << 32) || p.TT >= (int64_t(1) << 32)) return DGC_EINVAL;
     // tiles over k never exceed tiles over n, so TT also bounds encode tiles
     p.tiles = std::max<int64_t>(std::max<int64_t>(p.TT, p.ET), 1);
@@ -139,6 +150,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         for (int64_t i = p.etbase[t]; i < p.etbase[t + 1]; ++i) p.emap[size_t(i)] = uint32_t(t);
         for (int64_t i = p.gbase[t]; i < p.gbase[t + 1]; ++i) p.gmap[size_t(i)] = uint32_t(t);
     }
+    p.asmap.resize(size_t(p.AS));
+    for (int32_t t = 0; t < T; ++t)
+        for (int64_t i = p.asbase[t]; i < p.asbase[t + 1]; ++i) p.asmap[size_t(i)] = uint32_t(t);
     // carve
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -155,6 +169,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
     p.off_bltab = take(6 * T1 * sizeof(int64_t));
+    p.off_astab = take(2 * T1 * sizeof(int64_t));
+    p.off_asmap = take(size_t(p.AS) * 4);
+    p.off_ktgt = take(T1 * sizeof(int64_t));
     // Everything above is written from the host (layout tables at init, k
     // tables per call); everything from here on is device scratch, zeroed
     // at init.
@@ -222,6 +239,10 @@ struct dgc_state {
     std::vector<int64_t> bins_last;  // bin lengths of the last upload
     std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap, slbase (host copy)
     bool bins_valid = false;
+    std::vector<int64_t> ktgt_last;  // target k of the last sampled call
+    bool ktgt_valid = false;
+    std::vector<int64_t> bins_full;  // one 1024-element bin per piece
+    DevSample A{};
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
     DevBins B{};
     // device views
@@ -540,6 +561,11 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->B.gbase = bt + 3 * T1;
     st->B.pcap = bt + 4 * T1;
     st->B.slbase = bt + 5 * T1;
+    int64_t* at = reinterpret_cast<int64_t*>(ws + p.off_astab);
+    st->A.slines = at;
+    st->A.sbase = at + T1;
+    st->A.smap = reinterpret_cast<uint32_t*>(ws + p.off_asmap);
+    st->bins_full.assign(size_t(T), kMaxBin);
     st->B.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_blpdesc);
     st->B.cnt = reinterpret_cast<uint32_t*>(ws + p.off_blcnt);
     st->B.pre = reinterpret_cast<uint32_t*>(ws + p.off_blpre);
@@ -550,7 +576,9 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     if (p.off_pdesc >= p.off_scratch || p.off_smap >= p.off_scratch ||
         p.off_emap >= p.off_scratch || p.off_gmap >= p.off_scratch ||
         p.off_k >= p.off_scratch || p.off_kmap >= p.off_scratch ||
-        p.off_tab >= p.off_scratch || p.off_bltab >= p.off_scratch) {
+        p.off_tab >= p.off_scratch || p.off_bltab >= p.off_scratch ||
+        p.off_astab >= p.off_scratch || p.off_asmap >= p.off_scratch ||
+        p.off_ktgt >= p.off_scratch) {
         delete st;
         return DGC_EINVAL;
     }
@@ -566,6 +594,13 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
                                         hipMemcpyHostToDevice, stream) == hipSuccess;
     if (p.G) ok = ok && hipMemcpyAsync(ws + p.off_gmap, p.gmap.data(), size_t(p.G) * 4,
                                        hipMemcpyHostToDevice, stream) == hipSuccess;
+    std::vector<int64_t> atab(2 * T1, 0);
+    std::copy(p.aslines.begin(), p.aslines.end(), atab.begin());
+    std::copy(p.asbase.begin(), p.asbase.end(), atab.begin() + T1);
+    ok = ok && hipMemcpyAsync(at, atab.data(), atab.size() * 8, hipMemcpyHostToDevice,
+                              stream) == hipSuccess;
+    if (p.AS) ok = ok && hipMemcpyAsync(ws + p.off_asmap, p.asmap.data(), size_t(p.AS) * 4,
+                                        hipMemcpyHostToDevice, stream) == hipSuccess;
     // zero the scratch after the tables (histograms must start at zero) and
     // the state vectors u and v
     if (ok) {
@@ -715,8 +750,8 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
     const int64_t wb = cdiv(st->BP, kWavesPerBlock);  // one piece per wave
     if (st->BP > 0) {
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
-        k_bl_fused<<<grid_for(wb, wb), kBlock, 0, stream>>>(
-            g, st->u, st->v, st->L, st->K, st->B, st->sc, clip_on, st->m, pcap_limit,
+        k_bl_fused<kSelBins><<<grid_for(wb, wb), kBlock, 0, stream>>>(
+            g, st->u, st->v, st->L, st->B, st->ts, st->sc, clip_on, st->m, pcap_limit,
             reinterpret_cast<uint4*>(st->slots), st->BP, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
@@ -731,8 +766,92 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
     // are not delivered get their u and v back here
     if (st->BP > 0) {
         const int64_t gb = cdiv(st->BP, int64_t(kBlock));  // kWave pieces per wave
-        k_bl_gather<<<grid_for(gb, gb), kBlock, 0, stream>>>(
-            st->u, st->v, st->L, st->K, st->B, pcap_limit,
+        k_bl_gather<kSelBins><<<grid_for(gb, gb), kBlock, 0, stream>>>(
+            st->u, st->v, st->L, st->K, st->B, st->ts, pcap_limit,
+            reinterpret_cast<const uint4*>(st->slots), st->BP, out_idx, out_val);
+    }
+    DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
+int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
+                         const int64_t* cap, double clip, uint32_t* out_idx,
+                         float* out_val, int64_t* out_count, int64_t* out_total,
+                         double* out_norm, float* out_scale, hipStream_t stream) {
+    if (!st || !k) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    const int T = p.T;
+    for (int32_t t = 0; t < T; ++t)
+        if (k[t] < 0 || k[t] > p.sizes[size_t(t)]) return DGC_EINVAL;
+    int rc = check_k(st, cap);
+    if (rc != DGC_OK) return rc;
+    int64_t C = 0;
+    for (int32_t t = 0; t < T; ++t) C += cap[t];
+    if (p.n > 0 && (!g || !aligned(g, 16))) return DGC_EINVAL;
+    if (C > 0 && (!out_idx || !out_val || !aligned(out_idx, 4) || !aligned(out_val, 4)))
+        return DGC_EINVAL;
+    if (!out_count || !aligned(out_count, 8)) return DGC_EINVAL;
+    if (out_total && !aligned(out_total, 8)) return DGC_EINVAL;
+    if (std::isnan(clip)) return DGC_EINVAL;
+    if (!st->ktgt_valid || std::memcmp(st->ktgt_last.data(), k, size_t(T) * 8) != 0) {
+        st->ktgt_last.assign(k, k + T);
+        if (hipMemcpyAsync(st->ws + p.off_ktgt, st->ktgt_last.data(), size_t(T) * 8,
+                           hipMemcpyHostToDevice, stream) != hipSuccess)
+            return DGC_EHIP;
+        st->ktgt_valid = true;
+    }
+    rc = upload_k(st, cap, stream);
+    if (rc != DGC_OK) return rc;
+    rc = upload_bins(st, st->bins_full.data(), stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const bool clip_on = clip > 0.0;
+    const uint32_t pcap_limit = st->select_path == 1 ? 0u : 0xFFFFFFFFu;
+    const int64_t* ktgt = reinterpret_cast<const int64_t*>(st->ws + p.off_ktgt);
+
+    DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    if (clip_on) {
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
+    } else if (st->BP == 0) {
+        k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
+    }
+    // the threshold: three histogram levels over the sample
+    const int AS = int(p.AS);
+    if (AS > 0)
+        k_sm_hist<0><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<0><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    if (AS > 0)
+        k_sm_hist<1><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<1><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    if (AS > 0)
+        k_sm_hist<2><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<2><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    DGC_LAUNCH_CHECK();
+    const int64_t wb = cdiv(st->BP, kWavesPerBlock);  // one piece per wave
+    if (st->BP > 0) {
+        DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+        k_bl_fused<kSelThresh><<<grid_for(wb, wb), kBlock, 0, stream>>>(
+            g, st->u, st->v, st->L, st->B, st->ts, st->sc, clip_on, st->m, pcap_limit,
+            reinterpret_cast<uint4*>(st->slots), st->BP, out_norm, out_scale);
+        DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+    }
+    if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+        return DGC_EHIP;
+    if (st->BG > 0) {
+        const int64_t gb = cdiv(st->BG, kWavesPerBlock);
+        k_bl_group<<<grid_for(gb, gb), kBlock, 0, stream>>>(st->L, st->B, st->BG);
+    }
+    k_bl_tscan<<<T, kBlock, 0, stream>>>(st->K, st->B, out_count, out_total);
+    if (st->BP > 0) {
+        const int64_t gb = cdiv(st->BP, int64_t(kBlock));
+        k_bl_gather<kSelThresh><<<grid_for(gb, gb), kBlock, 0, stream>>>(
+            st->u, st->v, st->L, st->K, st->B, st->ts, pcap_limit,
             reinterpret_cast<const uint4*>(st->slots), st->BP, out_idx, out_val);
     }
     DGC_LAUNCH_CHECK();

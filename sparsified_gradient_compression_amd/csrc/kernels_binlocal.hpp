@@ -1,4 +1,6 @@
-// kernels_binlocal.hpp -- the bin-local selector on gfx950.
+// kernels_binlocal.hpp -- the bin-local selector on gfx950, and the
+// element-wise pass and placement it shares with the sampled threshold
+// (kernels_sampled.hpp).
 //
 // Source: the AdaComp page ("AdaComp : Adaptive Residual Gradient Compression
 // for Data-Parallel Distributed Training"), Abstract (residues are selected
@@ -35,6 +37,12 @@ namespace dgc {
 
 constexpr int64_t kBlGroup = 1024;  // pieces per prefix group
 constexpr int64_t kMaxBin = kPiece;  // largest bin length
+
+// Selection rule of the pass: per-bin maxima (bin-local, AdaComp), or one
+// threshold per tensor taken from TensorState::lo_key (the sampled
+// threshold of kernels_sampled.hpp): key >= theta and key != 0.
+constexpr int kSelBins = 0;
+constexpr int kSelThresh = 1;
 
 // Bin-local tables (device pointers into the workspace), passed by value.
 struct DevBins {
@@ -141,6 +149,25 @@ __device__ __forceinline__ void bl_flags(const float (&vn)[kRounds][4],
         }
 }
 
+template <bool kAligned, int kSel>
+__device__ __forceinline__ void sel_flags(const float (&vn)[kRounds][4],
+                                          const float (&un)[kRounds][4],
+                                          uint32_t len, uint32_t magic, uint32_t theta,
+                                          uint32_t* th, bool (&f)[kRounds][4]) {
+    if constexpr (kSel == kSelBins) {
+        bl_flags<kAligned>(vn, un, len, magic, th, f);
+    } else {
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t key = mag_key(vn[i][c]);
+                f[i][c] = bl_off<kAligned>(i, c, lane) < len && key != 0u && key >= theta;
+            }
+    }
+}
+
 // Ranks of the flagged elements in index order, and their number.
 template <bool kAligned>
 __device__ __forceinline__ uint32_t bl_ranks(const bool (&f)[kRounds][4],
@@ -175,12 +202,12 @@ __device__ __forceinline__ uint32_t bl_ranks(const bool (&f)[kRounds][4],
     return total;
 }
 
-template <bool kAligned>
+template <bool kAligned, int kSel>
 __device__ __forceinline__ void bl_fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    int64_t e0, uint32_t len, int t, const DevLayout& L, const DevK& K,
-    const DevBins& B, float s, float m, uint32_t pcap_limit, uint4* __restrict__ slots,
-    int64_t p, uint32_t* th) {
+    int64_t e0, uint32_t len, int t, const DevLayout& L, const DevBins& B,
+    const TensorState* __restrict__ ts, float s, float m, uint32_t pcap_limit,
+    uint4* __restrict__ slots, int64_t p, uint32_t* th) {
     const int lane = lane_id();
     const int64_t e1 = e0 + len;
     float un[kRounds][4], vn[kRounds][4];
@@ -215,11 +242,12 @@ __device__ __forceinline__ void bl_fused_piece(
         }
     }
     const uint32_t magic = uint32_t(B.magic[t]);
+    const uint32_t theta = kSel == kSelThresh ? ts[t].lo_key : 0u;
     const int64_t o = L.o[t];
     const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
     bool f[kRounds][4];
     uint32_t rank[kRounds][4];
-    bl_flags<kAligned>(vn, un, len, magic, th, f);
+    sel_flags<kAligned, kSel>(vn, un, len, magic, theta, th, f);
     const uint32_t total = bl_ranks<kAligned>(f, rank);
     // the slots keep u and v as they were, so masking here can be undone
     const bool early = total <= pcap;
@@ -264,15 +292,24 @@ __device__ __forceinline__ void bl_fused_piece(
     }
 }
 
+// LDS rows of the per-bin maxima (none for the threshold rule).
+template <int kSel>
+struct SelLds {
+    static constexpr int kRows = kSel == kSelBins ? kWavesPerBlock : 1;
+    static constexpr int kLen = kSel == kSelBins ? int(kMaxBin) : 4;
+};
+
 // Element-wise pass, one wave per piece.  With clipping off block 0 also
 // writes the call's scalar outputs (norm -1, scale 1).  pcap_limit = 0
 // sends every piece through the re-derivation in k_bl_gather (a test hook).
+template <int kSel>
 __global__ __launch_bounds__(kBlock) void k_bl_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
-    DevLayout L, DevK K, DevBins B, Scalars* __restrict__ sc, int clip_on, float m,
+    DevLayout L, DevBins B, const TensorState* __restrict__ ts,
+    Scalars* __restrict__ sc, int clip_on, float m,
     uint32_t pcap_limit, uint4* __restrict__ slots, int64_t n_pieces,
     double* __restrict__ out_norm, float* __restrict__ out_scale) {
-    __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
+    __shared__ __align__(16) uint32_t th[SelLds<kSel>::kRows][SelLds<kSel>::kLen];
     const float s = clip_on ? sc->scale : 1.0f;
     if (!clip_on && blockIdx.x == 0 && threadIdx.x == 0) {
         sc->norm = -1.0;
@@ -284,13 +321,13 @@ __global__ __launch_bounds__(kBlock) void k_bl_fused(
     if (p >= n_pieces) return;  // no block-wide barrier follows
     const PieceDesc d = B.pdesc[p];
     const int t = wave_uniform(int(d.tensor));
-    uint32_t* row = th[threadIdx.x >> 6];
+    uint32_t* row = th[kSel == kSelBins ? (threadIdx.x >> 6) : 0];
     if ((d.start & 3) == 0)
-        bl_fused_piece<true>(g, u, v, d.start, d.len, t, L, K, B, s, m, pcap_limit,
-                             slots, p, row);
+        bl_fused_piece<true, kSel>(g, u, v, d.start, d.len, t, L, B, ts, s, m, pcap_limit,
+                                   slots, p, row);
     else
-        bl_fused_piece<false>(g, u, v, d.start, d.len, t, L, K, B, s, m, pcap_limit,
-                              slots, p, row);
+        bl_fused_piece<false, kSel>(g, u, v, d.start, d.len, t, L, B, ts, s, m, pcap_limit,
+                                    slots, p, row);
 }
 
 // Piece descriptors for the current bin lengths, one thread per piece.
@@ -355,10 +392,10 @@ __global__ __launch_bounds__(kBlock) void k_bl_tscan(DevK K, DevBins B,
 
 // Re-derive one overflowed piece from u and v (as k_bl_fused left them:
 // unmasked) and deliver its entries from position pos0 on.
-template <bool kAligned>
+template <bool kAligned, int kSel>
 __device__ __forceinline__ void bl_redo_piece(
     float* __restrict__ u, float* __restrict__ v, int64_t e0, uint32_t len,
-    uint32_t magic, int64_t o, int64_t pos0, int64_t nd, int64_t obase,
+    uint32_t magic, uint32_t theta, int64_t o, int64_t pos0, int64_t nd, int64_t obase,
     uint32_t* __restrict__ out_idx, float* __restrict__ out_val, uint32_t* th) {
     const int lane = lane_id();
     const int64_t e1 = e0 + len;
@@ -373,7 +410,7 @@ __device__ __forceinline__ void bl_redo_piece(
         }
     bool f[kRounds][4];
     uint32_t rank[kRounds][4];
-    bl_flags<kAligned>(vn, un, len, magic, th, f);
+    sel_flags<kAligned, kSel>(vn, un, len, magic, theta, th, f);
     (void)bl_ranks<kAligned>(f, rank);
 #pragma unroll
     for (int i = 0; i < kRounds; ++i)
@@ -398,11 +435,13 @@ __device__ __forceinline__ void bl_redo_piece(
 // goff[group of p] + pre[p] within it.
 constexpr int kGatherUnroll = 4;
 
+template <int kSel>
 __global__ __launch_bounds__(kBlock) void k_bl_gather(
     float* __restrict__ u, float* __restrict__ v, DevLayout L, DevK K, DevBins B,
-    uint32_t pcap_limit, const uint4* __restrict__ slots, int64_t n_pieces,
+    const TensorState* __restrict__ ts, uint32_t pcap_limit,
+    const uint4* __restrict__ slots, int64_t n_pieces,
     uint32_t* __restrict__ out_idx, float* __restrict__ out_val) {
-    __shared__ __align__(16) uint32_t th[kWavesPerBlock][kMaxBin];
+    __shared__ __align__(16) uint32_t th[SelLds<kSel>::kRows][SelLds<kSel>::kLen];
     const int lane = lane_id();
     const int64_t q0 = ((int64_t(blockIdx.x) * kBlock + threadIdx.x) >> 6) * kWave;
     if (q0 >= n_pieces) return;  // no block-wide barrier follows
@@ -470,7 +509,7 @@ __global__ __launch_bounds__(kBlock) void k_bl_gather(
     }
     // overflowed pieces
     uint64_t todo = __ballot(redo);
-    uint32_t* row = th[threadIdx.x >> 6];
+    uint32_t* row = th[kSel == kSelBins ? (threadIdx.x >> 6) : 0];
     while (todo) {
         const int j = __builtin_ctzll(todo);
         todo &= todo - 1;
@@ -479,12 +518,13 @@ __global__ __launch_bounds__(kBlock) void k_bl_gather(
         const int64_t ob = __shfl(obase, j, kWave);
         const int64_t ndj = int64_t(uint32_t(__shfl(int(nd), j, kWave)));
         const int64_t oj = L.o[t];
+        const uint32_t theta = kSel == kSelThresh ? ts[t].lo_key : 0u;
         if ((d.start & 3) == 0)
-            bl_redo_piece<true>(u, v, d.start, d.len, uint32_t(B.magic[t]), oj, 0, ndj, ob,
-                                out_idx, out_val, row);
+            bl_redo_piece<true, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), theta, oj,
+                                      0, ndj, ob, out_idx, out_val, row);
         else
-            bl_redo_piece<false>(u, v, d.start, d.len, uint32_t(B.magic[t]), oj, 0, ndj, ob,
-                                 out_idx, out_val, row);
+            bl_redo_piece<false, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), theta, oj,
+                                       0, ndj, ob, out_idx, out_val, row);
     }
 }
 

@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.dgc_compress_binlocal.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
                                         P, P, P]
     L.dgc_compress_binlocal.restype = ctypes.c_int
+    L.dgc_compress_sampled.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
+                                       P, P, P]
+    L.dgc_compress_sampled.restype = ctypes.c_int
     L.dgc_encode_counts.argtypes = [P, P, P, P, P, P, P, P, P]
     L.dgc_encode_counts.restype = ctypes.c_int
     L.dgc_stream_capacity.argtypes = [P, P]
@@ -174,6 +177,16 @@ def dgc_compress_binlocal(st, g, bin_len, cap, clip: float, out_idx, out_val,
                                        _dp(out_total), _dp(out_norm),
                                        _dp(out_scale), _stream(stream)),
            "dgc_compress_binlocal")
+
+
+def dgc_compress_sampled(st, g, k, cap, clip: float, out_idx, out_val, out_count,
+                         out_total=None, out_norm=None, out_scale=None, stream=None):
+    kk, cc = _i64(k), _i64(cap)
+    _check(lib().dgc_compress_sampled(st, _dp(g), _hp(kk), _hp(cc), float(clip),
+                                      _dp(out_idx), _dp(out_val), _dp(out_count),
+                                      _dp(out_total), _dp(out_norm), _dp(out_scale),
+                                      _stream(stream)),
+           "dgc_compress_sampled")
 
 
 def dgc_stream_capacity(st, n_tensors: int) -> np.ndarray:
@@ -317,6 +330,15 @@ class Learner:
         dgc_compress_binlocal(self.state, g, bin_len, cap, clip, self.idx,
                               self.val, self.count, self.total, self.norm,
                               self.scale, stream)
+        return self.idx[:C], self.val[:C], self.count, self.total
+
+    def compress_sampled(self, g, k: Sequence[int], cap: Sequence[int], clip: float,
+                         stream=None):
+        """One step with the sampled threshold (about k[t] entries per
+        tensor).  Returns (idx, val, count, total) as compress_binlocal."""
+        C = int(sum(int(x) for x in cap))
+        dgc_compress_sampled(self.state, g, k, cap, clip, self.idx, self.val,
+                             self.count, self.total, self.norm, self.scale, stream)
         return self.idx[:C], self.val[:C], self.count, self.total
 
     def encode_counts(self, cap: Sequence[int], stream=None):

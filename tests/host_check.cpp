@@ -56,6 +56,8 @@ int main() {
                                 nullptr, nullptr, nullptr, nullptr) == DGC_EINVAL);
     CHECK(dgc_encode_counts(nullptr, one, nullptr, nullptr, nullptr, nullptr, nullptr,
                             nullptr, nullptr) == DGC_EINVAL);
+    CHECK(dgc_compress_sampled(nullptr, nullptr, one, one, 0.0, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, nullptr, nullptr) == DGC_EINVAL);
     for (int code = -6; code <= 1; ++code) CHECK(dgc_error_string(code) != nullptr);
     dgc_destroy_state(nullptr);
     std::printf("host check: ok\n");

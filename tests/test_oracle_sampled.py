@@ -184,3 +184,26 @@ def test_rejects_bad_arguments(orc):
     # all zero: theta 0, but zeros are never sent
     idx, _, total, theta = orc.sampled_select_mask(z.copy(), z.copy(), 5)
     assert idx.size == 0 and total == 0 and theta == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sampled_and_exact_sets_are_nested(orc, seed):
+    """Both selections are threshold sets ({key >= theta} and top-k, i.e.
+    {key > T} plus the lowest-index ties at T), so one contains the other
+    and they differ in exactly |count - k| entries, all between the two
+    thresholds: the deviation from exact top-k is measured by the count."""
+    rng = np.random.default_rng([38, seed])
+    n = int(rng.choice([70001, 1 << 20]))
+    k = n // int(rng.choice([4, 64, 1000]))
+    v = rng.laplace(0, 1e-3, n).astype(np.float32)
+    if seed % 2:
+        v[rng.random(n) < 0.3] = 0.0
+    ex, _ = orc.select_mask(np.zeros(n, np.float32), v.copy(), k)
+    sm, _, total, theta = orc.sampled_select_mask(np.zeros(n, np.float32), v.copy(), k, seed)
+    a, b = set(ex.tolist()), set(sm.tolist())
+    assert a <= b or b <= a
+    assert len(a ^ b) == abs(total - k)
+    ky = keys(v).astype(np.int64)
+    lo, hi = sorted([int(theta), int(np.sort(ky)[::-1][k - 1])])
+    for i in a ^ b:
+        assert lo <= ky[i] <= hi
