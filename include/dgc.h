@@ -66,6 +66,13 @@ extern "C" {
 #define DGC_OPT_KERNEL_TIMING 2 /* value 1: bracket the work of each call with
                                    HIP events on the call's stream (read with
                                    dgc_get_kernel_time); 0: off (default) */
+#define DGC_OPT_DECODE_PATH 3   /* dgc_decode_accumulate, per tensor: 0
+                                   automatic (default: merged when the
+                                   learners' streams hold at least n_t / 16
+                                   entries together, else each stream added
+                                   on its own); 1 always on its own; 2 always
+                                   merged -- the same results, only the speed
+                                   differs */
 
 /* Timers for dgc_get_kernel_time. */
 #define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress,
@@ -258,7 +265,9 @@ int dgc_encode_counts(const dgc_state* st, const int64_t* cap,
  * gradient exchange of synchronous SGD, DGC review Abstract):
  * for w = 0 .. n_learners-1 in order, per tensor, pos = -1 and for each
  * entry pos += run + 1; dense[o_t + pos] = fl(dense[o_t + pos] + value).
- * Fillers are added too (+0.0f).  The sum is not averaged.
+ * Fillers are added too (+0.0f).  The sum is not averaged.  Where the
+ * streams are dense (DGC_OPT_DECODE_PATH) the learners' entries are added
+ * block by block in one pass per 8 learners, still in learner order.
  *   runs, vals, entries  host arrays of n_learners device pointers, each
  *                        stream laid out as dgc_encode writes it for this
  *                        state's layout

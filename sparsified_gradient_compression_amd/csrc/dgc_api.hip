@@ -42,6 +42,9 @@ struct Plan {
     std::vector<int64_t> aslines, asbase;
     std::vector<uint32_t> asmap;
     int64_t AS = 0;
+    // merged decode: bounds per tensor (dense blocks + 1) and dense blocks
+    std::vector<int64_t> dbase, bbase;
+    int64_t DB = 0, NBLK = 0;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
@@ -54,7 +57,8 @@ struct Plan {
            off_amap = 0, off_slots = 0, off_olist = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
-           off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, total = 0;
+           off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, off_dtab = 0,
+           off_dmode = 0, off_bounds = 0, total = 0;
 };
 
 // Candidate slots per 1024-element piece: none for small tensors (they take
@@ -101,6 +105,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.etbase.assign(T + 1, 0);
     p.aslines.assign(T + 1, 0);
     p.asbase.assign(T + 1, 0);
+    p.dbase.assign(T + 1, 0);
+    p.bbase.assign(T + 1, 0);
     for (int32_t t = 0; t < T; ++t) {
         int64_t n = sizes[t], km = kmax[t];
         if (n < 0 || n >= (int64_t(1) << 32) || km < 0 || km > n) return DGC_EINVAL;
@@ -118,6 +124,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.etbase[t + 1] = p.etbase[t] + cdiv(km + n / 65536, kTile);
         p.aslines[t] = n <= kSmallN ? cdiv(n, kLine) : p.slines[t];
         p.asbase[t + 1] = p.asbase[t] + cdiv(p.aslines[t], kLinesPerSampleBlock);
+        p.bbase[t + 1] = p.bbase[t] + cdiv(n, kDecBlock);
+        p.dbase[t + 1] = p.dbase[t] + cdiv(n, kDecBlock) + 1;
         p.BP += cdiv(n, kBlMinPiece);
         p.BG += cdiv(cdiv(n, kBlMinPiece), kBlGroup);
     }
@@ -132,6 +140,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.ET = p.etbase[T];
     p.NB = cdiv(p.n, kNormChunk);
     p.AS = p.asbase[T];
+    p.DB = p.dbase[T];
+    p.NBLK = p.bbase[T];
     if (p.P >= (int64_t(1) << 32) || p.TT >= (int64_t(1) << 32)) return DGC_EINVAL;
     // tiles over k never exceed tiles over n, so TT also bounds encode tiles
     p.tiles = std::max<int64_t>(std::max<int64_t>(p.TT, p.ET), 1);
@@ -172,6 +182,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_astab = take(2 * T1 * sizeof(int64_t));
     p.off_asmap = take(size_t(p.AS) * 4);
     p.off_ktgt = take(T1 * sizeof(int64_t));
+    p.off_dtab = take(2 * T1 * sizeof(int64_t));
     // Everything above is written from the host (layout tables at init, k
     // tables per call); everything from here on is device scratch, zeroed
     // at init.
@@ -198,6 +209,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_blpre = take(size_t(p.BP) * 4);
     p.off_blgsum = take(size_t(p.BG) * 4);
     p.off_blgoff = take(size_t(p.BG) * 4);
+    p.off_dmode = take(size_t(T) * 4);
+    p.off_bounds = take(size_t(kDecBatch) * size_t(p.DB) * sizeof(uint2));
     p.total = off;
     return DGC_OK;
 }
@@ -243,6 +256,8 @@ struct dgc_state {
     bool ktgt_valid = false;
     std::vector<int64_t> bins_full;  // one 1024-element bin per piece
     DevSample A{};
+    DevDec Dd{};
+    int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
     DevBins B{};
     // device views
@@ -446,7 +461,7 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
     if (rc != DGC_OK) return rc;
     st->last_stream = stream;
     const int T = p.T;
-    const int pg = st->num_cus * 8;
+    const int64_t pg = st->KT;  // one workgroup per tile
     DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
     if (st->KT > 0)
         k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
@@ -566,6 +581,12 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->A.sbase = at + T1;
     st->A.smap = reinterpret_cast<uint32_t*>(ws + p.off_asmap);
     st->bins_full.assign(size_t(T), kMaxBin);
+    int64_t* dt = reinterpret_cast<int64_t*>(ws + p.off_dtab);
+    st->Dd.dbase = dt;
+    st->Dd.bbase = dt + T1;
+    st->Dd.dmode = reinterpret_cast<uint32_t*>(ws + p.off_dmode);
+    st->Dd.bounds = reinterpret_cast<uint2*>(ws + p.off_bounds);
+    st->Dd.DB = p.DB;
     st->B.pdesc = reinterpret_cast<PieceDesc*>(ws + p.off_blpdesc);
     st->B.cnt = reinterpret_cast<uint32_t*>(ws + p.off_blcnt);
     st->B.pre = reinterpret_cast<uint32_t*>(ws + p.off_blpre);
@@ -578,7 +599,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
         p.off_k >= p.off_scratch || p.off_kmap >= p.off_scratch ||
         p.off_tab >= p.off_scratch || p.off_bltab >= p.off_scratch ||
         p.off_astab >= p.off_scratch || p.off_asmap >= p.off_scratch ||
-        p.off_ktgt >= p.off_scratch) {
+        p.off_ktgt >= p.off_scratch || p.off_dtab >= p.off_scratch) {
         delete st;
         return DGC_EINVAL;
     }
@@ -601,6 +622,11 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
                               stream) == hipSuccess;
     if (p.AS) ok = ok && hipMemcpyAsync(ws + p.off_asmap, p.asmap.data(), size_t(p.AS) * 4,
                                         hipMemcpyHostToDevice, stream) == hipSuccess;
+    std::vector<int64_t> dec_tab(2 * T1, 0);
+    std::copy(p.dbase.begin(), p.dbase.end(), dec_tab.begin());
+    std::copy(p.bbase.begin(), p.bbase.end(), dec_tab.begin() + T1);
+    ok = ok && hipMemcpyAsync(dt, dec_tab.data(), dec_tab.size() * 8, hipMemcpyHostToDevice,
+                              stream) == hipSuccess;
     // zero the scratch after the tables (histograms must start at zero) and
     // the state vectors u and v
     if (ok) {
@@ -900,14 +926,43 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
     st->last_stream = stream;
     if (p.ET == 0) return DGC_OK;
     const int T = p.T;
-    const int pg = grid_for(p.ET, st->num_cus * 8);
+    // one workgroup per capacity tile: tiles past a stream's end exit at once
+    const int pg = grid_for(p.ET, p.ET);
     DGC_TRY(timer_begin(st, DGC_TIMER_DECODE, stream));
-    for (int32_t w = 0; w < n_learners; ++w) {
-        k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, runs[w], entries[w], st->ta,
-                                               st->sc, p.ET);
-        k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, st->ta, st->t64);
-        k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, runs[w], vals[w], entries[w],
-                                               st->t64, dense, st->sc, p.ET);
+    // learners in batches of kDecBatch; each batch's merged tensors are
+    // added by one merge pass before the next batch starts
+    for (int32_t b0 = 0; b0 < n_learners; b0 += kDecBatch) {
+        const int nbw = std::min<int32_t>(kDecBatch, n_learners - b0);
+        // can any tensor reach the merge threshold with full streams?
+        bool merge_on = st->decode_path == 2 && p.NBLK > 0;
+        // one learner reads and writes its lines once either way
+        if (st->decode_path == 0 && nbw >= 2)
+            for (int32_t t = 0; t < T && !merge_on; ++t) {
+                const int64_t nt = p.sizes[size_t(t)];
+                const int64_t cap = p.ebase[size_t(t) + 1] - p.ebase[size_t(t)];
+                merge_on = nt > 0 && 16 * int64_t(nbw) * cap >= nt;
+            }
+        DecBatch S{};
+        S.W = nbw;
+        for (int w = 0; w < nbw; ++w) {
+            S.runs[w] = runs[b0 + w];
+            S.vals[w] = vals[b0 + w];
+            S.entries[w] = entries[b0 + w];
+        }
+        if (merge_on)
+            k_dec_mode<<<int(cdiv(T, kBlock)), kBlock, 0, stream>>>(st->L, S, st->Dd,
+                                                                   st->decode_path);
+        for (int w = 0; w < nbw; ++w) {
+            k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.entries[w], st->ta,
+                                                   st->sc, p.ET);
+            k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, st->ta, st->t64);
+            k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.vals[w], S.entries[w],
+                                                   st->t64, dense, st->sc, p.ET,
+                                                   int(merge_on), st->Dd, w);
+            DGC_LAUNCH_CHECK();
+        }
+        if (merge_on)
+            k_dec_merge<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, S, st->Dd, dense, p.NBLK);
         DGC_LAUNCH_CHECK();
     }
     DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
@@ -974,6 +1029,11 @@ int dgc_set_fused_event(dgc_state* st, hipEvent_t ev) {
 
 int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
     if (!st) return DGC_EINVAL;
+    if (option == DGC_OPT_DECODE_PATH) {
+        if (value < 0 || value > 2) return DGC_EINVAL;
+        st->decode_path = int(value);
+        return DGC_OK;
+    }
     if (option == DGC_OPT_SELECT_PATH) {
         if (value != 0 && value != 1) return DGC_EINVAL;
         st->select_path = int(value);

@@ -137,6 +137,53 @@ __device__ __forceinline__ int64_t stream_len(const int64_t* entries, int t,
     return (e < 0 || e > cap) ? 0 : e;
 }
 
+// Merged decode.  A tensor whose learners' streams together hold at least
+// n_t / 16 entries touches most cache lines of its part of the dense sum
+// once per learner when each stream is added on its own.  For such a tensor
+// each learner's pass only records, per kDecBlock-element block of the
+// tensor, the first entry at or past the block start and that entry's
+// position; one merge pass then loads each block on chip, adds the learners'
+// entries in learner order (a barrier between learners, so every element
+// still sees fl(fl(d + x_0) + x_1) ...) and stores the block once.
+constexpr int64_t kDecBlock = 4096;
+constexpr int kDecBatch = 8;  // learners merged per pass
+constexpr uint32_t kDecScatter = 0, kDecMerge = 1;
+
+// Dense-block tables: tensor t has cdiv(n_t, kDecBlock) blocks; its bounds
+// are bounds[w * DB + dbase[t] + j] for j in [0, blocks_t] (the last one a
+// sentinel past the tensor's end).
+struct DevDec {
+    const int64_t* dbase;   // [T+1] first bound of each tensor (blocks_t + 1 each)
+    const int64_t* bbase;   // [T+1] first dense block of each tensor (blocks_t each)
+    uint32_t* dmode;        // [T] kDecScatter / kDecMerge for the current batch
+    uint2* bounds;          // [kDecBatch * DB] {first entry index, its position}
+    int64_t DB;
+};
+
+// The streams of one batch of learners (by value).
+struct DecBatch {
+    const uint16_t* runs[kDecBatch];
+    const float* vals[kDecBatch];
+    const int64_t* entries[kDecBatch];
+    int W;
+};
+
+// One thread per tensor: merged or scattered for this batch.  force: 0
+// automatic, 1 always scattered, 2 always merged.
+__global__ __launch_bounds__(kBlock) void k_dec_mode(DevLayout L, DecBatch S, DevDec Dd,
+                                                     int force) {
+    const int t = int(blockIdx.x) * kBlock + int(threadIdx.x);
+    if (t >= L.T) return;
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    const int64_t cap = L.ebase[t + 1] - L.ebase[t];
+    int64_t sum = 0;
+    for (int w = 0; w < S.W; ++w) sum += stream_len(S.entries[w], t, cap);
+    uint32_t mode = (16 * sum >= nt) ? kDecMerge : kDecScatter;
+    if (force == 1) mode = kDecScatter;
+    if (force == 2) mode = kDecMerge;
+    Dd.dmode[t] = nt > 0 ? mode : kDecScatter;
+}
+
 // Per capacity tile of one learner's stream: sum of (run + 1).  Flags an
 // entry count outside [0, capacity].
 __global__ __launch_bounds__(kBlock) void k_dec_count(
@@ -179,11 +226,16 @@ __global__ __launch_bounds__(kBlock) void k_dec_scan(
 // pos = (sum of run + 1 over the entries up to this one) - 1.  Entries whose
 // position reaches the tensor's end add nothing and flag the stream as
 // corrupt (positions only grow, so every later entry is past the end too).
+// For a tensor in merged mode (merge_on and dmode[t] == kDecMerge) the
+// entries are not added here: each records, for every dense block whose
+// first entry it is (previous position < block start <= its position), its
+// index and position in the learner's bound row (slot); the last entry also
+// fills the blocks after it with {E, 0}.
 __global__ __launch_bounds__(kBlock) void k_dec_write(
     DevLayout L, const uint16_t* __restrict__ runs,
     const float* __restrict__ vals, const int64_t* __restrict__ entries,
     const uint64_t* __restrict__ tile_p, float* __restrict__ dense,
-    Scalars* __restrict__ sc, int64_t n_etiles) {
+    Scalars* __restrict__ sc, int64_t n_etiles, int merge_on, DevDec Dd, int slot) {
     __shared__ uint32_t lds[kWavesPerBlock];
     for (int64_t vt = blockIdx.x; vt < n_etiles; vt += gridDim.x) {
         const int t = int(L.emap[vt]);
@@ -191,6 +243,9 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         const int64_t o = L.o[t], nt = L.o[t + 1] - o;
         const int64_t E = stream_len(entries, t, cap);
         const int64_t i0 = (vt - L.etbase[t]) * kTile;
+        const bool merged = merge_on && Dd.dmode[t] == kDecMerge;
+        const int64_t nb = (nt + kDecBlock - 1) / kDecBlock;  // sentinel index
+        uint2* bnd = merged ? Dd.bounds + int64_t(slot) * Dd.DB + Dd.dbase[t] : nullptr;
         uint64_t carry = tile_p[vt];
         bool bad = false;
         for (int q = 0; q < kPerThread; ++q) {
@@ -202,11 +257,113 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
             if (i < E) {
                 const int64_t pos = int64_t(carry) + ex + w - 1;
                 if (pos >= nt) bad = true;
-                else dense[o + pos] = __fadd_rn(dense[o + pos], vals[eb + i]);
+                if (!merged) {
+                    if (pos < nt) dense[o + pos] = __fadd_rn(dense[o + pos], vals[eb + i]);
+                } else {
+                    const int64_t prev = pos - int64_t(w);  // -1 for the first entry
+                    const int64_t b0 = prev < 0 ? 0 : prev / kDecBlock + 1;
+                    const int64_t b1 = min(pos / kDecBlock, nb);
+                    for (int64_t b = b0; b <= b1; ++b)
+                        bnd[b] = make_uint2(uint32_t(i), uint32_t(min(pos, nt)));
+                    if (i == E - 1)
+                        for (int64_t b = max(b0, b1 + 1); b <= nb; ++b)
+                            bnd[b] = make_uint2(uint32_t(E), 0u);
+                }
             }
             carry += tot;
         }
         if (bad) latch_error(sc, kErrCorrupt);
+    }
+}
+
+// Merge pass: one workgroup per dense block of a merged tensor.  The block
+// is loaded into LDS, each learner's entries inside it are added in learner
+// order, and the block is stored once.  Positions are rebuilt from the
+// recorded first position and the runs.  Every learner's first kBlock
+// entries are loaded together with the block (one wait for all of them).
+// Blocks no learner touches are left alone.
+__global__ __launch_bounds__(kBlock) void k_dec_merge(
+    DevLayout L, DecBatch S, DevDec Dd, float* __restrict__ dense, int64_t n_blocks) {
+    __shared__ float tile[kDecBlock];
+    __shared__ uint32_t lds[kWavesPerBlock];
+    const int64_t blk = blockIdx.x;
+    if (blk >= n_blocks) return;
+    const int t = find_seg(Dd.bbase, L.T, blk);
+    if (Dd.dmode[t] != kDecMerge) return;  // uniform
+    const int64_t j = blk - Dd.bbase[t];
+    const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+    const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
+    const int64_t lo_pos = j * kDecBlock;
+    const int64_t len = min(kDecBlock, nt - lo_pos);
+    const int64_t gb = Dd.dbase[t] + j;
+    const uint32_t tid = threadIdx.x;
+    uint32_t lo[kDecBatch], hi[kDecBatch], p0[kDecBatch];
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < kDecBatch; ++w) {
+        lo[w] = hi[w] = p0[w] = 0;
+        if (w < S.W && stream_len(S.entries[w], t, cap) > 0) {
+            const uint2* bnd = Dd.bounds + int64_t(w) * Dd.DB + gb;
+            const uint2 a = bnd[0], b = bnd[1];
+            lo[w] = a.x;
+            p0[w] = a.y;
+            hi[w] = max(a.x, b.x);
+            any = any || hi[w] > lo[w];
+        }
+    }
+    if (!any) return;  // uniform
+    // first round of every learner's entries, in flight with the block load
+    uint32_t r0[kDecBatch];
+    float x0[kDecBatch];
+#pragma unroll
+    for (int w = 0; w < kDecBatch; ++w) {
+        const uint32_t i = lo[w] + tid;
+        r0[w] = 0;
+        x0[w] = 0.0f;
+        if (i < hi[w]) {
+            r0[w] = S.runs[w][eb + i];
+            x0[w] = S.vals[w][eb + i];
+        }
+    }
+    float* d = dense + o + lo_pos;
+    float reg[kDecBlock / kBlock];
+#pragma unroll
+    for (int q = 0; q < int(kDecBlock / kBlock); ++q) {
+        const int64_t e = int64_t(q) * kBlock + tid;
+        reg[q] = e < len ? d[e] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < int(kDecBlock / kBlock); ++q) tile[q * kBlock + tid] = reg[q];
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kDecBatch; ++w) {
+        if (hi[w] <= lo[w]) continue;  // uniform
+        const uint16_t* rr = S.runs[w] + eb;
+        const float* vv = S.vals[w] + eb;
+        int64_t carry = int64_t(p0[w]);
+        for (uint32_t base = lo[w]; base < hi[w]; base += kBlock) {
+            const uint32_t i = base + tid;
+            uint32_t run = r0[w];
+            float x = x0[w];
+            if (base != lo[w] && i < hi[w]) {
+                run = rr[i];
+                x = vv[i];
+            }
+            const uint32_t wt = (i < hi[w] && i > lo[w]) ? run + 1u : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan(wt, lds, tot);
+            if (i < hi[w]) {
+                const int64_t at = carry + ex + wt - lo_pos;
+                if (at >= 0 && at < len) tile[at] = __fadd_rn(tile[at], x);
+            }
+            carry += tot;
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < int(kDecBlock / kBlock); ++q) {
+        const int64_t e = int64_t(q) * kBlock + tid;
+        if (e < len) d[e] = tile[e];
     }
 }
 

@@ -22,6 +22,7 @@ DGC_EHIP = -3
 DGC_ECORRUPT = -4
 DGC_OPT_SELECT_PATH = 1
 DGC_OPT_KERNEL_TIMING = 2
+DGC_OPT_DECODE_PATH = 3
 DGC_TIMER_FUSED = 0
 DGC_TIMER_COMPRESS = 1
 DGC_TIMER_ENCODE = 2

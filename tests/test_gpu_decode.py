@@ -1,0 +1,134 @@
+"""GPU parity of dgc_decode_accumulate on both of its paths: each learner's
+stream added on its own, and the merged pass (dense blocks held on chip,
+learners added in order) -- forced each way and automatic.  Streams are
+encoded by the oracle from seeded random selections at densities from 30%
+down to 0.1%; the dense sum starts from random values (and -0.0), so the
+order of the additions is visible in the bits.  The reference is the
+oracle's decoder run learner after learner.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import f32_bits, first_diff, say
+from sparsified_gradient_compression_amd import dgc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dgc.lib()
+    return torch
+
+
+def make_streams(rng, sizes, densities, cap):
+    """Per learner: oracle-encoded (runs, vals) per tensor, and the device
+    buffers laid out at the capacity offsets."""
+    import torch
+    C = int(cap[-1])
+    out = []
+    for d in densities:
+        runs = np.zeros(max(C, 1), np.uint16)
+        vals = np.zeros(max(C, 1), np.float32)
+        ent = np.zeros(len(sizes), np.int64)
+        per = []
+        for t, n in enumerate(sizes):
+            k = int(rng.binomial(n, d)) if n else 0
+            k = min(k, int(cap[t + 1] - cap[t]) - n // 65536)
+            idx = np.sort(rng.choice(n, size=k, replace=False)).astype(np.uint32) if k else \
+                np.zeros(0, np.uint32)
+            val = rng.standard_normal(k).astype(np.float32)
+            val[rng.random(k) < 0.05] = -0.0
+            r, v = oracle.encode(idx, val, cap=int(cap[t + 1] - cap[t]))
+            runs[cap[t]:cap[t] + r.size] = r
+            vals[cap[t]:cap[t] + r.size] = v
+            ent[t] = r.size
+            per.append((r, v))
+        out.append((per, torch.from_numpy(runs.view(np.int16)).cuda(),
+                    torch.from_numpy(vals).cuda(), torch.from_numpy(ent).cuda()))
+    return out
+
+
+def reference(sizes, dense0, streams):
+    want = dense0.copy()
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    for per, *_ in streams:
+        for t, (r, v) in enumerate(per):
+            assert oracle.decode_accumulate(r, v, want[off[t]:off[t + 1]]) == 0
+    return want
+
+
+def decode(L, streams, dense0, path):
+    import torch
+    L.set_option(dgc.DGC_OPT_DECODE_PATH, path)
+    dense = torch.from_numpy(dense0.copy()).cuda()
+    dgc.decode_accumulate(L, [(s[1], s[2], s[3]) for s in streams], dense)
+    torch.cuda.synchronize()
+    return dense.cpu().numpy()
+
+
+LAYOUTS = [
+    [1, 4095, 4096, 4097, 8192 + 3, 70001],
+    [1 << 20],
+    [0, 7, 65536, 65537, 131073, 300007, 5],
+]
+
+
+@pytest.mark.parametrize("layout", range(len(LAYOUTS)))
+@pytest.mark.parametrize("W,dens", [(1, [0.3]), (2, [0.05, 0.2]), (4, [0.05] * 4),
+                                    (5, [0.001, 0.3, 0.01, 0.1, 0.05]),
+                                    (9, [0.02] * 9), (17, [0.07] * 17)])
+def test_decode_paths_match_oracle(layout, W, dens):
+    sizes = LAYOUTS[layout]
+    rng = np.random.default_rng([91, layout, W])
+    L = dgc.Learner(sizes, sizes)
+    streams = make_streams(rng, sizes, dens, L.cap)
+    n = sum(sizes)
+    dense0 = rng.standard_normal(max(n, 1)).astype(np.float32)
+    dense0[rng.random(dense0.size) < 0.1] = -0.0
+    want = reference(sizes, dense0[:n], streams)
+    for path in (1, 2, 0):
+        say(f"decode layout {layout} W={W} path {path}")
+        got = decode(L, streams, dense0, path)[:n]
+        assert L.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got), f32_bits(want)), (path, first_diff(got, want))
+
+
+def test_merged_decode_flags_corrupt_streams():
+    """A stream that walks past its tensor's end, or claims more entries
+    than its capacity, is flagged on the merged path too, and nothing is
+    written outside the tensor."""
+    import torch
+    sizes = [10000, 5000]
+    L = dgc.Learner(sizes, sizes)
+    rng = np.random.default_rng(92)
+    streams = make_streams(rng, sizes, [0.3, 0.3], L.cap)
+    # learner 1, tensor 0: runs that pass the end of the 10000-element tensor
+    per, runs, vals, ent = streams[1]
+    r = runs.cpu().numpy().view(np.uint16).copy()
+    r[L.cap[0]:L.cap[0] + int(ent[0])] = 200
+    streams[1] = (per, torch.from_numpy(r.view(np.int16)).cuda(), vals, ent)
+    guard = 123.0
+    dense0 = np.full(sum(sizes) + 64, guard, np.float32)
+    got = decode(L, streams, dense0, 2)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert (got[sum(sizes):] == guard).all()
+    # entry count above capacity
+    per, runs, vals, ent = streams[0]
+    bad = ent.clone()
+    bad[1] = int(L.cap[2] - L.cap[1]) + 1
+    streams[0] = (per, runs, vals, bad)
+    decode(L, streams, dense0, 2)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert L.status() == dgc.DGC_OK
+
+
+def test_decode_option_rejects_bad_values():
+    L = dgc.Learner([100], [10])
+    with pytest.raises(dgc.DGCError):
+        L.set_option(dgc.DGC_OPT_DECODE_PATH, 3)
