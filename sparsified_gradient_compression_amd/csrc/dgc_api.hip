@@ -23,6 +23,12 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// Workgroups per compute unit of the encode / decode tile walks.
+#ifndef DGC_CODEC_BLOCKS_PER_CU
+#define DGC_CODEC_BLOCKS_PER_CU 32
+#endif
+constexpr int64_t kCodecBlocksPerCU = DGC_CODEC_BLOCKS_PER_CU;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -461,7 +467,7 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
     if (rc != DGC_OK) return rc;
     st->last_stream = stream;
     const int T = p.T;
-    const int64_t pg = st->KT;  // one workgroup per tile
+    const int64_t pg = int64_t(st->num_cus) * kCodecBlocksPerCU;
     DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
     if (st->KT > 0)
         k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
@@ -926,8 +932,9 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
     st->last_stream = stream;
     if (p.ET == 0) return DGC_OK;
     const int T = p.T;
-    // one workgroup per capacity tile: tiles past a stream's end exit at once
-    const int pg = grid_for(p.ET, p.ET);
+    // grid-stride over capacity tiles; a workgroup that reaches a tile past
+    // its stream's end skips to the next tensor
+    const int pg = grid_for(p.ET, int64_t(st->num_cus) * kCodecBlocksPerCU);
     DGC_TRY(timer_begin(st, DGC_TIMER_DECODE, stream));
     // learners in batches of kDecBatch; each batch's merged tensors are
     // added by one merge pass before the next batch starts
@@ -955,7 +962,7 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
         for (int w = 0; w < nbw; ++w) {
             k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.entries[w], st->ta,
                                                    st->sc, p.ET);
-            k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, st->ta, st->t64);
+            k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, S.entries[w], st->ta, st->t64);
             k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.vals[w], S.entries[w],
                                                    st->t64, dense, st->sc, p.ET,
                                                    int(merge_on), st->Dd, w);

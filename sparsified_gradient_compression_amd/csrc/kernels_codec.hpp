@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
     return uint32_t(gap >> 16);
 }
 
+// Grid-stride walk over per-tensor tiles: the tile after vt for this
+// workgroup that lies at or past `first` (the next tensor's first tile).
+// Once a tile lies past its tensor's entries so do the tensor's later
+// tiles, so a workgroup skips straight to the next tensor.
+__device__ __forceinline__ int64_t next_tensor_tile(int64_t vt, int64_t first,
+                                                    int64_t stride) {
+    if (first <= vt) return vt + stride;
+    return vt + (first - vt + stride - 1) / stride * stride;
+}
+
 // Entries of tensor t to encode: k_t, or, when the counts live on the
 // device (a data-dependent selector), that count if it lies in [0, k_t] and
 // else none (k_enc_scan flags it).
@@ -52,12 +62,16 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
     const uint32_t* __restrict__ idx, uint32_t* __restrict__ tile_f,
     Scalars* __restrict__ sc, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    for (int64_t vt = blockIdx.x; vt < n_ktiles; vt += gridDim.x) {
+    for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
         const int t = int(K.kmap[vt]);
         const int64_t kt = enc_len(K, kdev, t);
         const int64_t nt = L.o[t + 1] - L.o[t];
         const uint32_t* id = idx + K.koff[t];
         const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+        if (i0 >= kt) {  // uniform: nothing here or later in this tensor
+            vt = next_tensor_tile(vt, K.ktbase[t + 1], gridDim.x);
+            continue;
+        }
         uint32_t f = 0;
         bool bad = false;
         for (int q = 0; q < kPerThread; ++q) {
@@ -71,6 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
         uint32_t tot;
         block_exclusive_scan(f, lds, tot);
         if (threadIdx.x == 0) tile_f[vt] = tot;
+        vt += gridDim.x;
     }
 }
 
@@ -81,11 +96,13 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
     int64_t* __restrict__ entries, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
-    const int64_t kb = K.ktbase[t], ntile = K.ktbase[t + 1] - kb;
+    const int64_t kt = enc_len(K, kdev, t);
+    // only the tiles that hold entries (k_enc_count skips the rest)
+    const int64_t kb = K.ktbase[t], ntile = (kt + kTile - 1) / kTile;
     const uint32_t carry = block_scan_range<uint32_t>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
     if (threadIdx.x == 0) {
         if (kdev && (kdev[t] < 0 || kdev[t] > K.k[t])) latch_error(sc, kErrCorrupt);
-        entries[t] = enc_len(K, kdev, t) + int64_t(carry);
+        entries[t] = kt + int64_t(carry);
     }
 }
 
@@ -97,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
     const uint32_t* __restrict__ tile_foff, uint16_t* __restrict__ runs,
     float* __restrict__ vals, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    for (int64_t vt = blockIdx.x; vt < n_ktiles; vt += gridDim.x) {
+    for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
         const int t = int(K.kmap[vt]);
         const int64_t kt = enc_len(K, kdev, t);
         const int64_t nt = L.o[t + 1] - L.o[t];
@@ -105,6 +122,10 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         const float* vl = val + K.koff[t];
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
         const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+        if (i0 >= kt) {  // uniform: nothing here or later in this tensor
+            vt = next_tensor_tile(vt, K.ktbase[t + 1], gridDim.x);
+            continue;
+        }
         uint32_t carry = tile_foff[vt];
         for (int q = 0; q < kPerThread; ++q) {
             if (i0 + q * kBlock >= kt) break;  // uniform
@@ -126,6 +147,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
             }
             carry += tot;
         }
+        vt += gridDim.x;
     }
 }
 
@@ -191,7 +213,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
     const int64_t* __restrict__ entries, uint32_t* __restrict__ tile_s,
     Scalars* __restrict__ sc, int64_t n_etiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    for (int64_t vt = blockIdx.x; vt < n_etiles; vt += gridDim.x) {
+    for (int64_t vt = blockIdx.x; vt < n_etiles;) {
         const int t = int(L.emap[vt]);
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
         const int64_t j = vt - L.etbase[t];
@@ -201,6 +223,10 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
         }
         const int64_t E = stream_len(entries, t, cap);
         const int64_t i0 = j * kTile;
+        if (i0 >= E) {  // uniform: nothing here or later in this tensor
+            vt = next_tensor_tile(vt, L.etbase[t + 1], gridDim.x);
+            continue;
+        }
         uint32_t s = 0;
         for (int q = 0; q < kPerThread; ++q) {
             int64_t i = i0 + q * kBlock + threadIdx.x;
@@ -209,16 +235,19 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
         uint32_t tot;
         block_exclusive_scan(s, lds, tot);
         if (threadIdx.x == 0) tile_s[vt] = tot;
+        vt += gridDim.x;
     }
 }
 
-// One block per tensor: 64-bit exclusive scan of the tile sums.
+// One block per tensor: 64-bit exclusive scan of the sums of the tiles
+// that hold entries (k_dec_count skips the rest).
 __global__ __launch_bounds__(kBlock) void k_dec_scan(
-    DevLayout L, const uint32_t* __restrict__ tile_s,
+    DevLayout L, const int64_t* __restrict__ entries, const uint32_t* __restrict__ tile_s,
     uint64_t* __restrict__ tile_p) {
     __shared__ uint64_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
-    const int64_t tb = L.etbase[t], ntile = L.etbase[t + 1] - tb;
+    const int64_t tb = L.etbase[t], cap = L.ebase[t + 1] - L.ebase[t];
+    const int64_t ntile = (stream_len(entries, t, cap) + kTile - 1) / kTile;
     block_scan_range<uint64_t>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds);
 }
 
@@ -237,12 +266,16 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
     const uint64_t* __restrict__ tile_p, float* __restrict__ dense,
     Scalars* __restrict__ sc, int64_t n_etiles, int merge_on, DevDec Dd, int slot) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    for (int64_t vt = blockIdx.x; vt < n_etiles; vt += gridDim.x) {
+    for (int64_t vt = blockIdx.x; vt < n_etiles;) {
         const int t = int(L.emap[vt]);
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
         const int64_t o = L.o[t], nt = L.o[t + 1] - o;
         const int64_t E = stream_len(entries, t, cap);
         const int64_t i0 = (vt - L.etbase[t]) * kTile;
+        if (i0 >= E) {  // uniform: nothing here or later in this tensor
+            vt = next_tensor_tile(vt, L.etbase[t + 1], gridDim.x);
+            continue;
+        }
         const bool merged = merge_on && Dd.dmode[t] == kDecMerge;
         const int64_t nb = (nt + kDecBlock - 1) / kDecBlock;  // sentinel index
         uint2* bnd = merged ? Dd.bounds + int64_t(slot) * Dd.DB + Dd.dbase[t] : nullptr;
@@ -273,6 +306,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
             carry += tot;
         }
         if (bad) latch_error(sc, kErrCorrupt);
+        vt += gridDim.x;
     }
 }
 
