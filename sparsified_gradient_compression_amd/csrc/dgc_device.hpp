@@ -196,27 +196,29 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* lds, T& total) {
 }
 
 // Exclusive scan of in[0, count) into out[0, count), starting at `carry`,
-// by one block: each thread takes kScanPer consecutive values per round
-// (one block-wide scan per 256 * kScanPer values).  Returns carry + total.
-// Every thread must call it.
+// by one block: each thread takes PER consecutive values per round (one
+// block-wide scan per 256 * PER values; a round costs about one memory
+// round trip, so long per-tensor scans take many values per thread).
+// Returns carry + total.  Every thread must call it.
 constexpr int kScanPer = 8;
-template <typename TO>
+constexpr int kWideScanPer = 32;
+template <typename TO, int PER = kScanPer>
 __device__ __forceinline__ TO block_scan_range(const uint32_t* __restrict__ in,
                                                TO* __restrict__ out, int64_t count,
                                                TO carry, TO* lds) {
-    for (int64_t base = 0; base < count; base += int64_t(kBlock) * kScanPer) {
-        const int64_t i0 = base + int64_t(threadIdx.x) * kScanPer;
-        uint32_t x[kScanPer];
+    for (int64_t base = 0; base < count; base += int64_t(kBlock) * PER) {
+        const int64_t i0 = base + int64_t(threadIdx.x) * PER;
+        uint32_t x[PER];
         TO local = 0;
 #pragma unroll
-        for (int q = 0; q < kScanPer; ++q) {
+        for (int q = 0; q < PER; ++q) {
             x[q] = i0 + q < count ? in[i0 + q] : 0u;
             local += TO(x[q]);
         }
         TO tot;
         TO run = carry + block_exclusive_scan(local, lds, tot);
 #pragma unroll
-        for (int q = 0; q < kScanPer; ++q) {
+        for (int q = 0; q < PER; ++q) {
             if (i0 + q < count) out[i0 + q] = run;
             run += TO(x[q]);
         }

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
     const int64_t kt = enc_len(K, kdev, t);
     // only the tiles that hold entries (k_enc_count skips the rest)
     const int64_t kb = K.ktbase[t], ntile = (kt + kTile - 1) / kTile;
-    const uint32_t carry = block_scan_range<uint32_t>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
+    const uint32_t carry = block_scan_range<uint32_t, kWideScanPer>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
     if (threadIdx.x == 0) {
         if (kdev && (kdev[t] < 0 || kdev[t] > K.k[t])) latch_error(sc, kErrCorrupt);
         entries[t] = kt + int64_t(carry);
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_scan(
     const int t = blockIdx.x;
     const int64_t tb = L.etbase[t], cap = L.ebase[t + 1] - L.ebase[t];
     const int64_t ntile = (stream_len(entries, t, cap) + kTile - 1) / kTile;
-    block_scan_range<uint64_t>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds);
+    block_scan_range<uint64_t, kWideScanPer>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds);
 }
 
 // dense[o_t + pos] += value for every entry of one learner's stream, where

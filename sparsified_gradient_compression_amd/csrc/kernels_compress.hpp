@@ -274,12 +274,12 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
     int over = 0;
     if (k > 0) {
         const int64_t g0 = L.gbase[t], g1 = L.gbase[t + 1];
-        for (int64_t base = g0; base < g1; base += int64_t(kBlock) * kScanPer) {
-            const int64_t i0 = base + int64_t(threadIdx.x) * kScanPer;
-            uint32_t x[kScanPer];
+        for (int64_t base = g0; base < g1; base += int64_t(kBlock) * kWideScanPer) {
+            const int64_t i0 = base + int64_t(threadIdx.x) * kWideScanPer;
+            uint32_t x[kWideScanPer];
             uint32_t local = 0;
 #pragma unroll
-            for (int q = 0; q < kScanPer; ++q) {
+            for (int q = 0; q < kWideScanPer; ++q) {
                 uint32_t y = i0 + q < g1 ? gsum[i0 + q] : 0u;
                 over |= (y >> 31) != 0;
                 x[q] = y & 0x7FFFFFFFu;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
             uint32_t tot;
             uint32_t run = carry + block_exclusive_scan(local, lds, tot);
 #pragma unroll
-            for (int q = 0; q < kScanPer; ++q) {
+            for (int q = 0; q < kWideScanPer; ++q) {
                 if (i0 + q < g1) goff[i0 + q] = run;
                 run += x[q];
             }
@@ -539,12 +539,12 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
     const int t = blockIdx.x;
     const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
     uint32_t cg = 0, ce = 0;
-    for (uint32_t base = a0; base < a1; base += uint32_t(kBlock) * kScanPer) {
-        const uint32_t i0 = base + threadIdx.x * kScanPer;
-        uint32_t x[kScanPer];
+    for (uint32_t base = a0; base < a1; base += uint32_t(kBlock) * kWideScanPer) {
+        const uint32_t i0 = base + threadIdx.x * kWideScanPer;
+        uint32_t x[kWideScanPer];
         uint32_t lg = 0, le = 0;
 #pragma unroll
-        for (int q = 0; q < kScanPer; ++q) {
+        for (int q = 0; q < kWideScanPer; ++q) {
             x[q] = i0 + q < a1 ? tile_cnt[i0 + q] : 0u;
             lg += x[q] >> 16;
             le += x[q] & 0xFFFFu;
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
         uint32_t rg = cg + block_exclusive_scan(lg, lds, tg);
         uint32_t re = ce + block_exclusive_scan(le, lds, te);
 #pragma unroll
-        for (int q = 0; q < kScanPer; ++q) {
+        for (int q = 0; q < kWideScanPer; ++q) {
             if (i0 + q < a1) { off_gt[i0 + q] = rg; off_eq[i0 + q] = re; }
             rg += x[q] >> 16;
             re += x[q] & 0xFFFFu;

@@ -30,6 +30,9 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     dgc.lib()
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()  # memory cached by earlier test modules
     free, _ = torch.cuda.mem_get_info()
     if free < (200 << 30):
         pytest.skip("needs about 200 GiB of free device memory")
