@@ -184,7 +184,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_gmap = take(size_t(p.G) * 4);
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
-    p.off_bltab = take(6 * T1 * sizeof(int64_t));
+    p.off_bltab = take(7 * T1 * sizeof(int64_t));
     p.off_astab = take(2 * T1 * sizeof(int64_t));
     p.off_asmap = take(size_t(p.AS) * 4);
     p.off_ktgt = take(T1 * sizeof(int64_t));
@@ -256,7 +256,7 @@ struct dgc_state {
     bool k_valid = false;
     int64_t KT = 0;  // tiles over k of the last upload
     std::vector<int64_t> bins_last;  // bin lengths of the last upload
-    std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap, slbase (host copy)
+    std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap, slbase, rbins (host)
     bool bins_valid = false;
     std::vector<int64_t> ktgt_last;  // target k of the last sampled call
     bool ktgt_valid = false;
@@ -410,17 +410,20 @@ int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
         return DGC_OK;
     const size_t T1 = size_t(T) + 1;
     std::vector<int64_t>& tb = st->bl_tables;
-    tb.assign(6 * T1, 0);
+    tb.assign(7 * T1, 0);
     int64_t* plen = tb.data();
     int64_t* magic = plen + T1;
     int64_t* pbase = magic + T1;
     int64_t* gbase = pbase + T1;
     int64_t* pcap = gbase + T1;
     int64_t* slb = pcap + T1;
+    int64_t* rbins = slb + T1;
     for (int32_t t = 0; t < T; ++t) {
         const int64_t Lb = bin_len[t], n = p.sizes[size_t(t)];
         plen[t] = Lb * (kMaxBin / Lb);
         magic[t] = Lb == 1 ? 0 : ((int64_t(1) << 32) + Lb - 1) / Lb;
+        // bins of whole 256-element rounds of a 1024-element piece
+        rbins[t] = (Lb == 256 || Lb == 512 || Lb == 1024) ? Lb / 256 : 0;
         // the multiply-high bin index must equal e / L on every offset
         for (int64_t e = 0; e < plen[t]; ++e)
             if (Lb > 1 && int64_t((uint64_t(e) * uint64_t(magic[t])) >> 32) != e / Lb)
@@ -582,6 +585,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->B.gbase = bt + 3 * T1;
     st->B.pcap = bt + 4 * T1;
     st->B.slbase = bt + 5 * T1;
+    st->B.rbins = bt + 6 * T1;
     int64_t* at = reinterpret_cast<int64_t*>(ws + p.off_astab);
     st->A.slines = at;
     st->A.sbase = at + T1;

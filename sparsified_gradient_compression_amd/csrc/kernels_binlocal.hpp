@@ -52,6 +52,7 @@ struct DevBins {
     const int64_t* gbase;  // [T+1] first prefix group of each tensor
     const int64_t* pcap;   // [T] slots per piece
     const int64_t* slbase; // [T] first slot of each tensor (16-byte slots)
+    const int64_t* rbins;  // [T] rounds per bin when L is 256, 512 or 1024, else 0
     PieceDesc* pdesc;      // [pieces]
     uint32_t* cnt;         // [pieces] salient entries of each piece
     uint32_t* pre;         // [pieces] exclusive prefix inside its group
@@ -85,13 +86,44 @@ __device__ __forceinline__ uint32_t bl_off(int i, int c, int lane) {
 
 // Salient flags of one piece of len elements.  vn / un hold v and u after
 // the update (anything for elements past len).  th is this wave's 1024-entry
-// LDS row.
+// LDS row.  rb > 0 (aligned pieces of bins of 256, 512 or 1024 elements):
+// every bin is rb whole rounds of the float4 layout, so the bin maxima are
+// wave reductions of the rounds and no LDS is used.
 template <bool kAligned>
 __device__ __forceinline__ void bl_flags(const float (&vn)[kRounds][4],
                                          const float (&un)[kRounds][4],
-                                         uint32_t len, uint32_t magic,
+                                         uint32_t len, uint32_t magic, uint32_t rb,
                                          uint32_t* th, bool (&f)[kRounds][4]) {
     const int lane = lane_id();
+    if (kAligned && rb) {  // uniform
+        uint32_t rmax[kRounds];
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (bl_off<true>(i, c, lane) < len) m = max(m, mag_key(vn[i][c]));
+#pragma unroll
+            for (int d = kWave / 2; d >= 1; d >>= 1)
+                m = max(m, uint32_t(__shfl_xor(int(m), d, kWave)));
+            rmax[i] = m;
+        }
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i) {
+            const int b0 = i / int(rb) * int(rb);
+            uint32_t theta = 0;
+#pragma unroll
+            for (int j = 0; j < kRounds; ++j)
+                if (j >= b0 && j < b0 + int(rb)) theta = max(theta, rmax[j]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t key = mag_key(vn[i][c]);
+                const uint32_t ahead = mag_key(__fadd_rn(vn[i][c], un[i][c]));
+                f[i][c] = bl_off<true>(i, c, lane) < len && key != 0u && ahead >= theta;
+            }
+        }
+        return;
+    }
     uint4* th4 = reinterpret_cast<uint4*>(th);
     wave_lds_sync();  // after any reads of the row for a previous piece
 #pragma unroll
@@ -152,10 +184,11 @@ __device__ __forceinline__ void bl_flags(const float (&vn)[kRounds][4],
 template <bool kAligned, int kSel>
 __device__ __forceinline__ void sel_flags(const float (&vn)[kRounds][4],
                                           const float (&un)[kRounds][4],
-                                          uint32_t len, uint32_t magic, uint32_t theta,
-                                          uint32_t* th, bool (&f)[kRounds][4]) {
+                                          uint32_t len, uint32_t magic, uint32_t rb,
+                                          uint32_t theta, uint32_t* th,
+                                          bool (&f)[kRounds][4]) {
     if constexpr (kSel == kSelBins) {
-        bl_flags<kAligned>(vn, un, len, magic, th, f);
+        bl_flags<kAligned>(vn, un, len, magic, rb, th, f);
     } else {
         const int lane = lane_id();
 #pragma unroll
@@ -242,12 +275,13 @@ __device__ __forceinline__ void bl_fused_piece(
         }
     }
     const uint32_t magic = uint32_t(B.magic[t]);
+    const uint32_t rb = kSel == kSelBins ? uint32_t(B.rbins[t]) : 0u;
     const uint32_t theta = kSel == kSelThresh ? ts[t].lo_key : 0u;
     const int64_t o = L.o[t];
     const uint32_t pcap = min(uint32_t(B.pcap[t]), pcap_limit);
     bool f[kRounds][4];
     uint32_t rank[kRounds][4];
-    sel_flags<kAligned, kSel>(vn, un, len, magic, theta, th, f);
+    sel_flags<kAligned, kSel>(vn, un, len, magic, rb, theta, th, f);
     const uint32_t total = bl_ranks<kAligned>(f, rank);
     // the slots keep u and v as they were, so masking here can be undone
     const bool early = total <= pcap;
@@ -395,8 +429,9 @@ __global__ __launch_bounds__(kBlock) void k_bl_tscan(DevK K, DevBins B,
 template <bool kAligned, int kSel>
 __device__ __forceinline__ void bl_redo_piece(
     float* __restrict__ u, float* __restrict__ v, int64_t e0, uint32_t len,
-    uint32_t magic, uint32_t theta, int64_t o, int64_t pos0, int64_t nd, int64_t obase,
-    uint32_t* __restrict__ out_idx, float* __restrict__ out_val, uint32_t* th) {
+    uint32_t magic, uint32_t rb, uint32_t theta, int64_t o, int64_t pos0, int64_t nd,
+    int64_t obase, uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
+    uint32_t* th) {
     const int lane = lane_id();
     const int64_t e1 = e0 + len;
     float un[kRounds][4], vn[kRounds][4];
@@ -410,7 +445,7 @@ __device__ __forceinline__ void bl_redo_piece(
         }
     bool f[kRounds][4];
     uint32_t rank[kRounds][4];
-    sel_flags<kAligned, kSel>(vn, un, len, magic, theta, th, f);
+    sel_flags<kAligned, kSel>(vn, un, len, magic, rb, theta, th, f);
     (void)bl_ranks<kAligned>(f, rank);
 #pragma unroll
     for (int i = 0; i < kRounds; ++i)
@@ -519,12 +554,13 @@ __global__ __launch_bounds__(kBlock) void k_bl_gather(
         const int64_t ndj = int64_t(uint32_t(__shfl(int(nd), j, kWave)));
         const int64_t oj = L.o[t];
         const uint32_t theta = kSel == kSelThresh ? ts[t].lo_key : 0u;
+        const uint32_t rb = kSel == kSelBins ? uint32_t(B.rbins[t]) : 0u;
         if ((d.start & 3) == 0)
-            bl_redo_piece<true, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), theta, oj,
-                                      0, ndj, ob, out_idx, out_val, row);
+            bl_redo_piece<true, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), rb, theta,
+                                      oj, 0, ndj, ob, out_idx, out_val, row);
         else
-            bl_redo_piece<false, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), theta, oj,
-                                       0, ndj, ob, out_idx, out_val, row);
+            bl_redo_piece<false, kSel>(u, v, d.start, d.len, uint32_t(B.magic[t]), rb, theta,
+                                       oj, 0, ndj, ob, out_idx, out_val, row);
     }
 }
 

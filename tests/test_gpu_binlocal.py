@@ -140,7 +140,7 @@ def run(sizes, Ls, caps, grads, clip, learners=1, path=0, k_max=None, tag=""):
 # ---------------------------------------------------------------- workloads
 
 @pytest.mark.parametrize("path", [0, 1])
-@pytest.mark.parametrize("L", [1, 3, 50, 64, 500, 1000, 1024])
+@pytest.mark.parametrize("L", [1, 3, 50, 64, 256, 500, 512, 1000, 1024])
 def test_flat1m_bin_lengths(L, path):
     """One 2**20 tensor, Laplace gradients, two steps, no truncation."""
     wl = W.get("flat1m")
