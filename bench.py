@@ -230,7 +230,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU exchange is not part of this build)", file=sys.stderr)
+              "(the multi-GPU exchange of the streams is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparsified_gradient_compression_amd import dgc
