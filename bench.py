@@ -223,7 +223,30 @@ def cpu_baseline(wl, host_samples, n_chunks, seconds):
                    f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
                    "momentum, exact top-k, mask, encode, decode; "
                    f"{dt:.1f} s"),
+        "single_thread": single_thread(wl, host_samples[0][:wl.sizes[0]], k[:1]),
     }
+
+
+def single_thread(wl, g, k):
+    """The oracle on one thread: one learner-step of the first tensor."""
+    import oracle
+    cores = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        n = g.size
+        u = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+        t0 = time.perf_counter()
+        idx, val, _, _ = oracle.step(np.array([n], np.int64), np.array(k), g, u, v,
+                                     wl.momentum, wl.clip)
+        r, vv = oracle.encode(idx, val)
+        dense = np.zeros(n, np.float32)
+        oracle.decode_accumulate(r, vv, dense)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(n / dt / 1e9, 4), "unit": "G elem/s", "cores": 1,
+            "sample": f"one step of the first tensor ({n} elements), {dt:.2f} s"}
 
 
 def main():
@@ -434,6 +457,9 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": fused_bytes,
             "avg_launch_ms": round(fused_ms, 4),
+            # HBM bytes the counters saw per launch over this run's launch time
+            "traffic_GBps": (round(traffic / (fused_ms * 1e-3) / 1e9, 1)
+                             if traffic else None),
         },
         "detail": {
             "compress_ms_per_learner_step": round(compress_ms, 4),

@@ -26,6 +26,7 @@ from .c_oracle import (  # noqa: F401
     k_for_density,
     step,
     num_threads,
+    set_num_threads,
     binlocal_select_mask,
     binlocal_step,
     fmix32,

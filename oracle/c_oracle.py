@@ -47,6 +47,8 @@ def load():
     P = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     lib.orc_clip_scale.argtypes = [P, i64, ctypes.c_double, P, P]
     lib.orc_clip_scale.restype = ctypes.c_int
     lib.orc_momentum.argtypes = [P, i64, ctypes.c_float, ctypes.c_float, P, P]
@@ -90,6 +92,10 @@ def _ptr(a, dtype):
 
 def num_threads():
     return int(load().orc_num_threads())
+
+
+def set_num_threads(n):
+    load().orc_set_num_threads(int(n))
 
 
 def clip_scale(g, clip):

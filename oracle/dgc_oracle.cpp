@@ -70,6 +70,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Set the number of OpenMP threads for later calls (no effect without
+ * OpenMP).  Results do not depend on it. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Local gradient clipping (DGC review, "Proposed method": clipping bounds the
  * gradient locally, on each learner).  One norm over the learner's whole
