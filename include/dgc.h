@@ -87,9 +87,14 @@ typedef struct dgc_state dgc_state;
  * Workspace size for a layout.
  *   n_tensors  number of tensors T >= 1
  *   sizes      host int64[T], element counts n_t, 0 <= n_t < 2^32
- *   k_max      host int64[T], the largest k_t that dgc_compress will be
- *              given for tensor t (0 <= k_max[t] <= n_t); it sizes the
- *              candidate buffers and the encoded stream capacity
+ *   k_max      host int64[T], the largest k_t that dgc_compress, or the
+ *              largest cap[t] that dgc_compress_binlocal / dgc_compress_sampled,
+ *              will be given for tensor t (0 <= k_max[t] <= n_t); it sizes the
+ *              candidate buffers and the encoded stream capacity.  The
+ *              bin-local and sampled passes share the candidate slots out
+ *              among their pieces: a k_max well below the entries a piece
+ *              sends makes that piece take the slower re-derivation (same
+ *              results)
  *   bytes      out: bytes of device workspace dgc_init_state needs
  * Returns DGC_OK or DGC_EINVAL.
  */
