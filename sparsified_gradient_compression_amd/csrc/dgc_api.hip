@@ -60,7 +60,7 @@ struct Plan {
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
            off_runc = 0, off_gmap = 0, off_gsum = 0, off_goff = 0, off_atiles = 0, off_aoff = 0,
            off_scratch = 0,
-           off_amap = 0, off_slots = 0, off_olist = 0,
+           off_amap = 0, off_slots = 0, off_slotu = 0, off_olist = 0, off_olistu = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
            off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, off_dtab = 0,
@@ -204,7 +204,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_aoff = take(T1 * 4);
     p.off_amap = take(size_t(p.TT) * 4);
     p.off_slots = take(size_t(p.SL) * 8);
+    p.off_slotu = take(size_t(p.SL) * 4);
     p.off_olist = take(size_t(p.A) * 8);
+    p.off_olistu = take(size_t(p.A) * 4);
     p.off_ta = take(size_t(p.tiles) * 4);
     p.off_tb = take(size_t(p.tiles) * 4);
     p.off_tc = take(size_t(p.tiles) * 4);
@@ -276,6 +278,7 @@ struct dgc_state {
              *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
              *tc = nullptr;
     uint2 *slots = nullptr, *olist = nullptr;
+    float *slot_u = nullptr, *olist_u = nullptr;  // u saved with each candidate
     uint64_t* t64 = nullptr;
     double* partial = nullptr;
 };
@@ -573,6 +576,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->amap = reinterpret_cast<uint32_t*>(ws + p.off_amap);
     st->slots = reinterpret_cast<uint2*>(ws + p.off_slots);
     st->olist = reinterpret_cast<uint2*>(ws + p.off_olist);
+    st->slot_u = reinterpret_cast<float*>(ws + p.off_slotu);
+    st->olist_u = reinterpret_cast<float*>(ws + p.off_olistu);
     st->ta = reinterpret_cast<uint32_t*>(ws + p.off_ta);
     st->tb = reinterpret_cast<uint32_t*>(ws + p.off_tb);
     st->tc = reinterpret_cast<uint32_t*>(ws + p.off_tc);
@@ -709,7 +714,7 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
             g, st->u, st->v, st->L, st->ts, st->sc, clip_on, st->m, st->slots,
-            st->run_cnt, p.P, out_norm, out_scale);
+            st->slot_u, st->run_cnt, p.P, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
@@ -719,8 +724,9 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
                                            st->atiles);
     if (p.G > 0)
-        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots, st->run_cnt,
-                                                  st->goff, st->olist);
+        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots, st->slot_u,
+                                                  st->run_cnt, st->goff, st->olist,
+                                                  st->olist_u, st->u, st->v);
     k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
     k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
     DGC_LAUNCH_CHECK();
@@ -740,8 +746,9 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
                                                 st->amap, st->aoff, st->ta);
         k_emit_scan<<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
         k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
-                                                st->olist, st->amap, st->aoff, st->tb,
-                                                st->tc, out_idx, out_val, st->sc);
+                                                st->olist, st->olist_u, st->amap,
+                                                st->aoff, st->tb, st->tc, out_idx,
+                                                out_val, st->sc);
         DGC_LAUNCH_CHECK();
     }
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));

@@ -34,7 +34,7 @@ constexpr int64_t kGroup = 256;
 #endif
 constexpr int kTileShift = DGC_TILE_SHIFT;
 constexpr int64_t kTile = int64_t(1) << kTileShift;
-constexpr int kPerThread = int(kTile / kBlock);  // 16
+constexpr int kPerThread = int(kTile / kBlock);
 
 // Radix select on the 31-bit magnitude key: digits of 11, 10, 10 bits.
 constexpr int kBins0 = 2048;

@@ -26,28 +26,34 @@ __device__ __forceinline__ void st_stream(float* p, float a, float b, float c, f
 
 // Element-wise momentum correction + accumulation, and candidate output.
 // A wave owns one piece (<= 1024 elements, one tensor).  It loads g, u, v
-// as float4 (64 lanes x 4 units), updates u and v in registers and stores
-// them, then writes the piece's candidates (key >= lo) as one run in index
-// order into the piece's own pcap slots: ballot + popcount give each
-// candidate its rank; no atomics, so the layout is the same every run.
-// The loads depend only on the piece descriptor; the tensor's metadata is
-// read while they are in flight.
+// as float4 (64 lanes x 4 units) and updates u and v in registers; each
+// candidate (key >= lo) gets its rank in index order by ballot + popcount
+// (no atomics, so the layout is the same every run).  When the piece's
+// candidates fit its pcap slots, they are masked optimistically: u and v
+// are stored as +0 there, and the slots keep what the zeros replaced
+// (index and v in `slots`, u in `slot_u`).  The selection later puts back
+// the candidates it does not send, so the scattered masking writes shrink
+// to the few candidates outside the top k.  A piece with more candidates
+// than slots stores u and v unmasked and writes no slots; its count above
+// pcap sends the tensor to the dense path.  The loads depend only on the
+// piece descriptor; the tensor's metadata is read while they are in flight.
 template <bool kAligned>
 __device__ __forceinline__ void fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     int64_t e0, int64_t e1, int t, const DevLayout& L,
     const TensorState* __restrict__ ts, float s, float m,
-    uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt, int64_t p) {
+    uint2* __restrict__ slots, float* __restrict__ slot_u,
+    uint32_t* __restrict__ run_cnt, int64_t p) {
     const int lane = lane_id();
-    float vn[kRounds][4];
+    float un[kRounds][4], vn[kRounds][4];
     bool f[kRounds][4];
+    bool full[kRounds];
     uint32_t lo;
-    int64_t o;
+    int64_t o, pcap;
     if (kAligned) {
         // e0 is a multiple of 4: 64 * kRounds float4 units cover the piece.
         const int64_t ubase = e0 >> 2;
         float4 gv[kRounds], uv[kRounds], vv[kRounds];
-        bool full[kRounds];
 #pragma unroll
         for (int i = 0; i < kRounds; ++i) {
             int64_t el = (ubase + i * kWave + lane) << 2;
@@ -69,6 +75,7 @@ __device__ __forceinline__ void fused_piece(
         }
         lo = ts[t].lo_key;
         o = L.o[t];
+        pcap = L.pcap[t];
 #pragma unroll
         for (int i = 0; i < kRounds; ++i) {
             int64_t el = (ubase + i * kWave + lane) << 2;
@@ -78,16 +85,9 @@ __device__ __forceinline__ void fused_piece(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 momentum_update(gg[c], s, m, uu[c], vv4[c]);
+                un[i][c] = uu[c];
                 vn[i][c] = vv4[c];
                 f[i][c] = (el + c < e1) && mag_key(vv4[c]) >= lo;
-            }
-            if (full[i]) {
-                st_stream(u + el, uu[0], uu[1], uu[2], uu[3]);
-                st_stream(v + el, vv4[0], vv4[1], vv4[2], vv4[3]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (el + c < e1) { u[el + c] = uu[c]; v[el + c] = vv4[c]; }
             }
         }
     } else {
@@ -97,8 +97,10 @@ __device__ __forceinline__ void fused_piece(
         // follow (i, c, lane) order, which is index order here.
         lo = ts[t].lo_key;
         o = L.o[t];
+        pcap = L.pcap[t];
 #pragma unroll
         for (int i = 0; i < kRounds; ++i) {
+            full[i] = false;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 int64_t el = e0 + int64_t(i * 4 + c) * kWave + lane;
@@ -106,7 +108,7 @@ __device__ __forceinline__ void fused_piece(
                 float gg = ok ? g[el] : 0.f, uu = ok ? u[el] : 0.f,
                       vv = ok ? v[el] : 0.f;
                 momentum_update(gg, s, m, uu, vv);
-                if (ok) { u[el] = uu; v[el] = vv; }
+                un[i][c] = uu;
                 vn[i][c] = vv;
                 f[i][c] = ok && mag_key(vv) >= lo;
             }
@@ -143,21 +145,52 @@ __device__ __forceinline__ void fused_piece(
             }
         }
     }
+    // Masked stores: a candidate is stored as +0 when the piece's run fits.
+    const bool fits = total <= uint32_t(pcap);  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+        float su[4], sv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool z = fits && f[i][c];
+            su[c] = z ? 0.0f : un[i][c];
+            sv[c] = z ? 0.0f : vn[i][c];
+        }
+        if (kAligned) {
+            int64_t el = ((e0 >> 2) + i * kWave + lane) << 2;
+            if (full[i]) {
+                st_stream(u + el, su[0], su[1], su[2], su[3]);
+                st_stream(v + el, sv[0], sv[1], sv[2], sv[3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (el + c < e1) { u[el + c] = su[c]; v[el + c] = sv[c]; }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                int64_t el = e0 + int64_t(i * 4 + c) * kWave + lane;
+                if (el < e1) { u[el] = su[c]; v[el] = sv[c]; }
+            }
+        }
+    }
     // The piece's run goes to its own pcap slots; a count above pcap marks
     // the overflow (the tensor then takes the dense path).
     if (lane == 0) run_cnt[p] = total;
-    if (total) {
-        const uint32_t pcap = uint32_t(L.pcap[t]);
-        uint2* sl = slots + L.slbase[t] + (p - L.pbase[t]) * int64_t(pcap);
+    if (total && fits) {
+        const int64_t sb = L.slbase[t] + (p - L.pbase[t]) * pcap;
+        uint2* sl = slots + sb;
+        float* sul = slot_u + sb;
         const int64_t unit0 = e0 >> 2;
 #pragma unroll
         for (int i = 0; i < kRounds; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (f[i][c] && rank[i][c] < pcap) {
+                if (f[i][c]) {
                     int64_t el = kAligned ? (((unit0 + i * kWave + lane) << 2) + c)
                                           : (e0 + int64_t(i * 4 + c) * kWave + lane);
                     sl[rank[i][c]] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
+                    sul[rank[i][c]] = un[i][c];
                 }
     }
 }
@@ -167,8 +200,8 @@ __device__ __forceinline__ void fused_piece(
 __global__ __launch_bounds__(kBlock) void k_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     DevLayout L, const TensorState* __restrict__ ts, Scalars* __restrict__ sc,
-    int clip_on, float m, uint2* __restrict__ slots, uint32_t* __restrict__ run_cnt,
-    int64_t n_pieces, double* __restrict__ out_norm, float* __restrict__ out_scale) {
+    int clip_on, float m, uint2* __restrict__ slots, float* __restrict__ slot_u,
+    uint32_t* __restrict__ run_cnt, int64_t n_pieces, double* __restrict__ out_norm, float* __restrict__ out_scale) {
     const float s = clip_on ? sc->scale : 1.0f;
     if (!clip_on && blockIdx.x == 0 && threadIdx.x == 0) {
         sc->norm = -1.0;
@@ -184,9 +217,9 @@ __global__ __launch_bounds__(kBlock) void k_fused(
         const int64_t e0 = d.start;
         const int64_t e1 = e0 + d.len;
         if ((e0 & 3) == 0)
-            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
+            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, slot_u, run_cnt, p);
         else
-            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
+            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, slot_u, run_cnt, p);
     }
 }
 

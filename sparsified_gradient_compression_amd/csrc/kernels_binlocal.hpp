@@ -286,17 +286,6 @@ __device__ __forceinline__ void bl_fused_piece(
     // the slots keep u and v as they were, so masking here can be undone
     const bool early = total <= pcap;
     if (lane == 0) B.cnt[p] = total;
-    if (total && early) {
-        uint4* sl = slots + B.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
-#pragma unroll
-        for (int i = 0; i < kRounds; ++i)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (f[i][c])
-                    sl[rank[i][c]] = make_uint4(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
-                                                __float_as_uint(vn[i][c]),
-                                                __float_as_uint(un[i][c]), 0u);
-    }
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
         float uu[4], vv[4];
@@ -323,6 +312,17 @@ __device__ __forceinline__ void bl_fused_piece(
                 if (el < e1) { u[el] = uu[c]; v[el] = vv[c]; }
             }
         }
+    }
+    if (total && early) {
+        uint4* sl = slots + B.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (f[i][c])
+                    sl[rank[i][c]] = make_uint4(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
+                                                __float_as_uint(vn[i][c]),
+                                                __float_as_uint(un[i][c]), 0u);
     }
 }
 

@@ -313,42 +313,72 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
     }
 }
 
-// One block per group: concatenate the group's piece runs into the tensor's
-// index-ordered candidate list.  Threads walk the group's output positions
-// (coalesced writes) and find each one's piece by binary search over the
-// in-group prefix of the run lengths.
+// One block per group.  The fused pass masked the candidates of every piece
+// whose run fit its slots (u = v = +0 there; the slots hold the index, v
+// and u).  For a tensor on the list path, concatenate the group's piece
+// runs, with their saved u, into the tensor's index-ordered candidate list.
+// For any other tensor, put the slotted u and v back, so the dense path
+// reads the true values.  Threads walk the group's items (coalesced
+// accesses) and find each one's piece by binary search over the in-group
+// prefix of the run lengths.
 __global__ __launch_bounds__(kBlock) void k_gather(
     DevLayout L, const TensorState* __restrict__ ts,
-    const uint2* __restrict__ slots, const uint32_t* __restrict__ run_cnt,
-    const uint32_t* __restrict__ goff, uint2* __restrict__ olist) {
+    const uint2* __restrict__ slots, const float* __restrict__ slot_u,
+    const uint32_t* __restrict__ run_cnt, const uint32_t* __restrict__ goff,
+    uint2* __restrict__ olist, float* __restrict__ olist_u,
+    float* __restrict__ u, float* __restrict__ v) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t pre[kGroup + 1];
     const int64_t g = blockIdx.x;
     const int t = int(L.gmap[g]);
-    if (ts[t].mode != kModeList) return;  // uniform
+    const bool list = ts[t].mode == kModeList;  // uniform
     const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
     const int64_t np = min(kGroup, L.pbase[t + 1] - p0);  // signed: >= 1 here
     if (np <= 0) return;  // uniform; cannot happen with a valid group map
     const int tid = int(threadIdx.x);
-    const uint32_t c = tid < np ? run_cnt[p0 + tid] : 0u;
+    const int64_t pcap = L.pcap[t];
+    uint32_t c = tid < np ? run_cnt[p0 + tid] : 0u;
+    if (c > uint32_t(pcap)) c = 0;  // overflowed: no slots, nothing masked
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan(c, lds, tot);
     pre[threadIdx.x] = ex;
     if (threadIdx.x == 0) pre[kGroup] = tot;
     __syncthreads();
-    const int64_t pcap = L.pcap[t];
-    const uint2* src0 = slots + L.slbase[t] + (p0 - L.pbase[t]) * pcap;
-    // the list path guarantees this; it is checked so that no write can
-    // leave the tensor's list whatever the counts say
-    if (int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
-    uint2* dst = olist + L.obase[t] + goff[g];
-    for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
-        int lo = 0, hi = int(np);  // largest j < np with pre[j] <= q
-        while (hi - lo > 1) {
-            int mid = (lo + hi) >> 1;
-            if (pre[mid] <= q) lo = mid; else hi = mid;
+    if (tot == 0) return;  // uniform
+    const int64_t sb = L.slbase[t] + (p0 - L.pbase[t]) * pcap;
+    const uint2* src0 = slots + sb;
+    const float* su0 = slot_u + sb;
+    if (list) {
+        // the list path guarantees this; it is checked so that no write can
+        // leave the tensor's list whatever the counts say
+        if (int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
+        uint2* dst = olist + L.obase[t] + goff[g];
+        float* du = olist_u + L.obase[t] + goff[g];
+        for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
+            int lo = 0, hi = int(np);  // largest j < np with pre[j] <= q
+            while (hi - lo > 1) {
+                int mid = (lo + hi) >> 1;
+                if (pre[mid] <= q) lo = mid; else hi = mid;
+            }
+            const int64_t j = int64_t(lo) * pcap + (q - pre[lo]);
+            dst[q] = src0[j];
+            du[q] = su0[j];
         }
-        dst[q] = src0[int64_t(lo) * pcap + (q - pre[lo])];
+    } else {
+        const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+        for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
+            int lo = 0, hi = int(np);
+            while (hi - lo > 1) {
+                int mid = (lo + hi) >> 1;
+                if (pre[mid] <= q) lo = mid; else hi = mid;
+            }
+            const int64_t j = int64_t(lo) * pcap + (q - pre[lo]);
+            const uint2 it = src0[j];
+            if (int64_t(it.x) < nt) {
+                v[o + it.x] = __uint_as_float(it.y);
+                u[o + it.x] = su0[j];
+            }
+        }
     }
 }
 
@@ -563,16 +593,19 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
     }
 }
 
-// Per active tile: write the selected items in index order and mask u, v
-// there.  An item with key > T, or key == T while fewer than r ties precede
-// it, is sent; its output slot is (#sent before it) =
-// gt_before + min(eq_before, r).
+// Per active tile: write the selected items in index order.  An item with
+// key > T, or key == T while fewer than r ties precede it, is sent; its
+// output slot is (#sent before it) = gt_before + min(eq_before, r).  On the
+// dense path the sent items' u and v are masked here; on the list path the
+// fused pass has masked every candidate already, and the candidates not
+// sent get their u and v back.
 __global__ __launch_bounds__(kBlock) void k_emit_write(
     DevLayout L, DevK K, const TensorState* __restrict__ ts,
     float* __restrict__ u, float* __restrict__ v,
-    const uint2* __restrict__ olist, const uint32_t* __restrict__ amap,
-    const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ off_gt,
-    const uint32_t* __restrict__ off_eq, uint32_t* __restrict__ out_idx,
+    const uint2* __restrict__ olist, const float* __restrict__ olist_u,
+    const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
+    const uint32_t* __restrict__ off_gt, const uint32_t* __restrict__ off_eq,
+    uint32_t* __restrict__ out_idx,
     float* __restrict__ out_val, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds2[2 * kWavesPerBlock];
     const uint32_t A = aoff[L.T];
@@ -585,6 +618,8 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
         const int64_t o = L.o[t];
         float* vt_ = v + o;
         const uint2* ol = olist + L.obase[t];
+        const float* olu = olist_u + L.obase[t];
+        const bool dense = mode == kModeDense;
         uint32_t* oi = out_idx + K.koff[t];
         float* ov = out_val + K.koff[t];
         const int64_t kt = K.k[t];
@@ -612,8 +647,17 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
                 } else {
                     oi[slot] = it.x;
                     ov[slot] = __uint_as_float(it.y);
-                    u[o + it.x] = 0.0f;
-                    vt_[it.x] = 0.0f;
+                    if (dense) {
+                        u[o + it.x] = 0.0f;
+                        vt_[it.x] = 0.0f;
+                    }
+                }
+            } else if (ok && !dense) {
+                if (int64_t(it.x) >= nt) {
+                    bad = true;
+                } else {
+                    u[o + it.x] = olu[i];
+                    vt_[it.x] = __uint_as_float(it.y);
                 }
             }
             cg += tg;
