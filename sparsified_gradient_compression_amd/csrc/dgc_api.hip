@@ -60,7 +60,7 @@ struct Plan {
            off_kmap = 0, off_ts = 0, off_sc = 0, off_hist = 0, off_shist = 0,
            off_runc = 0, off_gmap = 0, off_gsum = 0, off_goff = 0, off_atiles = 0, off_aoff = 0,
            off_scratch = 0,
-           off_amap = 0, off_slots = 0, off_slotu = 0, off_olist = 0, off_olistu = 0,
+           off_amap = 0, off_slots = 0, off_olist = 0, off_olistv = 0, off_olistu = 0,
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
            off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, off_dtab = 0,
@@ -203,9 +203,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_atiles = take(size_t(T) * 4);
     p.off_aoff = take(T1 * 4);
     p.off_amap = take(size_t(p.TT) * 4);
-    p.off_slots = take(size_t(p.SL) * 8);
-    p.off_slotu = take(size_t(p.SL) * 4);
-    p.off_olist = take(size_t(p.A) * 8);
+    p.off_slots = take(size_t(p.SL) * sizeof(CandSlot));
+    p.off_olist = take(size_t(p.A) * 4);
+    p.off_olistv = take(size_t(p.A) * 4);
     p.off_olistu = take(size_t(p.A) * 4);
     p.off_ta = take(size_t(p.tiles) * 4);
     p.off_tb = take(size_t(p.tiles) * 4);
@@ -277,8 +277,12 @@ struct dgc_state {
              *run_cnt = nullptr, *gsum = nullptr, *goff = nullptr, *atiles = nullptr,
              *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
              *tc = nullptr;
-    uint2 *slots = nullptr, *olist = nullptr;
-    float *slot_u = nullptr, *olist_u = nullptr;  // u saved with each candidate
+    // exact path: 12-byte candidate slots; the bin-local and sampled passes
+    // read the same region as 16-byte slots
+    CandSlot* slots = nullptr;
+    // the ordered candidate list: local index, v and saved u per item
+    uint32_t* olist_i = nullptr;
+    float *olist_v = nullptr, *olist_u = nullptr;
     uint64_t* t64 = nullptr;
     double* partial = nullptr;
 };
@@ -434,11 +438,12 @@ int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
         const int64_t np_ = cdiv(n, plen[t]);
         pbase[t + 1] = pbase[t] + np_;
         gbase[t + 1] = gbase[t] + cdiv(np_, kBlGroup);
-        // the tensor's 8-byte candidate slots, taken as 16-byte slots
-        // {index, v, u, 0} and shared out among its pieces
-        slb[t] = (p.slbase[size_t(t)] + 1) / 2;
+        // the tensor's 12-byte candidate slots, taken as 16-byte slots
+        // {index, v, u, 0} and shared out among its pieces: the 16-byte
+        // units that lie wholly inside bytes [12 slbase[t], 12 slbase[t+1])
+        slb[t] = (3 * p.slbase[size_t(t)] + 3) / 4;
         const int64_t region =
-            std::max<int64_t>(0, p.slbase[size_t(t) + 1] / 2 - slb[t]);
+            std::max<int64_t>(0, 3 * p.slbase[size_t(t) + 1] / 4 - slb[t]);
         pcap[t] = np_ ? std::min<int64_t>(plen[t], region / np_) : 0;
     }
     if (pbase[T] > p.BP || gbase[T] > p.BG) return DGC_EINVAL;
@@ -574,9 +579,9 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->atiles = reinterpret_cast<uint32_t*>(ws + p.off_atiles);
     st->aoff = reinterpret_cast<uint32_t*>(ws + p.off_aoff);
     st->amap = reinterpret_cast<uint32_t*>(ws + p.off_amap);
-    st->slots = reinterpret_cast<uint2*>(ws + p.off_slots);
-    st->olist = reinterpret_cast<uint2*>(ws + p.off_olist);
-    st->slot_u = reinterpret_cast<float*>(ws + p.off_slotu);
+    st->slots = reinterpret_cast<CandSlot*>(ws + p.off_slots);
+    st->olist_i = reinterpret_cast<uint32_t*>(ws + p.off_olist);
+    st->olist_v = reinterpret_cast<float*>(ws + p.off_olistv);
     st->olist_u = reinterpret_cast<float*>(ws + p.off_olistu);
     st->ta = reinterpret_cast<uint32_t*>(ws + p.off_ta);
     st->tb = reinterpret_cast<uint32_t*>(ws + p.off_tb);
@@ -714,7 +719,7 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
             g, st->u, st->v, st->L, st->ts, st->sc, clip_on, st->m, st->slots,
-            st->slot_u, st->run_cnt, p.P, out_norm, out_scale);
+            st->run_cnt, p.P, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
@@ -724,29 +729,29 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
                                            st->atiles);
     if (p.G > 0)
-        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots, st->slot_u,
-                                                  st->run_cnt, st->goff, st->olist,
-                                                  st->olist_u, st->u, st->v);
+        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
+                                                  st->run_cnt, st->goff, st->olist_i,
+                                                  st->olist_v, st->olist_u, st->u, st->v);
     k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
     k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
     DGC_LAUNCH_CHECK();
     if (K > 0) {
         const int hg = grid_for(p.TT, pg);
-        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
+        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
                                              st->aoff, st->hist);
         k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
+        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
                                              st->aoff, st->hist);
         k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist, st->amap,
+        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
                                              st->aoff, st->hist);
         k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
         DGC_LAUNCH_CHECK();
-        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist,
+        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v,
                                                 st->amap, st->aoff, st->ta);
         k_emit_scan<<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
         k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
-                                                st->olist, st->olist_u, st->amap,
+                                                st->olist_i, st->olist_v, st->olist_u, st->amap,
                                                 st->aoff, st->tb, st->tc, out_idx,
                                                 out_val, st->sc);
         DGC_LAUNCH_CHECK();

@@ -95,6 +95,16 @@ struct PieceDesc {
     uint32_t len;
 };
 
+// A candidate of the exact path's element-wise pass: local index, v, and
+// the u that the candidate's masking replaced (12 bytes, one piece's slots
+// contiguous).
+struct CandSlot {
+    uint32_t idx;
+    float v;
+    float u;
+};
+static_assert(sizeof(CandSlot) == 12, "12-byte candidate slots");
+
 // Layout tables (device pointers into the workspace), passed by value.
 struct DevLayout {
     int32_t T;

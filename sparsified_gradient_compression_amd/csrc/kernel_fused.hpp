@@ -30,8 +30,8 @@ __device__ __forceinline__ void st_stream(float* p, float a, float b, float c, f
 // candidate (key >= lo) gets its rank in index order by ballot + popcount
 // (no atomics, so the layout is the same every run).  When the piece's
 // candidates fit its pcap slots, they are masked optimistically: u and v
-// are stored as +0 there, and the slots keep what the zeros replaced
-// (index and v in `slots`, u in `slot_u`).  The selection later puts back
+// are stored as +0 there, and each candidate's slot keeps what the zeros
+// replaced (index, v, u).  The selection later puts back
 // the candidates it does not send, so the scattered masking writes shrink
 // to the few candidates outside the top k.  A piece with more candidates
 // than slots stores u and v unmasked and writes no slots; its count above
@@ -42,8 +42,7 @@ __device__ __forceinline__ void fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     int64_t e0, int64_t e1, int t, const DevLayout& L,
     const TensorState* __restrict__ ts, float s, float m,
-    uint2* __restrict__ slots, float* __restrict__ slot_u,
-    uint32_t* __restrict__ run_cnt, int64_t p) {
+    CandSlot* __restrict__ slots, uint32_t* __restrict__ run_cnt, int64_t p) {
     const int lane = lane_id();
     float un[kRounds][4], vn[kRounds][4];
     bool f[kRounds][4];
@@ -178,9 +177,7 @@ __device__ __forceinline__ void fused_piece(
     // the overflow (the tensor then takes the dense path).
     if (lane == 0) run_cnt[p] = total;
     if (total && fits) {
-        const int64_t sb = L.slbase[t] + (p - L.pbase[t]) * pcap;
-        uint2* sl = slots + sb;
-        float* sul = slot_u + sb;
+        CandSlot* sl = slots + L.slbase[t] + (p - L.pbase[t]) * pcap;
         const int64_t unit0 = e0 >> 2;
 #pragma unroll
         for (int i = 0; i < kRounds; ++i)
@@ -189,8 +186,11 @@ __device__ __forceinline__ void fused_piece(
                 if (f[i][c]) {
                     int64_t el = kAligned ? (((unit0 + i * kWave + lane) << 2) + c)
                                           : (e0 + int64_t(i * 4 + c) * kWave + lane);
-                    sl[rank[i][c]] = make_uint2(uint32_t(el - o), __float_as_uint(vn[i][c]));
-                    sul[rank[i][c]] = un[i][c];
+                    CandSlot cs;
+                    cs.idx = uint32_t(el - o);
+                    cs.v = vn[i][c];
+                    cs.u = un[i][c];
+                    sl[rank[i][c]] = cs;
                 }
     }
 }
@@ -200,8 +200,8 @@ __device__ __forceinline__ void fused_piece(
 __global__ __launch_bounds__(kBlock) void k_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     DevLayout L, const TensorState* __restrict__ ts, Scalars* __restrict__ sc,
-    int clip_on, float m, uint2* __restrict__ slots, float* __restrict__ slot_u,
-    uint32_t* __restrict__ run_cnt, int64_t n_pieces, double* __restrict__ out_norm, float* __restrict__ out_scale) {
+    int clip_on, float m, CandSlot* __restrict__ slots, uint32_t* __restrict__ run_cnt,
+    int64_t n_pieces, double* __restrict__ out_norm, float* __restrict__ out_scale) {
     const float s = clip_on ? sc->scale : 1.0f;
     if (!clip_on && blockIdx.x == 0 && threadIdx.x == 0) {
         sc->norm = -1.0;
@@ -217,9 +217,9 @@ __global__ __launch_bounds__(kBlock) void k_fused(
         const int64_t e0 = d.start;
         const int64_t e1 = e0 + d.len;
         if ((e0 & 3) == 0)
-            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, slot_u, run_cnt, p);
+            fused_piece<true>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
         else
-            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, slot_u, run_cnt, p);
+            fused_piece<false>(g, u, v, e0, e1, t, L, ts, s, m, slots, run_cnt, p);
     }
 }
 

@@ -314,19 +314,21 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
 }
 
 // One block per group.  The fused pass masked the candidates of every piece
-// whose run fit its slots (u = v = +0 there; the slots hold the index, v
+// whose run fit its slots (u = v = +0 there; each slot holds the index, v
 // and u).  For a tensor on the list path, concatenate the group's piece
-// runs, with their saved u, into the tensor's index-ordered candidate list.
+// runs, with their saved u, into the tensor's index-ordered candidate list
+// (three arrays: local index, v, u).
 // For any other tensor, put the slotted u and v back, so the dense path
-// reads the true values.  Threads walk the group's items (coalesced
-// accesses) and find each one's piece by binary search over the in-group
-// prefix of the run lengths.
+// reads the true values.  Accesses are coalesced either way: long runs are
+// copied a piece per wave; for short ones, threads walk the group's items
+// and find each one's piece by binary search over the in-group prefix of
+// the run lengths.
 __global__ __launch_bounds__(kBlock) void k_gather(
     DevLayout L, const TensorState* __restrict__ ts,
-    const uint2* __restrict__ slots, const float* __restrict__ slot_u,
+    const CandSlot* __restrict__ slots,
     const uint32_t* __restrict__ run_cnt, const uint32_t* __restrict__ goff,
-    uint2* __restrict__ olist, float* __restrict__ olist_u,
-    float* __restrict__ u, float* __restrict__ v) {
+    uint32_t* __restrict__ olist_i, float* __restrict__ olist_v,
+    float* __restrict__ olist_u, float* __restrict__ u, float* __restrict__ v) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t pre[kGroup + 1];
     const int64_t g = blockIdx.x;
@@ -345,39 +347,41 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     if (threadIdx.x == 0) pre[kGroup] = tot;
     __syncthreads();
     if (tot == 0) return;  // uniform
-    const int64_t sb = L.slbase[t] + (p0 - L.pbase[t]) * pcap;
-    const uint2* src0 = slots + sb;
-    const float* su0 = slot_u + sb;
-    if (list) {
-        // the list path guarantees this; it is checked so that no write can
-        // leave the tensor's list whatever the counts say
-        if (int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
-        uint2* dst = olist + L.obase[t] + goff[g];
-        float* du = olist_u + L.obase[t] + goff[g];
-        for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
-            int lo = 0, hi = int(np);  // largest j < np with pre[j] <= q
-            while (hi - lo > 1) {
-                int mid = (lo + hi) >> 1;
-                if (pre[mid] <= q) lo = mid; else hi = mid;
-            }
-            const int64_t j = int64_t(lo) * pcap + (q - pre[lo]);
-            dst[q] = src0[j];
-            du[q] = su0[j];
+    const CandSlot* src0 = slots + L.slbase[t] + (p0 - L.pbase[t]) * pcap;
+    const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+    // the list path guarantees this; it is checked so that no write can
+    // leave the tensor's list whatever the counts say
+    if (list && int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
+    const int64_t d0 = list ? L.obase[t] + goff[g] : 0;
+    // item `rank` of piece j, the group's item `pos`
+    auto item = [&](int j, uint32_t rank, uint32_t pos) {
+        const CandSlot it = src0[int64_t(j) * pcap + rank];
+        if (list) {
+            olist_i[d0 + pos] = it.idx;
+            olist_v[d0 + pos] = it.v;
+            olist_u[d0 + pos] = it.u;
+        } else if (int64_t(it.idx) < nt) {
+            v[o + it.idx] = it.v;
+            u[o + it.idx] = it.u;
+        }
+    };
+    if (tot >= 32u * uint32_t(np)) {
+        // long runs: a wave copies one piece's run at a time
+        const int lane = lane_id();
+        for (int j = int(threadIdx.x) >> 6; j < np; j += kWavesPerBlock) {
+            const uint32_t b0 = pre[j], c = pre[j + 1] - b0;
+            for (uint32_t q = lane; q < c; q += kWave) item(j, q, b0 + q);
         }
     } else {
-        const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+        // short runs: threads walk the group's items and find each one's
+        // piece by binary search (largest j < np with pre[j] <= q)
         for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
             int lo = 0, hi = int(np);
             while (hi - lo > 1) {
                 int mid = (lo + hi) >> 1;
                 if (pre[mid] <= q) lo = mid; else hi = mid;
             }
-            const int64_t j = int64_t(lo) * pcap + (q - pre[lo]);
-            const uint2 it = src0[j];
-            if (int64_t(it.x) < nt) {
-                v[o + it.x] = __uint_as_float(it.y);
-                u[o + it.x] = su0[j];
-            }
+            item(lo, q - pre[lo], q);
         }
     }
 }
@@ -409,6 +413,15 @@ __global__ __launch_bounds__(kBlock) void k_active_map(
 
 // ---------------------------------------------------------------- select
 
+// The values of tensor t's selection source: v itself on the dense path,
+// else the candidate list's values (item i of the list is local index
+// olist_i[obase + i]; item i of the dense source is index i).
+__device__ __forceinline__ const float* source_values(uint32_t mode, const float* v,
+                                                      const float* olist_v,
+                                                      const DevLayout& L, int t) {
+    return mode == kModeDense ? v + L.o[t] : olist_v + L.obase[t];
+}
+
 template <int D>
 struct Digit;
 template <> struct Digit<0> { static constexpr int shift = 20, bits = 11; };
@@ -433,7 +446,7 @@ __device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_hist(
     DevLayout L, const TensorState* __restrict__ ts,
-    const float* __restrict__ v, const uint2* __restrict__ olist,
+    const float* __restrict__ v, const float* __restrict__ olist_v,
     const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
     uint32_t* __restrict__ hist) {
     constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
@@ -454,20 +467,11 @@ __global__ __launch_bounds__(kBlock) void k_hist(
         }
         const uint32_t prefix = ts[t].prefix;
         const int64_t i1 = min(len, i0 + kTile);
-        if (mode == kModeDense) {
-            const float* vt_ = v + L.o[t];
-            for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-                uint32_t key = mag_key(vt_[i]);
-                if (D == 0 || (key >> (shift + bits)) == prefix)
-                    atomicAdd(&h[(key >> shift) & dmask], 1u);
-            }
-        } else {
-            const uint2* src = olist + L.obase[t];
-            for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-                uint32_t key = src[i].y & 0x7FFFFFFFu;
-                if (D == 0 || (key >> (shift + bits)) == prefix)
-                    atomicAdd(&h[(key >> shift) & dmask], 1u);
-            }
+        const float* src = source_values(mode, v, olist_v, L, t);
+        for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
+            uint32_t key = mag_key(src[i]);
+            if (D == 0 || (key >> (shift + bits)) == prefix)
+                atomicAdd(&h[(key >> shift) & dmask], 1u);
         }
     }
     if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
@@ -520,20 +524,13 @@ __global__ __launch_bounds__(kBlock) void k_resolve(
 
 // ---------------------------------------------------------------- emit
 
-// Item i of tensor t's source: local index and value bits.
-__device__ __forceinline__ uint2 source_item(uint32_t mode, const float* vt_,
-                                             const uint2* ol, int64_t i) {
-    if (mode == kModeDense) return make_uint2(uint32_t(i), __float_as_uint(vt_[i]));
-    return ol[i];
-}
-
 // Tiles are visited in kPerThread rounds of 256 consecutive items (item
 // i0 + 256 q + tid), so every load and store of a round is coalesced.
 
 // Per active tile: packed (#key > T) << 16 | #key == T.
 __global__ __launch_bounds__(kBlock) void k_emit_count(
     DevLayout L, const TensorState* __restrict__ ts,
-    const float* __restrict__ v, const uint2* __restrict__ olist,
+    const float* __restrict__ v, const float* __restrict__ olist_v,
     const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
     uint32_t* __restrict__ tile_cnt) {
     __shared__ uint32_t lds[kWavesPerBlock];
@@ -544,14 +541,13 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
         const int64_t len = ts[t].len;
         const int64_t i0 = int64_t(a - aoff[t]) * kTile;
         const uint32_t T = ts[t].prefix;
-        const float* vt_ = v + L.o[t];
-        const uint2* ol = olist + L.obase[t];
+        const float* src = source_values(mode, v, olist_v, L, t);
         uint32_t cnt = 0;
 #pragma unroll 4
         for (int q = 0; q < kPerThread; ++q) {
             int64_t i = i0 + q * kBlock + threadIdx.x;
             if (i < len) {
-                uint32_t key = source_item(mode, vt_, ol, i).y & 0x7FFFFFFFu;
+                uint32_t key = mag_key(src[i]);
                 cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
             }
         }
@@ -602,8 +598,9 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
 __global__ __launch_bounds__(kBlock) void k_emit_write(
     DevLayout L, DevK K, const TensorState* __restrict__ ts,
     float* __restrict__ u, float* __restrict__ v,
-    const uint2* __restrict__ olist, const float* __restrict__ olist_u,
-    const uint32_t* __restrict__ amap, const uint32_t* __restrict__ aoff,
+    const uint32_t* __restrict__ olist_i, const float* __restrict__ olist_v,
+    const float* __restrict__ olist_u, const uint32_t* __restrict__ amap,
+    const uint32_t* __restrict__ aoff,
     const uint32_t* __restrict__ off_gt, const uint32_t* __restrict__ off_eq,
     uint32_t* __restrict__ out_idx,
     float* __restrict__ out_val, Scalars* __restrict__ sc) {
@@ -617,21 +614,34 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
         const uint32_t T = ts[t].prefix, r = ts[t].krem;
         const int64_t o = L.o[t];
         float* vt_ = v + o;
-        const uint2* ol = olist + L.obase[t];
-        const float* olu = olist_u + L.obase[t];
         const bool dense = mode == kModeDense;
+        const float* src = source_values(mode, v, olist_v, L, t);
+        const uint32_t* oli = olist_i + L.obase[t];
+        const float* olu = olist_u + L.obase[t];
         uint32_t* oi = out_idx + K.koff[t];
         float* ov = out_val + K.koff[t];
         const int64_t kt = K.k[t];
         const int64_t nt = L.o[t + 1] - o;
         uint32_t cg = off_gt[a], ce = off_eq[a];
         bool bad = false;
+        // every item of the tile is loaded before the first prefix round, so
+        // the rounds' block-wide barriers do not each wait for memory; on
+        // the list path the saved u comes too (the items not sent need it)
+        float val[kPerThread], usv[kPerThread];
+        uint32_t lidx[kPerThread];
+#pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
-            if (i0 + q * kBlock >= len) break;  // uniform
             const int64_t i = i0 + q * kBlock + threadIdx.x;
             const bool ok = i < len;
-            uint2 it = ok ? source_item(mode, vt_, ol, i) : make_uint2(0, 0);
-            const uint32_t key = it.y & 0x7FFFFFFFu;
+            val[q] = ok ? src[i] : 0.0f;
+            lidx[q] = ok ? (dense ? uint32_t(i) : oli[i]) : 0u;
+            usv[q] = ok && !dense ? olu[i] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            if (i0 + q * kBlock >= len) break;  // uniform
+            const bool ok = i0 + q * kBlock + threadIdx.x < len;
+            const uint32_t key = mag_key(val[q]);
             const bool gt = ok && key > T, eq = ok && key == T;
             uint32_t pg, pe, tg, te;
             block_flag_prefix2(gt, eq, lds2, pg, pe, tg, te);
@@ -642,22 +652,22 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
             else if (eq && eb < r) { send = true; slot = gb + eb; }
             if (send) {
                 // never write outside the outputs, whatever the counts say
-                if (int64_t(slot) >= kt || int64_t(it.x) >= nt) {
+                if (int64_t(slot) >= kt || int64_t(lidx[q]) >= nt) {
                     bad = true;
                 } else {
-                    oi[slot] = it.x;
-                    ov[slot] = __uint_as_float(it.y);
+                    oi[slot] = lidx[q];
+                    ov[slot] = val[q];
                     if (dense) {
-                        u[o + it.x] = 0.0f;
-                        vt_[it.x] = 0.0f;
+                        u[o + lidx[q]] = 0.0f;
+                        vt_[lidx[q]] = 0.0f;
                     }
                 }
             } else if (ok && !dense) {
-                if (int64_t(it.x) >= nt) {
+                if (int64_t(lidx[q]) >= nt) {
                     bad = true;
                 } else {
-                    u[o + it.x] = olu[i];
-                    vt_[it.x] = __uint_as_float(it.y);
+                    u[o + lidx[q]] = usv[q];
+                    vt_[lidx[q]] = val[q];
                 }
             }
             cg += tg;

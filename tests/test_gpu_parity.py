@@ -458,6 +458,44 @@ def test_empty_layout():
     assert L.status() == dgc.DGC_OK
 
 
+def test_dense_fallback_after_masking():
+    """The element-wise pass stores the window's candidates as +0 in every
+    piece whose run fits its slots.  A tensor whose candidates then turn out
+    incomplete takes the dense path, and those candidates must get their u
+    and v back before the dense select reads v.  Tensor 0: one piece of
+    large values (more candidates than its slots hold).  Tensor 1: 1% of
+    entries tie at one large magnitude, about 10 per piece (every piece
+    fits) but more than the candidate list holds.  Tensor 2: ordinary data
+    on the list path.  Same bits as the oracle over two steps, the second on
+    ordinary data added to the first step's residual."""
+    rng = np.random.default_rng(77)
+    sizes = [1 << 20, 1 << 22, 300000]
+    k = [1000, 1000, 300]
+    p = Pair(sizes, k)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    sign = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    big = slice(5 * 1024, 6 * 1024)
+    g[big] = rng.uniform(1.0, 2.0, 1024).astype(np.float32) * sign[big]
+    t1 = slice(int(off[1]), int(off[2]))
+    tie = rng.random(sizes[1]) < 0.01
+    g1 = g[t1]
+    g1[tie] = 0.5 * sign[t1][tie]
+    p.step(g, k, 0.0, tag="fallback s0")
+    info = p.learner.select_info()
+    no_window = 0xFFFFFFFF
+    # tensor 0: window used, a piece overflowed, dense path
+    assert info[0, 1] != no_window and info[0, 3] == 1 and info[0, 0] == 2, info[0].tolist()
+    # tensor 1: window used, no piece overflowed, too many candidates: dense
+    assert info[1, 1] != no_window and info[1, 3] == 0 and info[1, 0] == 2, info[1].tolist()
+    assert info[1, 2] > 8 * k[1] + 16384, info[1].tolist()
+    assert info[2, 0] == 1, info[2].tolist()
+    # the residual ties keep tensor 1 on the dense path; state and outputs
+    # must still match
+    p.step(rng.laplace(0, 1e-3, n).astype(np.float32), k, 0.0, tag="fallback s1")
+
+
 @pytest.mark.parametrize("path", [0, 1])
 def test_denormals_and_extremes(path):
     """Denormal and near-overflow magnitudes: keys are bit patterns, so the
