@@ -52,6 +52,7 @@ struct Plan {
     std::vector<int64_t> dbase, bbase;
     int64_t DB = 0, NBLK = 0;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
+    int64_t norm_chunk = 0;
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
@@ -144,7 +145,12 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.S = p.sbase[T];
     p.E = p.ebase[T];
     p.ET = p.etbase[T];
-    p.NB = cdiv(p.n, kNormChunk);
+    // norm chunks: the largest power of two in [2^12, 2^18] that still gives
+    // 256 workgroups (one per CU), so a small gradient still spreads over the
+    // chip (ResNet-50's 25.6M elements: 390 workgroups of 2^16, not 98)
+    p.norm_chunk = kNormChunk;
+    while (p.norm_chunk > kNormChunkMin && p.n / p.norm_chunk < 256) p.norm_chunk >>= 1;
+    p.NB = cdiv(p.n, p.norm_chunk);
     p.AS = p.asbase[T];
     p.DB = p.dbase[T];
     p.NBLK = p.bbase[T];
@@ -694,7 +700,8 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
     if (clip_on) {
-        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                   st->partial);
         k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
                                                out_norm, out_scale);
     } else if (p.P == 0) {
@@ -788,7 +795,8 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
     if (clip_on) {
-        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                   st->partial);
         k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
                                                out_norm, out_scale);
     } else if (st->BP == 0) {
@@ -860,7 +868,8 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
     if (clip_on) {
-        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, st->partial);
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                   st->partial);
         k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
                                                out_norm, out_scale);
     } else if (st->BP == 0) {

@@ -48,7 +48,9 @@ constexpr int64_t kSmallN = 65536;
 constexpr int64_t kMinSampleLines = 512;
 constexpr int64_t kLinesPerSampleBlock = 64;
 
-// Binary64 norm: one workgroup per 2^18 elements, fixed order.
+// Binary64 norm: one workgroup per chunk of 2^12 .. 2^18 elements (a power
+// of two, the largest that still gives 256 workgroups), fixed order.
+constexpr int64_t kNormChunkMin = int64_t(1) << 12;
 constexpr int64_t kNormChunk = int64_t(1) << 18;
 
 // Per-tensor selection modes (decided after the element-wise pass).

@@ -54,15 +54,15 @@ __global__ void k_set_scalars(Scalars* __restrict__ sc, double* __restrict__ out
 
 // ---------------------------------------------------------------- norm
 
-// Block b sums g^2 over [b*kNormChunk, min(n, (b+1)*kNormChunk)) in
-// binary64: thread-strided float4 loads, one accumulator per float4 lane
+// Block b sums g^2 over [b*chunk, min(n, (b+1)*chunk)) in binary64
+// (chunk a multiple of 4): thread-strided float4 loads, one accumulator per float4 lane
 // slot, then a fixed-order block reduction.  The squares of binary32 values
 // are exact in binary64, so only the additions round.
 __global__ __launch_bounds__(kBlock) void k_norm_partial(
-    const float* __restrict__ g, int64_t n, double* __restrict__ partial) {
+    const float* __restrict__ g, int64_t n, int64_t chunk, double* __restrict__ partial) {
     __shared__ double lds[kWavesPerBlock];
-    const int64_t lo = int64_t(blockIdx.x) * kNormChunk;
-    const int64_t hi = min(n, lo + kNormChunk);
+    const int64_t lo = int64_t(blockIdx.x) * chunk;
+    const int64_t hi = min(n, lo + chunk);
     const int64_t vlo = lo >> 2, vhi = hi >> 2;  // whole float4 units
     const float4* g4 = reinterpret_cast<const float4*>(g);
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
