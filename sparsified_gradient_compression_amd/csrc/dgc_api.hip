@@ -53,6 +53,7 @@ struct Plan {
     int64_t DB = 0, NBLK = 0;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t norm_chunk = 0;
+    bool short_sources = true;  // every tensor fits the per-tensor select
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
@@ -137,6 +138,11 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.BG += cdiv(cdiv(n, kBlMinPiece), kBlGroup);
     }
     p.n = p.o[T];
+    for (int32_t t = 0; t < T; ++t) {
+        const int64_t n = sizes[t];
+        const int64_t src = n <= kSmallN ? n : p.obase[t + 1] - p.obase[t];
+        if (n > kPerTensorMaxN || src > kPerTensorMaxItems) p.short_sources = false;
+    }
     p.P = p.pbase[T];
     p.G = p.gbase[T];
     p.TT = p.tbase[T];
@@ -272,6 +278,7 @@ struct dgc_state {
     DevSample A{};
     DevDec Dd{};
     int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged
+    int select_grid = 0;  // 0 automatic, 1 a workgroup per tensor, 2 spread passes
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
     DevBins B{};
     // device views
@@ -739,10 +746,18 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
                                                   st->run_cnt, st->goff, st->olist_i,
                                                   st->olist_v, st->olist_u, st->u, st->v);
-    k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
-    k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
-    DGC_LAUNCH_CHECK();
-    if (K > 0) {
+    // the select and emit: one workgroup per tensor when every selection
+    // source is short, else passes spread over the chip
+    const bool per_tensor = st->select_grid == 1 || (st->select_grid == 0 && p.short_sources);
+    if (K > 0 && per_tensor) {
+        k_select_tensor<<<T, kTsThreads, 0, stream>>>(
+            st->L, st->K, st->ts, st->u, st->v, st->olist_i, st->olist_v, st->olist_u,
+            out_idx, out_val, st->sc);
+        DGC_LAUNCH_CHECK();
+    } else if (K > 0) {
+        k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
+        k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
+        DGC_LAUNCH_CHECK();
         const int hg = grid_for(p.TT, pg);
         k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
                                              st->aoff, st->hist);
@@ -1069,6 +1084,11 @@ int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
     if (option == DGC_OPT_SELECT_PATH) {
         if (value != 0 && value != 1) return DGC_EINVAL;
         st->select_path = int(value);
+        return DGC_OK;
+    }
+    if (option == DGC_OPT_SELECT_GRID) {
+        if (value < 0 || value > 2) return DGC_EINVAL;
+        st->select_grid = int(value);
         return DGC_OK;
     }
     if (option == DGC_OPT_KERNEL_TIMING) {

@@ -677,4 +677,233 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     }
 }
 
+// ---------------------------------------------------------------- per tensor
+
+// The same select and emit for one tensor in one 1024-thread workgroup,
+// for layouts whose selection sources are all short (the host decides): the
+// three digit histograms live in LDS and are resolved in place, and the
+// emit splits the source into 16 index-ordered wave chunks whose counts
+// give each wave its output offsets.  One launch replaces the eleven of
+// the spread passes (active tiles, three histogram and resolve pairs,
+// count, scan, write), whose cost on small layouts is mostly the ~4.7 us
+// each dependent launch takes.  Results and the per-tensor record
+// (prefix = T, krem = r) are the same as the spread passes'.
+constexpr int kTsThreads = 1024;
+// The automatic choice takes the per-tensor workgroup when every tensor's
+// selection source is short: at most kPerTensorMaxItems items (the whole
+// tensor up to kSmallN elements, else the candidate list's capacity), and
+// every tensor at most kPerTensorMaxN elements, so that a fall-back to the
+// whole tensor costs one workgroup five sweeps of at most 4 MiB.  Longer
+// sources go faster as spread passes: one workgroup sweeps ~3.7 G items/s
+// (65536 items, 88 us), and the scattered restores of a long list need
+// more CUs than one per tensor.
+constexpr int64_t kPerTensorMaxItems = 32768;
+constexpr int64_t kPerTensorMaxN = int64_t(1) << 20;
+constexpr int kTsWaves = kTsThreads / kWave;
+constexpr int kTsHistUnroll = 8;  // keys loaded together per thread
+constexpr int kTsEmitUnroll = 4;  // 64-item rounds loaded together per wave
+
+// Exclusive scan across the 1024-thread workgroup; `lds` holds kTsWaves
+// values.  Every thread must call it.
+__device__ __forceinline__ uint32_t ts_block_scan(uint32_t x, uint32_t* lds, uint32_t& total) {
+    const int lane = lane_id();
+    const int wid = int(threadIdx.x) >> 6;
+    const uint32_t inc = wave_inclusive_scan(x);
+    if (lane == kWave - 1) lds[wid] = inc;
+    __syncthreads();
+    uint32_t wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w) {
+        const uint32_t s = lds[w];
+        if (w < wid) wpre += s;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return wpre + inc - x;
+}
+
+// Digit D of the radix select over src[0, len): histogram of the keys that
+// match the prefix, then the bin holding the krem-th largest; extends the
+// prefix and reduces krem.  Returns false (uniformly) if no bin holds it.
+template <int D>
+__device__ __forceinline__ bool ts_digit(const float* __restrict__ src, int64_t len,
+                                         uint32_t& prefix, uint32_t& krem, uint32_t* h,
+                                         uint32_t* lds, uint32_t* pick) {
+    constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
+    constexpr int bins = 1 << bits;
+    constexpr uint32_t dmask = uint32_t(bins) - 1u;
+    constexpr int per = (bins + kTsThreads - 1) / kTsThreads;
+    const int tid = int(threadIdx.x);
+    for (int b = tid; b < bins; b += kTsThreads) h[b] = 0;
+    if (tid == 0) pick[0] = kNoKey;
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
+        uint32_t key[kTsHistUnroll];
+#pragma unroll
+        for (int q = 0; q < kTsHistUnroll; ++q) {
+            const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
+            key[q] = i < len ? mag_key(src[i]) : kNoKey;
+        }
+#pragma unroll
+        for (int q = 0; q < kTsHistUnroll; ++q)
+            if (key[q] != kNoKey && (D == 0 || (key[q] >> (shift + bits)) == prefix))
+                atomicAdd(&h[(key[q] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread j owns bins bins-1-j*per ... bins-per-j*per (descending)
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        const int b = bins - 1 - (tid * per + q);
+        c[q] = b >= 0 ? h[b] : 0u;
+        mine += c[q];
+    }
+    uint32_t total;
+    uint32_t run = ts_block_scan(mine, lds, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            pick[0] = uint32_t(bins - 1 - (tid * per + q));
+            pick[1] = krem - run;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    const uint32_t b = pick[0], kr = pick[1];
+    __syncthreads();  // every thread has read pick before the next digit
+    if (b == kNoKey) return false;
+    prefix = (prefix << bits) | b;
+    krem = kr;
+    return true;
+}
+
+// One workgroup per tensor (grid = T).  Runs after k_group_scan and
+// k_gather, like the spread passes it replaces.
+__global__ __launch_bounds__(kTsThreads) void k_select_tensor(
+    DevLayout L, DevK K, TensorState* __restrict__ ts,
+    float* __restrict__ u, float* __restrict__ v,
+    const uint32_t* __restrict__ olist_i, const float* __restrict__ olist_v,
+    const float* __restrict__ olist_u, uint32_t* __restrict__ out_idx,
+    float* __restrict__ out_val, Scalars* __restrict__ sc) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t lds[kTsWaves];
+    __shared__ uint32_t wcnt[2 * kTsWaves];
+    __shared__ uint32_t pick[2];
+    const int t = blockIdx.x;
+    const uint32_t mode = ts[t].mode;
+    if (mode == kModeSkip) return;  // uniform
+    const int64_t len = ts[t].len;
+    const float* src = source_values(mode, v, olist_v, L, t);
+    uint32_t prefix = ts[t].prefix, krem = ts[t].krem;
+    bool ok = ts_digit<0>(src, len, prefix, krem, h, lds, pick);
+    ok = ok && ts_digit<1>(src, len, prefix, krem, h, lds, pick);
+    ok = ok && ts_digit<2>(src, len, prefix, krem, h, lds, pick);
+    if (!ok) {  // uniform
+        if (threadIdx.x == 0) latch_error(sc, kErrInternal);
+        return;
+    }
+    if (threadIdx.x == 0) {
+        ts[t].prefix = prefix;
+        ts[t].krem = krem;
+    }
+    // Emit in index order.  Wave w owns items [c0, c1), a run of whole
+    // 64-item rounds; a count pass gives every wave its offsets.
+    const uint32_t T = prefix, r = krem;
+    const bool dense = mode == kModeDense;
+    const int lane = lane_id(), w = int(threadIdx.x) >> 6;
+    const int64_t rounds = (len + kWave - 1) / kWave;
+    const int64_t rpw = (rounds + kTsWaves - 1) / kTsWaves;
+    const int64_t c0 = min(len, int64_t(w) * rpw * kWave);
+    const int64_t c1 = min(len, int64_t(w + 1) * rpw * kWave);
+    constexpr int64_t kStep = int64_t(kWave) * kTsEmitUnroll;
+    uint32_t ng = 0, ne = 0;
+    for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
+        uint32_t key[kTsEmitUnroll];
+#pragma unroll
+        for (int q = 0; q < kTsEmitUnroll; ++q) {
+            const int64_t i = b0 + int64_t(q) * kWave + lane;
+            key[q] = i < c1 ? mag_key(src[i]) : kNoKey;
+        }
+#pragma unroll
+        for (int q = 0; q < kTsEmitUnroll; ++q) {
+            ng += uint32_t(__popcll(__ballot(key[q] != kNoKey && key[q] > T)));
+            ne += uint32_t(__popcll(__ballot(key[q] == T)));
+        }
+    }
+    if (lane == 0) {
+        wcnt[w] = ng;
+        wcnt[kTsWaves + w] = ne;
+    }
+    __syncthreads();
+    uint32_t gb = 0, eb = 0;
+    for (int j = 0; j < w; ++j) {
+        gb += wcnt[j];
+        eb += wcnt[kTsWaves + j];
+    }
+    const int64_t o = L.o[t];
+    const int64_t nt = L.o[t + 1] - o;
+    float* vt_ = v + o;
+    const uint32_t* oli = olist_i + L.obase[t];
+    const float* olu = olist_u + L.obase[t];
+    uint32_t* oi = out_idx + K.koff[t];
+    float* ov = out_val + K.koff[t];
+    const int64_t kt = K.k[t];
+    const uint64_t lt = lanemask_lt();
+    bool bad = false;
+    for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
+        float val[kTsEmitUnroll], usv[kTsEmitUnroll];
+        uint32_t lidx[kTsEmitUnroll];
+        bool in[kTsEmitUnroll];
+#pragma unroll
+        for (int q = 0; q < kTsEmitUnroll; ++q) {
+            const int64_t i = b0 + int64_t(q) * kWave + lane;
+            in[q] = i < c1;
+            val[q] = in[q] ? src[i] : 0.0f;
+            lidx[q] = uint32_t(i);
+            usv[q] = 0.0f;
+            if (!dense && in[q]) {  // the list's index and saved u
+                lidx[q] = oli[i];
+                usv[q] = olu[i];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kTsEmitUnroll; ++q) {
+            const uint32_t key = mag_key(val[q]);
+            const bool gt = in[q] && key > T, eq = in[q] && key == T;
+            const uint64_t bg = __ballot(gt), be = __ballot(eq);
+            const uint32_t g1 = gb + uint32_t(__popcll(bg & lt));
+            const uint32_t e1 = eb + uint32_t(__popcll(be & lt));
+            bool send = false;
+            uint32_t slot = 0;
+            if (gt) { send = true; slot = g1 + min(e1, r); }
+            else if (eq && e1 < r) { send = true; slot = g1 + e1; }
+            if (send) {
+                // never write outside the outputs, whatever the counts say
+                if (int64_t(slot) >= kt || int64_t(lidx[q]) >= nt) {
+                    bad = true;
+                } else {
+                    oi[slot] = lidx[q];
+                    ov[slot] = val[q];
+                    if (dense) {
+                        u[o + lidx[q]] = 0.0f;
+                        vt_[lidx[q]] = 0.0f;
+                    }
+                }
+            } else if (in[q] && !dense) {
+                if (int64_t(lidx[q]) >= nt) {
+                    bad = true;
+                } else {
+                    u[o + lidx[q]] = usv[q];
+                    vt_[lidx[q]] = val[q];
+                }
+            }
+            gb += uint32_t(__popcll(bg));
+            eb += uint32_t(__popcll(be));
+        }
+    }
+    if (bad) latch_error(sc, kErrInternal);
+}
+
 }  // namespace dgc

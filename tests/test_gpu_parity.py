@@ -33,13 +33,14 @@ def ks_for(wl, step):
     return [dgc.k_for_density(s, wl.densities[step]) for s in wl.sizes]
 
 
-def run_workload(wl, steps=None, learners=None, path=0, encode=True, tag=""):
+def run_workload(wl, steps=None, learners=None, path=0, grid=0, encode=True, tag=""):
     steps = wl.steps if steps is None else steps
     learners = wl.learners if learners is None else learners
     kmax = [max(dgc.k_for_density(s, d) for d in wl.densities) for s in wl.sizes]
     pairs = [Pair(list(wl.sizes), kmax, wl.momentum) for _ in range(learners)]
     for p in pairs:
         p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+        p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
     for t in range(steps):
         k = ks_for(wl, t)
         outs = []
@@ -92,25 +93,35 @@ def check_decode(pairs, streams_per_learner, sizes, tag=""):
 
 # ---------------------------------------------------------------- workloads
 
+# GRIDS: the exact select and emit as one workgroup per tensor (1) or as
+# passes spread over the chip (2); the automatic choice takes 1 for every
+# layout here, so both are forced.
+GRIDS = [1, 2]
+
+
+@pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("path", [0, 1])
-def test_flat1m(path):
+def test_flat1m(path, grid):
     """2**20 Laplace entries, k = 1049, one step, no clipping."""
-    run_workload(W.get("flat1m"), path=path, tag=f"flat1m/p{path}")
+    run_workload(W.get("flat1m"), path=path, grid=grid, tag=f"flat1m/p{path}g{grid}")
 
 
-def test_resnet50_scaled_three_steps():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_resnet50_scaled_three_steps(grid):
     wl = W.scaled(W.get("resnet50"), 8)
-    run_workload(wl, steps=3, tag="rn50/8")
+    run_workload(wl, steps=3, grid=grid, tag=f"rn50/8 g{grid}")
 
 
-def test_deepspeech_scaled_four_learners():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_deepspeech_scaled_four_learners(grid):
     wl = W.scaled(W.get("deepspeech"), 40)
-    run_workload(wl, tag="ds/40")
+    run_workload(wl, grid=grid, tag=f"ds/40 g{grid}")
 
 
-def test_warmup_schedule_scaled():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_warmup_schedule_scaled(grid):
     wl = W.scaled(W.get("warmup350m"), 100)
-    run_workload(wl, tag="warm/100")
+    run_workload(wl, grid=grid, tag=f"warm/100 g{grid}")
 
 
 def test_flat1b_shape_scaled():
@@ -123,9 +134,10 @@ def test_flat1b_shape_scaled():
 RAGGED = [1, 0, 3, 64, 1000, 1023, 1025, 4097, 65536, 65537, 300001, 7]
 
 
+@pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("path", [0, 1])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_ragged_layout(path, seed):
+def test_ragged_layout(path, seed, grid):
     """Odd sizes (misaligned tensor starts, partial float4 units, partial
     pieces and tiles), an empty tensor, k from 0 to n."""
     rng = np.random.default_rng([31, seed])
@@ -142,6 +154,7 @@ def test_ragged_layout(path, seed):
     kmax = [max(ks[t] for ks in ks_steps) for t in range(len(sizes))]
     p = Pair(sizes, kmax)
     p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
     for step, k in enumerate(ks_steps):
         g = (rng.laplace(0, 1e-2, n) * (rng.random(n) < 0.9)).astype(np.float32)
         clip = [0.0, 0.5, 1e6][step]
@@ -151,8 +164,9 @@ def test_ragged_layout(path, seed):
         check_decode([p], [want], sizes, tag=f"ragged s{step}")
 
 
+@pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("path", [0, 1])
-def test_ties_and_zeros(path):
+def test_ties_and_zeros(path, grid):
     """Few distinct magnitudes (ties at the threshold everywhere), signed
     zeros, an all-zero tensor, and k = n."""
     rng = np.random.default_rng(32)
@@ -161,6 +175,7 @@ def test_ties_and_zeros(path):
     pool = np.array([0.0, -0.0, 1.0, -1.0, 0.5, -0.5, 0.25], np.float32)
     p = Pair(sizes, sizes)
     p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
     for step, k in enumerate([[200, 70, 5000, 131], [199999, 0, 1, 131072],
                               [1, 69999, 2500, 65536]]):
         g = pool[rng.integers(0, pool.size, n)]
@@ -371,15 +386,16 @@ def test_random_layouts_both_paths(seed):
     ks = [[int(rng.integers(0, s + 1)) if rng.random() < 0.3 else -(-s // 1000)
            for s in sizes] for _ in range(steps)]
     kmax = [max(ks[t][i] for t in range(steps)) for i in range(T)]
-    for path in (0, 1):
+    for path, grid in ((0, 1), (0, 2), (1, 1), (1, 2)):
         p = Pair(sizes, kmax)
         p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+        p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
         for step in range(steps):
             g = rng.laplace(0, 1e-2, n).astype(np.float32)
             g[rng.random(n) < 0.05] = 0.0
             clip = float(rng.choice([0.0, 0.5, 100.0]))
             u0, v0 = p.u.copy(), p.v.copy()
-            got, (o_idx, o_val) = p.step(g, ks[step], clip, tag=f"fuzz{seed} p{path} s{step}")
+            got, (o_idx, o_val) = p.step(g, ks[step], clip, tag=f"fuzz{seed} p{path}g{grid} s{step}")
             # the accumulated v before masking, from the oracle's own steps
             _, s32 = oracle.clip_scale(g, clip)
             oracle.momentum(g, s32, 0.9, u0, v0)
@@ -458,7 +474,8 @@ def test_empty_layout():
     assert L.status() == dgc.DGC_OK
 
 
-def test_dense_fallback_after_masking():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_dense_fallback_after_masking(grid):
     """The element-wise pass stores the window's candidates as +0 in every
     piece whose run fits its slots.  A tensor whose candidates then turn out
     incomplete takes the dense path, and those candidates must get their u
@@ -472,6 +489,7 @@ def test_dense_fallback_after_masking():
     sizes = [1 << 20, 1 << 22, 300000]
     k = [1000, 1000, 300]
     p = Pair(sizes, k)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
     off = np.concatenate([[0], np.cumsum(sizes)])
     n = int(off[-1])
     g = rng.laplace(0, 1e-3, n).astype(np.float32)
@@ -496,8 +514,9 @@ def test_dense_fallback_after_masking():
     p.step(rng.laplace(0, 1e-3, n).astype(np.float32), k, 0.0, tag="fallback s1")
 
 
+@pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("path", [0, 1])
-def test_denormals_and_extremes(path):
+def test_denormals_and_extremes(path, grid):
     """Denormal and near-overflow magnitudes: keys are bit patterns, so the
     order is exact and denormals are kept (no flush to zero)."""
     rng = np.random.default_rng(51)
@@ -505,9 +524,20 @@ def test_denormals_and_extremes(path):
     n = sum(sizes)
     p = Pair(sizes, [100, 3000, 262])
     p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
     for step in range(2):
         g = rng.laplace(0, 1e-38, n).astype(np.float32)  # mostly denormal
         g[rng.random(n) < 0.001] = np.float32(1e38) * np.float32(rng.choice([-1, 1]))
         g[rng.random(n) < 0.01] = np.float32(1.4e-45)
         k = [100, 3000 if step == 0 else 7, 262]
         p.step(g, k, 0.0, tag=f"denorm p{path} s{step}")
+
+
+def test_select_grid_option_rejects_bad_values():
+    L = dgc.Learner([100], [10])
+    for bad in (-1, 3):
+        with pytest.raises(dgc.DGCError):
+            L.set_option(dgc.DGC_OPT_SELECT_GRID, bad)
+    for good in (0, 1, 2):
+        L.set_option(dgc.DGC_OPT_SELECT_GRID, good)
+    L.close()
