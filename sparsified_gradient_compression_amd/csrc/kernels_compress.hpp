@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(
 }
 
 // One block per tensor: place the candidate threshold lo just below the
-// j-th largest sampled key, j = ceil(mu + 6 sqrt(mu) + 8) where mu = S*k/n
+// j-th largest sampled key, j = ceil(mu + 4 sqrt(mu) + 6) where mu = S*k/n
 // is how many of the S samples the true top k should hold.  Level 0 finds
 // the top-11-bit bin holding the j-th key (wbin) and how many samples lie
 // above it (wabove); level 1 finds the 10-bit sub-bin inside it, and lo is
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kBlock) void k_window(
         __syncthreads();
         if (k <= 0 || force_dense || L.slines[t] == 0) return;
         const double mu = double(total) * double(k) / double(nt);
-        const double jd = ceil(mu + 6.0 * sqrt(mu) + 8.0);
+        const double jd = ceil(mu + 4.0 * sqrt(mu) + 6.0);
         if (jd > double(total)) {  // (nearly) everything: take all elements
             if (threadIdx.x == 0) ts[t].lo_key = 0;
             return;
