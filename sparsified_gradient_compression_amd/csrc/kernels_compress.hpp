@@ -123,6 +123,38 @@ __global__ __launch_bounds__(kBlock) void k_norm_final(
 // tensor's row structure.  Level 0 histograms the top 11 key bits; level 1
 // revisits the same lines and histograms the next 10 bits of the keys whose
 // top 11 bits equal the bin chosen by level 0.
+// A block's sampled lines are shared out to its 32-lane groups: group grp
+// takes lines j0 + grp + kSampleGroups q (q < kLinesPerGroup) of [j0, j1);
+// sampled line j of a tensor with `stride` lines per sampled line lies at
+// j * stride + mix32(j * 0x9E3779B9 ^ t * 0x7F4A7C15) mod stride.  The keys
+// of the would-be v there: every load is issued before the first update,
+// so a group waits for memory once, not once per line.  ok[q] is false
+// past j1 or past the tensor's end.
+constexpr int kSampleGroups = kBlock / 32;
+constexpr int kLinesPerGroup = int(kLinesPerSampleBlock / kSampleGroups);
+__device__ __forceinline__ void sample_line_keys(
+    const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ v,
+    int64_t o, int64_t nt, int t, int64_t stride, int64_t j0, int64_t j1, float s, float m,
+    uint32_t (&key)[kLinesPerGroup], bool (&ok)[kLinesPerGroup]) {
+    const int grp = int(threadIdx.x) >> 5, gl = int(threadIdx.x) & 31;
+    float gg[kLinesPerGroup], uu[kLinesPerGroup], vv[kLinesPerGroup];
+#pragma unroll
+    for (int q = 0; q < kLinesPerGroup; ++q) {
+        const int64_t j = j0 + grp + int64_t(q) * kSampleGroups;
+        const uint32_t r = mix32(uint32_t(j) * 0x9E3779B9u ^ uint32_t(t) * 0x7F4A7C15u);
+        const int64_t e = (j * stride + int64_t(r % uint64_t(stride))) * kLine + gl;
+        ok[q] = j < j1 && e < nt;
+        gg[q] = ok[q] ? g[o + e] : 0.0f;
+        uu[q] = ok[q] ? u[o + e] : 0.0f;
+        vv[q] = ok[q] ? v[o + e] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kLinesPerGroup; ++q) {
+        momentum_update(gg[q], s, m, uu[q], vv[q]);
+        key[q] = mag_key(vv[q]);
+    }
+}
+
 template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_sample(
     const float* __restrict__ g, const float* __restrict__ u,
@@ -143,18 +175,14 @@ __global__ __launch_bounds__(kBlock) void k_sample(
     const int64_t j0 = (sb - L.sbase[t]) * kLinesPerSampleBlock;
     const int64_t j1 = min(ls, j0 + kLinesPerSampleBlock);
     const float s = clip_on ? sc->scale : 1.0f;
-    const int grp = threadIdx.x >> 5, gl = threadIdx.x & 31;
-    for (int64_t j = j0 + grp; j < j1; j += kBlock / 32) {
-        uint32_t r = mix32(uint32_t(j) * 0x9E3779B9u ^ uint32_t(t) * 0x7F4A7C15u);
-        int64_t line = j * stride + int64_t(r % uint64_t(stride));
-        int64_t e = line * kLine + gl;
-        if (e < nt) {
-            float uu = u[o + e], vv = v[o + e];
-            momentum_update(g[o + e], s, m, uu, vv);
-            uint32_t key = mag_key(vv);
-            if (LEVEL == 0) atomicAdd(&h[key >> 20], 1u);
-            else if ((key >> 20) == wbin) atomicAdd(&h[(key >> 10) & 1023u], 1u);
-        }
+    uint32_t key[kLinesPerGroup];
+    bool ok[kLinesPerGroup];
+    sample_line_keys(g, u, v, o, nt, t, stride, j0, j1, s, m, key, ok);
+#pragma unroll
+    for (int q = 0; q < kLinesPerGroup; ++q) {
+        if (!ok[q]) continue;
+        if (LEVEL == 0) atomicAdd(&h[key[q] >> 20], 1u);
+        else if ((key[q] >> 20) == wbin) atomicAdd(&h[(key[q] >> 10) & 1023u], 1u);
     }
     __syncthreads();
     uint32_t* row = shist + int64_t(t) * kHistBins;

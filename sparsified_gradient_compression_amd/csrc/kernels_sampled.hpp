@@ -15,6 +15,7 @@
 #pragma once
 
 #include "dgc_device.hpp"
+#include "kernels_compress.hpp"
 
 namespace dgc {
 
@@ -53,19 +54,15 @@ __global__ __launch_bounds__(kBlock) void k_sm_hist(
     const int64_t j0 = (sb - A.sbase[t]) * kLinesPerSampleBlock;
     const int64_t j1 = min(ls, j0 + kLinesPerSampleBlock);
     const float s = clip_on ? sc->scale : 1.0f;
-    const int grp = threadIdx.x >> 5, gl = threadIdx.x & 31;
-    for (int64_t j = j0 + grp; j < j1; j += kBlock / 32) {
-        const uint32_t r = mix32(uint32_t(j) * 0x9E3779B9u ^ uint32_t(t) * 0x7F4A7C15u);
-        const int64_t line = j * stride + int64_t(r % uint64_t(stride));
-        const int64_t e = line * kLine + gl;
-        if (e < nt) {
-            float uu = u[o + e], vv = v[o + e];
-            momentum_update(g[o + e], s, m, uu, vv);
-            const uint32_t key = mag_key(vv);
-            if (LEVEL == 0) atomicAdd(&h[key >> 20], 1u);
-            else if (LEVEL == 1 && (key >> 20) == sel) atomicAdd(&h[(key >> 10) & 1023u], 1u);
-            else if (LEVEL == 2 && (key >> 10) == sel) atomicAdd(&h[key & 1023u], 1u);
-        }
+    uint32_t key[kLinesPerGroup];
+    bool ok[kLinesPerGroup];
+    sample_line_keys(g, u, v, o, nt, t, stride, j0, j1, s, m, key, ok);
+#pragma unroll
+    for (int q = 0; q < kLinesPerGroup; ++q) {
+        if (!ok[q]) continue;
+        if (LEVEL == 0) atomicAdd(&h[key[q] >> 20], 1u);
+        else if (LEVEL == 1 && (key[q] >> 20) == sel) atomicAdd(&h[(key[q] >> 10) & 1023u], 1u);
+        else if (LEVEL == 2 && (key[q] >> 10) == sel) atomicAdd(&h[key[q] & 1023u], 1u);
     }
     __syncthreads();
     uint32_t* row = shist + int64_t(t) * kHistBins;
