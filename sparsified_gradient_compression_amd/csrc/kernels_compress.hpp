@@ -13,16 +13,24 @@
 //   sample/window            per tensor, keys of the would-be v on sampled
 //                            32-element lines -> a candidate threshold lo
 //   fused                    u, v update (20 B/elem); keys >= lo are
-//                            written, index-ordered, into the fixed slots of
-//                            their 1024-element piece (no atomics)
+//                            written, index-ordered, into the fixed 12-byte
+//                            slots {index, v, u} of their 1024-element piece
+//                            (no atomics) and stored as u = v = +0 when the
+//                            piece's run fits
 //   group_sum/scan, gather   per tensor: choose the source (candidates when
 //                            none overflowed and there are at least k, else
 //                            the whole tensor); concatenate the pieces' runs
-//                            into one index-ordered candidate list
-//   hist<D>/resolve<D>       three radix digits (11,10,10 bits) -> the k-th
+//                            into one index-ordered candidate list, or put
+//                            the masked candidates back for the whole tensor
+//   then either, spread over the chip:
+//     hist<D>/resolve<D>     three radix digits (11,10,10 bits) -> the k-th
 //                            largest key T and the tie quota r
-//   emit_count/scan/write    index-ordered output of {key > T} plus the
-//                            first r ties, and u = v = +0 there
+//     emit_count/scan/write  index-ordered output of {key > T} plus the
+//                            first r ties; the list's other candidates get
+//                            their u, v back (whole tensor: u = v = +0 at
+//                            the sent entries)
+//   or, for short sources, the same in one workgroup per tensor:
+//     select_tensor
 #pragma once
 
 #include "dgc_device.hpp"
