@@ -127,12 +127,25 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
             continue;
         }
         uint32_t carry = tile_foff[vt];
+        // every entry of the tile is loaded before the first round, so the
+        // rounds' barriers do not each wait for memory
+        uint32_t nfv[kPerThread];
+        int64_t gapv[kPerThread];
+        float xv[kPerThread];
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int64_t i = i0 + q * kBlock + threadIdx.x;
+            bool bad = false;
+            gapv[q] = -1;
+            nfv[q] = i < kt ? fillers_of(id, i, nt, bad, gapv[q]) : 0u;
+            xv[q] = i < kt ? vl[i] : 0.0f;
+        }
+#pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             if (i0 + q * kBlock >= kt) break;  // uniform
             const int64_t i = i0 + q * kBlock + threadIdx.x;
-            bool bad = false;
-            int64_t gap = -1;
-            const uint32_t nf = i < kt ? fillers_of(id, i, nt, bad, gap) : 0u;
+            const uint32_t nf = nfv[q];
+            const int64_t gap = gapv[q];
             uint32_t pre = 0, tot = 0;
             if (__syncthreads_or(nf != 0))  // fillers are rare: skip the scan
                 pre = block_exclusive_scan(nf, lds, tot);
@@ -142,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
                     if (pos < cap) { runs[eb + pos] = 65535; vals[eb + pos] = 0.0f; }
                 if (pos < cap) {
                     runs[eb + pos] = uint16_t(gap & 0xFFFF);
-                    vals[eb + pos] = vl[i];
+                    vals[eb + pos] = xv[q];
                 }
             }
             carry += tot;
