@@ -54,6 +54,10 @@ struct Plan {
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t norm_chunk = 0;
     bool short_sources = true;  // every tensor fits the per-tensor select
+    // per-tensor scans that can exceed kScanStagedMin values take the
+    // LDS-staged kernels: groups (selection source), tiles over n (emit),
+    // capacity tiles (decode)
+    bool staged_groups = false, staged_tiles = false, staged_etiles = false;
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
@@ -142,6 +146,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         const int64_t n = sizes[t];
         const int64_t src = n <= kSmallN ? n : p.obase[t + 1] - p.obase[t];
         if (n > kPerTensorMaxN || src > kPerTensorMaxItems) p.short_sources = false;
+        p.staged_groups |= p.gbase[t + 1] - p.gbase[t] > kScanStagedMin;
+        p.staged_tiles |= p.tbase[t + 1] - p.tbase[t] > kScanStagedMin;
+        p.staged_etiles |= p.etbase[t + 1] - p.etbase[t] > kScanStagedMin;
     }
     p.P = p.pbase[T];
     p.G = p.gbase[T];
@@ -279,6 +286,7 @@ struct dgc_state {
     DevDec Dd{};
     int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged
     int select_grid = 0;  // 0 automatic, 1 a workgroup per tensor, 2 spread passes
+    bool staged_k = false;  // some tensor has more than kScanStagedMin k tiles
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
     DevBins B{};
     // device views
@@ -390,6 +398,8 @@ int upload_k(dgc_state* st, const int64_t* k, hipStream_t s) {
         ktb[t + 1] = ktb[t] + cdiv(k[t], kTile);
     }
     st->KT = ktb[T];
+    st->staged_k = false;
+    for (int32_t t = 0; t < T; ++t) st->staged_k |= ktb[t + 1] - ktb[t] > kScanStagedMin;
     st->kmap_host.resize(size_t(std::max<int64_t>(st->KT, 1)));
     for (int32_t t = 0; t < T; ++t)
         for (int64_t i = ktb[t]; i < ktb[t + 1]; ++i) st->kmap_host[size_t(i)] = uint32_t(t);
@@ -496,8 +506,12 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
     if (st->KT > 0)
         k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
                                                                  st->ta, st->sc, st->KT);
-    k_enc_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb, entries,
-                                         st->sc);
+    if (st->staged_k)
+        k_enc_scan<true><<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb, entries,
+                                                   st->sc);
+    else
+        k_enc_scan<false><<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb,
+                                                    entries, st->sc);
     if (st->KT > 0)
         k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(
             st->L, st->K, kdev, idx, val, st->tb, runs, vals, st->KT);
@@ -740,8 +754,12 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         return DGC_EHIP;
     if (p.G > 0)
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
-    k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
-                                           st->atiles);
+    if (p.staged_groups)
+        k_group_scan<true><<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
+                                                     st->atiles);
+    else
+        k_group_scan<false><<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum,
+                                                      st->goff, st->atiles);
     if (p.G > 0)
         k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
                                                   st->run_cnt, st->goff, st->olist_i,
@@ -771,7 +789,10 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         DGC_LAUNCH_CHECK();
         k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v,
                                                 st->amap, st->aoff, st->ta);
-        k_emit_scan<<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
+        if (p.staged_tiles)
+            k_emit_scan<true><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
+        else
+            k_emit_scan<false><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
         k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
                                                 st->olist_i, st->olist_v, st->olist_u, st->amap,
                                                 st->aoff, st->tb, st->tc, out_idx,
@@ -1002,7 +1023,10 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
         for (int w = 0; w < nbw; ++w) {
             k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.entries[w], st->ta,
                                                    st->sc, p.ET);
-            k_dec_scan<<<T, kBlock, 0, stream>>>(st->L, S.entries[w], st->ta, st->t64);
+            if (p.staged_etiles)
+                k_dec_scan<true><<<T, kBlock, 0, stream>>>(st->L, S.entries[w], st->ta, st->t64);
+            else
+                k_dec_scan<false><<<T, kBlock, 0, stream>>>(st->L, S.entries[w], st->ta, st->t64);
             k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.vals[w], S.entries[w],
                                                    st->t64, dense, st->sc, p.ET,
                                                    int(merge_on), st->Dd, w);

@@ -207,33 +207,115 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* lds, T& total) {
     return wpre + inc - x;
 }
 
+// Long per-tensor scans run in one block, kScanRound values per round.  A
+// thread owns kScanPer consecutive values of a round (their sum feeds one
+// block-wide scan), but global loads and stores are lane-consecutive: all
+// kScanPer loads of a round are issued at once into registers, then
+// transposed through an LDS stage (index e + e/32, free of bank
+// conflicts).  Read directly, a thread's consecutive values put every lane
+// of a load on its own cache line, and the round costs one line request
+// per value.  Direct reads remain cheaper for a round of at most
+// kScanDirect values, and kernels whose scans are all short are built
+// without the stage (kStaged = false: 34 KB less LDS and fewer registers),
+// which the host picks when no tensor can need more than kScanStagedMin
+// values.
+constexpr int kScanPer = 32;
+constexpr int64_t kScanDirect = 2048;
+constexpr int64_t kScanStagedMin = 16384;
+constexpr int kScanRound = kBlock * kScanPer;
+constexpr int kScanStage = kScanRound + kScanRound / 32;
+__device__ __forceinline__ int scan_pad(int e) { return e + (e >> 5); }
+
+// Values [base, base + kScanRound) of in[0, count) (0 past count), each
+// thread's kScanPer consecutive ones in x.
+template <bool kStaged>
+__device__ __forceinline__ void scan_load_round(const uint32_t* __restrict__ in, int64_t base,
+                                                int64_t count, uint32_t* stage,
+                                                uint32_t (&x)[kScanPer]) {
+    const int tid = int(threadIdx.x);
+    if (!kStaged || count - base <= kScanDirect) {  // uniform
+        const int64_t i0 = base + int64_t(tid) * kScanPer;
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) x[q] = i0 + q < count ? in[i0 + q] : 0u;
+        return;
+    }
+    uint32_t c[kScanPer];
+#pragma unroll
+    for (int q = 0; q < kScanPer; ++q) {
+        const int64_t i = base + int64_t(q) * kBlock + tid;
+        c[q] = i < count ? in[i] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kScanPer; ++q) stage[scan_pad(q * kBlock + tid)] = c[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kScanPer; ++q) x[q] = stage[scan_pad(tid * kScanPer + q)];
+    __syncthreads();
+}
+
+// Store each thread's kScanPer consecutive results r of the round at
+// `base` into out[0, count), lane-consecutive, through the stage (32-bit
+// halves for 64-bit results).
+template <bool kStaged, typename TO>
+__device__ __forceinline__ void scan_store_round(TO* __restrict__ out, int64_t base,
+                                                 int64_t count, uint32_t* stage,
+                                                 const TO (&r)[kScanPer]) {
+    const int tid = int(threadIdx.x);
+    if (!kStaged || count - base <= kScanDirect) {  // uniform
+        const int64_t i0 = base + int64_t(tid) * kScanPer;
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q)
+            if (i0 + q < count) out[i0 + q] = r[q];
+        return;
+    }
+    constexpr int kHalves = sizeof(TO) / 4;
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q)
+            stage[scan_pad(tid * kScanPer + q)] = uint32_t(uint64_t(r[q]) >> (32 * hv));
+        __syncthreads();
+        uint32_t c[kScanPer];
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) c[q] = stage[scan_pad(q * kBlock + tid)];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) {
+            const int64_t i = base + int64_t(q) * kBlock + tid;
+            if (i >= count) continue;
+            if (kHalves == 1) {
+                out[i] = TO(c[q]);
+            } else {
+                uint32_t* w = reinterpret_cast<uint32_t*>(out + i);
+                w[hv] = c[q];  // little-endian halves of a 64-bit result
+            }
+        }
+    }
+}
+
 // Exclusive scan of in[0, count) into out[0, count), starting at `carry`,
-// by one block: each thread takes PER consecutive values per round (one
-// block-wide scan per 256 * PER values; a round costs about one memory
-// round trip, so long per-tensor scans take many values per thread).
-// Returns carry + total.  Every thread must call it.
-constexpr int kScanPer = 8;
-constexpr int kWideScanPer = 32;
-template <typename TO, int PER = kScanPer>
+// by one block.  `lds` holds kWavesPerBlock values, `stage` kScanStage
+// (unused unless kStaged).  Returns carry + total.  Every thread must call
+// it.
+template <typename TO, bool kStaged>
 __device__ __forceinline__ TO block_scan_range(const uint32_t* __restrict__ in,
                                                TO* __restrict__ out, int64_t count,
-                                               TO carry, TO* lds) {
-    for (int64_t base = 0; base < count; base += int64_t(kBlock) * PER) {
-        const int64_t i0 = base + int64_t(threadIdx.x) * PER;
-        uint32_t x[PER];
+                                               TO carry, TO* lds, uint32_t* stage) {
+    for (int64_t base = 0; base < count; base += kScanRound) {
+        uint32_t x[kScanPer];
+        scan_load_round<kStaged>(in, base, count, stage, x);
         TO local = 0;
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            x[q] = i0 + q < count ? in[i0 + q] : 0u;
-            local += TO(x[q]);
-        }
+        for (int q = 0; q < kScanPer; ++q) local += TO(x[q]);
         TO tot;
         TO run = carry + block_exclusive_scan(local, lds, tot);
+        TO r[kScanPer];
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            if (i0 + q < count) out[i0 + q] = run;
+        for (int q = 0; q < kScanPer; ++q) {
+            r[q] = run;
             run += TO(x[q]);
         }
+        scan_store_round<kStaged>(out, base, count, stage, r);
         carry += tot;
     }
     return carry;

@@ -417,7 +417,9 @@ __global__ __launch_bounds__(kBlock) void k_bl_tscan(DevK K, DevBins B,
     __shared__ uint32_t lds[kWavesPerBlock];
     const int t = blockIdx.x;
     const int64_t gb = B.gbase[t], ng = B.gbase[t + 1] - gb;
-    const uint32_t total = block_scan_range<uint32_t, kWideScanPer>(B.gsum + gb, B.goff + gb, ng, 0u, lds);
+    // a tensor has at most ceil(n / 513 / 1024) groups: short scans
+    const uint32_t total = block_scan_range<uint32_t, false>(B.gsum + gb, B.goff + gb, ng, 0u,
+                                                             lds, nullptr);
     if (threadIdx.x == 0) {
         out_count[t] = min(int64_t(total), K.k[t]);
         if (out_total) out_total[t] = int64_t(total);

@@ -90,16 +90,19 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
 }
 
 // One block per tensor: scan the filler counts; E_t = k_t + fillers.
+template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_enc_scan(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ tile_f, uint32_t* __restrict__ tile_foff,
     int64_t* __restrict__ entries, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
     const int64_t kt = enc_len(K, kdev, t);
     // only the tiles that hold entries (k_enc_count skips the rest)
     const int64_t kb = K.ktbase[t], ntile = (kt + kTile - 1) / kTile;
-    const uint32_t carry = block_scan_range<uint32_t, kWideScanPer>(tile_f + kb, tile_foff + kb, ntile, 0u, lds);
+    const uint32_t carry = block_scan_range<uint32_t, kStaged>(tile_f + kb, tile_foff + kb, ntile,
+                                                              0u, lds, stage);
     if (threadIdx.x == 0) {
         if (kdev && (kdev[t] < 0 || kdev[t] > K.k[t])) latch_error(sc, kErrCorrupt);
         entries[t] = kt + int64_t(carry);
@@ -254,14 +257,17 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
 
 // One block per tensor: 64-bit exclusive scan of the sums of the tiles
 // that hold entries (k_dec_count skips the rest).
+template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_dec_scan(
     DevLayout L, const int64_t* __restrict__ entries, const uint32_t* __restrict__ tile_s,
     uint64_t* __restrict__ tile_p) {
     __shared__ uint64_t lds[kWavesPerBlock];
+    __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
     const int64_t tb = L.etbase[t], cap = L.ebase[t + 1] - L.ebase[t];
     const int64_t ntile = (stream_len(entries, t, cap) + kTile - 1) / kTile;
-    block_scan_range<uint64_t, kWideScanPer>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds);
+    block_scan_range<uint64_t, kStaged>(tile_s + tb, tile_p + tb, ntile, uint64_t(0), lds,
+                                        stage);
 }
 
 // dense[o_t + pos] += value for every entry of one learner's stream, where

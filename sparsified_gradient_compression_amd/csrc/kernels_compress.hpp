@@ -298,36 +298,39 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
 // ordered list), then choose the selection source: the candidate list when
 // no piece overflowed and there are at least k candidates, else the whole
 // tensor.  Also counts the source's kTile-item tiles for the active-tile map.
+template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_group_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
     const uint32_t* __restrict__ gsum, uint32_t* __restrict__ goff,
     uint32_t* __restrict__ atiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t k = K.k[t];
     uint32_t carry = 0;
     int over = 0;
-    if (k > 0) {
-        const int64_t g0 = L.gbase[t], g1 = L.gbase[t + 1];
-        for (int64_t base = g0; base < g1; base += int64_t(kBlock) * kWideScanPer) {
-            const int64_t i0 = base + int64_t(threadIdx.x) * kWideScanPer;
-            uint32_t x[kWideScanPer];
+    if (k > 0) {  // uniform
+        const int64_t g0 = L.gbase[t], ng = L.gbase[t + 1] - g0;
+        for (int64_t base = 0; base < ng; base += kScanRound) {
+            uint32_t x[kScanPer];
+            scan_load_round<kStaged>(gsum + g0, base, ng, stage, x);
             uint32_t local = 0;
 #pragma unroll
-            for (int q = 0; q < kWideScanPer; ++q) {
-                uint32_t y = i0 + q < g1 ? gsum[i0 + q] : 0u;
-                over |= (y >> 31) != 0;
-                x[q] = y & 0x7FFFFFFFu;
+            for (int q = 0; q < kScanPer; ++q) {
+                over |= (x[q] >> 31) != 0;
+                x[q] &= 0x7FFFFFFFu;
                 local += x[q];
             }
             uint32_t tot;
             uint32_t run = carry + block_exclusive_scan(local, lds, tot);
+            uint32_t r[kScanPer];
 #pragma unroll
-            for (int q = 0; q < kWideScanPer; ++q) {
-                if (i0 + q < g1) goff[i0 + q] = run;
+            for (int q = 0; q < kScanPer; ++q) {
+                r[q] = run;
                 run += x[q];
             }
+            scan_store_round<kStaged>(goff + g0, base, ng, stage, r);
             carry += tot;
         }
     }
@@ -594,32 +597,41 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
 }
 
 // One block per tensor: exclusive scan of its tiles' (>T, ==T) counts.
+template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_emit_scan(
     const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ tile_cnt,
     uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
-    const uint32_t a0 = aoff[t], a1 = aoff[t + 1];
+    const uint32_t a0 = aoff[t];
+    const int64_t na = int64_t(aoff[t + 1]) - a0;
     uint32_t cg = 0, ce = 0;
-    for (uint32_t base = a0; base < a1; base += uint32_t(kBlock) * kWideScanPer) {
-        const uint32_t i0 = base + threadIdx.x * kWideScanPer;
-        uint32_t x[kWideScanPer];
+    for (int64_t base = 0; base < na; base += kScanRound) {
+        uint32_t x[kScanPer];
+        scan_load_round<kStaged>(tile_cnt + a0, base, na, stage, x);
         uint32_t lg = 0, le = 0;
 #pragma unroll
-        for (int q = 0; q < kWideScanPer; ++q) {
-            x[q] = i0 + q < a1 ? tile_cnt[i0 + q] : 0u;
+        for (int q = 0; q < kScanPer; ++q) {
             lg += x[q] >> 16;
             le += x[q] & 0xFFFFu;
         }
         uint32_t tg, te;
         uint32_t rg = cg + block_exclusive_scan(lg, lds, tg);
         uint32_t re = ce + block_exclusive_scan(le, lds, te);
+        uint32_t r[kScanPer];
 #pragma unroll
-        for (int q = 0; q < kWideScanPer; ++q) {
-            if (i0 + q < a1) { off_gt[i0 + q] = rg; off_eq[i0 + q] = re; }
+        for (int q = 0; q < kScanPer; ++q) {
+            r[q] = rg;
             rg += x[q] >> 16;
+        }
+        scan_store_round<kStaged>(off_gt + a0, base, na, stage, r);
+#pragma unroll
+        for (int q = 0; q < kScanPer; ++q) {
+            r[q] = re;
             re += x[q] & 0xFFFFu;
         }
+        scan_store_round<kStaged>(off_eq + a0, base, na, stage, r);
         cg += tg;
         ce += te;
     }
