@@ -243,11 +243,12 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
             vt = next_tensor_tile(vt, L.etbase[t + 1], gridDim.x);
             continue;
         }
+        // thread-consecutive entries, as in k_dec_write
         uint32_t s = 0;
-        for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = i0 + q * kBlock + threadIdx.x;
-            if (i < E) s += uint32_t(runs[eb + i]) + 1u;
-        }
+        const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c)
+            if (ib + c < E) s += uint32_t(runs[eb + ib + c]) + 1u;
         uint32_t tot;
         block_exclusive_scan(s, lds, tot);
         if (threadIdx.x == 0) tile_s[vt] = tot;
@@ -285,6 +286,8 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
     const uint64_t* __restrict__ tile_p, float* __restrict__ dense,
     Scalars* __restrict__ sc, int64_t n_etiles, int merge_on, DevDec Dd, int slot) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t trel[kTile];
+    __shared__ float tval[kTile];
     for (int64_t vt = blockIdx.x; vt < n_etiles;) {
         const int t = int(L.emap[vt]);
         const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
@@ -298,31 +301,68 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         const bool merged = merge_on && Dd.dmode[t] == kDecMerge;
         const int64_t nb = (nt + kDecBlock - 1) / kDecBlock;  // sentinel index
         uint2* bnd = merged ? Dd.bounds + int64_t(slot) * Dd.DB + Dd.dbase[t] : nullptr;
-        uint64_t carry = tile_p[vt];
+        // Each thread takes kPerThread consecutive entries of the tile: one
+        // load round and one block scan per tile give every entry its
+        // position (the thread's running sum after the scan).  The dense
+        // adds then go back to entry i0 + 256 q + tid, through LDS, so that a
+        // wave's adds stay close together when the stream is dense.
         bool bad = false;
-        for (int q = 0; q < kPerThread; ++q) {
-            if (i0 + q * kBlock >= E) break;  // uniform
-            const int64_t i = i0 + q * kBlock + threadIdx.x;
-            const uint32_t w = i < E ? uint32_t(runs[eb + i]) + 1u : 0u;
-            uint32_t tot;
-            const uint32_t ex = block_exclusive_scan(w, lds, tot);
-            if (i < E) {
-                const int64_t pos = int64_t(carry) + ex + w - 1;
-                if (pos >= nt) bad = true;
-                if (!merged) {
-                    if (pos < nt) dense[o + pos] = __fadd_rn(dense[o + pos], vals[eb + i]);
-                } else {
-                    const int64_t prev = pos - int64_t(w);  // -1 for the first entry
-                    const int64_t b0 = prev < 0 ? 0 : prev / kDecBlock + 1;
-                    const int64_t b1 = min(pos / kDecBlock, nb);
-                    for (int64_t b = b0; b <= b1; ++b)
-                        bnd[b] = make_uint2(uint32_t(i), uint32_t(min(pos, nt)));
-                    if (i == E - 1)
-                        for (int64_t b = max(b0, b1 + 1); b <= nb; ++b)
-                            bnd[b] = make_uint2(uint32_t(E), 0u);
-                }
+        const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+        uint32_t wv[kPerThread];
+        float xv[kPerThread];
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int64_t i = ib + c;
+            wv[c] = i < E ? uint32_t(runs[eb + i]) + 1u : 0u;
+            xv[c] = i < E && !merged ? vals[eb + i] : 0.0f;
+            s += wv[c];
+        }
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan(s, lds, tot);
+        const int64_t carry = int64_t(tile_p[vt]);
+        if (!merged) {  // uniform
+            // positions relative to the tile's start (< 1024 * 65536)
+            uint32_t rel = ex;
+#pragma unroll
+            for (int c = 0; c < kPerThread; ++c) {
+                rel += wv[c];
+                const int e = int(threadIdx.x) * kPerThread + c;
+                trel[e] = rel - 1u;
+                tval[e] = xv[c];
             }
-            carry += tot;
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kPerThread; ++q) {
+                const int e = q * kBlock + int(threadIdx.x);
+                if (i0 + e >= E) break;
+                const int64_t pos = carry + trel[e];
+                if (pos >= nt) bad = true;
+                else dense[o + pos] = __fadd_rn(dense[o + pos], tval[e]);
+            }
+            __syncthreads();  // before the next tile overwrites trel
+            if (bad) latch_error(sc, kErrCorrupt);
+            vt += gridDim.x;
+            continue;
+        }
+        int64_t run = carry + ex;  // entries' (run + 1) before this one
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int64_t i = ib + c;
+            if (i >= E) break;
+            run += wv[c];
+            const int64_t pos = run - 1;
+            if (pos >= nt) bad = true;
+            {
+                const int64_t prev = pos - int64_t(wv[c]);  // -1 for the first entry
+                const int64_t b0 = prev < 0 ? 0 : prev / kDecBlock + 1;
+                const int64_t b1 = min(pos / kDecBlock, nb);
+                for (int64_t b = b0; b <= b1; ++b)
+                    bnd[b] = make_uint2(uint32_t(i), uint32_t(min(pos, nt)));
+                if (i == E - 1)
+                    for (int64_t b = max(b0, b1 + 1); b <= nb; ++b)
+                        bnd[b] = make_uint2(uint32_t(E), 0u);
+            }
         }
         if (bad) latch_error(sc, kErrCorrupt);
         vt += gridDim.x;
