@@ -117,6 +117,9 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
     const uint32_t* __restrict__ tile_foff, uint16_t* __restrict__ runs,
     float* __restrict__ vals, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t sslot[kTile];
+    __shared__ uint16_t sgap[kTile];
+    __shared__ float sval[kTile];
     for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
         const int t = int(K.kmap[vt]);
         const int64_t kt = enc_len(K, kdev, t);
@@ -129,40 +132,60 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
             vt = next_tensor_tile(vt, K.ktbase[t + 1], gridDim.x);
             continue;
         }
-        uint32_t carry = tile_foff[vt];
-        // every entry of the tile is loaded before the first round, so the
-        // rounds' barriers do not each wait for memory
+        // Each thread takes kPerThread consecutive entries: one load round
+        // and at most one block scan (only when the tile has fillers) give
+        // every entry its slot.  The entries are then written back in the
+        // strided order through LDS, so a wave's stores stay contiguous.
+        const int64_t carry = int64_t(tile_foff[vt]);
+        const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
         uint32_t nfv[kPerThread];
         int64_t gapv[kPerThread];
         float xv[kPerThread];
+        uint32_t F = 0;
 #pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            const int64_t i = i0 + q * kBlock + threadIdx.x;
-            bool bad = false;
-            gapv[q] = -1;
-            nfv[q] = i < kt ? fillers_of(id, i, nt, bad, gapv[q]) : 0u;
-            xv[q] = i < kt ? vl[i] : 0.0f;
+        for (int c = 0; c < kPerThread; ++c) {
+            const int64_t i = ib + c;
+            bool bad = false;  // flagged by k_enc_count
+            gapv[c] = -1;
+            nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
+            xv[c] = i < kt ? vl[i] : 0.0f;
+            F += nfv[c];
         }
+        uint32_t pre = 0, tot = 0;
+        if (__syncthreads_or(F != 0))  // fillers are rare: skip the scan
+            pre = block_exclusive_scan(F, lds, tot);
+        // entry i lands at slot i + carry + (fillers of entries <= i); its
+        // own fillers fill the slots just before it.  sslot: slot - i0 -
+        // carry (below 1024 * 65537), or kNoKey for no entry.
+        uint32_t fb = pre;
 #pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            if (i0 + q * kBlock >= kt) break;  // uniform
-            const int64_t i = i0 + q * kBlock + threadIdx.x;
-            const uint32_t nf = nfv[q];
-            const int64_t gap = gapv[q];
-            uint32_t pre = 0, tot = 0;
-            if (__syncthreads_or(nf != 0))  // fillers are rare: skip the scan
-                pre = block_exclusive_scan(nf, lds, tot);
-            if (i < kt && gap >= 0) {
-                int64_t pos = i + int64_t(carry) + pre;
-                for (uint32_t z = 0; z < nf; ++z, ++pos)
+        for (int c = 0; c < kPerThread; ++c) {
+            const int64_t i = ib + c;
+            fb += nfv[c];
+            const int e = int(threadIdx.x) * kPerThread + c;
+            const bool ok = i < kt && gapv[c] >= 0;
+            sslot[e] = ok ? uint32_t(e) + fb : kNoKey;
+            sgap[e] = uint16_t(gapv[c] & 0xFFFF);
+            sval[e] = xv[c];
+            if (ok && nfv[c]) {
+                int64_t pos = i + carry + fb - nfv[c];
+                for (uint32_t z = 0; z < nfv[c]; ++z, ++pos)
                     if (pos < cap) { runs[eb + pos] = 65535; vals[eb + pos] = 0.0f; }
-                if (pos < cap) {
-                    runs[eb + pos] = uint16_t(gap & 0xFFFF);
-                    vals[eb + pos] = xv[q];
-                }
             }
-            carry += tot;
         }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int e = q * kBlock + int(threadIdx.x);
+            if (i0 + e >= kt) break;
+            if (sslot[e] == kNoKey) continue;
+            const int64_t pos = i0 + carry + sslot[e];
+            if (pos < cap) {
+                runs[eb + pos] = sgap[e];
+                vals[eb + pos] = sval[e];
+            }
+        }
+        __syncthreads();  // before the next tile overwrites the stage
         vt += gridDim.x;
     }
 }
