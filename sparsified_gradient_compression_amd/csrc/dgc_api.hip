@@ -55,9 +55,8 @@ struct Plan {
     int64_t norm_chunk = 0;
     bool short_sources = true;  // every tensor fits the per-tensor select
     // per-tensor scans that can exceed kScanStagedMin values take the
-    // LDS-staged kernels: groups (selection source), tiles over n (emit),
-    // capacity tiles (decode)
-    bool staged_groups = false, staged_tiles = false, staged_etiles = false;
+    // LDS-staged kernels: tiles over n (emit), capacity tiles (decode)
+    bool staged_tiles = false, staged_etiles = false;
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
@@ -146,7 +145,6 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         const int64_t n = sizes[t];
         const int64_t src = n <= kSmallN ? n : p.obase[t + 1] - p.obase[t];
         if (n > kPerTensorMaxN || src > kPerTensorMaxItems) p.short_sources = false;
-        p.staged_groups |= p.gbase[t + 1] - p.gbase[t] > kScanStagedMin;
         p.staged_tiles |= p.tbase[t + 1] - p.tbase[t] > kScanStagedMin;
         p.staged_etiles |= p.etbase[t + 1] - p.etbase[t] > kScanStagedMin;
     }
@@ -754,12 +752,8 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         return DGC_EHIP;
     if (p.G > 0)
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
-    if (p.staged_groups)
-        k_group_scan<true><<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
-                                                     st->atiles);
-    else
-        k_group_scan<false><<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum,
-                                                      st->goff, st->atiles);
+    k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
+                                           st->atiles);
     if (p.G > 0)
         k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
                                                   st->run_cnt, st->goff, st->olist_i,

@@ -298,23 +298,22 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
 // ordered list), then choose the selection source: the candidate list when
 // no piece overflowed and there are at least k candidates, else the whole
 // tensor.  Also counts the source's kTile-item tiles for the active-tile map.
-template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_group_scan(
     DevLayout L, DevK K, TensorState* __restrict__ ts,
     const uint32_t* __restrict__ gsum, uint32_t* __restrict__ goff,
     uint32_t* __restrict__ atiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t k = K.k[t];
     uint32_t carry = 0;
     int over = 0;
     if (k > 0) {  // uniform
+        // at most 16384 groups (n < 2^32): direct rounds, no LDS stage
         const int64_t g0 = L.gbase[t], ng = L.gbase[t + 1] - g0;
         for (int64_t base = 0; base < ng; base += kScanRound) {
             uint32_t x[kScanPer];
-            scan_load_round<kStaged>(gsum + g0, base, ng, stage, x);
+            scan_load_round<false>(gsum + g0, base, ng, nullptr, x);
             uint32_t local = 0;
 #pragma unroll
             for (int q = 0; q < kScanPer; ++q) {
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
                 r[q] = run;
                 run += x[q];
             }
-            scan_store_round<kStaged>(goff + g0, base, ng, stage, r);
+            scan_store_round<false>(goff + g0, base, ng, nullptr, r);
             carry += tot;
         }
     }
