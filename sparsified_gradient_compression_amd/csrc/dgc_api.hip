@@ -296,8 +296,7 @@ struct dgc_state {
              *run_cnt = nullptr, *gsum = nullptr, *goff = nullptr, *atiles = nullptr,
              *aoff = nullptr, *amap = nullptr, *ta = nullptr, *tb = nullptr,
              *tc = nullptr;
-    // exact path: 12-byte candidate slots; the bin-local and sampled passes
-    // read the same region as 16-byte slots
+    // 12-byte candidate slots {index, v, u}, shared by all three selectors
     CandSlot* slots = nullptr;
     // the ordered candidate list: local index, v and saved u per item
     uint32_t* olist_i = nullptr;
@@ -459,12 +458,9 @@ int upload_bins(dgc_state* st, const int64_t* bin_len, hipStream_t s) {
         const int64_t np_ = cdiv(n, plen[t]);
         pbase[t + 1] = pbase[t] + np_;
         gbase[t + 1] = gbase[t] + cdiv(np_, kBlGroup);
-        // the tensor's 12-byte candidate slots, taken as 16-byte slots
-        // {index, v, u, 0} and shared out among its pieces: the 16-byte
-        // units that lie wholly inside bytes [12 slbase[t], 12 slbase[t+1])
-        slb[t] = (3 * p.slbase[size_t(t)] + 3) / 4;
-        const int64_t region =
-            std::max<int64_t>(0, 3 * p.slbase[size_t(t) + 1] / 4 - slb[t]);
+        // the tensor's candidate slots, shared out among its pieces
+        slb[t] = p.slbase[size_t(t)];
+        const int64_t region = p.slbase[size_t(t) + 1] - slb[t];
         pcap[t] = np_ ? std::min<int64_t>(plen[t], region / np_) : 0;
     }
     if (pbase[T] > p.BP || gbase[T] > p.BG) return DGC_EINVAL;
@@ -838,7 +834,7 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_bl_fused<kSelBins><<<grid_for(wb, wb), kBlock, 0, stream>>>(
             g, st->u, st->v, st->L, st->B, st->ts, st->sc, clip_on, st->m, pcap_limit,
-            reinterpret_cast<uint4*>(st->slots), st->BP, out_norm, out_scale);
+            st->slots, st->BP, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
@@ -854,7 +850,7 @@ int dgc_compress_binlocal(dgc_state* st, const float* g, const int64_t* bin_len,
         const int64_t gb = cdiv(st->BP, int64_t(kBlock));  // kWave pieces per wave
         k_bl_gather<kSelBins><<<grid_for(gb, gb), kBlock, 0, stream>>>(
             st->u, st->v, st->L, st->K, st->B, st->ts, pcap_limit,
-            reinterpret_cast<const uint4*>(st->slots), st->BP, out_idx, out_val);
+            st->slots, st->BP, out_idx, out_val);
     }
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
@@ -925,7 +921,7 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
         DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
         k_bl_fused<kSelThresh><<<grid_for(wb, wb), kBlock, 0, stream>>>(
             g, st->u, st->v, st->L, st->B, st->ts, st->sc, clip_on, st->m, pcap_limit,
-            reinterpret_cast<uint4*>(st->slots), st->BP, out_norm, out_scale);
+            st->slots, st->BP, out_norm, out_scale);
         DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
@@ -939,7 +935,7 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
         const int64_t gb = cdiv(st->BP, int64_t(kBlock));
         k_bl_gather<kSelThresh><<<grid_for(gb, gb), kBlock, 0, stream>>>(
             st->u, st->v, st->L, st->K, st->B, st->ts, pcap_limit,
-            reinterpret_cast<const uint4*>(st->slots), st->BP, out_idx, out_val);
+            st->slots, st->BP, out_idx, out_val);
     }
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));

@@ -51,7 +51,7 @@ struct DevBins {
     const int64_t* pbase;  // [T+1] first piece of each tensor
     const int64_t* gbase;  // [T+1] first prefix group of each tensor
     const int64_t* pcap;   // [T] slots per piece
-    const int64_t* slbase; // [T] first slot of each tensor (16-byte slots)
+    const int64_t* slbase; // [T] first slot of each tensor (12-byte slots)
     const int64_t* rbins;  // [T] rounds per bin when L is 256, 512 or 1024, else 0
     PieceDesc* pdesc;      // [pieces]
     uint32_t* cnt;         // [pieces] salient entries of each piece
@@ -240,7 +240,7 @@ __device__ __forceinline__ void bl_fused_piece(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     int64_t e0, uint32_t len, int t, const DevLayout& L, const DevBins& B,
     const TensorState* __restrict__ ts, float s, float m, uint32_t pcap_limit,
-    uint4* __restrict__ slots, int64_t p, uint32_t* th) {
+    CandSlot* __restrict__ slots, int64_t p, uint32_t* th) {
     const int lane = lane_id();
     const int64_t e1 = e0 + len;
     float un[kRounds][4], vn[kRounds][4];
@@ -314,15 +314,14 @@ __device__ __forceinline__ void bl_fused_piece(
         }
     }
     if (total && early) {
-        uint4* sl = slots + B.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
+        CandSlot* sl = slots + B.slbase[t] + (p - B.pbase[t]) * int64_t(pcap);
 #pragma unroll
         for (int i = 0; i < kRounds; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (f[i][c])
-                    sl[rank[i][c]] = make_uint4(uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
-                                                __float_as_uint(vn[i][c]),
-                                                __float_as_uint(un[i][c]), 0u);
+                    sl[rank[i][c]] = CandSlot{uint32_t(e0 - o) + bl_off<kAligned>(i, c, lane),
+                                              vn[i][c], un[i][c]};
     }
 }
 
@@ -341,7 +340,7 @@ __global__ __launch_bounds__(kBlock) void k_bl_fused(
     const float* __restrict__ g, float* __restrict__ u, float* __restrict__ v,
     DevLayout L, DevBins B, const TensorState* __restrict__ ts,
     Scalars* __restrict__ sc, int clip_on, float m,
-    uint32_t pcap_limit, uint4* __restrict__ slots, int64_t n_pieces,
+    uint32_t pcap_limit, CandSlot* __restrict__ slots, int64_t n_pieces,
     double* __restrict__ out_norm, float* __restrict__ out_scale) {
     __shared__ __align__(16) uint32_t th[SelLds<kSel>::kRows][SelLds<kSel>::kLen];
     const float s = clip_on ? sc->scale : 1.0f;
@@ -476,7 +475,7 @@ template <int kSel>
 __global__ __launch_bounds__(kBlock) void k_bl_gather(
     float* __restrict__ u, float* __restrict__ v, DevLayout L, DevK K, DevBins B,
     const TensorState* __restrict__ ts, uint32_t pcap_limit,
-    const uint4* __restrict__ slots, int64_t n_pieces,
+    const CandSlot* __restrict__ slots, int64_t n_pieces,
     uint32_t* __restrict__ out_idx, float* __restrict__ out_val) {
     __shared__ __align__(16) uint32_t th[SelLds<kSel>::kRows][SelLds<kSel>::kLen];
     const int lane = lane_id();
@@ -509,7 +508,7 @@ __global__ __launch_bounds__(kBlock) void k_bl_gather(
     const uint32_t excl = inc - work;
     const uint32_t all = uint32_t(__shfl(int(inc), kWave - 1, kWave));
     for (uint32_t base = 0; base < all; base += kWave * kGatherUnroll) {
-        uint4 x[kGatherUnroll];
+        CandSlot x[kGatherUnroll];
         uint32_t r[kGatherUnroll];
         int src[kGatherUnroll];
 #pragma unroll
@@ -536,11 +535,11 @@ __global__ __launch_bounds__(kBlock) void k_bl_gather(
             const int64_t oj = __shfl(o, j, kWave);
             if (e >= all) continue;
             if (r[q] < ndj) {
-                out_idx[ob + r[q]] = x[q].x;
-                out_val[ob + r[q]] = __uint_as_float(x[q].y);
+                out_idx[ob + r[q]] = x[q].idx;
+                out_val[ob + r[q]] = x[q].v;
             } else {
-                v[oj + x[q].x] = __uint_as_float(x[q].y);
-                u[oj + x[q].x] = __uint_as_float(x[q].z);
+                v[oj + x[q].idx] = x[q].v;
+                u[oj + x[q].idx] = x[q].u;
             }
         }
     }
