@@ -2,8 +2,9 @@
 
 One step = the whole hot path over one batch of synthetic gradients: for each
 of the W learners, dgc_compress (clip, momentum correction, exact top-k,
-compaction, masking) and dgc_encode; then the dense sum is zeroed and all W
-streams are decoded into it (dgc_decode_accumulate).  Inputs are resident in
+compaction, masking) and dgc_encode; then all W streams are decoded into a
+fresh dense sum (dgc_decode_sum: every element written, none read, the same
+bits as zeroing and dgc_decode_accumulate).  Inputs are resident in
 HBM before the timed region; each step uses the next of the workload's
 gradient steps, cycling.
 
@@ -311,7 +312,6 @@ def main():
         fused_ev = [torch.cuda.Event() for _ in learners]
         for L, ev in zip(learners, fused_ev):
             L.set_fused_event(ev)
-        zero_stream = torch.cuda.Stream()
 
     def one_step(s):
         t = s % gsteps
@@ -326,10 +326,8 @@ def main():
                 if not args.fused_only:
                     L.encode_counts(step_caps)
             if not args.fused_only:
-                dense.zero_()
-                dgc.decode_accumulate(learners[0],
-                                      [(L.runs, L.vals, L.entries) for L in learners],
-                                      dense)
+                dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
+                               dense)
             return
         if not pipeline:
             for w, L in enumerate(learners):
@@ -337,10 +335,8 @@ def main():
                 if not args.fused_only:
                     L.encode(k)
             if not args.fused_only:
-                dense.zero_()
-                dgc.decode_accumulate(learners[0],
-                                      [(L.runs, L.vals, L.entries) for L in learners],
-                                      dense)
+                dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
+                               dense)
             return
         for w, L in enumerate(learners):
             st = streams[w]
@@ -353,14 +349,10 @@ def main():
                 if not args.fused_only:
                     L.encode(k, stream=st)
         if not args.fused_only:
-            zero_stream.wait_event(fused_ev[-1])
-            with torch.cuda.stream(zero_stream):
-                dense.zero_()
-            for st in streams + [zero_stream]:
+            for st in streams:
                 main.wait_stream(st)
-            dgc.decode_accumulate(learners[0],
-                                  [(L.runs, L.vals, L.entries) for L in learners], dense,
-                                  stream=main)
+            dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
+                           dense, stream=main)
         else:
             for st in streams:
                 main.wait_stream(st)

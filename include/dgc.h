@@ -302,6 +302,21 @@ int dgc_decode_accumulate(const dgc_state* st, int32_t n_learners,
                           hipStream_t stream);
 
 /*
+ * A fresh dense sum of several learners' streams (the aggregate one step of
+ * synchronous SGD applies, DGC review Abstract): the same result as zeroing
+ * dense to +0.0 and calling dgc_decode_accumulate, bit for bit, without the
+ * separate zeroing.  Every element of dense[n] is written, whatever it held
+ * before; each dense block is written once and read never (all tensors take
+ * the block-by-block path for the first 8 learners, later learners are
+ * added as dgc_decode_accumulate adds them).  n_learners == 0 gives all
+ * +0.0.  Arguments, ownership and errors as for dgc_decode_accumulate.
+ */
+int dgc_decode_sum(const dgc_state* st, int32_t n_learners,
+                   const uint16_t* const* runs, const float* const* vals,
+                   const int64_t* const* entries, float* dense,
+                   hipStream_t stream);
+
+/*
  * Wait for the state's last stream and return the latched device-side
  * error (DGC_OK or DGC_ECORRUPT: a corrupt stream in decoding, unsorted
  * input to an encoder, or a bad device count), clearing it.  Returns DGC_EHIP if the

@@ -42,7 +42,7 @@ struct Plan {
     std::vector<int64_t> o, pbase, tbase, obase, sbase, slines, ebase, etbase,
         slbase, pcap, gbase;
     std::vector<PieceDesc> pdesc;
-    std::vector<uint32_t> smap, emap, gmap;
+    std::vector<uint32_t> smap, emap, gmap, bmap;
     // sampled threshold: lines sampled per tensor (every line of a small
     // tensor), their sample blocks, and the tensor of each block
     std::vector<int64_t> aslines, asbase;
@@ -69,7 +69,7 @@ struct Plan {
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
            off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, off_dtab = 0,
-           off_dmode = 0, off_bounds = 0, total = 0;
+           off_dmode = 0, off_bounds = 0, off_bmap = 0, total = 0;
 };
 
 // Candidate slots per 1024-element piece: none for small tensors (they take
@@ -186,6 +186,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.asmap.resize(size_t(p.AS));
     for (int32_t t = 0; t < T; ++t)
         for (int64_t i = p.asbase[t]; i < p.asbase[t + 1]; ++i) p.asmap[size_t(i)] = uint32_t(t);
+    p.bmap.resize(size_t(p.NBLK));
+    for (int32_t t = 0; t < T; ++t)
+        for (int64_t i = p.bbase[t]; i < p.bbase[t + 1]; ++i) p.bmap[size_t(i)] = uint32_t(t);
     // carve
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -206,6 +209,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_asmap = take(size_t(p.AS) * 4);
     p.off_ktgt = take(T1 * sizeof(int64_t));
     p.off_dtab = take(2 * T1 * sizeof(int64_t));
+    p.off_bmap = take(size_t(p.NBLK) * 4);
     // Everything above is written from the host (layout tables at init, k
     // tables per call); everything from here on is device scratch, zeroed
     // at init.
@@ -625,6 +629,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     int64_t* dt = reinterpret_cast<int64_t*>(ws + p.off_dtab);
     st->Dd.dbase = dt;
     st->Dd.bbase = dt + T1;
+    st->Dd.bmap = reinterpret_cast<uint32_t*>(ws + p.off_bmap);
     st->Dd.dmode = reinterpret_cast<uint32_t*>(ws + p.off_dmode);
     st->Dd.bounds = reinterpret_cast<uint2*>(ws + p.off_bounds);
     st->Dd.DB = p.DB;
@@ -640,7 +645,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
         p.off_k >= p.off_scratch || p.off_kmap >= p.off_scratch ||
         p.off_tab >= p.off_scratch || p.off_bltab >= p.off_scratch ||
         p.off_astab >= p.off_scratch || p.off_asmap >= p.off_scratch ||
-        p.off_ktgt >= p.off_scratch || p.off_dtab >= p.off_scratch) {
+        p.off_ktgt >= p.off_scratch || p.off_dtab >= p.off_scratch ||
+        p.off_bmap >= p.off_scratch) {
         delete st;
         return DGC_EINVAL;
     }
@@ -656,6 +662,8 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
                                         hipMemcpyHostToDevice, stream) == hipSuccess;
     if (p.G) ok = ok && hipMemcpyAsync(ws + p.off_gmap, p.gmap.data(), size_t(p.G) * 4,
                                        hipMemcpyHostToDevice, stream) == hipSuccess;
+    if (p.NBLK) ok = ok && hipMemcpyAsync(ws + p.off_bmap, p.bmap.data(), size_t(p.NBLK) * 4,
+                                          hipMemcpyHostToDevice, stream) == hipSuccess;
     std::vector<int64_t> atab(2 * T1, 0);
     std::copy(p.aslines.begin(), p.aslines.end(), atab.begin());
     std::copy(p.asbase.begin(), p.asbase.end(), atab.begin() + T1);
@@ -964,15 +972,17 @@ int dgc_encode_counts(const dgc_state* cst, const int64_t* cap, const int64_t* c
     return encode_impl(st, cap, count, idx, val, runs, vals, entries, stream);
 }
 
-int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
-                          const uint16_t* const* runs, const float* const* vals,
-                          const int64_t* const* entries, float* dense,
-                          hipStream_t stream) {
-    dgc_state* st = const_cast<dgc_state*>(cst);
+// Shared by dgc_decode_accumulate (dense += the streams) and dgc_decode_sum
+// (fresh: dense = the streams, from +0.0).  A fresh sum takes the merged
+// path for every tensor of the first batch of learners, so each dense block
+// is written once and never read; later batches add as usual.
+static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const* runs,
+                       const float* const* vals, const int64_t* const* entries,
+                       float* dense, bool fresh, hipStream_t stream) {
     if (!st || n_learners < 0) return DGC_EINVAL;
-    if (n_learners == 0) return DGC_OK;
+    if (n_learners == 0 && !fresh) return DGC_OK;
     const Plan& p = st->plan;
-    if (!runs || !vals || !entries) return DGC_EINVAL;
+    if (n_learners > 0 && (!runs || !vals || !entries)) return DGC_EINVAL;
     if (p.n > 0 && (!dense || !aligned(dense, 4))) return DGC_EINVAL;
     for (int32_t w = 0; w < n_learners; ++w) {
         if (!entries[w] || !aligned(entries[w], 8)) return DGC_EINVAL;
@@ -981,7 +991,16 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
             return DGC_EINVAL;
     }
     st->last_stream = stream;
-    if (p.ET == 0) return DGC_OK;
+    if (n_learners == 0 || p.ET == 0) {
+        if (!fresh || p.n == 0) return DGC_OK;
+        // no entries at all: a fresh sum is all +0.0
+        DGC_TRY(timer_begin(st, DGC_TIMER_DECODE, stream));
+        k_fill_u32<<<grid_for(cdiv(p.n, kBlock), 8192), kBlock, 0, stream>>>(
+            reinterpret_cast<uint32_t*>(dense), p.n, 0u);
+        DGC_LAUNCH_CHECK();
+        DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
+        return DGC_OK;
+    }
     const int T = p.T;
     // grid-stride over capacity tiles; a workgroup that reaches a tile past
     // its stream's end skips to the next tensor
@@ -991,14 +1010,29 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
     // added by one merge pass before the next batch starts
     for (int32_t b0 = 0; b0 < n_learners; b0 += kDecBatch) {
         const int nbw = std::min<int32_t>(kDecBatch, n_learners - b0);
+        const bool fresh_batch = fresh && b0 == 0;
+        // A fresh sum zeroes dense at once when the tensors that can reach
+        // their merge threshold (n_t / kDecMergeFresh entries) with full
+        // streams hold less than 1/8 of the elements; otherwise the mode
+        // pass picks, per tensor, the merged path or zeroing first.
+        bool fill_all = fresh_batch && st->decode_path != 2;
+        if (fill_all && st->decode_path == 0) {
+            int64_t n_merge = 0;
+            for (int32_t t = 0; t < T; ++t) {
+                const int64_t nt = p.sizes[size_t(t)];
+                const int64_t cap = p.ebase[size_t(t) + 1] - p.ebase[size_t(t)];
+                if (nt > 0 && kDecMergeFresh * int64_t(nbw) * cap >= nt) n_merge += nt;
+            }
+            fill_all = 8 * n_merge < p.n;
+        }
         // can any tensor reach the merge threshold with full streams?
-        bool merge_on = st->decode_path == 2 && p.NBLK > 0;
+        bool merge_on = (st->decode_path == 2 || (fresh_batch && !fill_all)) && p.NBLK > 0;
         // one learner reads and writes its lines once either way
         if (st->decode_path == 0 && nbw >= 2)
             for (int32_t t = 0; t < T && !merge_on; ++t) {
                 const int64_t nt = p.sizes[size_t(t)];
                 const int64_t cap = p.ebase[size_t(t) + 1] - p.ebase[size_t(t)];
-                merge_on = nt > 0 && 16 * int64_t(nbw) * cap >= nt;
+                merge_on = nt > 0 && kDecMergeAcc * int64_t(nbw) * cap >= nt;
             }
         DecBatch S{};
         S.W = nbw;
@@ -1008,8 +1042,12 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
             S.entries[w] = entries[b0 + w];
         }
         if (merge_on)
-            k_dec_mode<<<int(cdiv(T, kBlock)), kBlock, 0, stream>>>(st->L, S, st->Dd,
-                                                                   st->decode_path);
+            k_dec_mode<<<int(cdiv(T, kBlock)), kBlock, 0, stream>>>(
+                st->L, S, st->Dd, st->decode_path, int(fresh_batch));
+        if (fresh_batch && merge_on)
+            k_dec_zero<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, st->Dd, dense, p.NBLK);
+        if (fill_all && p.n > 0)
+            k_dec_fill<<<int(cdiv(p.n, kDecBlock)), kBlock, 0, stream>>>(dense, p.n);
         for (int w = 0; w < nbw; ++w) {
             k_dec_count<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.entries[w], st->ta,
                                                    st->sc, p.ET);
@@ -1023,11 +1061,27 @@ int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
             DGC_LAUNCH_CHECK();
         }
         if (merge_on)
-            k_dec_merge<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, S, st->Dd, dense, p.NBLK);
+            k_dec_merge<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, S, st->Dd, dense, p.NBLK,
+                                                            int(fresh_batch));
         DGC_LAUNCH_CHECK();
     }
     DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
     return DGC_OK;
+}
+
+int dgc_decode_accumulate(const dgc_state* cst, int32_t n_learners,
+                          const uint16_t* const* runs, const float* const* vals,
+                          const int64_t* const* entries, float* dense,
+                          hipStream_t stream) {
+    return decode_impl(const_cast<dgc_state*>(cst), n_learners, runs, vals, entries, dense,
+                       false, stream);
+}
+
+int dgc_decode_sum(const dgc_state* cst, int32_t n_learners, const uint16_t* const* runs,
+                   const float* const* vals, const int64_t* const* entries, float* dense,
+                   hipStream_t stream) {
+    return decode_impl(const_cast<dgc_state*>(cst), n_learners, runs, vals, entries, dense,
+                       true, stream);
 }
 
 int dgc_get_status(dgc_state* st) {

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.dgc_encode.restype = ctypes.c_int
     L.dgc_decode_accumulate.argtypes = [P, i32, P, P, P, P, P]
     L.dgc_decode_accumulate.restype = ctypes.c_int
+    L.dgc_decode_sum.argtypes = [P, i32, P, P, P, P, P]
+    L.dgc_decode_sum.restype = ctypes.c_int
     L.dgc_get_status.argtypes = [P]
     L.dgc_get_status.restype = ctypes.c_int
     L.dgc_get_path_counts.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -212,19 +214,28 @@ def dgc_encode_counts(st, cap, count, idx, val, runs, vals, entries, stream=None
            "dgc_encode_counts")
 
 
-def dgc_decode_accumulate(st, runs: Sequence, vals: Sequence, entries: Sequence,
-                          dense, stream=None):
+def _decode(fn: str, st, runs: Sequence, vals: Sequence, entries: Sequence, dense,
+            stream=None):
     W = len(runs)
     assert len(vals) == W and len(entries) == W
     Arr = ctypes.c_void_p * max(W, 1)
     r = Arr(*[_dp(x) for x in runs])
     vv = Arr(*[_dp(x) for x in vals])
     e = Arr(*[_dp(x) for x in entries])
-    _check(lib().dgc_decode_accumulate(st, W, ctypes.cast(r, ctypes.c_void_p),
-                                       ctypes.cast(vv, ctypes.c_void_p),
-                                       ctypes.cast(e, ctypes.c_void_p), _dp(dense),
-                                       _stream(stream)),
-           "dgc_decode_accumulate")
+    _check(getattr(lib(), fn)(st, W, ctypes.cast(r, ctypes.c_void_p),
+                              ctypes.cast(vv, ctypes.c_void_p),
+                              ctypes.cast(e, ctypes.c_void_p), _dp(dense),
+                              _stream(stream)), fn)
+
+
+def dgc_decode_accumulate(st, runs: Sequence, vals: Sequence, entries: Sequence,
+                          dense, stream=None):
+    _decode("dgc_decode_accumulate", st, runs, vals, entries, dense, stream)
+
+
+def dgc_decode_sum(st, runs: Sequence, vals: Sequence, entries: Sequence, dense,
+                   stream=None):
+    _decode("dgc_decode_sum", st, runs, vals, entries, dense, stream)
 
 
 def dgc_get_status(st) -> int:
@@ -390,3 +401,10 @@ def decode_accumulate(layout_learner: Learner, streams: List[Tuple], dense,
     dgc_decode_accumulate(layout_learner.state, [s[0] for s in streams],
                           [s[1] for s in streams], [s[2] for s in streams],
                           dense, stream)
+
+
+def decode_sum(layout_learner: Learner, streams: List[Tuple], dense, stream=None):
+    """dense = the decoded streams [(runs, vals, entries), ...] summed in order
+    from +0.0 (every element of dense is written)."""
+    dgc_decode_sum(layout_learner.state, [s[0] for s in streams],
+                   [s[1] for s in streams], [s[2] for s in streams], dense, stream)

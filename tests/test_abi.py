@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     L = dgc.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -95,6 +95,8 @@ def test_init_and_calls_reject_bad_arguments_before_any_launch():
     assert L.dgc_compress_sampled(None, None, None, None, 0.0, None, None, None, None,
                                   None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_accumulate(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_decode_sum(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_decode_sum(None, 0, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_get_status(None) == dgc.DGC_EINVAL
     assert L.dgc_set_option(None, 1, 0) == dgc.DGC_EINVAL
     assert L.dgc_set_fused_event(None, None) == dgc.DGC_EINVAL

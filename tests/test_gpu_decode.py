@@ -132,3 +132,73 @@ def test_decode_option_rejects_bad_values():
     L = dgc.Learner([100], [10])
     with pytest.raises(dgc.DGCError):
         L.set_option(dgc.DGC_OPT_DECODE_PATH, 3)
+
+
+def decode_fresh(L, streams, n, path, guard=None):
+    """dgc_decode_sum into a buffer that holds NaNs, -0.0 and random values
+    (and, past n, a guard value that must survive)."""
+    import torch
+    L.set_option(dgc.DGC_OPT_DECODE_PATH, path)
+    rng = np.random.default_rng(n + 5)
+    junk = rng.standard_normal(n + 64).astype(np.float32)
+    junk[::7] = np.nan
+    junk[::11] = -0.0
+    if guard is not None:
+        junk[n:] = guard
+    dense = torch.from_numpy(junk).cuda()
+    dgc.decode_sum(L, [(s[1], s[2], s[3]) for s in streams], dense)
+    torch.cuda.synchronize()
+    return dense.cpu().numpy()
+
+
+@pytest.mark.parametrize("layout", range(len(LAYOUTS)))
+@pytest.mark.parametrize("W,dens", [(0, []), (1, [0.3]), (1, [0.001]),
+                                    (4, [0.001] * 4), (5, [0.001, 0.3, 0.01, 0.1, 0.05]),
+                                    (9, [0.02] * 9), (17, [0.07] * 17)])
+def test_decode_sum_matches_oracle(layout, W, dens):
+    """dgc_decode_sum = the oracle's decode of every learner onto +0.0, bit for
+    bit, whatever dense held; the decode-path option only steers learners
+    past the first 8."""
+    sizes = LAYOUTS[layout]
+    rng = np.random.default_rng([93, layout, W])
+    L = dgc.Learner(sizes, sizes)
+    streams = make_streams(rng, sizes, dens, L.cap)
+    n = sum(sizes)
+    want = reference(sizes, np.zeros(n, np.float32), streams)
+    for path in (1, 2, 0):
+        say(f"decode_sum layout {layout} W={W} path {path}")
+        got = decode_fresh(L, streams, n, path, guard=77.0)
+        assert L.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got[:n]), f32_bits(want)), (path, first_diff(got[:n], want))
+        assert (got[n:] == 77.0).all()
+
+
+def test_decode_sum_without_capacity():
+    """A layout whose streams have no capacity at all (k = 0, tensors under
+    65536 elements): the fresh sum is all +0.0."""
+    sizes = [100, 3, 65535]
+    L = dgc.Learner(sizes, [0, 0, 0])
+    assert int(L.cap[-1]) == 0
+    streams = make_streams(np.random.default_rng(94), sizes, [0.1, 0.1], L.cap)
+    n = sum(sizes)
+    got = decode_fresh(L, streams, n, 0, guard=5.0)
+    assert L.status() == dgc.DGC_OK
+    assert (f32_bits(got[:n]) == 0).all()
+    assert (got[n:] == 5.0).all()
+
+
+def test_decode_sum_flags_corrupt_streams():
+    import torch
+    sizes = [10000, 5000]
+    L = dgc.Learner(sizes, sizes)
+    rng = np.random.default_rng(95)
+    streams = make_streams(rng, sizes, [0.3, 0.3], L.cap)
+    per, runs, vals, ent = streams[1]
+    r = runs.cpu().numpy().view(np.uint16).copy()
+    r[L.cap[0]:L.cap[0] + int(ent[0])] = 200
+    streams[1] = (per, torch.from_numpy(r.view(np.int16)).cuda(), vals, ent)
+    got = decode_fresh(L, streams, sum(sizes), 0, guard=123.0)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert (got[sum(sizes):] == 123.0).all()
+    assert np.isfinite(got[:sum(sizes)]).all()  # every element written
+    assert L.status() == dgc.DGC_OK
