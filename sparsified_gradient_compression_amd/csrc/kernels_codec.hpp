@@ -39,7 +39,10 @@ __device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
 // Grid-stride walk over per-tensor tiles: the tile after vt for this
 // workgroup that lies at or past `first` (the next tensor's first tile).
 // Once a tile lies past its tensor's entries so do the tensor's later
-// tiles, so a workgroup skips straight to the next tensor.
+// tiles, so a workgroup skips straight to the next tensor.  A workgroup's
+// tiles only grow, so the walks below keep the current tensor's metadata
+// and load it again only when a tile lies past that tensor's last tile:
+// most tiles then wait for one round of loads instead of three.
 __device__ __forceinline__ int64_t next_tensor_tile(int64_t vt, int64_t first,
                                                     int64_t stride) {
     if (first <= vt) return vt + stride;
@@ -62,14 +65,20 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
     const uint32_t* __restrict__ idx, uint32_t* __restrict__ tile_f,
     Scalars* __restrict__ sc, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    int64_t tb = 0, te = 0, kt = 0, nt = 0;  // current tensor: tiles [tb, te)
+    const uint32_t* id = idx;
     for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
-        const int t = int(K.kmap[vt]);
-        const int64_t kt = enc_len(K, kdev, t);
-        const int64_t nt = L.o[t + 1] - L.o[t];
-        const uint32_t* id = idx + K.koff[t];
-        const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+        if (vt >= te) {  // uniform: the next tensor
+            const int t = int(K.kmap[vt]);
+            kt = enc_len(K, kdev, t);
+            nt = L.o[t + 1] - L.o[t];
+            id = idx + K.koff[t];
+            tb = K.ktbase[t];
+            te = K.ktbase[t + 1];
+        }
+        const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= kt) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, K.ktbase[t + 1], gridDim.x);
+            vt = next_tensor_tile(vt, te, gridDim.x);
             continue;
         }
         uint32_t f = 0;
@@ -120,16 +129,24 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
     __shared__ uint32_t sslot[kTile];
     __shared__ uint16_t sgap[kTile];
     __shared__ float sval[kTile];
+    int64_t tb = 0, te = 0, kt = 0, nt = 0, eb = 0, cap = 0;  // current tensor
+    const uint32_t* id = idx;
+    const float* vl = val;
     for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
-        const int t = int(K.kmap[vt]);
-        const int64_t kt = enc_len(K, kdev, t);
-        const int64_t nt = L.o[t + 1] - L.o[t];
-        const uint32_t* id = idx + K.koff[t];
-        const float* vl = val + K.koff[t];
-        const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
-        const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+        if (vt >= te) {  // uniform: the next tensor
+            const int t = int(K.kmap[vt]);
+            kt = enc_len(K, kdev, t);
+            nt = L.o[t + 1] - L.o[t];
+            id = idx + K.koff[t];
+            vl = val + K.koff[t];
+            eb = L.ebase[t];
+            cap = L.ebase[t + 1] - eb;
+            tb = K.ktbase[t];
+            te = K.ktbase[t + 1];
+        }
+        const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= kt) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, K.ktbase[t + 1], gridDim.x);
+            vt = next_tensor_tile(vt, te, gridDim.x);
             continue;
         }
         // Each thread takes kPerThread consecutive entries: one load round
@@ -262,18 +279,22 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
     const int64_t* __restrict__ entries, uint32_t* __restrict__ tile_s,
     Scalars* __restrict__ sc, int64_t n_etiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
+    int64_t tb = 0, te = 0, eb = 0, E = 0;  // current tensor: tiles [tb, te)
     for (int64_t vt = blockIdx.x; vt < n_etiles;) {
-        const int t = int(L.emap[vt]);
-        const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
-        const int64_t j = vt - L.etbase[t];
-        if (j == 0 && threadIdx.x == 0) {
-            int64_t e = entries[t];
-            if (e < 0 || e > cap) latch_error(sc, kErrCorrupt);
+        if (vt >= te) {  // uniform: the next tensor
+            const int t = int(L.emap[vt]);
+            eb = L.ebase[t];
+            const int64_t cap = L.ebase[t + 1] - eb;
+            tb = L.etbase[t];
+            te = L.etbase[t + 1];
+            const int64_t e = entries[t];
+            if (vt == tb && threadIdx.x == 0 && (e < 0 || e > cap))
+                latch_error(sc, kErrCorrupt);
+            E = (e < 0 || e > cap) ? 0 : e;
         }
-        const int64_t E = stream_len(entries, t, cap);
-        const int64_t i0 = j * kTile;
+        const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= E) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, L.etbase[t + 1], gridDim.x);
+            vt = next_tensor_tile(vt, te, gridDim.x);
             continue;
         }
         // thread-consecutive entries, as in k_dec_write
@@ -321,19 +342,29 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t trel[kTile];
     __shared__ float tval[kTile];
+    // current tensor: tiles [tb, te)
+    int64_t tb = 0, te = 0, eb = 0, o = 0, nt = 0, E = 0, nb = 0;
+    bool merged = false;
+    uint2* bnd = nullptr;
     for (int64_t vt = blockIdx.x; vt < n_etiles;) {
-        const int t = int(L.emap[vt]);
-        const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
-        const int64_t o = L.o[t], nt = L.o[t + 1] - o;
-        const int64_t E = stream_len(entries, t, cap);
-        const int64_t i0 = (vt - L.etbase[t]) * kTile;
+        if (vt >= te) {  // uniform: the next tensor
+            const int t = int(L.emap[vt]);
+            eb = L.ebase[t];
+            const int64_t cap = L.ebase[t + 1] - eb;
+            o = L.o[t];
+            nt = L.o[t + 1] - o;
+            E = stream_len(entries, t, cap);
+            tb = L.etbase[t];
+            te = L.etbase[t + 1];
+            merged = merge_on && Dd.dmode[t] == kDecMerge;
+            nb = (nt + kDecBlock - 1) / kDecBlock;  // sentinel index
+            bnd = merged ? Dd.bounds + int64_t(slot) * Dd.DB + Dd.dbase[t] : nullptr;
+        }
+        const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= E) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, L.etbase[t + 1], gridDim.x);
+            vt = next_tensor_tile(vt, te, gridDim.x);
             continue;
         }
-        const bool merged = merge_on && Dd.dmode[t] == kDecMerge;
-        const int64_t nb = (nt + kDecBlock - 1) / kDecBlock;  // sentinel index
-        uint2* bnd = merged ? Dd.bounds + int64_t(slot) * Dd.DB + Dd.dbase[t] : nullptr;
         // Each thread takes kPerThread consecutive entries of the tile: one
         // load round and one block scan per tile give every entry its
         // position (the thread's running sum after the scan).  The dense

@@ -477,7 +477,10 @@ __device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* row) {
 
 // Active tiles: a in [0, aoff[T]) is tile (a - aoff[t]) of tensor
 // t = amap[a]; the tile covers source items [kTile j, kTile (j + 1)) of the
-// tensor's source (candidate list or whole tensor), clipped to len.
+// tensor's source (candidate list or whole tensor), clipped to len.  A
+// workgroup's tiles only grow, so the walks keep the current tensor's state
+// and load it again only past that tensor's last active tile (one round of
+// dependent loads per tile instead of three).
 
 // Histogram of digit D over the keys that match the prefix found so far.
 // Workgroups stride over the active tiles.
@@ -494,18 +497,23 @@ __global__ __launch_bounds__(kBlock) void k_hist(
     __syncthreads();
     const uint32_t A = aoff[L.T];
     int cur_t = -1;
+    uint32_t ab = 0, ae = 0, prefix = 0;  // current tensor: active tiles [ab, ae)
+    int64_t len = 0;
+    const float* src = v;
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
-        const int t = int(amap[a]);
-        const uint32_t mode = ts[t].mode;
-        const int64_t len = ts[t].len;
-        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
-        if (t != cur_t) {
+        if (a >= ae) {  // uniform: the next tensor
+            const int t = int(amap[a]);
+            const uint32_t mode = ts[t].mode;
+            len = ts[t].len;
+            prefix = ts[t].prefix;
+            ab = aoff[t];
+            ae = aoff[t + 1];
+            src = source_values(mode, v, olist_v, L, t);
             if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
             cur_t = t;
         }
-        const uint32_t prefix = ts[t].prefix;
+        const int64_t i0 = int64_t(a - ab) * kTile;
         const int64_t i1 = min(len, i0 + kTile);
-        const float* src = source_values(mode, v, olist_v, L, t);
         for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
             uint32_t key = mag_key(src[i]);
             if (D == 0 || (key >> (shift + bits)) == prefix)
@@ -573,13 +581,20 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
     uint32_t* __restrict__ tile_cnt) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const uint32_t A = aoff[L.T];
+    uint32_t ab = 0, ae = 0, T = 0;  // current tensor: active tiles [ab, ae)
+    int64_t len = 0;
+    const float* src = v;
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
-        const int t = int(amap[a]);
-        const uint32_t mode = ts[t].mode;
-        const int64_t len = ts[t].len;
-        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
-        const uint32_t T = ts[t].prefix;
-        const float* src = source_values(mode, v, olist_v, L, t);
+        if (a >= ae) {  // uniform: the next tensor
+            const int t = int(amap[a]);
+            const uint32_t mode = ts[t].mode;
+            len = ts[t].len;
+            T = ts[t].prefix;
+            ab = aoff[t];
+            ae = aoff[t + 1];
+            src = source_values(mode, v, olist_v, L, t);
+        }
+        const int64_t i0 = int64_t(a - ab) * kTile;
         uint32_t cnt = 0;
 #pragma unroll 4
         for (int q = 0; q < kPerThread; ++q) {
@@ -653,22 +668,37 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     float* __restrict__ out_val, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds2[2 * kWavesPerBlock];
     const uint32_t A = aoff[L.T];
+    // current tensor: active tiles [ab, ae)
+    uint32_t ab = 0, ae = 0, T = 0, r = 0;
+    int64_t len = 0, o = 0, kt = 0, nt = 0;
+    bool dense = false;
+    float* vt_ = v;
+    const float* src = v;
+    const uint32_t* oli = olist_i;
+    const float* olu = olist_u;
+    uint32_t* oi = out_idx;
+    float* ov = out_val;
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
-        const int t = int(amap[a]);
-        const uint32_t mode = ts[t].mode;
-        const int64_t len = ts[t].len;
-        const int64_t i0 = int64_t(a - aoff[t]) * kTile;
-        const uint32_t T = ts[t].prefix, r = ts[t].krem;
-        const int64_t o = L.o[t];
-        float* vt_ = v + o;
-        const bool dense = mode == kModeDense;
-        const float* src = source_values(mode, v, olist_v, L, t);
-        const uint32_t* oli = olist_i + L.obase[t];
-        const float* olu = olist_u + L.obase[t];
-        uint32_t* oi = out_idx + K.koff[t];
-        float* ov = out_val + K.koff[t];
-        const int64_t kt = K.k[t];
-        const int64_t nt = L.o[t + 1] - o;
+        if (a >= ae) {  // uniform: the next tensor
+            const int t = int(amap[a]);
+            const uint32_t mode = ts[t].mode;
+            len = ts[t].len;
+            T = ts[t].prefix;
+            r = ts[t].krem;
+            o = L.o[t];
+            nt = L.o[t + 1] - o;
+            vt_ = v + o;
+            dense = mode == kModeDense;
+            src = source_values(mode, v, olist_v, L, t);
+            oli = olist_i + L.obase[t];
+            olu = olist_u + L.obase[t];
+            oi = out_idx + K.koff[t];
+            ov = out_val + K.koff[t];
+            kt = K.k[t];
+            ab = aoff[t];
+            ae = aoff[t + 1];
+        }
+        const int64_t i0 = int64_t(a - ab) * kTile;
         uint32_t cg = off_gt[a], ce = off_eq[a];
         bool bad = false;
         // every item of the tile is loaded before the first prefix round, so
