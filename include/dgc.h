@@ -306,10 +306,13 @@ int dgc_decode_accumulate(const dgc_state* st, int32_t n_learners,
  * synchronous SGD applies, DGC review Abstract): the same result as zeroing
  * dense to +0.0 and calling dgc_decode_accumulate, bit for bit, without the
  * separate zeroing.  Every element of dense[n] is written, whatever it held
- * before; each dense block is written once and read never (all tensors take
- * the block-by-block path for the first 8 learners, later learners are
- * added as dgc_decode_accumulate adds them).  n_learners == 0 gives all
- * +0.0.  Arguments, ownership and errors as for dgc_decode_accumulate.
+ * before.  For the first 8 learners either every tensor takes the
+ * block-by-block path (each dense block written once, read never) or, when
+ * the layout's streams cannot be dense enough for that to pay, dense is
+ * zeroed and each stream added on its own; later learners are added as
+ * dgc_decode_accumulate adds them.  DGC_OPT_DECODE_PATH 1 forces the second
+ * way, 2 the first.  n_learners == 0 gives all +0.0.  Arguments, ownership
+ * and errors as for dgc_decode_accumulate.
  */
 int dgc_decode_sum(const dgc_state* st, int32_t n_learners,
                    const uint16_t* const* runs, const float* const* vals,

@@ -69,7 +69,7 @@ struct Plan {
            off_ta = 0, off_tb = 0, off_tc = 0, off_t64 = 0, off_part = 0,
            off_bltab = 0, off_blpdesc = 0, off_blcnt = 0, off_blpre = 0, off_blgsum = 0,
            off_blgoff = 0, off_astab = 0, off_asmap = 0, off_ktgt = 0, off_dtab = 0,
-           off_dmode = 0, off_bounds = 0, off_bmap = 0, total = 0;
+           off_dmode = 0, off_bounds = 0, off_bmap = 0, off_bsel = 0, total = 0;
 };
 
 // Candidate slots per 1024-element piece: none for small tensors (they take
@@ -240,6 +240,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_blgoff = take(size_t(p.BG) * 4);
     p.off_dmode = take(size_t(T) * 4);
     p.off_bounds = take(size_t(kDecBatch) * size_t(p.DB) * sizeof(uint2));
+    p.off_bsel = take(size_t(p.NBLK) * 4);
     p.total = off;
     return DGC_OK;
 }
@@ -630,6 +631,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     st->Dd.dbase = dt;
     st->Dd.bbase = dt + T1;
     st->Dd.bmap = reinterpret_cast<uint32_t*>(ws + p.off_bmap);
+    st->Dd.bsel = reinterpret_cast<uint32_t*>(ws + p.off_bsel);
     st->Dd.dmode = reinterpret_cast<uint32_t*>(ws + p.off_dmode);
     st->Dd.bounds = reinterpret_cast<uint2*>(ws + p.off_bounds);
     st->Dd.DB = p.DB;
@@ -1011,10 +1013,10 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
     for (int32_t b0 = 0; b0 < n_learners; b0 += kDecBatch) {
         const int nbw = std::min<int32_t>(kDecBatch, n_learners - b0);
         const bool fresh_batch = fresh && b0 == 0;
-        // A fresh sum zeroes dense at once when the tensors that can reach
-        // their merge threshold (n_t / kDecMergeFresh entries) with full
-        // streams hold less than 1/8 of the elements; otherwise the mode
-        // pass picks, per tensor, the merged path or zeroing first.
+        // A fresh sum zeroes dense at once and scatters every tensor when the
+        // tensors that could reach n_t / kDecMergeFresh entries with full
+        // streams hold less than 1/8 of the elements; otherwise it merges
+        // every tensor (each block written once, never read).
         bool fill_all = fresh_batch && st->decode_path != 2;
         if (fill_all && st->decode_path == 0) {
             int64_t n_merge = 0;
@@ -1042,10 +1044,8 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
             S.entries[w] = entries[b0 + w];
         }
         if (merge_on)
-            k_dec_mode<<<int(cdiv(T, kBlock)), kBlock, 0, stream>>>(
-                st->L, S, st->Dd, st->decode_path, int(fresh_batch));
-        if (fresh_batch && merge_on)
-            k_dec_zero<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, st->Dd, dense, p.NBLK);
+            k_dec_mode<<<int(cdiv(p.NBLK, kBlock)), kBlock, 0, stream>>>(
+                st->L, S, st->Dd, fresh_batch ? 2 : st->decode_path, p.NBLK);
         if (fill_all && p.n > 0)
             k_dec_fill<<<int(cdiv(p.n, kDecBlock)), kBlock, 0, stream>>>(dense, p.n);
         for (int w = 0; w < nbw; ++w) {
@@ -1061,8 +1061,8 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
             DGC_LAUNCH_CHECK();
         }
         if (merge_on)
-            k_dec_merge<<<int(p.NBLK), kBlock, 0, stream>>>(st->L, S, st->Dd, dense, p.NBLK,
-                                                            int(fresh_batch));
+            k_dec_merge<<<int(kXcds * cdiv(p.NBLK, kXcds)), kBlock, 0, stream>>>(
+                st->L, S, st->Dd, dense, p.NBLK, int(fresh_batch));
         DGC_LAUNCH_CHECK();
     }
     DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));

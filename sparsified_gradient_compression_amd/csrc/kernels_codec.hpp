@@ -225,12 +225,16 @@ __device__ __forceinline__ int64_t stream_len(const int64_t* entries, int t,
 // still sees fl(fl(d + x_0) + x_1) ...) and stores the block once.
 constexpr int64_t kDecBlock = 4096;
 constexpr int kDecBatch = 8;  // learners merged per pass
-// A tensor is merged when its streams together hold at least n_t / kDecMergeAcc
-// entries (accumulating: the merged pass reads and writes every block) or
-// n_t / kDecMergeFresh (a fresh sum: the merged pass only writes, the
-// scattered path has to zero the tensor first).
+constexpr int64_t kXcds = 8;  // XCDs of an MI355X (block order of the merge pass)
+// Accumulating, a tensor is merged when its streams together hold at least
+// n_t / kDecMergeAcc entries (the merged pass reads and writes every block).
+// A fresh sum merges every tensor (the merged pass only writes, and the
+// scattered path would have to zero the tensor first), unless the tensors
+// that could hold n_t / kDecMergeFresh entries are a small part of the
+// layout: then the host zeroes the sum and every tensor is scattered.
 constexpr int64_t kDecMergeAcc = 16, kDecMergeFresh = 256;
 constexpr uint32_t kDecScatter = 0, kDecMerge = 1;
+constexpr uint32_t kBselMerged = 0x80000000u;
 
 // Dense-block tables: tensor t has cdiv(n_t, kDecBlock) blocks; its bounds
 // are bounds[w * DB + dbase[t] + j] for j in [0, blocks_t] (the last one a
@@ -239,6 +243,7 @@ struct DevDec {
     const int64_t* dbase;   // [T+1] first bound of each tensor (blocks_t + 1 each)
     const int64_t* bbase;   // [T+1] first dense block of each tensor (blocks_t each)
     const uint32_t* bmap;   // [NBLK] tensor of each dense block
+    uint32_t* bsel;         // [NBLK] this batch: tensor | kBselMerged if merged
     uint32_t* dmode;        // [T] kDecScatter / kDecMerge for the current batch
     uint2* bounds;          // [kDecBatch * DB] {first entry index, its position}
     int64_t DB;
@@ -252,24 +257,27 @@ struct DecBatch {
     int W;
 };
 
-// One thread per tensor: merged or scattered for this batch.  force: 0
-// automatic, 1 always scattered, 2 always merged.  A fresh sum (the block is
-// written, never read, on the merged path; zeroed first on the scattered
-// one) merges from n_t / kDecMergeFresh entries on, an accumulated one from
-// n_t / kDecMergeAcc.
+// One thread per dense block: the mode of the block's tensor for this
+// batch (merged or scattered; force: 0 automatic, 1 always scattered, 2
+// always merged).  The thread of a tensor's first block writes dmode[t] for
+// the write passes; every thread writes bsel[blk] for the merge pass, which
+// then finds its block's tensor in a line this pass has just written (the
+// block map itself would be a miss to HBM at the head of every merge
+// workgroup's chain: 1.06 against 0.93 ms for a fresh 2^30-element sum).
 __global__ __launch_bounds__(kBlock) void k_dec_mode(DevLayout L, DecBatch S, DevDec Dd,
-                                                     int force, int fresh) {
-    const int t = int(blockIdx.x) * kBlock + int(threadIdx.x);
-    if (t >= L.T) return;
+                                                     int force, int64_t n_blocks) {
+    const int64_t blk = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (blk >= n_blocks) return;
+    const int t = int(Dd.bmap[blk]);
     const int64_t nt = L.o[t + 1] - L.o[t];
     const int64_t cap = L.ebase[t + 1] - L.ebase[t];
     int64_t sum = 0;
     for (int w = 0; w < S.W; ++w) sum += stream_len(S.entries[w], t, cap);
-    uint32_t mode = ((fresh ? kDecMergeFresh : kDecMergeAcc) * sum >= nt) ? kDecMerge
-                                                                          : kDecScatter;
+    uint32_t mode = (kDecMergeAcc * sum >= nt) ? kDecMerge : kDecScatter;
     if (force == 1) mode = kDecScatter;
     if (force == 2) mode = kDecMerge;
-    Dd.dmode[t] = nt > 0 ? mode : kDecScatter;
+    if (blk == Dd.bbase[t]) Dd.dmode[t] = mode;
+    Dd.bsel[blk] = uint32_t(t) | (mode == kDecMerge ? kBselMerged : 0u);
 }
 
 // Per capacity tile of one learner's stream: sum of (run + 1).  Flags an
@@ -439,36 +447,10 @@ __device__ __forceinline__ bool aligned16(const float* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
-// A fresh sum on the scattered path.  k_dec_zero takes one dense block per
-// workgroup and zeroes it when its tensor is scattered in this batch (the
-// merged tensors' blocks are written by k_dec_merge).  k_dec_fill zeroes all
-// of dense, 16 KB per workgroup, when the host has found every tensor
-// scattered.  Plain 16-byte stores, one workgroup per 16 KB: on MI355X that
-// fills at about 6 TB/s, against 5 TB/s for a resident grid-stride loop and
-// a few percent less with nontemporal stores.
-__device__ __forceinline__ void zero_range(float* __restrict__ d, int64_t len, uint32_t tid) {
-    if (len == kDecBlock && aligned16(d)) {  // uniform
-#pragma unroll
-        for (int q = 0; q < int(kDecBlock / kBlock) / 4; ++q)
-            reinterpret_cast<float4*>(d)[q * kBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-        for (int64_t e = tid; e < len; e += kBlock) d[e] = 0.0f;
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_dec_zero(DevLayout L, DevDec Dd,
-                                                     float* __restrict__ dense,
-                                                     int64_t n_blocks) {
-    const int64_t blk = blockIdx.x;
-    if (blk >= n_blocks) return;
-    const int t = int(Dd.bmap[blk]);
-    const uint32_t mode = Dd.dmode[t];
-    const int64_t o = L.o[t], nt = L.o[t + 1] - o;
-    const int64_t lo_pos = (blk - Dd.bbase[t]) * kDecBlock;
-    if (mode == kDecScatter)  // uniform
-        zero_range(dense + o + lo_pos, min(kDecBlock, nt - lo_pos), threadIdx.x);
-}
-
+// A fresh sum whose tensors are all scattered: dense is zeroed first.
+// Plain 16-byte stores, one workgroup per 16 KB: on MI355X that fills at
+// about 6 TB/s, against 5 TB/s for a resident grid-stride loop and a few
+// percent less with nontemporal stores.
 // dense[0, n) = +0.0: 16-byte stores from the first 16-byte boundary on,
 // kDecBlock / 4 of them per workgroup; workgroup 0 also writes the head and
 // the tail.
@@ -504,7 +486,12 @@ __global__ __launch_bounds__(kBlock) void k_dec_fill(float* __restrict__ dense, 
 // together with the block.  When no learner has more than kWave entries in
 // the block, wave 0 holds them all after that round and adds them learner
 // by learner: within one wave the LDS updates of learner w complete before
-// those of learner w + 1, so no barrier separates the learners.  Whole
+// those of learner w + 1, so no barrier separates the learners.
+//
+// Workgroup g runs on XCD g mod kXcds (MI355X dispatches workgroups to its
+// eight XCDs round robin), and each XCD walks one contiguous range of
+// blocks: neighbouring blocks share the cache lines of the block map, the
+// bounds and the entries, and those lines then stay in one XCD's L2.  Whole
 // aligned blocks are stored with nontemporal 16-byte stores: on MI355X that
 // took a fresh 2^30-element sum from 1.28 to 0.99 ms against plain stores
 // (a pure fill is the other way round, see k_dec_fill).
@@ -513,12 +500,15 @@ __global__ __launch_bounds__(kBlock) void k_dec_merge(
     int fresh) {
     __shared__ __attribute__((aligned(16))) float tile[kDecBlock];
     __shared__ uint32_t lds[kWavesPerBlock];
-    const int64_t blk = blockIdx.x;
+    const int64_t per = (n_blocks + kXcds - 1) / kXcds;  // grid: kXcds * per
+    const int64_t blk = int64_t(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (blk >= n_blocks) return;
     const uint32_t tid = threadIdx.x;
-    const int t = int(Dd.bmap[blk]);
+    // round 1: the block's tensor and mode (written by k_dec_mode)
+    const uint32_t bs = Dd.bsel[blk];
+    if (!(bs & kBselMerged)) return;  // uniform
+    const int t = int(bs & ~kBselMerged);
     // round 2: all of it depends on t only
-    const uint32_t mode = Dd.dmode[t];
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
     const int64_t j = blk - Dd.bbase[t];
@@ -536,7 +526,6 @@ __global__ __launch_bounds__(kBlock) void k_dec_merge(
             bb[w] = bnd[1];
         }
     }
-    if (mode != kDecMerge) return;  // uniform
     const int64_t lo_pos = j * kDecBlock;
     const int64_t len = min(kDecBlock, nt - lo_pos);
     uint32_t lo[kDecBatch], hi[kDecBatch], p0[kDecBatch];
