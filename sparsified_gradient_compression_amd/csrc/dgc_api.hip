@@ -513,7 +513,7 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
                                                     entries, st->sc);
     if (st->KT > 0)
         k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(
-            st->L, st->K, kdev, idx, val, st->tb, runs, vals, st->KT);
+            st->L, st->K, kdev, idx, val, st->tb, runs, vals, st->sc, st->KT);
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_ENCODE, stream));
     return DGC_OK;

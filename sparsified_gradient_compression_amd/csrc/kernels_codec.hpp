@@ -59,7 +59,12 @@ __device__ __forceinline__ int64_t enc_len(const DevK& K, const int64_t* kdev, i
     return (c < 0 || c > k) ? 0 : c;
 }
 
-// Per k-tile: number of fillers its entries need.
+// Per k-tile: number of fillers its entries need.  A filler needs a gap of
+// at least 65536, and the gaps of a tile's entries add up to (its last
+// index) - (the index before its first) - (its entries): a tile spanning
+// less than that needs none, which two loads show (DGC's 0.1% spans ~1M
+// positions per tile and takes the entry-by-entry count; denser streams
+// mostly do not).  Index order is checked by k_enc_write.
 __global__ __launch_bounds__(kBlock) void k_enc_count(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ idx, uint32_t* __restrict__ tile_f,
@@ -79,6 +84,13 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
         const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= kt) {  // uniform: nothing here or later in this tensor
             vt = next_tensor_tile(vt, te, gridDim.x);
+            continue;
+        }
+        const int64_t i1 = min(kt, i0 + kTile);
+        const int64_t before = i0 ? int64_t(id[i0 - 1]) : -1;
+        if (int64_t(id[i1 - 1]) - before - (i1 - i0) < 65536) {  // uniform
+            if (threadIdx.x == 0) tile_f[vt] = 0;
+            vt += gridDim.x;
             continue;
         }
         uint32_t f = 0;
@@ -120,11 +132,13 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
 
 // Entry i lands at slot i + (fillers of entries <= i); its own fillers fill
 // the slots just before it.
+// An index not above the previous one or outside the tensor latches
+// DGC_ECORRUPT; such an entry is not written.
 __global__ __launch_bounds__(kBlock) void k_enc_write(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ idx, const float* __restrict__ val,
     const uint32_t* __restrict__ tile_foff, uint16_t* __restrict__ runs,
-    float* __restrict__ vals, int64_t n_ktiles) {
+    float* __restrict__ vals, Scalars* __restrict__ sc, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t sslot[kTile];
     __shared__ uint16_t sgap[kTile];
@@ -159,15 +173,16 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         int64_t gapv[kPerThread];
         float xv[kPerThread];
         uint32_t F = 0;
+        bool bad = false;
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) {
             const int64_t i = ib + c;
-            bool bad = false;  // flagged by k_enc_count
             gapv[c] = -1;
             nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
             xv[c] = i < kt ? vl[i] : 0.0f;
             F += nfv[c];
         }
+        if (bad) latch_error(sc, kErrCorrupt);
         uint32_t pre = 0, tot = 0;
         if (__syncthreads_or(F != 0))  // fillers are rare: skip the scan
             pre = block_exclusive_scan(F, lds, tot);
@@ -447,13 +462,12 @@ __device__ __forceinline__ bool aligned16(const float* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
-// A fresh sum whose tensors are all scattered: dense is zeroed first.
-// Plain 16-byte stores, one workgroup per 16 KB: on MI355X that fills at
-// about 6 TB/s, against 5 TB/s for a resident grid-stride loop and a few
-// percent less with nontemporal stores.
-// dense[0, n) = +0.0: 16-byte stores from the first 16-byte boundary on,
-// kDecBlock / 4 of them per workgroup; workgroup 0 also writes the head and
-// the tail.
+// A fresh sum whose tensors are all scattered: dense[0, n) = +0.0 first.
+// 16-byte stores from the first 16-byte boundary on, kDecBlock / 4 of them
+// per workgroup; workgroup 0 also writes the head and the tail.  Plain
+// stores, one workgroup per 16 KB: on MI355X that fills at about 6 TB/s,
+// against 5 TB/s for a resident grid-stride loop and a few percent less
+// with nontemporal stores.
 __global__ __launch_bounds__(kBlock) void k_dec_fill(float* __restrict__ dense, int64_t n) {
     const int64_t head =
         min(n, int64_t((16 - (reinterpret_cast<uintptr_t>(dense) & 15)) & 15) / 4);

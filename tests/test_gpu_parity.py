@@ -541,3 +541,26 @@ def test_select_grid_option_rejects_bad_values():
     for good in (0, 1, 2):
         L.set_option(dgc.DGC_OPT_SELECT_GRID, good)
     L.close()
+
+
+@pytest.mark.parametrize("gap", [65534, 65535, 65536, 65537, 131072, 200000])
+def test_encode_dense_tiles_with_one_long_gap(gap):
+    """Tiles of 1024 consecutive indices need no filler, and the count pass
+    settles them from the tile's span alone; one gap of `gap` zeros lands
+    inside the second tile (after entry 1500), another before the first
+    entry of the fourth tile (entry 3072).  Streams against the oracle."""
+    import torch
+    n = 10000 + 2 * gap
+    idx = np.concatenate([np.arange(1500), 1500 + gap + np.arange(1572),
+                          3072 + 2 * gap + np.arange(1000)]).astype(np.uint32)
+    assert idx[-1] < n and np.all(np.diff(idx.astype(np.int64)) > 0)
+    val = np.random.default_rng(gap).standard_normal(idx.size).astype(np.float32)
+    p = Pair([n], [idx.size])
+    L = p.learner
+    L.idx[:idx.size].copy_(torch.from_numpy(idx.view(np.int32)))
+    L.val[:idx.size].copy_(torch.from_numpy(val))
+    got = gpu_streams(p, [idx.size])[0]
+    want = oracle.encode(idx, val, cap=idx.size + n // 65536)
+    assert np.array_equal(got[0], want[0])
+    assert np.array_equal(f32_bits(got[1]), f32_bits(want[1]))
+    assert L.status() == dgc.DGC_OK
