@@ -146,6 +146,14 @@ def test_flat1b_full_sampled():
             gi = gi.flatten()
             ref[gi] = ref[gi] + L.val
         assert torch.equal(ref, dense)
+
+        # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
+        fresh = torch.full_like(dense, float("nan"))
+        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
+        torch.cuda.synchronize()
+        assert learners[0].status() == dgc.DGC_OK
+        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
+        del fresh
         del dense, ref
 
 
@@ -249,6 +257,14 @@ def test_flat1b_binlocal_full_sampled():
                 assert oracle.decode_accumulate(r, v_, want) == 0
             got = dense[c * C:(c + 1) * C].cpu().numpy()
             assert np.array_equal(f32_bits(got), f32_bits(want)), (t, c)
+
+        # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
+        fresh = torch.full_like(dense, float("nan"))
+        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
+        torch.cuda.synchronize()
+        assert learners[0].status() == dgc.DGC_OK
+        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
+        del fresh
         del dense
 
 
@@ -353,4 +369,12 @@ def test_flat1b_sampled_full_sampled():
                 assert oracle.decode_accumulate(r, v_, want_d) == 0
             got = dense[c * C:(c + 1) * C].cpu().numpy()
             assert np.array_equal(f32_bits(got), f32_bits(want_d)), (t, c)
+
+        # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
+        fresh = torch.full_like(dense, float("nan"))
+        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
+        torch.cuda.synchronize()
+        assert learners[0].status() == dgc.DGC_OK
+        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
+        del fresh
         del dense

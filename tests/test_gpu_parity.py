@@ -74,21 +74,28 @@ def check_paths(pair, sizes, k, path, tag=""):
 
 def check_decode(pairs, streams_per_learner, sizes, tag=""):
     """Decode every learner's GPU-encoded stream (learner order) into one
-    dense sum and compare with the oracle decoding the oracle's streams."""
+    dense sum and compare with the oracle decoding the oracle's streams:
+    accumulated onto zeros (dgc_decode_accumulate) and as a fresh sum
+    written over NaNs (dgc_decode_sum, what the benchmark times)."""
     import torch
     n = int(sum(sizes))
-    dense = torch.zeros(max(n, 1), dtype=torch.float32, device="cuda")
-    dgc.decode_accumulate(pairs[0].learner,
-                          [(p.learner.runs, p.learner.vals, p.learner.entries)
-                           for p in pairs], dense)
-    got = dense[:n].cpu().numpy()
-    assert pairs[0].learner.status() == dgc.DGC_OK
     want = np.zeros(n, np.float32)
     off = np.concatenate([[0], np.cumsum(sizes)])
     for streams in streams_per_learner:
         for t, (wr, wv) in enumerate(streams):
             assert oracle.decode_accumulate(wr, wv, want[off[t]:off[t + 1]]) == 0
-    assert np.array_equal(f32_bits(got), f32_bits(want)), (tag, first_diff(got, want))
+    streams = [(p.learner.runs, p.learner.vals, p.learner.entries) for p in pairs]
+    for fresh in (False, True):
+        if fresh:
+            dense = torch.full((max(n, 1),), float("nan"), dtype=torch.float32, device="cuda")
+            dgc.decode_sum(pairs[0].learner, streams, dense)
+        else:
+            dense = torch.zeros(max(n, 1), dtype=torch.float32, device="cuda")
+            dgc.decode_accumulate(pairs[0].learner, streams, dense)
+        got = dense[:n].cpu().numpy()
+        assert pairs[0].learner.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got), f32_bits(want)), (tag, fresh, first_diff(got, want))
+        del dense
 
 
 # ---------------------------------------------------------------- workloads
