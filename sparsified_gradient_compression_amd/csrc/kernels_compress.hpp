@@ -357,10 +357,11 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
 // runs, with their saved u, into the tensor's index-ordered candidate list
 // (three arrays: local index, v, u).
 // For any other tensor, put the slotted u and v back, so the dense path
-// reads the true values.  Accesses are coalesced either way: long runs are
-// copied a piece per wave; for short ones, threads walk the group's items
-// and find each one's piece by binary search over the in-group prefix of
-// the run lengths.
+// reads the true values.  Threads walk the group's items, several loads in
+// flight each, and find each item's piece by binary search over the
+// in-group prefix of the run lengths; accesses are coalesced.
+constexpr int kGatherBatch = 8;  // slot loads in flight per thread
+
 __global__ __launch_bounds__(kBlock) void k_gather(
     DevLayout L, const TensorState* __restrict__ ts,
     const CandSlot* __restrict__ slots,
@@ -391,9 +392,8 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     // leave the tensor's list whatever the counts say
     if (list && int64_t(goff[g]) + tot > L.obase[t + 1] - L.obase[t]) return;
     const int64_t d0 = list ? L.obase[t] + goff[g] : 0;
-    // item `rank` of piece j, the group's item `pos`
-    auto item = [&](int j, uint32_t rank, uint32_t pos) {
-        const CandSlot it = src0[int64_t(j) * pcap + rank];
+    // the group's item `pos`, read from its slot
+    auto put = [&](const CandSlot& it, uint32_t pos) {
         if (list) {
             olist_i[d0 + pos] = it.idx;
             olist_v[d0 + pos] = it.v;
@@ -403,23 +403,29 @@ __global__ __launch_bounds__(kBlock) void k_gather(
             u[o + it.idx] = it.u;
         }
     };
-    if (tot >= 32u * uint32_t(np)) {
-        // long runs: a wave copies one piece's run at a time
-        const int lane = lane_id();
-        for (int j = int(threadIdx.x) >> 6; j < np; j += kWavesPerBlock) {
-            const uint32_t b0 = pre[j], c = pre[j + 1] - b0;
-            for (uint32_t q = lane; q < c; q += kWave) item(j, q, b0 + q);
-        }
-    } else {
-        // short runs: threads walk the group's items and find each one's
-        // piece by binary search (largest j < np with pre[j] <= q)
-        for (uint32_t q = threadIdx.x; q < tot; q += kBlock) {
-            int lo = 0, hi = int(np);
-            while (hi - lo > 1) {
-                int mid = (lo + hi) >> 1;
-                if (pre[mid] <= q) lo = mid; else hi = mid;
+    // Threads take the group's items q = q0 + u kBlock + tid, kGatherBatch
+    // at a time: each finds its piece by binary search over the piece
+    // prefixes (largest j < np with pre[j] <= q), the batch's slot loads go
+    // out together, then its stores.  Consecutive threads read consecutive
+    // slots of one run and write consecutive list entries.
+    for (uint32_t q0 = 0; q0 < tot; q0 += kGatherBatch * kBlock) {
+        CandSlot it[kGatherBatch];
+#pragma unroll
+        for (int b = 0; b < kGatherBatch; ++b) {
+            const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
+            if (q < tot) {
+                int lo = 0, hi = int(np);
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (pre[mid] <= q) lo = mid; else hi = mid;
+                }
+                it[b] = src0[int64_t(lo) * pcap + (q - pre[lo])];
             }
-            item(lo, q - pre[lo], q);
+        }
+#pragma unroll
+        for (int b = 0; b < kGatherBatch; ++b) {
+            const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
+            if (q < tot) put(it[b], q);
         }
     }
 }
@@ -513,9 +519,18 @@ __global__ __launch_bounds__(kBlock) void k_hist(
             cur_t = t;
         }
         const int64_t i0 = int64_t(a - ab) * kTile;
-        const int64_t i1 = min(len, i0 + kTile);
-        for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-            uint32_t key = mag_key(src[i]);
+        // all of the tile's loads first, then the LDS increments: one wait
+        // for memory per tile
+        float x[kPerThread];
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int64_t i = i0 + q * kBlock + threadIdx.x;
+            x[q] = i < len ? src[i] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            if (i0 + q * kBlock + threadIdx.x >= len) break;
+            const uint32_t key = mag_key(x[q]);
             if (D == 0 || (key >> (shift + bits)) == prefix)
                 atomicAdd(&h[(key >> shift) & dmask], 1u);
         }
