@@ -202,3 +202,32 @@ def test_decode_sum_flags_corrupt_streams():
     assert (got[sum(sizes):] == 123.0).all()
     assert np.isfinite(got[:sum(sizes)]).all()  # every element written
     assert L.status() == dgc.DGC_OK
+
+
+@pytest.mark.parametrize("path", [0, 1, 2])
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_decode_sum_into_unaligned_dense(path, shift):
+    """The dense sum may start at any 4-byte boundary: a view `shift`
+    elements into a buffer of NaNs, with guards on both sides.  The
+    zero-fill's head and tail and the merge's element-wise stores (no
+    16-byte block) are exercised; the result is the oracle's."""
+    import torch
+    sizes = [4096 * 5 + 3, 65536 + 1024, 7]
+    rng = np.random.default_rng([96, path, shift])
+    L = dgc.Learner(sizes, sizes)
+    L.set_option(dgc.DGC_OPT_DECODE_PATH, path)
+    streams = make_streams(rng, sizes, [0.05, 0.2, 0.001], L.cap)
+    n = sum(sizes)
+    want = reference(sizes, np.zeros(n, np.float32), streams)
+    buf = torch.full((n + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[:shift] = 11.0
+    buf[shift + n:] = 22.0
+    dense = buf[shift:shift + n]
+    assert dense.data_ptr() % 16 != 0
+    dgc.decode_sum(L, [(s[1], s[2], s[3]) for s in streams], dense)
+    torch.cuda.synchronize()
+    assert L.status() == dgc.DGC_OK
+    got = buf.cpu().numpy()
+    assert np.array_equal(f32_bits(got[shift:shift + n]), f32_bits(want)), first_diff(
+        got[shift:shift + n], want)
+    assert (got[:shift] == 11.0).all() and (got[shift + n:] == 22.0).all()
