@@ -97,7 +97,8 @@ def check_residual(L, sel, vals, u_new, v_new):
 
 
 def check_roundtrip(L, sel, vals, encode):
-    """The stream decodes (into zeros) to exactly the sent entries."""
+    """The stream decodes (into zeros) to exactly the sent entries, and
+    dgc_decode_sum gives the same bits over a buffer of NaNs."""
     import torch
     encode()
     dense = torch.zeros(N, dtype=torch.float32, device="cuda")
@@ -108,7 +109,19 @@ def check_roundtrip(L, sel, vals, encode):
     want[sel] = vals
     for c in chunks():
         assert torch.equal(bits(dense[c] + 0.0), bits(want[c] + 0.0))
-    del dense, want
+    del want
+    # the same stream as a fresh sum over NaNs: automatic path, then merged
+    for path in (0, 2):
+        L.set_option(dgc.DGC_OPT_DECODE_PATH, path)
+        fresh = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        dgc.decode_sum(L, [(L.runs, L.vals, L.entries)], fresh)
+        torch.cuda.synchronize()
+        assert L.status() == dgc.DGC_OK
+        for c in chunks():
+            assert torch.equal(bits(fresh[c]), bits(dense[c])), path
+        del fresh
+    L.set_option(dgc.DGC_OPT_DECODE_PATH, 0)
+    del dense
 
 
 @pytest.mark.timeout(900)
