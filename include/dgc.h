@@ -236,8 +236,9 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
 /*
  * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is
  * the first entry slot of tensor t; tensor t may use up to
- * cap_offsets[t+1] - cap_offsets[t] = k_max[t] + floor(n_t / 65536) entries,
- * enough for any selection of at most k_max[t] indices.
+ * cap_offsets[t+1] - cap_offsets[t] entries: k_max[t] + floor(n_t / 65536),
+ * enough for any selection of at most k_max[t] indices, rounded up to a
+ * multiple of 8 (every tensor's stream then starts 16-byte aligned).
  */
 int dgc_stream_capacity(const dgc_state* st, int64_t* cap_offsets);
 

@@ -131,8 +131,11 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.obase[t + 1] = p.obase[t] + list_cap(n, km, np_ * p.pcap[t]);
         p.slines[t] = sample_lines(n);
         p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
-        p.ebase[t + 1] = p.ebase[t] + km + n / 65536;
-        p.etbase[t + 1] = p.etbase[t] + cdiv(km + n / 65536, kTile);
+        // a multiple of kStreamAlign entries per tensor, so that every
+        // tensor's stream starts 16-byte aligned in the run and value arrays
+        const int64_t ecap = cdiv(km + n / 65536, kStreamAlign) * kStreamAlign;
+        p.ebase[t + 1] = p.ebase[t] + ecap;
+        p.etbase[t + 1] = p.etbase[t] + cdiv(ecap, kTile);
         p.aslines[t] = n <= kSmallN ? cdiv(n, kLine) : p.slines[t];
         p.asbase[t + 1] = p.asbase[t] + cdiv(p.aslines[t], kLinesPerSampleBlock);
         p.bbase[t + 1] = p.bbase[t] + cdiv(n, kDecBlock);

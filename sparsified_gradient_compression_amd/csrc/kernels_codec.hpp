@@ -224,6 +224,32 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
 
 // ---------------------------------------------------------------- decode
 
+// Each tensor's stream capacity is a multiple of kStreamAlign entries, so
+// a thread's kPerThread consecutive entries (a multiple of kPerThread from
+// the stream start) sit at 8-byte aligned runs and 16-byte aligned values
+// whenever the arrays themselves are 16-byte aligned: one load each.
+constexpr int64_t kStreamAlign = 8;
+static_assert(kStreamAlign % kPerThread == 0 && kPerThread == 4, "vector stream loads");
+
+__device__ __forceinline__ bool aligned_as(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// (run + 1) of the thread's entries ib .. ib + 3 (0 past E).
+__device__ __forceinline__ void load_run_weights(const uint16_t* __restrict__ r, int64_t ib,
+                                                 int64_t E, bool vec, uint32_t (&w)[4]) {
+    if (vec && ib + 4 <= E) {
+        const uint2 x = *reinterpret_cast<const uint2*>(r + ib);
+        w[0] = (x.x & 0xFFFFu) + 1u;
+        w[1] = (x.x >> 16) + 1u;
+        w[2] = (x.y & 0xFFFFu) + 1u;
+        w[3] = (x.y >> 16) + 1u;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[c] = ib + c < E ? uint32_t(r[ib + c]) + 1u : 0u;
+    }
+}
+
 __device__ __forceinline__ int64_t stream_len(const int64_t* entries, int t,
                                               int64_t cap) {
     int64_t e = entries[t];
@@ -321,11 +347,10 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
             continue;
         }
         // thread-consecutive entries, as in k_dec_write
-        uint32_t s = 0;
         const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
-#pragma unroll
-        for (int c = 0; c < kPerThread; ++c)
-            if (ib + c < E) s += uint32_t(runs[eb + ib + c]) + 1u;
+        uint32_t w[kPerThread];
+        load_run_weights(runs + eb, ib, E, aligned_as(runs + eb, 8), w);
+        const uint32_t s = w[0] + w[1] + w[2] + w[3];
         uint32_t tot;
         block_exclusive_scan(s, lds, tot);
         if (threadIdx.x == 0) tile_s[vt] = tot;
@@ -396,15 +421,21 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         bool bad = false;
         const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
         uint32_t wv[kPerThread];
-        float xv[kPerThread];
-        uint32_t s = 0;
+        float xv[kPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
+        load_run_weights(runs + eb, ib, E, aligned_as(runs + eb, 8), wv);
+        if (!merged) {  // uniform
+            if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
+                const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
+                xv[0] = x.x;
+                xv[1] = x.y;
+                xv[2] = x.z;
+                xv[3] = x.w;
+            } else {
 #pragma unroll
-        for (int c = 0; c < kPerThread; ++c) {
-            const int64_t i = ib + c;
-            wv[c] = i < E ? uint32_t(runs[eb + i]) + 1u : 0u;
-            xv[c] = i < E && !merged ? vals[eb + i] : 0.0f;
-            s += wv[c];
+                for (int c = 0; c < kPerThread; ++c) xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
+            }
         }
+        const uint32_t s = wv[0] + wv[1] + wv[2] + wv[3];
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan(s, lds, tot);
         const int64_t carry = int64_t(tile_p[vt]);
