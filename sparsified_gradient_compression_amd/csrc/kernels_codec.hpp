@@ -20,20 +20,36 @@ namespace dgc {
 
 // ---------------------------------------------------------------- encode
 
+// Each tensor's stream capacity is a multiple of kStreamAlign entries, so
+// a thread's kPerThread consecutive entries (a multiple of kPerThread from
+// the stream start) sit at 8-byte aligned runs and 16-byte aligned values
+// whenever the arrays themselves are 16-byte aligned: one load or store
+// each instead of four.
+constexpr int64_t kStreamAlign = 8;
+static_assert(kStreamAlign % kPerThread == 0 && kPerThread == 4, "vector stream access");
+
+__device__ __forceinline__ bool aligned_as(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
 // Tiles of kTile entries are visited in kPerThread rounds of 256 consecutive
 // entries (entry i0 + 256 q + tid), so loads and stores are coalesced.
 
-// Fillers needed by entry i of a tensor's sorted index list (0 for an entry
-// whose index is not above the previous one or not inside the tensor, which
-// is flagged).
-__device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
-                                               int64_t nt, bool& bad,
-                                               int64_t& gap) {
-    const int64_t cur = id[i];
-    const int64_t prev = i ? int64_t(id[i - 1]) : -1;
+// Fillers needed by an entry at index cur after one at prev (-1 before the
+// first): 0 for an index not above the previous one or not inside the
+// tensor, which is flagged.
+__device__ __forceinline__ uint32_t fillers_after(int64_t prev, int64_t cur, int64_t nt,
+                                                  bool& bad, int64_t& gap) {
     if (cur <= prev || cur >= nt) { bad = true; gap = -1; return 0; }
     gap = cur - prev - 1;
     return uint32_t(gap >> 16);
+}
+
+// The same for entry i of a tensor's sorted index list.
+__device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
+                                               int64_t nt, bool& bad,
+                                               int64_t& gap) {
+    return fillers_after(i ? int64_t(id[i - 1]) : -1, int64_t(id[i]), nt, bad, gap);
 }
 
 // Grid-stride walk over per-tensor tiles: the tile after vt for this
@@ -146,6 +162,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
     int64_t tb = 0, te = 0, kt = 0, nt = 0, eb = 0, cap = 0;  // current tensor
     const uint32_t* id = idx;
     const float* vl = val;
+    bool vin = false, vout = false;  // 16-byte loads of idx, val; stores of runs, vals
     for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
         if (vt >= te) {  // uniform: the next tensor
             const int t = int(K.kmap[vt]);
@@ -157,6 +174,8 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
             cap = L.ebase[t + 1] - eb;
             tb = K.ktbase[t];
             te = K.ktbase[t + 1];
+            vin = aligned_as(id, 16) && aligned_as(vl, 16);
+            vout = aligned_as(runs + eb, 8) && aligned_as(vals + eb, 16);
         }
         const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= kt) {  // uniform: nothing here or later in this tensor
@@ -165,7 +184,9 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         }
         // Each thread takes kPerThread consecutive entries: one load round
         // and at most one block scan (only when the tile has fillers) give
-        // every entry its slot.  The entries are then written back in the
+        // every entry its slot.  Without fillers up to the tile's end the
+        // thread's entries land in kPerThread consecutive aligned slots and
+        // are stored as vectors; otherwise they are written back in the
         // strided order through LDS, so a wave's stores stay contiguous.
         const int64_t carry = int64_t(tile_foff[vt]);
         const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
@@ -174,18 +195,58 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         float xv[kPerThread];
         uint32_t F = 0;
         bool bad = false;
+        if (vin && ib + kPerThread <= kt) {
+            const uint4 x = *reinterpret_cast<const uint4*>(id + ib);
+            const float4 y = *reinterpret_cast<const float4*>(vl + ib);
+            const int64_t cur[kPerThread] = {x.x, x.y, x.z, x.w};
+            xv[0] = y.x;
+            xv[1] = y.y;
+            xv[2] = y.z;
+            xv[3] = y.w;
+            int64_t prev = ib ? int64_t(id[ib - 1]) : -1;
 #pragma unroll
-        for (int c = 0; c < kPerThread; ++c) {
-            const int64_t i = ib + c;
-            gapv[c] = -1;
-            nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
-            xv[c] = i < kt ? vl[i] : 0.0f;
-            F += nfv[c];
+            for (int c = 0; c < kPerThread; ++c) {
+                nfv[c] = fillers_after(prev, cur[c], nt, bad, gapv[c]);
+                prev = cur[c];
+                F += nfv[c];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < kPerThread; ++c) {
+                const int64_t i = ib + c;
+                gapv[c] = -1;
+                nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
+                xv[c] = i < kt ? vl[i] : 0.0f;
+                F += nfv[c];
+            }
         }
         if (bad) latch_error(sc, kErrCorrupt);
         uint32_t pre = 0, tot = 0;
-        if (__syncthreads_or(F != 0))  // fillers are rare: skip the scan
+        const bool anyF = __syncthreads_or(F != 0);
+        if (anyF)  // fillers are rare: skip the scan
             pre = block_exclusive_scan(F, lds, tot);
+        else if (vout && (carry & (kPerThread - 1)) == 0) {  // uniform
+            // entry i lands at slot i + carry
+            const int64_t pos = ib + carry;
+            if (ib + kPerThread <= kt && pos + kPerThread <= cap && gapv[0] >= 0 &&
+                gapv[1] >= 0 && gapv[2] >= 0 && gapv[3] >= 0) {
+                const uint2 r = make_uint2(
+                    uint32_t(gapv[0] & 0xFFFF) | (uint32_t(gapv[1] & 0xFFFF) << 16),
+                    uint32_t(gapv[2] & 0xFFFF) | (uint32_t(gapv[3] & 0xFFFF) << 16));
+                *reinterpret_cast<uint2*>(runs + eb + pos) = r;
+                *reinterpret_cast<float4*>(vals + eb + pos) =
+                    make_float4(xv[0], xv[1], xv[2], xv[3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < kPerThread; ++c)
+                    if (ib + c < kt && gapv[c] >= 0 && pos + c < cap) {
+                        runs[eb + pos + c] = uint16_t(gapv[c] & 0xFFFF);
+                        vals[eb + pos + c] = xv[c];
+                    }
+            }
+            vt += gridDim.x;
+            continue;
+        }
         // entry i lands at slot i + carry + (fillers of entries <= i); its
         // own fillers fill the slots just before it.  sslot: slot - i0 -
         // carry (below 1024 * 65537), or kNoKey for no entry.
@@ -224,16 +285,6 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
 
 // ---------------------------------------------------------------- decode
 
-// Each tensor's stream capacity is a multiple of kStreamAlign entries, so
-// a thread's kPerThread consecutive entries (a multiple of kPerThread from
-// the stream start) sit at 8-byte aligned runs and 16-byte aligned values
-// whenever the arrays themselves are 16-byte aligned: one load each.
-constexpr int64_t kStreamAlign = 8;
-static_assert(kStreamAlign % kPerThread == 0 && kPerThread == 4, "vector stream loads");
-
-__device__ __forceinline__ bool aligned_as(const void* p, uintptr_t a) {
-    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
-}
 
 // (run + 1) of the thread's entries ib .. ib + 3 (0 past E).
 __device__ __forceinline__ void load_run_weights(const uint16_t* __restrict__ r, int64_t ib,
