@@ -82,10 +82,11 @@ int64_t piece_cap(int64_t n, int64_t kmax) {
     return std::min<int64_t>(kPiece, cdiv(6 * kPiece * kmax, n) + 24);
 }
 
-// Capacity of a tensor's ordered candidate list.
+// Capacity of a tensor's ordered candidate list, a multiple of 4 items so
+// that every tensor's list starts 16-byte aligned.
 int64_t list_cap(int64_t n, int64_t kmax, int64_t slots) {
     if (n <= kSmallN) return 0;
-    return std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384);
+    return cdiv(std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384), 4) * 4;
 }
 
 // Bin-local pieces are L * floor(1024 / L) elements, never fewer than 513

@@ -466,6 +466,26 @@ __device__ __forceinline__ const float* source_values(uint32_t mode, const float
     return mode == kModeDense ? v + L.o[t] : olist_v + L.obase[t];
 }
 
+// Items ib .. ib + kPerThread - 1 of a selection source (0 past len): one
+// 16-byte load when they are all there and 16-byte aligned (candidate lists
+// start 16-byte aligned; a tensor's v does when its offset is a multiple of
+// 4).
+__device__ __forceinline__ void load_items(const float* __restrict__ src, int64_t ib,
+                                           int64_t len, float (&x)[kPerThread]) {
+    static_assert(kPerThread == 4, "one float4 per thread");
+    if (ib + kPerThread <= len &&
+        (reinterpret_cast<uintptr_t>(src + ib) & 15) == 0) {
+        const float4 y = *reinterpret_cast<const float4*>(src + ib);
+        x[0] = y.x;
+        x[1] = y.y;
+        x[2] = y.z;
+        x[3] = y.w;
+    } else {
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) x[q] = ib + q < len ? src[ib + q] : 0.0f;
+    }
+}
+
 template <int D>
 struct Digit;
 template <> struct Digit<0> { static constexpr int shift = 20, bits = 11; };
@@ -518,18 +538,14 @@ __global__ __launch_bounds__(kBlock) void k_hist(
             if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
             cur_t = t;
         }
-        const int64_t i0 = int64_t(a - ab) * kTile;
-        // all of the tile's loads first, then the LDS increments: one wait
-        // for memory per tile
+        // a thread's kPerThread consecutive items (a histogram does not
+        // depend on the order): one 16-byte load when the source allows
+        const int64_t ib = int64_t(a - ab) * kTile + int64_t(threadIdx.x) * kPerThread;
         float x[kPerThread];
+        load_items(src, ib, len, x);
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
-            const int64_t i = i0 + q * kBlock + threadIdx.x;
-            x[q] = i < len ? src[i] : 0.0f;
-        }
-#pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            if (i0 + q * kBlock + threadIdx.x >= len) break;
+            if (ib + q >= len) break;
             const uint32_t key = mag_key(x[q]);
             if (D == 0 || (key >> (shift + bits)) == prefix)
                 atomicAdd(&h[(key >> shift) & dmask], 1u);
@@ -609,13 +625,16 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
             ae = aoff[t + 1];
             src = source_values(mode, v, olist_v, L, t);
         }
-        const int64_t i0 = int64_t(a - ab) * kTile;
+        // a thread's kPerThread consecutive items (the tile's counts do not
+        // depend on the order)
+        const int64_t ib = int64_t(a - ab) * kTile + int64_t(threadIdx.x) * kPerThread;
+        float x[kPerThread];
+        load_items(src, ib, len, x);
         uint32_t cnt = 0;
-#pragma unroll 4
+#pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = i0 + q * kBlock + threadIdx.x;
-            if (i < len) {
-                uint32_t key = mag_key(src[i]);
+            if (ib + q < len) {
+                const uint32_t key = mag_key(x[q]);
                 cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
             }
         }
