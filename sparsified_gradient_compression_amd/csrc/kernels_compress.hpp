@@ -470,19 +470,21 @@ __device__ __forceinline__ const float* source_values(uint32_t mode, const float
 // 16-byte load when they are all there and 16-byte aligned (candidate lists
 // start 16-byte aligned; a tensor's v does when its offset is a multiple of
 // 4).
-__device__ __forceinline__ void load_items(const float* __restrict__ src, int64_t ib,
-                                           int64_t len, float (&x)[kPerThread]) {
-    static_assert(kPerThread == 4, "one float4 per thread");
+template <typename T>
+__device__ __forceinline__ void load_items(const T* __restrict__ src, int64_t ib, int64_t len,
+                                           T (&x)[kPerThread]) {
+    static_assert(kPerThread == 4 && sizeof(T) == 4, "one 16-byte load per thread");
     if (ib + kPerThread <= len &&
         (reinterpret_cast<uintptr_t>(src + ib) & 15) == 0) {
-        const float4 y = *reinterpret_cast<const float4*>(src + ib);
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        const T4 y = *reinterpret_cast<const T4*>(src + ib);
         x[0] = y.x;
         x[1] = y.y;
         x[2] = y.z;
         x[3] = y.w;
     } else {
 #pragma unroll
-        for (int q = 0; q < kPerThread; ++q) x[q] = ib + q < len ? src[ib + q] : 0.0f;
+        for (int q = 0; q < kPerThread; ++q) x[q] = ib + q < len ? src[ib + q] : T(0);
     }
 }
 
@@ -700,7 +702,9 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     const uint32_t* __restrict__ off_gt, const uint32_t* __restrict__ off_eq,
     uint32_t* __restrict__ out_idx,
     float* __restrict__ out_val, Scalars* __restrict__ sc) {
-    __shared__ uint32_t lds2[2 * kWavesPerBlock];
+    __shared__ uint32_t lds2[kWavesPerBlock];
+    __shared__ uint32_t s_idx[kTile];
+    __shared__ float s_val[kTile];
     const uint32_t A = aoff[L.T];
     // current tensor: active tiles [ab, ae)
     uint32_t ab = 0, ae = 0, T = 0, r = 0;
@@ -732,48 +736,61 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
             ab = aoff[t];
             ae = aoff[t + 1];
         }
-        const int64_t i0 = int64_t(a - ab) * kTile;
-        uint32_t cg = off_gt[a], ce = off_eq[a];
+        // A thread takes 4 consecutive items (vector loads; on the list path
+        // the saved u comes too, the items not sent need it).  One block
+        // scan of the packed (#key > T, #key == T) counts gives each item
+        // its place in index order; the sent items are staged in LDS by
+        // their rank among the tile's sent items and stored coalesced.
+        const uint32_t cg = off_gt[a], ce = off_eq[a];
+        const int64_t ib = int64_t(a - ab) * kTile + int64_t(threadIdx.x) * kPerThread;
         bool bad = false;
-        // every item of the tile is loaded before the first prefix round, so
-        // the rounds' block-wide barriers do not each wait for memory; on
-        // the list path the saved u comes too (the items not sent need it)
-        float val[kPerThread], usv[kPerThread];
+        float val[kPerThread], usv[kPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
         uint32_t lidx[kPerThread];
+        load_items(src, ib, len, val);
+        if (dense) {
 #pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            const int64_t i = i0 + q * kBlock + threadIdx.x;
-            const bool ok = i < len;
-            val[q] = ok ? src[i] : 0.0f;
-            lidx[q] = ok ? (dense ? uint32_t(i) : oli[i]) : 0u;
-            usv[q] = ok && !dense ? olu[i] : 0.0f;
+            for (int q = 0; q < kPerThread; ++q) lidx[q] = uint32_t(ib + q);
+        } else {
+            load_items(oli, ib, len, lidx);
+            load_items(olu, ib, len, usv);
         }
+        bool gt[kPerThread], eq[kPerThread];
+        uint32_t c = 0;
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
-            if (i0 + q * kBlock >= len) break;  // uniform
-            const bool ok = i0 + q * kBlock + threadIdx.x < len;
+            const bool ok = ib + q < len;
             const uint32_t key = mag_key(val[q]);
-            const bool gt = ok && key > T, eq = ok && key == T;
-            uint32_t pg, pe, tg, te;
-            block_flag_prefix2(gt, eq, lds2, pg, pe, tg, te);
-            const uint32_t gb = cg + pg, eb = ce + pe;
+            gt[q] = ok && key > T;
+            eq[q] = ok && key == T;
+            c += (gt[q] ? (1u << 16) : 0u) + (eq[q] ? 1u : 0u);
+        }
+        uint32_t tot;
+        const uint32_t pre = block_exclusive_scan(c, lds2, tot);
+        // items sent before the tile, and by the end of it
+        const uint32_t sent0 = cg + min(ce, r);
+        const uint32_t sent1 = cg + (tot >> 16) + min(ce + (tot & 0xFFFFu), r);
+        uint32_t gb = cg + (pre >> 16), eb = ce + (pre & 0xFFFFu);
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
             bool send = false;
             uint32_t slot = 0;
-            if (gt) { send = true; slot = gb + min(eb, r); }
-            else if (eq && eb < r) { send = true; slot = gb + eb; }
+            if (gt[q]) { send = true; slot = gb + min(eb, r); }
+            else if (eq[q] && eb < r) { send = true; slot = gb + eb; }
+            gb += gt[q];
+            eb += eq[q];
             if (send) {
                 // never write outside the outputs, whatever the counts say
-                if (int64_t(slot) >= kt || int64_t(lidx[q]) >= nt) {
+                if (int64_t(slot) >= kt || int64_t(lidx[q]) >= nt || slot - sent0 >= kTile) {
                     bad = true;
                 } else {
-                    oi[slot] = lidx[q];
-                    ov[slot] = val[q];
+                    s_idx[slot - sent0] = lidx[q];
+                    s_val[slot - sent0] = val[q];
                     if (dense) {
                         u[o + lidx[q]] = 0.0f;
                         vt_[lidx[q]] = 0.0f;
                     }
                 }
-            } else if (ok && !dense) {
+            } else if (ib + q < len && !dense) {
                 if (int64_t(lidx[q]) >= nt) {
                     bad = true;
                 } else {
@@ -781,9 +798,16 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
                     vt_[lidx[q]] = val[q];
                 }
             }
-            cg += tg;
-            ce += te;
         }
+        __syncthreads();
+        const uint32_t ns = min(sent1 - sent0, uint32_t(kTile));
+        for (uint32_t e = threadIdx.x; e < ns; e += kBlock) {
+            if (int64_t(sent0 + e) < kt) {
+                oi[sent0 + e] = s_idx[e];
+                ov[sent0 + e] = s_val[e];
+            }
+        }
+        __syncthreads();  // before the next tile overwrites the stage
         if (bad) latch_error(sc, kErrInternal);
     }
 }
