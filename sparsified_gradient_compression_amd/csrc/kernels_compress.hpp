@@ -126,41 +126,62 @@ __global__ __launch_bounds__(kBlock) void k_norm_final(
 
 // Keys of the would-be v on sampled lines.  Block b belongs to one tensor
 // (smap); it visits kLinesPerSampleBlock of the tensor's sampled lines, one
-// 32-lane group per line.  Sampled line j lies at a hashed offset inside
+// 8-lane group per line (16 bytes of each of g, u, v per lane).  Sampled line j lies at a hashed offset inside
 // the j-th of slines equal strides, so sampling does not alias with the
 // tensor's row structure.  Level 0 histograms the top 11 key bits; level 1
 // revisits the same lines and histograms the next 10 bits of the keys whose
 // top 11 bits equal the bin chosen by level 0.
-// A block's sampled lines are shared out to its 32-lane groups: group grp
+// A block's sampled lines are shared out to its 8-lane groups: group grp
 // takes lines j0 + grp + kSampleGroups q (q < kLinesPerGroup) of [j0, j1);
 // sampled line j of a tensor with `stride` lines per sampled line lies at
 // j * stride + mix32(j * 0x9E3779B9 ^ t * 0x7F4A7C15) mod stride.  The keys
 // of the would-be v there: every load is issued before the first update,
-// so a group waits for memory once, not once per line.  ok[q] is false
+// so a group waits for memory once, not once per line.  ok[q][c] is false
 // past j1 or past the tensor's end.
-constexpr int kSampleGroups = kBlock / 32;
+constexpr int kLineLanes = int(kLine / 4);  // 16 bytes per lane and array
+constexpr int kSampleGroups = kBlock / kLineLanes;
 constexpr int kLinesPerGroup = int(kLinesPerSampleBlock / kSampleGroups);
 __device__ __forceinline__ void sample_line_keys(
     const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ v,
     int64_t o, int64_t nt, int t, int64_t stride, int64_t j0, int64_t j1, float s, float m,
-    uint32_t (&key)[kLinesPerGroup], bool (&ok)[kLinesPerGroup]) {
-    const int grp = int(threadIdx.x) >> 5, gl = int(threadIdx.x) & 31;
-    float gg[kLinesPerGroup], uu[kLinesPerGroup], vv[kLinesPerGroup];
+    uint32_t (&key)[kLinesPerGroup][4], bool (&ok)[kLinesPerGroup][4]) {
+    const int grp = int(threadIdx.x) / kLineLanes, gl = int(threadIdx.x) % kLineLanes;
+    float gg[kLinesPerGroup][4], uu[kLinesPerGroup][4], vv[kLinesPerGroup][4];
 #pragma unroll
     for (int q = 0; q < kLinesPerGroup; ++q) {
         const int64_t j = j0 + grp + int64_t(q) * kSampleGroups;
         const uint32_t r = mix32(uint32_t(j) * 0x9E3779B9u ^ uint32_t(t) * 0x7F4A7C15u);
-        const int64_t e = (j * stride + int64_t(r % uint64_t(stride))) * kLine + gl;
-        ok[q] = j < j1 && e < nt;
-        gg[q] = ok[q] ? g[o + e] : 0.0f;
-        uu[q] = ok[q] ? u[o + e] : 0.0f;
-        vv[q] = ok[q] ? v[o + e] : 0.0f;
+        const int64_t e = (j * stride + int64_t(r % uint64_t(stride))) * kLine + 4 * gl;
+        const bool line = j < j1;
+        const float *pg = g + o + e, *pu = u + o + e, *pv = v + o + e;
+        if (line && e + 4 <= nt &&
+            ((reinterpret_cast<uintptr_t>(pg) | reinterpret_cast<uintptr_t>(pu) |
+              reinterpret_cast<uintptr_t>(pv)) & 15) == 0) {
+            const float4 a = *reinterpret_cast<const float4*>(pg);
+            const float4 b = *reinterpret_cast<const float4*>(pu);
+            const float4 c = *reinterpret_cast<const float4*>(pv);
+            gg[q][0] = a.x; gg[q][1] = a.y; gg[q][2] = a.z; gg[q][3] = a.w;
+            uu[q][0] = b.x; uu[q][1] = b.y; uu[q][2] = b.z; uu[q][3] = b.w;
+            vv[q][0] = c.x; vv[q][1] = c.y; vv[q][2] = c.z; vv[q][3] = c.w;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) ok[q][c4] = true;
+        } else {
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                ok[q][c4] = line && e + c4 < nt;
+                gg[q][c4] = ok[q][c4] ? pg[c4] : 0.0f;
+                uu[q][c4] = ok[q][c4] ? pu[c4] : 0.0f;
+                vv[q][c4] = ok[q][c4] ? pv[c4] : 0.0f;
+            }
+        }
     }
 #pragma unroll
-    for (int q = 0; q < kLinesPerGroup; ++q) {
-        momentum_update(gg[q], s, m, uu[q], vv[q]);
-        key[q] = mag_key(vv[q]);
-    }
+    for (int q = 0; q < kLinesPerGroup; ++q)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            momentum_update(gg[q][c4], s, m, uu[q][c4], vv[q][c4]);
+            key[q][c4] = mag_key(vv[q][c4]);
+        }
 }
 
 template <int LEVEL>
@@ -183,15 +204,18 @@ __global__ __launch_bounds__(kBlock) void k_sample(
     const int64_t j0 = (sb - L.sbase[t]) * kLinesPerSampleBlock;
     const int64_t j1 = min(ls, j0 + kLinesPerSampleBlock);
     const float s = clip_on ? sc->scale : 1.0f;
-    uint32_t key[kLinesPerGroup];
-    bool ok[kLinesPerGroup];
+    uint32_t key[kLinesPerGroup][4];
+    bool ok[kLinesPerGroup][4];
     sample_line_keys(g, u, v, o, nt, t, stride, j0, j1, s, m, key, ok);
 #pragma unroll
-    for (int q = 0; q < kLinesPerGroup; ++q) {
-        if (!ok[q]) continue;
-        if (LEVEL == 0) atomicAdd(&h[key[q] >> 20], 1u);
-        else if ((key[q] >> 20) == wbin) atomicAdd(&h[(key[q] >> 10) & 1023u], 1u);
-    }
+    for (int q = 0; q < kLinesPerGroup; ++q)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            if (!ok[q][c4]) continue;
+            const uint32_t kk = key[q][c4];
+            if (LEVEL == 0) atomicAdd(&h[kk >> 20], 1u);
+            else if ((kk >> 20) == wbin) atomicAdd(&h[(kk >> 10) & 1023u], 1u);
+        }
     __syncthreads();
     uint32_t* row = shist + int64_t(t) * kHistBins;
     for (int b = threadIdx.x; b < kBins0; b += kBlock)

@@ -54,16 +54,19 @@ __global__ __launch_bounds__(kBlock) void k_sm_hist(
     const int64_t j0 = (sb - A.sbase[t]) * kLinesPerSampleBlock;
     const int64_t j1 = min(ls, j0 + kLinesPerSampleBlock);
     const float s = clip_on ? sc->scale : 1.0f;
-    uint32_t key[kLinesPerGroup];
-    bool ok[kLinesPerGroup];
+    uint32_t key[kLinesPerGroup][4];
+    bool ok[kLinesPerGroup][4];
     sample_line_keys(g, u, v, o, nt, t, stride, j0, j1, s, m, key, ok);
 #pragma unroll
-    for (int q = 0; q < kLinesPerGroup; ++q) {
-        if (!ok[q]) continue;
-        if (LEVEL == 0) atomicAdd(&h[key[q] >> 20], 1u);
-        else if (LEVEL == 1 && (key[q] >> 20) == sel) atomicAdd(&h[(key[q] >> 10) & 1023u], 1u);
-        else if (LEVEL == 2 && (key[q] >> 10) == sel) atomicAdd(&h[key[q] & 1023u], 1u);
-    }
+    for (int q = 0; q < kLinesPerGroup; ++q)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            if (!ok[q][c4]) continue;
+            const uint32_t kk = key[q][c4];
+            if (LEVEL == 0) atomicAdd(&h[kk >> 20], 1u);
+            else if (LEVEL == 1 && (kk >> 20) == sel) atomicAdd(&h[(kk >> 10) & 1023u], 1u);
+            else if (LEVEL == 2 && (kk >> 10) == sel) atomicAdd(&h[kk & 1023u], 1u);
+        }
     __syncthreads();
     uint32_t* row = shist + int64_t(t) * kHistBins;
     for (int b = threadIdx.x; b < bins; b += kBlock)
