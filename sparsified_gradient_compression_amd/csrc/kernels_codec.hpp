@@ -540,10 +540,6 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
 
 typedef float dec_f4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bool aligned16(const float* p) {
-    return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
-}
-
 // A fresh sum whose tensors are all scattered: dense[0, n) = +0.0 first.
 // 16-byte stores from the first 16-byte boundary on, kDecBlock / 4 of them
 // per workgroup; workgroup 0 also writes the head and the tail.  Plain
@@ -652,7 +648,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_merge(
         }
     }
     float* d = dense + o + lo_pos;
-    const bool vec = len == kDecBlock && aligned16(d);  // uniform
+    const bool vec = len == kDecBlock && aligned_as(d, 16);  // uniform
     constexpr int kQ = int(kDecBlock / kBlock);       // values per thread
     float reg[kQ];
     if (vec) {
