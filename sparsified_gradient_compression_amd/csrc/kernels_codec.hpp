@@ -474,18 +474,22 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         uint32_t wv[kPerThread];
         float xv[kPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
         load_run_weights(runs + eb, ib, E, aligned_as(runs + eb, 8), wv);
-        if (!merged) {  // uniform
-            if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
-                const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
-                xv[0] = x.x;
-                xv[1] = x.y;
-                xv[2] = x.z;
-                xv[3] = x.w;
-            } else {
+        // The values are loaded on the merged path too, where they are not
+        // added here: the merge pass reads them next and then finds them in
+        // cache instead of waiting on HBM at the end of its chain of loads
+        // (fresh 2^30-element sum of 4 learners: 0.93 -> 0.81 ms).
+        if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
+            const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
+            xv[0] = x.x;
+            xv[1] = x.y;
+            xv[2] = x.z;
+            xv[3] = x.w;
+        } else {
 #pragma unroll
-                for (int c = 0; c < kPerThread; ++c) xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
-            }
+            for (int c = 0; c < kPerThread; ++c) xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
         }
+        if (merged)  // keep the loads: their values are not used on this path
+            asm volatile("" ::"v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
         const uint32_t s = wv[0] + wv[1] + wv[2] + wv[3];
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan(s, lds, tot);
