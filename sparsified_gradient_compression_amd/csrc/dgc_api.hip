@@ -1040,6 +1040,9 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
                 const int64_t cap = p.ebase[size_t(t) + 1] - p.ebase[size_t(t)];
                 merge_on = nt > 0 && kDecMergeAcc * int64_t(nbw) * cap >= nt;
             }
+        // the bounds passes also load the values (for the merge to find in
+        // cache) when the batch's value capacity is at most kDecWarmBytes
+        const bool warm = merge_on && int64_t(nbw) * p.E * 4 <= kDecWarmBytes;
         DecBatch S{};
         S.W = nbw;
         for (int w = 0; w < nbw; ++w) {
@@ -1061,7 +1064,7 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
                 k_dec_scan<false><<<T, kBlock, 0, stream>>>(st->L, S.entries[w], st->ta, st->t64);
             k_dec_write<<<pg, kBlock, 0, stream>>>(st->L, S.runs[w], S.vals[w], S.entries[w],
                                                    st->t64, dense, st->sc, p.ET,
-                                                   int(merge_on), st->Dd, w);
+                                                   int(merge_on), st->Dd, w, int(warm));
             DGC_LAUNCH_CHECK();
         }
         if (merge_on)

@@ -325,6 +325,10 @@ constexpr int64_t kXcds = 8;  // XCDs of an MI355X (block order of the merge pas
 // that could hold n_t / kDecMergeFresh entries are a small part of the
 // layout: then the host zeroes the sum and every tensor is scattered.
 constexpr int64_t kDecMergeAcc = 16, kDecMergeFresh = 256;
+// Value bytes of a batch's streams (at capacity) up to which the bounds
+// passes also load the values: a quarter of MI355X's 256 MB last-level
+// cache.
+constexpr int64_t kDecWarmBytes = int64_t(64) << 20;
 constexpr uint32_t kDecScatter = 0, kDecMerge = 1;
 constexpr uint32_t kBselMerged = 0x80000000u;
 
@@ -437,7 +441,8 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
     DevLayout L, const uint16_t* __restrict__ runs,
     const float* __restrict__ vals, const int64_t* __restrict__ entries,
     const uint64_t* __restrict__ tile_p, float* __restrict__ dense,
-    Scalars* __restrict__ sc, int64_t n_etiles, int merge_on, DevDec Dd, int slot) {
+    Scalars* __restrict__ sc, int64_t n_etiles, int merge_on, DevDec Dd, int slot,
+    int warm) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t trel[kTile];
     __shared__ float tval[kTile];
@@ -474,22 +479,28 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         uint32_t wv[kPerThread];
         float xv[kPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
         load_run_weights(runs + eb, ib, E, aligned_as(runs + eb, 8), wv);
-        // The values are loaded on the merged path too, where they are not
-        // added here: the merge pass reads them next and then finds them in
-        // cache instead of waiting on HBM at the end of its chain of loads
-        // (fresh 2^30-element sum of 4 learners: 0.93 -> 0.81 ms).
-        if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
-            const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
-            xv[0] = x.x;
-            xv[1] = x.y;
-            xv[2] = x.z;
-            xv[3] = x.w;
-        } else {
+        // With warm set the values are loaded on the merged path too, where
+        // they are not added here: the merge pass reads them next and then
+        // finds them in cache instead of waiting on HBM at the end of its
+        // chain of loads (fresh 2^30-element sum of 4 sparse learners: 0.93
+        // -> 0.81 ms).  The host sets it only when the batch's values fit
+        // well inside the last-level cache; larger ones would only be read
+        // twice.
+        if (!merged || warm) {  // uniform
+            if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
+                const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
+                xv[0] = x.x;
+                xv[1] = x.y;
+                xv[2] = x.z;
+                xv[3] = x.w;
+            } else {
 #pragma unroll
-            for (int c = 0; c < kPerThread; ++c) xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
+                for (int c = 0; c < kPerThread; ++c)
+                    xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
+            }
+            if (merged)  // keep the loads: their values are not used on this path
+                asm volatile("" ::"v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
         }
-        if (merged)  // keep the loads: their values are not used on this path
-            asm volatile("" ::"v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
         const uint32_t s = wv[0] + wv[1] + wv[2] + wv[3];
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan(s, lds, tot);
