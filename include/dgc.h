@@ -65,7 +65,10 @@ extern "C" {
                                    slots) -- the same results, slower */
 #define DGC_OPT_KERNEL_TIMING 2 /* value 1: bracket the work of each call with
                                    HIP events on the call's stream (read with
-                                   dgc_get_kernel_time); 0: off (default) */
+                                   dgc_get_kernel_time); 2: only the
+                                   element-wise pass (DGC_TIMER_FUSED, two
+                                   events per compress call); 0: off
+                                   (default) */
 #define DGC_OPT_DECODE_PATH 3   /* dgc_decode_accumulate, per tensor: 0
                                    automatic (default: merged when the
                                    learners' streams hold at least n_t / 16
@@ -94,6 +97,21 @@ extern "C" {
 #define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate */
 
 typedef struct dgc_state dgc_state;
+
+/*
+ * Warm-up schedule (DGC review, "Proposed method": warm-up starts at a low
+ * sparsity and raises it step by step): the number of entries a tensor of
+ * n elements sends at density num / den,
+ *   k = ceil(n * num / den),
+ * computed in exact integer arithmetic (128-bit product).  The density is
+ * a fraction, never a binary floating-point number: ceil(350e6 * (1 -
+ * 0.999)) in binary64 is 350001, not 350000.
+ *   n          element count, n >= 0
+ *   num, den   density numerator and denominator, 0 <= num <= den, den >= 1
+ * Returns k (0 <= k <= n), or DGC_EINVAL (negative) for arguments outside
+ * those ranges.  Pure host arithmetic: no state, no GPU, thread-safe.
+ */
+int64_t dgc_k_for_density(int64_t n, int64_t num, int64_t den);
 
 /*
  * Workspace size for a layout.

@@ -267,7 +267,7 @@ struct Timer {
 
 struct dgc_state {
     Plan plan;
-    bool timing = false;
+    int timing = 0;  // DGC_OPT_KERNEL_TIMING: 0 off, 1 every timer, 2 the element-wise pass
     Timer timers[4];
     float m = 0.9f;
     float* u = nullptr;
@@ -328,8 +328,12 @@ int timer_collect(Timer& tm, int slot) {
     return DGC_OK;
 }
 
+bool timer_on(const dgc_state* st, int which) {
+    return st->timing == 1 || (st->timing == 2 && which == DGC_TIMER_FUSED);
+}
+
 int timer_begin(dgc_state* st, int which, hipStream_t s) {
-    if (!st->timing) return DGC_OK;
+    if (!timer_on(st, which)) return DGC_OK;
     Timer& tm = st->timers[which];
     if (!tm.created) {
         for (int i = 0; i < Timer::kRing; ++i)
@@ -346,7 +350,7 @@ int timer_begin(dgc_state* st, int which, hipStream_t s) {
 }
 
 int timer_end(dgc_state* st, int which, hipStream_t s) {
-    if (!st->timing) return DGC_OK;
+    if (!timer_on(st, which)) return DGC_OK;
     Timer& tm = st->timers[which];
     if (tm.open < 0) return DGC_OK;
     if (hipEventRecord(tm.stop[tm.open], s) != hipSuccess) return DGC_EHIP;
@@ -526,6 +530,12 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
 }  // namespace
 
 extern "C" {
+
+int64_t dgc_k_for_density(int64_t n, int64_t num, int64_t den) {
+    if (n < 0 || den < 1 || num < 0 || num > den) return DGC_EINVAL;
+    const __int128 p = __int128(n) * num;
+    return int64_t((p + den - 1) / den);  // <= n because num <= den
+}
 
 int dgc_workspace_bytes(int32_t n_tensors, const int64_t* sizes,
                         const int64_t* k_max, size_t* bytes) {
@@ -1050,9 +1060,14 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
             S.vals[w] = vals[b0 + w];
             S.entries[w] = entries[b0 + w];
         }
+        // A fresh batch that merges merges every tensor, each block starting
+        // at +0.0; one that zero-filled dense first is an accumulate batch
+        // from there on (each tensor merged only where its streams are
+        // dense enough).
+        const bool merge_fresh = fresh_batch && !fill_all;
         if (merge_on)
             k_dec_mode<<<int(cdiv(p.NBLK, kBlock)), kBlock, 0, stream>>>(
-                st->L, S, st->Dd, fresh_batch ? 2 : st->decode_path, p.NBLK);
+                st->L, S, st->Dd, merge_fresh ? 2 : st->decode_path, p.NBLK);
         if (fill_all && p.n > 0)
             k_dec_fill<<<int(cdiv(p.n, kDecBlock)), kBlock, 0, stream>>>(dense, p.n);
         for (int w = 0; w < nbw; ++w) {
@@ -1069,7 +1084,7 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
         }
         if (merge_on)
             k_dec_merge<<<int(kXcds * cdiv(p.NBLK, kXcds)), kBlock, 0, stream>>>(
-                st->L, S, st->Dd, dense, p.NBLK, int(fresh_batch));
+                st->L, S, st->Dd, dense, p.NBLK, int(merge_fresh));
         DGC_LAUNCH_CHECK();
     }
     DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
@@ -1167,8 +1182,8 @@ int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
         return DGC_OK;
     }
     if (option == DGC_OPT_KERNEL_TIMING) {
-        if (value != 0 && value != 1) return DGC_EINVAL;
-        st->timing = value == 1;
+        if (value < 0 || value > 2) return DGC_EINVAL;
+        st->timing = int(value);
         return DGC_OK;
     }
     return DGC_EINVAL;

@@ -40,9 +40,8 @@ class DGCError(RuntimeError):
 
 
 def lib_path() -> str:
-    """The library to load: DGC_LIBRARY if set (an alternative build of the
-    same sources), else the in-tree build."""
-    return os.environ.get("DGC_LIBRARY") or _build.LIB
+    """The library this binding loads: the in-tree build, always."""
+    return _build.LIB
 
 
 def lib() -> ctypes.CDLL:
@@ -58,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
+    L.dgc_k_for_density.argtypes = [i64, i64, i64]
+    L.dgc_k_for_density.restype = i64
     L.dgc_workspace_bytes.argtypes = [i32, P, P, ctypes.POINTER(ctypes.c_size_t)]
     L.dgc_workspace_bytes.restype = ctypes.c_int
     L.dgc_init_state.argtypes = [ctypes.POINTER(P), i32, P, P, ctypes.c_float,
@@ -286,14 +287,37 @@ def dgc_destroy_state(st):
     lib().dgc_destroy_state(st)
 
 
-# ---------------------------------------------------------------- host logic
+def _density_fraction(density) -> Tuple[int, int]:
+    """(num, den) of an exact density: a Fraction, an int, or a (num, den)
+    pair.  Binary floating point is refused: 1 / 1000 is not 1/1000."""
+    if isinstance(density, tuple) and len(density) == 2:
+        num, den = density
+        if not all(isinstance(x, (int, np.integer)) and not isinstance(x, bool)
+                   for x in (num, den)):
+            raise TypeError("density (num, den) must be integers")
+        return int(num), int(den)
+    if isinstance(density, (float, np.floating)):
+        raise TypeError("density must be exact (Fraction or (num, den)), not a "
+                        f"float: {density!r} is not an exact fraction in binary")
+    if isinstance(density, (Fraction, int, np.integer)) and not isinstance(density, bool):
+        d = Fraction(density)
+        return d.numerator, d.denominator
+    raise TypeError(f"density must be a Fraction, an int or (num, den), not "
+                    f"{type(density).__name__}")
 
-def k_for_density(n: int, density: Fraction) -> int:
-    """Warm-up schedule (DGC review, "Proposed method": sparsity rises step
-    by step): k = ceil(n * density) with density an exact fraction, in
-    integer arithmetic."""
-    d = Fraction(density)
-    return int(-((-int(n) * d.numerator) // d.denominator)) if n > 0 else 0
+
+def dgc_k_for_density(n: int, num: int, den: int) -> int:
+    k = int(lib().dgc_k_for_density(int(n), int(num), int(den)))
+    if k < 0:
+        raise DGCError(k, "dgc_k_for_density")
+    return k
+
+
+def k_for_density(n: int, density) -> int:
+    """Entries a tensor of n elements sends at an exact density (warm-up
+    schedule), computed by the library's dgc_k_for_density."""
+    num, den = _density_fraction(density)
+    return dgc_k_for_density(n, num, den)
 
 
 class Learner:

@@ -13,6 +13,16 @@ import oracle
 from sparsified_gradient_compression_amd import dgc
 
 
+def oracle_k(n, density):
+    """k for a tensor of n elements at an exact density, from the oracle's
+    own warm-up schedule; the library's (dgc_k_for_density) must agree."""
+    from fractions import Fraction
+    d = Fraction(density)
+    k = oracle.k_for_density(n, d.numerator, d.denominator)
+    assert dgc.k_for_density(n, d) == k, (n, d)
+    return k
+
+
 def f32_bits(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) >= 19, names
     L = dgc.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -103,16 +103,51 @@ def test_init_and_calls_reject_bad_arguments_before_any_launch():
     L.dgc_destroy_state(None)
 
 
-def test_k_schedule_host_logic():
+def test_k_schedule_through_the_c_symbol():
+    """dgc_k_for_density (DGC review, "Proposed method", warm-up): exact
+    ceil(n * num / den) in the library, called through the raw C symbol."""
+    L = dgc.lib()
+    assert L.dgc_k_for_density(350_000_000, 1, 1000) == 350_000
+    assert L.dgc_k_for_density(350_000_000, 1, 4) == 87_500_000
+    assert L.dgc_k_for_density(350_000_000, 1, 250) == 1_400_000
+    assert L.dgc_k_for_density(1 << 20, 1, 1000) == 1049
+    assert L.dgc_k_for_density(1 << 24, 1, 1000) == 16778
+    assert L.dgc_k_for_density(64, 1, 1000) == 1
+    assert L.dgc_k_for_density(0, 1, 1000) == 0
+    assert L.dgc_k_for_density(7, 0, 5) == 0
+    assert L.dgc_k_for_density(7, 5, 5) == 7
+    # the 128-bit product: n * num overflows int64 here
+    n, num, den = (1 << 62) + 3, (1 << 40) - 1, 1 << 40
+    assert L.dgc_k_for_density(n, num, den) == -(-n * num // den)
+    for bad in ((-1, 1, 2), (5, 1, 0), (5, -1, 2), (5, 3, 2)):
+        assert L.dgc_k_for_density(*bad) == dgc.DGC_EINVAL, bad
+
+
+def test_k_schedule_binding_is_exact():
     assert dgc.k_for_density(350_000_000, Fraction(1, 1000)) == 350_000
+    assert dgc.k_for_density(350_000_000, (1, 1000)) == 350_000
     assert dgc.k_for_density(1 << 20, Fraction(1, 1000)) == 1049
-    assert dgc.k_for_density(1 << 24, Fraction(1, 1000)) == 16778
     assert dgc.k_for_density(64, Fraction(1, 1000)) == 1
     assert dgc.k_for_density(0, Fraction(1, 1000)) == 0
+    assert dgc.k_for_density(10, 1) == 10
     for n in range(1, 3000, 7):
         for d in (Fraction(1, 4), Fraction(1, 250), Fraction(3, 7)):
             want = -(-n * d.numerator // d.denominator)
             assert dgc.k_for_density(n, d) == want
+
+
+def test_k_schedule_refuses_binary_floats():
+    """1 / 1000 in binary64 is slightly above 1/1000, so a float density
+    would give ceil(350e6 * 0.001) = 350001; the binding refuses it."""
+    for bad in (1 / 1000, 0.25, np.float32(0.5), np.float64(0.001)):
+        with pytest.raises(TypeError):
+            dgc.k_for_density(350_000_000, bad)
+    with pytest.raises(TypeError):
+        dgc.k_for_density(100, (1.0, 1000))
+    with pytest.raises(TypeError):
+        dgc.k_for_density(100, "1/1000")
+    with pytest.raises(dgc.DGCError):
+        dgc.k_for_density(100, Fraction(3, 2))
 
 
 def test_build_flags_keep_ieee_binary32():

@@ -231,3 +231,25 @@ def test_decode_sum_into_unaligned_dense(path, shift):
     assert np.array_equal(f32_bits(got[shift:shift + n]), f32_bits(want)), first_diff(
         got[shift:shift + n], want)
     assert (got[:shift] == 11.0).all() and (got[shift + n:] == 22.0).all()
+
+
+@pytest.mark.parametrize("W", [2, 4, 9])
+def test_decode_sum_small_capacity_mixed_layout(W):
+    """A fresh sum whose layout is mostly sparse (a 2^20 tensor with room for
+    n/10000 entries) but holds one small dense tensor (64 elements, full
+    capacity): the library zero-fills dense first and then merges only the
+    tensors whose streams are dense enough.  Bit for bit the oracle's
+    decode onto +0.0 on every path setting."""
+    sizes = [64, 1 << 20, 3]
+    kmax = [64, (1 << 20) // 10000, 3]
+    rng = np.random.default_rng([97, W])
+    L = dgc.Learner(sizes, kmax)
+    streams = make_streams(rng, sizes, [0.3] * W, L.cap)
+    n = sum(sizes)
+    want = reference(sizes, np.zeros(n, np.float32), streams)
+    for path in (0, 1, 2):
+        say(f"decode_sum small capacity W={W} path {path}")
+        got = decode_fresh(L, streams, n, path, guard=9.0)
+        assert L.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got[:n]), f32_bits(want)), (path, first_diff(got[:n], want))
+        assert (got[n:] == 9.0).all()

@@ -3,16 +3,19 @@
 resnet50 (25.6M, 161 tensors, 10 steps), deepspeech (122M, 4 learners) and
 warmup350m (350M, k from 87.5M down to 350k) are compared with the oracle in
 full.  flat1b (2**30 elements in 64 chunks, 4 learners x 3 steps) runs in
-the launch configuration the benchmark times; the oracle recomputes four
-sampled chunks per learner-step in full (its norm is over the whole
-gradient), and properties that hold at any size are checked on every chunk.
+the launch configuration the benchmark times and is compared with the oracle
+in full as well: every chunk's indices, values, stream and u/v state, for
+each of the three selectors, and the four learners' dense sum of every step.
+The learners run one after another (learner-major) so that the host holds
+one learner's oracle state (8 GiB) at a time; a learner's results do not
+depend on the others'.
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import f32_bits, first_diff, say
+from gpu_harness import f32_bits, first_diff, oracle_k, say
 from sparsified_gradient_compression_amd import dgc
 from sparsified_gradient_compression_amd import workloads as W
 from test_gpu_parity import run_workload
@@ -44,337 +47,174 @@ def test_warmup350m_full():
     run_workload(W.get("warmup350m"), tag="warm350m")
 
 
-SAMPLED = (0, 17, 42, 63)
+def _host(t):
+    return t.cpu().numpy()
 
 
-@pytest.mark.timeout(1200)
-def test_flat1b_full_sampled():
+def _flat1b_full(selector):
+    """flat1b at full size, compared with the oracle on all 64 chunks.
+
+    selector: "topk" (dgc_compress, k = ceil(n_t / 1000)), "binlocal"
+    (bins of 512, at most n_t / 8 delivered) or "sampled" (target k, at
+    most 4 k delivered)."""
     import torch
     wl = W.get("flat1b")
     C = wl.sizes[0]
     T = len(wl.sizes)
-    k = [dgc.k_for_density(C, wl.densities[0])] * T
+    sizes = np.array(wl.sizes, np.int64)
+    k = [oracle_k(C, wl.densities[0])] * T
     assert k[0] == 16778
+    if selector == "topk":
+        cap = list(k)
+    elif selector == "binlocal":
+        cap = [C // 8] * T
+    else:
+        cap = [4 * k[0]] * T
+    coff = np.concatenate([[0], np.cumsum(cap)])
     m = np.float32(wl.momentum)
-    learners = [dgc.Learner(list(wl.sizes), k, wl.momentum) for _ in range(wl.learners)]
-    # oracle state of the sampled chunks, per learner
-    ou = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
-    ov = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
     g_host = np.empty(wl.n, np.float32)
-    for t in range(wl.steps):
-        o_streams = []  # per learner: {chunk: (runs, vals)}
-        for w, L in enumerate(learners):
-            say(f"flat1b step {t} learner {w}: generate")
+    # per step: each learner's GPU stream (device copies) and oracle streams
+    gpu_st = [[] for _ in range(wl.steps)]
+    orc_st = [[] for _ in range(wl.steps)]
+    layout = None
+    for w in range(wl.learners):
+        L = dgc.Learner(list(wl.sizes), cap, wl.momentum)
+        ou = np.zeros(wl.n, np.float32)
+        ov = np.zeros(wl.n, np.float32)
+        for t in range(wl.steps):
+            tag = f"flat1b {selector} learner {w} step {t}"
+            say(f"{tag}: generate")
             W.gradient(wl, w, t, out=g_host)
             g = torch.from_numpy(g_host).cuda()
-            u_prev = L.u.clone()
-            v_prev = L.v.clone()
-            say(f"flat1b step {t} learner {w}: compress")
-            idx, val = L.compress(g, k, wl.clip)
-            L.encode(k)
+            say(f"{tag}: compress on the GPU")
+            if selector == "topk":
+                L.compress(g, k, wl.clip)
+                L.encode(k)
+            elif selector == "binlocal":
+                L.compress_binlocal(g, [512] * T, cap, wl.clip)
+                L.encode_counts(cap)
+            else:
+                L.compress_sampled(g, k, cap, wl.clip)
+                L.encode_counts(cap)
             torch.cuda.synchronize()
-            assert L.status() == dgc.DGC_OK
-            assert L.path_counts() == (T, 0)
+            del g
+            assert L.status() == dgc.DGC_OK, tag
+            say(f"{tag}: oracle")
+            if selector == "topk":
+                o_idx, o_val, o_norm, o_s = oracle.step(sizes, np.array(k), g_host, ou, ov,
+                                                        wl.momentum, wl.clip)
+                o_cnt = np.array(k, np.int64)
+                assert L.path_counts() == (T, 0), tag
+            elif selector == "binlocal":
+                o_idx, o_val, o_cnt, o_tot, o_norm, o_s = oracle.binlocal_step(
+                    sizes, [512] * T, cap, g_host, ou, ov, wl.momentum, wl.clip)
+            else:
+                o_idx, o_val, o_cnt, o_tot, o_th, o_norm, o_s = oracle.sampled_step(
+                    sizes, k, cap, g_host, ou, ov, wl.momentum, wl.clip)
+            say(f"{tag}: compare")
             norm = float(L.norm.cpu()[0])
             s = np.float32(L.scale.cpu()[0])
-            # ---- oracle on the sampled chunks
-            o_norm, o_s = oracle.clip_scale(g_host, wl.clip)
-            assert abs(norm - o_norm) <= 1e-6 * o_norm and s == o_s, (norm, o_norm, s, o_s)
-            gi = idx.cpu().numpy().view(np.uint32).reshape(T, k[0])
-            gvv = val.cpu().numpy().reshape(T, k[0])
-            cap = L.cap
-            runs = L.runs.cpu().numpy().view(np.uint16)
-            svals = L.vals.cpu().numpy()
-            ent = L.entries.cpu().numpy()
-            o_streams.append({})
-            for c in SAMPLED:
-                sl = slice(c * C, (c + 1) * C)
-                oracle.momentum(g_host[sl], o_s, m, ou[w][c], ov[w][c])
-                o_idx, o_val = oracle.select_mask(ou[w][c], ov[w][c], k[0])
-                assert np.array_equal(gi[c], o_idx), (t, w, c, first_diff(gi[c], o_idx))
-                assert np.array_equal(f32_bits(gvv[c]), f32_bits(o_val)), (t, w, c)
-                assert np.array_equal(f32_bits(L.u[sl].cpu().numpy()), f32_bits(ou[w][c]))
-                assert np.array_equal(f32_bits(L.v[sl].cpu().numpy()), f32_bits(ov[w][c]))
-                o_r, o_v = oracle.encode(o_idx, o_val, cap=int(cap[c + 1] - cap[c]))
-                assert ent[c] == o_r.size
-                assert np.array_equal(runs[cap[c]:cap[c] + ent[c]], o_r)
-                assert np.array_equal(f32_bits(svals[cap[c]:cap[c] + ent[c]]), f32_bits(o_v))
-                o_streams[-1][c] = (o_r, o_v)
-            # ---- properties on every chunk (torch on the GPU, separate ops:
-            # no contraction)
-            sd = torch.tensor(float(s), dtype=torch.float32, device="cuda")
-            md = torch.tensor(float(m), dtype=torch.float32, device="cuda")
-            u_new = torch.add(torch.mul(md, u_prev), torch.mul(g, sd))
-            v_pre = torch.add(v_prev, u_new)
-            del u_prev, v_prev
-            gidx = idx.long().view(T, k[0]) + torch.arange(T, device="cuda").view(T, 1) * C
-            assert bool((gidx[:, 1:] > gidx[:, :-1]).all())
-            gidx = gidx.flatten()
-            sent = torch.zeros_like(v_pre)
-            sent[gidx] = val
-            # sent + residual == accumulated v, bitwise
-            assert torch.equal((sent + L.v[: wl.n]).view(torch.int32),
-                               (v_pre + 0.0).view(torch.int32))
-            mask = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
-            mask[gidx] = True
-            assert bool((L.u[: wl.n][mask] == 0).all())
-            assert torch.equal(L.u[: wl.n][~mask].view(torch.int32),
-                               u_new[~mask].view(torch.int32))
-            keys = (v_pre.view(torch.int32) & 0x7FFFFFFF).view(T, C)
-            top = torch.topk(keys, k[0], dim=1).values
-            got_keys = (val.view(torch.int32) & 0x7FFFFFFF).view(T, k[0])
-            assert torch.equal(torch.sort(top, dim=1).values,
-                               torch.sort(got_keys, dim=1).values)
-            del sent, mask, keys, top, v_pre, u_new, g
-        # ---- decode of the four learners' streams, in learner order
-        say(f"flat1b step {t}: decode")
+            assert abs(norm - o_norm) <= 1e-6 * o_norm and s == o_s, (tag, norm, o_norm, s, o_s)
+            if selector == "topk":
+                gi = _host(L.idx[:int(sum(k))]).view(np.uint32)
+                gv = _host(L.val[:int(sum(k))])
+                cnt = o_cnt
+                assert np.array_equal(gi, o_idx), (tag, first_diff(gi, o_idx))
+                assert np.array_equal(f32_bits(gv), f32_bits(o_val)), tag
+            else:
+                cnt = _host(L.count)
+                tot = _host(L.total)
+                assert np.array_equal(cnt, o_cnt), (tag, first_diff(cnt, o_cnt))
+                assert np.array_equal(tot, o_tot), (tag, first_diff(tot, o_tot))
+                if selector == "sampled":
+                    # the count follows k (the sample's quantile), not exactly
+                    assert (tot > k[0] // 2).all() and (tot < 3 * k[0] // 2).all(), (
+                        tag, tot.min(), tot.max())
+                    info = L.select_info()
+                    assert (info[:, 0] == 3).all(), tag
+                    assert np.array_equal(info[:, 4], o_th.astype(np.int64)), tag
+                gi = _host(L.idx[:int(coff[-1])]).view(np.uint32)
+                gv = _host(L.val[:int(coff[-1])])
+                for c in range(T):
+                    a, b = coff[c], coff[c] + cnt[c]
+                    assert np.array_equal(gi[a:b], o_idx[a:b]), (tag, c)
+                    assert np.array_equal(f32_bits(gv[a:b]), f32_bits(o_val[a:b])), (tag, c)
+            gu = _host(L.u[: wl.n])
+            assert np.array_equal(f32_bits(gu), f32_bits(ou)), (tag, "u", first_diff(
+                f32_bits(gu), f32_bits(ou)))
+            del gu
+            gvv = _host(L.v[: wl.n])
+            assert np.array_equal(f32_bits(gvv), f32_bits(ov)), (tag, "v", first_diff(
+                f32_bits(gvv), f32_bits(ov)))
+            del gvv
+            # every chunk's stream, against the oracle's encoding
+            scap = L.cap
+            runs = _host(L.runs).view(np.uint16)
+            svals = _host(L.vals)
+            ent = _host(L.entries)
+            ostreams = []
+            kcum = np.concatenate([[0], np.cumsum(cnt)]) if selector == "topk" else coff
+            for c in range(T):
+                a = kcum[c]
+                o_r, o_v = oracle.encode(o_idx[a:a + cnt[c]], o_val[a:a + cnt[c]],
+                                         cap=int(scap[c + 1] - scap[c]))
+                assert ent[c] == o_r.size, (tag, c, ent[c], o_r.size)
+                assert np.array_equal(runs[scap[c]:scap[c] + ent[c]], o_r), (tag, c)
+                assert np.array_equal(f32_bits(svals[scap[c]:scap[c] + ent[c]]),
+                                      f32_bits(o_v)), (tag, c)
+                ostreams.append((o_r, o_v))
+            orc_st[t].append(ostreams)
+            gpu_st[t].append((L.runs.clone(), L.vals.clone(), L.entries.clone()))
+            del runs, svals
+        if layout is None:
+            layout = L
+        else:
+            L.close()
+            del L
+        del ou, ov
+    del g_host
+    # the four learners' dense sum of each step, in learner order
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    for t in range(wl.steps):
+        say(f"flat1b {selector} step {t}: decode")
+        want = np.zeros(wl.n, np.float32)
+        for ostreams in orc_st[t]:
+            for c, (o_r, o_v) in enumerate(ostreams):
+                assert oracle.decode_accumulate(o_r, o_v, want[off[c]:off[c + 1]]) == 0
         dense = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
-        dgc.decode_accumulate(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                              dense)
+        dgc.decode_accumulate(layout, gpu_st[t], dense)
         torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        for c in SAMPLED:
-            want = np.zeros(C, np.float32)
-            for w in range(len(learners)):
-                r, v_ = o_streams[w][c]
-                assert oracle.decode_accumulate(r, v_, want) == 0
-            got = dense[c * C:(c + 1) * C].cpu().numpy()
-            assert np.array_equal(f32_bits(got), f32_bits(want)), (t, c)
-        ref = torch.zeros_like(dense)
-        for L in learners:
-            gi = L.idx.long().view(T, k[0]) + torch.arange(T, device="cuda").view(T, 1) * C
-            gi = gi.flatten()
-            ref[gi] = ref[gi] + L.val
-        assert torch.equal(ref, dense)
-
+        assert layout.status() == dgc.DGC_OK
+        got = _host(dense)
+        assert np.array_equal(f32_bits(got), f32_bits(want)), (t, first_diff(
+            f32_bits(got), f32_bits(want)))
+        del got
         # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
-        fresh = torch.full_like(dense, float("nan"))
-        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
+        dense.fill_(float("nan"))
+        dgc.decode_sum(layout, gpu_st[t], dense)
         torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
-        del fresh
-        del dense, ref
+        assert layout.status() == dgc.DGC_OK
+        got = _host(dense)
+        assert np.array_equal(f32_bits(got), f32_bits(want)), (t, "fresh")
+        del got, dense, want
+    layout.close()
 
 
 @pytest.mark.timeout(1200)
-def test_flat1b_binlocal_full_sampled():
-    """The bin-local selector (AdaComp page) at full size in the benchmark's
-    configuration: bins of 512, at most n_t/8 entries per chunk, 4 learners
-    x 3 steps.  The oracle recomputes four sampled chunks per learner-step;
-    on every chunk: delivered = min(salient, cap), the delivered set is the
-    salient set (none truncated here) found independently with torch, sent +
-    residual == accumulated v bitwise, u = +0 exactly where sent."""
-    import torch
-    wl = W.get("flat1b")
-    C = wl.sizes[0]
-    T = len(wl.sizes)
-    Lb = 512
-    cap = [C // 8] * T
-    m = np.float32(wl.momentum)
-    learners = [dgc.Learner(list(wl.sizes), cap, wl.momentum) for _ in range(wl.learners)]
-    ou = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
-    ov = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
-    g_host = np.empty(wl.n, np.float32)
-    coff = np.arange(T + 1) * cap[0]
-    for t in range(wl.steps):
-        o_streams = []
-        for w, L in enumerate(learners):
-            say(f"flat1b binlocal step {t} learner {w}: generate")
-            W.gradient(wl, w, t, out=g_host)
-            g = torch.from_numpy(g_host).cuda()
-            u_prev = L.u.clone()
-            v_prev = L.v.clone()
-            say(f"flat1b binlocal step {t} learner {w}: compress")
-            idx, val, count, total = L.compress_binlocal(g, [Lb] * T, cap, wl.clip)
-            L.encode_counts(cap)
-            torch.cuda.synchronize()
-            assert L.status() == dgc.DGC_OK
-            cnt = count.cpu().numpy()
-            tot = total.cpu().numpy()
-            assert np.array_equal(cnt, np.minimum(tot, cap[0])) and (tot <= cap[0]).all()
-            s = np.float32(L.scale.cpu()[0])
-            o_norm, o_s = oracle.clip_scale(g_host, wl.clip)
-            assert s == o_s
-            gi = idx.cpu().numpy().view(np.uint32)
-            gvv = val.cpu().numpy()
-            scap = L.cap
-            runs = L.runs.cpu().numpy().view(np.uint16)
-            svals = L.vals.cpu().numpy()
-            ent = L.entries.cpu().numpy()
-            o_streams.append({})
-            for c in SAMPLED:
-                sl = slice(c * C, (c + 1) * C)
-                oracle.momentum(g_host[sl], o_s, m, ou[w][c], ov[w][c])
-                o_idx, o_val, o_tot = oracle.binlocal_select_mask(ou[w][c], ov[w][c], Lb,
-                                                                  cap[c])
-                a = coff[c]
-                assert tot[c] == o_tot and cnt[c] == o_idx.size, (t, w, c)
-                assert np.array_equal(gi[a:a + cnt[c]], o_idx), (t, w, c)
-                assert np.array_equal(f32_bits(gvv[a:a + cnt[c]]), f32_bits(o_val)), (t, w, c)
-                assert np.array_equal(f32_bits(L.u[sl].cpu().numpy()), f32_bits(ou[w][c]))
-                assert np.array_equal(f32_bits(L.v[sl].cpu().numpy()), f32_bits(ov[w][c]))
-                o_r, o_v = oracle.encode(o_idx, o_val, cap=int(scap[c + 1] - scap[c]))
-                assert ent[c] == o_r.size
-                assert np.array_equal(runs[scap[c]:scap[c] + ent[c]], o_r)
-                assert np.array_equal(f32_bits(svals[scap[c]:scap[c] + ent[c]]), f32_bits(o_v))
-                o_streams[-1][c] = (o_r, o_v)
-            # ---- properties on every chunk (torch, separate ops: no contraction)
-            sd = torch.tensor(float(s), dtype=torch.float32, device="cuda")
-            md = torch.tensor(float(m), dtype=torch.float32, device="cuda")
-            u_new = torch.add(torch.mul(md, u_prev), torch.mul(g, sd))
-            v_pre = torch.add(v_prev, u_new)
-            del u_prev, v_prev, g
-            key = (v_pre.view(torch.int32) & 0x7FFFFFFF).view(-1, Lb)
-            ahead = (torch.add(v_pre, u_new).view(torch.int32) & 0x7FFFFFFF).view(-1, Lb)
-            theta = key.max(dim=1, keepdim=True).values
-            salient = ((key != 0) & (ahead >= theta)).flatten()
-            del key, ahead, theta
-            assert int(salient.sum()) == int(tot.sum())
-            sel = torch.cat([idx[coff[c]:coff[c] + cnt[c]].long() + c * C for c in range(T)])
-            vsel = torch.cat([val[coff[c]:coff[c] + cnt[c]] for c in range(T)])
-            mask = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
-            mask[sel] = True
-            assert torch.equal(mask, salient)
-            sent = torch.zeros_like(v_pre)
-            sent[sel] = vsel
-            assert torch.equal((sent + L.v[: wl.n]).view(torch.int32),
-                               (v_pre + 0.0).view(torch.int32))
-            assert bool((L.u[: wl.n][mask].view(torch.int32) == 0).all())
-            assert torch.equal(L.u[: wl.n][~mask].view(torch.int32),
-                               u_new[~mask].view(torch.int32))
-            del sent, mask, salient, sel, vsel, v_pre, u_new
-        say(f"flat1b binlocal step {t}: decode")
-        dense = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
-        dgc.decode_accumulate(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                              dense)
-        torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        for c in SAMPLED:
-            want = np.zeros(C, np.float32)
-            for w in range(len(learners)):
-                r, v_ = o_streams[w][c]
-                assert oracle.decode_accumulate(r, v_, want) == 0
-            got = dense[c * C:(c + 1) * C].cpu().numpy()
-            assert np.array_equal(f32_bits(got), f32_bits(want)), (t, c)
-
-        # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
-        fresh = torch.full_like(dense, float("nan"))
-        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
-        torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
-        del fresh
-        del dense
+def test_flat1b_full():
+    """Exact top-k at k = ceil(2^24 / 1000) = 16778 per chunk."""
+    _flat1b_full("topk")
 
 
 @pytest.mark.timeout(1200)
-def test_flat1b_sampled_full_sampled():
-    """The sampled-threshold selector (DGC review, RQ4) at full size in the
-    benchmark's configuration: k = 16778 per chunk, at most 4 k delivered,
-    4 learners x 3 steps.  The oracle recomputes four sampled chunks per
-    learner-step (threshold, sent set, state, stream); on every chunk the
-    sent set is {key >= theta, key != 0} found with torch, the residual and
-    masking hold bitwise, and the count stays within 0.5 k .. 1.5 k."""
-    import torch
-    wl = W.get("flat1b")
-    C = wl.sizes[0]
-    T = len(wl.sizes)
-    k = [dgc.k_for_density(C, wl.densities[0])] * T
-    cap = [4 * k[0]] * T
-    m = np.float32(wl.momentum)
-    learners = [dgc.Learner(list(wl.sizes), cap, wl.momentum) for _ in range(wl.learners)]
-    ou = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
-    ov = [{c: np.zeros(C, np.float32) for c in SAMPLED} for _ in learners]
-    g_host = np.empty(wl.n, np.float32)
-    coff = np.arange(T + 1) * cap[0]
-    for t in range(wl.steps):
-        o_streams = []
-        for w, L in enumerate(learners):
-            say(f"flat1b sampled step {t} learner {w}: generate")
-            W.gradient(wl, w, t, out=g_host)
-            g = torch.from_numpy(g_host).cuda()
-            u_prev = L.u.clone()
-            v_prev = L.v.clone()
-            say(f"flat1b sampled step {t} learner {w}: compress")
-            idx, val, count, total = L.compress_sampled(g, k, cap, wl.clip)
-            L.encode_counts(cap)
-            torch.cuda.synchronize()
-            assert L.status() == dgc.DGC_OK
-            info = L.select_info()
-            assert (info[:, 0] == 3).all()
-            theta = info[:, 4]
-            cnt = count.cpu().numpy()
-            tot = total.cpu().numpy()
-            assert np.array_equal(cnt, np.minimum(tot, cap[0]))
-            assert (tot > k[0] // 2).all() and (tot < 3 * k[0] // 2).all(), (tot.min(), tot.max())
-            s = np.float32(L.scale.cpu()[0])
-            _, o_s = oracle.clip_scale(g_host, wl.clip)
-            assert s == o_s
-            gi = idx.cpu().numpy().view(np.uint32)
-            gvv = val.cpu().numpy()
-            scap = L.cap
-            runs = L.runs.cpu().numpy().view(np.uint16)
-            svals = L.vals.cpu().numpy()
-            ent = L.entries.cpu().numpy()
-            o_streams.append({})
-            for c in SAMPLED:
-                sl = slice(c * C, (c + 1) * C)
-                oracle.momentum(g_host[sl], o_s, m, ou[w][c], ov[w][c])
-                o_idx, o_val, o_tot, o_th = oracle.sampled_select_mask(ou[w][c], ov[w][c],
-                                                                       k[c], c, cap[c])
-                a = coff[c]
-                assert theta[c] == o_th and tot[c] == o_tot, (t, w, c)
-                assert np.array_equal(gi[a:a + cnt[c]], o_idx), (t, w, c)
-                assert np.array_equal(f32_bits(gvv[a:a + cnt[c]]), f32_bits(o_val)), (t, w, c)
-                assert np.array_equal(f32_bits(L.u[sl].cpu().numpy()), f32_bits(ou[w][c]))
-                assert np.array_equal(f32_bits(L.v[sl].cpu().numpy()), f32_bits(ov[w][c]))
-                o_r, o_v = oracle.encode(o_idx, o_val, cap=int(scap[c + 1] - scap[c]))
-                assert ent[c] == o_r.size
-                assert np.array_equal(runs[scap[c]:scap[c] + ent[c]], o_r)
-                assert np.array_equal(f32_bits(svals[scap[c]:scap[c] + ent[c]]), f32_bits(o_v))
-                o_streams[-1][c] = (o_r, o_v)
-            sd = torch.tensor(float(s), dtype=torch.float32, device="cuda")
-            md = torch.tensor(float(m), dtype=torch.float32, device="cuda")
-            u_new = torch.add(torch.mul(md, u_prev), torch.mul(g, sd))
-            v_pre = torch.add(v_prev, u_new)
-            del u_prev, v_prev, g
-            key = (v_pre.view(torch.int32) & 0x7FFFFFFF).view(T, C)
-            th = torch.from_numpy(theta.astype(np.int64)).cuda().view(T, 1)
-            want = ((key != 0) & (key.long() >= th)).flatten()
-            del key
-            sel = torch.cat([idx[coff[c]:coff[c] + cnt[c]].long() + c * C for c in range(T)])
-            vsel = torch.cat([val[coff[c]:coff[c] + cnt[c]] for c in range(T)])
-            mask = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
-            mask[sel] = True
-            assert torch.equal(mask, want)
-            sent = torch.zeros_like(v_pre)
-            sent[sel] = vsel
-            assert torch.equal((sent + L.v[: wl.n]).view(torch.int32),
-                               (v_pre + 0.0).view(torch.int32))
-            assert bool((L.u[: wl.n][mask].view(torch.int32) == 0).all())
-            assert torch.equal(L.u[: wl.n][~mask].view(torch.int32),
-                               u_new[~mask].view(torch.int32))
-            del sent, mask, want, sel, vsel, v_pre, u_new
-        say(f"flat1b sampled step {t}: decode")
-        dense = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
-        dgc.decode_accumulate(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                              dense)
-        torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        for c in SAMPLED:
-            want_d = np.zeros(C, np.float32)
-            for w in range(len(learners)):
-                r, v_ = o_streams[w][c]
-                assert oracle.decode_accumulate(r, v_, want_d) == 0
-            got = dense[c * C:(c + 1) * C].cpu().numpy()
-            assert np.array_equal(f32_bits(got), f32_bits(want_d)), (t, c)
+def test_flat1b_binlocal_full():
+    """The bin-local selector (AdaComp page) in the benchmark's
+    configuration: bins of 512, at most n_t / 8 entries per chunk."""
+    _flat1b_full("binlocal")
 
-        # the fresh sum the benchmark times: dgc_decode_sum into a buffer of NaNs
-        fresh = torch.full_like(dense, float("nan"))
-        dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners], fresh)
-        torch.cuda.synchronize()
-        assert learners[0].status() == dgc.DGC_OK
-        assert torch.equal(fresh.view(torch.int32), dense.view(torch.int32)), t
-        del fresh
-        del dense
+
+@pytest.mark.timeout(1200)
+def test_flat1b_sampled_full():
+    """The sampled-threshold selector (DGC review, RQ4) in the benchmark's
+    configuration: target k = 16778 per chunk, at most 4 k delivered."""
+    _flat1b_full("sampled")

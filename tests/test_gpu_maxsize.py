@@ -15,7 +15,7 @@ chunks), with exact ties and zeros planted.
 import numpy as np
 import pytest
 
-from gpu_harness import say
+from gpu_harness import oracle_k, say
 from sparsified_gradient_compression_amd import dgc
 
 pytestmark = pytest.mark.gpu
@@ -127,7 +127,7 @@ def check_roundtrip(L, sel, vals, encode):
 @pytest.mark.timeout(900)
 def test_max_tensor_exact_topk():
     import torch
-    k = dgc.k_for_density(N, __import__("fractions").Fraction(1, 1000))
+    k = oracle_k(N, __import__("fractions").Fraction(1, 1000))
     L = dgc.Learner([N], [k])
     for step in range(2):
         say(f"max size top-k step {step}: generate")

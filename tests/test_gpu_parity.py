@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from gpu_harness import (Pair, compare_streams, f32_bits, first_diff,
-                         gpu_streams, oracle_streams, say)
+                         gpu_streams, oracle_k, oracle_streams, say)
 from sparsified_gradient_compression_amd import dgc
 from sparsified_gradient_compression_amd import workloads as W
 
@@ -30,13 +30,13 @@ def gpu():
 
 
 def ks_for(wl, step):
-    return [dgc.k_for_density(s, wl.densities[step]) for s in wl.sizes]
+    return [oracle_k(s, wl.densities[step]) for s in wl.sizes]
 
 
 def run_workload(wl, steps=None, learners=None, path=0, grid=0, encode=True, tag=""):
     steps = wl.steps if steps is None else steps
     learners = wl.learners if learners is None else learners
-    kmax = [max(dgc.k_for_density(s, d) for d in wl.densities) for s in wl.sizes]
+    kmax = [max(oracle_k(s, d) for d in wl.densities) for s in wl.sizes]
     pairs = [Pair(list(wl.sizes), kmax, wl.momentum) for _ in range(learners)]
     for p in pairs:
         p.learner.set_option(dgc.DGC_OPT_SELECT_PATH, path)

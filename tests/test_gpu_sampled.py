@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import f32_bits, first_diff, say
+from gpu_harness import f32_bits, first_diff, oracle_k, say
 from sparsified_gradient_compression_amd import dgc
 from sparsified_gradient_compression_amd import workloads as W
 from test_gpu_binlocal import check_decode
@@ -118,7 +118,7 @@ def run(sizes, ks, caps, grads, clip, learners=1, path=0, k_max=None, tag=""):
 def test_flat1m(path):
     wl = W.get("flat1m")
     n = wl.n
-    k = [dgc.k_for_density(n, wl.densities[0])]
+    k = [oracle_k(n, wl.densities[0])]
     run([n], [k, k], [[n], [n]], lambda w, s: W.gradient(wl, w, s), 0.0, path=path,
         tag=f"flat1m p{path}")
 
@@ -129,7 +129,7 @@ def test_resnet50_layout_scaled(path):
     are line samples; k = ceil(n/1000), clipping on, three steps."""
     wl = W.scaled(W.get("resnet50"), 8)
     sizes = list(wl.sizes)
-    k = [dgc.k_for_density(s, wl.densities[0]) for s in sizes]
+    k = [oracle_k(s, wl.densities[0]) for s in sizes]
     cap = [min(s, 4 * kk + 64) for s, kk in zip(sizes, k)]
     run(sizes, [k] * 3, [cap] * 3, lambda w, s: W.gradient(wl, w, s), wl.clip,
         k_max=cap, path=path, tag=f"rn50/8 p{path}")
@@ -139,14 +139,14 @@ def test_warmup_schedule_scaled():
     """One 3.5M tensor through the warm-up densities 1/4 ... 1/1000."""
     wl = W.scaled(W.get("warmup350m"), 100)
     n = wl.n
-    ks = [[dgc.k_for_density(n, d)] for d in wl.densities]
+    ks = [[oracle_k(n, d)] for d in wl.densities]
     run([n], ks, [[n]] * len(ks), lambda w, s: W.gradient(wl, w, s), wl.clip, tag="warm/100")
 
 
 def test_flat1b_shape_scaled_four_learners():
     wl = W.scaled(W.get("flat1b"), 256)
     sizes = list(wl.sizes)
-    k = [dgc.k_for_density(s, wl.densities[0]) for s in sizes]
+    k = [oracle_k(s, wl.densities[0]) for s in sizes]
     cap = [4 * kk for kk in k]
     run(sizes, [k] * 2, [cap] * 2, lambda w, s: W.gradient(wl, w, s), wl.clip, learners=4,
         k_max=cap, tag="1b/256")
