@@ -4,14 +4,21 @@ One step = the whole hot path over one batch of synthetic gradients: for each
 of the W learners, dgc_compress (clip, momentum correction, exact top-k,
 compaction, masking) and dgc_encode; then all W streams are decoded into a
 fresh dense sum (dgc_decode_sum: every element written, none read, the same
-bits as zeroing and dgc_decode_accumulate).  Inputs are resident in
-HBM before the timed region; each step uses the next of the workload's
-gradient steps, cycling.
+bits as zeroing and dgc_decode_accumulate).  Inputs are resident in HBM
+before the timed region; each step uses the next of the workload's gradient
+steps, cycling.
 
-Prints one JSON line: value = gradient elements compressed per second
-(all learners) in G elem/s; roofline = the element-wise pass (the dominant
-kernel) timed with HIP events on its stream; cpu_baseline = the CPU oracle
-timed on a bounded sample of the same workload.
+Prints one JSON line.  value = gradient elements compressed per second (all
+learners) over the K timed steps, wall clock; the timed region carries only
+two HIP events per learner-step, around the element-wise pass (the dominant
+kernel), whose average duration gives roofline.achieved, plus one event per
+step boundary for the per-step median.  A separate, untimed measurement pass
+with every library timer on gives the medians over steps x learners of the
+compress, encode and decode times.  With the default workload (flat1b) and
+selector, detail.workloads repeats the same measurement, bounded, on the
+other four workloads (flat1m, resnet50, deepspeech, warmup350m).
+cpu_baseline = the CPU oracle timed on a bounded sample of the headline
+workload.
 
 With --selector binlocal the step uses AdaComp's bin-local selector instead
 of exact top-k (dgc_compress_binlocal + dgc_encode_counts, bins of
@@ -28,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -47,10 +55,20 @@ TRAFFIC = {
     "sampled": (os.path.join(ROOT, "profiles", "sm_fused_flat1b_traffic.json"),
                 ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
 }
+# the other workloads measured after the headline: (name, timed steps)
+OTHER_WORKLOADS = (("flat1m", 200), ("resnet50", 50), ("deepspeech", 20),
+                   ("warmup350m", 10))
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def file_sha16(path):
+    h = hashlib.sha256()
+    with open(path, "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_source_sha(selector="topk"):
@@ -83,6 +101,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flat1b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip detail.workloads (the other four workloads)")
+    ap.add_argument("--measure-steps", type=int, default=10,
+                    help="steps of the untimed pass with every library timer on")
     ap.add_argument("--cpu-sample-chunks", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="cycle the oracle over the sample until this long")
@@ -97,6 +119,9 @@ def parse():
                          "previous learner's element-wise pass is done")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
+    ap.add_argument("--timers", choices=("fused", "off"), default="fused",
+                    help="library timers in the timed region: the element-wise "
+                         "pass only (default), or none (then roofline is null)")
     ap.add_argument("--selector", choices=("topk", "binlocal", "sampled"), default="topk",
                     help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, or "
                          "the sampled threshold")
@@ -250,6 +275,254 @@ def single_thread(wl, g, k):
             "sample": f"one step of the first tensor ({n} elements), {dt:.2f} s"}
 
 
+def med(xs):
+    return round(float(statistics.median(xs)), 4) if xs else None
+
+
+class Run:
+    """One workload and selector on the GPU: every (learner, step) gradient
+    resident in HBM, one Learner per simulated learner, and the dense sum."""
+
+    def __init__(self, wl, selector, args, gsteps, host_sample_chunks=0):
+        import torch
+        from sparsified_gradient_compression_amd import dgc
+        from sparsified_gradient_compression_amd import workloads as W
+        self.dgc = dgc
+        self.wl = wl
+        self.selector = selector
+        self.args = args
+        T = len(wl.sizes)
+        self.T = T
+        self.binlocal = selector == "binlocal"
+        self.sampled = selector == "sampled"
+        if self.binlocal:
+            self.bins = [args.bin_len] * T
+            self.caps = [s // args.cap_den for s in wl.sizes]
+            self.ks = [self.caps]  # the delivery capacity takes k's place
+            kmax = self.caps
+        else:
+            self.ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
+            kmax = [max(k[t] for k in self.ks) for t in range(T)]
+            if self.sampled:
+                # deliver at most 4 k per tensor, following each step's k
+                self.caps_by_step = [[min(s, 4 * kk) for s, kk in zip(wl.sizes, k)]
+                                     for k in self.ks]
+                kmax = [max(c[t] for c in self.caps_by_step) for t in range(T)]
+        self.gsteps = gsteps
+        n = wl.n
+        self.grads = {}
+        self.host_samples = []
+        g_host = np.empty(n, np.float32)
+        n_sample = sum(wl.sizes[:host_sample_chunks])
+        for t in range(gsteps):
+            for w in range(wl.learners):
+                t0 = time.perf_counter()
+                W.gradient(wl, w, t, out=g_host)
+                self.grads[(w, t)] = torch.from_numpy(g_host).cuda()
+                if w == 0 and n_sample:
+                    self.host_samples.append(g_host[:n_sample].copy())
+                if n >= (1 << 26):
+                    log(f"{wl.name}: gradient learner {w} step {t}: "
+                        f"{time.perf_counter() - t0:.1f} s")
+        del g_host
+        torch.cuda.synchronize()
+        self.learners = [dgc.Learner(list(wl.sizes), kmax, wl.momentum)
+                         for _ in range(wl.learners)]
+        self.dense = torch.zeros(n, dtype=torch.float32, device="cuda")
+        self.main = torch.cuda.current_stream()
+        self.pipeline = args.pipeline and selector == "topk"
+        if self.pipeline:
+            # One stream per learner.  Learner w+1 starts once learner w's
+            # element-wise pass is done (event recorded by the library), so
+            # its clip norm and element-wise pass overlap learner w's short
+            # selection and encode kernels, and no two element-wise passes
+            # overlap.
+            self.streams = [torch.cuda.Stream() for _ in self.learners]
+            self.fused_ev = [torch.cuda.Event() for _ in self.learners]
+            for L, ev in zip(self.learners, self.fused_ev):
+                L.set_fused_event(ev)
+
+    def k_of_step(self, s):
+        return self.ks[(s % self.gsteps) % len(self.ks)]
+
+    def step(self, s):
+        """Enqueue step s: every learner's compress + encode, then the
+        learners' fresh dense sum."""
+        dgc, args, learners = self.dgc, self.args, self.learners
+        t = s % self.gsteps
+        k = self.ks[t % len(self.ks)]
+        streams_of = lambda: [(L.runs, L.vals, L.entries) for L in learners]  # noqa: E731
+        if self.binlocal or self.sampled:
+            step_caps = self.caps if self.binlocal else self.caps_by_step[t % len(self.ks)]
+            for w, L in enumerate(learners):
+                if self.binlocal:
+                    L.compress_binlocal(self.grads[(w, t)], self.bins, step_caps,
+                                        self.wl.clip)
+                else:
+                    L.compress_sampled(self.grads[(w, t)], k, step_caps, self.wl.clip)
+                if not args.fused_only:
+                    L.encode_counts(step_caps)
+            if not args.fused_only:
+                dgc.decode_sum(learners[0], streams_of(), self.dense)
+            return
+        if not self.pipeline:
+            for w, L in enumerate(learners):
+                L.compress(self.grads[(w, t)], k, self.wl.clip)
+                if not args.fused_only:
+                    L.encode(k)
+            if not args.fused_only:
+                dgc.decode_sum(learners[0], streams_of(), self.dense)
+            return
+        import torch
+        for w, L in enumerate(learners):
+            st = self.streams[w]
+            if w == 0:
+                st.wait_stream(self.main)  # the previous step's decode is done
+            else:
+                st.wait_event(self.fused_ev[w - 1])
+            with torch.cuda.stream(st):
+                L.compress(self.grads[(w, t)], k, self.wl.clip, stream=st)
+                if not args.fused_only:
+                    L.encode(k, stream=st)
+        for st in self.streams:
+            self.main.wait_stream(st)
+        if not args.fused_only:
+            dgc.decode_sum(learners[0], streams_of(), self.dense, stream=self.main)
+
+    def set_timing(self, mode):
+        for L in self.learners:
+            L.set_option(self.dgc.DGC_OPT_KERNEL_TIMING, mode)
+
+    def drain_timers(self):
+        for L in self.learners:
+            for tm in range(4):
+                L.kernel_time(tm)
+
+    def check(self):
+        for L in self.learners:
+            assert L.status() == self.dgc.DGC_OK
+
+    def timed(self, first, steps, timers):
+        """Steps [first, first + steps) bracketed by synchronisations; returns
+        (wall seconds, per-step ms from events on the main stream, average
+        element-wise pass ms or None)."""
+        import torch
+        self.drain_timers()
+        self.set_timing(2 if timers == "fused" else 0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(steps):
+            self.step(first + i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        fused = None
+        if timers == "fused":
+            tot, cnt = 0.0, 0
+            for L in self.learners:
+                a, b = L.kernel_time(self.dgc.DGC_TIMER_FUSED)
+                tot, cnt = tot + a, cnt + b
+            fused = tot / max(cnt, 1)
+        self.set_timing(0)
+        self.check()
+        return elapsed, step_ms, fused
+
+    def measure(self, first, steps):
+        """Untimed pass with every library timer on, read after each step:
+        per (step, learner) compress and element-wise ms, per step encode
+        (mean over learners) and decode ms.  Returns lists and the k of each
+        measured step."""
+        dgc = self.dgc
+        self.drain_timers()
+        self.set_timing(1)
+        rec = {"compress": [], "fused": [], "encode": [], "decode": [], "k": []}
+        for i in range(steps):
+            self.step(first + i)
+            rec["k"].append(self.k_of_step(first + i))
+            enc = []
+            for w, L in enumerate(self.learners):
+                c, nc = L.kernel_time(dgc.DGC_TIMER_COMPRESS)
+                f, nf = L.kernel_time(dgc.DGC_TIMER_FUSED)
+                e, ne = L.kernel_time(dgc.DGC_TIMER_ENCODE)
+                d, nd = L.kernel_time(dgc.DGC_TIMER_DECODE)
+                rec["compress"].append((i, c / max(nc, 1)))
+                if nf:
+                    rec["fused"].append((i, f / nf))
+                if ne:
+                    enc.append(e / ne)
+                if nd:
+                    rec["decode"].append(d / nd)
+            if enc:
+                rec["encode"].append(sum(enc) / len(enc))
+        self.set_timing(0)
+        self.check()
+        return rec
+
+    def close(self):
+        import torch
+        for L in self.learners:
+            L.close()
+        self.learners = []
+        self.grads = {}
+        self.dense = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def compress_alg_bytes(wl, k):
+    """Algorithmic bytes of one learner's compress at per-tensor k: read g,
+    u, v and write u, v (20 B/elem), the norm's re-read of g (4 B/elem with
+    clipping), the selected (index, value) written and u, v zeroed there
+    (16 B per entry)."""
+    clip = 1 if wl.clip > 0 else 0
+    return wl.n * (20 + 4 * clip) + 16 * int(sum(k))
+
+
+def workload_record(run, steps, warmup, measure_steps, timers):
+    """Whole-step throughput over `steps` timed steps, then the measurement
+    pass; the per-density compress figures when k changes per step."""
+    wl = run.wl
+    for s in range(warmup):
+        run.step(s)
+    elapsed, step_ms, fused = run.timed(warmup, steps, timers)
+    rec = run.measure(warmup + steps, measure_steps)
+    comp = [c for _, c in rec["compress"]]
+    by_step = {}
+    for (i, c) in rec["compress"]:
+        by_step.setdefault(i, []).append(c)
+    alg = [compress_alg_bytes(wl, rec["k"][i]) for i in sorted(by_step)]
+    step_c = [statistics.mean(by_step[i]) for i in sorted(by_step)]
+    frac = sum(alg) / (sum(step_c) * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    out = {
+        "workload": wl.name,
+        "elements_per_learner": wl.n,
+        "tensors": len(wl.sizes),
+        "learners": wl.learners,
+        "steps_timed": steps,
+        "whole_step_G_elem_per_s": round(wl.n * wl.learners * steps / elapsed / 1e9, 3),
+        "step_ms_median": med(step_ms),
+        "compress_ms_median": med(comp),
+        "k_fused_ms_median": med([f for _, f in rec["fused"]]),
+        "encode_ms_median": med(rec["encode"]),
+        "decode_ms_median": med(rec["decode"]),
+        "compress_alg_frac_of_peak": round(frac, 4),
+    }
+    if len(set(wl.densities)) > 1:
+        per = {}
+        for i, c in zip(sorted(by_step), step_c):
+            d = str(wl.densities[(warmup + steps + i) % run.gsteps % len(run.ks)])
+            per.setdefault(d, []).append((c, compress_alg_bytes(wl, rec["k"][i])))
+        out["per_density"] = [
+            {"density": d, "compress_ms": round(statistics.median(c for c, _ in v), 4),
+             "frac_of_peak": round(v[0][1] / (statistics.median(c for c, _ in v) * 1e-3)
+                                   / 1e9 / HBM_PEAK_GBPS, 4)}
+            for d, v in per.items()]
+    return out, elapsed, step_ms, fused, rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -265,114 +538,16 @@ def main():
     torch.cuda.set_device(0)
     wl = W.get(args.workload)
     T = len(wl.sizes)
-    binlocal = args.selector == "binlocal"
-    sampled = args.selector == "sampled"
-    if binlocal:
-        bins = [args.bin_len] * T
-        caps = [s // args.cap_den for s in wl.sizes]
-        ks = [caps]  # the delivery capacity takes k's place in the layout
-        kmax = caps
-    else:
-        ks = [[dgc.k_for_density(s, d) for s in wl.sizes] for d in wl.densities]
-        kmax = [max(k[t] for k in ks) for t in range(T)]
-        if sampled:
-            # deliver at most 4 k per tensor, following each step's k
-            caps_by_step = [[min(s, 4 * kk) for s, kk in zip(wl.sizes, k)] for k in ks]
-            kmax = [max(c[t] for c in caps_by_step) for t in range(T)]
     n = wl.n
-
-    # ---- inputs: every (learner, step) gradient resident in HBM
-    grads = {}
-    host_samples = []
-    g_host = np.empty(n, np.float32)
-    n_sample = sum(wl.sizes[:args.cpu_sample_chunks])
     gsteps = args.grad_steps if args.grad_steps > 0 else wl.steps
-    for t in range(gsteps):
-        for w in range(wl.learners):
-            t0 = time.perf_counter()
-            W.gradient(wl, w, t, out=g_host)
-            grads[(w, t)] = torch.from_numpy(g_host).cuda()
-            if w == 0 and not args.no_cpu_baseline:
-                host_samples.append(g_host[:n_sample].copy())
-            log(f"gradient learner {w} step {t}: {time.perf_counter() - t0:.1f} s")
-    torch.cuda.synchronize()
-
-    learners = [dgc.Learner(list(wl.sizes), kmax, wl.momentum) for _ in range(wl.learners)]
-    for L in learners:
-        L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 1)
-    dense = torch.zeros(n, dtype=torch.float32, device="cuda")
-    main = torch.cuda.current_stream()
-    pipeline = args.pipeline and not (binlocal or sampled)
-    if pipeline:
-        # One stream per learner.  Learner w+1 starts once learner w's
-        # element-wise pass is done (event recorded by the library), so its
-        # clip norm and element-wise pass overlap learner w's short selection
-        # and encode kernels, and no two element-wise passes overlap.
-        streams = [torch.cuda.Stream() for _ in learners]
-        fused_ev = [torch.cuda.Event() for _ in learners]
-        for L, ev in zip(learners, fused_ev):
-            L.set_fused_event(ev)
-
-    def one_step(s):
-        t = s % gsteps
-        k = ks[t % len(ks)]
-        if binlocal or sampled:
-            step_caps = caps if binlocal else caps_by_step[t % len(ks)]
-            for w, L in enumerate(learners):
-                if binlocal:
-                    L.compress_binlocal(grads[(w, t)], bins, step_caps, wl.clip)
-                else:
-                    L.compress_sampled(grads[(w, t)], k, step_caps, wl.clip)
-                if not args.fused_only:
-                    L.encode_counts(step_caps)
-            if not args.fused_only:
-                dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                               dense)
-            return
-        if not pipeline:
-            for w, L in enumerate(learners):
-                L.compress(grads[(w, t)], k, wl.clip)
-                if not args.fused_only:
-                    L.encode(k)
-            if not args.fused_only:
-                dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                               dense)
-            return
-        for w, L in enumerate(learners):
-            st = streams[w]
-            if w == 0:
-                st.wait_stream(main)  # the previous step's decode is done
-            else:
-                st.wait_event(fused_ev[w - 1])
-            with torch.cuda.stream(st):
-                L.compress(grads[(w, t)], k, wl.clip, stream=st)
-                if not args.fused_only:
-                    L.encode(k, stream=st)
-        if not args.fused_only:
-            for st in streams:
-                main.wait_stream(st)
-            dgc.decode_sum(learners[0], [(L.runs, L.vals, L.entries) for L in learners],
-                           dense, stream=main)
-        else:
-            for st in streams:
-                main.wait_stream(st)
-
+    run = Run(wl, args.selector, args, gsteps,
+              0 if args.no_cpu_baseline else args.cpu_sample_chunks)
     for s in range(args.warmup):
-        one_step(s)
+        run.step(s)
     torch.cuda.synchronize()
-    for L in learners:
-        for tm in range(4):
-            L.kernel_time(tm)
-        assert L.status() == dgc.DGC_OK
+    run.check()
     log("timed region")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        one_step(s)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    for L in learners:
-        assert L.status() == dgc.DGC_OK
+    elapsed, step_ms, fused_ms = run.timed(args.warmup, args.steps, args.timers)
     if args.calibrate_copy:
         # a plain copy of known size: reads 1 GiB, writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -381,21 +556,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    times = {}
-    for name, tm in (("fused", dgc.DGC_TIMER_FUSED), ("compress", dgc.DGC_TIMER_COMPRESS),
-                     ("encode", dgc.DGC_TIMER_ENCODE), ("decode", dgc.DGC_TIMER_DECODE)):
-        tot, cnt = 0.0, 0
-        for L in learners:
-            a, b = L.kernel_time(tm)
-            tot += a
-            cnt += b
-        times[name] = (tot, cnt)
+    log("measurement pass")
+    first = args.warmup + args.steps
+    rec = run.measure(first, args.measure_steps) if args.measure_steps > 0 else None
+    learners = run.learners
+    ks = run.ks
     elems = n * wl.learners * args.steps
     value = elems / elapsed / 1e9
-    fused_ms = times["fused"][0] / max(times["fused"][1], 1)
-    compress_ms = times["compress"][0] / max(times["compress"][1], 1)
     clip = 1 if wl.clip > 0 else 0
-    if binlocal or sampled:
+    last = first + max(args.measure_steps, 1) - 1
+    if run.binlocal or run.sampled:
         # the last step's salient and delivered counts, all learners
         salient = int(sum(int(L.total.sum()) for L in learners)) // len(learners)
         delivered = int(sum(int(L.count.sum()) for L in learners)) // len(learners)
@@ -405,17 +575,32 @@ def main():
         # + norm re-read; + slot read, output write and u/v masking per entry
         pipeline_bytes = n * (20 + 4 * clip) + 8 * salient + 16 * delivered
         kernel_name = ("k_bl_fused (clip-scale + momentum correction + accumulation + "
-                       + ("per-bin maxima + salient entries to slots)" if binlocal else
+                       + ("per-bin maxima + salient entries to slots)" if run.binlocal else
                           "entries at or above the sampled threshold to slots)"))
     else:
         fused_bytes = 20 * n  # read g, u, v; write u, v
-        k_total = sum(ks[0])
-        pipeline_bytes = n * (20 + 4 * clip) + 16 * k_total
+        pipeline_bytes = compress_alg_bytes(wl, ks[0])
         kernel_name = ("k_fused (clip-scale + momentum correction + accumulation + "
                        "candidate output)")
-    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
-    traffic = measured_traffic(n, args.selector)
-
+    roofline = None
+    if fused_ms:
+        achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
+        traffic = measured_traffic(n, args.selector)
+        roofline = {
+            "bound": "hbm",
+            "kernel": kernel_name,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": fused_bytes,
+            "avg_launch_ms": round(fused_ms, 4),
+            # HBM bytes the counters saw per launch over this run's launch time
+            "traffic_GBps": (round(traffic / (fused_ms * 1e-3) / 1e9, 1)
+                             if traffic else None),
+        }
+    lib_path = dgc.lib_path()
     out = {
         "metric": "gradient elements compressed/sec (G elem/s) and % of MI355X peak HBM GB/s",
         "value": round(value, 3),
@@ -439,37 +624,38 @@ def main():
             "momentum": wl.momentum,
             "gradient_steps": wl.steps,
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": kernel_name,
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": fused_bytes,
-            "avg_launch_ms": round(fused_ms, 4),
-            # HBM bytes the counters saw per launch over this run's launch time
-            "traffic_GBps": (round(traffic / (fused_ms * 1e-3) / 1e9, 1)
-                             if traffic else None),
-        },
+        "roofline": roofline,
         "detail": {
-            "compress_ms_per_learner_step": round(compress_ms, 4),
-            "encode_ms_per_call": round(times["encode"][0] / max(times["encode"][1], 1), 4),
-            "decode_ms_per_call": round(times["decode"][0] / max(times["decode"][1], 1), 4),
-            "compress_pipeline_alg_GBps": round(pipeline_bytes / (compress_ms * 1e-3) / 1e9, 1),
-            "compress_pipeline_frac_of_peak": round(
-                pipeline_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "compress_G_elem_per_s": round(n / (compress_ms * 1e-3) / 1e9, 2),
+            "library": {"path": os.path.relpath(lib_path, ROOT),
+                        "sha16": file_sha16(lib_path)},
+            "timed_region_timers": ("two HIP events per learner-step around the "
+                                    "element-wise pass" if args.timers == "fused"
+                                    else "none"),
+            "step_ms_median": med(step_ms),
+            "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
         },
     }
     det = out["detail"]
-    if binlocal or sampled:
-        if binlocal:
+    if rec is not None:
+        comp = [c for _, c in rec["compress"]]
+        comp_med = statistics.median(comp)
+        det.update({
+            "measured_steps": args.measure_steps,
+            "compress_ms_median": med(comp),
+            "k_fused_ms_median": med([f for _, f in rec["fused"]]),
+            "encode_ms_median": med(rec["encode"]),
+            "decode_ms_median": med(rec["decode"]),
+            "compress_pipeline_alg_GBps": round(pipeline_bytes / (comp_med * 1e-3) / 1e9, 1),
+            "compress_pipeline_frac_of_peak": round(
+                pipeline_bytes / (comp_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "compress_G_elem_per_s": round(n / (comp_med * 1e-3) / 1e9, 2),
+        })
+    if run.binlocal or run.sampled:
+        if run.binlocal:
             out["config"].update({"bin_len": args.bin_len,
                                   "cap_per_tensor": f"n_t // {args.cap_den}"})
         else:
-            klast = np.array(ks[(args.warmup + args.steps - 1) % gsteps % len(ks)])
+            klast = np.array(run.k_of_step(last))
             ratio = np.concatenate([L.total.cpu().numpy() / np.maximum(klast, 1)
                                     for L in learners])
             out["config"].update({"k_per_tensor": int(klast[0]) if len(set(klast)) == 1
@@ -485,27 +671,41 @@ def main():
     else:
         path = [L.path_counts() for L in learners]
         info = np.concatenate([L.select_info() for L in learners])
-        kk = np.array(ks[(args.warmup + args.steps - 1) % gsteps] * len(learners))
+        kk = np.array(list(run.k_of_step(last)) * len(learners))
         listed = info[:, 0] == 1
         cand_ratio = info[listed, 2] / np.maximum(kk[listed], 1)
         out["config"].update({
             "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
             "density": str(wl.densities[0])})
         det.update({
-            "learner_pipelining": pipeline,
+            "learner_pipelining": run.pipeline,
             "select_path_window_dense": [int(sum(p[0] for p in path)),
                                          int(sum(p[1] for p in path))],
             "overflow_tensors": int(info[:, 3].sum()),
             "window_candidates_over_k": ([round(float(cand_ratio.min()), 3),
                                           round(float(cand_ratio.max()), 3)]
                                          if cand_ratio.size else None)})
+    host_samples = run.host_samples
+    run.close()
+    del run
+    if (not args.no_workloads and args.workload == "flat1b" and args.selector == "topk"
+            and not args.fused_only and not args.pipeline):
+        det["workloads"] = []
+        for name, steps in OTHER_WORKLOADS:
+            log(f"workload {name}")
+            owl = W.get(name)
+            orun = Run(owl, "topk", args, owl.steps)
+            r, *_ = workload_record(orun, steps, owl.steps, 2 * owl.steps
+                                    if owl.steps > 1 else 10, args.timers)
+            orun.close()
+            det["workloads"].append(r)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        if binlocal:
+        if args.selector == "binlocal":
             out["cpu_baseline"] = cpu_baseline_binlocal(
                 wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds,
                 args.bin_len, args.cap_den)
-        elif sampled:
+        elif args.selector == "sampled":
             out["cpu_baseline"] = cpu_baseline_sampled(
                 wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds)
         else:
