@@ -32,4 +32,7 @@ from .c_oracle import (  # noqa: F401
     fmix32,
     sampled_select_mask,
     sampled_step,
+    shared_gather_mask,
+    shared_step,
+    shared_sum,
 )

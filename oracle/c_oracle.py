@@ -79,6 +79,13 @@ def load():
                                      ctypes.c_float, ctypes.c_double, P, P, P,
                                      P, P, P, P]
     lib.orc_sampled_step.restype = ctypes.c_int
+    lib.orc_shared_gather_mask.argtypes = [P, P, i64, P, i64, P]
+    lib.orc_shared_gather_mask.restype = i64
+    lib.orc_shared_step.argtypes = [ctypes.c_int32, P, P, P, P, P, P,
+                                    ctypes.c_float, ctypes.c_double, P, P, P]
+    lib.orc_shared_step.restype = ctypes.c_int
+    lib.orc_shared_sum.argtypes = [ctypes.c_int32, P, i64, P]
+    lib.orc_shared_sum.restype = None
     _lib = lib
     return lib
 
@@ -278,3 +285,56 @@ def sampled_step(sizes, k, cap, g, u, v, m, clip):
     if rc != 0:
         raise ValueError("bad k or capacity")
     return idx[:C], val[:C], count, total, theta, float(norm[0]), np.float32(scale[0])
+
+
+def shared_gather_mask(u, v, idx):
+    """A learner's values at the shared (ascending) local indices idx of one
+    tensor, then masking there, in place.  Returns val."""
+    assert u.size == v.size
+    idx = np.ascontiguousarray(idx, dtype=np.uint32)
+    k = idx.size
+    val = np.zeros(max(k, 1), np.float32)
+    got = load().orc_shared_gather_mask(_ptr(u, np.float32), _ptr(v, np.float32),
+                                        v.size, _ptr(idx, np.uint32) if k else None,
+                                        k, _ptr(val, np.float32))
+    if got < 0:
+        raise ValueError("shared indices not strictly ascending or out of range")
+    return val[:k].copy()
+
+
+def shared_step(sizes, k, idx, g, u, v, m, clip):
+    """One step of a learner that takes the leader's index set idx (every
+    tensor's k[t] local indices back to back, as step() writes them); in
+    place on u, v.  Returns (val, norm, scale)."""
+    sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+    k = np.ascontiguousarray(k, dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.uint32)
+    K = int(k.sum())
+    assert idx.size == K
+    val = np.zeros(max(K, 1), np.float32)
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    ib = idx if K else np.zeros(1, np.uint32)
+    rc = load().orc_shared_step(len(sizes), _ptr(sizes, np.int64), _ptr(k, np.int64),
+                                _ptr(ib, np.uint32), _ptr(g, np.float32),
+                                _ptr(u, np.float32), _ptr(v, np.float32),
+                                float(np.float32(m)), float(clip),
+                                _ptr(val, np.float32), _ptr(norm, np.float64),
+                                _ptr(scale, np.float32))
+    if rc != 0:
+        raise ValueError("bad k or shared indices")
+    return val[:K].copy(), float(norm[0]), np.float32(scale[0])
+
+
+def shared_sum(vals):
+    """Element-wise sum of the learners' value vectors in learner order from
+    +0.0 (binary32)."""
+    vals = [np.ascontiguousarray(x, dtype=np.float32) for x in vals]
+    K = vals[0].size if vals else 0
+    assert all(x.size == K for x in vals)
+    out = np.zeros(max(K, 1), np.float32)
+    Arr = ctypes.c_void_p * max(len(vals), 1)
+    ptrs = Arr(*[x.ctypes.data for x in vals])
+    load().orc_shared_sum(len(vals), ctypes.cast(ptrs, ctypes.c_void_p), K,
+                          _ptr(out, np.float32))
+    return out[:K].copy()

@@ -463,4 +463,88 @@ int orc_sampled_step(int32_t T, const int64_t* sizes, const int64_t* k,
     return 0;
 }
 
+/*
+ * Commutative, shared-index compression (the ScaleComp abstract on the
+ * taxoreview.com page: the learners' gradient distributions are alike, which
+ * allows a commutative compressor whose communication cost does not grow
+ * with the number of learners and which an all-reduce can carry).  The page
+ * gives no mechanism; the reading taken here is the plainest one:
+ *   - every learner of a step sends its v at one shared index set S per
+ *     tensor; keeping the same indices on every learner is what makes the
+ *     compressor commute with the sum over learners (selection at fixed
+ *     indices is linear);
+ *   - S is one learner's exact top-k (the DGC rule, ties toward the lower
+ *     index), that learner being the step's leader, t mod W;
+ *   - each learner masks u and v at S (momentum factor masking at the
+ *     shared set) and keeps the rest as its residual.
+ * This function is what a learner other than the leader does with S:
+ * writes val[j] = v[idx[j]] (signed, before masking) for j < k, then sets
+ * u and v to +0.0f at those indices.  idx must be strictly ascending and
+ * below n.  Returns k, or -1 if k < 0 or the indices are not so.
+ */
+int64_t orc_shared_gather_mask(float* u, float* v, int64_t n, const uint32_t* idx,
+                               int64_t k, float* val) {
+    if (k < 0) return -1;
+    int64_t prev = -1;
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t i = (int64_t)idx[j];
+        if (i <= prev || i >= n) return -1;
+        prev = i;
+    }
+    for (int64_t j = 0; j < k; ++j) val[j] = v[idx[j]];
+    for (int64_t j = 0; j < k; ++j) {
+        u[idx[j]] = 0.0f;
+        v[idx[j]] = 0.0f;
+    }
+    return k;
+}
+
+/*
+ * One step of a learner that is not the leader: clip and momentum as in
+ * orc_step, then per tensor orc_shared_gather_mask with the shared local
+ * indices idx[koff_t .. koff_t + k[t]) (koff_t = k[0] + ... + k[t-1], the
+ * layout orc_step writes).  val receives the values at the same offsets.
+ * Returns 0, or -1 on a bad k or bad indices.
+ */
+int orc_shared_step(int32_t T, const int64_t* sizes, const int64_t* k,
+                    const uint32_t* idx, const float* g, float* u, float* v,
+                    float m, double clip, float* val, double* norm_out,
+                    float* scale_out) {
+    int64_t n = 0;
+    std::vector<int64_t> off((size_t)T + 1, 0), koff((size_t)T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        if (k[t] < 0 || k[t] > sizes[t]) return -1;
+        off[(size_t)t + 1] = off[(size_t)t] + sizes[t];
+        koff[(size_t)t + 1] = koff[(size_t)t] + k[t];
+        n += sizes[t];
+    }
+    orc_clip_scale(g, n, clip, norm_out, scale_out);
+    orc_momentum(g, n, *scale_out, m, u, v);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t got = orc_shared_gather_mask(u + off[(size_t)t], v + off[(size_t)t],
+                                             sizes[t], idx + koff[(size_t)t], k[t],
+                                             val + koff[(size_t)t]);
+        if (got != k[t]) bad = 1;
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * The aggregate of shared-index compression: the element-wise sum of the W
+ * learners' value vectors (each K long, the same index set), in learner
+ * order from +0.0: out[j] = fl(...fl(fl(+0 + vals[0][j]) + vals[1][j])...
+ * + vals[W-1][j]).  This is the reduction an all-reduce of K floats carries;
+ * its size does not depend on W.
+ */
+void orc_shared_sum(int32_t W, const float* const* vals, int64_t K, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; ++j) {
+        float s = 0.0f;
+        for (int32_t w = 0; w < W; ++w) s = s + vals[w][j];
+        out[j] = s;
+    }
+}
+
 }  /* extern "C" */
