@@ -26,9 +26,13 @@ of exact top-k (dgc_compress_binlocal + dgc_encode_counts, bins of
 With --selector sampled it uses the sampled (approximate) threshold for the
 same k as top-k (dgc_compress_sampled + dgc_encode_counts, at most 4 k per
 tensor delivered) and reports how far the sent counts are from k.
+With --selector shared it uses shared-index compression (the ScaleComp
+reading): the leader (step mod W) runs dgc_compress + dgc_encode, the other
+learners dgc_compress_shared at its indices, and dgc_shared_sum adds the
+value vectors in learner order into the fresh dense sum.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat1b]
-                    [--selector topk|binlocal|sampled] [--bin-len 512] [--cap-den 8]
+                    [--selector topk|binlocal|sampled|shared] [--bin-len 512] [--cap-den 8]
 """
 
 import argparse
@@ -122,9 +126,10 @@ def parse():
     ap.add_argument("--timers", choices=("fused", "off"), default="fused",
                     help="library timers in the timed region: the element-wise "
                          "pass only (default), or none (then roofline is null)")
-    ap.add_argument("--selector", choices=("topk", "binlocal", "sampled"), default="topk",
-                    help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, or "
-                         "the sampled threshold")
+    ap.add_argument("--selector", choices=("topk", "binlocal", "sampled", "shared"),
+                    default="topk",
+                    help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, the "
+                         "sampled threshold, or shared-index compression (ScaleComp)")
     ap.add_argument("--bin-len", type=int, default=512,
                     help="bin length for --selector binlocal (1..1024)")
     ap.add_argument("--cap-den", type=int, default=8,
@@ -212,6 +217,58 @@ def cpu_baseline_sampled(wl, host_samples, n_chunks, seconds):
     }
 
 
+def cpu_baseline_shared(wl, host_samples, n_chunks, seconds):
+    """As cpu_baseline, with shared-index compression: per gradient step the
+    leader's exact top-k, the other learners' gather and mask at its set
+    (each with its own state, all fed learner 0's sample gradient), the
+    learner-order sum and the dense scatter."""
+    import oracle
+    sizes = np.array(wl.sizes[:n_chunks], np.int64)
+    d = wl.densities[0]
+    k = np.array([oracle.k_for_density(int(s), d.numerator, d.denominator) for s in sizes])
+    n = int(sizes.sum())
+    Wn = wl.learners
+    us = [np.zeros(n, np.float32) for _ in range(Wn)]
+    vs = [np.zeros(n, np.float32) for _ in range(Wn)]
+    dense = np.zeros(n, np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    koff = np.concatenate([[0], np.cumsum(k)])
+    t0 = time.perf_counter()
+    steps = 0
+    for cycle in range(4):
+        for g in host_samples:
+            g = g[:n]
+            lead = steps % Wn
+            idx, lval, _, _ = oracle.step(sizes, k, g, us[lead], vs[lead], wl.momentum,
+                                          wl.clip)
+            vals = []
+            for w in range(Wn):
+                if w == lead:
+                    vals.append(lval)
+                else:
+                    vals.append(oracle.shared_step(sizes, k, idx, g, us[w], vs[w],
+                                                   wl.momentum, wl.clip)[0])
+            ssum = oracle.shared_sum(vals)
+            dense[:] = 0
+            for t in range(len(sizes)):
+                dense[offs[t] + idx[koff[t]:koff[t + 1]].astype(np.int64)] = \
+                    ssum[koff[t]:koff[t + 1]]
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * Wn * steps / dt / 1e9, 4),
+        "unit": "G elem/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{Wn} learners fed learner 0's gradients, {steps} steps, first "
+                   f"{n_chunks} of {len(wl.sizes)} tensors ({n} elements per learner): "
+                   "clip, momentum, the leader's exact top-k, the others' gather and "
+                   f"mask at its set, learner-order sum, dense scatter; {dt:.1f} s"),
+    }
+
+
 def cpu_baseline(wl, host_samples, n_chunks, seconds):
     """The oracle as it stands on the first n_chunks tensors of learner 0:
     compress + encode + decode per gradient step, cycling over the steps
@@ -295,6 +352,7 @@ class Run:
         self.T = T
         self.binlocal = selector == "binlocal"
         self.sampled = selector == "sampled"
+        self.shared = selector == "shared"
         if self.binlocal:
             self.bins = [args.bin_len] * T
             self.caps = [s // args.cap_den for s in wl.sizes]
@@ -329,6 +387,9 @@ class Run:
         self.learners = [dgc.Learner(list(wl.sizes), kmax, wl.momentum)
                          for _ in range(wl.learners)]
         self.dense = torch.zeros(n, dtype=torch.float32, device="cuda")
+        if self.shared:
+            self.out_sum = torch.empty(max(int(sum(kmax)), 1), dtype=torch.float32,
+                                       device="cuda")
         self.main = torch.cuda.current_stream()
         self.pipeline = args.pipeline and selector == "topk"
         if self.pipeline:
@@ -352,6 +413,24 @@ class Run:
         t = s % self.gsteps
         k = self.ks[t % len(self.ks)]
         streams_of = lambda: [(L.runs, L.vals, L.entries) for L in learners]  # noqa: E731
+        if self.shared:
+            # the leader (step mod W) selects and encodes its index set (the
+            # set's broadcast, in the pages' run-length format); the others
+            # send and mask at it; the value vectors are summed in learner
+            # order into the fresh dense sum
+            lead = s % len(learners)
+            Ld = learners[lead]
+            K = int(sum(k))
+            Ld.compress(self.grads[(lead, t)], k, self.wl.clip)
+            if not args.fused_only:
+                Ld.encode(k)
+            for w, L in enumerate(learners):
+                if w != lead:
+                    L.compress_shared(self.grads[(w, t)], k, Ld.idx[:K], self.wl.clip)
+            if not args.fused_only:
+                dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, Ld.idx[:K],
+                               self.out_sum, self.dense)
+            return
         if self.binlocal or self.sampled:
             step_caps = self.caps if self.binlocal else self.caps_by_step[t % len(self.ks)]
             for w, L in enumerate(learners):
@@ -577,6 +656,16 @@ def main():
         kernel_name = ("k_bl_fused (clip-scale + momentum correction + accumulation + "
                        + ("per-bin maxima + salient entries to slots)" if run.binlocal else
                           "entries at or above the sampled threshold to slots)"))
+    elif run.shared:
+        fused_bytes = 20 * n  # read g, u, v; write u, v (both passes)
+        # per learner-step, the mean of one leader (top-k) and W - 1 followers
+        # (the norm, 20 B/elem, the shared indices read, the values written)
+        K = int(sum(ks[0]))
+        follower = n * (20 + 4 * clip) + 8 * K
+        pipeline_bytes = (compress_alg_bytes(wl, ks[0]) + (wl.learners - 1) * follower) \
+            / wl.learners
+        kernel_name = ("k_fused (leader) and k_sh_fused (the others: clip-scale + momentum "
+                       "correction + accumulation + values at the shared indices, masked)")
     else:
         fused_bytes = 20 * n  # read g, u, v; write u, v
         pipeline_bytes = compress_alg_bytes(wl, ks[0])
@@ -668,6 +757,11 @@ def main():
                     "salient_fraction": round(salient / n, 5),
                     "delivered_per_learner": delivered,
                     "truncated_tensors": truncated})
+    elif run.shared:
+        out["config"].update({
+            "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
+            "density": str(wl.densities[0]),
+            "leader": "step mod learners (exact top-k); the others at its indices"})
     else:
         path = [L.path_counts() for L in learners]
         info = np.concatenate([L.select_info() for L in learners])
@@ -708,6 +802,9 @@ def main():
         elif args.selector == "sampled":
             out["cpu_baseline"] = cpu_baseline_sampled(
                 wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds)
+        elif args.selector == "shared":
+            out["cpu_baseline"] = cpu_baseline_shared(
+                wl, host_samples, min(args.cpu_sample_chunks, 16), args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline(wl, host_samples, args.cpu_sample_chunks,
                                                args.cpu_seconds)

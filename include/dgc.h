@@ -91,10 +91,12 @@ extern "C" {
 
 /* Timers for dgc_get_kernel_time. */
 #define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress,
-                                 dgc_compress_binlocal or dgc_compress_sampled */
+                                 dgc_compress_binlocal, dgc_compress_sampled or
+                                 dgc_compress_shared */
 #define DGC_TIMER_COMPRESS 1  /* all of one of those calls */
 #define DGC_TIMER_ENCODE 2    /* all of dgc_encode / dgc_encode_counts */
-#define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate */
+#define DGC_TIMER_DECODE 3    /* all of dgc_decode_accumulate, dgc_decode_sum
+                                 or dgc_shared_sum */
 
 typedef struct dgc_state dgc_state;
 
@@ -250,6 +252,65 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
                          const int64_t* cap, double clip, uint32_t* out_idx,
                          float* out_val, int64_t* out_count, int64_t* out_total,
                          double* out_norm, float* out_scale, hipStream_t stream);
+
+/*
+ * One step of a learner that sends at a shared index set: commutative
+ * compression (the ScaleComp abstract on the taxoreview.com page: the
+ * learners' gradient distributions are alike, which allows a compressor
+ * that commutes with the sum over learners, whose communication cost does
+ * not grow with their number and which an all-reduce can carry).  Reading:
+ * each step one learner, the leader (step mod W), selects with
+ * dgc_compress; every other learner calls this with the leader's out_idx,
+ * so all learners send their v at the same indices, and dgc_shared_sum
+ * adds their value vectors.  Steps 1, 2 and 4 are dgc_compress's; step 3
+ * becomes:
+ *   3s. out_val[j] = v[shared_idx[j]] for tensor t's k[t] shared local
+ *       indices (at offset K_t = k[0] + ... + k[t-1]); u and v are masked
+ *       (+0.0f) there
+ * Arguments:
+ *   g          device const float[n], 16-byte aligned
+ *   k          host int64[T], 0 <= k[t] <= k_max[t]: the shared set's size
+ *   shared_idx device const uint32[sum k], 4-byte aligned: per tensor k[t]
+ *              strictly ascending local indices below n_t (dgc_compress's
+ *              out_idx has this layout)
+ *   clip       as for dgc_compress
+ *   out_val    device float[sum k], 4-byte aligned: the values of v at the
+ *              shared indices (signed, before masking), same offsets
+ *   out_norm, out_scale  as for dgc_compress
+ * A shared_idx that is not ascending or leaves its tensor latches
+ * DGC_ECORRUPT (dgc_get_status); the affected values are then unspecified,
+ * but nothing is written outside out_val, u and v.  Deterministic.
+ * Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_compress_shared(dgc_state* st, const float* g, const int64_t* k,
+                        const uint32_t* shared_idx, double clip, float* out_val,
+                        double* out_norm, float* out_scale, hipStream_t stream);
+
+/*
+ * The aggregate of shared-index compression (ScaleComp abstract, as for
+ * dgc_compress_shared): the element-wise sum of the learners' value vectors
+ * in learner order from +0.0,
+ *   out_sum[j] = fl(...fl(fl(+0 + vals[0][j]) + vals[1][j])... + vals[W-1][j]),
+ * K = sum k floats whatever the number of learners (what an all-reduce
+ * carries), and optionally the fresh dense sum: out_sum scattered at the
+ * shared indices, +0.0 everywhere else -- the same bits as encoding every
+ * learner's (shared_idx, values) and dgc_decode_sum of those streams.
+ *   vals       host array of n_learners device pointers, each float[sum k]
+ *              laid out as dgc_compress_shared's out_val (the leader's is
+ *              dgc_compress's out_val)
+ *   k          host int64[T], as given to the compress calls
+ *   shared_idx device const uint32[sum k]: the shared indices (read only
+ *              when dense is set)
+ *   out_sum    device float[sum k], 4-byte aligned: out, the learner-order
+ *              sums (required when sum k > 0)
+ *   dense      device float[n], 4-byte aligned, or NULL: out, every element
+ *              written
+ * n_learners = 0 gives +0.0 sums.  An index outside its tensor latches
+ * DGC_ECORRUPT and is not written.  Returns DGC_OK, DGC_EINVAL or DGC_EHIP.
+ */
+int dgc_shared_sum(const dgc_state* st, int32_t n_learners, const float* const* vals,
+                   const int64_t* k, const uint32_t* shared_idx, float* out_sum,
+                   float* dense, hipStream_t stream);
 
 /*
  * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is

@@ -16,6 +16,7 @@
 #include "kernels_codec.hpp"
 #include "kernels_compress.hpp"
 #include "kernels_sampled.hpp"
+#include "kernels_shared.hpp"
 
 using namespace dgc;
 
@@ -963,6 +964,92 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
     }
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
+int dgc_compress_shared(dgc_state* st, const float* g, const int64_t* k,
+                        const uint32_t* shared_idx, double clip, float* out_val,
+                        double* out_norm, float* out_scale, hipStream_t stream) {
+    if (!st) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (p.n > 0 && (!g || !aligned(g, 16))) return DGC_EINVAL;
+    if (K > 0 && (!shared_idx || !out_val || !aligned(shared_idx, 4) || !aligned(out_val, 4)))
+        return DGC_EINVAL;
+    if (std::isnan(clip)) return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const bool clip_on = clip > 0.0;
+    DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    if (clip_on) {
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                   st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
+    } else if (p.P == 0) {
+        k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
+    }
+    DGC_LAUNCH_CHECK();
+    if (p.P > 0) {
+        // the pieces' shared runs go where dgc_compress keeps its candidate
+        // counts (one 32-bit word per piece)
+        k_sh_poff<<<grid_for(cdiv(p.P, kBlock), cdiv(p.P, kBlock)), kBlock, 0, stream>>>(
+            st->L, st->K, shared_idx, st->run_cnt, p.P);
+        DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+        k_sh_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), cdiv(p.P, kWavesPerBlock)), kBlock, 0,
+                     stream>>>(g, st->u, st->v, st->L, st->K, st->sc, clip_on, st->m,
+                               shared_idx, st->run_cnt, out_val, p.P, out_norm, out_scale);
+        DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+    }
+    DGC_LAUNCH_CHECK();
+    if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+        return DGC_EHIP;
+    DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
+int dgc_shared_sum(const dgc_state* cst, int32_t n_learners, const float* const* vals,
+                   const int64_t* k, const uint32_t* shared_idx, float* out_sum,
+                   float* dense, hipStream_t stream) {
+    dgc_state* st = const_cast<dgc_state*>(cst);
+    if (!st || n_learners < 0) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (K > 0 && (!out_sum || !aligned(out_sum, 4))) return DGC_EINVAL;
+    if (K > 0 && n_learners > 0 && !vals) return DGC_EINVAL;
+    for (int32_t w = 0; K > 0 && w < n_learners; ++w)
+        if (!vals[w] || !aligned(vals[w], 4)) return DGC_EINVAL;
+    if (dense && !aligned(dense, 4)) return DGC_EINVAL;
+    if (dense && K > 0 && (!shared_idx || !aligned(shared_idx, 4))) return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    DGC_TRY(timer_begin(st, DGC_TIMER_DECODE, stream));
+    if (dense && p.n > 0)
+        k_dec_fill<<<int(cdiv(p.n, kDecBlock)), kBlock, 0, stream>>>(dense, p.n);
+    if (K > 0) {
+        const int pg = grid_for(st->KT, int64_t(st->num_cus) * kCodecBlocksPerCU);
+        int32_t w0 = 0;
+        do {
+            ShBatch B{};
+            B.W = std::min<int32_t>(kShBatch, n_learners - w0);
+            for (int w = 0; w < B.W; ++w) B.vals[w] = vals[w0 + w];
+            const bool last = w0 + B.W >= n_learners;
+            k_sh_sum<<<pg, kBlock, 0, stream>>>(st->L, st->K, B, int(w0 == 0), shared_idx,
+                                                out_sum, last ? dense : nullptr, st->sc,
+                                                st->KT);
+            w0 += B.W;
+        } while (w0 < n_learners);
+    }
+    DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
     return DGC_OK;
 }
 

@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.dgc_compress_sampled.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
                                        P, P, P]
     L.dgc_compress_sampled.restype = ctypes.c_int
+    L.dgc_compress_shared.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P]
+    L.dgc_compress_shared.restype = ctypes.c_int
+    L.dgc_shared_sum.argtypes = [P, i32, P, P, P, P, P, P]
+    L.dgc_shared_sum.restype = ctypes.c_int
     L.dgc_encode_counts.argtypes = [P, P, P, P, P, P, P, P, P]
     L.dgc_encode_counts.restype = ctypes.c_int
     L.dgc_stream_capacity.argtypes = [P, P]
@@ -192,6 +196,26 @@ def dgc_compress_sampled(st, g, k, cap, clip: float, out_idx, out_val, out_count
                                       _dp(out_total), _dp(out_norm), _dp(out_scale),
                                       _stream(stream)),
            "dgc_compress_sampled")
+
+
+def dgc_compress_shared(st, g, k, shared_idx, clip: float, out_val, out_norm=None,
+                        out_scale=None, stream=None):
+    kk = _i64(k)
+    _check(lib().dgc_compress_shared(st, _dp(g), _hp(kk), _dp(shared_idx), float(clip),
+                                     _dp(out_val), _dp(out_norm), _dp(out_scale),
+                                     _stream(stream)),
+           "dgc_compress_shared")
+
+
+def dgc_shared_sum(st, vals: Sequence, k, shared_idx, out_sum, dense=None, stream=None):
+    kk = _i64(k)
+    W = len(vals)
+    Arr = ctypes.c_void_p * max(W, 1)
+    vv = Arr(*[_dp(x) for x in vals])
+    _check(lib().dgc_shared_sum(st, W, ctypes.cast(vv, ctypes.c_void_p), _hp(kk),
+                                _dp(shared_idx), _dp(out_sum), _dp(dense),
+                                _stream(stream)),
+           "dgc_shared_sum")
 
 
 def dgc_stream_capacity(st, n_tensors: int) -> np.ndarray:
@@ -378,6 +402,14 @@ class Learner:
                              self.count, self.total, self.norm, self.scale, stream)
         return self.idx[:C], self.val[:C], self.count, self.total
 
+    def compress_shared(self, g, k: Sequence[int], shared_idx, clip: float, stream=None):
+        """One step at another learner's index set (shared_idx: that
+        learner's idx, sum(k) entries).  Returns the val view (sum(k))."""
+        K = int(sum(int(x) for x in k))
+        dgc_compress_shared(self.state, g, k, shared_idx, clip, self.val, self.norm,
+                            self.scale, stream)
+        return self.val[:K]
+
     def encode_counts(self, cap: Sequence[int], stream=None):
         """Encode what compress_binlocal delivered (counts on the device)."""
         dgc_encode_counts(self.state, cap, self.count, self.idx, self.val,
@@ -432,3 +464,10 @@ def decode_sum(layout_learner: Learner, streams: List[Tuple], dense, stream=None
     from +0.0 (every element of dense is written)."""
     dgc_decode_sum(layout_learner.state, [s[0] for s in streams],
                    [s[1] for s in streams], [s[2] for s in streams], dense, stream)
+
+
+def shared_sum(layout_learner: Learner, vals: Sequence, k: Sequence[int], shared_idx,
+               out_sum, dense=None, stream=None):
+    """out_sum = the learners' value vectors summed in learner order from +0.0;
+    dense (optional) = out_sum scattered at shared_idx, +0.0 elsewhere."""
+    dgc_shared_sum(layout_learner.state, vals, k, shared_idx, out_sum, dense, stream)

@@ -94,6 +94,9 @@ def test_init_and_calls_reject_bad_arguments_before_any_launch():
                                None) == dgc.DGC_EINVAL
     assert L.dgc_compress_sampled(None, None, None, None, 0.0, None, None, None, None,
                                   None, None, None) == dgc.DGC_EINVAL
+    assert L.dgc_compress_shared(None, None, None, None, 0.0, None, None, None,
+                                 None) == dgc.DGC_EINVAL
+    assert L.dgc_shared_sum(None, 1, None, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_accumulate(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_sum(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_sum(None, 0, None, None, None, None, None) == dgc.DGC_EINVAL

@@ -218,3 +218,76 @@ def test_flat1b_sampled_full():
     """The sampled-threshold selector (DGC review, RQ4) in the benchmark's
     configuration: target k = 16778 per chunk, at most 4 k delivered."""
     _flat1b_full("sampled")
+
+
+@pytest.mark.timeout(1200)
+def test_flat1b_shared_full():
+    """Shared-index compression (ScaleComp abstract; reading: the leader of
+    step t is learner t mod 4 and selects with dgc_compress, the others send
+    and mask at its indices) at full size: every learner's values and u/v
+    state on all 64 chunks, the learner-order sums and the fresh dense sum,
+    for 3 steps, against the oracle.  Step-major (the followers need the
+    leader's set), so the host holds the four learners' oracle state."""
+    import torch
+    wl = W.get("flat1b")
+    C = wl.sizes[0]
+    T = len(wl.sizes)
+    sizes = np.array(wl.sizes, np.int64)
+    k = [oracle_k(C, wl.densities[0])] * T
+    K = sum(k)
+    learners = [dgc.Learner(list(wl.sizes), k, wl.momentum) for _ in range(wl.learners)]
+    ou = [np.zeros(wl.n, np.float32) for _ in learners]
+    ov = [np.zeros(wl.n, np.float32) for _ in learners]
+    g_host = np.empty(wl.n, np.float32)
+    out_sum = torch.empty(K, dtype=torch.float32, device="cuda")
+    for t in range(wl.steps):
+        lead = t % wl.learners
+        order = [lead] + [w for w in range(wl.learners) if w != lead]
+        o_vals = {}
+        for w in order:
+            tag = f"flat1b shared step {t} learner {w} (leader {lead})"
+            say(f"{tag}: generate + GPU")
+            W.gradient(wl, w, t, out=g_host)
+            g = torch.from_numpy(g_host).cuda()
+            L = learners[w]
+            if w == lead:
+                L.compress(g, k, wl.clip)
+            else:
+                L.compress_shared(g, k, learners[lead].idx[:K], wl.clip)
+            torch.cuda.synchronize()
+            del g
+            assert L.status() == dgc.DGC_OK, tag
+            say(f"{tag}: oracle")
+            if w == lead:
+                o_idx, o_vals[w], o_norm, o_s = oracle.step(sizes, np.array(k), g_host, ou[w],
+                                                            ov[w], wl.momentum, wl.clip)
+                assert np.array_equal(_host(L.idx[:K]).view(np.uint32), o_idx), tag
+            else:
+                o_vals[w], o_norm, o_s = oracle.shared_step(sizes, k, o_idx, g_host, ou[w],
+                                                            ov[w], wl.momentum, wl.clip)
+            say(f"{tag}: compare")
+            assert abs(float(L.norm.cpu()[0]) - o_norm) <= 1e-6 * o_norm, tag
+            assert np.float32(L.scale.cpu()[0]) == o_s, tag
+            assert np.array_equal(f32_bits(_host(L.val[:K])), f32_bits(o_vals[w])), tag
+            for name, dev, want in (("u", L.u, ou[w]), ("v", L.v, ov[w])):
+                got = _host(dev[: wl.n])
+                assert np.array_equal(f32_bits(got), f32_bits(want)), (tag, name, first_diff(
+                    f32_bits(got), f32_bits(want)))
+                del got
+        say(f"flat1b shared step {t}: sum")
+        dense = torch.full((wl.n,), float("nan"), dtype=torch.float32, device="cuda")
+        dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, learners[lead].idx[:K],
+                       out_sum, dense)
+        torch.cuda.synchronize()
+        assert learners[0].status() == dgc.DGC_OK
+        o_sum = oracle.shared_sum([o_vals[w] for w in range(wl.learners)])
+        assert np.array_equal(f32_bits(_host(out_sum)), f32_bits(o_sum)), t
+        want = np.zeros(wl.n, np.float32)
+        koff = np.arange(T + 1, dtype=np.int64) * k[0]
+        for c in range(T):
+            want[c * C + o_idx[koff[c]:koff[c + 1]].astype(np.int64)] = o_sum[koff[c]:koff[c + 1]]
+        got = _host(dense)
+        assert np.array_equal(f32_bits(got), f32_bits(want)), (t, "dense")
+        del got, want, dense
+    for L in learners:
+        L.close()
