@@ -313,6 +313,33 @@ int dgc_shared_sum(const dgc_state* st, int32_t n_learners, const float* const* 
                    float* dense, hipStream_t stream);
 
 /*
+ * dgc_shared_sum without a state or workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): it allocates nothing, on the
+ * device or the host.  Its per-call tables (the layout's offsets, the k
+ * tables) and its status latch live in a static device array of 640 KiB
+ * that the library holds on each GPU it runs on until the process ends;
+ * its address on a device is looked up once, on the first call there.
+ *   n_tensors  1 <= T <= 16384 (more returns DGC_ECAPACITY, before anything
+ *              is enqueued)
+ *   sizes      host int64[T], 0 <= n_t < 2^32: the layout (n = sum)
+ *   k          host int64[T], 0 <= k[t] <= n_t
+ *   n_learners, vals, shared_idx, out_sum, dense  as for dgc_shared_sum
+ *   status     device int32[1], 4-byte aligned, or NULL: out, DGC_OK, or
+ *              DGC_ECORRUPT when an index left its tensor (that entry is
+ *              not written to dense)
+ * The results are dgc_shared_sum's, bit for bit.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams,
+ * other threads) race; calls in one stream's order do not.  The host
+ * arrays may be reused as soon as the call returns.  Returns DGC_OK,
+ * DGC_EINVAL, DGC_ECAPACITY or DGC_EHIP.
+ */
+int dgc_shared_sum_static(int32_t n_tensors, const int64_t* sizes, int32_t n_learners,
+                          const float* const* vals, const int64_t* k,
+                          const uint32_t* shared_idx, float* out_sum, float* dense,
+                          int32_t* status, hipStream_t stream);
+
+/*
  * Capacity layout of encoded streams: cap_offsets[t] (host int64[T+1]) is
  * the first entry slot of tensor t; tensor t may use up to
  * cap_offsets[t+1] - cap_offsets[t] entries: k_max[t] + floor(n_t / 65536),

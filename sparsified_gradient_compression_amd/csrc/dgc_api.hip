@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -248,6 +249,91 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_bsel = take(size_t(p.NBLK) * 4);
     p.total = off;
     return DGC_OK;
+}
+
+// ---------------------------------------------------------------- static scratch
+
+// dgc_shared_sum_static keeps its per-call tables and its status latch in
+// this file-scope device array instead of a workspace: kStaticMaxTensors
+// tensors at most.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses the array's name as an address:
+// the address on each device comes from hipGetSymbolAddress.
+constexpr int32_t kStaticMaxTensors = 16384;
+constexpr size_t kStaticTable = (size_t(kStaticMaxTensors + 1) * 8 + kAlign - 1) / kAlign * kAlign;
+// Scalars (status latch), then sizes, k, o, koff, ktbase
+constexpr size_t kStaticScratchBytes = kAlign + 5 * kStaticTable;
+static_assert(sizeof(Scalars) <= kAlign, "scalars fit their slot");
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kStaticMaxDevices = 64;
+struct StaticScratch {
+    std::once_flag once;
+    int rc = DGC_EHIP;
+    char* ptr = nullptr;  // device address of `scratch` on this device
+    int num_cus = 0;
+};
+StaticScratch g_static[kStaticMaxDevices];
+
+// The device address of `scratch` on device `dev` (current), found once.
+int static_scratch(int dev, char** ptr, int* num_cus) {
+    if (dev < 0 || dev >= kStaticMaxDevices) return DGC_EINVAL;
+    StaticScratch& S = g_static[dev];
+    std::call_once(S.once, [&S, dev]() {
+        void* p = nullptr;
+        int cus = 0;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+            return;
+        S.ptr = static_cast<char*>(p);
+        S.num_cus = cus;
+        S.rc = DGC_OK;
+    });
+    if (S.rc != DGC_OK) return S.rc;
+    *ptr = S.ptr;
+    *num_cus = S.num_cus;
+    return DGC_OK;
+}
+
+// One block: the layout and k tables of a static call from the copied
+// sizes and k (exclusive prefix sums), and the status latch cleared.
+__global__ __launch_bounds__(kBlock) void k_static_tables(
+    int32_t T, const int64_t* __restrict__ sz, const int64_t* __restrict__ kk,
+    int64_t* __restrict__ o, int64_t* __restrict__ koff, int64_t* __restrict__ ktbase,
+    Scalars* __restrict__ sc) {
+    __shared__ int64_t lds[kWavesPerBlock];
+    int64_t co = 0, ck = 0, ct = 0;
+    for (int32_t base = 0; base < T; base += kBlock) {
+        const int32_t t = base + int32_t(threadIdx.x);
+        const int64_t n = t < T ? sz[t] : 0, k = t < T ? kk[t] : 0;
+        const int64_t tiles = (k + kTile - 1) / kTile;
+        int64_t to, tk, tt;
+        const int64_t eo = block_exclusive_scan(n, lds, to);
+        const int64_t ek = block_exclusive_scan(k, lds, tk);
+        const int64_t et = block_exclusive_scan(tiles, lds, tt);
+        if (t < T) {
+            o[t] = co + eo;
+            koff[t] = ck + ek;
+            ktbase[t] = ct + et;
+        }
+        co += to;
+        ck += tk;
+        ct += tt;
+    }
+    if (threadIdx.x == 0) {
+        o[T] = co;
+        koff[T] = ck;
+        ktbase[T] = ct;
+        sc->status = 0;
+    }
+}
+
+// The call's status for the caller: DGC_OK, or DGC_ECORRUPT when an index
+// left its tensor.
+__global__ void k_static_status(const Scalars* __restrict__ sc, int32_t* __restrict__ status) {
+    if (threadIdx.x == 0)
+        *status = sc->status == kErrCorrupt ? DGC_ECORRUPT : (sc->status ? DGC_EHIP : DGC_OK);
 }
 
 }  // namespace
@@ -1050,6 +1136,71 @@ int dgc_shared_sum(const dgc_state* cst, int32_t n_learners, const float* const*
     }
     DGC_LAUNCH_CHECK();
     DGC_TRY(timer_end(st, DGC_TIMER_DECODE, stream));
+    return DGC_OK;
+}
+
+int dgc_shared_sum_static(int32_t n_tensors, const int64_t* sizes, int32_t n_learners,
+                          const float* const* vals, const int64_t* k,
+                          const uint32_t* shared_idx, float* out_sum, float* dense,
+                          int32_t* status, hipStream_t stream) {
+    if (n_tensors <= 0 || !sizes || !k || n_learners < 0) return DGC_EINVAL;
+    if (n_tensors > kStaticMaxTensors) return DGC_ECAPACITY;
+    const int32_t T = n_tensors;
+    int64_t n = 0, K = 0, KT = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        if (sizes[t] < 0 || sizes[t] >= (int64_t(1) << 32) || k[t] < 0 || k[t] > sizes[t])
+            return DGC_EINVAL;
+        n += sizes[t];
+        K += k[t];
+        KT += cdiv(k[t], kTile);
+    }
+    if (K > 0 && (!out_sum || !aligned(out_sum, 4))) return DGC_EINVAL;
+    if (K > 0 && n_learners > 0 && !vals) return DGC_EINVAL;
+    for (int32_t w = 0; K > 0 && w < n_learners; ++w)
+        if (!vals[w] || !aligned(vals[w], 4)) return DGC_EINVAL;
+    if (dense && !aligned(dense, 4)) return DGC_EINVAL;
+    if (dense && K > 0 && (!shared_idx || !aligned(shared_idx, 4))) return DGC_EINVAL;
+    if (status && !aligned(status, 4)) return DGC_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DGC_EHIP;
+    char* base = nullptr;
+    int num_cus = 0;
+    DGC_TRY(static_scratch(dev, &base, &num_cus));
+    Scalars* sc = reinterpret_cast<Scalars*>(base);
+    int64_t* sz = reinterpret_cast<int64_t*>(base + kAlign);
+    int64_t* kk = reinterpret_cast<int64_t*>(base + kAlign + kStaticTable);
+    int64_t* o = reinterpret_cast<int64_t*>(base + kAlign + 2 * kStaticTable);
+    int64_t* koff = reinterpret_cast<int64_t*>(base + kAlign + 3 * kStaticTable);
+    int64_t* ktbase = reinterpret_cast<int64_t*>(base + kAlign + 4 * kStaticTable);
+    // pageable sources are staged by the runtime before the calls return
+    if (hipMemcpyAsync(sz, sizes, size_t(T) * 8, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(kk, k, size_t(T) * 8, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return DGC_EHIP;
+    k_static_tables<<<1, kBlock, 0, stream>>>(T, sz, kk, o, koff, ktbase, sc);
+    DevLayout L{};
+    L.T = T;
+    L.o = o;
+    DevK Kd{};
+    Kd.k = kk;
+    Kd.koff = koff;
+    Kd.ktbase = ktbase;
+    if (dense && n > 0)
+        k_dec_fill<<<int(cdiv(n, kDecBlock)), kBlock, 0, stream>>>(dense, n);
+    if (K > 0) {
+        const int pg = grid_for(KT, int64_t(num_cus) * kCodecBlocksPerCU);
+        int32_t w0 = 0;
+        do {
+            ShBatch B{};
+            B.W = std::min<int32_t>(kShBatch, n_learners - w0);
+            for (int w = 0; w < B.W; ++w) B.vals[w] = vals[w0 + w];
+            const bool last = w0 + B.W >= n_learners;
+            k_sh_sum<<<pg, kBlock, 0, stream>>>(L, Kd, B, int(w0 == 0), shared_idx, out_sum,
+                                                last ? dense : nullptr, sc, KT);
+            w0 += B.W;
+        } while (w0 < n_learners);
+    }
+    if (status) k_static_status<<<1, 64, 0, stream>>>(sc, status);
+    DGC_LAUNCH_CHECK();
     return DGC_OK;
 }
 
