@@ -86,6 +86,8 @@ def kernel_source_sha(selector="topk"):
 def measured_traffic(n_elems, selector="topk"):
     """HBM bytes per launch of the element-wise pass from the committed
     rocprofv3 counter summary, if it was taken on the current kernel."""
+    if selector not in TRAFFIC:
+        return None
     try:
         with open(TRAFFIC[selector][0]) as f:
             rec = json.load(f)
