@@ -125,6 +125,9 @@ def parse():
                          "previous learner's element-wise pass is done")
     ap.add_argument("--fused-only", action="store_true",
                     help="time only dgc_compress calls (for profiling runs)")
+    ap.add_argument("--select-grid", type=int, choices=(0, 1, 2), default=0,
+                    help="DGC_OPT_SELECT_GRID for dgc_compress: 0 automatic, 1 a workgroup "
+                         "per tensor, 2 the spread passes")
     ap.add_argument("--timers", choices=("fused", "off"), default="fused",
                     help="library timers in the timed region: the element-wise "
                          "pass only (default), or none (then roofline is null)")
@@ -388,6 +391,8 @@ class Run:
         torch.cuda.synchronize()
         self.learners = [dgc.Learner(list(wl.sizes), kmax, wl.momentum)
                          for _ in range(wl.learners)]
+        for L in self.learners:
+            L.set_option(dgc.DGC_OPT_SELECT_GRID, args.select_grid)
         self.dense = torch.zeros(n, dtype=torch.float32, device="cuda")
         if self.shared:
             self.out_sum = torch.empty(max(int(sum(kmax)), 1), dtype=torch.float32,

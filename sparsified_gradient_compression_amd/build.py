@@ -20,7 +20,7 @@ LIB = os.path.join(LIBDIR, "libdgc.so")
 SOURCES = [os.path.join(CSRC, "dgc_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in
                      ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp", "kernels_sampled.hpp",
-                      "kernels_compress.hpp", "kernels_codec.hpp", "kernels_shared.hpp")] + [os.path.join(ROOT, "include", "dgc.h")]
+                      "kernels_compress.hpp", "kernels_codec.hpp", "kernels_shared.hpp", "kernels_tensor.hpp")] + [os.path.join(ROOT, "include", "dgc.h")]
 
 ARCH = os.environ.get("DGC_OFFLOAD_ARCH", "gfx950")
 

@@ -18,6 +18,7 @@
 #include "kernels_compress.hpp"
 #include "kernels_sampled.hpp"
 #include "kernels_shared.hpp"
+#include "kernels_tensor.hpp"
 
 using namespace dgc;
 
@@ -48,6 +49,9 @@ struct Plan {
     // sampled threshold: lines sampled per tensor (every line of a small
     // tensor), their sample blocks, and the tensor of each block
     std::vector<int64_t> aslines, asbase;
+    // per-tensor window of the per-tensor path: lines sampled per tensor
+    // (every line up to kMinSampleLines of them, else as slines)
+    std::vector<int64_t> wlines;
     std::vector<uint32_t> asmap;
     int64_t AS = 0;
     // merged decode: bounds per tensor (dense blocks + 1) and dense blocks
@@ -56,6 +60,10 @@ struct Plan {
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t norm_chunk = 0;
     bool short_sources = true;  // every tensor fits the per-tensor select
+    // every tensor holds at most kTensorPathMaxN elements: dgc_compress takes
+    // the per-tensor window and finish kernels, and small tensors get the
+    // sample window (all of their lines) and candidate slots too
+    bool tensor_path = true;
     // per-tensor scans that can exceed kScanStagedMin values take the
     // LDS-staged kernels: tiles over n (emit), capacity tiles (decode)
     bool staged_tiles = false, staged_etiles = false;
@@ -74,20 +82,21 @@ struct Plan {
            off_dmode = 0, off_bounds = 0, off_bmap = 0, off_bsel = 0, total = 0;
 };
 
-// Candidate slots per 1024-element piece: none for small tensors (they take
-// the dense path), else about six times the pieces' share of k_max plus
-// 24 -- the sample window aims at 1.5-2.5 k candidates, so a piece overflows
-// (sending its tensor to the dense path) only with a negligible probability
-// for unstructured data.
-int64_t piece_cap(int64_t n, int64_t kmax) {
-    if (n <= kSmallN) return 0;
+// Candidate slots per 1024-element piece: about six times the pieces' share
+// of k_max plus 24 -- the sample window aims at 1.5-2.5 k candidates, so a
+// piece overflows (sending its tensor to the dense path) only with a
+// negligible probability for unstructured data.  Small tensors get none
+// unless their whole tensor is sampled (the per-tensor path); otherwise
+// they take the dense path.
+int64_t piece_cap(int64_t n, int64_t kmax, bool small_slots) {
+    if (n == 0 || (n <= kSmallN && !small_slots)) return 0;
     return std::min<int64_t>(kPiece, cdiv(6 * kPiece * kmax, n) + 24);
 }
 
 // Capacity of a tensor's ordered candidate list, a multiple of 4 items so
 // that every tensor's list starts 16-byte aligned.
-int64_t list_cap(int64_t n, int64_t kmax, int64_t slots) {
-    if (n <= kSmallN) return 0;
+int64_t list_cap(int64_t n, int64_t kmax, int64_t slots, bool small_slots) {
+    if (n <= kSmallN && !small_slots) return 0;
     return cdiv(std::min<int64_t>(std::min<int64_t>(n, slots), 8 * kmax + 16384), 4) * 4;
 }
 
@@ -119,8 +128,11 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.etbase.assign(T + 1, 0);
     p.aslines.assign(T + 1, 0);
     p.asbase.assign(T + 1, 0);
+    p.wlines.assign(T + 1, 0);
     p.dbase.assign(T + 1, 0);
     p.bbase.assign(T + 1, 0);
+    for (int32_t t = 0; t < T; ++t)
+        if (sizes[t] > kTensorPathMaxN) p.tensor_path = false;
     for (int32_t t = 0; t < T; ++t) {
         int64_t n = sizes[t], km = kmax[t];
         if (n < 0 || n >= (int64_t(1) << 32) || km < 0 || km > n) return DGC_EINVAL;
@@ -129,9 +141,9 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.pbase[t + 1] = p.pbase[t] + np_;
         p.gbase[t + 1] = p.gbase[t] + cdiv(np_, kGroup);
         p.tbase[t + 1] = p.tbase[t] + cdiv(n, kTile);
-        p.pcap[t] = piece_cap(n, km);
+        p.pcap[t] = piece_cap(n, km, p.tensor_path);
         p.slbase[t + 1] = p.slbase[t] + np_ * p.pcap[t];
-        p.obase[t + 1] = p.obase[t] + list_cap(n, km, np_ * p.pcap[t]);
+        p.obase[t + 1] = p.obase[t] + list_cap(n, km, np_ * p.pcap[t], p.tensor_path);
         p.slines[t] = sample_lines(n);
         p.sbase[t + 1] = p.sbase[t] + cdiv(p.slines[t], kLinesPerSampleBlock);
         // a multiple of kStreamAlign entries per tensor, so that every
@@ -140,6 +152,8 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
         p.ebase[t + 1] = p.ebase[t] + ecap;
         p.etbase[t + 1] = p.etbase[t] + cdiv(ecap, kTile);
         p.aslines[t] = n <= kSmallN ? cdiv(n, kLine) : p.slines[t];
+        p.wlines[t] = std::min<int64_t>(cdiv(n, kLine),
+                                        std::max<int64_t>(kMinSampleLines, cdiv(n, kLine) / 256));
         p.asbase[t + 1] = p.asbase[t] + cdiv(p.aslines[t], kLinesPerSampleBlock);
         p.bbase[t + 1] = p.bbase[t] + cdiv(n, kDecBlock);
         p.dbase[t + 1] = p.dbase[t] + cdiv(n, kDecBlock) + 1;
@@ -211,7 +225,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     p.off_k = take((3 * T1) * sizeof(int64_t));
     p.off_kmap = take(size_t(p.TT) * 4);
     p.off_bltab = take(7 * T1 * sizeof(int64_t));
-    p.off_astab = take(2 * T1 * sizeof(int64_t));
+    p.off_astab = take(3 * T1 * sizeof(int64_t));
     p.off_asmap = take(size_t(p.AS) * 4);
     p.off_ktgt = take(T1 * sizeof(int64_t));
     p.off_dtab = take(2 * T1 * sizeof(int64_t));
@@ -377,6 +391,7 @@ struct dgc_state {
     bool ktgt_valid = false;
     std::vector<int64_t> bins_full;  // one 1024-element bin per piece
     DevSample A{};
+    const int64_t* wlines = nullptr;  // [T] lines the per-tensor window samples
     DevDec Dd{};
     int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged
     int select_grid = 0;  // 0 automatic, 1 a workgroup per tensor, 2 spread passes
@@ -726,6 +741,7 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     int64_t* at = reinterpret_cast<int64_t*>(ws + p.off_astab);
     st->A.slines = at;
     st->A.sbase = at + T1;
+    st->wlines = at + 2 * T1;
     st->A.smap = reinterpret_cast<uint32_t*>(ws + p.off_asmap);
     st->bins_full.assign(size_t(T), kMaxBin);
     int64_t* dt = reinterpret_cast<int64_t*>(ws + p.off_dtab);
@@ -767,9 +783,10 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
                                        hipMemcpyHostToDevice, stream) == hipSuccess;
     if (p.NBLK) ok = ok && hipMemcpyAsync(ws + p.off_bmap, p.bmap.data(), size_t(p.NBLK) * 4,
                                           hipMemcpyHostToDevice, stream) == hipSuccess;
-    std::vector<int64_t> atab(2 * T1, 0);
+    std::vector<int64_t> atab(3 * T1, 0);
     std::copy(p.aslines.begin(), p.aslines.end(), atab.begin());
     std::copy(p.asbase.begin(), p.asbase.end(), atab.begin() + T1);
+    std::copy(p.wlines.begin(), p.wlines.end(), atab.begin() + 2 * T1);
     ok = ok && hipMemcpyAsync(at, atab.data(), atab.size() * 8, hipMemcpyHostToDevice,
                               stream) == hipSuccess;
     if (p.AS) ok = ok && hipMemcpyAsync(ws + p.off_asmap, p.asmap.data(), size_t(p.AS) * 4,
@@ -825,6 +842,33 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     const int pg = st->num_cus * 8;  // persistent grids
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    const int force_dense = st->select_path == 1;
+    if (p.tensor_path && st->select_grid != 2) {
+        // per-tensor kernels: norm partials, window, element-wise pass, finish
+        if (clip_on)
+            k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                       st->partial);
+        k_window_tensor<<<T, kTsThreads, 0, stream>>>(
+            g, st->u, st->v, st->L, st->K, st->wlines, st->partial, p.NB, clip, int(clip_on),
+            st->sc, out_norm, out_scale, st->ts, st->m, force_dense);
+        DGC_LAUNCH_CHECK();
+        if (p.P > 0) {
+            int64_t fb = st->fused_blocks > 0 ? st->fused_blocks : cdiv(p.P, kWavesPerBlock);
+            DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+            k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
+                g, st->u, st->v, st->L, st->ts, st->sc, clip_on, st->m, st->slots,
+                st->run_cnt, p.P, out_norm, out_scale);
+            DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+        }
+        if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+            return DGC_EHIP;
+        k_finish_tensor<<<T, kTsThreads, 0, stream>>>(
+            st->L, st->K, st->ts, st->slots, st->run_cnt, st->u, st->v, st->olist_i,
+            st->olist_v, st->olist_u, out_idx, out_val, st->sc);
+        DGC_LAUNCH_CHECK();
+        DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+        return DGC_OK;
+    }
     if (clip_on) {
         k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
                                                                    st->partial);
@@ -834,7 +878,6 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
     }
     DGC_LAUNCH_CHECK();
-    const int force_dense = st->select_path == 1;
     if (p.S > 0 && !force_dense)
         k_sample<0><<<int(p.S), kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->sc,
                                                      clip_on, st->ts, st->m, st->shist);

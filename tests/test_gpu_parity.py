@@ -48,7 +48,7 @@ def run_workload(wl, steps=None, learners=None, path=0, grid=0, encode=True, tag
             say(f"{tag} step {t} learner {w} n={wl.n} T={len(wl.sizes)}")
             g = W.gradient(wl, w, t)
             got, (o_idx, o_val) = p.step(g, k, wl.clip, tag=f"{tag} s{t} w{w}")
-            check_paths(p, wl.sizes, k, path, tag=f"{tag} s{t} w{w}")
+            check_paths(p, wl.sizes, k, path, grid, tag=f"{tag} s{t} w{w}")
             if encode:
                 want = oracle_streams(wl.sizes, k, o_idx, o_val)
                 gs = gpu_streams(p, k)
@@ -59,16 +59,22 @@ def run_workload(wl, steps=None, learners=None, path=0, grid=0, encode=True, tag
     return pairs
 
 
-SMALL_N = 65536  # tensors up to this size take the dense path
+SMALL_N = 65536  # on the spread passes, tensors up to this size take the dense path
+TENSOR_PATH_MAX_N = 1 << 22  # layouts within this take the per-tensor kernels
 
 
-def check_paths(pair, sizes, k, path, tag=""):
-    """On unstructured gradients the automatic path takes the sample
-    window for every tensor above SMALL_N elements (with k > 0) and the
-    dense path for the smaller ones; the forced path is dense throughout."""
+def check_paths(pair, sizes, k, path, grid=0, tag=""):
+    """On unstructured gradients the automatic path takes the sample window
+    for every tensor with k > 0 -- on the per-tensor kernels (every tensor
+    at most 2^22 elements, grid not forced to the spread passes) small
+    tensors too, since their whole tensor is sampled; on the spread passes
+    only those above SMALL_N elements, the smaller ones taking the dense
+    path.  The forced dense path is dense throughout."""
+    per_tensor = grid != 2 and max(sizes) <= TENSOR_PATH_MAX_N
     info = pair.learner.select_info()
     for t, (n, kt) in enumerate(zip(sizes, k)):
-        want = 0 if kt == 0 else (1 if (path == 0 and n > SMALL_N) else 2)
+        window = path == 0 and (n > SMALL_N or per_tensor)
+        want = 0 if kt == 0 else (1 if window else 2)
         assert info[t, 0] == want, (tag, t, n, kt, info[t].tolist())
 
 
