@@ -492,13 +492,37 @@ int grid_for(int64_t work, int64_t cap) {
     return int(std::max<int64_t>(1, std::min<int64_t>(work, cap)));
 }
 
-// Upload k, its output offsets and its tile map when they change.
+// Upload k, its output offsets and its tile map when they change.  Up to
+// kKArgTensors tensors, k travels in the launch's arguments and one small
+// kernel writes every table on the device (nothing waits on the host);
+// larger layouts copy host-built tables (pageable copies, staged by the
+// runtime before the call returns).
 int upload_k(dgc_state* st, const int64_t* k, hipStream_t s) {
     const Plan& p = st->plan;
     const int32_t T = p.T;
     if (st->k_valid && std::memcmp(st->k_last.data(), k, size_t(T) * 8) == 0)
         return DGC_OK;
     st->k_last.assign(k, k + T);
+    // tile counts on the host too: they size the later launches
+    int64_t KT = 0;
+    st->staged_k = false;
+    for (int32_t t = 0; t < T; ++t) {
+        const int64_t tiles = cdiv(k[t], kTile);
+        st->staged_k |= tiles > kScanStagedMin;
+        KT += tiles;
+    }
+    st->KT = KT;
+    int64_t* dk = reinterpret_cast<int64_t*>(st->ws + p.off_k);
+    if (T <= kKArgTensors) {
+        KArgs a{};
+        a.T = T;
+        for (int32_t t = 0; t < T; ++t) a.k[t] = k[t];
+        k_ktables<<<T, kBlock, 0, s>>>(a, dk, dk + (T + 1), dk + 2 * (T + 1),
+                                       reinterpret_cast<uint32_t*>(st->ws + p.off_kmap));
+        if (hipGetLastError() != hipSuccess) return DGC_EHIP;
+        st->k_valid = true;
+        return DGC_OK;
+    }
     std::vector<int64_t>& tb = st->k_tables;
     tb.assign(3 * (size_t(T) + 1), 0);
     int64_t* kk = tb.data();
@@ -509,16 +533,12 @@ int upload_k(dgc_state* st, const int64_t* k, hipStream_t s) {
         koff[t + 1] = koff[t] + k[t];
         ktb[t + 1] = ktb[t] + cdiv(k[t], kTile);
     }
-    st->KT = ktb[T];
-    st->staged_k = false;
-    for (int32_t t = 0; t < T; ++t) st->staged_k |= ktb[t + 1] - ktb[t] > kScanStagedMin;
     st->kmap_host.resize(size_t(std::max<int64_t>(st->KT, 1)));
     for (int32_t t = 0; t < T; ++t)
         for (int64_t i = ktb[t]; i < ktb[t + 1]; ++i) st->kmap_host[size_t(i)] = uint32_t(t);
     // Pageable-source copies are staged by the runtime before returning,
     // so the host vectors may change on the next call.
-    if (hipMemcpyAsync(st->ws + p.off_k, tb.data(), tb.size() * 8,
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+    if (hipMemcpyAsync(dk, tb.data(), tb.size() * 8, hipMemcpyHostToDevice, s) != hipSuccess)
         return DGC_EHIP;
     if (st->KT > 0 &&
         hipMemcpyAsync(st->ws + p.off_kmap, st->kmap_host.data(),

@@ -48,6 +48,38 @@ __global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* __restrict__ p,
         p[i] = val;
 }
 
+// The per-call k tables of a layout of at most kKArgTensors tensors, from k
+// passed by value: block t writes k[t], koff[t] = k[0] + ... + k[t-1],
+// ktbase[t] (tiles of kTile entries before tensor t) and tensor t's entries
+// of the tile map; the last block also writes the totals at index T.
+constexpr int kKArgTensors = 480;
+struct KArgs {
+    int32_t T;
+    int64_t k[kKArgTensors];
+};
+__global__ __launch_bounds__(kBlock) void k_ktables(KArgs a, int64_t* __restrict__ kk,
+                                                    int64_t* __restrict__ koff,
+                                                    int64_t* __restrict__ ktbase,
+                                                    uint32_t* __restrict__ kmap) {
+    const int t = blockIdx.x;
+    int64_t off = 0, tb = 0;
+    for (int i = 0; i < t; ++i) {  // a few hundred scalar adds at most
+        off += a.k[i];
+        tb += (a.k[i] + kTile - 1) / kTile;
+    }
+    const int64_t tiles = (a.k[t] + kTile - 1) / kTile;
+    if (threadIdx.x == 0) {
+        kk[t] = a.k[t];
+        koff[t] = off;
+        ktbase[t] = tb;
+        if (t == a.T - 1) {
+            koff[a.T] = off + a.k[t];
+            ktbase[a.T] = tb + tiles;
+        }
+    }
+    for (int64_t i = threadIdx.x; i < tiles; i += kBlock) kmap[tb + i] = uint32_t(t);
+}
+
 // Scalar outputs when nothing else writes them (an empty layout with
 // clipping off).
 __global__ void k_set_scalars(Scalars* __restrict__ sc, double* __restrict__ out_norm,
