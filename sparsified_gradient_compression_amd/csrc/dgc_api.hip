@@ -924,19 +924,23 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
                                            st->atiles);
-    if (p.G > 0)
-        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
-                                                  st->run_cnt, st->goff, st->olist_i,
-                                                  st->olist_v, st->olist_u, st->u, st->v);
     // the select and emit: one workgroup per tensor when every selection
     // source is short, else passes spread over the chip
     const bool per_tensor = st->select_grid == 1 || (st->select_grid == 0 && p.short_sources);
+    // for the spread passes the gather also histograms the lists' top 21
+    // bits, which k_resolve21 turns into T's top 21 bits where it can
+    if (p.G > 0)
+        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
+                                                  st->run_cnt, st->goff, st->olist_i,
+                                                  st->olist_v, st->olist_u, st->u, st->v,
+                                                  per_tensor ? nullptr : st->hist);
     if (K > 0 && per_tensor) {
         k_select_tensor<<<T, kTsThreads, 0, stream>>>(
             st->L, st->K, st->ts, st->u, st->v, st->olist_i, st->olist_v, st->olist_u,
             out_idx, out_val, st->sc);
         DGC_LAUNCH_CHECK();
     } else if (K > 0) {
+        k_resolve21<<<T, kBlock, 0, stream>>>(st->ts, st->hist);
         k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
         k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
         DGC_LAUNCH_CHECK();

@@ -78,7 +78,9 @@ struct TensorState {
     uint32_t wbin;      // sample window: chosen top-11-bit bin (or kNoKey)
     uint32_t wabove;    // sample window: samples above wbin
     uint32_t wj;        // sample window: rank j of the targeted sample
-    uint32_t pad[4];
+    uint32_t done21;    // the top 21 bits of T were found from the gather's
+                        // histogram (the first two digit passes skip it)
+    uint32_t pad[3];
 };
 
 // Per-call scalars.

@@ -403,8 +403,29 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
         ts[t].len = uint32_t(len);
         ts[t].prefix = 0;
         ts[t].krem = uint32_t(k > 0 ? k : 0);
+        ts[t].done21 = 0;
         atiles[t] = mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift);
     }
+}
+
+// Histogram increment with wave aggregation: twice, the bin of the lowest
+// pending lane takes every lane of the wave that shares it with one LDS
+// atomic (ballot + popcount); the lanes left add one each.  Keys that crowd
+// into a few bins (the top digit of a candidate list) then cost a few
+// atomics per wave instead of 64 on one address.  Every lane of the wave
+// must call it.
+__device__ __forceinline__ void hist_inc(uint32_t* h, uint32_t bin, bool valid) {
+    uint64_t todo = __ballot(valid);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (!todo) break;  // uniform
+        const int leader = __ffsll((unsigned long long)todo) - 1;
+        const uint32_t b = __shfl(bin, leader, kWave);
+        const uint64_t same = __ballot(valid && bin == b) & todo;
+        if (lane_id() == leader) atomicAdd(&h[b], uint32_t(__popcll(same)));
+        todo &= ~same;
+    }
+    if ((todo >> lane_id()) & 1u) atomicAdd(&h[bin], 1u);
 }
 
 // One block per group.  The fused pass masked the candidates of every piece
@@ -415,7 +436,10 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
 // For any other tensor, put the slotted u and v back, so the dense path
 // reads the true values.  Threads walk the group's items, several loads in
 // flight each, and find each item's piece by binary search over the
-// in-group prefix of the run lengths; accesses are coalesced.
+// in-group prefix of the run lengths; accesses are coalesced.  With `hist`
+// set (the spread passes follow), the list's keys are also counted by their
+// top 21 bits above the window edge into the tensor's histogram row, for
+// k_resolve21.
 constexpr int kGatherBatch = 8;  // slot loads in flight per thread
 
 __global__ __launch_bounds__(kBlock) void k_gather(
@@ -423,12 +447,16 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     const CandSlot* __restrict__ slots,
     const uint32_t* __restrict__ run_cnt, const uint32_t* __restrict__ goff,
     uint32_t* __restrict__ olist_i, float* __restrict__ olist_v,
-    float* __restrict__ olist_u, float* __restrict__ u, float* __restrict__ v) {
+    float* __restrict__ olist_u, float* __restrict__ u, float* __restrict__ v,
+    uint32_t* __restrict__ hist) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t pre[kGroup + 1];
+    __shared__ uint32_t h21[kHistBins];
     const int64_t g = blockIdx.x;
     const int t = int(L.gmap[g]);
     const bool list = ts[t].mode == kModeList;  // uniform
+    const uint32_t lo21 = ts[t].lo_key >> 10;
+    for (int b = threadIdx.x; b < kHistBins; b += kBlock) h21[b] = 0;
     const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
     const int64_t np = min(kGroup, L.pbase[t + 1] - p0);  // signed: >= 1 here
     if (np <= 0) return;  // uniform; cannot happen with a valid group map
@@ -482,6 +510,70 @@ __global__ __launch_bounds__(kBlock) void k_gather(
         for (int b = 0; b < kGatherBatch; ++b) {
             const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
             if (q < tot) put(it[b], q);
+            // the list's keys by their top 21 bits above the window edge
+            // (every candidate is at least lo); bin 2047 takes the rest
+            if (list && hist) {  // uniform
+                const uint32_t d = (mag_key(it[b].v) >> 10) - lo21;
+                hist_inc(h21, d < uint32_t(kHistBins - 1) ? d : uint32_t(kHistBins - 1),
+                         q < tot);
+            }
+        }
+    }
+    if (list && hist) {  // uniform: add the group's counts to the tensor's row
+        __syncthreads();
+        uint32_t* row = hist + int64_t(t) * kHistBins;
+        for (int b = threadIdx.x; b < kHistBins; b += kBlock)
+            if (h21[b]) atomicAdd(&row[b], h21[b]);
+    }
+}
+
+// One block per tensor, after k_gather: on the list path, the bin of the
+// gather's histogram that holds the krem-th largest key gives the top 21
+// bits of T (lo21 + bin) unless it is the open top bin; then prefix and
+// krem are set and done21 marks the tensor, so the first two digit passes
+// skip it.  Clears the row.
+__global__ __launch_bounds__(kBlock) void k_resolve21(TensorState* __restrict__ ts,
+                                                      uint32_t* __restrict__ hist) {
+    constexpr int per = kHistBins / kBlock;
+    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t pick[2];
+    const int t = blockIdx.x;
+    if (ts[t].mode != kModeList) {  // uniform
+        if (threadIdx.x == 0) ts[t].done21 = 0;
+        return;
+    }
+    uint32_t* row = hist + int64_t(t) * kHistBins;
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        c[q] = row[kHistBins - 1 - (threadIdx.x * per + q)];
+        mine += c[q];
+    }
+    if (threadIdx.x == 0) pick[0] = kNoKey;
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(mine, lds, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) row[kHistBins - 1 - (threadIdx.x * per + q)] = 0;
+    const uint32_t krem = ts[t].krem;
+    const uint32_t lo21 = ts[t].lo_key >> 10;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            pick[0] = uint32_t(kHistBins - 1 - (threadIdx.x * per + q));
+            pick[1] = krem - run;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t b = pick[0];
+        if (b == kNoKey || b == uint32_t(kHistBins - 1)) {
+            ts[t].done21 = 0;
+        } else {
+            ts[t].prefix = lo21 + b;
+            ts[t].krem = pick[1];
+            ts[t].done21 = 1;
         }
     }
 }
@@ -595,6 +687,12 @@ __global__ __launch_bounds__(kBlock) void k_hist(
             src = source_values(mode, v, olist_v, L, t);
             if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
             cur_t = t;
+            if (D < 2 && ts[t].done21) {  // uniform: resolved from the gather
+                // this workgroup's next tile at or past the tensor's end (the
+                // loop's step adds the last stride)
+                a += ((ae - a + gridDim.x - 1) / gridDim.x - 1) * gridDim.x;
+                continue;
+            }
         }
         // a thread's kPerThread consecutive items (a histogram does not
         // depend on the order): one 16-byte load when the source allows
@@ -626,6 +724,7 @@ __global__ __launch_bounds__(kBlock) void k_resolve(
     __shared__ int found;
     const int t = blockIdx.x;
     if (ts[t].mode == kModeSkip) return;
+    if (D < 2 && ts[t].done21) return;  // the gather's histogram resolved it
     uint32_t* row = hist + int64_t(t) * kHistBins;
     uint32_t c[per];
     uint32_t mine = 0;

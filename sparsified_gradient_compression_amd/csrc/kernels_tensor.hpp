@@ -46,26 +46,6 @@ constexpr int kFinItems = 10240;
 constexpr int kFinRounds = int((kTensorPathMaxN / kPiece + kTsThreads - 1) / kTsThreads);
 constexpr int kFinEmitUnroll = 4;  // 64-item rounds loaded together per wave
 
-// Histogram increment with wave aggregation: twice, the bin of the lowest
-// pending lane takes every lane of the wave that shares it with one LDS
-// atomic (ballot + popcount); the lanes left add one each.  Keys that crowd
-// into a few bins (the top digit of a candidate list) then cost a few
-// atomics per wave instead of 64 on one address.  Every lane of the wave
-// must call it.
-__device__ __forceinline__ void hist_inc(uint32_t* h, uint32_t bin, bool valid) {
-    uint64_t todo = __ballot(valid);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        if (!todo) break;  // uniform
-        const int leader = __ffsll((unsigned long long)todo) - 1;
-        const uint32_t b = __shfl(bin, leader, kWave);
-        const uint64_t same = __ballot(valid && bin == b) & todo;
-        if (lane_id() == leader) atomicAdd(&h[b], uint32_t(__popcll(same)));
-        todo &= ~same;
-    }
-    if ((todo >> lane_id()) & 1u) atomicAdd(&h[bin], 1u);
-}
-
 // S = the binary64 sum of the norm partials in k_norm_final's order: its
 // 256 threads are this block's first four waves, each summing a strided
 // share, then a butterfly per wave and the four wave sums in order.  The
