@@ -58,6 +58,8 @@ TRAFFIC = {
                  ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
     "sampled": (os.path.join(ROOT, "profiles", "sm_fused_flat1b_traffic.json"),
                 ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
+    "shared": (os.path.join(ROOT, "profiles", "sh_fused_flat1b_traffic.json"),
+               ("dgc_device.hpp", "kernel_fused.hpp", "kernels_shared.hpp")),
 }
 # the other workloads measured after the headline: (name, timed steps)
 OTHER_WORKLOADS = (("flat1m", 200), ("resnet50", 50), ("deepspeech", 20),
