@@ -32,6 +32,8 @@ from .c_oracle import (  # noqa: F401
     fmix32,
     sampled_select_mask,
     sampled_step,
+    hier_select_mask,
+    hier_step,
     shared_gather_mask,
     shared_step,
     shared_sum,

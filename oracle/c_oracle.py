@@ -79,6 +79,11 @@ def load():
                                      ctypes.c_float, ctypes.c_double, P, P, P,
                                      P, P, P, P]
     lib.orc_sampled_step.restype = ctypes.c_int
+    lib.orc_hier_select_mask.argtypes = [P, P, i64, i64, ctypes.c_int32, P, P, P, P]
+    lib.orc_hier_select_mask.restype = i64
+    lib.orc_hier_step.argtypes = [ctypes.c_int32, P, P, P, P, P, ctypes.c_float,
+                                  ctypes.c_double, P, P, P, P, P, P, P]
+    lib.orc_hier_step.restype = ctypes.c_int
     lib.orc_shared_gather_mask.argtypes = [P, P, i64, P, i64, P]
     lib.orc_shared_gather_mask.restype = i64
     lib.orc_shared_step.argtypes = [ctypes.c_int32, P, P, P, P, P, P,
@@ -285,6 +290,51 @@ def sampled_step(sizes, k, cap, g, u, v, m, clip):
     if rc != 0:
         raise ValueError("bad k or capacity")
     return idx[:C], val[:C], count, total, theta, float(norm[0]), np.float32(scale[0])
+
+
+def hier_select_mask(u, v, k, t=0):
+    """Hierarchical selection of one tensor (index t of its layout): the
+    sampled threshold, then an exact select of k among its survivors when
+    more than k pass; masking in place.  Returns (idx, val, total, theta)."""
+    assert u.size == v.size
+    k = int(k)
+    idx = np.zeros(max(k, 1), np.uint32)
+    val = np.zeros(max(k, 1), np.float32)
+    total = np.zeros(1, np.int64)
+    theta = np.zeros(1, np.uint32)
+    got = load().orc_hier_select_mask(
+        _ptr(u, np.float32), _ptr(v, np.float32), v.size, k, int(t),
+        _ptr(idx, np.uint32), _ptr(val, np.float32), _ptr(total, np.int64),
+        _ptr(theta, np.uint32))
+    if got < 0:
+        raise ValueError("bad k")
+    return idx[:got].copy(), val[:got].copy(), int(total[0]), int(theta[0])
+
+
+def hier_step(sizes, k, g, u, v, m, clip):
+    """One learner step with the hierarchical selector (in place on u, v).
+    Returns (idx, val, count, total, theta, norm, scale); idx/val have sum(k)
+    slots, tensor t's count[t] sent entries at offset sum(k[:t])."""
+    sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+    k = np.ascontiguousarray(k, dtype=np.int64)
+    K = int(k.sum())
+    idx = np.zeros(max(K, 1), np.uint32)
+    val = np.zeros(max(K, 1), np.float32)
+    T = len(sizes)
+    count = np.zeros(T, np.int64)
+    total = np.zeros(T, np.int64)
+    theta = np.zeros(T, np.uint32)
+    norm = np.zeros(1, np.float64)
+    scale = np.zeros(1, np.float32)
+    rc = load().orc_hier_step(
+        T, _ptr(sizes, np.int64), _ptr(k, np.int64), _ptr(g, np.float32),
+        _ptr(u, np.float32), _ptr(v, np.float32), float(np.float32(m)), float(clip),
+        _ptr(idx, np.uint32), _ptr(val, np.float32), _ptr(count, np.int64),
+        _ptr(total, np.int64), _ptr(theta, np.uint32), _ptr(norm, np.float64),
+        _ptr(scale, np.float32))
+    if rc != 0:
+        raise ValueError("bad k")
+    return idx[:K], val[:K], count, total, theta, float(norm[0]), np.float32(scale[0])
 
 
 def shared_gather_mask(u, v, idx):

@@ -40,6 +40,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <vector>
+#include <utility>
 
 #ifdef _OPENMP
 #include <omp.h>
@@ -246,6 +247,31 @@ static uint32_t fmix32(uint32_t h) {
 extern "C" uint32_t orc_fmix32(uint32_t h) { return fmix32(h); }
 
 /*
+ * The sampled threshold theta of one tensor (the first level of the sampled
+ * and hierarchical selectors below): the J-th largest key of the sampled
+ * lines, J = ceil(S*k/n), S the number of sampled elements; the lines are
+ * placed as described for orc_sampled_select_mask.  Needs 1 <= k <= n.
+ */
+static uint32_t sampled_threshold(const float* v, int64_t n, int64_t k, int32_t t) {
+    const int64_t lines = (n + 31) / 32;
+    const int64_t ls = n <= 65536 ? lines
+                                  : std::min<int64_t>(lines, std::max<int64_t>(512, lines / 256));
+    const int64_t stride = lines / ls;
+    std::vector<uint32_t> sample;
+    for (int64_t j = 0; j < ls; ++j) {
+        const uint32_t r = fmix32((uint32_t)j * 0x9E3779B9u ^ (uint32_t)t * 0x7F4A7C15u);
+        const int64_t line = j * stride + (int64_t)(r % (uint64_t)stride);
+        for (int64_t e = line * 32; e < std::min(n, line * 32 + 32); ++e)
+            sample.push_back(magnitude_key(v[e]));
+    }
+    const int64_t S = (int64_t)sample.size();
+    const int64_t J = (S * k + n - 1) / n;
+    std::nth_element(sample.begin(), sample.begin() + (J - 1), sample.end(),
+                     [](uint32_t a, uint32_t b) { return a > b; });
+    return sample[(size_t)(J - 1)];
+}
+
+/*
  * Sampled-threshold selection of one tensor (tensor index t in its layout),
  * then momentum factor masking.
  *
@@ -277,22 +303,7 @@ int64_t orc_sampled_select_mask(float* u, float* v, int64_t n, int64_t k,
     *total = 0;
     *theta = 0xFFFFFFFFu;
     if (k == 0) return 0;
-    const int64_t lines = (n + 31) / 32;
-    const int64_t ls = n <= 65536 ? lines
-                                  : std::min<int64_t>(lines, std::max<int64_t>(512, lines / 256));
-    const int64_t stride = lines / ls;
-    std::vector<uint32_t> sample;
-    for (int64_t j = 0; j < ls; ++j) {
-        const uint32_t r = fmix32((uint32_t)j * 0x9E3779B9u ^ (uint32_t)t * 0x7F4A7C15u);
-        const int64_t line = j * stride + (int64_t)(r % (uint64_t)stride);
-        for (int64_t e = line * 32; e < std::min(n, line * 32 + 32); ++e)
-            sample.push_back(magnitude_key(v[e]));
-    }
-    const int64_t S = (int64_t)sample.size();
-    const int64_t J = (S * k + n - 1) / n;
-    std::nth_element(sample.begin(), sample.begin() + (J - 1), sample.end(),
-                     [](uint32_t a, uint32_t b) { return a > b; });
-    const uint32_t th = sample[(size_t)(J - 1)];
+    const uint32_t th = sampled_threshold(v, n, k, t);
     *theta = th;
     int64_t sent = 0, out = 0;
     for (int64_t i = 0; i < n; ++i) {
@@ -310,6 +321,68 @@ int64_t orc_sampled_select_mask(float* u, float* v, int64_t n, int64_t k,
         v[idx[j]] = 0.0f;
     }
     *total = sent;
+    return out;
+}
+
+/*
+ * Hierarchical thresholding of one tensor (tensor index t in its layout):
+ * the sampled threshold as the first level, an exact select among what
+ * passes it as the second, then momentum factor masking.
+ *
+ * Source: the DGC review, "Research questions" (RQ4 names hierarchical
+ * thresholding as a runtime strategy for scalable selection) and "Proposed
+ * method" (only large entries are sent).  The page names the strategy only;
+ * the reading taken puts two levels on the sampled threshold:
+ *   level 1  theta from the sample (sampled_threshold); the survivors are
+ *            the non-zero entries with key(v_i) >= theta
+ *   level 2  more than k survivors: the k of them that come first under
+ *            (key descending, index ascending), the DGC rule; at most k
+ *            survivors: all of them
+ *   sent     in index order; u = v = +0.0f there, the rest untouched
+ * so the count is min(k, survivors), never more than k.  k = 0 sends
+ * nothing.
+ *
+ * Writes the sent indices / values (v before masking, at most k of them),
+ * the survivor count into *total and theta into *theta (0xFFFFFFFF for
+ * k = 0).  Returns the number sent, or -1 for a k outside [0, n].
+ */
+int64_t orc_hier_select_mask(float* u, float* v, int64_t n, int64_t k, int32_t t,
+                             uint32_t* idx, float* val, int64_t* total,
+                             uint32_t* theta) {
+    if (k < 0 || k > n) return -1;
+    *total = 0;
+    *theta = 0xFFFFFFFFu;
+    if (k == 0) return 0;
+    const uint32_t th = sampled_threshold(v, n, k, t);
+    *theta = th;
+    // level 1: (key, index) of every survivor
+    std::vector<std::pair<uint32_t, uint32_t>> surv;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t key = magnitude_key(v[i]);
+        if (key != 0 && key >= th) surv.push_back({key, (uint32_t)i});
+    }
+    *total = (int64_t)surv.size();
+    // level 2: the first k under (key descending, index ascending)
+    if ((int64_t)surv.size() > k) {
+        std::sort(surv.begin(), surv.end(),
+                  [](const std::pair<uint32_t, uint32_t>& a,
+                     const std::pair<uint32_t, uint32_t>& b) {
+                      return a.first != b.first ? a.first > b.first : a.second < b.second;
+                  });
+        surv.resize((size_t)k);
+    }
+    std::vector<uint32_t> sel;
+    for (const auto& s : surv) sel.push_back(s.second);
+    std::sort(sel.begin(), sel.end());
+    const int64_t out = (int64_t)sel.size();
+    for (int64_t j = 0; j < out; ++j) {
+        idx[j] = sel[(size_t)j];
+        val[j] = v[sel[(size_t)j]];
+    }
+    for (int64_t j = 0; j < out; ++j) {
+        u[idx[j]] = 0.0f;
+        v[idx[j]] = 0.0f;
+    }
     return out;
 }
 
@@ -459,6 +532,36 @@ int orc_sampled_step(int32_t T, const int64_t* sizes, const int64_t* k,
         count[t] = orc_sampled_select_mask(
             u + off[(size_t)t], v + off[(size_t)t], sizes[t], k[t], cap[t], t,
             idx + coff[(size_t)t], val + coff[(size_t)t], total + t, theta + t);
+    }
+    return 0;
+}
+
+/*
+ * One learner step with the hierarchical selector: clip and momentum as in
+ * orc_step, then per tensor orc_hier_select_mask with target k[t].  Tensor
+ * t's sent entries go to idx/val at offset k[0] + ... + k[t-1]; count[t] =
+ * number sent (min(k[t], total[t])), total[t] = survivors of the first
+ * level, theta[t] the threshold.  Returns 0, or -1 on a bad k.
+ */
+int orc_hier_step(int32_t T, const int64_t* sizes, const int64_t* k, const float* g,
+                  float* u, float* v, float m, double clip, uint32_t* idx, float* val,
+                  int64_t* count, int64_t* total, uint32_t* theta, double* norm_out,
+                  float* scale_out) {
+    int64_t n = 0;
+    for (int32_t t = 0; t < T; ++t) n += sizes[t];
+    std::vector<int64_t> off((size_t)T + 1, 0), koff((size_t)T + 1, 0);
+    for (int32_t t = 0; t < T; ++t) {
+        if (k[t] < 0 || k[t] > sizes[t]) return -1;
+        off[(size_t)t + 1] = off[(size_t)t] + sizes[t];
+        koff[(size_t)t + 1] = koff[(size_t)t] + k[t];
+    }
+    orc_clip_scale(g, n, clip, norm_out, scale_out);
+    orc_momentum(g, n, *scale_out, m, u, v);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        count[t] = orc_hier_select_mask(
+            u + off[(size_t)t], v + off[(size_t)t], sizes[t], k[t], t,
+            idx + koff[(size_t)t], val + koff[(size_t)t], total + t, theta + t);
     }
     return 0;
 }
