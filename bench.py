@@ -26,13 +26,16 @@ of exact top-k (dgc_compress_binlocal + dgc_encode_counts, bins of
 With --selector sampled it uses the sampled (approximate) threshold for the
 same k as top-k (dgc_compress_sampled + dgc_encode_counts, at most 4 k per
 tensor delivered) and reports how far the sent counts are from k.
+With --selector hier it uses hierarchical thresholding for the same k:
+the sampled threshold, then an exact select of k among its survivors when
+more than k pass (dgc_compress_hier + dgc_encode_counts, at most k sent).
 With --selector shared it uses shared-index compression (the ScaleComp
 reading): the leader (step mod W) runs dgc_compress + dgc_encode, the other
 learners dgc_compress_shared at its indices, and dgc_shared_sum adds the
 value vectors in learner order into the fresh dense sum.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat1b]
-                    [--selector topk|binlocal|sampled|shared] [--bin-len 512] [--cap-den 8]
+                    [--selector topk|binlocal|sampled|hier|shared] [--bin-len 512] [--cap-den 8]
 """
 
 import argparse
@@ -58,6 +61,8 @@ TRAFFIC = {
                  ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
     "sampled": (os.path.join(ROOT, "profiles", "sm_fused_flat1b_traffic.json"),
                 ("dgc_device.hpp", "kernel_fused.hpp", "kernels_binlocal.hpp")),
+    "hier": (os.path.join(ROOT, "profiles", "hier_fused_flat1b_traffic.json"),
+             ("dgc_device.hpp", "kernel_fused.hpp")),
     "shared": (os.path.join(ROOT, "profiles", "sh_fused_flat1b_traffic.json"),
                ("dgc_device.hpp", "kernel_fused.hpp", "kernels_shared.hpp")),
 }
@@ -125,15 +130,13 @@ def parse():
     ap.add_argument("--pipeline", action="store_true",
                     help="run each learner on its own stream, starting once the "
                          "previous learner's element-wise pass is done")
-    ap.add_argument("--fused-only", action="store_true",
-                    help="time only dgc_compress calls (for profiling runs)")
     ap.add_argument("--select-grid", type=int, choices=(0, 1, 2), default=0,
                     help="DGC_OPT_SELECT_GRID for dgc_compress: 0 automatic, 1 a workgroup "
                          "per tensor, 2 the spread passes")
     ap.add_argument("--timers", choices=("fused", "off"), default="fused",
                     help="library timers in the timed region: the element-wise "
                          "pass only (default), or none (then roofline is null)")
-    ap.add_argument("--selector", choices=("topk", "binlocal", "sampled", "shared"),
+    ap.add_argument("--selector", choices=("topk", "binlocal", "sampled", "hier", "shared"),
                     default="topk",
                     help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, the "
                          "sampled threshold, or shared-index compression (ScaleComp)")
@@ -221,6 +224,45 @@ def cpu_baseline_sampled(wl, host_samples, n_chunks, seconds):
                    f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
                    "momentum, sampled threshold, mask, encode, decode; "
                    f"{dt:.1f} s"),
+    }
+
+
+def cpu_baseline_hier(wl, host_samples, n_chunks, seconds):
+    """As cpu_baseline, with the oracle's hierarchical selector."""
+    import oracle
+    sizes = np.array(wl.sizes[:n_chunks], np.int64)
+    d = wl.densities[0]
+    k = np.array([oracle.k_for_density(int(s), d.numerator, d.denominator) for s in sizes])
+    n = int(sizes.sum())
+    u = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dense = np.zeros(n, np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    koff = np.concatenate([[0], np.cumsum(k)])
+    t0 = time.perf_counter()
+    steps = 0
+    for cycle in range(4):
+        for g in host_samples:
+            idx, val, cnt, _, _, _, _ = oracle.hier_step(sizes, k, g, u, v, wl.momentum,
+                                                         wl.clip)
+            dense[:] = 0
+            for t in range(len(sizes)):
+                a = koff[t]
+                r, vv = oracle.encode(idx[a:a + cnt[t]], val[a:a + cnt[t]])
+                oracle.decode_accumulate(r, vv, dense[offs[t]:offs[t + 1]])
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * steps / dt / 1e9, 4),
+        "unit": "G elem/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"learner 0, {steps} steps, first {n_chunks} of "
+                   f"{len(wl.sizes)} tensors ({n} elements): clip over the sample, "
+                   "momentum, sampled threshold, exact select among its survivors, "
+                   f"mask, encode, decode; {dt:.1f} s"),
     }
 
 
@@ -359,6 +401,7 @@ class Run:
         self.T = T
         self.binlocal = selector == "binlocal"
         self.sampled = selector == "sampled"
+        self.hier = selector == "hier"
         self.shared = selector == "shared"
         if self.binlocal:
             self.bins = [args.bin_len] * T
@@ -431,14 +474,18 @@ class Run:
             Ld = learners[lead]
             K = int(sum(k))
             Ld.compress(self.grads[(lead, t)], k, self.wl.clip)
-            if not args.fused_only:
-                Ld.encode(k)
+            Ld.encode(k)
             for w, L in enumerate(learners):
                 if w != lead:
                     L.compress_shared(self.grads[(w, t)], k, Ld.idx[:K], self.wl.clip)
-            if not args.fused_only:
-                dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, Ld.idx[:K],
-                               self.out_sum, self.dense)
+            dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, Ld.idx[:K],
+                           self.out_sum, self.dense)
+            return
+        if self.hier:
+            for w, L in enumerate(learners):
+                L.compress_hier(self.grads[(w, t)], k, self.wl.clip)
+                L.encode_counts(k)
+            dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         if self.binlocal or self.sampled:
             step_caps = self.caps if self.binlocal else self.caps_by_step[t % len(self.ks)]
@@ -448,18 +495,14 @@ class Run:
                                         self.wl.clip)
                 else:
                     L.compress_sampled(self.grads[(w, t)], k, step_caps, self.wl.clip)
-                if not args.fused_only:
-                    L.encode_counts(step_caps)
-            if not args.fused_only:
-                dgc.decode_sum(learners[0], streams_of(), self.dense)
+                L.encode_counts(step_caps)
+            dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         if not self.pipeline:
             for w, L in enumerate(learners):
                 L.compress(self.grads[(w, t)], k, self.wl.clip)
-                if not args.fused_only:
-                    L.encode(k)
-            if not args.fused_only:
-                dgc.decode_sum(learners[0], streams_of(), self.dense)
+                L.encode(k)
+            dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         import torch
         for w, L in enumerate(learners):
@@ -470,12 +513,10 @@ class Run:
                 st.wait_event(self.fused_ev[w - 1])
             with torch.cuda.stream(st):
                 L.compress(self.grads[(w, t)], k, self.wl.clip, stream=st)
-                if not args.fused_only:
-                    L.encode(k, stream=st)
+                L.encode(k, stream=st)
         for st in self.streams:
             self.main.wait_stream(st)
-        if not args.fused_only:
-            dgc.decode_sum(learners[0], streams_of(), self.dense, stream=self.main)
+        dgc.decode_sum(learners[0], streams_of(), self.dense, stream=self.main)
 
     def set_timing(self, mode):
         for L in self.learners:
@@ -680,6 +721,8 @@ def main():
         pipeline_bytes = compress_alg_bytes(wl, ks[0])
         kernel_name = ("k_fused (clip-scale + momentum correction + accumulation + "
                        "candidate output)")
+        if run.hier:
+            kernel_name = kernel_name[:-1] + ": the first level's survivors)"
     roofline = None
     if fused_ms:
         achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
@@ -766,6 +809,25 @@ def main():
                     "salient_fraction": round(salient / n, 5),
                     "delivered_per_learner": delivered,
                     "truncated_tensors": truncated})
+    elif run.hier:
+        klast = np.array(run.k_of_step(last))
+        info = np.concatenate([L.select_info() for L in learners])
+        kk = np.concatenate([klast] * len(learners))
+        sent = np.concatenate([L.count.cpu().numpy() for L in learners])
+        listed = info[:, 0] == 1
+        out["config"].update({
+            "k_per_tensor": int(klast[0]) if len(set(klast)) == 1 else "per tensor",
+            "density": str(wl.densities[0])})
+        det.update({
+            "sent_over_k_min_mean_max": [round(float(x), 4) for x in (
+                (sent / np.maximum(kk, 1)).min(), (sent / np.maximum(kk, 1)).mean(),
+                (sent / np.maximum(kk, 1)).max())],
+            "survivors_over_k_min_max": ([round(float((info[listed, 2] / kk[listed]).min()), 3),
+                                         round(float((info[listed, 2] / kk[listed]).max()), 3)]
+                                        if listed.any() else None),
+            "sources_list_whole_select_dense": [
+                int((listed & (info[:, 2] <= kk)).sum()), int((listed & (info[:, 2] > kk)).sum()),
+                int((info[:, 0] == 2).sum())]})
     elif run.shared:
         out["config"].update({
             "k_per_tensor": ks[0][0] if len(set(ks[0])) == 1 else "per tensor",
@@ -792,7 +854,7 @@ def main():
     run.close()
     del run
     if (not args.no_workloads and args.workload == "flat1b" and args.selector == "topk"
-            and not args.fused_only and not args.pipeline):
+            and not args.pipeline):
         det["workloads"] = []
         for name, steps in OTHER_WORKLOADS:
             log(f"workload {name}")
@@ -810,6 +872,9 @@ def main():
                 args.bin_len, args.cap_den)
         elif args.selector == "sampled":
             out["cpu_baseline"] = cpu_baseline_sampled(
+                wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds)
+        elif args.selector == "hier":
+            out["cpu_baseline"] = cpu_baseline_hier(
                 wl, host_samples, args.cpu_sample_chunks, args.cpu_seconds)
         elif args.selector == "shared":
             out["cpu_baseline"] = cpu_baseline_shared(

@@ -254,6 +254,44 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
                          double* out_norm, float* out_scale, hipStream_t stream);
 
 /*
+ * One learner step with hierarchical thresholding (DGC review, "Research
+ * questions": RQ4 names hierarchical thresholding as a runtime strategy for
+ * scalable selection; "Proposed method": only large entries are sent).  The
+ * page names the strategy only; the reading taken stacks two levels:
+ *   level 1  dgc_compress_sampled's threshold theta_t from the sampled
+ *            lines (the ceil(S k_t / n_t)-th largest sampled key); the
+ *            survivors are the non-zero entries with |v| key >= theta_t
+ *   level 2  more than k_t survivors: the k_t of them first under (key
+ *            descending, index ascending), the rule of dgc_compress; at
+ *            most k_t: all of them
+ * so a tensor sends E_t = min(k_t, survivors) entries, never more than k_t,
+ * and exactly dgc_compress's selection whenever at least k_t survive.
+ * Steps 1, 2 and 4 are dgc_compress's (clip, momentum, masking of the sent
+ * entries).  The survivors are the element-wise pass's candidates; the
+ * exact select then runs on them (or on the whole tensor under the floor
+ * max(theta_t, 1) when a piece's candidates overflow its slots).
+ * Arguments:
+ *   g, k, clip, out_norm, out_scale  as for dgc_compress (k host int64[T],
+ *              0 <= k[t] <= k_max[t])
+ *   out_idx    device uint32[sum k], 4-byte aligned: tensor t's sent local
+ *              indices, ascending, at offset K_t = k[0] + ... + k[t-1]; the
+ *              first out_count[t] slots are written, the rest untouched
+ *   out_val    device float[sum k], 4-byte aligned: their values (signed,
+ *              before masking), same slots
+ *   out_count  device int64[T], 8-byte aligned: E_t
+ * With DGC_OPT_SELECT_PATH 1 the survivors are not kept as candidates and
+ * the select always runs on the whole tensor (the same results, slower).
+ * dgc_get_select_info then reports as for dgc_compress ([1] is
+ * max(theta_t, 1), or 0xFFFFFFFF on the forced whole-tensor path; [2] the
+ * survivors; a whole list of at most k_t has T = 0 and r = 0).
+ * Deterministic; encode with dgc_encode_counts (cap = k).  Returns DGC_OK,
+ * DGC_EINVAL (also for a k above k_max) or DGC_EHIP.
+ */
+int dgc_compress_hier(dgc_state* st, const float* g, const int64_t* k, double clip,
+                      uint32_t* out_idx, float* out_val, int64_t* out_count,
+                      double* out_norm, float* out_scale, hipStream_t stream);
+
+/*
  * One step of a learner that sends at a shared index set: commutative
  * compression (the ScaleComp abstract on the taxoreview.com page: the
  * learners' gradient distributions are alike, which allows a compressor
@@ -442,8 +480,8 @@ int dgc_get_status(dgc_state* st);
 int dgc_get_path_counts(dgc_state* st, int64_t* n_window, int64_t* n_dense);
 
 /*
- * Per-tensor record of the last dgc_compress or dgc_compress_sampled (waits
- * for the stream):
+ * Per-tensor record of the last dgc_compress, dgc_compress_sampled or
+ * dgc_compress_hier (waits for the stream):
  * info (host int64[6 * n_tensors]) receives for each tensor
  *   [0] path: 0 = k was 0, 1 = sample window, 2 = dense exact path,
  *       3 = the sampled threshold of dgc_compress_sampled (then [1] and [4]

@@ -102,6 +102,14 @@ def _ptr(a, dtype):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _check_sizes(sizes, *arrays):
+    """Every dense array of a step holds the layout's n elements (the C
+    oracle reads that many)."""
+    n = int(np.sum(np.asarray(sizes, np.int64)))
+    for a in arrays:
+        assert a.size == n, (a.size, n)
+
+
 def num_threads():
     return int(load().orc_num_threads())
 
@@ -177,6 +185,7 @@ def step(sizes, k, g, u, v, m, clip):
     Returns (idx, val, norm, scale); idx/val hold every tensor's k entries
     back to back in tensor order, with local (per-tensor) indices.
     """
+    _check_sizes(sizes, g, u, v)
     sizes = np.ascontiguousarray(sizes, dtype=np.int64)
     k = np.ascontiguousarray(k, dtype=np.int64)
     K = int(k.sum())
@@ -221,6 +230,7 @@ def binlocal_step(sizes, L, cap, g, u, v, m, clip):
     slots; tensor t's delivered entries sit at offset sum(cap[:t]) and only
     the first count[t] of its cap[t] slots are written.
     """
+    _check_sizes(sizes, g, u, v)
     sizes = np.ascontiguousarray(sizes, dtype=np.int64)
     L = np.ascontiguousarray(L, dtype=np.int64)
     cap = np.ascontiguousarray(cap, dtype=np.int64)
@@ -269,6 +279,7 @@ def sampled_step(sizes, k, cap, g, u, v, m, clip):
     """One learner step with the sampled-threshold selector (in place on u,
     v).  Returns (idx, val, count, total, theta, norm, scale); idx/val have
     sum(cap) slots, tensor t's delivered entries at offset sum(cap[:t])."""
+    _check_sizes(sizes, g, u, v)
     sizes = np.ascontiguousarray(sizes, dtype=np.int64)
     k = np.ascontiguousarray(k, dtype=np.int64)
     cap = np.ascontiguousarray(cap, dtype=np.int64)
@@ -315,6 +326,7 @@ def hier_step(sizes, k, g, u, v, m, clip):
     """One learner step with the hierarchical selector (in place on u, v).
     Returns (idx, val, count, total, theta, norm, scale); idx/val have sum(k)
     slots, tensor t's count[t] sent entries at offset sum(k[:t])."""
+    _check_sizes(sizes, g, u, v)
     sizes = np.ascontiguousarray(sizes, dtype=np.int64)
     k = np.ascontiguousarray(k, dtype=np.int64)
     K = int(k.sum())
@@ -356,6 +368,7 @@ def shared_step(sizes, k, idx, g, u, v, m, clip):
     """One step of a learner that takes the leader's index set idx (every
     tensor's k[t] local indices back to back, as step() writes them); in
     place on u, v.  Returns (val, norm, scale)."""
+    _check_sizes(sizes, g, u, v)
     sizes = np.ascontiguousarray(sizes, dtype=np.int64)
     k = np.ascontiguousarray(k, dtype=np.int64)
     idx = np.ascontiguousarray(idx, dtype=np.uint32)

@@ -841,6 +841,72 @@ int dgc_init_state(dgc_state** out, int32_t n_tensors, const int64_t* sizes,
     return DGC_OK;
 }
 
+// The select and emit after the element-wise pass on the spread path:
+// candidate totals and sources, the gather, then either one workgroup per
+// tensor (every selection source short) or passes spread over the chip.
+// With out_count set, each tensor's sent count is written too (zeros when
+// every k is 0).
+static int enqueue_select(dgc_state* st, int64_t K, uint32_t* out_idx, float* out_val,
+                   int64_t* out_count, hipStream_t stream) {
+    const Plan& p = st->plan;
+    const int T = p.T;
+    const int pg = st->num_cus * 8;  // persistent grids
+    if (p.G > 0)
+        k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
+    k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
+                                           st->atiles);
+    // the select and emit: one workgroup per tensor when every selection
+    // source is short, else passes spread over the chip
+    const bool per_tensor = st->select_grid == 1 || (st->select_grid == 0 && p.short_sources);
+    // for the spread passes the gather also histograms the lists' top 21
+    // bits, which k_resolve21 turns into T's top 21 bits where it can
+    if (p.G > 0)
+        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
+                                                  st->run_cnt, st->goff, st->olist_i,
+                                                  st->olist_v, st->olist_u, st->u, st->v,
+                                                  per_tensor ? nullptr : st->hist);
+    if (K > 0 && per_tensor) {
+        k_select_tensor<<<T, kTsThreads, 0, stream>>>(
+            st->L, st->K, st->ts, st->u, st->v, st->olist_i, st->olist_v, st->olist_u,
+            out_idx, out_val, out_count, st->sc);
+        DGC_LAUNCH_CHECK();
+    } else if (K > 0) {
+        k_resolve21<<<T, kBlock, 0, stream>>>(st->ts, st->hist);
+        k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
+        k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
+        DGC_LAUNCH_CHECK();
+        const int hg = grid_for(p.TT, pg);
+        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
+                                             st->aoff, st->hist);
+        k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
+        DGC_LAUNCH_CHECK();
+        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v,
+                                                st->amap, st->aoff, st->ta);
+        if (p.staged_tiles)
+            k_emit_scan<true><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc,
+                                                        st->ts, out_count);
+        else
+            k_emit_scan<false><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc,
+                                                         st->ts, out_count);
+        k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
+                                                st->olist_i, st->olist_v, st->olist_u, st->amap,
+                                                st->aoff, st->tb, st->tc, out_idx,
+                                                out_val, st->sc);
+        DGC_LAUNCH_CHECK();
+    }
+    if (K == 0 && out_count)
+        k_fill_u32<<<grid_for(cdiv(2 * int64_t(T), kBlock), 64), kBlock, 0, stream>>>(
+            reinterpret_cast<uint32_t*>(out_count), 2 * int64_t(T), 0u);
+    DGC_LAUNCH_CHECK();
+    return DGC_OK;
+}
+
 int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
                  uint32_t* out_idx, float* out_val, double* out_norm,
                  float* out_scale, hipStream_t stream) {
@@ -859,7 +925,6 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     st->last_stream = stream;
     const int T = p.T;
     const bool clip_on = clip > 0.0;
-    const int pg = st->num_cus * 8;  // persistent grids
 
     DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
     const int force_dense = st->select_path == 1;
@@ -884,7 +949,7 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
             return DGC_EHIP;
         k_finish_tensor<<<T, kTsThreads, 0, stream>>>(
             st->L, st->K, st->ts, st->slots, st->run_cnt, st->u, st->v, st->olist_i,
-            st->olist_v, st->olist_u, out_idx, out_val, st->sc);
+            st->olist_v, st->olist_u, out_idx, out_val, nullptr, st->sc);
         DGC_LAUNCH_CHECK();
         DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
         return DGC_OK;
@@ -920,53 +985,7 @@ int dgc_compress(dgc_state* st, const float* g, const int64_t* k, double clip,
     }
     if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
         return DGC_EHIP;
-    if (p.G > 0)
-        k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
-    k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
-                                           st->atiles);
-    // the select and emit: one workgroup per tensor when every selection
-    // source is short, else passes spread over the chip
-    const bool per_tensor = st->select_grid == 1 || (st->select_grid == 0 && p.short_sources);
-    // for the spread passes the gather also histograms the lists' top 21
-    // bits, which k_resolve21 turns into T's top 21 bits where it can
-    if (p.G > 0)
-        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
-                                                  st->run_cnt, st->goff, st->olist_i,
-                                                  st->olist_v, st->olist_u, st->u, st->v,
-                                                  per_tensor ? nullptr : st->hist);
-    if (K > 0 && per_tensor) {
-        k_select_tensor<<<T, kTsThreads, 0, stream>>>(
-            st->L, st->K, st->ts, st->u, st->v, st->olist_i, st->olist_v, st->olist_u,
-            out_idx, out_val, st->sc);
-        DGC_LAUNCH_CHECK();
-    } else if (K > 0) {
-        k_resolve21<<<T, kBlock, 0, stream>>>(st->ts, st->hist);
-        k_active_scan<<<1, kBlock, 0, stream>>>(T, st->atiles, st->aoff);
-        k_active_map<<<T, kBlock, 0, stream>>>(st->atiles, st->aoff, st->amap);
-        DGC_LAUNCH_CHECK();
-        const int hg = grid_for(p.TT, pg);
-        k_hist<0><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
-                                             st->aoff, st->hist);
-        k_resolve<0><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<1><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
-                                             st->aoff, st->hist);
-        k_resolve<1><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        k_hist<2><<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v, st->amap,
-                                             st->aoff, st->hist);
-        k_resolve<2><<<T, kBlock, 0, stream>>>(st->ts, st->hist, st->sc);
-        DGC_LAUNCH_CHECK();
-        k_emit_count<<<hg, kBlock, 0, stream>>>(st->L, st->ts, st->v, st->olist_v,
-                                                st->amap, st->aoff, st->ta);
-        if (p.staged_tiles)
-            k_emit_scan<true><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
-        else
-            k_emit_scan<false><<<T, kBlock, 0, stream>>>(st->aoff, st->ta, st->tb, st->tc);
-        k_emit_write<<<hg, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->u, st->v,
-                                                st->olist_i, st->olist_v, st->olist_u, st->amap,
-                                                st->aoff, st->tb, st->tc, out_idx,
-                                                out_val, st->sc);
-        DGC_LAUNCH_CHECK();
-    }
+    DGC_TRY(enqueue_select(st, K, out_idx, out_val, nullptr, stream));
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
     return DGC_OK;
 }
@@ -1084,15 +1103,15 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
     if (AS > 0)
         k_sm_hist<0><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
                                                 clip_on, st->ts, st->m, st->shist);
-    k_sm_pick<0><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    k_sm_pick<0><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts, 0);
     if (AS > 0)
         k_sm_hist<1><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
                                                 clip_on, st->ts, st->m, st->shist);
-    k_sm_pick<1><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    k_sm_pick<1><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts, 0);
     if (AS > 0)
         k_sm_hist<2><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
                                                 clip_on, st->ts, st->m, st->shist);
-    k_sm_pick<2><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts);
+    k_sm_pick<2><<<T, kBlock, 0, stream>>>(st->L, ktgt, st->shist, st->ts, 0);
     DGC_LAUNCH_CHECK();
     const int64_t wb = cdiv(st->BP, kWavesPerBlock);  // one piece per wave
     if (st->BP > 0) {
@@ -1116,6 +1135,76 @@ int dgc_compress_sampled(dgc_state* st, const float* g, const int64_t* k,
             st->slots, st->BP, out_idx, out_val);
     }
     DGC_LAUNCH_CHECK();
+    DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
+    return DGC_OK;
+}
+
+int dgc_compress_hier(dgc_state* st, const float* g, const int64_t* k, double clip,
+                      uint32_t* out_idx, float* out_val, int64_t* out_count,
+                      double* out_norm, float* out_scale, hipStream_t stream) {
+    if (!st) return DGC_EINVAL;
+    const Plan& p = st->plan;
+    int rc = check_k(st, k);
+    if (rc != DGC_OK) return rc;
+    int64_t K = 0;
+    for (int32_t t = 0; t < p.T; ++t) K += k[t];
+    if (p.n > 0 && (!g || !aligned(g, 16))) return DGC_EINVAL;
+    if (K > 0 && (!out_idx || !out_val || !aligned(out_idx, 4) || !aligned(out_val, 4)))
+        return DGC_EINVAL;
+    if (!out_count || !aligned(out_count, 8)) return DGC_EINVAL;
+    if (std::isnan(clip)) return DGC_EINVAL;
+    rc = upload_k(st, k, stream);
+    if (rc != DGC_OK) return rc;
+    st->last_stream = stream;
+    const int T = p.T;
+    const bool clip_on = clip > 0.0;
+    // 2: the forced whole-tensor path (no candidates, the floor still set)
+    const int hier = st->select_path == 1 ? 2 : 1;
+
+    DGC_TRY(timer_begin(st, DGC_TIMER_COMPRESS, stream));
+    if (clip_on) {
+        k_norm_partial<<<grid_for(p.NB, p.NB), kBlock, 0, stream>>>(g, p.n, p.norm_chunk,
+                                                                   st->partial);
+        k_norm_final<<<1, kBlock, 0, stream>>>(st->partial, p.NB, clip, st->sc,
+                                               out_norm, out_scale);
+    } else if (p.P == 0) {
+        k_set_scalars<<<1, 64, 0, stream>>>(st->sc, out_norm, out_scale);
+    }
+    // level 1: the sampled threshold, three histogram levels over the sample
+    const int AS = int(p.AS);
+    if (AS > 0)
+        k_sm_hist<0><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<0><<<T, kBlock, 0, stream>>>(st->L, st->K.k, st->shist, st->ts, hier);
+    if (AS > 0)
+        k_sm_hist<1><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<1><<<T, kBlock, 0, stream>>>(st->L, st->K.k, st->shist, st->ts, hier);
+    if (AS > 0)
+        k_sm_hist<2><<<AS, kBlock, 0, stream>>>(g, st->u, st->v, st->L, st->A, st->sc,
+                                                clip_on, st->ts, st->m, st->shist);
+    k_sm_pick<2><<<T, kBlock, 0, stream>>>(st->L, st->K.k, st->shist, st->ts, hier);
+    DGC_LAUNCH_CHECK();
+    // the element-wise pass: the survivors are the candidates
+    if (p.P > 0) {
+        int64_t fb = st->fused_blocks > 0 ? st->fused_blocks : cdiv(p.P, kWavesPerBlock);
+        DGC_TRY(timer_begin(st, DGC_TIMER_FUSED, stream));
+        k_fused<<<grid_for(cdiv(p.P, kWavesPerBlock), fb), kBlock, 0, stream>>>(
+            g, st->u, st->v, st->L, st->ts, st->sc, clip_on, st->m, st->slots,
+            st->run_cnt, p.P, out_norm, out_scale);
+        DGC_TRY(timer_end(st, DGC_TIMER_FUSED, stream));
+    }
+    if (st->fused_event && hipEventRecord(st->fused_event, stream) != hipSuccess)
+        return DGC_EHIP;
+    // level 2: the exact select of k among them, or all of at most k
+    if (p.tensor_path && st->select_grid != 2) {
+        k_finish_tensor<<<T, kTsThreads, 0, stream>>>(
+            st->L, st->K, st->ts, st->slots, st->run_cnt, st->u, st->v, st->olist_i,
+            st->olist_v, st->olist_u, out_idx, out_val, out_count, st->sc);
+        DGC_LAUNCH_CHECK();
+    } else {
+        DGC_TRY(enqueue_select(st, K, out_idx, out_val, out_count, stream));
+    }
     DGC_TRY(timer_end(st, DGC_TIMER_COMPRESS, stream));
     return DGC_OK;
 }

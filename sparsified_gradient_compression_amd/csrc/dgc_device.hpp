@@ -78,10 +78,19 @@ struct TensorState {
     uint32_t wbin;      // sample window: chosen top-11-bit bin (or kNoKey)
     uint32_t wabove;    // sample window: samples above wbin
     uint32_t wj;        // sample window: rank j of the targeted sample
-    uint32_t done21;    // the top 21 bits of T were found from the gather's
-                        // histogram (the first two digit passes skip it)
-    uint32_t pad[3];
+    uint32_t done21;    // kDone21: the top 21 bits of T were found from the
+                        // gather's histogram (the first two digit passes
+                        // skip it); kDoneAll: T and r are final (no digit
+                        // pass)
+    uint32_t floor;     // hierarchical selector: the survivors' least key,
+                        // max(theta, 1); keys below it count as 0 in the
+                        // select.  0 for exact top-k
+    uint32_t pad[2];
 };
+
+// TensorState::done21
+constexpr uint32_t kDone21 = 1;
+constexpr uint32_t kDoneAll = 2;
 
 // Per-call scalars.
 struct Scalars {
@@ -141,6 +150,13 @@ struct DevK {
 
 __device__ __forceinline__ uint32_t mag_key(float x) {
     return __float_as_uint(x) & 0x7FFFFFFFu;
+}
+
+// The key the select ranks under the hierarchical selector's floor: keys
+// below it (not survivors of the first level) count as 0.  The identity for
+// floor 0.
+__device__ __forceinline__ uint32_t floor_key(uint32_t key, uint32_t floor) {
+    return key >= floor ? key : 0u;
 }
 
 // u <- fl(fl(m*u) + fl(g*s)); v <- fl(v + u).  Each operation rounds once

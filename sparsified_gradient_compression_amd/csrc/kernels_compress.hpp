@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kBlock) void k_window(
         if (threadIdx.x == 0) {
             ts[t].lo_key = kNoKey;
             ts[t].wbin = kNoKey;
+            ts[t].floor = 0;  // exact top-k
         }
         __syncthreads();
         if (k <= 0 || force_dense || L.slines[t] == 0) return;
@@ -350,6 +351,25 @@ __global__ __launch_bounds__(kBlock) void k_group_sum(
     if (threadIdx.x == 0) gsum[g] = tot | (over ? 0x80000000u : 0u);
 }
 
+// The selection source of a tensor with C candidates (over: a piece ran
+// out of slots; cap: the list's capacity).  Exact top-k (floor 0): the
+// list when it is whole and holds k to cap items, else the whole tensor.
+// Hierarchical selector (floor > 0): the candidates are the first level's
+// survivors when the window edge is the floor; a whole list of at most k
+// of them is sent as it is (send_all), a longer one is selected from, and
+// otherwise the whole tensor is selected from under floor_key.
+__device__ __forceinline__ uint32_t select_mode(int64_t k, uint32_t C, int over, uint64_t cap,
+                                                uint32_t lo_key, uint32_t floor) {
+    if (k <= 0) return kModeSkip;
+    if (over || uint64_t(C) > cap) return kModeDense;
+    if (floor != 0 && lo_key == floor) return kModeList;
+    return int64_t(C) < k ? kModeDense : kModeList;
+}
+
+__device__ __forceinline__ bool send_all(int64_t k, uint32_t C, uint32_t floor) {
+    return floor != 0 && int64_t(C) <= k;
+}
+
 // One block per tensor: scan its groups' counts (their offsets in the
 // ordered list), then choose the selection source: the candidate list when
 // no piece overflowed and there are at least k candidates, else the whole
@@ -391,10 +411,10 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
     }
     over = __syncthreads_or(over);
     const uint64_t cap = uint64_t(L.obase[t + 1] - L.obase[t]);
-    uint32_t mode;
-    if (k <= 0) mode = kModeSkip;
-    else if (over || uint64_t(carry) > cap || int64_t(carry) < k) mode = kModeDense;
-    else mode = kModeList;
+    const uint32_t mode = select_mode(k, carry, over, cap, ts[t].lo_key, ts[t].floor);
+    // the hierarchical selector's complete survivor list of at most k: all
+    // of it is sent (T = 0, r = 0, no digit pass)
+    const bool all = mode == kModeList && send_all(k, carry, ts[t].floor);
     const int64_t len = mode == kModeList ? int64_t(carry) : nt;
     if (threadIdx.x == 0) {
         ts[t].total = carry;
@@ -402,8 +422,8 @@ __global__ __launch_bounds__(kBlock) void k_group_scan(
         ts[t].mode = mode;
         ts[t].len = uint32_t(len);
         ts[t].prefix = 0;
-        ts[t].krem = uint32_t(k > 0 ? k : 0);
-        ts[t].done21 = 0;
+        ts[t].krem = all ? 0u : uint32_t(k > 0 ? k : 0);
+        ts[t].done21 = all ? kDoneAll : 0u;
         atiles[t] = mode == kModeSkip ? 0u : uint32_t((len + kTile - 1) >> kTileShift);
     }
 }
@@ -455,6 +475,8 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     const int64_t g = blockIdx.x;
     const int t = int(L.gmap[g]);
     const bool list = ts[t].mode == kModeList;  // uniform
+    // the list's top-21-bit histogram, unless nothing is left to select
+    const bool hist21 = list && hist && ts[t].done21 == 0;
     const uint32_t lo21 = ts[t].lo_key >> 10;
     for (int b = threadIdx.x; b < kHistBins; b += kBlock) h21[b] = 0;
     const int64_t p0 = L.pbase[t] + (g - L.gbase[t]) * kGroup;
@@ -512,14 +534,14 @@ __global__ __launch_bounds__(kBlock) void k_gather(
             if (q < tot) put(it[b], q);
             // the list's keys by their top 21 bits above the window edge
             // (every candidate is at least lo); bin 2047 takes the rest
-            if (list && hist) {  // uniform
+            if (hist21) {  // uniform
                 const uint32_t d = (mag_key(it[b].v) >> 10) - lo21;
                 hist_inc(h21, d < uint32_t(kHistBins - 1) ? d : uint32_t(kHistBins - 1),
                          q < tot);
             }
         }
     }
-    if (list && hist) {  // uniform: add the group's counts to the tensor's row
+    if (hist21) {  // uniform: add the group's counts to the tensor's row
         __syncthreads();
         uint32_t* row = hist + int64_t(t) * kHistBins;
         for (int b = threadIdx.x; b < kHistBins; b += kBlock)
@@ -538,6 +560,7 @@ __global__ __launch_bounds__(kBlock) void k_resolve21(TensorState* __restrict__ 
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t pick[2];
     const int t = blockIdx.x;
+    if (ts[t].done21 == kDoneAll) return;  // uniform: sent whole, row untouched
     if (ts[t].mode != kModeList) {  // uniform
         if (threadIdx.x == 0) ts[t].done21 = 0;
         return;
@@ -573,7 +596,7 @@ __global__ __launch_bounds__(kBlock) void k_resolve21(TensorState* __restrict__ 
         } else {
             ts[t].prefix = lo21 + b;
             ts[t].krem = pick[1];
-            ts[t].done21 = 1;
+            ts[t].done21 = kDone21;
         }
     }
 }
@@ -673,7 +696,8 @@ __global__ __launch_bounds__(kBlock) void k_hist(
     __syncthreads();
     const uint32_t A = aoff[L.T];
     int cur_t = -1;
-    uint32_t ab = 0, ae = 0, prefix = 0;  // current tensor: active tiles [ab, ae)
+    // current tensor: active tiles [ab, ae)
+    uint32_t ab = 0, ae = 0, prefix = 0, fl = 0;
     int64_t len = 0;
     const float* src = v;
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
@@ -682,12 +706,14 @@ __global__ __launch_bounds__(kBlock) void k_hist(
             const uint32_t mode = ts[t].mode;
             len = ts[t].len;
             prefix = ts[t].prefix;
+            fl = ts[t].floor;
             ab = aoff[t];
             ae = aoff[t + 1];
             src = source_values(mode, v, olist_v, L, t);
             if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
             cur_t = t;
-            if (D < 2 && ts[t].done21) {  // uniform: resolved from the gather
+            // uniform: resolved from the gather (D < 2), or nothing to select
+            if (ts[t].done21 > (D < 2 ? 0u : kDone21)) {
                 // this workgroup's next tile at or past the tensor's end (the
                 // loop's step adds the last stride)
                 a += ((ae - a + gridDim.x - 1) / gridDim.x - 1) * gridDim.x;
@@ -702,12 +728,20 @@ __global__ __launch_bounds__(kBlock) void k_hist(
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             if (ib + q >= len) break;
-            const uint32_t key = mag_key(x[q]);
+            const uint32_t key = floor_key(mag_key(x[q]), fl);
             if (D == 0 || (key >> (shift + bits)) == prefix)
                 atomicAdd(&h[(key >> shift) & dmask], 1u);
         }
     }
     if (cur_t >= 0) flush_hist(h, hist + int64_t(cur_t) * kHistBins);
+}
+
+// r once the last digit is placed: under the hierarchical selector's floor
+// T = 0 means fewer than k survivors, which are then all sent (the keys at
+// 0 are not survivors), so r = 0.
+template <int D>
+__device__ __forceinline__ uint32_t last_rank(uint32_t T, uint32_t r, uint32_t floor) {
+    return (D == 2 && T == 0 && floor != 0) ? 0u : r;
 }
 
 // One block per tensor: find the bin of digit D holding the krem-th largest
@@ -724,7 +758,8 @@ __global__ __launch_bounds__(kBlock) void k_resolve(
     __shared__ int found;
     const int t = blockIdx.x;
     if (ts[t].mode == kModeSkip) return;
-    if (D < 2 && ts[t].done21) return;  // the gather's histogram resolved it
+    // the gather's histogram resolved it (D < 2), or nothing to select
+    if (ts[t].done21 > (D < 2 ? 0u : kDone21)) return;
     uint32_t* row = hist + int64_t(t) * kHistBins;
     uint32_t c[per];
     uint32_t mine = 0;
@@ -740,14 +775,16 @@ __global__ __launch_bounds__(kBlock) void k_resolve(
     for (int q = 0; q < per; ++q) row[bins - 1 - (threadIdx.x * per + q)] = 0;
     const uint32_t krem = ts[t].krem;
     const uint32_t prefix = ts[t].prefix;
+    const uint32_t fl = ts[t].floor;
     __syncthreads();  // every thread has read prefix/krem before the update
     uint32_t run = above;
 #pragma unroll
     for (int q = 0; q < per; ++q) {
         if (run < krem && krem <= run + c[q]) {
             uint32_t b = uint32_t(bins - 1 - (threadIdx.x * per + q));
-            ts[t].prefix = (prefix << Digit<D>::bits) | b;
-            ts[t].krem = krem - run;
+            const uint32_t np = (prefix << Digit<D>::bits) | b;
+            ts[t].prefix = np;
+            ts[t].krem = last_rank<D>(np, krem - run, fl);
             found = 1;
         }
         run += c[q];
@@ -769,7 +806,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
     uint32_t* __restrict__ tile_cnt) {
     __shared__ uint32_t lds[kWavesPerBlock];
     const uint32_t A = aoff[L.T];
-    uint32_t ab = 0, ae = 0, T = 0;  // current tensor: active tiles [ab, ae)
+    uint32_t ab = 0, ae = 0, T = 0, fl = 0;  // current tensor: active tiles [ab, ae)
     int64_t len = 0;
     const float* src = v;
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
@@ -778,6 +815,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
             const uint32_t mode = ts[t].mode;
             len = ts[t].len;
             T = ts[t].prefix;
+            fl = ts[t].floor;
             ab = aoff[t];
             ae = aoff[t + 1];
             src = source_values(mode, v, olist_v, L, t);
@@ -791,7 +829,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             if (ib + q < len) {
-                const uint32_t key = mag_key(x[q]);
+                const uint32_t key = floor_key(mag_key(x[q]), fl);
                 cnt += (key > T) ? (1u << 16) : (key == T ? 1u : 0u);
             }
         }
@@ -802,10 +840,13 @@ __global__ __launch_bounds__(kBlock) void k_emit_count(
 }
 
 // One block per tensor: exclusive scan of its tiles' (>T, ==T) counts.
+// With out_count set, also the tensor's sent count, #key > T + min(#key ==
+// T, r) (k_t for exact top-k).
 template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_emit_scan(
     const uint32_t* __restrict__ aoff, const uint32_t* __restrict__ tile_cnt,
-    uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq) {
+    uint32_t* __restrict__ off_gt, uint32_t* __restrict__ off_eq,
+    const TensorState* __restrict__ ts, int64_t* __restrict__ out_count) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t stage[kStaged ? kScanStage : 1];
     const int t = blockIdx.x;
@@ -840,6 +881,8 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
         cg += tg;
         ce += te;
     }
+    if (out_count && threadIdx.x == 0)
+        out_count[t] = ts[t].mode == kModeSkip ? 0 : int64_t(cg) + min(ce, ts[t].krem);
 }
 
 // Per active tile: write the selected items in index order.  An item with
@@ -862,7 +905,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     __shared__ float s_val[kTile];
     const uint32_t A = aoff[L.T];
     // current tensor: active tiles [ab, ae)
-    uint32_t ab = 0, ae = 0, T = 0, r = 0;
+    uint32_t ab = 0, ae = 0, T = 0, r = 0, fl = 0;
     int64_t len = 0, o = 0, kt = 0, nt = 0;
     bool dense = false;
     float* vt_ = v;
@@ -878,6 +921,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
             len = ts[t].len;
             T = ts[t].prefix;
             r = ts[t].krem;
+            fl = ts[t].floor;
             o = L.o[t];
             nt = L.o[t + 1] - o;
             vt_ = v + o;
@@ -914,7 +958,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             const bool ok = ib + q < len;
-            const uint32_t key = mag_key(val[q]);
+            const uint32_t key = floor_key(mag_key(val[q]), fl);
             gt[q] = ok && key > T;
             eq[q] = ok && key == T;
             c += (gt[q] ? (1u << 16) : 0u) + (eq[q] ? 1u : 0u);
@@ -993,6 +1037,18 @@ constexpr int kTsWaves = kTsThreads / kWave;
 constexpr int kTsHistUnroll = 8;  // keys loaded together per thread
 constexpr int kTsEmitUnroll = 4;  // 64-item rounds loaded together per wave
 
+// The tensor's sent count from the emit's per-wave counts (wcnt[w]: keys
+// > T of wave w, wcnt[kTsWaves + w]: keys == T): #key > T + min(#key == T,
+// r).
+__device__ __forceinline__ int64_t sent_count(const uint32_t* wcnt, uint32_t r) {
+    uint32_t g = 0, e = 0;
+    for (int j = 0; j < kTsWaves; ++j) {
+        g += wcnt[j];
+        e += wcnt[kTsWaves + j];
+    }
+    return int64_t(g) + min(e, r);
+}
+
 // Exclusive scan across the 1024-thread workgroup; `lds` holds kTsWaves
 // values.  Every thread must call it.
 __device__ __forceinline__ uint32_t ts_block_scan(uint32_t x, uint32_t* lds, uint32_t& total) {
@@ -1018,8 +1074,8 @@ __device__ __forceinline__ uint32_t ts_block_scan(uint32_t x, uint32_t* lds, uin
 // prefix and reduces krem.  Returns false (uniformly) if no bin holds it.
 template <int D>
 __device__ __forceinline__ bool ts_digit(const float* __restrict__ src, int64_t len,
-                                         uint32_t& prefix, uint32_t& krem, uint32_t* h,
-                                         uint32_t* lds, uint32_t* pick) {
+                                         uint32_t fl, uint32_t& prefix, uint32_t& krem,
+                                         uint32_t* h, uint32_t* lds, uint32_t* pick) {
     constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
     constexpr int bins = 1 << bits;
     constexpr uint32_t dmask = uint32_t(bins) - 1u;
@@ -1033,7 +1089,7 @@ __device__ __forceinline__ bool ts_digit(const float* __restrict__ src, int64_t 
 #pragma unroll
         for (int q = 0; q < kTsHistUnroll; ++q) {
             const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
-            key[q] = i < len ? mag_key(src[i]) : kNoKey;
+            key[q] = i < len ? floor_key(mag_key(src[i]), fl) : kNoKey;
         }
 #pragma unroll
         for (int q = 0; q < kTsHistUnroll; ++q)
@@ -1065,7 +1121,7 @@ __device__ __forceinline__ bool ts_digit(const float* __restrict__ src, int64_t 
     __syncthreads();  // every thread has read pick before the next digit
     if (b == kNoKey) return false;
     prefix = (prefix << bits) | b;
-    krem = kr;
+    krem = last_rank<D>(prefix, kr, fl);
     return true;
 }
 
@@ -1076,20 +1132,28 @@ __global__ __launch_bounds__(kTsThreads) void k_select_tensor(
     float* __restrict__ u, float* __restrict__ v,
     const uint32_t* __restrict__ olist_i, const float* __restrict__ olist_v,
     const float* __restrict__ olist_u, uint32_t* __restrict__ out_idx,
-    float* __restrict__ out_val, Scalars* __restrict__ sc) {
+    float* __restrict__ out_val, int64_t* __restrict__ out_count,
+    Scalars* __restrict__ sc) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t lds[kTsWaves];
     __shared__ uint32_t wcnt[2 * kTsWaves];
     __shared__ uint32_t pick[2];
     const int t = blockIdx.x;
     const uint32_t mode = ts[t].mode;
-    if (mode == kModeSkip) return;  // uniform
+    if (mode == kModeSkip) {  // uniform
+        if (out_count && threadIdx.x == 0) out_count[t] = 0;
+        return;
+    }
     const int64_t len = ts[t].len;
     const float* src = source_values(mode, v, olist_v, L, t);
+    const uint32_t fl = ts[t].floor;
     uint32_t prefix = ts[t].prefix, krem = ts[t].krem;
-    bool ok = ts_digit<0>(src, len, prefix, krem, h, lds, pick);
-    ok = ok && ts_digit<1>(src, len, prefix, krem, h, lds, pick);
-    ok = ok && ts_digit<2>(src, len, prefix, krem, h, lds, pick);
+    bool ok = true;
+    if (ts[t].done21 != kDoneAll) {  // uniform
+        ok = ts_digit<0>(src, len, fl, prefix, krem, h, lds, pick);
+        ok = ok && ts_digit<1>(src, len, fl, prefix, krem, h, lds, pick);
+        ok = ok && ts_digit<2>(src, len, fl, prefix, krem, h, lds, pick);
+    }
     if (!ok) {  // uniform
         if (threadIdx.x == 0) latch_error(sc, kErrInternal);
         return;
@@ -1114,7 +1178,7 @@ __global__ __launch_bounds__(kTsThreads) void k_select_tensor(
 #pragma unroll
         for (int q = 0; q < kTsEmitUnroll; ++q) {
             const int64_t i = b0 + int64_t(q) * kWave + lane;
-            key[q] = i < c1 ? mag_key(src[i]) : kNoKey;
+            key[q] = i < c1 ? floor_key(mag_key(src[i]), fl) : kNoKey;
         }
 #pragma unroll
         for (int q = 0; q < kTsEmitUnroll; ++q) {
@@ -1132,6 +1196,7 @@ __global__ __launch_bounds__(kTsThreads) void k_select_tensor(
         gb += wcnt[j];
         eb += wcnt[kTsWaves + j];
     }
+    if (out_count && threadIdx.x == 0) out_count[t] = sent_count(wcnt, r);
     const int64_t o = L.o[t];
     const int64_t nt = L.o[t + 1] - o;
     float* vt_ = v + o;
@@ -1160,7 +1225,7 @@ __global__ __launch_bounds__(kTsThreads) void k_select_tensor(
         }
 #pragma unroll
         for (int q = 0; q < kTsEmitUnroll; ++q) {
-            const uint32_t key = mag_key(val[q]);
+            const uint32_t key = floor_key(mag_key(val[q]), fl);
             const bool gt = in[q] && key > T, eq = in[q] && key == T;
             const uint64_t bg = __ballot(gt), be = __ballot(eq);
             const uint32_t g1 = gb + uint32_t(__popcll(bg & lt));

@@ -81,10 +81,16 @@ __global__ __launch_bounds__(kBlock) void k_sm_hist(
 //   ts.wabove level-1 prefix (top 21 bits)
 //   ts.wj     rank still sought inside the current bin
 //   ts.lo_key = ts.prefix = theta; ts.total = S; ts.krem = J
+// For the hierarchical selector (hier 1) the last level sets instead
+//   ts.floor = ts.lo_key = max(theta, 1)
+// so that the element-wise pass takes the first level's survivors (non-zero,
+// key >= theta) as candidates; with hier 2 (no candidates wanted: the
+// forced whole-tensor path) lo_key stays kNoKey.  Until then floor is
+// kNoKey (nothing survives), or 0 for the sampled selector (hier 0).
 template <int LEVEL>
 __global__ __launch_bounds__(kBlock) void k_sm_pick(
     DevLayout L, const int64_t* __restrict__ ktgt, uint32_t* __restrict__ shist,
-    TensorState* __restrict__ ts) {
+    TensorState* __restrict__ ts, int hier) {
     constexpr int bins = LEVEL == 0 ? kBins0 : 1024;
     constexpr int per = bins / kBlock;
     __shared__ uint32_t lds[kWavesPerBlock];
@@ -114,6 +120,7 @@ __global__ __launch_bounds__(kBlock) void k_sm_pick(
             ts[t].total = total;
             ts[t].krem = 0;
             ts[t].overflow = 0;
+            ts[t].floor = hier ? kNoKey : 0u;
         }
         __syncthreads();
         const int64_t k = ktgt[t];
@@ -135,7 +142,13 @@ __global__ __launch_bounds__(kBlock) void k_sm_pick(
                 ts[t].wabove = (wbin << 10) | b;
             } else {
                 const uint32_t theta = (wabove << 10) | b;
-                ts[t].lo_key = theta;
+                if (hier) {
+                    const uint32_t fl = theta > 0u ? theta : 1u;
+                    ts[t].floor = fl;
+                    ts[t].lo_key = hier == 1 ? fl : kNoKey;
+                } else {
+                    ts[t].lo_key = theta;
+                }
                 ts[t].prefix = theta;
             }
             ts[t].wj = rank - run;

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
         ts[t].wbin = kNoKey;
         ts[t].wabove = 0;
         ts[t].wj = 0;
+        ts[t].floor = 0;  // exact top-k
     }
     if (!active) return;  // uniform
     uint32_t key[kWtRounds][4];
@@ -362,7 +363,8 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     const uint32_t* __restrict__ run_cnt, float* __restrict__ u, float* __restrict__ v,
     uint32_t* __restrict__ olist_i, float* __restrict__ olist_v,
     float* __restrict__ olist_u, uint32_t* __restrict__ out_idx,
-    float* __restrict__ out_val, Scalars* __restrict__ sc) {
+    float* __restrict__ out_val, int64_t* __restrict__ out_count,
+    Scalars* __restrict__ sc) {
     __shared__ uint32_t sidx[kFinItems];
     __shared__ float sv[kFinItems];
     __shared__ float su[kFinItems];
@@ -379,6 +381,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     const uint32_t pcap = uint32_t(L.pcap[t]);
     const int64_t cap = L.obase[t + 1] - L.obase[t];
     const uint32_t lo_key = ts[t].lo_key;  // the window's lower edge
+    const uint32_t fl = ts[t].floor;       // 0, or the hierarchical floor
     if (np > int64_t(kFinRounds) * kTsThreads) {  // uniform; the host keeps such layouts off
         if (tid == 0) latch_error(sc, kErrInternal);
         return;
@@ -401,10 +404,9 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     over = __syncthreads_or(over);
     uint32_t C;
     ts_block_scan(mine, lds, C);
-    uint32_t mode;
-    if (k <= 0) mode = kModeSkip;
-    else if (over || int64_t(C) > cap || int64_t(C) < k) mode = kModeDense;
-    else mode = kModeList;
+    const uint32_t mode = select_mode(k, C, over, uint64_t(cap), lo_key, fl);
+    // the hierarchical selector's whole survivor list of at most k: all sent
+    const bool all = mode == kModeList && send_all(k, C, fl);
     const int64_t len = mode == kModeList ? int64_t(C) : nt;
     if (tid == 0) {
         ts[t].total = C;
@@ -412,9 +414,13 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
         ts[t].mode = mode;
         ts[t].len = uint32_t(len);
         ts[t].prefix = 0;
-        ts[t].krem = uint32_t(k > 0 ? k : 0);
+        ts[t].krem = all ? 0u : uint32_t(k > 0 ? k : 0);
+        ts[t].done21 = all ? kDoneAll : 0u;
     }
-    if (mode == kModeSkip) return;  // uniform
+    if (mode == kModeSkip) {  // uniform
+        if (out_count && tid == 0) out_count[t] = 0;
+        return;
+    }
     const bool list = mode == kModeList;
     const bool in_lds = list && len <= kFinItems;
     // 2. gather: every round's run offsets first (one block scan a round,
@@ -471,23 +477,27 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     // 3. the three digits
     const float* srcv = list ? olist_v + L.obase[t] : v + o;
     auto val_at = [&](int64_t i) -> float { return in_lds ? sv[i] : srcv[i]; };
-    auto key_at = [&](int64_t i) -> uint32_t { return mag_key(val_at(i)); };
+    auto key_at = [&](int64_t i) -> uint32_t { return floor_key(mag_key(val_at(i)), fl); };
     // On the list, every key is at least the window's lower edge lo: the top
     // 21 bits of T come from one histogram of (key >> 10) - (lo >> 10) when
     // they lie within 2046 bins of lo's, else from the first two digits.
-    uint32_t prefix = 0, krem = uint32_t(k);
-    bool ok = list && lo_key != kNoKey &&
-              fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, lds, pick);
-    if (!ok) {  // uniform
-        prefix = 0;
+    uint32_t prefix = 0, krem = 0;
+    if (!all) {  // uniform
         krem = uint32_t(k);
-        ok = fin_digit<0>(key_at, len, prefix, krem, h, lds, pick);
-        ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, lds, pick);
-    }
-    ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, lds, pick);
-    if (!ok) {  // uniform
-        if (tid == 0) latch_error(sc, kErrInternal);
-        return;
+        bool ok = list && lo_key != kNoKey &&
+                  fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, lds, pick);
+        if (!ok) {  // uniform
+            prefix = 0;
+            krem = uint32_t(k);
+            ok = fin_digit<0>(key_at, len, prefix, krem, h, lds, pick);
+            ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, lds, pick);
+        }
+        ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, lds, pick);
+        if (!ok) {  // uniform
+            if (tid == 0) latch_error(sc, kErrInternal);
+            return;
+        }
+        krem = last_rank<2>(prefix, krem, fl);
     }
     if (tid == 0) {
         ts[t].prefix = prefix;
@@ -527,6 +537,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
         gb += wcnt[j];
         eb += wcnt[kTsWaves + j];
     }
+    if (out_count && tid == 0) out_count[t] = sent_count(wcnt, r);
     float* vt_ = v + o;
     const uint32_t* oli = olist_i + L.obase[t];
     const float* olu = olist_u + L.obase[t];
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
         }
 #pragma unroll
         for (int q = 0; q < kFinEmitUnroll; ++q) {
-            const uint32_t key = mag_key(val[q]);
+            const uint32_t key = floor_key(mag_key(val[q]), fl);
             const bool gt = in[q] && key > T, eq = in[q] && key == T;
             const uint64_t bg = __ballot(gt), be = __ballot(eq);
             const uint32_t g1 = gb + uint32_t(__popcll(bg & lt));

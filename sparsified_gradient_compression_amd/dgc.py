@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.dgc_compress_sampled.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
                                        P, P, P]
     L.dgc_compress_sampled.restype = ctypes.c_int
+    L.dgc_compress_hier.argtypes = [P, P, P, ctypes.c_double, P, P, P, P, P, P]
+    L.dgc_compress_hier.restype = ctypes.c_int
     L.dgc_compress_shared.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P]
     L.dgc_compress_shared.restype = ctypes.c_int
     L.dgc_shared_sum.argtypes = [P, i32, P, P, P, P, P, P]
@@ -186,6 +188,15 @@ def dgc_compress_binlocal(st, g, bin_len, cap, clip: float, out_idx, out_val,
                                        _dp(out_total), _dp(out_norm),
                                        _dp(out_scale), _stream(stream)),
            "dgc_compress_binlocal")
+
+
+def dgc_compress_hier(st, g, k, clip: float, out_idx, out_val, out_count,
+                      out_norm=None, out_scale=None, stream=None):
+    kk = _i64(k)
+    _check(lib().dgc_compress_hier(st, _dp(g), _hp(kk), float(clip), _dp(out_idx),
+                                   _dp(out_val), _dp(out_count), _dp(out_norm),
+                                   _dp(out_scale), _stream(stream)),
+           "dgc_compress_hier")
 
 
 def dgc_compress_sampled(st, g, k, cap, clip: float, out_idx, out_val, out_count,
@@ -375,8 +386,17 @@ class Learner:
         self.count = torch.empty(self.T, dtype=torch.int64, device=dev)
         self.total = torch.empty(self.T, dtype=torch.int64, device=dev)
 
+    def _check_grad(self, g):
+        """The kernels read n floats from g: refuse a shorter or differently
+        typed gradient here, before any launch."""
+        import torch
+        if g.dtype != torch.float32 or g.numel() < self.n:
+            raise ValueError(f"gradient must be float32 with at least {self.n} elements "
+                             f"(got {g.dtype}, {g.numel()})")
+
     def compress(self, g, k: Sequence[int], clip: float, stream=None):
         """One step; returns (idx, val) views holding sum(k) entries."""
+        self._check_grad(g)
         K = int(sum(int(x) for x in k))
         dgc_compress(self.state, g, k, clip, self.idx, self.val, self.norm,
                      self.scale, stream)
@@ -387,6 +407,7 @@ class Learner:
         """One step with the bin-local selector.  Returns (idx, val, count,
         total): idx/val hold sum(cap) slots, tensor t's count[t] delivered
         entries first in its cap[t] slots; total[t] = salient entries."""
+        self._check_grad(g)
         C = int(sum(int(x) for x in cap))
         dgc_compress_binlocal(self.state, g, bin_len, cap, clip, self.idx,
                               self.val, self.count, self.total, self.norm,
@@ -397,14 +418,26 @@ class Learner:
                          stream=None):
         """One step with the sampled threshold (about k[t] entries per
         tensor).  Returns (idx, val, count, total) as compress_binlocal."""
+        self._check_grad(g)
         C = int(sum(int(x) for x in cap))
         dgc_compress_sampled(self.state, g, k, cap, clip, self.idx, self.val,
                              self.count, self.total, self.norm, self.scale, stream)
         return self.idx[:C], self.val[:C], self.count, self.total
 
+    def compress_hier(self, g, k: Sequence[int], clip: float, stream=None):
+        """One step with hierarchical thresholding (at most k[t] entries per
+        tensor).  Returns (idx, val, count): idx/val hold sum(k) slots,
+        tensor t's count[t] sent entries first in its k[t] slots."""
+        self._check_grad(g)
+        K = int(sum(int(x) for x in k))
+        dgc_compress_hier(self.state, g, k, clip, self.idx, self.val, self.count,
+                          self.norm, self.scale, stream)
+        return self.idx[:K], self.val[:K], self.count
+
     def compress_shared(self, g, k: Sequence[int], shared_idx, clip: float, stream=None):
         """One step at another learner's index set (shared_idx: that
         learner's idx, sum(k) entries).  Returns the val view (sum(k))."""
+        self._check_grad(g)
         K = int(sum(int(x) for x in k))
         dgc_compress_shared(self.state, g, k, shared_idx, clip, self.val, self.norm,
                             self.scale, stream)

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) >= 19, names
+    assert len(names) >= 20, names
     L = dgc.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -96,6 +96,8 @@ def test_init_and_calls_reject_bad_arguments_before_any_launch():
                                   None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_compress_shared(None, None, None, None, 0.0, None, None, None,
                                  None) == dgc.DGC_EINVAL
+    assert L.dgc_compress_hier(None, None, None, 0.0, None, None, None, None, None,
+                               None) == dgc.DGC_EINVAL
     assert L.dgc_shared_sum(None, 1, None, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_accumulate(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL
     assert L.dgc_decode_sum(None, 1, None, None, None, None, None) == dgc.DGC_EINVAL

@@ -5,7 +5,8 @@ warmup350m (350M, k from 87.5M down to 350k) are compared with the oracle in
 full.  flat1b (2**30 elements in 64 chunks, 4 learners x 3 steps) runs in
 the launch configuration the benchmark times and is compared with the oracle
 in full as well: every chunk's indices, values, stream and u/v state, for
-each of the three selectors, and the four learners' dense sum of every step.
+each of the four one-learner selectors, and the four learners' dense sum of
+every step.
 The learners run one after another (learner-major) so that the host holds
 one learner's oracle state (8 GiB) at a time; a learner's results do not
 depend on the others'.
@@ -55,8 +56,8 @@ def _flat1b_full(selector):
     """flat1b at full size, compared with the oracle on all 64 chunks.
 
     selector: "topk" (dgc_compress, k = ceil(n_t / 1000)), "binlocal"
-    (bins of 512, at most n_t / 8 delivered) or "sampled" (target k, at
-    most 4 k delivered)."""
+    (bins of 512, at most n_t / 8 delivered), "sampled" (target k, at
+    most 4 k delivered) or "hier" (dgc_compress_hier: at most k sent)."""
     import torch
     wl = W.get("flat1b")
     C = wl.sizes[0]
@@ -64,7 +65,7 @@ def _flat1b_full(selector):
     sizes = np.array(wl.sizes, np.int64)
     k = [oracle_k(C, wl.densities[0])] * T
     assert k[0] == 16778
-    if selector == "topk":
+    if selector in ("topk", "hier"):
         cap = list(k)
     elif selector == "binlocal":
         cap = [C // 8] * T
@@ -93,6 +94,9 @@ def _flat1b_full(selector):
             elif selector == "binlocal":
                 L.compress_binlocal(g, [512] * T, cap, wl.clip)
                 L.encode_counts(cap)
+            elif selector == "hier":
+                L.compress_hier(g, k, wl.clip)
+                L.encode_counts(cap)
             else:
                 L.compress_sampled(g, k, cap, wl.clip)
                 L.encode_counts(cap)
@@ -108,6 +112,9 @@ def _flat1b_full(selector):
             elif selector == "binlocal":
                 o_idx, o_val, o_cnt, o_tot, o_norm, o_s = oracle.binlocal_step(
                     sizes, [512] * T, cap, g_host, ou, ov, wl.momentum, wl.clip)
+            elif selector == "hier":
+                o_idx, o_val, o_cnt, o_tot, o_th, o_norm, o_s = oracle.hier_step(
+                    sizes, k, g_host, ou, ov, wl.momentum, wl.clip)
             else:
                 o_idx, o_val, o_cnt, o_tot, o_th, o_norm, o_s = oracle.sampled_step(
                     sizes, k, cap, g_host, ou, ov, wl.momentum, wl.clip)
@@ -123,8 +130,14 @@ def _flat1b_full(selector):
                 assert np.array_equal(f32_bits(gv), f32_bits(o_val)), tag
             else:
                 cnt = _host(L.count)
-                tot = _host(L.total)
                 assert np.array_equal(cnt, o_cnt), (tag, first_diff(cnt, o_cnt))
+                if selector == "hier":
+                    # at most k; exactly k wherever k or more survive
+                    assert (cnt == np.minimum(k[0], o_tot)).all(), tag
+                    info = L.select_info()
+                    tot = np.where(info[:, 0] == 1, info[:, 2], o_tot)
+                else:
+                    tot = _host(L.total)
                 assert np.array_equal(tot, o_tot), (tag, first_diff(tot, o_tot))
                 if selector == "sampled":
                     # the count follows k (the sample's quantile), not exactly
@@ -218,6 +231,13 @@ def test_flat1b_sampled_full():
     """The sampled-threshold selector (DGC review, RQ4) in the benchmark's
     configuration: target k = 16778 per chunk, at most 4 k delivered."""
     _flat1b_full("sampled")
+
+
+@pytest.mark.timeout(1200)
+def test_flat1b_hier_full():
+    """Hierarchical thresholding (DGC review, RQ4): the sampled threshold
+    for k = 16778, then an exact select of k among its survivors."""
+    _flat1b_full("hier")
 
 
 @pytest.mark.timeout(1200)

@@ -317,8 +317,9 @@ def test_k_above_k_max_is_rejected():
     g = torch.zeros(1000, device="cuda")
     with pytest.raises(dgc.DGCError):
         p.learner.compress(g, [6], 0.0)
+    g1 = torch.zeros(1001, device="cuda")
     with pytest.raises(dgc.DGCError):
-        p.learner.compress(g[1:], [1], 0.0)  # misaligned gradient
+        p.learner.compress(g1[1:], [1], 0.0)  # misaligned gradient (1000 elements)
 
 
 def test_pipelined_learners_on_streams():
