@@ -11,7 +11,7 @@ import pytest
 from conftest import ROOT
 
 
-@pytest.mark.parametrize("selector", ["topk", "binlocal", "sampled", "shared"])
+@pytest.mark.parametrize("selector", ["topk", "binlocal", "sampled", "hier", "shared"])
 def test_traffic_record_matches_current_kernel_sources(selector):
     import bench
     path, _ = bench.TRAFFIC[selector]
