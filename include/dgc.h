@@ -76,18 +76,19 @@ extern "C" {
                                    on its own); 1 always on its own; 2 always
                                    merged -- the same results, only the speed
                                    differs */
-#define DGC_OPT_SELECT_GRID 4   /* dgc_compress, the exact select and emit
-                                   after the candidates are gathered: 0
-                                   automatic (default: one 1024-thread
-                                   workgroup per tensor when every tensor has
-                                   at most 2^20 elements and at most 32768
-                                   to select from -- all of it up to 65536
-                                   elements, else its candidate list's
-                                   capacity -- else passes spread over all
-                                   workgroups); 1 always a workgroup per
-                                   tensor (slow for long sources); 2 always
-                                   the spread passes -- the same results, only
-                                   the speed differs */
+#define DGC_OPT_SELECT_GRID 4   /* dgc_compress and dgc_compress_hier, the
+                                   exact select and emit: 0 automatic
+                                   (default: when every tensor has at most
+                                   2^22 elements, one 1024-thread workgroup
+                                   per tensor for the window and for the
+                                   gather, select and emit; else passes
+                                   spread over all workgroups); 1 the same
+                                   per-tensor kernels, and on layouts with a
+                                   larger tensor one workgroup per tensor
+                                   for the select and emit after the spread
+                                   gather (slow for long sources); 2 always
+                                   the spread passes -- the same results,
+                                   only the speed differs */
 
 /* Timers for dgc_get_kernel_time. */
 #define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress,

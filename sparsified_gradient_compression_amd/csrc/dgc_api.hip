@@ -59,7 +59,6 @@ struct Plan {
     int64_t DB = 0, NBLK = 0;
     int64_t n = 0, P = 0, G = 0, TT = 0, A = 0, SL = 0, S = 0, E = 0, ET = 0, NB = 0;
     int64_t norm_chunk = 0;
-    bool short_sources = true;  // every tensor fits the per-tensor select
     // every tensor holds at most kTensorPathMaxN elements: dgc_compress takes
     // the per-tensor window and finish kernels, and small tensors get the
     // sample window (all of their lines) and candidate slots too
@@ -162,9 +161,6 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     }
     p.n = p.o[T];
     for (int32_t t = 0; t < T; ++t) {
-        const int64_t n = sizes[t];
-        const int64_t src = n <= kSmallN ? n : p.obase[t + 1] - p.obase[t];
-        if (n > kPerTensorMaxN || src > kPerTensorMaxItems) p.short_sources = false;
         p.staged_tiles |= p.tbase[t + 1] - p.tbase[t] > kScanStagedMin;
         p.staged_etiles |= p.etbase[t + 1] - p.etbase[t] > kScanStagedMin;
     }
@@ -855,9 +851,9 @@ static int enqueue_select(dgc_state* st, int64_t K, uint32_t* out_idx, float* ou
         k_group_sum<<<int(p.G), kBlock, 0, stream>>>(st->L, st->run_cnt, st->gsum);
     k_group_scan<<<T, kBlock, 0, stream>>>(st->L, st->K, st->ts, st->gsum, st->goff,
                                            st->atiles);
-    // the select and emit: one workgroup per tensor when every selection
-    // source is short, else passes spread over the chip
-    const bool per_tensor = st->select_grid == 1 || (st->select_grid == 0 && p.short_sources);
+    // the select and emit: one workgroup per tensor when asked for, else
+    // passes spread over the chip
+    const bool per_tensor = st->select_grid == 1;
     // for the spread passes the gather also histograms the lists' top 21
     // bits, which k_resolve21 turns into T's top 21 bits where it can
     if (p.G > 0)

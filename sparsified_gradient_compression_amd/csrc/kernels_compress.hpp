@@ -1014,25 +1014,16 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
 // ---------------------------------------------------------------- per tensor
 
 // The same select and emit for one tensor in one 1024-thread workgroup,
-// for layouts whose selection sources are all short (the host decides): the
-// three digit histograms live in LDS and are resolved in place, and the
-// emit splits the source into 16 index-ordered wave chunks whose counts
-// give each wave its output offsets.  One launch replaces the eleven of
-// the spread passes (active tiles, three histogram and resolve pairs,
-// count, scan, write), whose cost on small layouts is mostly the ~4.7 us
-// each dependent launch takes.  Results and the per-tensor record
-// (prefix = T, krem = r) are the same as the spread passes'.
+// after the spread path's gather (DGC_OPT_SELECT_GRID 1 on layouts that the
+// per-tensor kernels of kernels_tensor.hpp do not take): the three digit
+// histograms live in LDS and are resolved in place, and the emit splits the
+// source into 16 index-ordered wave chunks whose counts give each wave its
+// output offsets.  One launch replaces the eleven of the spread passes
+// (active tiles, three histogram and resolve pairs, count, scan, write).
+// One workgroup sweeps ~3.7 G items/s, so long sources go faster as spread
+// passes.  Results and the per-tensor record (prefix = T, krem = r) are the
+// same as the spread passes'.
 constexpr int kTsThreads = 1024;
-// The automatic choice takes the per-tensor workgroup when every tensor's
-// selection source is short: at most kPerTensorMaxItems items (the whole
-// tensor up to kSmallN elements, else the candidate list's capacity), and
-// every tensor at most kPerTensorMaxN elements, so that a fall-back to the
-// whole tensor costs one workgroup five sweeps of at most 4 MiB.  Longer
-// sources go faster as spread passes: one workgroup sweeps ~3.7 G items/s
-// (65536 items, 88 us), and the scattered restores of a long list need
-// more CUs than one per tensor.
-constexpr int64_t kPerTensorMaxItems = 32768;
-constexpr int64_t kPerTensorMaxN = int64_t(1) << 20;
 constexpr int kTsWaves = kTsThreads / kWave;
 constexpr int kTsHistUnroll = 8;  // keys loaded together per thread
 constexpr int kTsEmitUnroll = 4;  // 64-item rounds loaded together per wave
