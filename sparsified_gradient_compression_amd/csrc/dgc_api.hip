@@ -856,11 +856,14 @@ static int enqueue_select(dgc_state* st, int64_t K, uint32_t* out_idx, float* ou
     const bool per_tensor = st->select_grid == 1;
     // for the spread passes the gather also histograms the lists' top 21
     // bits, which k_resolve21 turns into T's top 21 bits where it can
+    // at an average density of 1/8 or more the pieces hold long runs: the
+    // gather copies them run by run, several workgroups per group
+    const int runs = K * kGatherRunDensity >= p.n ? 1 : 0;
+    const int split = runs ? kGatherSplit : 1;
     if (p.G > 0)
-        k_gather<<<int(p.G), kBlock, 0, stream>>>(st->L, st->ts, st->slots,
-                                                  st->run_cnt, st->goff, st->olist_i,
-                                                  st->olist_v, st->olist_u, st->u, st->v,
-                                                  per_tensor ? nullptr : st->hist);
+        k_gather<<<int(p.G * split), kBlock, 0, stream>>>(
+            st->L, st->ts, st->slots, st->run_cnt, st->goff, st->olist_i, st->olist_v,
+            st->olist_u, st->u, st->v, per_tensor ? nullptr : st->hist, split, runs);
     if (K > 0 && per_tensor) {
         k_select_tensor<<<T, kTsThreads, 0, stream>>>(
             st->L, st->K, st->ts, st->u, st->v, st->olist_i, st->olist_v, st->olist_u,

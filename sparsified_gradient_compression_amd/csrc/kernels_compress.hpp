@@ -460,7 +460,18 @@ __device__ __forceinline__ void hist_inc(uint32_t* h, uint32_t bin, bool valid) 
 // set (the spread passes follow), the list's keys are also counted by their
 // top 21 bits above the window edge into the tensor's histogram row, for
 // k_resolve21.
-constexpr int kGatherBatch = 8;  // slot loads in flight per thread
+// With `runs` set (the host sets it at high k, where pieces hold long runs)
+// a wave copies whole runs instead: the group's pieces are split over
+// `split` workgroups (grid = groups x split), each wave takes every fourth
+// of its workgroup's pieces and copies the piece's run, 64 items a round,
+// kGatherRunUnroll rounds in flight: no search, 32-bit offsets, and the
+// list's open top histogram bin (most of a dense list) counted in registers.
+// At 25% density the per-item search made the gather issue ~112 vector
+// instructions per item, which bounded it, not its bytes.
+constexpr int kGatherBatch = 8;      // slot loads in flight per thread
+constexpr int kGatherSplit = 4;      // workgroups per group with `runs`
+constexpr int kGatherRunUnroll = 4;  // 64-item rounds in flight per wave
+constexpr int64_t kGatherRunDensity = 8;  // runs when sum k >= n / 8
 
 __global__ __launch_bounds__(kBlock) void k_gather(
     DevLayout L, const TensorState* __restrict__ ts,
@@ -468,11 +479,12 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     const uint32_t* __restrict__ run_cnt, const uint32_t* __restrict__ goff,
     uint32_t* __restrict__ olist_i, float* __restrict__ olist_v,
     float* __restrict__ olist_u, float* __restrict__ u, float* __restrict__ v,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, int split, int runs) {
     __shared__ uint32_t lds[kWavesPerBlock];
     __shared__ uint32_t pre[kGroup + 1];
     __shared__ uint32_t h21[kHistBins];
-    const int64_t g = blockIdx.x;
+    const int64_t g = blockIdx.x / split;
+    const uint32_t part = blockIdx.x % split;
     const int t = int(L.gmap[g]);
     const bool list = ts[t].mode == kModeList;  // uniform
     // the list's top-21-bit histogram, unless nothing is left to select
@@ -509,17 +521,59 @@ __global__ __launch_bounds__(kBlock) void k_gather(
             u[o + it.idx] = it.u;
         }
     };
-    // Threads take the group's items q = q0 + u kBlock + tid, kGatherBatch
-    // at a time: each finds its piece by binary search over the piece
-    // prefixes (largest j < np with pre[j] <= q), the batch's slot loads go
-    // out together, then its stores.  Consecutive threads read consecutive
+    if (runs) {  // uniform
+        // this workgroup's pieces [ja, jb); wave w takes ja + w, ja + w + 4, ...
+        const int ja = int(np * part / split), jb = int(np * (part + 1) / split);
+        const int lane = lane_id();
+        uint32_t open = 0;  // items in the open top bin
+        for (int j = ja + (tid >> 6); j < jb; j += kWavesPerBlock) {
+            const uint32_t pos0 = pre[j], cnt = pre[j + 1] - pos0;
+            const CandSlot* sp = src0 + int64_t(j) * pcap;
+            for (uint32_t i0 = 0; i0 < cnt; i0 += kWave * kGatherRunUnroll) {
+                CandSlot it[kGatherRunUnroll];
+#pragma unroll
+                for (int r = 0; r < kGatherRunUnroll; ++r) {
+                    const uint32_t i = i0 + uint32_t(r * kWave + lane);
+                    if (i < cnt) it[r] = sp[i];
+                }
+#pragma unroll
+                for (int r = 0; r < kGatherRunUnroll; ++r) {
+                    const uint32_t i = i0 + uint32_t(r * kWave + lane);
+                    if (i >= cnt) continue;
+                    put(it[r], pos0 + i);
+                    if (hist21) {  // uniform
+                        const uint32_t d = (mag_key(it[r].v) >> 10) - lo21;
+                        if (d < uint32_t(kHistBins - 1)) atomicAdd(&h21[d], 1u);
+                        else ++open;
+                    }
+                }
+            }
+        }
+        if (hist21) {  // uniform: add the workgroup's counts to the tensor's row
+            for (int d = kWave / 2; d >= 1; d >>= 1) open += __shfl_xor(open, d, kWave);
+            if (lane == 0 && open) atomicAdd(&h21[kHistBins - 1], open);
+            __syncthreads();
+            uint32_t* row = hist + int64_t(t) * kHistBins;
+            for (int b = threadIdx.x; b < kHistBins; b += kBlock)
+                if (h21[b]) atomicAdd(&row[b], h21[b]);
+        }
+        return;
+    }
+    // This workgroup's share of the group's items: [qa, qb).
+    const uint32_t qa = uint32_t(uint64_t(tot) * part / uint32_t(split));
+    const uint32_t qb = uint32_t(uint64_t(tot) * (part + 1) / uint32_t(split));
+    if (qa >= qb) return;  // uniform
+    // Threads take the items q = q0 + u kBlock + tid, kGatherBatch at a
+    // time: each finds its piece by binary search over the piece prefixes
+    // (largest j < np with pre[j] <= q), the batch's slot loads go out
+    // together, then its stores.  Consecutive threads read consecutive
     // slots of one run and write consecutive list entries.
-    for (uint32_t q0 = 0; q0 < tot; q0 += kGatherBatch * kBlock) {
+    for (uint32_t q0 = qa; q0 < qb; q0 += kGatherBatch * kBlock) {
         CandSlot it[kGatherBatch];
 #pragma unroll
         for (int b = 0; b < kGatherBatch; ++b) {
             const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
-            if (q < tot) {
+            if (q < qb) {
                 int lo = 0, hi = int(np);
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
@@ -531,13 +585,13 @@ __global__ __launch_bounds__(kBlock) void k_gather(
 #pragma unroll
         for (int b = 0; b < kGatherBatch; ++b) {
             const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
-            if (q < tot) put(it[b], q);
+            if (q < qb) put(it[b], q);
             // the list's keys by their top 21 bits above the window edge
             // (every candidate is at least lo); bin 2047 takes the rest
             if (hist21) {  // uniform
                 const uint32_t d = (mag_key(it[b].v) >> 10) - lo21;
                 hist_inc(h21, d < uint32_t(kHistBins - 1) ? d : uint32_t(kHistBins - 1),
-                         q < tot);
+                         q < qb);
             }
         }
     }
@@ -914,6 +968,31 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
     const float* olu = olist_u;
     uint32_t* oi = out_idx;
     float* ov = out_val;
+    // A thread takes 4 consecutive items of a tile (vector loads; on the
+    // list path the saved u comes too, the items not sent need it).  The
+    // next tile of the same tensor is loaded before this one is worked on
+    // (its loads then wait behind this tile's scan and stores, not in
+    // front of the next one's).
+    auto load_tile = [&](uint32_t at, uint32_t& cg, uint32_t& ce, float (&val)[kPerThread],
+                         uint32_t (&lidx)[kPerThread], float (&usv)[kPerThread]) {
+        cg = off_gt[at];
+        ce = off_eq[at];
+        const int64_t ib = int64_t(at - ab) * kTile + int64_t(threadIdx.x) * kPerThread;
+        load_items(src, ib, len, val);
+        if (dense) {
+#pragma unroll
+            for (int q = 0; q < kPerThread; ++q) {
+                lidx[q] = uint32_t(ib + q);
+                usv[q] = 0.0f;
+            }
+        } else {
+            load_items(oli, ib, len, lidx);
+            load_items(olu, ib, len, usv);
+        }
+    };
+    bool have = false;  // the tile's loads were issued by the previous iteration
+    uint32_t ncg = 0, nce = 0, nlidx[kPerThread];
+    float nval[kPerThread], nusv[kPerThread];
     for (uint32_t a = blockIdx.x; a < A; a += gridDim.x) {
         if (a >= ae) {  // uniform: the next tensor
             const int t = int(amap[a]);
@@ -934,25 +1013,31 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
             kt = K.k[t];
             ab = aoff[t];
             ae = aoff[t + 1];
+            have = false;
         }
-        // A thread takes 4 consecutive items (vector loads; on the list path
-        // the saved u comes too, the items not sent need it).  One block
-        // scan of the packed (#key > T, #key == T) counts gives each item
-        // its place in index order; the sent items are staged in LDS by
-        // their rank among the tile's sent items and stored coalesced.
-        const uint32_t cg = off_gt[a], ce = off_eq[a];
+        // One block scan of the packed (#key > T, #key == T) counts gives
+        // each item its place in index order; the sent items are staged in
+        // LDS by their rank among the tile's sent items and stored coalesced.
+        uint32_t cg, ce;
+        float val[kPerThread], usv[kPerThread];
+        uint32_t lidx[kPerThread];
+        if (have) {  // uniform
+            cg = ncg;
+            ce = nce;
+#pragma unroll
+            for (int q = 0; q < kPerThread; ++q) {
+                val[q] = nval[q];
+                lidx[q] = nlidx[q];
+                usv[q] = nusv[q];
+            }
+        } else {
+            load_tile(a, cg, ce, val, lidx, usv);
+        }
+        const uint32_t an = a + gridDim.x;
+        have = an < ae;  // uniform
+        if (have) load_tile(an, ncg, nce, nval, nlidx, nusv);
         const int64_t ib = int64_t(a - ab) * kTile + int64_t(threadIdx.x) * kPerThread;
         bool bad = false;
-        float val[kPerThread], usv[kPerThread] = {0.0f, 0.0f, 0.0f, 0.0f};
-        uint32_t lidx[kPerThread];
-        load_items(src, ib, len, val);
-        if (dense) {
-#pragma unroll
-            for (int q = 0; q < kPerThread; ++q) lidx[q] = uint32_t(ib + q);
-        } else {
-            load_items(oli, ib, len, lidx);
-            load_items(olu, ib, len, usv);
-        }
         bool gt[kPerThread], eq[kPerThread];
         uint32_t c = 0;
 #pragma unroll

@@ -528,6 +528,33 @@ def test_dense_fallback_after_masking(grid):
     p.step(rng.laplace(0, 1e-3, n).astype(np.float32), k, 0.0, tag="fallback s1")
 
 
+@pytest.mark.parametrize("grid", [0, 2])
+def test_dense_fallback_with_run_gather(grid):
+    """At an average density of 1/8 or more the spread path's gather copies
+    whole runs (several workgroups per piece group).  Tensors 0 and 2 (the
+    last above 2^22 elements, so the layout takes the spread passes) select
+    at density 1/4 from their lists; tensor 1 (k = 1000, about 29 slots per
+    piece) has one piece of 500 large values that overflows, so it takes the
+    dense path and the run gather must give its other pieces' candidates
+    their u and v back.  Same bits as the oracle over two steps."""
+    rng = np.random.default_rng(78)
+    sizes = [1 << 20, 1 << 20, (1 << 22) + 3]
+    k = [1 << 18, 1000, oracle_k(sizes[2], Fraction(1, 4))]
+    assert sum(k) * 8 >= sum(sizes)
+    p = Pair(sizes, k)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    n = int(off[-1])
+    g = rng.laplace(0, 1e-3, n).astype(np.float32)
+    a = int(off[1]) + 7 * 1024
+    g[a:a + 500] = rng.uniform(1.0, 2.0, 500).astype(np.float32)
+    p.step(g, k, 0.0, tag="run gather s0")
+    info = p.learner.select_info()
+    assert info[0, 0] == 1 and info[2, 0] == 1, info.tolist()
+    assert info[1, 0] == 2 and info[1, 3] == 1, info[1].tolist()
+    p.step(rng.laplace(0, 1e-3, n).astype(np.float32), k, 0.5, tag="run gather s1")
+
+
 @pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("path", [0, 1])
 def test_denormals_and_extremes(path, grid):
