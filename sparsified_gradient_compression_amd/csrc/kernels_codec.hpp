@@ -80,49 +80,64 @@ __device__ __forceinline__ int64_t enc_len(const DevK& K, const int64_t* kdev, i
 // index) - (the index before its first) - (its entries): a tile spanning
 // less than that needs none, which two loads show (DGC's 0.1% spans ~1M
 // positions per tile and takes the entry-by-entry count; denser streams
-// mostly do not).  Index order is checked by k_enc_write.
+// mostly do not).  A workgroup tests its next kEncTest tiles at once, one
+// thread each (a dense stream's tiles then cost one round of loads per
+// kEncTest tiles instead of one each), and counts entry by entry only the
+// tiles the test does not settle.  Index order is checked by k_enc_write.
+constexpr int kEncTest = 16;
+
 __global__ __launch_bounds__(kBlock) void k_enc_count(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ idx, uint32_t* __restrict__ tile_f,
     Scalars* __restrict__ sc, int64_t n_ktiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
-    int64_t tb = 0, te = 0, kt = 0, nt = 0;  // current tensor: tiles [tb, te)
-    const uint32_t* id = idx;
-    for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
-        if (vt >= te) {  // uniform: the next tensor
-            const int t = int(K.kmap[vt]);
-            kt = enc_len(K, kdev, t);
-            nt = L.o[t + 1] - L.o[t];
-            id = idx + K.koff[t];
-            tb = K.ktbase[t];
-            te = K.ktbase[t + 1];
-        }
-        const int64_t i0 = (vt - tb) * kTile;
-        if (i0 >= kt) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, te, gridDim.x);
-            continue;
-        }
-        const int64_t i1 = min(kt, i0 + kTile);
-        const int64_t before = i0 ? int64_t(id[i0 - 1]) : -1;
-        if (int64_t(id[i1 - 1]) - before - (i1 - i0) < 65536) {  // uniform
-            if (threadIdx.x == 0) tile_f[vt] = 0;
-            vt += gridDim.x;
-            continue;
-        }
-        uint32_t f = 0;
-        bool bad = false;
-        for (int q = 0; q < kPerThread; ++q) {
-            int64_t i = i0 + q * kBlock + threadIdx.x;
-            if (i < kt) {
-                int64_t gap;
-                f += fillers_of(id, i, nt, bad, gap);
+    __shared__ uint32_t full[kEncTest];  // tests (thread numbers) left unsettled
+    __shared__ uint32_t nfull;
+    const int64_t G = gridDim.x;
+    for (int64_t vt0 = blockIdx.x; vt0 < n_ktiles; vt0 += G * kEncTest) {
+        if (threadIdx.x == 0) nfull = 0;
+        __syncthreads();
+        if (threadIdx.x < uint32_t(kEncTest)) {
+            const int64_t vt = vt0 + int64_t(threadIdx.x) * G;
+            if (vt < n_ktiles) {
+                const int t = int(K.kmap[vt]);
+                const int64_t kt = enc_len(K, kdev, t);
+                const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+                if (i0 < kt) {  // else nothing here: the scan stops before this tile
+                    const uint32_t* id = idx + K.koff[t];
+                    const int64_t i1 = min(kt, i0 + kTile);
+                    const int64_t before = i0 ? int64_t(id[i0 - 1]) : -1;
+                    if (int64_t(id[i1 - 1]) - before - (i1 - i0) < 65536)
+                        tile_f[vt] = 0;
+                    else
+                        full[atomicAdd(&nfull, 1u)] = threadIdx.x;
+                }
             }
         }
-        if (bad) latch_error(sc, kErrCorrupt);
-        uint32_t tot;
-        block_exclusive_scan(f, lds, tot);
-        if (threadIdx.x == 0) tile_f[vt] = tot;
-        vt += gridDim.x;
+        __syncthreads();
+        const uint32_t nf = nfull;
+        for (uint32_t q = 0; q < nf; ++q) {  // uniform
+            const int64_t vt = vt0 + int64_t(full[q]) * G;
+            const int t = int(K.kmap[vt]);
+            const int64_t kt = enc_len(K, kdev, t);
+            const int64_t nt = L.o[t + 1] - L.o[t];
+            const uint32_t* id = idx + K.koff[t];
+            const int64_t i0 = (vt - K.ktbase[t]) * kTile;
+            uint32_t f = 0;
+            bool bad = false;
+            for (int c = 0; c < kPerThread; ++c) {
+                const int64_t i = i0 + c * kBlock + threadIdx.x;
+                if (i < kt) {
+                    int64_t gap;
+                    f += fillers_of(id, i, nt, bad, gap);
+                }
+            }
+            if (bad) latch_error(sc, kErrCorrupt);
+            uint32_t tot;
+            block_exclusive_scan(f, lds, tot);
+            if (threadIdx.x == 0) tile_f[vt] = tot;
+        }
+        __syncthreads();  // every thread has read full[] before the next round resets it
     }
 }
 
