@@ -131,7 +131,8 @@ def parse():
                     help="run each learner on its own stream, starting once the "
                          "previous learner's element-wise pass is done")
     ap.add_argument("--select-grid", type=int, choices=(0, 1, 2), default=0,
-                    help="DGC_OPT_SELECT_GRID for dgc_compress: 0 automatic, 1 a workgroup "
+                    help="DGC_OPT_SELECT_GRID for dgc_compress and dgc_compress_hier: 0 "
+                         "automatic, 1 a workgroup "
                          "per tensor, 2 the spread passes")
     ap.add_argument("--timers", choices=("fused", "off"), default="fused",
                     help="library timers in the timed region: the element-wise "
