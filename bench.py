@@ -140,7 +140,13 @@ def parse():
     ap.add_argument("--selector", choices=("topk", "binlocal", "sampled", "hier", "shared"),
                     default="topk",
                     help="exact per-tensor top-k (DGC), AdaComp's bin-local rule, the "
-                         "sampled threshold, or shared-index compression (ScaleComp)")
+                         "sampled threshold, the sampled threshold with an exact "
+                         "top-k among its survivors, or shared-index compression "
+                         "(ScaleComp)")
+    ap.add_argument("--records", default="",
+                    help="write one JSON line per (measured step, learner) to this "
+                         "file: k, sent entries, stream entries, times, algorithmic "
+                         "bytes and rates")
     ap.add_argument("--bin-len", type=int, default=512,
                     help="bin length for --selector binlocal (1..1024)")
     ap.add_argument("--cap-den", type=int, default=8,
@@ -568,11 +574,12 @@ class Run:
         dgc = self.dgc
         self.drain_timers()
         self.set_timing(1)
-        rec = {"compress": [], "fused": [], "encode": [], "decode": [], "k": []}
+        rec = {"compress": [], "fused": [], "encode": [], "decode": [], "k": [], "rows": []}
         for i in range(steps):
             self.step(first + i)
-            rec["k"].append(self.k_of_step(first + i))
-            enc = []
+            k = self.k_of_step(first + i)
+            rec["k"].append(k)
+            enc, rows, dec = [], [], None
             for w, L in enumerate(self.learners):
                 c, nc = L.kernel_time(dgc.DGC_TIMER_COMPRESS)
                 f, nf = L.kernel_time(dgc.DGC_TIMER_FUSED)
@@ -585,6 +592,19 @@ class Run:
                     enc.append(e / ne)
                 if nd:
                     rec["decode"].append(d / nd)
+                    dec = d / nd
+                # per (step, learner): what left the learner and its times
+                sent = (int(sum(k)) if self.selector in ("topk", "shared")
+                        else int(L.count.sum()))
+                rows.append({"step": first + i, "gradient_step": (first + i) % self.gsteps,
+                             "learner": w, "k": int(sum(k)), "sent": sent,
+                             "stream_entries": int(L.entries.sum()) if ne else None,
+                             "compress_ms": round(c / max(nc, 1), 5),
+                             "k_fused_ms": round(f / nf, 5) if nf else None,
+                             "encode_ms": round(e / ne, 5) if ne else None})
+            for r in rows:
+                r["decode_ms_all_learners"] = round(dec, 5) if dec is not None else None
+            rec["rows"].extend(rows)
             if enc:
                 rec["encode"].append(sum(enc) / len(enc))
         self.set_timing(0)
@@ -609,6 +629,26 @@ def compress_alg_bytes(wl, k):
     (16 B per entry)."""
     clip = 1 if wl.clip > 0 else 0
     return wl.n * (20 + 4 * clip) + 16 * int(sum(k))
+
+
+def write_records(path, wl, selector, rows):
+    """One JSON line per (measured step, learner): the workload and selector,
+    the step's k and what was sent, the library's timings, and the compress
+    call's algorithmic bytes (counted as compress_alg_bytes counts them, at
+    the entries sent) with its rate and fraction of 8 TB/s.  Appends."""
+    with open(path, "a") as f:
+        for r in rows:
+            alg = compress_alg_bytes(wl, [r["sent"]])
+            ms = r["compress_ms"]
+            out = {"workload": wl.name, "selector": selector, "elements": wl.n,
+                   "tensors": len(wl.sizes), "learners": wl.learners, "clip": wl.clip}
+            out.update(r)
+            out.update({"compress_alg_bytes": alg,
+                        "compress_GBps": round(alg / (ms * 1e-3) / 1e9, 1) if ms else None,
+                        "compress_frac_of_peak": (round(alg / (ms * 1e-3) / 1e9 /
+                                                        HBM_PEAK_GBPS, 4) if ms else None),
+                        "compress_G_elem_per_s": round(wl.n / (ms * 1e-3) / 1e9, 2) if ms else None})
+            f.write(json.dumps(out) + "\n")
 
 
 def workload_record(run, steps, warmup, measure_steps, timers):
@@ -667,6 +707,8 @@ def main():
     dgc.lib()
     torch.cuda.set_device(0)
     wl = W.get(args.workload)
+    if args.records:
+        open(args.records, "w").close()
     T = len(wl.sizes)
     n = wl.n
     gsteps = args.grad_steps if args.grad_steps > 0 else wl.steps
@@ -689,6 +731,8 @@ def main():
     log("measurement pass")
     first = args.warmup + args.steps
     rec = run.measure(first, args.measure_steps) if args.measure_steps > 0 else None
+    if args.records and rec is not None:
+        write_records(args.records, wl, args.selector, rec["rows"])
     learners = run.learners
     ks = run.ks
     elems = n * wl.learners * args.steps
@@ -861,8 +905,10 @@ def main():
             log(f"workload {name}")
             owl = W.get(name)
             orun = Run(owl, "topk", args, owl.steps)
-            r, *_ = workload_record(orun, steps, owl.steps, 2 * owl.steps
-                                    if owl.steps > 1 else 10, args.timers)
+            r, _, _, _, orec = workload_record(orun, steps, owl.steps, 2 * owl.steps
+                                               if owl.steps > 1 else 10, args.timers)
+            if args.records:
+                write_records(args.records, owl, "topk", orec["rows"])
             orun.close()
             det["workloads"].append(r)
     if not args.no_cpu_baseline:
