@@ -448,6 +448,25 @@ __device__ __forceinline__ void hist_inc(uint32_t* h, uint32_t bin, bool valid) 
     if ((todo >> lane_id()) & 1u) atomicAdd(&h[bin], 1u);
 }
 
+// For each of B items q[b]: the last j in [0, n) with pre[j] <= q[b] (pre
+// non-decreasing, pre[0] = 0), i.e. the piece that holds item q[b] when
+// pre[j] is the number of items before piece j.  Branchless halving of the
+// range [j, j + len), the same steps for every item, so the B searches go
+// in lockstep with their LDS reads in flight together (a search per item in
+// turn waits on one read at a time).  Every read is in [0, n).
+template <int B>
+__device__ __forceinline__ void piece_of(const uint32_t* pre, int n, const uint32_t (&q)[B],
+                                         int (&j)[B]) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) j[b] = 0;
+    for (int len = n; len > 1;) {  // uniform
+        const int half = len >> 1;
+#pragma unroll
+        for (int b = 0; b < B; ++b) j[b] = pre[j[b] + half] <= q[b] ? j[b] + half : j[b];
+        len -= half;
+    }
+}
+
 // One block per group.  The fused pass masked the candidates of every piece
 // whose run fit its slots (u = v = +0 there; each slot holds the index, v
 // and u).  For a tensor on the list path, concatenate the group's piece
@@ -570,17 +589,14 @@ __global__ __launch_bounds__(kBlock) void k_gather(
     // slots of one run and write consecutive list entries.
     for (uint32_t q0 = qa; q0 < qb; q0 += kGatherBatch * kBlock) {
         CandSlot it[kGatherBatch];
+        uint32_t qs[kGatherBatch];
+        int js[kGatherBatch];
+#pragma unroll
+        for (int b = 0; b < kGatherBatch; ++b) qs[b] = q0 + uint32_t(b) * kBlock + threadIdx.x;
+        piece_of(pre, int(np), qs, js);
 #pragma unroll
         for (int b = 0; b < kGatherBatch; ++b) {
-            const uint32_t q = q0 + uint32_t(b) * kBlock + threadIdx.x;
-            if (q < qb) {
-                int lo = 0, hi = int(np);
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (pre[mid] <= q) lo = mid; else hi = mid;
-                }
-                it[b] = src0[int64_t(lo) * pcap + (q - pre[lo])];
-            }
+            if (qs[b] < qb) it[b] = src0[int64_t(js[b]) * pcap + (qs[b] - pre[js[b]])];
         }
 #pragma unroll
         for (int b = 0; b < kGatherBatch; ++b) {

@@ -18,8 +18,8 @@
 //   fused          the element-wise pass (unchanged)
 //   finish_tensor  one 1024-thread workgroup per tensor: the pieces' counts
 //                  (source choice), the runs gathered into the ordered
-//                  candidate list with the keys kept in LDS, the three radix
-//                  digits over those keys, and the index-ordered emit
+//                  candidate list with the keys kept in LDS, the k-th
+//                  largest key over those keys, and the index-ordered emit
 // Decisions, results and the per-tensor record are the spread passes'.
 #pragma once
 
@@ -42,9 +42,41 @@ static_assert((kTensorPathMaxN / kLine) / 256 <= kMinSampleLines,
 // Candidate-list items held in LDS by finish_tensor (longer lists go to
 // the ordered list in memory instead).
 constexpr int kFinItems = 10240;
-// Rounds of 1024 pieces in finish_tensor (4096 pieces = 2^22 elements).
-constexpr int kFinRounds = int((kTensorPathMaxN / kPiece + kTsThreads - 1) / kTsThreads);
+// Consecutive pieces per thread in finish_tensor (4096 pieces = 2^22
+// elements over 1024 threads).
+constexpr int kFinPieces = int((kTensorPathMaxN / kPiece + kTsThreads - 1) / kTsThreads);
 constexpr int kFinEmitUnroll = 4;  // 64-item rounds loaded together per wave
+// Lists in LDS of at most this many items select by counting (fin_direct).
+constexpr int kFinDirect = 128;
+
+// Inclusive scans over the wave with DPP moves (row_shr 1, 2, 4, 8 within
+// each 16-lane row, then row_bcast 15 and 31 across rows): six ALU steps in
+// place of six LDS-routed shuffles.  A lane a move cannot reach gets 0,
+// the identity of both operations here.
+#define DGC_DPP(x, ctrl, rows) \
+    uint32_t(__builtin_amdgcn_update_dpp(0, int(x), (ctrl), (rows), 0xF, true))
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t x) {
+    x += DGC_DPP(x, 0x111, 0xF);  // row_shr:1
+    x += DGC_DPP(x, 0x112, 0xF);  // row_shr:2
+    x += DGC_DPP(x, 0x114, 0xF);  // row_shr:4
+    x += DGC_DPP(x, 0x118, 0xF);  // row_shr:8
+    x += DGC_DPP(x, 0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+    x += DGC_DPP(x, 0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t x) {
+    x = max(x, DGC_DPP(x, 0x111, 0xF));
+    x = max(x, DGC_DPP(x, 0x112, 0xF));
+    x = max(x, DGC_DPP(x, 0x114, 0xF));
+    x = max(x, DGC_DPP(x, 0x118, 0xF));
+    x = max(x, DGC_DPP(x, 0x142, 0xA));
+    x = max(x, DGC_DPP(x, 0x143, 0xC));
+    return x;
+}
+#undef DGC_DPP
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
+    return uint32_t(__builtin_amdgcn_readlane(int(x), lane));
+}
 
 // S = the binary64 sum of the norm partials in k_norm_final's order: its
 // 256 threads are this block's first four waves, each summing a strided
@@ -221,23 +253,72 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
     }
 }
 
-// Digit D of the radix select over the keys key_at(0 .. len-1): histogram of
-// the keys that match the prefix (wave-aggregated increments for the top
-// digit), then the bin
-// holding the krem-th largest; extends the prefix and reduces krem.  Returns
-// false (uniformly) if no bin holds it.
+// The selection rounds of finish_tensor share one histogram h (2048
+// bins), zero on entry: each round reads its bins and zeroes them again,
+// three barriers apart from the next round's increments.  Each round has
+// its own scan row (kTsWaves words) and pick (2 words, kNoKey in pick[0]
+// on entry), so nothing needs a barrier before reuse: a round costs three
+// barriers (counts done; wave sums posted; pick posted).
+
+// Exclusive scan over the block; `row` (kTsWaves words) is not reused.
+__device__ __forceinline__ uint32_t fin_block_scan(uint32_t x, uint32_t* row, uint32_t& total) {
+    const int lane = lane_id();
+    const int wid = int(threadIdx.x) >> 6;
+    const uint32_t inc = wave_scan_add(x);
+    if (lane == kWave - 1) row[wid] = inc;
+    __syncthreads();
+    uint32_t wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w) {
+        const uint32_t s = row[w];
+        if (w < wid) wpre += s;
+        tot += s;
+    }
+    total = tot;
+    return wpre + inc - x;
+}
+
+// After the counts are in h[0, bins): the bin, counted from the top, that
+// holds the krem-th largest, into pick; the bins are zeroed again.
+template <int bins>
+__device__ __forceinline__ void fin_pick(uint32_t* h, uint32_t krem, uint32_t* row,
+                                         uint32_t* pick) {
+    constexpr int per = (bins + kTsThreads - 1) / kTsThreads;
+    const int tid = int(threadIdx.x);
+    uint32_t c[per];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        const int b = bins - 1 - (tid * per + q);
+        c[q] = b >= 0 ? h[b] : 0u;
+        if (b >= 0) h[b] = 0;
+        mine += c[q];
+    }
+    uint32_t total;
+    uint32_t run = fin_block_scan(mine, row, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            pick[0] = uint32_t(bins - 1 - (tid * per + q));
+            pick[1] = krem - run;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+}
+
+// Digit D of the radix select over key_at(0 .. len-1): histogram of the
+// keys that match the prefix (wave-aggregated increments for the top
+// digit), then the bin holding the krem-th largest; extends the prefix and
+// reduces krem.  Returns false (uniformly) if no bin holds it.
 template <int D, typename KeyAt>
 __device__ __forceinline__ bool fin_digit(const KeyAt& key_at, int64_t len, uint32_t& prefix,
-                                          uint32_t& krem, uint32_t* h, uint32_t* lds,
+                                          uint32_t& krem, uint32_t* h, uint32_t* row,
                                           uint32_t* pick) {
     constexpr int shift = Digit<D>::shift, bits = Digit<D>::bits;
     constexpr int bins = 1 << bits;
     constexpr uint32_t dmask = uint32_t(bins) - 1u;
-    constexpr int per = (bins + kTsThreads - 1) / kTsThreads;
     const int tid = int(threadIdx.x);
-    for (int b = tid; b < bins; b += kTsThreads) h[b] = 0;
-    if (tid == 0) pick[0] = kNoKey;
-    __syncthreads();
     for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
         uint32_t key[kTsHistUnroll];
 #pragma unroll
@@ -257,27 +338,8 @@ __device__ __forceinline__ bool fin_digit(const KeyAt& key_at, int64_t len, uint
         }
     }
     __syncthreads();
-    uint32_t c[per];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        const int b = bins - 1 - (tid * per + q);
-        c[q] = b >= 0 ? h[b] : 0u;
-        mine += c[q];
-    }
-    uint32_t total;
-    uint32_t run = ts_block_scan(mine, lds, total);
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        if (run < krem && krem <= run + c[q]) {
-            pick[0] = uint32_t(bins - 1 - (tid * per + q));
-            pick[1] = krem - run;
-        }
-        run += c[q];
-    }
-    __syncthreads();
+    fin_pick<bins>(h, krem, row, pick);
     const uint32_t b = pick[0], kr = pick[1];
-    __syncthreads();  // every thread has read pick before the next digit
     if (b == kNoKey) return false;
     prefix = (prefix << bits) | b;
     krem = kr;
@@ -286,21 +348,19 @@ __device__ __forceinline__ bool fin_digit(const KeyAt& key_at, int64_t len, uint
 
 // The top 21 bits of the krem-th largest key among keys_at(0 .. len-1),
 // all of them at least lo21 << 10, from one histogram of (key >> 10) - lo21
-// (wave-aggregated increments; bin 2047 collects everything 2047 bins or
-// more above lo21).  Sets prefix to those 21 bits and reduces krem; returns
-// false (uniformly) when the krem-th key lies in the open top bin, or a key
-// is below lo21 << 10, so that the caller takes the plain digits.
+// (bin 2047 collects everything 2047 bins or more above lo21, counted in
+// registers: most keys of a long list land there).  Sets prefix to those
+// 21 bits and reduces krem; returns false (uniformly) when the krem-th key
+// lies in the open top bin, or a key is below lo21 << 10, so that the
+// caller takes the plain digits.
 template <typename KeyAt>
 __device__ __forceinline__ bool fin_prefix21(const KeyAt& key_at, int64_t len, uint32_t lo21,
                                              uint32_t& prefix, uint32_t& krem, uint32_t* h,
-                                             uint32_t* lds, uint32_t* pick) {
+                                             uint32_t* row, uint32_t* pick) {
     constexpr int bins = kHistBins;  // 2048
-    constexpr int per = bins / kTsThreads;
     const int tid = int(threadIdx.x);
-    for (int b = tid; b < bins; b += kTsThreads) h[b] = 0;
-    if (tid == 0) pick[0] = kNoKey;
-    __syncthreads();
     int below = 0;
+    uint32_t open = 0;
     for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
         uint32_t key[kTsHistUnroll];
 #pragma unroll
@@ -314,46 +374,145 @@ __device__ __forceinline__ bool fin_prefix21(const KeyAt& key_at, int64_t len, u
             const uint32_t p21 = key[q] >> 10;
             below |= in && p21 < lo21;
             const uint32_t d = p21 - lo21;
-            hist_inc(h, d < uint32_t(bins - 1) ? d : uint32_t(bins - 1), in && p21 >= lo21);
+            if (in && p21 >= lo21) {
+                if (d < uint32_t(bins - 1)) atomicAdd(&h[d], 1u);
+                else ++open;
+            }
         }
     }
+    open = lane_value(wave_scan_add(open), kWave - 1);
+    if (lane_id() == 0 && open) atomicAdd(&h[bins - 1], open);
     below = __syncthreads_or(below);
-    uint32_t c[per];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        c[q] = h[bins - 1 - (tid * per + q)];
-        mine += c[q];
-    }
-    uint32_t total;
-    uint32_t run = ts_block_scan(mine, lds, total);
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-        if (run < krem && krem <= run + c[q]) {
-            pick[0] = uint32_t(bins - 1 - (tid * per + q));
-            pick[1] = krem - run;
-        }
-        run += c[q];
-    }
-    __syncthreads();
+    fin_pick<bins>(h, krem, row, pick);
     const uint32_t b = pick[0], kr = pick[1];
-    __syncthreads();  // every thread has read pick before h is reused
     if (below || b == kNoKey || b == uint32_t(bins - 1)) return false;
     prefix = lo21 + b;
     krem = kr;
     return true;
 }
 
+// The krem-th largest of the keys key_at(0 .. len-1), len <= kTsThreads,
+// by counting: thread i compares its key with every other (broadcast LDS
+// reads); the key with g keys above it and e equal, g < krem <= g + e, is
+// the k-th largest.  Sets prefix to that key and krem to krem - g (the keys
+// equal to it that are taken); returns false (uniformly) if none is.
+template <typename KeyAt>
+__device__ __forceinline__ bool fin_direct(const KeyAt& key_at, int64_t len, uint32_t& prefix,
+                                           uint32_t& krem, uint32_t* pick) {
+    const int tid = int(threadIdx.x);
+    if (tid < len) {
+        const uint32_t key = key_at(tid);
+        uint32_t g = 0, e = 0;
+        for (int64_t j = 0; j < len; ++j) {
+            const uint32_t kj = key_at(j);
+            g += kj > key;
+            e += kj == key;
+        }
+        if (g < krem && krem <= g + e) {  // every such thread holds the same key
+            pick[0] = key;
+            pick[1] = krem - g;
+        }
+    }
+    __syncthreads();
+    if (pick[0] == kNoKey) return false;
+    prefix = pick[0];
+    krem = pick[1];
+    return true;
+}
+
+// After fin_prefix21: the keys whose top 21 bits are the prefix (one bin
+// of 1024 key values) copied into lst (wave-aggregated positions from the
+// counter *cnt, zero on entry), then the krem-th largest of them by
+// counting.  Returns 1 with prefix the k-th largest key T and krem the keys
+// equal to it that are taken; 0 if none is; -1 (uniformly) when more than
+// kTsThreads keys share the bin, so that the caller takes digit 2.
+template <typename KeyAt>
+__device__ __forceinline__ int fin_low10(const KeyAt& key_at, int64_t len, uint32_t& prefix,
+                                         uint32_t& krem, uint32_t* lst, uint32_t* cnt,
+                                         uint32_t* pick) {
+    const int tid = int(threadIdx.x);
+    const uint32_t p21 = prefix;
+    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
+        uint32_t key[kTsHistUnroll];
+#pragma unroll
+        for (int q = 0; q < kTsHistUnroll; ++q) {
+            const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
+            key[q] = i < len ? key_at(i) : kNoKey;
+        }
+#pragma unroll
+        for (int q = 0; q < kTsHistUnroll; ++q) {
+            const bool in = key[q] != kNoKey && (key[q] >> 10) == p21;
+            const uint64_t bm = __ballot(in);
+            if (bm) {  // uniform
+                uint32_t base = 0;
+                if (lane_id() == 0) base = atomicAdd(cnt, uint32_t(__popcll(bm)));
+                base = lane_value(base, 0);
+                const uint32_t pos = base + uint32_t(__popcll(bm & lanemask_lt()));
+                if (in && pos < uint32_t(kTsThreads)) lst[pos] = key[q];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t m = *cnt;
+    if (m > uint32_t(kTsThreads)) return -1;
+    return fin_direct([&](int64_t j) -> uint32_t { return lst[j]; }, int64_t(m), prefix, krem,
+                      pick) ? 1 : 0;
+}
+
+// Orders this wave's LDS accesses before its later ones (lanes exchange
+// data through LDS with no block barrier).
+__device__ __forceinline__ void fin_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
+// Exclusive scan over the 1024-thread block with the block total, and
+// whether any thread's flag is set, in one exchange.  `lds` holds
+// 2 kTsWaves values.
+__device__ __forceinline__ uint32_t ts_block_scan_any(uint32_t x, int flag, uint32_t* lds,
+                                                      uint32_t& total, int& any) {
+    const int lane = lane_id();
+    const int wid = int(threadIdx.x) >> 6;
+    const uint32_t inc = wave_scan_add(x);
+    const bool wf = __ballot(flag != 0) != 0;
+    if (lane == kWave - 1) {
+        lds[wid] = inc;
+        lds[kTsWaves + wid] = wf ? 1u : 0u;
+    }
+    __syncthreads();
+    uint32_t wpre = 0, tot = 0, f = 0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w) {
+        const uint32_t s = lds[w];
+        if (w < wid) wpre += s;
+        tot += s;
+        f |= lds[kTsWaves + w];
+    }
+    __syncthreads();
+    total = tot;
+    any = int(f);
+    return wpre + inc - x;
+}
+
 // One 1024-thread workgroup per tensor (grid = T), after k_fused.
-//   1. the tensor's pieces (at most 4096, counts kept in registers):
-//      candidate total and overflow -> the source (the candidate list when
+//   1. the tensor's pieces (at most 4096, up to four consecutive ones per
+//      thread, counts kept in registers; one block scan gives the total and
+//      every piece's offset): candidate total and overflow -> the source
+//      (the candidate list when
 //      no piece overflowed and there are k to capacity of them, else the
 //      whole tensor), as k_group_scan decides it
 //   2. list: the pieces' runs copied in piece order into LDS (index, v,
-//      saved u; lists longer than kFinItems go to the ordered list in
-//      memory instead); whole tensor: the slotted candidates' u and v put
-//      back (the fused pass masked them)
-//   3. three radix digits over the keys -> T and r
+//      saved u; each wave copies the runs of its own threads' pieces, and
+//      finds an item's piece from start-of-run marks; lists longer than
+//      kFinItems go to the ordered list in memory instead, each item
+//      finding its piece by binary search); whole tensor: the slotted
+//      candidates' u and v put back (the fused pass masked them)
+//   3. T and r: lists of at most kFinDirect items in LDS by counting;
+//      else the top 21 bits from one histogram above the window edge, then
+//      the last 10 by counting among the keys that share them (digit 2
+//      when more than 1024 do); else the three radix digits
 //   4. the emit of k_select_tensor: sent items to the outputs in index
 //      order; on the list, the items not sent get u and v back; on the whole
 //      tensor, u = v = +0 at the sent ones
@@ -367,14 +526,21 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     Scalars* __restrict__ sc) {
     __shared__ uint32_t sidx[kFinItems];
     __shared__ float sv[kFinItems];
-    __shared__ float su[kFinItems];
+    // the saved u as bits; before that, the start-of-run marks of the gather
+    __shared__ uint32_t su[kFinItems];
     __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t pre[kFinRounds * kTsThreads];
-    __shared__ uint32_t lds[kTsWaves];
+    __shared__ uint32_t pre[kFinPieces * kTsThreads];
+    __shared__ uint32_t lds[2 * kTsWaves];
     __shared__ uint32_t wcnt[2 * kTsWaves];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t rows[4 * kTsWaves];  // the selection rounds' scan rows
+    __shared__ uint32_t pick[10];            // and picks
+    __shared__ uint32_t lcnt;                // fin_low10's counter
     const int t = blockIdx.x;
     const int tid = int(threadIdx.x);
+    // zero on entry to the selection rounds (barriers follow)
+    for (int b = tid; b < kHistBins; b += kTsThreads) h[b] = 0;
+    if (tid < 10) pick[tid] = kNoKey;
+    if (tid == 0) lcnt = 0;
     const int64_t k = K.k[t];
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t p0 = L.pbase[t], np = L.pbase[t + 1] - p0;
@@ -382,18 +548,22 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     const int64_t cap = L.obase[t + 1] - L.obase[t];
     const uint32_t lo_key = ts[t].lo_key;  // the window's lower edge
     const uint32_t fl = ts[t].floor;       // 0, or the hierarchical floor
-    if (np > int64_t(kFinRounds) * kTsThreads) {  // uniform; the host keeps such layouts off
+    if (np > int64_t(kFinPieces) * kTsThreads) {  // uniform; the host keeps such layouts off
         if (tid == 0) latch_error(sc, kErrInternal);
         return;
     }
-    // 1. candidates and overflow: piece tid + 1024 c is round c's
-    uint32_t cnt[kFinRounds];
+    // 1. candidates and overflow: thread tid owns the consecutive pieces
+    // [q0, q1) (at most kFinPieces, spread evenly over the threads), so one
+    // block scan gives the total and each piece's offset in the list
+    const int64_t q0 = int64_t(tid) * np / kTsThreads;
+    const int64_t q1 = int64_t(tid + 1) * np / kTsThreads;
+    uint32_t cnt[kFinPieces];
     uint32_t mine = 0;
     int over = 0;
 #pragma unroll
-    for (int c = 0; c < kFinRounds; ++c) {
-        const int64_t q = int64_t(c) * kTsThreads + tid;
-        uint32_t x = (k > 0 && q < np) ? run_cnt[p0 + q] : 0u;
+    for (int c = 0; c < kFinPieces; ++c) {
+        const int64_t q = q0 + c;
+        uint32_t x = (k > 0 && q < q1) ? run_cnt[p0 + q] : 0u;
         if (x > pcap) {  // overflowed: no slots, nothing masked
             over = 1;
             x = 0;
@@ -401,9 +571,8 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
         cnt[c] = x;
         mine += x;
     }
-    over = __syncthreads_or(over);
     uint32_t C;
-    ts_block_scan(mine, lds, C);
+    const uint32_t base = ts_block_scan_any(mine, over, lds, C, over);
     const uint32_t mode = select_mode(k, C, over, uint64_t(cap), lo_key, fl);
     // the hierarchical selector's whole survivor list of at most k: all sent
     const bool all = mode == kModeList && send_all(k, C, fl);
@@ -423,57 +592,121 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     }
     const bool list = mode == kModeList;
     const bool in_lds = list && len <= kFinItems;
-    // 2. gather: every round's run offsets first (one block scan a round,
-    // into LDS), then all items at once with consecutive threads on
-    // consecutive items (coalesced), each finding its piece by binary search
-    // over the offsets, kGatherBatch slot loads in flight per thread
+    // 2. gather, into LDS (the list when it fits), else into the ordered
+    // list in memory or back into u and v
+    bool gbad = false;
     if (C > 0) {  // uniform
         const CandSlot* src0 = slots + L.slbase[t];
         const int64_t d0 = L.obase[t];
-        uint32_t carry = 0;
+        uint32_t run = base;
 #pragma unroll
-        for (int c = 0; c < kFinRounds; ++c) {
-            if (int64_t(c) * kTsThreads >= np) break;  // uniform
-            uint32_t ctot;
-            pre[c * kTsThreads + tid] = carry + ts_block_scan(cnt[c], lds, ctot);
-            carry += ctot;
+        for (int c = 0; c < kFinPieces; ++c) {
+            if (q0 + c < q1) pre[q0 + c] = run;
+            run += cnt[c];
         }
-        __syncthreads();
-        const int npi = int(np);
-        for (uint32_t i0 = 0; i0 < C; i0 += kGatherBatch * kTsThreads) {
-            CandSlot it[kGatherBatch];
+        const int lane = lane_id();
+        if (in_lds) {  // uniform
+            // The wave's own pieces hold the list's items [wb, we), and the
+            // first of them starts a run.  Mark each run's start with its
+            // piece + 1 (every other item 0): the running max of the marks
+            // is then the piece of each item.  Marks, offsets and items are
+            // the wave's own: no block barrier.
+            // (every index below is also checked against the buffers, so
+            // that no count can move an access out of them)
+            const uint32_t wb = lane_value(base, 0);
+            const uint32_t we = min(lane_value(base + mine, kWave - 1), uint32_t(kFinItems));
+            for (uint32_t i = wb + uint32_t(lane); i < we; i += kWave) su[i] = 0u;
+            fin_wave_sync();
+            run = base;
 #pragma unroll
-            for (int b = 0; b < kGatherBatch; ++b) {
-                const uint32_t i = i0 + uint32_t(b) * kTsThreads + uint32_t(tid);
-                if (i < C) {
-                    int lo = 0, hi = npi;  // the last piece j with pre[j] <= i
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (pre[mid] <= i) lo = mid; else hi = mid;
+            for (int c = 0; c < kFinPieces; ++c) {
+                if (cnt[c] && run < we) su[run] = uint32_t(q0 + c) + 1u;
+                run += cnt[c];
+            }
+            fin_wave_sync();
+            uint32_t carry = 0;  // the piece + 1 of the item before a round
+            for (uint32_t i0 = wb; i0 < we; i0 += uint32_t(kWave * kGatherBatch)) {
+                // the rounds' running maxima independently, then the carries
+                uint32_t pc[kGatherBatch];
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t i = i0 + uint32_t(b * kWave + lane);
+                    pc[b] = wave_inclusive_max(i < we ? su[i] : 0u);
+                }
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t last = uint32_t(__builtin_amdgcn_readlane(int(pc[b]), kWave - 1));
+                    pc[b] = max(pc[b], carry);  // >= 1 below we
+                    carry = max(carry, last);
+                }
+                CandSlot it[kGatherBatch];
+                bool got[kGatherBatch];
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t i = i0 + uint32_t(b * kWave + lane);
+                    const uint32_t j = pc[b] - 1u;
+                    got[b] = false;
+                    if (i < we && j < uint32_t(np)) {
+                        const uint32_t off = i - pre[j];
+                        got[b] = off < pcap;
+                        if (got[b]) it[b] = src0[int64_t(j) * pcap + off];
                     }
-                    it[b] = src0[int64_t(lo) * pcap + (i - pre[lo])];
+                    if (i < we && !got[b]) gbad = true;
+                }
+                // su[i] (a mark) is read only by the lane that writes it here
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t i = i0 + uint32_t(b * kWave + lane);
+                    if (got[b]) {
+                        sidx[i] = it[b].idx;
+                        sv[i] = it[b].v;
+                        su[i] = __float_as_uint(it[b].u);
+                    }
                 }
             }
+        } else {
+            // Consecutive threads on consecutive items (coalesced), each
+            // finding its piece by binary search over the offsets
+            // (kGatherBatch searches in lockstep), kGatherBatch slot loads
+            // in flight per thread.
+            __syncthreads();
+            const int npi = int(np);
+            for (uint32_t i0 = 0; i0 < C; i0 += kGatherBatch * kTsThreads) {
+                CandSlot it[kGatherBatch];
+                uint32_t is[kGatherBatch];
+                int js[kGatherBatch];
 #pragma unroll
-            for (int b = 0; b < kGatherBatch; ++b) {
-                const uint32_t i = i0 + uint32_t(b) * kTsThreads + uint32_t(tid);
-                if (i >= C) continue;
-                if (in_lds) {
-                    sidx[i] = it[b].idx;
-                    sv[i] = it[b].v;
-                    su[i] = it[b].u;
-                } else if (list) {
-                    olist_i[d0 + i] = it[b].idx;
-                    olist_v[d0 + i] = it[b].v;
-                    olist_u[d0 + i] = it[b].u;
-                } else if (int64_t(it[b].idx) < nt) {
-                    v[o + it[b].idx] = it[b].v;
-                    u[o + it[b].idx] = it[b].u;
+                for (int b = 0; b < kGatherBatch; ++b)
+                    is[b] = i0 + uint32_t(b) * kTsThreads + uint32_t(tid);
+                piece_of(pre, npi, is, js);  // the last piece j with pre[j] <= i
+                bool got[kGatherBatch];
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t off = is[b] - pre[js[b]];
+                    got[b] = is[b] < C && off < pcap;
+                    if (got[b]) it[b] = src0[int64_t(js[b]) * pcap + off];
+                    if (is[b] < C && !got[b]) gbad = true;
+                }
+#pragma unroll
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    const uint32_t i = is[b];
+                    if (!got[b]) continue;
+                    if (list) {
+                        olist_i[d0 + i] = it[b].idx;
+                        olist_v[d0 + i] = it[b].v;
+                        olist_u[d0 + i] = it[b].u;
+                    } else if (int64_t(it[b].idx) < nt) {
+                        v[o + it[b].idx] = it[b].v;
+                        u[o + it[b].idx] = it[b].u;
+                    }
                 }
             }
         }
     }
-    __syncthreads();
+    if (__syncthreads_or(gbad)) {  // uniform: counts that do not add up
+        if (tid == 0) latch_error(sc, kErrInternal);
+        return;
+    }
     // 3. the three digits
     const float* srcv = list ? olist_v + L.obase[t] : v + o;
     auto val_at = [&](int64_t i) -> float { return in_lds ? sv[i] : srcv[i]; };
@@ -484,15 +717,27 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
     uint32_t prefix = 0, krem = 0;
     if (!all) {  // uniform
         krem = uint32_t(k);
-        bool ok = list && lo_key != kNoKey &&
-                  fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, lds, pick);
-        if (!ok) {  // uniform
-            prefix = 0;
-            krem = uint32_t(k);
-            ok = fin_digit<0>(key_at, len, prefix, krem, h, lds, pick);
-            ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, lds, pick);
+        bool ok;
+        if (in_lds && len <= kFinDirect) {  // uniform: a short list
+            ok = fin_direct(key_at, len, prefix, krem, pick);
+        } else {
+            ok = list && lo_key != kNoKey &&
+                 fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, rows, pick);
+            int low = -1;  // the last 10 bits: by counting within the prefix's bin
+            if (ok) {  // uniform; pre is free after the gather
+                low = fin_low10(key_at, len, prefix, krem, pre, &lcnt, pick + 8);
+                ok = low != 0;
+            } else {
+                prefix = 0;
+                krem = uint32_t(k);
+                ok = fin_digit<0>(key_at, len, prefix, krem, h, rows + kTsWaves, pick + 2);
+                ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, rows + 2 * kTsWaves,
+                                        pick + 4);
+            }
+            if (low < 0)  // uniform
+                ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, rows + 3 * kTsWaves,
+                                        pick + 6);
         }
-        ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, lds, pick);
         if (!ok) {  // uniform
             if (tid == 0) latch_error(sc, kErrInternal);
             return;
@@ -558,7 +803,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
             usv[q] = 0.0f;
             if (!dense && in[q]) {  // the list's index and saved u
                 lidx[q] = in_lds ? sidx[i] : oli[i];
-                usv[q] = in_lds ? su[i] : olu[i];
+                usv[q] = in_lds ? __uint_as_float(su[i]) : olu[i];
             }
         }
 #pragma unroll
