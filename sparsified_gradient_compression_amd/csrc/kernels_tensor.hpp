@@ -49,6 +49,11 @@ constexpr int kFinEmitUnroll = 4;  // 64-item rounds loaded together per wave
 // Lists in LDS of at most this many items select by counting (fin_direct).
 constexpr int kFinDirect = 128;
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // Inclusive scans over the wave with DPP moves (row_shr 1, 2, 4, 8 within
 // each 16-lane row, then row_bcast 15 and 31 across rows): six ALU steps in
 // place of six LDS-routed shuffles.  A lane a move cannot reach gets 0,
@@ -635,7 +640,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
                 }
 #pragma unroll
                 for (int b = 0; b < kGatherBatch; ++b) {
-                    const uint32_t last = uint32_t(__builtin_amdgcn_readlane(int(pc[b]), kWave - 1));
+                    const uint32_t last = lane_value(pc[b], kWave - 1);
                     pc[b] = max(pc[b], carry);  // >= 1 below we
                     carry = max(carry, last);
                 }
@@ -707,141 +712,156 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
         if (tid == 0) latch_error(sc, kErrInternal);
         return;
     }
-    // 3. the three digits
-    const float* srcv = list ? olist_v + L.obase[t] : v + o;
-    auto val_at = [&](int64_t i) -> float { return in_lds ? sv[i] : srcv[i]; };
-    auto key_at = [&](int64_t i) -> uint32_t { return floor_key(mag_key(val_at(i)), fl); };
-    // On the list, every key is at least the window's lower edge lo: the top
-    // 21 bits of T come from one histogram of (key >> 10) - (lo >> 10) when
-    // they lie within 2046 bins of lo's, else from the first two digits.
-    uint32_t prefix = 0, krem = 0;
-    if (!all) {  // uniform
-        krem = uint32_t(k);
-        bool ok;
-        if (in_lds && len <= kFinDirect) {  // uniform: a short list
-            ok = fin_direct(key_at, len, prefix, krem, pick);
-        } else {
-            ok = list && lo_key != kNoKey &&
-                 fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, rows, pick);
-            int low = -1;  // the last 10 bits: by counting within the prefix's bin
-            if (ok) {  // uniform; pre is free after the gather
-                low = fin_low10(key_at, len, prefix, krem, pre, &lcnt, pick + 8);
-                ok = low != 0;
+    // Phases 3 and 4 are compiled twice, for the list in LDS and for items
+    // in memory, so that every read goes to its own memory (a pointer that
+    // could be either becomes a generic load waited for one at a time).
+    auto finish = [&](auto lds_tag) {
+        constexpr bool kLds = decltype(lds_tag)::value;
+        // 3. T and r
+        const float* srcv = list ? olist_v + L.obase[t] : v + o;
+        auto val_at = [&](int64_t i) -> float {
+            if constexpr (kLds) return sv[i]; else return srcv[i];
+        };
+        auto key_at = [&](int64_t i) -> uint32_t { return floor_key(mag_key(val_at(i)), fl); };
+        // On the list, every key is at least the window's lower edge lo: the top
+        // 21 bits of T come from one histogram of (key >> 10) - (lo >> 10) when
+        // they lie within 2046 bins of lo's, else from the first two digits.
+        uint32_t prefix = 0, krem = 0;
+        if (!all) {  // uniform
+            krem = uint32_t(k);
+            bool ok;
+            if (kLds && len <= kFinDirect) {  // uniform: a short list
+                ok = fin_direct(key_at, len, prefix, krem, pick);
             } else {
-                prefix = 0;
-                krem = uint32_t(k);
-                ok = fin_digit<0>(key_at, len, prefix, krem, h, rows + kTsWaves, pick + 2);
-                ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, rows + 2 * kTsWaves,
-                                        pick + 4);
-            }
-            if (low < 0)  // uniform
-                ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, rows + 3 * kTsWaves,
-                                        pick + 6);
-        }
-        if (!ok) {  // uniform
-            if (tid == 0) latch_error(sc, kErrInternal);
-            return;
-        }
-        krem = last_rank<2>(prefix, krem, fl);
-    }
-    if (tid == 0) {
-        ts[t].prefix = prefix;
-        ts[t].krem = krem;
-    }
-    // 4. emit in index order: wave w owns items [c0, c1), a run of whole
-    // 64-item rounds; a count pass gives every wave its output offsets
-    const uint32_t T = prefix, r = krem;
-    const bool dense = !list;
-    const int lane = lane_id(), w = tid >> 6;
-    const int64_t rounds = (len + kWave - 1) / kWave;
-    const int64_t rpw = (rounds + kTsWaves - 1) / kTsWaves;
-    const int64_t c0 = min(len, int64_t(w) * rpw * kWave);
-    const int64_t c1 = min(len, int64_t(w + 1) * rpw * kWave);
-    constexpr int64_t kStep = int64_t(kWave) * kFinEmitUnroll;
-    uint32_t ng = 0, ne = 0;
-    for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
-        uint32_t kk[kFinEmitUnroll];
-#pragma unroll
-        for (int q = 0; q < kFinEmitUnroll; ++q) {
-            const int64_t i = b0 + int64_t(q) * kWave + lane;
-            kk[q] = i < c1 ? key_at(i) : kNoKey;
-        }
-#pragma unroll
-        for (int q = 0; q < kFinEmitUnroll; ++q) {
-            ng += uint32_t(__popcll(__ballot(kk[q] != kNoKey && kk[q] > T)));
-            ne += uint32_t(__popcll(__ballot(kk[q] == T)));
-        }
-    }
-    if (lane == 0) {
-        wcnt[w] = ng;
-        wcnt[kTsWaves + w] = ne;
-    }
-    __syncthreads();
-    uint32_t gb = 0, eb = 0;
-    for (int j = 0; j < w; ++j) {
-        gb += wcnt[j];
-        eb += wcnt[kTsWaves + j];
-    }
-    if (out_count && tid == 0) out_count[t] = sent_count(wcnt, r);
-    float* vt_ = v + o;
-    const uint32_t* oli = olist_i + L.obase[t];
-    const float* olu = olist_u + L.obase[t];
-    uint32_t* oi = out_idx + K.koff[t];
-    float* ov = out_val + K.koff[t];
-    const uint64_t lt = lanemask_lt();
-    bool bad = false;
-    for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
-        float val[kFinEmitUnroll], usv[kFinEmitUnroll];
-        uint32_t lidx[kFinEmitUnroll];
-        bool in[kFinEmitUnroll];
-#pragma unroll
-        for (int q = 0; q < kFinEmitUnroll; ++q) {
-            const int64_t i = b0 + int64_t(q) * kWave + lane;
-            in[q] = i < c1;
-            val[q] = in[q] ? val_at(i) : 0.0f;
-            lidx[q] = uint32_t(i);
-            usv[q] = 0.0f;
-            if (!dense && in[q]) {  // the list's index and saved u
-                lidx[q] = in_lds ? sidx[i] : oli[i];
-                usv[q] = in_lds ? __uint_as_float(su[i]) : olu[i];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kFinEmitUnroll; ++q) {
-            const uint32_t key = floor_key(mag_key(val[q]), fl);
-            const bool gt = in[q] && key > T, eq = in[q] && key == T;
-            const uint64_t bg = __ballot(gt), be = __ballot(eq);
-            const uint32_t g1 = gb + uint32_t(__popcll(bg & lt));
-            const uint32_t e1 = eb + uint32_t(__popcll(be & lt));
-            bool send = false;
-            uint32_t slot = 0;
-            if (gt) { send = true; slot = g1 + min(e1, r); }
-            else if (eq && e1 < r) { send = true; slot = g1 + e1; }
-            if (send) {
-                // never write outside the outputs, whatever the counts say
-                if (int64_t(slot) >= k || int64_t(lidx[q]) >= nt) {
-                    bad = true;
+                ok = list && lo_key != kNoKey &&
+                     fin_prefix21(key_at, len, lo_key >> 10, prefix, krem, h, rows, pick);
+                int low = -1;  // the last 10 bits: by counting within the prefix's bin
+                if (ok) {  // uniform; pre is free after the gather
+                    low = fin_low10(key_at, len, prefix, krem, pre, &lcnt, pick + 8);
+                    ok = low != 0;
                 } else {
-                    oi[slot] = lidx[q];
-                    ov[slot] = val[q];
-                    if (dense) {
-                        u[o + lidx[q]] = 0.0f;
-                        vt_[lidx[q]] = 0.0f;
+                    prefix = 0;
+                    krem = uint32_t(k);
+                    ok = fin_digit<0>(key_at, len, prefix, krem, h, rows + kTsWaves, pick + 2);
+                    ok = ok && fin_digit<1>(key_at, len, prefix, krem, h, rows + 2 * kTsWaves,
+                                            pick + 4);
+                }
+                if (low < 0)  // uniform
+                    ok = ok && fin_digit<2>(key_at, len, prefix, krem, h, rows + 3 * kTsWaves,
+                                            pick + 6);
+            }
+            if (!ok) {  // uniform
+                if (tid == 0) latch_error(sc, kErrInternal);
+                return;
+            }
+            krem = last_rank<2>(prefix, krem, fl);
+        }
+        if (tid == 0) {
+            ts[t].prefix = prefix;
+            ts[t].krem = krem;
+        }
+        // 4. emit in index order: wave w owns items [c0, c1), a run of whole
+        // 64-item rounds; a count pass gives every wave its output offsets
+        const uint32_t T = prefix, r = krem;
+        const bool dense = !list;
+        const int lane = lane_id(), w = tid >> 6;
+        const int64_t rounds = (len + kWave - 1) / kWave;
+        const int64_t rpw = (rounds + kTsWaves - 1) / kTsWaves;
+        const int64_t c0 = min(len, int64_t(w) * rpw * kWave);
+        const int64_t c1 = min(len, int64_t(w + 1) * rpw * kWave);
+        constexpr int64_t kStep = int64_t(kWave) * kFinEmitUnroll;
+        uint32_t ng = 0, ne = 0;
+        for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
+            uint32_t kk[kFinEmitUnroll];
+    #pragma unroll
+            for (int q = 0; q < kFinEmitUnroll; ++q) {
+                const int64_t i = b0 + int64_t(q) * kWave + lane;
+                kk[q] = i < c1 ? key_at(i) : kNoKey;
+            }
+    #pragma unroll
+            for (int q = 0; q < kFinEmitUnroll; ++q) {
+                ng += uint32_t(__popcll(__ballot(kk[q] != kNoKey && kk[q] > T)));
+                ne += uint32_t(__popcll(__ballot(kk[q] == T)));
+            }
+        }
+        if (lane == 0) {
+            wcnt[w] = ng;
+            wcnt[kTsWaves + w] = ne;
+        }
+        __syncthreads();
+        uint32_t gb = 0, eb = 0;
+        for (int j = 0; j < w; ++j) {
+            gb += wcnt[j];
+            eb += wcnt[kTsWaves + j];
+        }
+        if (out_count && tid == 0) out_count[t] = sent_count(wcnt, r);
+        float* vt_ = v + o;
+        const uint32_t* oli = olist_i + L.obase[t];
+        const float* olu = olist_u + L.obase[t];
+        uint32_t* oi = out_idx + K.koff[t];
+        float* ov = out_val + K.koff[t];
+        const uint64_t lt = lanemask_lt();
+        bool bad = false;
+        for (int64_t b0 = c0; b0 < c1; b0 += kStep) {
+            float val[kFinEmitUnroll], usv[kFinEmitUnroll];
+            uint32_t lidx[kFinEmitUnroll];
+            bool in[kFinEmitUnroll];
+    #pragma unroll
+            for (int q = 0; q < kFinEmitUnroll; ++q) {
+                const int64_t i = b0 + int64_t(q) * kWave + lane;
+                in[q] = i < c1;
+                val[q] = in[q] ? val_at(i) : 0.0f;
+                lidx[q] = uint32_t(i);
+                usv[q] = 0.0f;
+                if (!dense && in[q]) {  // the list's index and saved u
+                    if constexpr (kLds) {
+                        lidx[q] = sidx[i];
+                        usv[q] = __uint_as_float(su[i]);
+                    } else {
+                        lidx[q] = oli[i];
+                        usv[q] = olu[i];
                     }
                 }
-            } else if (in[q] && !dense) {
-                if (int64_t(lidx[q]) >= nt) {
-                    bad = true;
-                } else {
-                    u[o + lidx[q]] = usv[q];
-                    vt_[lidx[q]] = val[q];
-                }
             }
-            gb += uint32_t(__popcll(bg));
-            eb += uint32_t(__popcll(be));
+    #pragma unroll
+            for (int q = 0; q < kFinEmitUnroll; ++q) {
+                const uint32_t key = floor_key(mag_key(val[q]), fl);
+                const bool gt = in[q] && key > T, eq = in[q] && key == T;
+                const uint64_t bg = __ballot(gt), be = __ballot(eq);
+                const uint32_t g1 = gb + uint32_t(__popcll(bg & lt));
+                const uint32_t e1 = eb + uint32_t(__popcll(be & lt));
+                bool send = false;
+                uint32_t slot = 0;
+                if (gt) { send = true; slot = g1 + min(e1, r); }
+                else if (eq && e1 < r) { send = true; slot = g1 + e1; }
+                if (send) {
+                    // never write outside the outputs, whatever the counts say
+                    if (int64_t(slot) >= k || int64_t(lidx[q]) >= nt) {
+                        bad = true;
+                    } else {
+                        oi[slot] = lidx[q];
+                        ov[slot] = val[q];
+                        if (dense) {
+                            u[o + lidx[q]] = 0.0f;
+                            vt_[lidx[q]] = 0.0f;
+                        }
+                    }
+                } else if (in[q] && !dense) {
+                    if (int64_t(lidx[q]) >= nt) {
+                        bad = true;
+                    } else {
+                        u[o + lidx[q]] = usv[q];
+                        vt_[lidx[q]] = val[q];
+                    }
+                }
+                gb += uint32_t(__popcll(bg));
+                eb += uint32_t(__popcll(be));
+            }
         }
-    }
-    if (bad) latch_error(sc, kErrInternal);
+        if (bad) latch_error(sc, kErrInternal);
+    };
+    if (in_lds) finish(BoolTag<true>{});  // uniform
+    else finish(BoolTag<false>{});
 }
 
 }  // namespace dgc
