@@ -83,6 +83,24 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
     return uint32_t(__builtin_amdgcn_readlane(int(x), lane));
 }
 
+// Exclusive scan over the block; `row` (kTsWaves words) is not reused.
+__device__ __forceinline__ uint32_t fin_block_scan(uint32_t x, uint32_t* row, uint32_t& total) {
+    const int lane = lane_id();
+    const int wid = int(threadIdx.x) >> 6;
+    const uint32_t inc = wave_scan_add(x);
+    if (lane == kWave - 1) row[wid] = inc;
+    __syncthreads();
+    uint32_t wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w) {
+        const uint32_t s = row[w];
+        if (w < wid) wpre += s;
+        tot += s;
+    }
+    total = tot;
+    return wpre + inc - x;
+}
+
 // S = the binary64 sum of the norm partials in k_norm_final's order: its
 // 256 threads are this block's first four waves, each summing a strided
 // share, then a butterfly per wave and the four wave sums in order.  The
@@ -120,7 +138,8 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
     double clip, int clip_on, Scalars* __restrict__ sc, double* __restrict__ out_norm,
     float* __restrict__ out_scale, TensorState* __restrict__ ts, float m, int force_dense) {
     __shared__ uint32_t h[kBins0];
-    __shared__ uint32_t lds[kTsWaves];
+    __shared__ uint32_t h1[1024];
+    __shared__ uint32_t rows[2 * kTsWaves];  // one scan row per level
     __shared__ uint32_t pick[2];
     __shared__ double dl[kWavesPerBlock];
     const int t = blockIdx.x;
@@ -129,7 +148,10 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t ls = wlines[t];  // at most kWtRounds * kWtLinesPerRound
     const bool active = k > 0 && !force_dense && ls > 0 && nt > 0;  // uniform
+    // zero on entry (a barrier follows before any use)
     for (int b = tid; b < kBins0; b += kTsThreads) h[b] = 0;
+    for (int b = tid; b < 1024; b += kTsThreads) h1[b] = 0;
+    if (tid == 0) pick[0] = kNoKey;
     // Sampled line j (j < ls) starts at line j * stride + mix32(j * 0x9E3779B9
     // ^ t * 0x7F4A7C15) mod stride; stride = 1 samples every line.  Lane gl of
     // the 8-lane group grp takes elements 4 gl .. 4 gl + 3 of lines grp,
@@ -188,7 +210,7 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
             if (out_norm) *out_norm = -1.0;
             if (out_scale) *out_scale = 1.0f;
         }
-        __syncthreads();  // h cleared
+        __syncthreads();  // h, h1 and pick cleared
     }
     if (tid == 0) {
         ts[t].lo_key = kNoKey;
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
     // thread tid owns bins 2047 - 2 tid and 2046 - 2 tid (descending)
     const uint32_t c0 = h[kBins0 - 1 - 2 * tid], c1 = h[kBins0 - 2 - 2 * tid];
     uint32_t total;
-    const uint32_t above = ts_block_scan(c0 + c1, lds, total);
+    const uint32_t above = fin_block_scan(c0 + c1, rows, total);
     const double mu = double(total) * double(k) / double(nt);
     const double jd = ceil(mu + 4.0 * sqrt(mu) + 6.0);
     if (jd > double(total)) {  // uniform: (nearly) everything is a candidate
@@ -224,8 +246,6 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
         return;
     }
     const uint32_t j = uint32_t(jd);
-    if (tid == 0) pick[0] = kNoKey;
-    __syncthreads();
     if (above < j && j <= above + c0) {
         pick[0] = uint32_t(kBins0 - 1 - 2 * tid);
         pick[1] = above;
@@ -237,18 +257,16 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
     const uint32_t wbin = pick[0], wabove = pick[1];
     if (wbin == kNoKey) return;  // uniform; cannot happen when j <= total
     // level 1: the next 10 bits of the keys in bin wbin
-    for (int b = tid; b < 1024; b += kTsThreads) h[b] = 0;
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < kWtRounds; ++r)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
             if (key[r][c4] != kNoKey && (key[r][c4] >> 20) == wbin)
-                atomicAdd(&h[(key[r][c4] >> 10) & 1023u], 1u);
+                atomicAdd(&h1[(key[r][c4] >> 10) & 1023u], 1u);
     __syncthreads();
-    const uint32_t c2 = h[1023 - tid];
+    const uint32_t c2 = h1[1023 - tid];
     uint32_t tot1;
-    const uint32_t ab1 = ts_block_scan(c2, lds, tot1);
+    const uint32_t ab1 = fin_block_scan(c2, rows + kTsWaves, tot1);
     const uint32_t jr = j - wabove;
     if (ab1 < jr && jr <= ab1 + c2) {
         ts[t].lo_key = (wbin << 20) | (uint32_t(1023 - tid) << 10);
@@ -265,23 +283,6 @@ __global__ __launch_bounds__(kTsThreads) void k_window_tensor(
 // on entry), so nothing needs a barrier before reuse: a round costs three
 // barriers (counts done; wave sums posted; pick posted).
 
-// Exclusive scan over the block; `row` (kTsWaves words) is not reused.
-__device__ __forceinline__ uint32_t fin_block_scan(uint32_t x, uint32_t* row, uint32_t& total) {
-    const int lane = lane_id();
-    const int wid = int(threadIdx.x) >> 6;
-    const uint32_t inc = wave_scan_add(x);
-    if (lane == kWave - 1) row[wid] = inc;
-    __syncthreads();
-    uint32_t wpre = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kTsWaves; ++w) {
-        const uint32_t s = row[w];
-        if (w < wid) wpre += s;
-        tot += s;
-    }
-    total = tot;
-    return wpre + inc - x;
-}
 
 // After the counts are in h[0, bins): the bin, counted from the top, that
 // holds the krem-th largest, into pick; the bins are zeroed again.
