@@ -191,16 +191,32 @@ __device__ __forceinline__ int find_seg(const int64_t* __restrict__ base,
     return lo;
 }
 
-// Inclusive scan within a wave (Hillis-Steele with shuffles).
+// Inclusive scan within a wave.  32-bit integers: DPP moves (row_shr 1, 2,
+// 4, 8 within each 16-lane row, then row_bcast 15 and 31 across rows), six
+// ALU steps; a lane a move cannot reach gets 0.  Wider types: Hillis-Steele
+// with shuffles (each routed through the LDS crossbar).
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T x) {
-    const int lane = lane_id();
+    if constexpr (sizeof(T) == 4) {
+#define DGC_DPP_ADD(ctrl, rows) \
+    x += T(__builtin_amdgcn_update_dpp(0, int(x), (ctrl), (rows), 0xF, true))
+        DGC_DPP_ADD(0x111, 0xF);  // row_shr:1
+        DGC_DPP_ADD(0x112, 0xF);  // row_shr:2
+        DGC_DPP_ADD(0x114, 0xF);  // row_shr:4
+        DGC_DPP_ADD(0x118, 0xF);  // row_shr:8
+        DGC_DPP_ADD(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+        DGC_DPP_ADD(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef DGC_DPP_ADD
+        return x;
+    } else {
+        const int lane = lane_id();
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
+        for (int d = 1; d < kWave; d <<= 1) {
+            T y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        return x;
     }
-    return x;
 }
 
 // Exclusive scan across the 256-thread block.  `lds` holds kWavesPerBlock

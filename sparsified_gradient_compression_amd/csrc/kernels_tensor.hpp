@@ -54,21 +54,10 @@ struct BoolTag {
     static constexpr bool value = B;
 };
 
-// Inclusive scans over the wave with DPP moves (row_shr 1, 2, 4, 8 within
-// each 16-lane row, then row_bcast 15 and 31 across rows): six ALU steps in
-// place of six LDS-routed shuffles.  A lane a move cannot reach gets 0,
-// the identity of both operations here.
+// Inclusive max over the wave with the DPP moves of wave_inclusive_scan; a
+// lane a move cannot reach gets 0, the identity here.
 #define DGC_DPP(x, ctrl, rows) \
     uint32_t(__builtin_amdgcn_update_dpp(0, int(x), (ctrl), (rows), 0xF, true))
-__device__ __forceinline__ uint32_t wave_scan_add(uint32_t x) {
-    x += DGC_DPP(x, 0x111, 0xF);  // row_shr:1
-    x += DGC_DPP(x, 0x112, 0xF);  // row_shr:2
-    x += DGC_DPP(x, 0x114, 0xF);  // row_shr:4
-    x += DGC_DPP(x, 0x118, 0xF);  // row_shr:8
-    x += DGC_DPP(x, 0x142, 0xA);  // row_bcast:15 into rows 1 and 3
-    x += DGC_DPP(x, 0x143, 0xC);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
 __device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t x) {
     x = max(x, DGC_DPP(x, 0x111, 0xF));
     x = max(x, DGC_DPP(x, 0x112, 0xF));
@@ -87,7 +76,7 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
 __device__ __forceinline__ uint32_t fin_block_scan(uint32_t x, uint32_t* row, uint32_t& total) {
     const int lane = lane_id();
     const int wid = int(threadIdx.x) >> 6;
-    const uint32_t inc = wave_scan_add(x);
+    const uint32_t inc = wave_inclusive_scan(x);
     if (lane == kWave - 1) row[wid] = inc;
     __syncthreads();
     uint32_t wpre = 0, tot = 0;
@@ -386,7 +375,7 @@ __device__ __forceinline__ bool fin_prefix21(const KeyAt& key_at, int64_t len, u
             }
         }
     }
-    open = lane_value(wave_scan_add(open), kWave - 1);
+    open = lane_value(wave_inclusive_scan(open), kWave - 1);
     if (lane_id() == 0 && open) atomicAdd(&h[bins - 1], open);
     below = __syncthreads_or(below);
     fin_pick<bins>(h, krem, row, pick);
@@ -481,7 +470,7 @@ __device__ __forceinline__ uint32_t ts_block_scan_any(uint32_t x, int flag, uint
                                                       uint32_t& total, int& any) {
     const int lane = lane_id();
     const int wid = int(threadIdx.x) >> 6;
-    const uint32_t inc = wave_scan_add(x);
+    const uint32_t inc = wave_inclusive_scan(x);
     const bool wf = __ballot(flag != 0) != 0;
     if (lane == kWave - 1) {
         lds[wid] = inc;
