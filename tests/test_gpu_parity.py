@@ -489,6 +489,49 @@ def test_empty_layout():
 
 
 @pytest.mark.parametrize("grid", GRIDS)
+def test_threshold_bin_crowded(grid):
+    """T inside a cluster of keys that share their top 21 bits (values 1.0 +
+    i ulp, i < 1000, each three times): on the per-tensor kernels the keys of
+    T's 21-bit bin are too many (> 1024) to count one by one, so the last
+    digit pass decides T and r; a candidate list that fits in LDS (3100
+    items), one in memory (12100 items, above the 10240 that fit), and a
+    short list (at most 128 candidates, selected by counting) with ties at
+    T, against the oracle bit for bit."""
+    rng = np.random.default_rng(77)
+    sizes = [100000, 300000, 20000]
+    n = sum(sizes)
+    g = np.zeros(n, np.float32)
+    one = np.float32(1.0).view(np.uint32)
+
+    def cluster(lo, size, count, above):
+        pos = lo + rng.permutation(size)[:count + above]
+        ulps = np.arange(count) % 1000
+        g[pos[:count]] = (one + ulps.astype(np.uint32)).view(np.float32)
+        g[pos[:count]] *= rng.choice(np.float32([-1, 1]), count)
+        g[pos[count:]] = np.float32(2.0)
+
+    cluster(0, 100000, 3000, 100)
+    cluster(100000, 300000, 12000, 100)
+    # the short list: 100 keys at 0.5 and 20 at 0.75, k = 40 (20 ties sent)
+    pos = 400000 + rng.permutation(20000)[:120]
+    g[pos[:100]] = 0.5
+    g[pos[100:]] = 0.75
+    k = [1200, 4000, 40]
+    p = Pair(sizes, k)
+    p.learner.set_option(dgc.DGC_OPT_SELECT_GRID, grid)
+    got, (o_idx, o_val) = p.step(g, k, 0.0, tag=f"crowded g{grid}")
+    compare_streams(gpu_streams(p, k), oracle_streams(sizes, k, o_idx, o_val),
+                    tag=f"crowded g{grid}")
+    info = p.learner.select_info()
+    # the spread passes take tensors of at most 65536 elements densely
+    assert info[:, 0].tolist() == ([1, 1, 1] if grid == 1 else [1, 1, 2]), info.tolist()
+    assert info[0, 2] == 3100 and info[1, 2] == 12100, info.tolist()
+    if grid == 1:
+        assert info[2, 2] == 120, info.tolist()
+    assert info[2, 4] == np.float32(0.5).view(np.uint32) and info[2, 5] == 20, info.tolist()
+
+
+@pytest.mark.parametrize("grid", GRIDS)
 def test_dense_fallback_after_masking(grid):
     """The element-wise pass stores the window's candidates as +0 in every
     piece whose run fits its slots.  A tensor whose candidates then turn out
