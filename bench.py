@@ -567,14 +567,17 @@ class Run:
         return elapsed, step_ms, fused
 
     def measure(self, first, steps):
-        """Untimed pass with every library timer on, read after each step:
-        per (step, learner) compress and element-wise ms, per step encode
-        (mean over learners) and decode ms.  Returns lists and the k of each
-        measured step."""
+        """Untimed passes over the same steps, the library's timers read
+        after each step.  The first brackets each call (compress, encode,
+        decode); the second only the element-wise pass, since events inside a
+        compress call would add their own overhead to it.  Per (step,
+        learner) compress and element-wise ms, per step encode (mean over
+        learners) and decode ms.  Returns lists and the k of each measured
+        step."""
         dgc = self.dgc
         self.drain_timers()
-        self.set_timing(1)
         rec = {"compress": [], "fused": [], "encode": [], "decode": [], "k": [], "rows": []}
+        self.set_timing(3)
         for i in range(steps):
             self.step(first + i)
             k = self.k_of_step(first + i)
@@ -582,12 +585,9 @@ class Run:
             enc, rows, dec = [], [], None
             for w, L in enumerate(self.learners):
                 c, nc = L.kernel_time(dgc.DGC_TIMER_COMPRESS)
-                f, nf = L.kernel_time(dgc.DGC_TIMER_FUSED)
                 e, ne = L.kernel_time(dgc.DGC_TIMER_ENCODE)
                 d, nd = L.kernel_time(dgc.DGC_TIMER_DECODE)
                 rec["compress"].append((i, c / max(nc, 1)))
-                if nf:
-                    rec["fused"].append((i, f / nf))
                 if ne:
                     enc.append(e / ne)
                 if nd:
@@ -600,13 +600,21 @@ class Run:
                              "learner": w, "k": int(sum(k)), "sent": sent,
                              "stream_entries": int(L.entries.sum()) if ne else None,
                              "compress_ms": round(c / max(nc, 1), 5),
-                             "k_fused_ms": round(f / nf, 5) if nf else None,
+                             "k_fused_ms": None,
                              "encode_ms": round(e / ne, 5) if ne else None})
             for r in rows:
                 r["decode_ms_all_learners"] = round(dec, 5) if dec is not None else None
             rec["rows"].extend(rows)
             if enc:
                 rec["encode"].append(sum(enc) / len(enc))
+        self.set_timing(2)
+        for i in range(steps):
+            self.step(first + i)
+            for w, L in enumerate(self.learners):
+                f, nf = L.kernel_time(dgc.DGC_TIMER_FUSED)
+                if nf:
+                    rec["fused"].append((i, f / nf))
+                    rec["rows"][i * len(self.learners) + w]["k_fused_ms"] = round(f / nf, 5)
         self.set_timing(0)
         self.check()
         return rec
@@ -651,13 +659,17 @@ def write_records(path, wl, selector, rows):
             f.write(json.dumps(out) + "\n")
 
 
-def workload_record(run, steps, warmup, measure_steps, timers):
+def workload_record(run, steps, warmup, measure_steps):
     """Whole-step throughput over `steps` timed steps, then the measurement
     pass; the per-density compress figures when k changes per step."""
     wl = run.wl
     for s in range(warmup):
         run.step(s)
-    elapsed, step_ms, fused = run.timed(warmup, steps, timers)
+    # no library timers in this timed region (the element-wise pass is
+    # timed in the measurement pass): an event record between two kernels
+    # delays the second by a few microseconds, a visible share of a small
+    # workload's step
+    elapsed, step_ms, fused = run.timed(warmup, steps, "off")
     rec = run.measure(warmup + steps, measure_steps)
     comp = [c for _, c in rec["compress"]]
     by_step = {}
@@ -906,7 +918,7 @@ def main():
             owl = W.get(name)
             orun = Run(owl, "topk", args, owl.steps)
             r, _, _, _, orec = workload_record(orun, steps, owl.steps, 2 * owl.steps
-                                               if owl.steps > 1 else 10, args.timers)
+                                               if owl.steps > 1 else 10)
             if args.records:
                 write_records(args.records, owl, "topk", orec["rows"])
             orun.close()

@@ -67,7 +67,12 @@ extern "C" {
                                    HIP events on the call's stream (read with
                                    dgc_get_kernel_time); 2: only the
                                    element-wise pass (DGC_TIMER_FUSED, two
-                                   events per compress call); 0: off
+                                   events per compress call); 3: each call,
+                                   but not its element-wise pass (an event
+                                   record between two kernels delays the
+                                   second by a few microseconds, so mode 1's
+                                   DGC_TIMER_COMPRESS includes that
+                                   overhead and mode 3's does not); 0: off
                                    (default) */
 #define DGC_OPT_DECODE_PATH 3   /* dgc_decode_accumulate, per tensor: 0
                                    automatic (default: merged when the

@@ -427,7 +427,8 @@ int timer_collect(Timer& tm, int slot) {
 }
 
 bool timer_on(const dgc_state* st, int which) {
-    return st->timing == 1 || (st->timing == 2 && which == DGC_TIMER_FUSED);
+    return st->timing == 1 || (st->timing == 2 && which == DGC_TIMER_FUSED) ||
+           (st->timing == 3 && which != DGC_TIMER_FUSED);
 }
 
 int timer_begin(dgc_state* st, int which, hipStream_t s) {
@@ -1575,7 +1576,7 @@ int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
         return DGC_OK;
     }
     if (option == DGC_OPT_KERNEL_TIMING) {
-        if (value < 0 || value > 2) return DGC_EINVAL;
+        if (value < 0 || value > 3) return DGC_EINVAL;
         st->timing = int(value);
         return DGC_OK;
     }

@@ -464,6 +464,17 @@ def test_kernel_timers():
     assert (n_f, n_c, n_e) == (3, 3, 3)
     assert 0 < ms_f < ms_c and ms_e > 0
     assert L.kernel_time(dgc.DGC_TIMER_FUSED) == (0.0, 0)  # read resets
+    # mode 2: the element-wise pass only; mode 3: each call but not that pass
+    for mode, want in ((2, (2, 0, 0)), (3, (0, 2, 2))):
+        L.set_option(dgc.DGC_OPT_KERNEL_TIMING, mode)
+        for _ in range(2):
+            L.compress(g, k, wl.clip)
+            L.encode(k)
+        got = tuple(L.kernel_time(t)[1] for t in (dgc.DGC_TIMER_FUSED, dgc.DGC_TIMER_COMPRESS,
+                                                 dgc.DGC_TIMER_ENCODE))
+        assert got == want, (mode, got)
+    with pytest.raises(dgc.DGCError):
+        L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 4)
     L.set_option(dgc.DGC_OPT_KERNEL_TIMING, 0)
 
 
