@@ -955,6 +955,14 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(
         out_count[t] = ts[t].mode == kModeSkip ? 0 : int64_t(cg) + min(ce, ts[t].krem);
 }
 
+// Where rank e of a tile's sent items sits in the LDS stage: bits 5-6 of e
+// swizzle bits 0-1.  A thread stages its 4 consecutive items, so the lanes
+// of one store are 4 ranks apart and, unswizzled, lanes l, l + 8, l + 16
+// and l + 24 hit one bank; swizzled they do not, and the coalesced reads
+// (consecutive ranks) stay a permutation of each 32-rank row.  A bijection
+// on [0, kTile).
+__device__ __forceinline__ uint32_t stage_at(uint32_t e) { return e ^ ((e >> 5) & 3u); }
+
 // Per active tile: write the selected items in index order.  An item with
 // key > T, or key == T while fewer than r ties precede it, is sent; its
 // output slot is (#sent before it) = gt_before + min(eq_before, r).  On the
@@ -1083,8 +1091,8 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
                 if (int64_t(slot) >= kt || int64_t(lidx[q]) >= nt || slot - sent0 >= kTile) {
                     bad = true;
                 } else {
-                    s_idx[slot - sent0] = lidx[q];
-                    s_val[slot - sent0] = val[q];
+                    s_idx[stage_at(slot - sent0)] = lidx[q];
+                    s_val[stage_at(slot - sent0)] = val[q];
                     if (dense) {
                         u[o + lidx[q]] = 0.0f;
                         vt_[lidx[q]] = 0.0f;
@@ -1103,8 +1111,8 @@ __global__ __launch_bounds__(kBlock) void k_emit_write(
         const uint32_t ns = min(sent1 - sent0, uint32_t(kTile));
         for (uint32_t e = threadIdx.x; e < ns; e += kBlock) {
             if (int64_t(sent0 + e) < kt) {
-                oi[sent0 + e] = s_idx[e];
-                ov[sent0 + e] = s_val[e];
+                oi[sent0 + e] = s_idx[stage_at(e)];
+                ov[sent0 + e] = s_val[stage_at(e)];
             }
         }
         __syncthreads();  // before the next tile overwrites the stage
