@@ -31,7 +31,7 @@ namespace dgc {
 // Layouts whose tensors all hold at most this many elements take the
 // per-tensor kernels: a tensor samples min(lines, max(512, lines / 256))
 // of its 32-element lines, at most 512 (4 rounds of 128 lines for one
-// workgroup), and has at most 4096 pieces (4 rounds of the gather).  Larger
+// workgroup), and has at most 4096 pieces (at most 4 per thread).  Larger
 // tensors have lists too long for one workgroup to walk quickly (one CU
 // against the spread passes' whole chip).
 constexpr int64_t kTensorPathMaxN = int64_t(1) << 22;
