@@ -702,6 +702,10 @@ def workload_record(run, steps, warmup, measure_steps):
              "frac_of_peak": round(v[0][1] / (statistics.median(c for c, _ in v) * 1e-3)
                                    / 1e9 / HBM_PEAK_GBPS, 4)}
             for d, v in per.items()]
+        # the mean of the per-density fractions (each step weighted alike),
+        # beside compress_alg_frac_of_peak (all bytes over all time)
+        out["compress_alg_frac_of_peak_mean_over_densities"] = round(
+            statistics.mean(x["frac_of_peak"] for x in out["per_density"]), 4)
     return out, elapsed, step_ms, fused, rec
 
 
