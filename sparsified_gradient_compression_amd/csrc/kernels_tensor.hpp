@@ -48,6 +48,11 @@ constexpr int kFinPieces = int((kTensorPathMaxN / kPiece + kTsThreads - 1) / kTs
 constexpr int kFinEmitUnroll = 4;  // 64-item rounds loaded together per wave
 // Lists in LDS of at most this many items select by counting (fin_direct).
 constexpr int kFinDirect = 128;
+// Keys per thread per pass of the selection rounds, and 64-item rounds per
+// batch of the wave gather (code unrolled this many times is fetched cold at
+// every launch, and most tensors are short).
+constexpr int kFinUnroll = 4;
+constexpr int kFinBatch = 4;
 
 template <bool B>
 struct BoolTag {
@@ -314,17 +319,17 @@ __device__ __forceinline__ bool fin_digit(const KeyAt& key_at, int64_t len, uint
     constexpr int bins = 1 << bits;
     constexpr uint32_t dmask = uint32_t(bins) - 1u;
     const int tid = int(threadIdx.x);
-    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
-        uint32_t key[kTsHistUnroll];
+    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kFinUnroll) {
+        uint32_t key[kFinUnroll];
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
             key[q] = i < len ? key_at(i) : kNoKey;
         }
         // the candidates' top digit crowds into a few bins: aggregate per
         // wave; the lower digits spread out, one atomic per key
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             if (D == 0) {
                 hist_inc(h, key[q] >> shift, key[q] != kNoKey);
             } else if (key[q] != kNoKey && (key[q] >> (shift + bits)) == prefix) {
@@ -356,15 +361,15 @@ __device__ __forceinline__ bool fin_prefix21(const KeyAt& key_at, int64_t len, u
     const int tid = int(threadIdx.x);
     int below = 0;
     uint32_t open = 0;
-    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
-        uint32_t key[kTsHistUnroll];
+    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kFinUnroll) {
+        uint32_t key[kFinUnroll];
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
             key[q] = i < len ? key_at(i) : kNoKey;
         }
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             const bool in = key[q] != kNoKey;
             const uint32_t p21 = key[q] >> 10;
             below |= in && p21 < lo21;
@@ -427,15 +432,15 @@ __device__ __forceinline__ int fin_low10(const KeyAt& key_at, int64_t len, uint3
                                          uint32_t* pick) {
     const int tid = int(threadIdx.x);
     const uint32_t p21 = prefix;
-    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kTsHistUnroll) {
-        uint32_t key[kTsHistUnroll];
+    for (int64_t i0 = 0; i0 < len; i0 += int64_t(kTsThreads) * kFinUnroll) {
+        uint32_t key[kFinUnroll];
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             const int64_t i = i0 + int64_t(q) * kTsThreads + tid;
             key[q] = i < len ? key_at(i) : kNoKey;
         }
 #pragma unroll
-        for (int q = 0; q < kTsHistUnroll; ++q) {
+        for (int q = 0; q < kFinUnroll; ++q) {
             const bool in = key[q] != kNoKey && (key[q] >> 10) == p21;
             const uint64_t bm = __ballot(in);
             if (bm) {  // uniform
@@ -620,24 +625,24 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
             }
             fin_wave_sync();
             uint32_t carry = 0;  // the piece + 1 of the item before a round
-            for (uint32_t i0 = wb; i0 < we; i0 += uint32_t(kWave * kGatherBatch)) {
+            for (uint32_t i0 = wb; i0 < we; i0 += uint32_t(kWave * kFinBatch)) {
                 // the rounds' running maxima independently, then the carries
-                uint32_t pc[kGatherBatch];
+                uint32_t pc[kFinBatch];
 #pragma unroll
-                for (int b = 0; b < kGatherBatch; ++b) {
+                for (int b = 0; b < kFinBatch; ++b) {
                     const uint32_t i = i0 + uint32_t(b * kWave + lane);
                     pc[b] = wave_inclusive_max(i < we ? su[i] : 0u);
                 }
 #pragma unroll
-                for (int b = 0; b < kGatherBatch; ++b) {
+                for (int b = 0; b < kFinBatch; ++b) {
                     const uint32_t last = lane_value(pc[b], kWave - 1);
                     pc[b] = max(pc[b], carry);  // >= 1 below we
                     carry = max(carry, last);
                 }
-                CandSlot it[kGatherBatch];
-                bool got[kGatherBatch];
+                CandSlot it[kFinBatch];
+                bool got[kFinBatch];
 #pragma unroll
-                for (int b = 0; b < kGatherBatch; ++b) {
+                for (int b = 0; b < kFinBatch; ++b) {
                     const uint32_t i = i0 + uint32_t(b * kWave + lane);
                     const uint32_t j = pc[b] - 1u;
                     got[b] = false;
@@ -650,7 +655,7 @@ __global__ __launch_bounds__(kTsThreads) void k_finish_tensor(
                 }
                 // su[i] (a mark) is read only by the lane that writes it here
 #pragma unroll
-                for (int b = 0; b < kGatherBatch; ++b) {
+                for (int b = 0; b < kFinBatch; ++b) {
                     const uint32_t i = i0 + uint32_t(b * kWave + lane);
                     if (got[b]) {
                         sidx[i] = it[b].idx;
