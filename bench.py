@@ -39,6 +39,7 @@ value vectors in learner order into the fresh dense sum.
 """
 
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -143,6 +144,9 @@ def parse():
                          "sampled threshold, the sampled threshold with an exact "
                          "top-k among its survivors, or shared-index compression "
                          "(ScaleComp)")
+    ap.add_argument("--ranges", action="store_true",
+                    help="roctx ranges around each step, learner call and decode "
+                         "(for rocprofv3 --marker-trace); off by default")
     ap.add_argument("--records", default="",
                     help="write one JSON line per (measured step, learner) to this "
                          "file: k, sent entries, stream entries, times, algorithmic "
@@ -465,9 +469,22 @@ class Run:
     def k_of_step(self, s):
         return self.ks[(s % self.gsteps) % len(self.ks)]
 
+    def rng(self, name):
+        """A roctx range (torch's markers map to roctx on ROCm) with
+        --ranges, else nothing: rocprofv3 --marker-trace then shows each
+        step, learner call and decode on the kernel timeline."""
+        if not self.args.ranges:
+            return contextlib.nullcontext()
+        import torch
+        return torch.cuda.nvtx.range(name)
+
     def step(self, s):
         """Enqueue step s: every learner's compress + encode, then the
         learners' fresh dense sum."""
+        with self.rng(f"step {s}"):
+            self._step(s)
+
+    def _step(self, s):
         dgc, args, learners = self.dgc, self.args, self.learners
         t = s % self.gsteps
         k = self.ks[t % len(self.ks)]
@@ -480,36 +497,45 @@ class Run:
             lead = s % len(learners)
             Ld = learners[lead]
             K = int(sum(k))
-            Ld.compress(self.grads[(lead, t)], k, self.wl.clip)
-            Ld.encode(k)
+            with self.rng(f"learner {lead} leader"):
+                Ld.compress(self.grads[(lead, t)], k, self.wl.clip)
+                Ld.encode(k)
             for w, L in enumerate(learners):
                 if w != lead:
-                    L.compress_shared(self.grads[(w, t)], k, Ld.idx[:K], self.wl.clip)
-            dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, Ld.idx[:K],
-                           self.out_sum, self.dense)
+                    with self.rng(f"learner {w} shared"):
+                        L.compress_shared(self.grads[(w, t)], k, Ld.idx[:K], self.wl.clip)
+            with self.rng("shared sum"):
+                dgc.shared_sum(learners[0], [L.val[:K] for L in learners], k, Ld.idx[:K],
+                               self.out_sum, self.dense)
             return
         if self.hier:
             for w, L in enumerate(learners):
-                L.compress_hier(self.grads[(w, t)], k, self.wl.clip)
-                L.encode_counts(k)
-            dgc.decode_sum(learners[0], streams_of(), self.dense)
+                with self.rng(f"learner {w}"):
+                    L.compress_hier(self.grads[(w, t)], k, self.wl.clip)
+                    L.encode_counts(k)
+            with self.rng("decode"):
+                dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         if self.binlocal or self.sampled:
             step_caps = self.caps if self.binlocal else self.caps_by_step[t % len(self.ks)]
             for w, L in enumerate(learners):
-                if self.binlocal:
-                    L.compress_binlocal(self.grads[(w, t)], self.bins, step_caps,
-                                        self.wl.clip)
-                else:
-                    L.compress_sampled(self.grads[(w, t)], k, step_caps, self.wl.clip)
-                L.encode_counts(step_caps)
-            dgc.decode_sum(learners[0], streams_of(), self.dense)
+                with self.rng(f"learner {w}"):
+                    if self.binlocal:
+                        L.compress_binlocal(self.grads[(w, t)], self.bins, step_caps,
+                                            self.wl.clip)
+                    else:
+                        L.compress_sampled(self.grads[(w, t)], k, step_caps, self.wl.clip)
+                    L.encode_counts(step_caps)
+            with self.rng("decode"):
+                dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         if not self.pipeline:
             for w, L in enumerate(learners):
-                L.compress(self.grads[(w, t)], k, self.wl.clip)
-                L.encode(k)
-            dgc.decode_sum(learners[0], streams_of(), self.dense)
+                with self.rng(f"learner {w}"):
+                    L.compress(self.grads[(w, t)], k, self.wl.clip)
+                    L.encode(k)
+            with self.rng("decode"):
+                dgc.decode_sum(learners[0], streams_of(), self.dense)
             return
         import torch
         for w, L in enumerate(learners):

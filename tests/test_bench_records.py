@@ -38,3 +38,15 @@ def test_records_without_times(tmp_path):
     r = json.loads(path.read_text())
     assert r["compress_alg_bytes"] == 64 * 20 + 16 * 3
     assert r["compress_GBps"] is None and r["compress_frac_of_peak"] is None
+
+
+def test_ranges_are_roctx_ranges_or_nothing():
+    """--ranges wraps the step's calls in torch's range markers (roctx on
+    ROCm; they need no GPU); without it, a context that does nothing."""
+    import contextlib
+    import bench
+    off = SimpleNamespace(args=SimpleNamespace(ranges=False))
+    assert isinstance(bench.Run.rng(off, "step 0"), contextlib.nullcontext)
+    on = SimpleNamespace(args=SimpleNamespace(ranges=True))
+    with bench.Run.rng(on, "step 0"):
+        pass
