@@ -633,10 +633,10 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
         k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
                                                                  st->ta, st->sc, st->KT);
     if (st->staged_k)
-        k_enc_scan<true><<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb, entries,
+        k_enc_scan<true><<<T, kBlock, 0, stream>>>(st->K, kdev, st->ta, st->tb, entries,
                                                    st->sc);
     else
-        k_enc_scan<false><<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, st->ta, st->tb,
+        k_enc_scan<false><<<T, kBlock, 0, stream>>>(st->K, kdev, st->ta, st->tb,
                                                     entries, st->sc);
     if (st->KT > 0)
         k_enc_write<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void k_enc_count(
 // One block per tensor: scan the filler counts; E_t = k_t + fillers.
 template <bool kStaged>
 __global__ __launch_bounds__(kBlock) void k_enc_scan(
-    DevLayout L, DevK K, const int64_t* __restrict__ kdev,
+    DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ tile_f, uint32_t* __restrict__ tile_foff,
     int64_t* __restrict__ entries, Scalars* __restrict__ sc) {
     __shared__ uint32_t lds[kWavesPerBlock];
