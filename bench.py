@@ -135,6 +135,13 @@ def parse():
                     help="DGC_OPT_SELECT_GRID for dgc_compress and dgc_compress_hier: 0 "
                          "automatic, 1 a workgroup "
                          "per tensor, 2 the spread passes")
+    ap.add_argument("--encode-path", type=int, choices=(0, 1, 2), default=0,
+                    help="DGC_OPT_ENCODE_PATH: 0 automatic, 1 a workgroup per "
+                         "tensor, 2 the tiled passes")
+    ap.add_argument("--decode-path", type=int, choices=(0, 1, 2, 3), default=0,
+                    help="DGC_OPT_DECODE_PATH: 0 automatic, 1 each stream on its own "
+                         "(tiled passes), 2 merged, 3 each stream on its own (a "
+                         "workgroup per tensor)")
     ap.add_argument("--timers", choices=("fused", "off"), default="fused",
                     help="library timers in the timed region: the element-wise "
                          "pass only (default), or none (then roofline is null)")
@@ -449,6 +456,8 @@ class Run:
                          for _ in range(wl.learners)]
         for L in self.learners:
             L.set_option(dgc.DGC_OPT_SELECT_GRID, args.select_grid)
+            L.set_option(dgc.DGC_OPT_ENCODE_PATH, args.encode_path)
+            L.set_option(dgc.DGC_OPT_DECODE_PATH, args.decode_path)
         self.dense = torch.zeros(n, dtype=torch.float32, device="cuda")
         if self.shared:
             self.out_sum = torch.empty(max(int(sum(kmax)), 1), dtype=torch.float32,

@@ -78,9 +78,15 @@ extern "C" {
                                    automatic (default: merged when the
                                    learners' streams hold at least n_t / 16
                                    entries together, else each stream added
-                                   on its own); 1 always on its own; 2 always
-                                   merged -- the same results, only the speed
-                                   differs */
+                                   on its own -- by one workgroup per tensor,
+                                   for up to 8 learners in one launch, when
+                                   no tensor's streams can hold more than
+                                   8192 entries together at capacity, else
+                                   by passes spread over 1024-entry tiles);
+                                   1 always on its own, spread; 2 always
+                                   merged; 3 always on its own, a workgroup
+                                   per tensor -- the same results, only the
+                                   speed differs */
 #define DGC_OPT_SELECT_GRID 4   /* dgc_compress and dgc_compress_hier, the
                                    exact select and emit: 0 automatic
                                    (default: when every tensor has at most
@@ -94,6 +100,16 @@ extern "C" {
                                    gather (slow for long sources); 2 always
                                    the spread passes -- the same results,
                                    only the speed differs */
+
+#define DGC_OPT_ENCODE_PATH 5   /* dgc_encode and dgc_encode_counts: 0
+                                   automatic (default: when no tensor sends
+                                   more than 8192 entries, one workgroup per
+                                   tensor counts, scans and writes its stream
+                                   in one launch; else three passes spread
+                                   over 1024-entry tiles); 1 always the
+                                   workgroup per tensor; 2 always the tiled
+                                   passes -- the same results, only the
+                                   speed differs */
 
 /* Timers for dgc_get_kernel_time. */
 #define DGC_TIMER_FUSED 0     /* the element-wise pass of dgc_compress,

@@ -66,6 +66,7 @@ struct Plan {
     // per-tensor scans that can exceed kScanStagedMin values take the
     // LDS-staged kernels: tiles over n (emit), capacity tiles (decode)
     bool staged_tiles = false, staged_etiles = false;
+    int64_t et_max = 0;  // most capacity tiles of one tensor
     // bin-local selector: most pieces and prefix groups any bin length gives
     int64_t BP = 0, BG = 0;
     int64_t tiles = 0;  // entries of each per-tile array
@@ -163,6 +164,7 @@ int make_plan(int32_t T, const int64_t* sizes, const int64_t* kmax, Plan& p) {
     for (int32_t t = 0; t < T; ++t) {
         p.staged_tiles |= p.tbase[t + 1] - p.tbase[t] > kScanStagedMin;
         p.staged_etiles |= p.etbase[t + 1] - p.etbase[t] > kScanStagedMin;
+        p.et_max = std::max(p.et_max, p.etbase[t + 1] - p.etbase[t]);
     }
     p.P = p.pbase[T];
     p.G = p.gbase[T];
@@ -380,6 +382,7 @@ struct dgc_state {
     std::vector<uint32_t> kmap_host;
     bool k_valid = false;
     int64_t KT = 0;  // tiles over k of the last upload
+    int64_t kt_max = 0;  // most tiles over k of one tensor (last upload)
     std::vector<int64_t> bins_last;  // bin lengths of the last upload
     std::vector<int64_t> bl_tables;  // plen, magic, pbase, gbase, pcap, slbase, rbins (host)
     bool bins_valid = false;
@@ -389,7 +392,8 @@ struct dgc_state {
     DevSample A{};
     const int64_t* wlines = nullptr;  // [T] lines the per-tensor window samples
     DevDec Dd{};
-    int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged
+    int decode_path = 0;  // 0 automatic, 1 scattered, 2 merged, 3 scattered per tensor
+    int encode_path = 0;  // 0 automatic, 1 a workgroup per tensor, 2 tiled passes
     int select_grid = 0;  // 0 automatic, 1 a workgroup per tensor, 2 spread passes
     bool staged_k = false;  // some tensor has more than kScanStagedMin k tiles
     int64_t BP = 0, BG = 0;  // bin-local pieces and groups of the last upload
@@ -503,9 +507,11 @@ int upload_k(dgc_state* st, const int64_t* k, hipStream_t s) {
     // tile counts on the host too: they size the later launches
     int64_t KT = 0;
     st->staged_k = false;
+    st->kt_max = 0;
     for (int32_t t = 0; t < T; ++t) {
         const int64_t tiles = cdiv(k[t], kTile);
         st->staged_k |= tiles > kScanStagedMin;
+        st->kt_max = std::max(st->kt_max, tiles);
         KT += tiles;
     }
     st->KT = KT;
@@ -629,6 +635,13 @@ int encode_impl(dgc_state* st, const int64_t* k, const int64_t* kdev,
     const int T = p.T;
     const int64_t pg = int64_t(st->num_cus) * kCodecBlocksPerCU;
     DGC_TRY(timer_begin(st, DGC_TIMER_ENCODE, stream));
+    if (st->encode_path == 1 || (st->encode_path == 0 && st->kt_max <= kEncTensorTiles)) {
+        k_enc_tensor<<<T, kBlock, 0, stream>>>(st->L, st->K, kdev, idx, val, runs, vals,
+                                               entries, st->sc);
+        DGC_LAUNCH_CHECK();
+        DGC_TRY(timer_end(st, DGC_TIMER_ENCODE, stream));
+        return DGC_OK;
+    }
     if (st->KT > 0)
         k_enc_count<<<grid_for(st->KT, pg), kBlock, 0, stream>>>(st->L, st->K, kdev, idx,
                                                                  st->ta, st->sc, st->KT);
@@ -1459,6 +1472,19 @@ static int decode_impl(dgc_state* st, int32_t n_learners, const uint16_t* const*
         // from there on (each tensor merged only where its streams are
         // dense enough).
         const bool merge_fresh = fresh_batch && !fill_all;
+        // scattered, the batch's streams added by one workgroup per tensor:
+        // when forced, or when no tensor's streams can hold more than
+        // kDecTensorTiles tiles together
+        const bool per_tensor =
+            !merge_on && (st->decode_path == 3 ||
+                          (st->decode_path == 0 && nbw * p.et_max <= kDecTensorTiles));
+        if (per_tensor) {
+            if (fill_all && p.n > 0)
+                k_dec_fill<<<int(cdiv(p.n, kDecBlock)), kBlock, 0, stream>>>(dense, p.n);
+            k_dec_tensor<<<T, kBlock, 0, stream>>>(st->L, S, dense, st->sc);
+            DGC_LAUNCH_CHECK();
+            continue;
+        }
         if (merge_on)
             k_dec_mode<<<int(cdiv(p.NBLK, kBlock)), kBlock, 0, stream>>>(
                 st->L, S, st->Dd, merge_fresh ? 2 : st->decode_path, p.NBLK);
@@ -1560,8 +1586,13 @@ int dgc_set_fused_event(dgc_state* st, hipEvent_t ev) {
 
 int dgc_set_option(dgc_state* st, int32_t option, int64_t value) {
     if (!st) return DGC_EINVAL;
-    if (option == DGC_OPT_DECODE_PATH) {
+    if (option == DGC_OPT_ENCODE_PATH) {
         if (value < 0 || value > 2) return DGC_EINVAL;
+        st->encode_path = int(value);
+        return DGC_OK;
+    }
+    if (option == DGC_OPT_DECODE_PATH) {
+        if (value < 0 || value > 3) return DGC_EINVAL;
         st->decode_path = int(value);
         return DGC_OK;
     }

@@ -83,8 +83,12 @@ __device__ __forceinline__ int64_t enc_len(const DevK& K, const int64_t* kdev, i
 // mostly do not).  A workgroup tests its next kEncTest tiles at once, one
 // thread each (a dense stream's tiles then cost one round of loads per
 // kEncTest tiles instead of one each), and counts entry by entry only the
-// tiles the test does not settle.  Index order is checked by k_enc_write.
+// tiles the test does not settle.  Index order is checked by the write.
 constexpr int kEncTest = 16;
+
+// The automatic choice takes one workgroup per tensor (k_enc_tensor) when
+// no tensor holds more than this many tiles of entries.
+constexpr int64_t kEncTensorTiles = 8;
 
 __global__ __launch_bounds__(kBlock) void k_enc_count(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
@@ -161,19 +165,133 @@ __global__ __launch_bounds__(kBlock) void k_enc_scan(
     }
 }
 
-// Entry i lands at slot i + (fillers of entries <= i); its own fillers fill
-// the slots just before it.
-// An index not above the previous one or outside the tensor latches
-// DGC_ECORRUPT; such an entry is not written.
+// LDS of one encode workgroup: the block scan's wave totals and the stage
+// that writes a tile with fillers back in strided order.
+struct EncStage {
+    uint32_t lds[kWavesPerBlock];
+    uint32_t sslot[kTile];
+    uint16_t sgap[kTile];
+    float sval[kTile];
+};
+
+// One tile of a tensor's sorted list: entries [i0, min(kt, i0 + kTile)) of
+// id / vl (nt elements), with `carry` fillers before the tile.  Entry i
+// lands at slot i + carry + (fillers of the tile's entries up to and
+// including i) of runs / vals (the tensor's cap slots); its own fillers
+// fill the slots just before it.  An index not above the previous one or
+// outside the tensor latches DGC_ECORRUPT and is not written.  vin / vout:
+// id and vl are 16-byte aligned; runs 8-byte and vals 16-byte aligned.
+// Every thread of the block calls it; it returns the tile's fillers, the
+// same in every thread.
+__device__ __forceinline__ uint32_t enc_tile(
+    const uint32_t* __restrict__ id, const float* __restrict__ vl, int64_t i0, int64_t kt,
+    int64_t nt, int64_t carry, uint16_t* __restrict__ runs, float* __restrict__ vals,
+    int64_t cap, bool vin, bool vout, Scalars* __restrict__ sc, EncStage& S) {
+    // Each thread takes kPerThread consecutive entries: one load round
+    // and at most one block scan (only when the tile has fillers) give
+    // every entry its slot.  Without fillers up to the tile's end the
+    // thread's entries land in kPerThread consecutive aligned slots and
+    // are stored as vectors; otherwise they are written back in the
+    // strided order through LDS, so a wave's stores stay contiguous.
+    const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+    uint32_t nfv[kPerThread];
+    int64_t gapv[kPerThread];
+    float xv[kPerThread];
+    uint32_t F = 0;
+    bool bad = false;
+    if (vin && ib + kPerThread <= kt) {
+        const uint4 x = *reinterpret_cast<const uint4*>(id + ib);
+        const float4 y = *reinterpret_cast<const float4*>(vl + ib);
+        const int64_t cur[kPerThread] = {x.x, x.y, x.z, x.w};
+        xv[0] = y.x;
+        xv[1] = y.y;
+        xv[2] = y.z;
+        xv[3] = y.w;
+        int64_t prev = ib ? int64_t(id[ib - 1]) : -1;
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            nfv[c] = fillers_after(prev, cur[c], nt, bad, gapv[c]);
+            prev = cur[c];
+            F += nfv[c];
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int64_t i = ib + c;
+            gapv[c] = -1;
+            nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
+            xv[c] = i < kt ? vl[i] : 0.0f;
+            F += nfv[c];
+        }
+    }
+    if (bad) latch_error(sc, kErrCorrupt);
+    uint32_t pre = 0, tot = 0;
+    const bool anyF = __syncthreads_or(F != 0);
+    if (anyF)  // fillers are rare: skip the scan
+        pre = block_exclusive_scan(F, S.lds, tot);
+    else if (vout && (carry & (kPerThread - 1)) == 0) {  // uniform
+        // entry i lands at slot i + carry
+        const int64_t pos = ib + carry;
+        if (ib + kPerThread <= kt && pos + kPerThread <= cap && gapv[0] >= 0 &&
+            gapv[1] >= 0 && gapv[2] >= 0 && gapv[3] >= 0) {
+            const uint2 r = make_uint2(
+                uint32_t(gapv[0] & 0xFFFF) | (uint32_t(gapv[1] & 0xFFFF) << 16),
+                uint32_t(gapv[2] & 0xFFFF) | (uint32_t(gapv[3] & 0xFFFF) << 16));
+            *reinterpret_cast<uint2*>(runs + pos) = r;
+            *reinterpret_cast<float4*>(vals + pos) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < kPerThread; ++c)
+                if (ib + c < kt && gapv[c] >= 0 && pos + c < cap) {
+                    runs[pos + c] = uint16_t(gapv[c] & 0xFFFF);
+                    vals[pos + c] = xv[c];
+                }
+        }
+        return 0;  // no LDS touched since the barrier above
+    }
+    // entry i lands at slot i + carry + (fillers of entries <= i); its own
+    // fillers fill the slots just before it.  sslot: slot - i0 - carry
+    // (below 1024 * 65537), or kNoKey for no entry.
+    uint32_t fb = pre;
+#pragma unroll
+    for (int c = 0; c < kPerThread; ++c) {
+        const int64_t i = ib + c;
+        fb += nfv[c];
+        const int e = int(threadIdx.x) * kPerThread + c;
+        const bool ok = i < kt && gapv[c] >= 0;
+        S.sslot[e] = ok ? uint32_t(e) + fb : kNoKey;
+        S.sgap[e] = uint16_t(gapv[c] & 0xFFFF);
+        S.sval[e] = xv[c];
+        if (ok && nfv[c]) {
+            int64_t pos = i + carry + fb - nfv[c];
+            for (uint32_t z = 0; z < nfv[c]; ++z, ++pos)
+                if (pos < cap) { runs[pos] = 65535; vals[pos] = 0.0f; }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int e = q * kBlock + int(threadIdx.x);
+        if (i0 + e >= kt) break;
+        if (S.sslot[e] == kNoKey) continue;
+        const int64_t pos = i0 + carry + S.sslot[e];
+        if (pos < cap) {
+            runs[pos] = S.sgap[e];
+            vals[pos] = S.sval[e];
+        }
+    }
+    __syncthreads();  // before the next tile overwrites the stage
+    return tot;
+}
+
+// The write pass over all tiles of all tensors, each at the filler offset
+// k_enc_scan gave it.
 __global__ __launch_bounds__(kBlock) void k_enc_write(
     DevLayout L, DevK K, const int64_t* __restrict__ kdev,
     const uint32_t* __restrict__ idx, const float* __restrict__ val,
     const uint32_t* __restrict__ tile_foff, uint16_t* __restrict__ runs,
     float* __restrict__ vals, Scalars* __restrict__ sc, int64_t n_ktiles) {
-    __shared__ uint32_t lds[kWavesPerBlock];
-    __shared__ uint32_t sslot[kTile];
-    __shared__ uint16_t sgap[kTile];
-    __shared__ float sval[kTile];
+    __shared__ EncStage S;
     int64_t tb = 0, te = 0, kt = 0, nt = 0, eb = 0, cap = 0;  // current tensor
     const uint32_t* id = idx;
     const float* vl = val;
@@ -197,104 +315,37 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
             vt = next_tensor_tile(vt, te, gridDim.x);
             continue;
         }
-        // Each thread takes kPerThread consecutive entries: one load round
-        // and at most one block scan (only when the tile has fillers) give
-        // every entry its slot.  Without fillers up to the tile's end the
-        // thread's entries land in kPerThread consecutive aligned slots and
-        // are stored as vectors; otherwise they are written back in the
-        // strided order through LDS, so a wave's stores stay contiguous.
-        const int64_t carry = int64_t(tile_foff[vt]);
-        const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
-        uint32_t nfv[kPerThread];
-        int64_t gapv[kPerThread];
-        float xv[kPerThread];
-        uint32_t F = 0;
-        bool bad = false;
-        if (vin && ib + kPerThread <= kt) {
-            const uint4 x = *reinterpret_cast<const uint4*>(id + ib);
-            const float4 y = *reinterpret_cast<const float4*>(vl + ib);
-            const int64_t cur[kPerThread] = {x.x, x.y, x.z, x.w};
-            xv[0] = y.x;
-            xv[1] = y.y;
-            xv[2] = y.z;
-            xv[3] = y.w;
-            int64_t prev = ib ? int64_t(id[ib - 1]) : -1;
-#pragma unroll
-            for (int c = 0; c < kPerThread; ++c) {
-                nfv[c] = fillers_after(prev, cur[c], nt, bad, gapv[c]);
-                prev = cur[c];
-                F += nfv[c];
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < kPerThread; ++c) {
-                const int64_t i = ib + c;
-                gapv[c] = -1;
-                nfv[c] = i < kt ? fillers_of(id, i, nt, bad, gapv[c]) : 0u;
-                xv[c] = i < kt ? vl[i] : 0.0f;
-                F += nfv[c];
-            }
-        }
-        if (bad) latch_error(sc, kErrCorrupt);
-        uint32_t pre = 0, tot = 0;
-        const bool anyF = __syncthreads_or(F != 0);
-        if (anyF)  // fillers are rare: skip the scan
-            pre = block_exclusive_scan(F, lds, tot);
-        else if (vout && (carry & (kPerThread - 1)) == 0) {  // uniform
-            // entry i lands at slot i + carry
-            const int64_t pos = ib + carry;
-            if (ib + kPerThread <= kt && pos + kPerThread <= cap && gapv[0] >= 0 &&
-                gapv[1] >= 0 && gapv[2] >= 0 && gapv[3] >= 0) {
-                const uint2 r = make_uint2(
-                    uint32_t(gapv[0] & 0xFFFF) | (uint32_t(gapv[1] & 0xFFFF) << 16),
-                    uint32_t(gapv[2] & 0xFFFF) | (uint32_t(gapv[3] & 0xFFFF) << 16));
-                *reinterpret_cast<uint2*>(runs + eb + pos) = r;
-                *reinterpret_cast<float4*>(vals + eb + pos) =
-                    make_float4(xv[0], xv[1], xv[2], xv[3]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < kPerThread; ++c)
-                    if (ib + c < kt && gapv[c] >= 0 && pos + c < cap) {
-                        runs[eb + pos + c] = uint16_t(gapv[c] & 0xFFFF);
-                        vals[eb + pos + c] = xv[c];
-                    }
-            }
-            vt += gridDim.x;
-            continue;
-        }
-        // entry i lands at slot i + carry + (fillers of entries <= i); its
-        // own fillers fill the slots just before it.  sslot: slot - i0 -
-        // carry (below 1024 * 65537), or kNoKey for no entry.
-        uint32_t fb = pre;
-#pragma unroll
-        for (int c = 0; c < kPerThread; ++c) {
-            const int64_t i = ib + c;
-            fb += nfv[c];
-            const int e = int(threadIdx.x) * kPerThread + c;
-            const bool ok = i < kt && gapv[c] >= 0;
-            sslot[e] = ok ? uint32_t(e) + fb : kNoKey;
-            sgap[e] = uint16_t(gapv[c] & 0xFFFF);
-            sval[e] = xv[c];
-            if (ok && nfv[c]) {
-                int64_t pos = i + carry + fb - nfv[c];
-                for (uint32_t z = 0; z < nfv[c]; ++z, ++pos)
-                    if (pos < cap) { runs[eb + pos] = 65535; vals[eb + pos] = 0.0f; }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            const int e = q * kBlock + int(threadIdx.x);
-            if (i0 + e >= kt) break;
-            if (sslot[e] == kNoKey) continue;
-            const int64_t pos = i0 + carry + sslot[e];
-            if (pos < cap) {
-                runs[eb + pos] = sgap[e];
-                vals[eb + pos] = sval[e];
-            }
-        }
-        __syncthreads();  // before the next tile overwrites the stage
+        enc_tile(id, vl, i0, kt, nt, int64_t(tile_foff[vt]), runs + eb, vals + eb, cap, vin,
+                 vout, sc, S);
         vt += gridDim.x;
+    }
+}
+
+// The count, scan and write in one launch, one workgroup per tensor: its
+// tiles in order, each one's fillers carried into the next.  Each of the
+// three tiled passes is a launch of a few microseconds however little it
+// does, so layouts whose tensors hold few tiles each take this one.
+__global__ __launch_bounds__(kBlock) void k_enc_tensor(
+    DevLayout L, DevK K, const int64_t* __restrict__ kdev,
+    const uint32_t* __restrict__ idx, const float* __restrict__ val,
+    uint16_t* __restrict__ runs, float* __restrict__ vals,
+    int64_t* __restrict__ entries, Scalars* __restrict__ sc) {
+    __shared__ EncStage S;
+    const int t = blockIdx.x;
+    const int64_t kt = enc_len(K, kdev, t);
+    const int64_t nt = L.o[t + 1] - L.o[t];
+    const uint32_t* id = idx + K.koff[t];
+    const float* vl = val + K.koff[t];
+    const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
+    const bool vin = aligned_as(id, 16) && aligned_as(vl, 16);
+    const bool vout = aligned_as(runs + eb, 8) && aligned_as(vals + eb, 16);
+    int64_t carry = 0;
+    for (int64_t i0 = 0; i0 < kt; i0 += kTile)
+        carry += enc_tile(id, vl, i0, kt, nt, carry, runs + eb, vals + eb, cap, vin, vout, sc,
+                          S);
+    if (threadIdx.x == 0) {
+        if (kdev && (kdev[t] < 0 || kdev[t] > K.k[t])) latch_error(sc, kErrCorrupt);
+        entries[t] = kt + carry;
     }
 }
 
@@ -322,6 +373,57 @@ __device__ __forceinline__ int64_t stream_len(const int64_t* entries, int t,
     return (e < 0 || e > cap) ? 0 : e;
 }
 
+// Values of the thread's entries ib .. ib + 3 (0 past E).
+__device__ __forceinline__ void load_vals4(const float* __restrict__ v, int64_t ib, int64_t E,
+                                           bool vec, float (&x)[4]) {
+    if (vec && ib + 4 <= E) {
+        const float4 y = *reinterpret_cast<const float4*>(v + ib);
+        x[0] = y.x;
+        x[1] = y.y;
+        x[2] = y.z;
+        x[3] = y.w;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = ib + c < E ? v[ib + c] : 0.0f;
+    }
+}
+
+// Adds one tile of a stream, entries [i0, min(E, i0 + kTile)), into a
+// tensor's part of the dense sum (nt elements).  The thread holds the
+// (run + 1) weights wv and values xv of entries i0 + 4 tid .. + 3 and their
+// exclusive weight prefix ex within the tile; carry = the weights of the
+// stream's entries before the tile.  The adds go back to entry
+// i0 + 256 q + tid through LDS, so that a wave's adds stay close together
+// when the stream is dense.  Returns whether an entry of this thread lies
+// at or past the tensor's end (it adds nothing).  Every thread calls it; it
+// ends with a barrier.
+__device__ __forceinline__ bool dec_add_tile(int64_t i0, int64_t E, int64_t carry, uint32_t ex,
+                                             const uint32_t (&wv)[4], const float (&xv)[4],
+                                             float* __restrict__ dense_t, int64_t nt,
+                                             uint32_t* trel, float* tval) {
+    // positions relative to the tile's start (< 1024 * 65536)
+    uint32_t rel = ex;
+#pragma unroll
+    for (int c = 0; c < kPerThread; ++c) {
+        rel += wv[c];
+        const int e = int(threadIdx.x) * kPerThread + c;
+        trel[e] = rel - 1u;
+        tval[e] = xv[c];
+    }
+    __syncthreads();
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int e = q * kBlock + int(threadIdx.x);
+        if (i0 + e >= E) break;
+        const int64_t pos = carry + trel[e];
+        if (pos >= nt) bad = true;
+        else dense_t[pos] = __fadd_rn(dense_t[pos], tval[e]);
+    }
+    __syncthreads();  // before the next tile overwrites trel
+    return bad;
+}
+
 // Merged decode.  A tensor whose learners' streams together hold at least
 // n_t / 16 entries touches most cache lines of its part of the dense sum
 // once per learner when each stream is added on its own.  For such a tensor
@@ -340,6 +442,9 @@ constexpr int64_t kXcds = 8;  // XCDs of an MI355X (block order of the merge pas
 // that could hold n_t / kDecMergeFresh entries are a small part of the
 // layout: then the host zeroes the sum and every tensor is scattered.
 constexpr int64_t kDecMergeAcc = 16, kDecMergeFresh = 256;
+// Scattered batches take one workgroup per tensor (k_dec_tensor) when no
+// tensor's streams can hold more than this many tiles together.
+constexpr int64_t kDecTensorTiles = 8;
 // Value bytes of a batch's streams (at capacity) up to which the bounds
 // passes also load the values: a quarter of MI355X's 256 MB last-level
 // cache.
@@ -486,9 +591,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         }
         // Each thread takes kPerThread consecutive entries of the tile: one
         // load round and one block scan per tile give every entry its
-        // position (the thread's running sum after the scan).  The dense
-        // adds then go back to entry i0 + 256 q + tid, through LDS, so that a
-        // wave's adds stay close together when the stream is dense.
+        // position (the thread's running sum after the scan).
         bool bad = false;
         const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
         uint32_t wv[kPerThread];
@@ -502,17 +605,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         // well inside the last-level cache; larger ones would only be read
         // twice.
         if (!merged || warm) {  // uniform
-            if (ib + 4 <= E && aligned_as(vals + eb, 16)) {
-                const float4 x = *reinterpret_cast<const float4*>(vals + eb + ib);
-                xv[0] = x.x;
-                xv[1] = x.y;
-                xv[2] = x.z;
-                xv[3] = x.w;
-            } else {
-#pragma unroll
-                for (int c = 0; c < kPerThread; ++c)
-                    xv[c] = ib + c < E ? vals[eb + ib + c] : 0.0f;
-            }
+            load_vals4(vals + eb, ib, E, aligned_as(vals + eb, 16), xv);
             if (merged)  // keep the loads: their values are not used on this path
                 asm volatile("" ::"v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]));
         }
@@ -521,26 +614,8 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         const uint32_t ex = block_exclusive_scan(s, lds, tot);
         const int64_t carry = int64_t(tile_p[vt]);
         if (!merged) {  // uniform
-            // positions relative to the tile's start (< 1024 * 65536)
-            uint32_t rel = ex;
-#pragma unroll
-            for (int c = 0; c < kPerThread; ++c) {
-                rel += wv[c];
-                const int e = int(threadIdx.x) * kPerThread + c;
-                trel[e] = rel - 1u;
-                tval[e] = xv[c];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < kPerThread; ++q) {
-                const int e = q * kBlock + int(threadIdx.x);
-                if (i0 + e >= E) break;
-                const int64_t pos = carry + trel[e];
-                if (pos >= nt) bad = true;
-                else dense[o + pos] = __fadd_rn(dense[o + pos], tval[e]);
-            }
-            __syncthreads();  // before the next tile overwrites trel
-            if (bad) latch_error(sc, kErrCorrupt);
+            if (dec_add_tile(i0, E, carry, ex, wv, xv, dense + o, nt, trel, tval))
+                latch_error(sc, kErrCorrupt);
             vt += gridDim.x;
             continue;
         }
@@ -566,6 +641,47 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         if (bad) latch_error(sc, kErrCorrupt);
         vt += gridDim.x;
     }
+}
+
+// The scattered decode of a batch of learners in one launch, one workgroup
+// per tensor: the learners in order (each tile ends with a barrier, so an
+// element sees fl(fl(d + x_0) + x_1) ...), each stream's tiles in order with
+// the position carried from tile to tile; an entry count outside
+// [0, capacity] or a position past the tensor's end is flagged as in the
+// tiled passes.  Each of k_dec_count, k_dec_scan and k_dec_write is a
+// launch of a few microseconds however little it does, so layouts whose
+// streams hold few tiles per tensor take this one.
+__global__ __launch_bounds__(kBlock) void k_dec_tensor(DevLayout L, DecBatch S,
+                                                       float* __restrict__ dense,
+                                                       Scalars* __restrict__ sc) {
+    __shared__ uint32_t lds[kWavesPerBlock];
+    __shared__ uint32_t trel[kTile];
+    __shared__ float tval[kTile];
+    const int t = blockIdx.x;
+    const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
+    const int64_t o = L.o[t], nt = L.o[t + 1] - o;
+    bool bad = false;
+    for (int w = 0; w < S.W; ++w) {
+        const int64_t e = S.entries[w][t];
+        bad |= e < 0 || e > cap;
+        const int64_t E = (e < 0 || e > cap) ? 0 : e;
+        const uint16_t* r = S.runs[w] + eb;
+        const float* v = S.vals[w] + eb;
+        const bool rvec = aligned_as(r, 8), vvec = aligned_as(v, 16);
+        int64_t carry = 0;
+        for (int64_t i0 = 0; i0 < E; i0 += kTile) {
+            const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+            uint32_t wv[kPerThread];
+            float xv[kPerThread];
+            load_run_weights(r, ib, E, rvec, wv);
+            load_vals4(v, ib, E, vvec, xv);
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan(wv[0] + wv[1] + wv[2] + wv[3], lds, tot);
+            bad |= dec_add_tile(i0, E, carry, ex, wv, xv, dense + o, nt, trel, tval);
+            carry += tot;
+        }
+    }
+    if (bad) latch_error(sc, kErrCorrupt);
 }
 
 typedef float dec_f4 __attribute__((ext_vector_type(4)));

@@ -24,6 +24,7 @@ DGC_OPT_SELECT_PATH = 1
 DGC_OPT_KERNEL_TIMING = 2
 DGC_OPT_DECODE_PATH = 3
 DGC_OPT_SELECT_GRID = 4
+DGC_OPT_ENCODE_PATH = 5
 DGC_TIMER_FUSED = 0
 DGC_TIMER_COMPRESS = 1
 DGC_TIMER_ENCODE = 2

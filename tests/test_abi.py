@@ -36,6 +36,20 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_binding_constants_match_the_header():
+    """Every integer #define of include/dgc.h that the binding names holds
+    the header's value, and the binding names every DGC_OPT_, DGC_TIMER_
+    and error code."""
+    defs = dict((m.group(1), int(m.group(2))) for m in re.finditer(
+        r"#define\s+(DGC_\w+)\s+\(?(-?\d+)\)?", open(HEADER).read()))
+    assert len(defs) >= 15, defs
+    for name, value in defs.items():
+        if name.startswith(("DGC_OPT_", "DGC_TIMER_", "DGC_E", "DGC_OK")):
+            assert getattr(dgc, name) == value, name
+        elif hasattr(dgc, name):
+            assert getattr(dgc, name) == value, name
+
+
 def test_error_strings():
     assert dgc.dgc_error_string(0) == "ok"
     assert dgc.dgc_error_string(-1) == "invalid argument"

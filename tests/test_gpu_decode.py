@@ -1,6 +1,8 @@
-"""GPU parity of dgc_decode_accumulate on both of its paths: each learner's
-stream added on its own, and the merged pass (dense blocks held on chip,
-learners added in order) -- forced each way and automatic.  Streams are
+"""GPU parity of dgc_decode_accumulate on its paths: each learner's stream
+added on its own (by passes spread over 1024-entry tiles, or by one
+workgroup per tensor for a batch of learners), and the merged pass (dense
+blocks held on chip, learners added in order) -- forced each way and
+automatic.  Streams are
 encoded by the oracle from seeded random selections at densities from 30%
 down to 0.1%; the dense sum starts from random values (and -0.0), so the
 order of the additions is visible in the bits.  The reference is the
@@ -92,7 +94,7 @@ def test_decode_paths_match_oracle(layout, W, dens):
     dense0 = rng.standard_normal(max(n, 1)).astype(np.float32)
     dense0[rng.random(dense0.size) < 0.1] = -0.0
     want = reference(sizes, dense0[:n], streams)
-    for path in (1, 2, 0):
+    for path in (1, 2, 3, 0):
         say(f"decode layout {layout} W={W} path {path}")
         got = decode(L, streams, dense0, path)[:n]
         assert L.status() == dgc.DGC_OK
@@ -131,7 +133,11 @@ def test_merged_decode_flags_corrupt_streams():
 def test_decode_option_rejects_bad_values():
     L = dgc.Learner([100], [10])
     with pytest.raises(dgc.DGCError):
-        L.set_option(dgc.DGC_OPT_DECODE_PATH, 3)
+        L.set_option(dgc.DGC_OPT_DECODE_PATH, 4)
+    with pytest.raises(dgc.DGCError):
+        L.set_option(dgc.DGC_OPT_DECODE_PATH, -1)
+    for good in (0, 1, 2, 3):
+        L.set_option(dgc.DGC_OPT_DECODE_PATH, good)
 
 
 def decode_fresh(L, streams, n, path, guard=None):
@@ -165,7 +171,7 @@ def test_decode_sum_matches_oracle(layout, W, dens):
     streams = make_streams(rng, sizes, dens, L.cap)
     n = sum(sizes)
     want = reference(sizes, np.zeros(n, np.float32), streams)
-    for path in (1, 2, 0):
+    for path in (1, 2, 3, 0):
         say(f"decode_sum layout {layout} W={W} path {path}")
         got = decode_fresh(L, streams, n, path, guard=77.0)
         assert L.status() == dgc.DGC_OK
@@ -187,7 +193,8 @@ def test_decode_sum_without_capacity():
     assert (got[n:] == 5.0).all()
 
 
-def test_decode_sum_flags_corrupt_streams():
+@pytest.mark.parametrize("path", [0, 3])
+def test_decode_sum_flags_corrupt_streams(path):
     import torch
     sizes = [10000, 5000]
     L = dgc.Learner(sizes, sizes)
@@ -197,14 +204,14 @@ def test_decode_sum_flags_corrupt_streams():
     r = runs.cpu().numpy().view(np.uint16).copy()
     r[L.cap[0]:L.cap[0] + int(ent[0])] = 200
     streams[1] = (per, torch.from_numpy(r.view(np.int16)).cuda(), vals, ent)
-    got = decode_fresh(L, streams, sum(sizes), 0, guard=123.0)
+    got = decode_fresh(L, streams, sum(sizes), path, guard=123.0)
     assert L.status() == dgc.DGC_ECORRUPT
     assert (got[sum(sizes):] == 123.0).all()
     assert np.isfinite(got[:sum(sizes)]).all()  # every element written
     assert L.status() == dgc.DGC_OK
 
 
-@pytest.mark.parametrize("path", [0, 1, 2])
+@pytest.mark.parametrize("path", [0, 1, 2, 3])
 @pytest.mark.parametrize("shift", [1, 2, 3])
 def test_decode_sum_into_unaligned_dense(path, shift):
     """The dense sum may start at any 4-byte boundary: a view `shift`
@@ -247,9 +254,82 @@ def test_decode_sum_small_capacity_mixed_layout(W):
     streams = make_streams(rng, sizes, [0.3] * W, L.cap)
     n = sum(sizes)
     want = reference(sizes, np.zeros(n, np.float32), streams)
-    for path in (0, 1, 2):
+    for path in (0, 1, 2, 3):
         say(f"decode_sum small capacity W={W} path {path}")
         got = decode_fresh(L, streams, n, path, guard=9.0)
         assert L.status() == dgc.DGC_OK
         assert np.array_equal(f32_bits(got[:n]), f32_bits(want)), (path, first_diff(got[:n], want))
         assert (got[n:] == 9.0).all()
+
+
+@pytest.mark.parametrize("path", [1, 3])
+def test_scattered_decode_of_corrupt_streams_matches_oracle(path):
+    """On both scattered paths a stream that walks past its tensor's end adds
+    its entries up to that point (as the oracle's decoder does) and is
+    flagged; one whose entry count exceeds its capacity adds nothing for
+    that tensor and is flagged; the other streams add as usual, in learner
+    order."""
+    import torch
+    sizes = [3000, 70001, 5]
+    L = dgc.Learner(sizes, [300, 200, 5])
+    rng = np.random.default_rng([98, path])
+    streams = make_streams(rng, sizes, [0.05] * 3, L.cap)  # per learner
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    # learner 1, tensor 0: every run 40, so the walk passes 3000 part-way
+    per, runs, vals, ent = streams[1]
+    r = runs.cpu().numpy().view(np.uint16).copy()
+    e0 = int(ent[0])
+    assert 41 * e0 > sizes[0]
+    r[L.cap[0]:L.cap[0] + e0] = 40
+    streams[1] = (per, torch.from_numpy(r.view(np.int16)).cuda(), vals, ent)
+    # learner 2, tensor 1: an entry count above the capacity
+    per2, runs2, vals2, ent2 = streams[2]
+    bad = ent2.clone()
+    bad[1] = int(L.cap[2] - L.cap[1]) + 1
+    streams[2] = (per2, runs2, vals2, bad)
+    dense0 = rng.standard_normal(sum(sizes)).astype(np.float32)
+    want = dense0.copy()
+    for w, (_, rr, vv, ee) in enumerate(streams):
+        rh = rr.cpu().numpy().view(np.uint16)
+        vh = vv.cpu().numpy()
+        eh = ee.cpu().numpy()
+        for t in range(len(sizes)):
+            cap_t = int(L.cap[t + 1] - L.cap[t])
+            if eh[t] < 0 or eh[t] > cap_t:
+                continue
+            a = int(L.cap[t])
+            rc = oracle.decode_accumulate(rh[a:a + eh[t]].copy(), vh[a:a + eh[t]].copy(),
+                                          want[off[t]:off[t + 1]])
+            assert rc == (-1 if (w, t) == (1, 0) else 0)
+    got = decode(L, streams, dense0, path)
+    assert L.status() == dgc.DGC_ECORRUPT
+    assert L.status() == dgc.DGC_OK
+    assert np.array_equal(f32_bits(got), f32_bits(want)), first_diff(got, want)
+
+
+@pytest.mark.parametrize("W", [1, 2, 4, 8, 9])
+def test_decode_small_capacity_layouts_every_path(W):
+    """Layouts whose streams hold few tiles per tensor (the automatic choice
+    takes one workgroup per tensor for up to 8 tiles per tensor and batch):
+    accumulate and fresh sums on every path setting, bit for bit the
+    oracle's decode in learner order."""
+    sizes = [1 << 20, 5000, 70001, 1, 0, 2359296]
+    kmax = [1049, 5, 71, 1, 0, 2360]
+    rng = np.random.default_rng([99, W])
+    L = dgc.Learner(sizes, kmax)
+    streams = make_streams(rng, sizes, [0.001] * W, L.cap)
+    n = sum(sizes)
+    dense0 = rng.standard_normal(n).astype(np.float32)
+    dense0[rng.random(n) < 0.1] = -0.0
+    want_acc = reference(sizes, dense0, streams)
+    want_fresh = reference(sizes, np.zeros(n, np.float32), streams)
+    for path in (0, 1, 2, 3):
+        say(f"decode small capacity W={W} path {path}")
+        got = decode(L, streams, dense0, path)
+        assert L.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got), f32_bits(want_acc)), (path, first_diff(got, want_acc))
+        got = decode_fresh(L, streams, n, path, guard=3.0)
+        assert L.status() == dgc.DGC_OK
+        assert np.array_equal(f32_bits(got[:n]), f32_bits(want_fresh)), (
+            path, first_diff(got[:n], want_fresh))
+        assert (got[n:] == 3.0).all()

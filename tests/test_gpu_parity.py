@@ -258,9 +258,13 @@ def test_checkpoint_resume_bitwise():
 
 # ---------------------------------------------------------------- codec
 
-def test_encode_golden_gaps_on_gpu():
+ENCODE_PATHS = [1, 2]  # DGC_OPT_ENCODE_PATH: a workgroup per tensor; the tiled passes
+
+
+@pytest.mark.parametrize("enc", ENCODE_PATHS)
+def test_encode_golden_gaps_on_gpu(enc):
     """The hand-derived streams of tests/golden/encode_cases.json, encoded
-    by the GPU from the golden indices."""
+    by the GPU from the golden indices, on both encode paths."""
     import torch
     from conftest import load_golden
     gold = load_golden("encode_cases.json")
@@ -273,6 +277,7 @@ def test_encode_golden_gaps_on_gpu():
         ti = torch.from_numpy(idx.view(np.int32)).cuda()
         tv = torch.from_numpy(val).cuda()
         L = p.learner
+        L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
         L.idx[:idx.size].copy_(ti)
         L.val[:idx.size].copy_(tv)
         got = gpu_streams(p, k)[0]
@@ -429,13 +434,15 @@ def test_random_layouts_both_paths(seed):
             compare_streams(gpu_streams(p, ks[step]), want, tag=f"fuzz{seed}")
 
 
-def test_encode_flags_unsorted_indices():
+@pytest.mark.parametrize("enc", ENCODE_PATHS)
+def test_encode_flags_unsorted_indices(enc):
     """dgc_encode expects each tensor's indices strictly ascending and inside
     the tensor; anything else latches DGC_ECORRUPT and writes nothing out of
     place."""
     import torch
     p = Pair([1000, 70000], [4, 4])
     L = p.learner
+    L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
     bad = np.array([5, 3, 9, 12, 1, 2, 70000, 7], np.uint32)  # descending / out of range
     L.idx[:8].copy_(torch.from_numpy(bad.view(np.int32)))
     L.val[:8].copy_(torch.ones(8))
@@ -638,8 +645,9 @@ def test_select_grid_option_rejects_bad_values():
     L.close()
 
 
+@pytest.mark.parametrize("enc", ENCODE_PATHS)
 @pytest.mark.parametrize("gap", [65534, 65535, 65536, 65537, 131072, 200000])
-def test_encode_dense_tiles_with_one_long_gap(gap):
+def test_encode_dense_tiles_with_one_long_gap(gap, enc):
     """Tiles of 1024 consecutive indices need no filler, and the count pass
     settles them from the tile's span alone; one gap of `gap` zeros lands
     inside the second tile (after entry 1500), another before the first
@@ -652,6 +660,7 @@ def test_encode_dense_tiles_with_one_long_gap(gap):
     val = np.random.default_rng(gap).standard_normal(idx.size).astype(np.float32)
     p = Pair([n], [idx.size])
     L = p.learner
+    L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
     L.idx[:idx.size].copy_(torch.from_numpy(idx.view(np.int32)))
     L.val[:idx.size].copy_(torch.from_numpy(val))
     got = gpu_streams(p, [idx.size])[0]
@@ -659,3 +668,73 @@ def test_encode_dense_tiles_with_one_long_gap(gap):
     assert np.array_equal(got[0], want[0])
     assert np.array_equal(f32_bits(got[1]), f32_bits(want[1]))
     assert L.status() == dgc.DGC_OK
+
+
+def filler_heavy_indices(rng, k):
+    """k sorted distinct indices: runs of neighbours and short gaps, with up
+    to 12 gaps of one to three fillers' length at random entries (a filler
+    offset that is not a multiple of 4 then carries into later tiles).
+    Returns the indices and a tensor size that holds them."""
+    gaps = rng.integers(0, 3, k).astype(np.int64)
+    if k:
+        at = rng.choice(k, min(k, 12), replace=False)
+        gaps[at] = rng.integers(65535, 4 * 65536 + 2, at.size)
+    pos = np.cumsum(gaps + 1) - 1
+    n = int(pos[-1]) + 1 + int(rng.integers(0, 70000)) if k else int(rng.integers(1, 5000))
+    return pos.astype(np.uint32), n
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_encode_paths_agree(seed):
+    """Both encode paths (a workgroup per tensor, the tiled passes) and the
+    automatic choice give the oracle's streams, through dgc_encode and
+    through dgc_encode_counts, on layouts with empty, one-entry, ragged and
+    many-tile tensors and with many fillers; the device-count variant with
+    counts below the capacity."""
+    import torch
+    rng = np.random.default_rng(700 + seed)
+    ks = [0, 1, 5, 1023, 1024, 1025, 4096, 4097, 9000, 3 * 1024 + 7]
+    rng.shuffle(ks)
+    made = [filler_heavy_indices(rng, k) for k in ks]
+    idx = [m[0] for m in made]
+    sizes = [m[1] for m in made]
+    val = [rng.standard_normal(k).astype(np.float32) for k in ks]
+    p = Pair(sizes, ks)
+    L = p.learner
+    L.idx[:sum(ks)].copy_(torch.from_numpy(np.concatenate(idx).view(np.int32)))
+    L.val[:sum(ks)].copy_(torch.from_numpy(np.concatenate(val)))
+    want = oracle_streams(sizes, ks, np.concatenate(idx), np.concatenate(val))
+    assert sum(len(w[0]) for w in want) > sum(ks) + 50  # fillers present
+    for enc in (0, 1, 2):
+        say(f"encode paths seed {seed} enc {enc}")
+        L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
+        L.runs.fill_(7)
+        compare_streams(gpu_streams(p, ks), want, tag=f"seed{seed} enc{enc}")
+        assert L.status() == dgc.DGC_OK
+    # device counts: tensor t encodes its first c_t entries of the k_t slots
+    cnt = [int(rng.integers(0, k + 1)) for k in ks]
+    want_c = oracle_streams(sizes, cnt, np.concatenate([i[:c] for i, c in zip(idx, cnt)]),
+                            np.concatenate([v[:c] for v, c in zip(val, cnt)]))
+    for enc in (1, 2):
+        say(f"encode counts seed {seed} enc {enc}")
+        L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
+        L.count.copy_(torch.tensor(cnt, dtype=torch.int64))
+        runs, vals, entries = L.encode_counts(ks)
+        torch.cuda.synchronize()
+        assert L.status() == dgc.DGC_OK
+        r = runs.cpu().numpy().view(np.uint16)
+        v = vals.cpu().numpy()
+        e = entries.cpu().numpy()
+        got = [(r[L.cap[t]:L.cap[t] + e[t]], v[L.cap[t]:L.cap[t] + e[t]])
+               for t in range(len(sizes))]
+        compare_streams(got, want_c, tag=f"seed{seed} counts enc{enc}")
+
+
+def test_encode_path_option_rejects_bad_values():
+    L = dgc.Learner([10], [1])
+    for bad in (-1, 3):
+        with pytest.raises(dgc.DGCError):
+            L.set_option(dgc.DGC_OPT_ENCODE_PATH, bad)
+    for good in (0, 1, 2):
+        L.set_option(dgc.DGC_OPT_ENCODE_PATH, good)
+    L.close()
