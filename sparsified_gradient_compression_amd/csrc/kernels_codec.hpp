@@ -52,17 +52,19 @@ __device__ __forceinline__ uint32_t fillers_of(const uint32_t* id, int64_t i,
     return fillers_after(i ? int64_t(id[i - 1]) : -1, int64_t(id[i]), nt, bad, gap);
 }
 
-// Grid-stride walk over per-tensor tiles: the tile after vt for this
-// workgroup that lies at or past `first` (the next tensor's first tile).
-// Once a tile lies past its tensor's entries so do the tensor's later
-// tiles, so a workgroup skips straight to the next tensor.  A workgroup's
-// tiles only grow, so the walks below keep the current tensor's metadata
-// and load it again only when a tile lies past that tensor's last tile:
-// most tiles then wait for one round of loads instead of three.
-__device__ __forceinline__ int64_t next_tensor_tile(int64_t vt, int64_t first,
-                                                    int64_t stride) {
-    if (first <= vt) return vt + stride;
-    return vt + (first - vt + stride - 1) / stride * stride;
+// Walks over per-tensor tiles: workgroup b takes the run of consecutive
+// tiles [c0, c1), the n tiles cut into gridDim.x runs.  A workgroup's tiles
+// then mostly share a tensor, so the walks below keep the current tensor's
+// metadata and load it again only when a tile lies past that tensor's last
+// tile: most tiles wait for one round of loads instead of three (with
+// tiles dealt out grid-stride, a stride above a tensor's tile count put
+// every tile in a new tensor).  Once a tile lies past its tensor's
+// entries so do the tensor's later tiles, so a walk skips straight to the
+// next tensor.
+__device__ __forceinline__ void tile_run(int64_t n, int64_t& c0, int64_t& c1) {
+    const int64_t per = (n + int64_t(gridDim.x) - 1) / int64_t(gridDim.x);
+    c0 = min(n, int64_t(blockIdx.x) * per);
+    c1 = min(n, c0 + per);
 }
 
 // Entries of tensor t to encode: k_t, or, when the counts live on the
@@ -296,7 +298,9 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
     const uint32_t* id = idx;
     const float* vl = val;
     bool vin = false, vout = false;  // 16-byte loads of idx, val; stores of runs, vals
-    for (int64_t vt = blockIdx.x; vt < n_ktiles;) {
+    int64_t c0, c1;
+    tile_run(n_ktiles, c0, c1);
+    for (int64_t vt = c0; vt < c1;) {
         if (vt >= te) {  // uniform: the next tensor
             const int t = int(K.kmap[vt]);
             kt = enc_len(K, kdev, t);
@@ -312,12 +316,12 @@ __global__ __launch_bounds__(kBlock) void k_enc_write(
         }
         const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= kt) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, te, gridDim.x);
+            vt = te;
             continue;
         }
         enc_tile(id, vl, i0, kt, nt, int64_t(tile_foff[vt]), runs + eb, vals + eb, cap, vin,
                  vout, sc, S);
-        vt += gridDim.x;
+        ++vt;
     }
 }
 
@@ -504,7 +508,9 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
     Scalars* __restrict__ sc, int64_t n_etiles) {
     __shared__ uint32_t lds[kWavesPerBlock];
     int64_t tb = 0, te = 0, eb = 0, E = 0;  // current tensor: tiles [tb, te)
-    for (int64_t vt = blockIdx.x; vt < n_etiles;) {
+    int64_t c0, c1;
+    tile_run(n_etiles, c0, c1);
+    for (int64_t vt = c0; vt < c1;) {
         if (vt >= te) {  // uniform: the next tensor
             const int t = int(L.emap[vt]);
             eb = L.ebase[t];
@@ -518,7 +524,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
         }
         const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= E) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, te, gridDim.x);
+            vt = te;
             continue;
         }
         // thread-consecutive entries, as in k_dec_write
@@ -529,7 +535,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_count(
         uint32_t tot;
         block_exclusive_scan(s, lds, tot);
         if (threadIdx.x == 0) tile_s[vt] = tot;
-        vt += gridDim.x;
+        ++vt;
     }
 }
 
@@ -570,7 +576,9 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
     int64_t tb = 0, te = 0, eb = 0, o = 0, nt = 0, E = 0, nb = 0;
     bool merged = false;
     uint2* bnd = nullptr;
-    for (int64_t vt = blockIdx.x; vt < n_etiles;) {
+    int64_t c0, c1;
+    tile_run(n_etiles, c0, c1);
+    for (int64_t vt = c0; vt < c1;) {
         if (vt >= te) {  // uniform: the next tensor
             const int t = int(L.emap[vt]);
             eb = L.ebase[t];
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         }
         const int64_t i0 = (vt - tb) * kTile;
         if (i0 >= E) {  // uniform: nothing here or later in this tensor
-            vt = next_tensor_tile(vt, te, gridDim.x);
+            vt = te;
             continue;
         }
         // Each thread takes kPerThread consecutive entries of the tile: one
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
         if (!merged) {  // uniform
             if (dec_add_tile(i0, E, carry, ex, wv, xv, dense + o, nt, trel, tval))
                 latch_error(sc, kErrCorrupt);
-            vt += gridDim.x;
+            ++vt;
             continue;
         }
         int64_t run = carry + ex;  // entries' (run + 1) before this one
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_write(
             }
         }
         if (bad) latch_error(sc, kErrCorrupt);
-        vt += gridDim.x;
+        ++vt;
     }
 }
 
