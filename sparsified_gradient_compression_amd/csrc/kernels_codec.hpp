@@ -392,6 +392,42 @@ __device__ __forceinline__ void load_vals4(const float* __restrict__ v, int64_t 
     }
 }
 
+// A thread's 4 entries from ib as loaded: run words and values by one 8- and
+// one 16-byte load from min(ib, cap - 4).  A tensor's stream capacity cap
+// is a multiple of kStreamAlign entries, so the address always lies inside
+// it and the loads need no branch; the words are decoded (masked past E)
+// only where they are used, so loads issued for the next tile stay in
+// flight until then.  Needs the runs 8-byte and the values 16-byte aligned
+// and cap >= 4.
+struct RawEntries {
+    uint2 r;
+    float4 v;
+};
+
+__device__ __forceinline__ void load_raw(const uint16_t* __restrict__ r,
+                                         const float* __restrict__ v, int64_t ib, int64_t cap,
+                                         RawEntries& x) {
+    const int64_t ic = min(ib, cap - 4);
+    x.r = *reinterpret_cast<const uint2*>(r + ic);
+    x.v = *reinterpret_cast<const float4*>(v + ic);
+}
+
+// (run + 1) of the loaded entries ib .. ib + 3 (0 past E), and their values.
+__device__ __forceinline__ void raw_entries(const RawEntries& x, int64_t ib, int64_t E,
+                                            uint32_t (&w)[4], float (&val)[4]) {
+    w[0] = (x.r.x & 0xFFFFu) + 1u;
+    w[1] = (x.r.x >> 16) + 1u;
+    w[2] = (x.r.y & 0xFFFFu) + 1u;
+    w[3] = (x.r.y >> 16) + 1u;
+    val[0] = x.v.x;
+    val[1] = x.v.y;
+    val[2] = x.v.z;
+    val[3] = x.v.w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (ib + c >= E) w[c] = 0u;
+}
+
 // Adds one tile of a stream, entries [i0, min(E, i0 + kTile)), into a
 // tensor's part of the dense sum (nt elements).  The thread holds the
 // (run + 1) weights wv and values xv of entries i0 + 4 tid .. + 3 and their
@@ -416,13 +452,27 @@ __device__ __forceinline__ bool dec_add_tile(int64_t i0, int64_t E, int64_t carr
     }
     __syncthreads();
     bool bad = false;
+    int64_t at[kPerThread];  // position of each add, -1 for none
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         const int e = q * kBlock + int(threadIdx.x);
-        if (i0 + e >= E) break;
-        const int64_t pos = carry + trel[e];
-        if (pos >= nt) bad = true;
-        else dense_t[pos] = __fadd_rn(dense_t[pos], tval[e]);
+        at[q] = -1;
+        if (i0 + e < E) {
+            const int64_t pos = carry + trel[e];
+            if (pos >= nt) bad = true;
+            else at[q] = pos;
+        }
+    }
+    // The four dense loads go out together (a lane without an add reads
+    // element 0, which a tensor with entries in range has), so a tile waits
+    // for one round trip, not four.
+    if (nt > 0) {  // uniform
+        float d[kPerThread];
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) d[q] = dense_t[at[q] < 0 ? 0 : at[q]];
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q)
+            if (at[q] >= 0) dense_t[at[q]] = __fadd_rn(d[q], tval[q * kBlock + int(threadIdx.x)]);
     }
     __syncthreads();  // before the next tile overwrites trel
     return bad;
@@ -676,17 +726,47 @@ __global__ __launch_bounds__(kBlock) void k_dec_tensor(DevLayout L, DecBatch S,
         const uint16_t* r = S.runs[w] + eb;
         const float* v = S.vals[w] + eb;
         const bool rvec = aligned_as(r, 8), vvec = aligned_as(v, 16);
+        // With aligned streams the next tile's entries are loaded before
+        // this tile's adds read their dense lines: the two return together,
+        // so each tile after the first waits for one round trip, not two.
+        const bool pre = rvec && vvec && E > 0;  // uniform
         int64_t carry = 0;
-        for (int64_t i0 = 0; i0 < E; i0 += kTile) {
-            const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
-            uint32_t wv[kPerThread];
-            float xv[kPerThread];
-            load_run_weights(r, ib, E, rvec, wv);
-            load_vals4(v, ib, E, vvec, xv);
+        // scan and add one tile whose entries the thread holds
+        auto add = [&](int64_t i0, const uint32_t (&wv)[kPerThread],
+                       const float (&xv)[kPerThread]) {
             uint32_t tot;
             const uint32_t ex = block_exclusive_scan(wv[0] + wv[1] + wv[2] + wv[3], lds, tot);
             bad |= dec_add_tile(i0, E, carry, ex, wv, xv, dense + o, nt, trel, tval);
             carry += tot;
+        };
+        if (pre) {
+            // separate loops: a branch inside one would merge the next
+            // tile's registers there and wait for its loads
+            RawEntries cur;
+            load_raw(r, v, int64_t(threadIdx.x) * kPerThread, cap, cur);
+            for (int64_t i0 = 0; i0 < E; i0 += kTile) {
+                const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+                // issued on every iteration (the last one repeats this
+                // tile's address), so that this tile's words are one load
+                // round behind it and their wait need not drain it
+                RawEntries nxt;
+                load_raw(r, v, i0 + kTile < E ? ib + kTile : ib, cap, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t wv[kPerThread];
+                float xv[kPerThread];
+                raw_entries(cur, ib, E, wv, xv);
+                add(i0, wv, xv);
+                cur = nxt;
+            }
+        } else {
+            for (int64_t i0 = 0; i0 < E; i0 += kTile) {
+                const int64_t ib = i0 + int64_t(threadIdx.x) * kPerThread;
+                uint32_t wv[kPerThread];
+                float xv[kPerThread];
+                load_run_weights(r, ib, E, rvec, wv);
+                load_vals4(v, ib, E, vvec, xv);
+                add(i0, wv, xv);
+            }
         }
     }
     if (bad) latch_error(sc, kErrCorrupt);
