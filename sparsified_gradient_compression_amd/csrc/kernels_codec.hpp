@@ -830,11 +830,11 @@ __global__ __launch_bounds__(kBlock) void k_dec_merge(
     const int64_t blk = int64_t(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (blk >= n_blocks) return;
     const uint32_t tid = threadIdx.x;
-    // round 1: the block's tensor and mode (written by k_dec_mode)
+    // first loads: the block's tensor and mode (written by k_dec_mode)
     const uint32_t bs = Dd.bsel[blk];
     if (!(bs & kBselMerged)) return;  // uniform
     const int t = int(bs & ~kBselMerged);
-    // round 2: all of it depends on t only
+    // second loads: all of them depend on t only
     const int64_t o = L.o[t], nt = L.o[t + 1] - o;
     const int64_t eb = L.ebase[t], cap = L.ebase[t + 1] - eb;
     const int64_t j = blk - Dd.bbase[t];
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_merge(
         }
     }
     if (!any && !fresh) return;  // uniform
-    // round 3: every learner's first kBlock entries, and the block
+    // third loads: every learner's first kBlock entries, and the block
     uint32_t r0[kDecBatch];
     float x0[kDecBatch];
 #pragma unroll
