@@ -738,3 +738,61 @@ def test_encode_path_option_rejects_bad_values():
     for good in (0, 1, 2):
         L.set_option(dgc.DGC_OPT_ENCODE_PATH, good)
     L.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_codec_with_misaligned_buffers(seed):
+    """Index, value, run and stream-value buffers one element past an aligned
+    start (4-, 4-, 2- and 4-byte aligned, so no 8- or 16-byte access fits):
+    both encode paths give the oracle's streams, and both scattered decode
+    paths (spread passes, a workgroup per tensor) read them back into the
+    oracle's sum."""
+    import torch
+    rng = np.random.default_rng(900 + seed)
+    ks = [3, 1024, 1, 2051, 0, 700]
+    made = [filler_heavy_indices(rng, k) for k in ks]
+    idx = np.concatenate([m[0] for m in made])
+    sizes = [m[1] for m in made]
+    val = rng.standard_normal(idx.size).astype(np.float32)
+    K = idx.size
+    L = dgc.Learner(sizes, ks)
+    C = int(L.cap[-1])
+    ib = torch.zeros(K + 8, dtype=torch.int32, device="cuda")
+    vb = torch.zeros(K + 8, dtype=torch.float32, device="cuda")
+    ib[1:1 + K] = torch.from_numpy(idx.view(np.int32)).cuda()
+    vb[1:1 + K] = torch.from_numpy(val).cuda()
+    rb = torch.zeros(C + 16, dtype=torch.int16, device="cuda")
+    sb = torch.zeros(C + 16, dtype=torch.float32, device="cuda")
+    runs, svals = rb[1:1 + C], sb[1:1 + C]
+    ent = torch.zeros(len(ks), dtype=torch.int64, device="cuda")
+    assert ib[1:].data_ptr() % 16 and runs.data_ptr() % 8 and svals.data_ptr() % 16
+    want = oracle_streams(sizes, ks, idx, val)
+    n = sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    dense0 = rng.standard_normal(n).astype(np.float32)
+    want_sum = dense0.copy()
+    for t, (wr, wv) in enumerate(want):
+        assert oracle.decode_accumulate(wr, wv, want_sum[off[t]:off[t + 1]]) == 0
+    for enc in (1, 2):
+        say(f"misaligned codec seed {seed} enc {enc}")
+        L.set_option(dgc.DGC_OPT_ENCODE_PATH, enc)
+        rb.fill_(7)
+        dgc.dgc_encode(L.state, ks, ib[1:], vb[1:], runs, svals, ent)
+        torch.cuda.synchronize()
+        assert L.status() == dgc.DGC_OK
+        r = runs.cpu().numpy().view(np.uint16)
+        s = svals.cpu().numpy()
+        e = ent.cpu().numpy()
+        got = [(r[L.cap[t]:L.cap[t] + e[t]], s[L.cap[t]:L.cap[t] + e[t]])
+               for t in range(len(ks))]
+        compare_streams(got, want, tag=f"misaligned enc{enc}")
+        for path in (1, 3):
+            L.set_option(dgc.DGC_OPT_DECODE_PATH, path)
+            dense = torch.from_numpy(dense0.copy()).cuda()
+            dgc.decode_accumulate(L, [(runs, svals, ent)], dense)
+            torch.cuda.synchronize()
+            assert L.status() == dgc.DGC_OK
+            gd = dense.cpu().numpy()
+            assert np.array_equal(f32_bits(gd), f32_bits(want_sum)), (
+                enc, path, first_diff(gd, want_sum))
+    L.close()
